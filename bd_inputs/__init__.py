@@ -39,6 +39,8 @@ TID = {
     "lens": 10, "cache_k": 11, "cache_v": 12, "carry": 13,
     "prompt": 20, "committed": 21, "tokens": 22,
     "mask": 30, "plant": 40,
+    # stand-alone operands for single-call tests
+    "q": 50, "blk_k": 51, "blk_v": 52, "h": 53, "conf": 54,
 }
 
 

@@ -1,0 +1,69 @@
+"""ctypes loader of libbd.so (the gfx950 HIP library built by build.py).
+
+Loading fails loudly when the library is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbd.so")
+
+BD_OK, BD_EINVAL, BD_EUNSUPPORTED, BD_ECAPACITY, BD_EHIP = 0, 1, 2, 3, 4
+BD_F32, BD_BF16 = 0, 1
+
+c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class BdRows(ctypes.Structure):
+    """Row map: logical row r -> buffer row (r // group) * stride + offset + r % group."""
+    _fields_ = [("group", ctypes.c_int32), ("stride", ctypes.c_int32), ("offset", ctypes.c_int32)]
+
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "bd_version": (ctypes.c_char_p, []),
+    "bd_status_string": (ctypes.c_char_p, [c_int]),
+    "bd_last_hip_error": (c_int, []),
+    "bd_block_attn_workspace_size": (c_size_t, [c_int] * 8),
+    "bd_block_attn": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
+                              c_void_p, c_int, c_int,
+                              c_void_p, c_void_p, c_void_p, c_int,
+                              c_void_p, c_void_p, c_int,
+                              c_float, c_void_p, c_void_p,
+                              c_void_p, c_size_t, c_void_p]),
+    "bd_lmhead_workspace_size": (c_size_t, [c_int] * 4),
+    "bd_lmhead_confidence": (c_int, [c_int, c_int, c_int, c_int,
+                                     c_void_p, c_int, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
+    "bd_threshold_unmask": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_float,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "bd_kv_append": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                             c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    "bd_embed_rows": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "bd_linear": (c_int, [c_int, c_int, c_int, c_int, c_void_p, BdRows, c_void_p,
+                          c_void_p, BdRows, c_void_p, BdRows, c_void_p]),
+    "bd_qkv_proj": (c_int, [c_int, c_int, c_int, c_void_p, BdRows,
+                            c_void_p, c_int, c_void_p, BdRows,
+                            c_void_p, c_void_p, c_int, c_void_p, BdRows, c_void_p, BdRows, c_void_p]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libbd.so not found at {LIB_PATH}; build it with "
+                          "`python -m block_diffusion_decoding_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,204 @@
+// C-ABI entry points of libbd (declared in include/bd.h): argument checks on
+// the host, workspace carving, then the launchers of the kernel files.
+#include <cstdint>
+
+#include "bd_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bd_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return BD_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return BD_EHIP;
+}
+
+bool valid_dtype(bd_dtype dt) { return dt == BD_F32 || dt == BD_BF16; }
+
+bool valid_rows(const bd_rows& r) { return r.group >= 1 && r.stride >= 0 && r.offset >= 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bd_version(void) { return "libbd 0.1 (gfx950)"; }
+
+const char* bd_status_string(bd_status s) {
+  switch (s) {
+    case BD_OK: return "ok";
+    case BD_EINVAL: return "invalid argument";
+    case BD_EUNSUPPORTED: return "unsupported";
+    case BD_ECAPACITY: return "cache capacity exceeded";
+    case BD_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int bd_last_hip_error(void) { return g_last_hip_error; }
+
+// ---------------------------------------------------------------------------
+size_t bd_block_attn_workspace_size(bd_dtype dt, int B, int Hq, int Hkv, int d, int n_q, int cap, int n_blk) {
+  if (!valid_dtype(dt) || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || n_q <= 0 || cap < 0 || n_blk <= 0)
+    return 0;
+  return bd_attn_plan(dt, B, Hq, Hkv, d, n_q, cap, n_blk).ws_bytes;
+}
+
+bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const void* q, int n_q, int q_off,
+                        const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
+                        const void* k_blk, const void* v_blk, int n_blk, float scale, void* o, float* lse,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dt) || B < 0 || n_q < 0) return BD_EINVAL;
+  if (B == 0 || n_q == 0) return BD_OK;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D < 1 || n_blk < 1 || n_blk % D != 0 || q_off < 0 ||
+      q_off + n_q > n_blk || cap < 0)
+    return BD_EINVAL;
+  if (d != 64 && d != 128) return BD_EUNSUPPORTED;
+  if (!q || !kv_len || !k_blk || !v_blk || !o || (cap > 0 && (!k_cache || !v_cache))) return BD_EINVAL;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
+      (cap > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return BD_EINVAL;
+  if (!(scale == scale)) return BD_EINVAL;
+  const BdAttnPlan p = bd_attn_plan(dt, B, Hq, Hkv, d, n_q, cap, n_blk);
+  if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)))
+    return BD_EINVAL;
+  BdAttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_len = kv_len;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_o) : nullptr;
+  a.part_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_ml) : nullptr;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.d = d;
+  a.D = D;
+  a.n_q = n_q;
+  a.q_off = q_off;
+  a.cap = cap;
+  a.n_blk = n_blk;
+  a.scale = scale;
+  return hip_status(bd_attn_launch(dt, p, a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+size_t bd_lmhead_workspace_size(bd_dtype dt, int M, int hidden, int V) {
+  if (!valid_dtype(dt) || M <= 0 || hidden <= 0 || V <= 0) return 0;
+  return bd_lm_plan(dt, M, hidden, V).ws_bytes;
+}
+
+bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
+                               const int32_t* row_idx, const void* w, int32_t* argmax, float* conf,
+                               float* max_logit, float* lse, float* logits, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
+  if (M == 0) return BD_OK;
+  if (hidden <= 0 || V <= 0 || n_src <= 0 || !h_src || !w || !argmax || !conf) return BD_EINVAL;
+  if (row_idx == nullptr && n_src < M) return BD_EINVAL;
+  if (dt == BD_BF16 && (hidden % 256 != 0 || !aligned16(h_src) || !aligned16(w))) return BD_EUNSUPPORTED;
+  const BdLmPlan p = bd_lm_plan(dt, M, hidden, V);
+  if (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)) return BD_EINVAL;
+  const size_t n = (size_t)M * p.nvt;
+  BdLmArgs a{};
+  a.h = h_src;
+  a.n_src = n_src;
+  a.row_idx = row_idx;
+  a.w = w;
+  a.argmax = argmax;
+  a.conf = conf;
+  a.max_logit = max_logit;
+  a.lse = lse;
+  a.logits = logits;
+  a.M = M;
+  a.hidden = hidden;
+  a.V = V;
+  a.pmax = static_cast<float*>(workspace);
+  a.psum = a.pmax + n;
+  a.pidx = reinterpret_cast<int32_t*>(a.psum + n);
+  return hip_status(bd_lm_launch(dt, p, a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+bd_status bd_threshold_unmask(int B, int D, int win_lo, int win_len, const float* conf, const int32_t* argmax,
+                              float threshold, int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
+                              int32_t* unmasked_pos, void* stream) {
+  if (B < 0) return BD_EINVAL;
+  if (B == 0) return BD_OK;
+  if (D < 1 || D > 64 || win_lo < 0 || win_len < 1 || win_len > 64 || win_lo + win_len > D) return BD_EINVAL;
+  if (!conf || !argmax || !tokens || !mask_bits || !(threshold == threshold)) return BD_EINVAL;
+  return hip_status(bd_unmask_launch(B, D, win_lo, win_len, conf, argmax, threshold, tokens, mask_bits,
+                                     n_unmasked, unmasked_pos, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+bd_status bd_kv_append(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache, void* v_cache, int32_t* kv_len,
+                       const int32_t* kv_len_host, const void* k_blk, const void* v_blk, int n_blk, int n_rows,
+                       void* stream) {
+  if (!valid_dtype(dt) || B < 0 || n_rows < 0) return BD_EINVAL;
+  if (B == 0 || n_rows == 0) return BD_OK;
+  if (Hkv <= 0 || d <= 0 || cap <= 0 || n_blk < n_rows || !k_cache || !v_cache || !kv_len || !k_blk || !v_blk)
+    return BD_EINVAL;
+  if ((d * (dt == BD_F32 ? 4 : 2)) % 16 != 0 || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(k_blk) || !aligned16(v_blk))
+    return BD_EINVAL;
+  if (kv_len_host != nullptr)
+    for (int b = 0; b < B; ++b)
+      if (kv_len_host[b] < 0 || (long)kv_len_host[b] + n_rows > cap) return BD_ECAPACITY;
+  return hip_status(bd_append_launch(dt, B, Hkv, d, cap, k_cache, v_cache, kv_len, k_blk, v_blk, n_blk, n_rows,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V, const void* E,
+                        const int32_t* tokens, const uint64_t* mask_bits, const void* plant, void* x,
+                        void* stream) {
+  if (!valid_dtype(dt) || B < 0 || n_rows < 0) return BD_EINVAL;
+  if (B == 0 || n_rows == 0) return BD_OK;
+  if (D < 1 || (mask_bits != nullptr && D > 64) || row_off < 0 || row_off + n_rows > D || hidden <= 0 || V <= 0 ||
+      !E || !tokens || !x)
+    return BD_EINVAL;
+  return hip_status(bd_embed_launch(dt, B, D, row_off, n_rows, hidden, V, E, tokens, mask_bits, plant, x,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const BdGemmSeg* segs, int nseg,
+                             void* stream) {
+  if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
+  if (M == 0) return BD_OK;
+  if (K <= 0 || !x || !valid_rows(xr)) return BD_EINVAL;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].N <= 0 || !segs[i].w || !segs[i].y || !valid_rows(segs[i].yr)) return BD_EINVAL;
+    if (segs[i].res && !valid_rows(segs[i].rr)) return BD_EINVAL;
+  }
+  if (dt == BD_BF16) {
+    if (K % 256 != 0 || !aligned16(x)) return BD_EUNSUPPORTED;
+    for (int i = 0; i < nseg; ++i)
+      if (!aligned16(segs[i].w)) return BD_EUNSUPPORTED;
+  }
+  return hip_status(bd_gemm_launch(dt, M, K, x, xr, segs, nseg, static_cast<hipStream_t>(stream)));
+}
+
+bd_status bd_linear(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr, const void* w, const void* res,
+                    bd_rows rr, void* y, bd_rows yr, void* stream) {
+  BdGemmSeg seg{w, y, yr, res, rr, N};
+  return gemm_common(dt, M, K, x, xr, &seg, 1, stream);
+}
+
+bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,
+                      bd_rows qr, const void* wk, const void* wv, int Nkv, void* k, bd_rows kr, void* v, bd_rows vr,
+                      void* stream) {
+  const bd_rows none{1, 1, 0};
+  BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
+                       {wv, v, vr, nullptr, none, Nkv}};
+  return gemm_common(dt, M, K, x, xr, segs, 3, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels of libbd.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bd.h"
+
+typedef __bf16 bd_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float bd_f32x4 __attribute__((ext_vector_type(4)));
+
+#define BD_LOG2E 1.4426950408889634f
+#define BD_LN2 0.6931471805599453f
+#define BD_NEG_INF (-__builtin_inff())
+
+// bf16 is stored as its 16 raw bits.
+__device__ __forceinline__ float bd_bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bd_f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t bd_pack_bf2(float lo, float hi) {
+  return bd_f2bf(lo) | (bd_f2bf(hi) << 16);
+}
+
+// v_mfma_f32_16x16x32_bf16.  Lane l supplies A row (l % 16) and B column
+// (l % 16), eight consecutive K slots 8*(l/16) .. 8*(l/16)+7 each; it receives
+// C rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).  Any fixed permutation of
+// the K slots applied to both A and B leaves the product unchanged, which the
+// kernels use to pick load-friendly K orders.
+__device__ __forceinline__ bd_f32x4 bd_mfma16(const uint4& a, const uint4& b, bd_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8, a),
+                                                __builtin_bit_cast(bd_bf16x8, b), c, 0, 0, 0);
+}
+
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float bd_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float bd_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Row maps (see bd_rows in bd.h).
+__device__ __forceinline__ int bd_map_row(const bd_rows& m, int r) {
+  return (r / m.group) * m.stride + m.offset + (r % m.group);
+}
+
+// (max, argmax, sum of exp(x - max)) triples: the combine is associative and
+// commutative up to the rounding of the sum; argmax ties go to the lower index.
+struct BdArgStat {
+  float m;
+  int i;
+  float s;
+};
+
+__device__ __forceinline__ BdArgStat bd_stat_combine(BdArgStat a, BdArgStat b) {
+  BdArgStat r;
+  r.m = fmaxf(a.m, b.m);
+  r.i = (a.m > b.m) ? a.i : (b.m > a.m) ? b.i : min(a.i, b.i);
+  float sa = (a.m == BD_NEG_INF) ? 0.f : a.s * bd_exp2((a.m - r.m) * BD_LOG2E);
+  float sb = (b.m == BD_NEG_INF) ? 0.f : b.s * bd_exp2((b.m - r.m) * BD_LOG2E);
+  r.s = sa + sb;
+  return r;
+}
+
+__device__ __forceinline__ BdArgStat bd_stat_shfl_xor(BdArgStat a, int mask) {
+  BdArgStat b;
+  b.m = __shfl_xor(a.m, mask);
+  b.i = __shfl_xor(a.i, mask);
+  b.s = __shfl_xor(a.s, mask);
+  return b;
+}

@@ -1,0 +1,96 @@
+// Host-side launchers of the libbd kernels (internal; the C ABI is bd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bd.h"
+
+// ---- attention -----------------------------------------------------------
+struct BdAttnPlan {
+  int R;          // query rows per (sequence, KV head) = n_q * G
+  int QT;         // 16-row query tiles
+  int qpw;        // query tiles per wave
+  int nqg;        // query-tile groups (work items along the query rows)
+  int chunk;      // keys per work item
+  int nchunks;    // key chunks (max over sequences)
+  size_t part_o;  // workspace offsets / sizes in bytes
+  size_t part_ml;
+  size_t ws_bytes;
+};
+
+BdAttnPlan bd_attn_plan(bd_dtype dt, int B, int Hq, int Hkv, int d, int n_q, int cap, int n_blk);
+
+struct BdAttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* kv_len;
+  const void* k_blk;
+  const void* v_blk;
+  void* o;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+  int B, Hq, Hkv, G, d, D, n_q, q_off, cap, n_blk;
+  float scale;
+};
+
+hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& a, hipStream_t s);
+
+// ---- LM head ---------------------------------------------------------------
+struct BdLmPlan {
+  int cols_per_wg;  // vocabulary columns per work-group
+  int nvt;          // vocabulary tiles (work-groups along V)
+  int rows_per_wg;  // rows of h per work-group
+  int nmb;          // row blocks
+  size_t ws_bytes;  // partial (max, argmax, sum) per (row, tile)
+};
+
+BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V);
+
+struct BdLmArgs {
+  const void* h;
+  int n_src;
+  const int32_t* row_idx;
+  const void* w;
+  int32_t* argmax;
+  float* conf;
+  float* max_logit;
+  float* lse;
+  float* logits;
+  int M, hidden, V;
+  float* pmax;
+  int32_t* pidx;
+  float* psum;
+};
+
+hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& a, hipStream_t s);
+
+// ---- projections -------------------------------------------------------------
+struct BdGemmSeg {
+  const void* w;   // [N, K]
+  void* y;         // rows of N elements
+  bd_rows yr;
+  const void* res; // optional residual, rows of N elements
+  bd_rows rr;
+  int N;
+};
+
+hipError_t bd_gemm_launch(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
+                          const BdGemmSeg* segs, int nseg, hipStream_t s);
+
+hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
+                           const void* E, const int32_t* tokens, const uint64_t* mask_bits,
+                           const void* plant, void* x, hipStream_t s);
+
+// ---- unmask / append ---------------------------------------------------------
+hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* conf,
+                            const int32_t* argmax, float threshold, int32_t* tokens,
+                            uint64_t* mask_bits, int32_t* n_unmasked, int32_t* unmasked_pos,
+                            hipStream_t s);
+
+hipError_t bd_append_launch(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache,
+                            void* v_cache, int32_t* kv_len, const void* k_blk, const void* v_blk,
+                            int n_blk, int n_rows, hipStream_t s);

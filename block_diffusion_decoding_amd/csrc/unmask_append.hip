@@ -1,0 +1,92 @@
+// Confidence-threshold unmasking and the block-level cache append.
+//
+// Unmask: "Fast-dLLM v2: Efficient Block-Diffusion LLM" notes, Key design 3
+// (masked positions whose confidence exceeds the threshold are decoded in
+// parallel, the rest wait; threshold 1.0 reduces to one token per step) and
+// the "Fast-dLLM" v1 article, Core technique 2.  One wavefront per sequence:
+// a ballot over the window's lanes gives the passing set, a wave max gives
+// the fallback pick, and mbcnt-style prefix counts compact the positions.
+//
+// Append: Key design 3 and the v2 news article's hierarchical-cache
+// paragraph -- a finished block's K/V become read-only context.
+#include "bd_device.h"
+#include "bd_launch.h"
+
+namespace {
+
+__global__ __launch_bounds__(64) void unmask_kernel(int D, int win_lo, int win_len, const float* conf,
+                                                    const int32_t* argmax, float thr, int32_t* tokens,
+                                                    uint64_t* mask_bits, int32_t* n_unmasked,
+                                                    int32_t* unmasked_pos) {
+  const int b = blockIdx.x;
+  const int r = threadIdx.x;
+  const int pos = win_lo + r;
+  const uint64_t bits = mask_bits[b];
+  const bool cand = r < win_len && ((bits >> pos) & 1ull);
+  float c = cand ? conf[(size_t)b * win_len + r] : BD_NEG_INF;
+  if (c != c) c = BD_NEG_INF;  // a NaN confidence never passes and ranks last
+  uint64_t pick = __ballot(cand && c > thr);
+  const uint64_t cands = __ballot(cand);
+  if (pick == 0 && cands != 0) {
+    float best = cand ? c : BD_NEG_INF;
+    for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+    const uint64_t eq = __ballot(cand && c == best);
+    pick = eq & (~eq + 1ull);  // lowest position among the most confident
+  }
+  const bool mine = (pick >> r) & 1ull;
+  if (mine) tokens[(size_t)b * D + pos] = argmax[(size_t)b * win_len + r];
+  const int n = __popcll(pick);
+  if (unmasked_pos != nullptr && r < win_len) {
+    const int rank = __popcll(pick & ((1ull << r) - 1ull));
+    if (mine) unmasked_pos[(size_t)b * win_len + rank] = pos;
+    if (r >= n) unmasked_pos[(size_t)b * win_len + r] = -1;
+  }
+  if (r == 0) {
+    mask_bits[b] = bits & ~(pick << win_lo);
+    if (n_unmasked != nullptr) n_unmasked[b] = n;
+  }
+}
+
+// One work-group per sequence: copy n_rows in-block rows behind the committed
+// rows of every KV head, then advance the committed length.
+__global__ __launch_bounds__(256) void append_kernel(int Hkv, int row_bytes, int cap, uint8_t* k_cache,
+                                                     uint8_t* v_cache, int32_t* kv_len, const uint8_t* k_blk,
+                                                     const uint8_t* v_blk, int n_blk, int n_rows) {
+  const int b = blockIdx.x;
+  int L = kv_len[b];
+  L = L < 0 ? 0 : L;
+  const int pieces = row_bytes / 16;
+  const int total = Hkv * n_rows * pieces;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int p = e % pieces;
+    const int row = (e / pieces) % n_rows;
+    const int h = e / pieces / n_rows;
+    if (L + row >= cap) continue;
+    const size_t src = (((size_t)b * n_blk + row) * Hkv + h) * row_bytes + p * 16;
+    const size_t dst = (((size_t)b * Hkv + h) * cap + L + row) * row_bytes + p * 16;
+    *reinterpret_cast<uint4*>(k_cache + dst) = *reinterpret_cast<const uint4*>(k_blk + src);
+    *reinterpret_cast<uint4*>(v_cache + dst) = *reinterpret_cast<const uint4*>(v_blk + src);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) kv_len[b] = L + n_rows;
+}
+
+}  // namespace
+
+hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* conf, const int32_t* argmax,
+                            float threshold, int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
+                            int32_t* unmasked_pos, hipStream_t s) {
+  hipLaunchKernelGGL(unmask_kernel, dim3(B), dim3(64), 0, s, D, win_lo, win_len, conf, argmax, threshold, tokens,
+                     mask_bits, n_unmasked, unmasked_pos);
+  return hipGetLastError();
+}
+
+hipError_t bd_append_launch(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache, void* v_cache,
+                            int32_t* kv_len, const void* k_blk, const void* v_blk, int n_blk, int n_rows,
+                            hipStream_t s) {
+  const int row_bytes = d * (dt == BD_F32 ? 4 : 2);
+  hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, s, Hkv, row_bytes, cap,
+                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), kv_len,
+                     static_cast<const uint8_t*>(k_blk), static_cast<const uint8_t*>(v_blk), n_blk, n_rows);
+  return hipGetLastError();
+}

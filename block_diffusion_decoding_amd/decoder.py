@@ -1,0 +1,240 @@
+"""Block-diffusion refinement driver on one GPU (one attention layer + LM head).
+
+Every arithmetic step runs in libbd's HIP kernels through ``ops``; torch only
+allocates device memory and supplies the stream.  Names follow the method
+("Fast-dLLM v2: Efficient Block-Diffusion LLM" notes, Key designs 2-4):
+
+* block of D positions, windows (sub-blocks) of S positions, threshold tau;
+* exact step (E-step): every block row is recomputed; it also refreshes the
+  DualCache snapshot (in-block K/V of all D rows and the output rows);
+* DualCache step (DC-step): only the S window rows are recomputed; the other
+  in-block K/V and output rows come from the snapshot;
+* commit: forward pass over the finished clean block, its K/V appended to the
+  block-level cache and its last output row kept as the carry.
+
+Device buffers (per sequence b):
+  cache_k/v [B, Hkv, cap, d]   block-level cache, kv_len [B] committed rows
+  blk_k/v   [B, D, Hkv, d]     in-block K/V (fresh rows + snapshot rows)
+  H         [B, 1 + D, hidden] row 0 = carry, row 1 + j = output row of block
+                               position j (so position j is predicted from
+                               row j: the token shift is row j - 1 of the block)
+  tokens    [B, D] int32, mask_bits [B] (bit j = position j is [MASK])
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import ops
+from .ops import dense, rows
+
+
+@dataclass
+class Dims:
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    hidden: int
+    V: int
+    D: int = 32
+    cap: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+class BlockDecoder:
+    """Owns the device state of a batch of sequences decoded block by block."""
+
+    def __init__(self, dims: Dims, weights: dict, dtype=torch.bfloat16, device="cuda"):
+        self.dims = dims
+        self.dtype = dtype
+        self.device = torch.device(device)
+        dev, dt = self.device, dtype
+        B, D, Hq, Hkv, d, hid = dims.B, dims.D, dims.Hq, dims.Hkv, dims.d, dims.hidden
+        assert Hq * d == hid or True
+        self.W = {k: v.to(dev, dt).contiguous() for k, v in weights.items()}
+        assert self.W["E"].shape == (dims.V + 1, hid)
+        self.cache_k = torch.zeros(B, Hkv, dims.cap, d, dtype=dt, device=dev)
+        self.cache_v = torch.zeros_like(self.cache_k)
+        self.kv_len = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.kv_len_host = np.zeros(B, dtype=np.int32)
+        self.blk_k = torch.zeros(B, D, Hkv, d, dtype=dt, device=dev)
+        self.blk_v = torch.zeros_like(self.blk_k)
+        self.H = torch.zeros(B, 1 + D, hid, dtype=dt, device=dev)
+        self.X = torch.zeros(B, D, hid, dtype=dt, device=dev)
+        self.q = torch.zeros(B, D, Hq, d, dtype=dt, device=dev)
+        self.o = torch.zeros(B, D, Hq, d, dtype=dt, device=dev)
+        self.tokens = torch.zeros(B, D, dtype=torch.int32, device=dev)
+        self.mask_bits = torch.zeros(B, dtype=torch.int64, device=dev)
+        self.plant = None
+        self.n_unmasked = torch.zeros(B, dtype=torch.int32, device=dev)
+        self._win = {}
+        self.last = None
+
+    # ------------------------------------------------------------------ state
+    def set_synthetic_prefix(self, kv_len, cache_k, cache_v, carry):
+        """Committed context given directly (random K/V rows and carry row)."""
+        L = np.asarray(kv_len, dtype=np.int32)
+        self.cache_k.copy_(torch.as_tensor(cache_k).to(self.device, self.dtype))
+        self.cache_v.copy_(torch.as_tensor(cache_v).to(self.device, self.dtype))
+        self.kv_len.copy_(torch.from_numpy(L).to(self.device))
+        self.kv_len_host = L.copy()
+        self.H[:, 0].copy_(torch.as_tensor(carry).to(self.device, self.dtype))
+
+    def set_tokens(self, tokens, masked):
+        """Token state of the current block: tokens [B, D], masked [B, D] bool."""
+        D = self.dims.D
+        t = np.asarray(tokens, dtype=np.int32)
+        m = np.asarray(masked, dtype=bool)
+        bits = np.zeros(self.dims.B, dtype=np.uint64)
+        for j in range(D):
+            bits |= m[:, j].astype(np.uint64) << np.uint64(j)
+        self.tokens.copy_(torch.from_numpy(t).to(self.device))
+        self.mask_bits.copy_(torch.from_numpy(bits.view(np.int64)).to(self.device))
+
+    def set_block(self, tokens, masked, plant=None, carry_offset=None):
+        """Current block: tokens [B, D], masked [B, D] bool, optional plant
+        [B, D, hidden] (offset on the block's input rows) and carry offset."""
+        self.set_tokens(tokens, masked)
+        self.plant = None if plant is None else torch.as_tensor(plant).to(self.device, self.dtype).contiguous()
+        if carry_offset is not None:
+            self.H[:, 0] += torch.as_tensor(carry_offset).to(self.device, self.dtype)
+
+    def new_block(self):
+        B, D = self.dims.B, self.dims.D
+        self.set_block(np.zeros((B, D), np.int32), np.ones((B, D), bool))
+
+    def masked_host(self) -> np.ndarray:
+        bits = self.mask_bits.cpu().numpy().view(np.uint64)
+        return np.stack([(bits >> np.uint64(j)) & np.uint64(1) for j in range(self.dims.D)], 1).astype(bool)
+
+    # ------------------------------------------------------------ step parts
+    def _window(self, s: int, S: int):
+        """Per-window LM-head buffers; row_idx expresses the token shift."""
+        key = (s, S)
+        w = self._win.get(key)
+        if w is None:
+            B, D = self.dims.B, self.dims.D
+            idx = np.array([b * (1 + D) + s * S + r for b in range(B) for r in range(S)], dtype=np.int32)
+            w = dict(row_idx=torch.from_numpy(idx).to(self.device),
+                     argmax=torch.zeros(B, S, dtype=torch.int32, device=self.device),
+                     conf=torch.zeros(B, S, dtype=torch.float32, device=self.device),
+                     maxl=torch.zeros(B, S, dtype=torch.float32, device=self.device),
+                     lse=torch.zeros(B, S, dtype=torch.float32, device=self.device),
+                     pos=torch.zeros(B, S, dtype=torch.int32, device=self.device))
+            self._win[key] = w
+        return w
+
+    def _forward_rows(self, lo: int, n: int):
+        """Input rows, Q/K/V and attention of block rows [lo, lo + n)."""
+        dm, W = self.dims, self.W
+        B, D = dm.B, dm.D
+        X = self.X[:, :n] if n == D else self.X.view(-1)[: B * n * dm.hidden].view(B, n, dm.hidden)
+        q = self.q.view(-1)[: B * n * dm.Hq * dm.d].view(B, n, dm.Hq, dm.d)
+        o = self.o.view(-1)[: B * n * dm.Hq * dm.d].view(B, n, dm.Hq, dm.d)
+        ops.bd_embed_rows(W["E"], self.tokens, self.mask_bits, X, row_off=lo, n_rows=n, plant=self.plant)
+        kr = rows(n, D, lo)
+        ops.bd_qkv_proj(X, dense(B * n), W["Wq"], q, dense(B * n), W["Wk"], W["Wv"], self.blk_k, kr,
+                        self.blk_v, kr, M=B * n)
+        ops.bd_block_attn(q, self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, o,
+                          D=D, q_off=lo)
+        return X, o
+
+    def _lm_and_unmask(self, s: int, S: int, tau: float):
+        w = self._window(s, S)
+        dm = self.dims
+        ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"], w["conf"],
+                                 max_logit=w["maxl"], lse=w["lse"])
+        ops.bd_threshold_unmask(w["conf"], w["argmax"], self.tokens, self.mask_bits, win_lo=s * S,
+                                threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
+        self.last = w
+
+    def e_step(self, s: int, S: int, tau: float):
+        """Exact step for window s; refreshes the DualCache snapshot."""
+        dm = self.dims
+        B, D = dm.B, dm.D
+        X, o = self._forward_rows(0, D)
+        ops.bd_linear(o, dense(B * D), self.W["Wo"], self.H, rows(D, 1 + D, 1), M=B * D,
+                      res=X, rr=dense(B * D))
+        self._lm_and_unmask(s, S, tau)
+
+    def dc_step(self, s: int, S: int, tau: float):
+        """DualCache step for window s (snapshot rows outside the window)."""
+        dm = self.dims
+        B, D = dm.B, dm.D
+        X, o = self._forward_rows(s * S, S)
+        ops.bd_linear(o, dense(B * S), self.W["Wo"], self.H, rows(S, 1 + D, 1 + s * S), M=B * S,
+                      res=X, rr=dense(B * S))
+        self._lm_and_unmask(s, S, tau)
+
+    def commit(self, check_capacity: bool = True):
+        """Forward over the finished block, append its K/V, keep the carry."""
+        dm = self.dims
+        B, D = dm.B, dm.D
+        X, o = self._forward_rows(0, D)
+        ops.bd_linear(o, rows(1, D, D - 1), self.W["Wo"], self.H, rows(1, 1 + D, 0), M=B,
+                      res=X, rr=rows(1, D, D - 1))
+        ops.bd_kv_append(self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, n_rows=D,
+                         kv_len_host=self.kv_len_host if check_capacity else None)
+        self.kv_len_host = self.kv_len_host + D
+
+    def prefill(self, prompt):
+        """Block-aligned prompt [B, P] under the hybrid mask (multi-block
+        attention); its K/V fill the cache and its last output row is the carry."""
+        dm, W = self.dims, self.W
+        B, D = dm.B, dm.D
+        prompt = np.asarray(prompt, dtype=np.int32)
+        P = prompt.shape[1]
+        assert P % D == 0
+        dev, dt = self.device, self.dtype
+        toks = torch.from_numpy(prompt).to(dev)
+        X = torch.empty(B, P, dm.hidden, dtype=dt, device=dev)
+        q = torch.empty(B, P, dm.Hq, dm.d, dtype=dt, device=dev)
+        o = torch.empty_like(q)
+        pk = torch.empty(B, P, dm.Hkv, dm.d, dtype=dt, device=dev)
+        pv = torch.empty_like(pk)
+        zero_len = torch.zeros(B, dtype=torch.int32, device=dev)
+        ops.bd_embed_rows(W["E"], toks, None, X, row_off=0, n_rows=P)
+        ops.bd_qkv_proj(X, dense(B * P), W["Wq"], q, dense(B * P), W["Wk"], W["Wv"], pk, dense(B * P),
+                        pv, dense(B * P), M=B * P)
+        ops.bd_block_attn(q, self.cache_k, self.cache_v, zero_len, pk, pv, o, D=D, q_off=0)
+        ops.bd_linear(o, rows(1, P, P - 1), W["Wo"], self.H, rows(1, 1 + D, 0), M=B,
+                      res=X, rr=rows(1, P, P - 1))
+        self.kv_len.zero_()
+        self.kv_len_host = np.zeros(B, dtype=np.int32)
+        ops.bd_kv_append(self.cache_k, self.cache_v, self.kv_len, pk, pv, n_rows=P, kv_len_host=self.kv_len_host)
+        self.kv_len_host = self.kv_len_host + P
+
+    # ------------------------------------------------------------------ loop
+    def decode_block(self, S: int, tau: float, mode: str = "dual", steps_per_window: int | None = None,
+                     on_step=None):
+        """Decode the current block window by window (lockstep over the batch),
+        then commit it.  With ``steps_per_window`` the number of steps per
+        window is fixed (no host synchronisation); otherwise the window ends
+        when no position of it is masked in any sequence."""
+        D = self.dims.D
+        n = 0
+        for s in range(D // S):
+            k = 0
+            while True:
+                if steps_per_window is not None:
+                    if k >= steps_per_window:
+                        break
+                else:
+                    bits = self.mask_bits.cpu().numpy().view(np.uint64)
+                    wmask = np.uint64(((1 << S) - 1) << (s * S))
+                    if not np.any(bits & wmask):
+                        break
+                kind = "E" if (k == 0 or mode == "exact") else "DC"
+                (self.e_step if kind == "E" else self.dc_step)(s, S, tau)
+                if on_step is not None:
+                    on_step(n, s, kind)
+                k += 1
+                n += 1
+        self.commit()
+        return n

@@ -1,0 +1,171 @@
+"""Python binding of libbd: one function per C-ABI call, same names.
+
+Argument marshalling only: tensors supply device pointers, the current torch
+stream supplies the HIP stream, and every step runs in the library's HIP
+kernels.  A non-OK status raises ``BdError``.  Shapes follow include/bd.h.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import BdRows
+
+_DT = {torch.float32: _lib.BD_F32, torch.bfloat16: _lib.BD_BF16}
+
+
+class BdError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        lib = _lib.load()
+        msg = lib.bd_status_string(status).decode()
+        extra = f" (hipError {lib.bd_last_hip_error()})" if status == _lib.BD_EHIP else ""
+        super().__init__(f"{name}: {msg}{extra}")
+        self.status = status
+
+
+def _check(name, status):
+    if status != _lib.BD_OK:
+        raise BdError(name, status)
+
+
+def _p(t):
+    """Device pointer of a tensor (or 0 for None); tensors must be contiguous."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libbd tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dt(t):
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def rows(group: int, stride: int, offset: int = 0) -> BdRows:
+    return BdRows(int(group), int(stride), int(offset))
+
+
+def dense(n: int) -> BdRows:
+    return BdRows(int(n), int(n), 0)
+
+
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device, tag: str = "") -> torch.Tensor:
+    """A cached zero-initialised workspace per (device, tag), grown on demand."""
+    key = (str(device), tag)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------
+def bd_block_attn_workspace_size(dtype, B, Hq, Hkv, d, n_q, cap, n_blk) -> int:
+    return int(_lib.load().bd_block_attn_workspace_size(_DT[dtype], B, Hq, Hkv, d, n_q, cap, n_blk))
+
+
+def bd_block_attn(q, k_cache, v_cache, kv_len, k_blk, v_blk, o, *, D, q_off=0, scale=None, lse=None,
+                  ws=None, stream=None):
+    """q [B, n_q, Hq, d]; k/v_cache [B, Hkv, cap, d]; kv_len [B] int32; k/v_blk [B, n_blk, Hkv, d];
+    o [B, n_q, Hq, d]; lse [B, Hq, n_q] fp32 or None."""
+    lib = _lib.load()
+    B, n_q, Hq, d = q.shape
+    _, Hkv, cap, _ = k_cache.shape
+    n_blk = k_blk.shape[1]
+    if scale is None:
+        scale = d ** -0.5
+    dt = _dt(q)
+    need = lib.bd_block_attn_workspace_size(dt, B, Hq, Hkv, d, n_q, cap, n_blk)
+    if ws is None:
+        ws = workspace(need, q.device, "attn")
+    st = lib.bd_block_attn(dt, B, Hq, Hkv, d, D, _p(q), n_q, q_off, _p(k_cache), _p(v_cache), _p(kv_len), cap,
+                           _p(k_blk), _p(v_blk), n_blk, float(scale), _p(o), _p(lse), _p(ws), ws.numel(),
+                           _stream(stream))
+    _check("bd_block_attn", st)
+    return o
+
+
+def bd_lmhead_workspace_size(dtype, M, hidden, V) -> int:
+    return int(_lib.load().bd_lmhead_workspace_size(_DT[dtype], M, hidden, V))
+
+
+def bd_lmhead_confidence(h_src, row_idx, w, argmax, conf, *, max_logit=None, lse=None, logits=None, M=None,
+                         ws=None, stream=None):
+    """h_src [n_src, hidden]; row_idx [M] int32 or None; w [V, hidden]; argmax [M] int32; conf [M] fp32."""
+    lib = _lib.load()
+    hidden = h_src.shape[-1]
+    n_src = h_src.numel() // hidden
+    V = w.shape[0]
+    if M is None:
+        M = row_idx.numel() if row_idx is not None else n_src
+    dt = _dt(h_src)
+    need = lib.bd_lmhead_workspace_size(dt, M, hidden, V)
+    if ws is None:
+        ws = workspace(need, h_src.device, "lm")
+    st = lib.bd_lmhead_confidence(dt, M, hidden, V, _p(h_src), n_src, _p(row_idx), _p(w), _p(argmax), _p(conf),
+                                  _p(max_logit), _p(lse), _p(logits), _p(ws), ws.numel(), _stream(stream))
+    _check("bd_lmhead_confidence", st)
+
+
+def bd_threshold_unmask(conf, argmax, tokens, mask_bits, *, win_lo, threshold, n_unmasked=None,
+                        unmasked_pos=None, stream=None):
+    """conf/argmax [B, win_len]; tokens [B, D] int32; mask_bits [B] (64-bit)."""
+    lib = _lib.load()
+    B, win_len = conf.shape
+    D = tokens.shape[1]
+    st = lib.bd_threshold_unmask(B, D, win_lo, win_len, _p(conf), _p(argmax), float(threshold), _p(tokens),
+                                 _p(mask_bits), _p(n_unmasked), _p(unmasked_pos), _stream(stream))
+    _check("bd_threshold_unmask", st)
+
+
+def bd_kv_append(k_cache, v_cache, kv_len, k_blk, v_blk, *, n_rows, kv_len_host=None, stream=None):
+    """k/v_cache [B, Hkv, cap, d]; kv_len [B] int32 (in/out); k/v_blk [B, n_blk, Hkv, d]."""
+    lib = _lib.load()
+    B, Hkv, cap, d = k_cache.shape
+    n_blk = k_blk.shape[1]
+    host = None
+    if kv_len_host is not None:
+        import numpy as np
+        host = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+    st = lib.bd_kv_append(_dt(k_cache), B, Hkv, d, cap, _p(k_cache), _p(v_cache), _p(kv_len),
+                          None if host is None else host.ctypes.data, _p(k_blk), _p(v_blk), n_blk, n_rows,
+                          _stream(stream))
+    _check("bd_kv_append", st)
+
+
+def bd_embed_rows(E, tokens, mask_bits, x, *, row_off, n_rows, plant=None, stream=None):
+    """E [V+1, hidden]; tokens [B, D] int32; mask_bits [B] or None; x [B, n_rows, hidden]."""
+    lib = _lib.load()
+    B, D = tokens.shape
+    V = E.shape[0] - 1
+    st = lib.bd_embed_rows(_dt(E), B, D, row_off, n_rows, E.shape[1], V, _p(E), _p(tokens), _p(mask_bits),
+                           _p(plant), _p(x), _stream(stream))
+    _check("bd_embed_rows", st)
+
+
+def bd_linear(x, xr, w, y, yr, *, M, res=None, rr=None, stream=None):
+    """y[yr(m)] = x[xr(m)] w^T (+ res[rr(m)]); w [N, K]."""
+    lib = _lib.load()
+    N, K = w.shape
+    st = lib.bd_linear(_dt(w), M, N, K, _p(x), xr, _p(w), _p(res), rr if rr is not None else dense(1), _p(y), yr,
+                       _stream(stream))
+    _check("bd_linear", st)
+
+
+def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, stream=None):
+    lib = _lib.load()
+    Nq, K = wq.shape
+    Nkv = wk.shape[0]
+    st = lib.bd_qkv_proj(_dt(wq), M, K, _p(x), xr, _p(wq), Nq, _p(q), qr, _p(wk), _p(wv), Nkv, _p(k), kr, _p(v),
+                         vr, _stream(stream))
+    _check("bd_qkv_proj", st)

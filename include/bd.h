@@ -1,0 +1,221 @@
+/*
+ * bd.h -- C ABI of libbd: one block-diffusion refinement step on MI355X (gfx950).
+ *
+ * The method (Fast-dLLM v2) decodes a sequence block by block.  Inside the
+ * current block of D positions the model refines masked positions in
+ * parallel; finished blocks become read-only context in a block-level KV
+ * cache.  One refinement step is:
+ *
+ *   input rows + Q/K/V projections     bd_embed_rows, bd_qkv_proj   (support)
+ *   hybrid-mask GQA attention           bd_block_attn
+ *   output projection + residual        bd_linear                    (support)
+ *   LM head with token shift + softmax
+ *     confidence / argmax               bd_lmhead_confidence
+ *   confidence-threshold unmasking      bd_threshold_unmask
+ *   (block finished) cache append       bd_kv_append
+ *
+ * Sources, by page title and section:
+ *   [v2 notes]   "Fast-dLLM v2: Efficient Block-Diffusion LLM" (ICLR 2026 paper
+ *                notes): Framework, flowchart, Key designs 1-4.
+ *   [v1 article] "Fast-dLLM: Training-free Acceleration of Diffusion LLM by
+ *                Enabling KV Cache and Parallel Decoding" (article), Core
+ *                technique 1 (block-wise KV cache, DualCache) and 2
+ *                (confidence-aware parallel decoding).
+ *   [v2 news]    Fast-dLLM v2 news article: block structure and hierarchical
+ *                cache paragraphs.
+ *
+ * Conventions (every call):
+ *   - Tensor pointers are DEVICE pointers owned by the caller, dense row-major
+ *     in the layouts given below.  The library never allocates or frees them.
+ *   - Scratch memory, where a call needs it, is a caller-owned device
+ *     `workspace` of at least the size the matching *_workspace_size()
+ *     returns.  It must be zero-filled before its first use and may then be
+ *     reused by later calls on the same stream; it must not be shared by
+ *     calls that can run concurrently.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return at once.  Argument errors are detected on the host
+ *     before anything is launched and return BD_EINVAL (or BD_ECAPACITY /
+ *     BD_EUNSUPPORTED); nothing is written in that case.  A launch failure
+ *     returns BD_EHIP and bd_last_hip_error() gives the hipError_t.
+ *   - Empty work (B == 0, n_q == 0, M == 0, n_rows == 0) is a no-op returning
+ *     BD_OK.
+ *   - dtype selects the storage type of the floating-point tensors (fp32 or
+ *     bf16).  Accumulation is always fp32; conf, max, lse are fp32; token
+ *     ids and indices are int32.
+ *   - No exceptions cross the ABI; the only global state is the last HIP error
+ *     (thread-local).
+ */
+#ifndef BD_H
+#define BD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bd_status {
+  BD_OK = 0,
+  BD_EINVAL = 1,        /* bad argument (null pointer, shape, small workspace) */
+  BD_EUNSUPPORTED = 2,  /* valid but not implemented (e.g. head dim) */
+  BD_ECAPACITY = 3,     /* a cache append would exceed its capacity */
+  BD_EHIP = 4           /* a HIP runtime call failed */
+} bd_status;
+
+typedef enum bd_dtype { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
+
+/* Row map of a 2-D operand: logical row r lives at buffer row
+ *   (r / group) * stride + offset + (r % group).
+ * {n, n, 0} is the dense identity for an operand of n rows.  It lets one call
+ * read or write a window of rows of every sequence of a [B, R, cols] buffer:
+ * {rows_per_seq, R, first_row}.  group >= 1, stride >= 0, offset >= 0. */
+typedef struct bd_rows {
+  int32_t group;
+  int32_t stride;
+  int32_t offset;
+} bd_rows;
+
+const char* bd_version(void);
+const char* bd_status_string(bd_status s);
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int bd_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * bd_block_attn -- hybrid-mask grouped-query attention of the fresh rows of
+ * the current block ([v2 notes] Framework and Key design 2: attention is
+ * bidirectional inside a block and causal across blocks; the own block is
+ * seen whole, masked positions included; [v2 news] block structure).
+ *
+ *   q       [B, n_q, Hq, d]     queries of in-block rows q_off .. q_off+n_q-1
+ *   k_cache [B, Hkv, cap, d]    block-level cache: committed rows [0, kv_len[b])
+ *   v_cache [B, Hkv, cap, d]    ([v2 notes] Key design 3: finished blocks are
+ *                                read-only context)
+ *   kv_len  [B] int32 (device)  committed length per sequence (ragged); values
+ *                               are clamped to [0, cap]
+ *   k_blk   [B, n_blk, Hkv, d]  K/V of the in-block rows: the fresh rows of this
+ *   v_blk   [B, n_blk, Hkv, d]  step plus, in a DualCache step, the snapshot rows
+ *                               of the rest of the block ([v2 notes] Key design 3;
+ *                               [v1 article] Core technique 1).  n_blk = D for a
+ *                               refinement step, a multiple of D for a multi-block
+ *                               prefill.
+ *   o       [B, n_q, Hq, d]     output (dtype of q)
+ *   lse     [B, Hq, n_q] fp32   natural log-sum-exp of the scaled scores, or NULL
+ *
+ * Query row i (in-block row r = q_off + i, block index r / D) sees every cache
+ * row and the in-block rows c with c / D <= r / D.  Query head h reads KV head
+ * h / (Hq / Hkv).  Scores are scale * q.k.  Supported: d in {64, 128}; bf16
+ * uses MFMA, fp32 a plain VALU kernel.  Requires Hq % Hkv == 0, D >= 1,
+ * q_off + n_q <= n_blk, n_blk % D == 0.
+ * ---------------------------------------------------------------------- */
+size_t bd_block_attn_workspace_size(bd_dtype dt, int B, int Hq, int Hkv, int d, int n_q,
+                                    int cap, int n_blk);
+bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D,
+                        const void* q, int n_q, int q_off,
+                        const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
+                        const void* k_blk, const void* v_blk, int n_blk,
+                        float scale, void* o, float* lse,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bd_lmhead_confidence -- LM head with token shift and fused softmax
+ * statistics ([v2 notes] Key design 2: the prediction for a masked position i
+ * is read from the output row of position i-1; [v1 article] Core technique 2:
+ * the confidence of a position is the probability the model gives its
+ * predicted token).
+ *
+ *   h_src   [n_src, hidden]     output rows (dtype)
+ *   row_idx [M] int32 (device)  output row m uses h_src[row_idx[m]]; NULL =
+ *                               identity (M <= n_src).  The token shift is
+ *                               expressed here.  An index outside [0, n_src)
+ *                               yields argmax -1 and NaN statistics for that row.
+ *   w       [V, hidden]         LM-head weights, row-major (dtype)
+ *   argmax  [M] int32           lowest vocabulary id among the maximal logits
+ *   conf    [M] fp32            max softmax probability = exp(max - lse)
+ *   max_logit, lse [M] fp32     max logit and natural log-sum-exp (may be NULL)
+ *   logits  [M, V] fp32         debug dump of the logits, or NULL
+ *
+ * The logits are never materialised unless `logits` is given.
+ * ---------------------------------------------------------------------- */
+size_t bd_lmhead_workspace_size(bd_dtype dt, int M, int hidden, int V);
+bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V,
+                               const void* h_src, int n_src, const int32_t* row_idx,
+                               const void* w,
+                               int32_t* argmax, float* conf, float* max_logit, float* lse,
+                               float* logits,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bd_threshold_unmask -- confidence-aware parallel unmasking in the active
+ * window ([v2 notes] Key design 3; [v1 article] Core technique 2).
+ *
+ * Window = positions [win_lo, win_lo + win_len) of each sequence's block.
+ *   conf, argmax [B, win_len]   entry r predicts position win_lo + r
+ *   tokens       [B, D] int32   in/out: unmasked positions receive argmax
+ *   mask_bits    [B] uint64     in/out: bit j set <=> position j is [MASK]
+ *   n_unmasked   [B] int32      out: number unmasked in this step (may be NULL)
+ *   unmasked_pos [B, win_len]   out: unmasked positions ascending, -1 padded
+ *                               (may be NULL)
+ * Candidates are masked window positions.  Every candidate with
+ * conf > threshold is unmasked; if candidates exist and none passes, the single
+ * most confident candidate is (lowest position on ties).  threshold = 1.0 thus
+ * decodes one token per step.  Requires 1 <= D <= 64,
+ * 0 <= win_lo, win_lo + win_len <= D, win_len <= 64.
+ * ---------------------------------------------------------------------- */
+bd_status bd_threshold_unmask(int B, int D, int win_lo, int win_len,
+                              const float* conf, const int32_t* argmax, float threshold,
+                              int32_t* tokens, uint64_t* mask_bits,
+                              int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bd_kv_append -- commit a finished block to the block-level cache ([v2
+ * notes] Key design 3: a decoded block's K/V become read-only context; [v2
+ * news] hierarchical cache: reused like an autoregressive KV cache).
+ *
+ *   k_blk, v_blk [B, n_blk, Hkv, d]   rows [0, n_rows) are appended
+ *   k_cache, v_cache [B, Hkv, cap, d] rows [kv_len[b], kv_len[b] + n_rows) written
+ *   kv_len [B] int32 (device)         in/out: kv_len[b] += n_rows
+ *   kv_len_host [B] int32 or NULL     host mirror of kv_len before the call; when
+ *                                     given, overflow of cap returns BD_ECAPACITY
+ *                                     before any launch.  Without it, rows that
+ *                                     would land at or past cap are dropped.
+ * ---------------------------------------------------------------------- */
+bd_status bd_kv_append(bd_dtype dt, int B, int Hkv, int d, int cap,
+                       void* k_cache, void* v_cache, int32_t* kv_len, const int32_t* kv_len_host,
+                       const void* k_blk, const void* v_blk, int n_blk, int n_rows, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Support calls (not one of the four steps above; they complete the step).
+ * ---------------------------------------------------------------------- */
+
+/* Input rows of the block ([v2 notes] Key design 2: a masked position takes
+ * the learnable [MASK] embedding, row V of E).
+ *   E [V+1, hidden]; tokens [B, D] int32; mask_bits [B] uint64, or NULL when no
+ *   position is masked (then D may exceed 64, e.g. a multi-block prompt);
+ *   plant [B, D, hidden] or NULL: an additive offset per block row;
+ *   x [B, n_rows, hidden] out: row i of sequence b is block position row_off + i.
+ * A token id outside [0, V) on an unmasked position yields a NaN row. */
+bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
+                        const void* E, const int32_t* tokens, const uint64_t* mask_bits,
+                        const void* plant, void* x, void* stream);
+
+/* y[yr(m), n] = sum_k x[xr(m), k] * w[n, k]  (+ res[rr(m), n] when res != NULL)
+ * for m < M, n < N.  x rows hold K elements, y/res rows hold N elements;
+ * w is [N, K] row-major.  bf16 uses MFMA with fp32 accumulation. */
+bd_status bd_linear(bd_dtype dt, int M, int N, int K,
+                    const void* x, bd_rows xr, const void* w,
+                    const void* res, bd_rows rr, void* y, bd_rows yr, void* stream);
+
+/* The three input projections of one attention layer in one launch:
+ *   q[qr(m)] = x[xr(m)] Wq^T  (Nq columns), k[kr(m)] = x[xr(m)] Wk^T and
+ *   v[vr(m)] = x[xr(m)] Wv^T  (Nkv columns each). */
+bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
+                      const void* wq, int Nq, void* q, bd_rows qr,
+                      const void* wk, const void* wv, int Nkv,
+                      void* k, bd_rows kr, void* v, bd_rows vr, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BD_H */

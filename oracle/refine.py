@@ -87,7 +87,7 @@ class Model:
     @classmethod
     def from_weights(cls, w, cfg) -> "Model":
         f = lambda a: np.asarray(a, dtype=F64)
-        return cls(f(w.E), f(w.Wq), f(w.Wk), f(w.Wv), f(w.Wo), w.Wlm, cfg.Hq, cfg.Hkv, cfg.d)
+        return cls(f(w.E), f(w.Wq), f(w.Wk), f(w.Wv), f(w.Wo), f(w.Wlm), cfg.Hq, cfg.Hkv, cfg.d)
 
 
 def kv_head(h: int, G: int) -> int:
@@ -163,7 +163,8 @@ def output(model: Model, X: np.ndarray, O: np.ndarray) -> np.ndarray:
 
 
 def lm_logits(Wlm: np.ndarray, h: np.ndarray) -> np.ndarray:
-    """logits = h Wlm^T in float64; Wlm rows are lifted to float64 in chunks."""
+    """logits = h Wlm^T in float64 (Wlm rows lifted to float64 chunk by chunk
+    when they are stored in a narrower type)."""
     h = np.atleast_2d(np.asarray(h, dtype=F64))
     out = np.empty((h.shape[0], Wlm.shape[0]), dtype=F64)
     for v0 in range(0, Wlm.shape[0], _VCHUNK):

@@ -1,0 +1,135 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, build the driver
+and the oracle from the same draws, and the tolerance rules.
+
+Tolerances (per element type): 1e-3 relative for fp32, 2e-2 for bf16.
+* rows (attention outputs, hidden rows, logits): per row
+  |d|_2 / |ref|_2 <= rtol and every element |d| <= rtol * (|ref| + RMS(row));
+* max / lse: |d| <= rtol * max(1, RMS(logits row)); conf: |d| / conf <= rtol;
+* argmax: exact unless the oracle's top-2 gap <= rtol * max(|l1|, RMS(row));
+* unmask sets: exact except positions whose oracle confidence is within 1e-3
+  of the threshold; a fallback pick is compared only when the best two
+  candidate confidences differ by more than rtol * conf.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import bd_inputs as bi
+from oracle import refine as R
+
+DEV = "cuda"
+TOL = {"f32": 1e-3, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tdt(dtype: str):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def up(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(DEV) if dtype is None else t.to(DEV, dtype)
+
+
+def down(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rows_close(got, ref, rtol, what=""):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64).reshape(ref.shape)
+    g2 = got.reshape(-1, ref.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    d = g2 - r2
+    rn = np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r2, axis=1), 1e-30)
+    rms = np.sqrt((r2 ** 2).mean(axis=1, keepdims=True))
+    bad = np.abs(d) > rtol * (np.abs(r2) + rms)
+    assert np.isfinite(g2).all(), f"{what}: non-finite output"
+    assert rn.max() <= rtol and not bad.any(), \
+        f"{what}: max row rel err {rn.max():.3g} (rtol {rtol}), {bad.sum()} elements out of tolerance"
+    return float(rn.max())
+
+
+def lm_stats_close(argmax, conf, mx, lse, ref_logits, rtol, what=""):
+    """GPU (argmax, conf, max, lse) of each row against fp64 logits."""
+    ref_logits = np.atleast_2d(ref_logits)
+    am, rmx, rlse, rconf = R.confidence(ref_logits)
+    rms = np.sqrt((ref_logits ** 2).mean(axis=1))
+    tol = rtol * np.maximum(1.0, rms)
+    if mx is not None:
+        assert np.all(np.abs(mx - rmx) <= tol), f"{what}: max logit"
+    if lse is not None:
+        assert np.all(np.abs(lse - rlse) <= tol), f"{what}: lse"
+    assert np.all(np.abs(conf - rconf) <= rtol * rconf), \
+        f"{what}: conf max rel err {np.max(np.abs(conf - rconf) / rconf):.3g}"
+    top2 = np.sort(ref_logits, axis=1)[:, -2:]
+    gap = top2[:, 1] - top2[:, 0]
+    exempt = gap <= rtol * np.maximum(np.abs(top2[:, 1]), rms)
+    ok = (argmax == am) | exempt
+    assert ok.all(), f"{what}: argmax differs on rows {np.nonzero(~ok)[0][:10]}"
+    # an exempt row must still pick a token whose logit ties the maximum within tolerance
+    for m in np.nonzero(exempt & (argmax != am))[0]:
+        assert 0 <= argmax[m] < ref_logits.shape[1]
+        assert rmx[m] - ref_logits[m, argmax[m]] <= rtol * max(abs(rmx[m]), rms[m])
+    return int(exempt.sum())
+
+
+def unmask_close(got_masked, ref_masked, before_masked, ref_conf_win, win_lo, tau, rtol, what=""):
+    """Compare unmask decisions of one window (bool arrays [B, D])."""
+    B, D = ref_masked.shape
+    for b in range(B):
+        W = len(ref_conf_win[b])
+        cand = [r for r in range(W) if before_masked[b, win_lo + r]]
+        conf = np.asarray(ref_conf_win[b])
+        near = {r for r in cand if abs(conf[r] - tau) <= 1e-3}
+        passing = [r for r in cand if conf[r] > tau]
+        fallback_tie = False
+        if not passing and len(cand) >= 2:
+            cs = sorted((conf[r] for r in cand), reverse=True)
+            fallback_tie = cs[0] - cs[1] <= rtol * cs[0]
+        for r in range(W):
+            if r in near or (fallback_tie and not passing):
+                continue
+            j = win_lo + r
+            assert got_masked[b, j] == ref_masked[b, j], f"{what}: seq {b} position {j} unmask decision differs"
+        # outside the window nothing changes
+        outside = np.ones(D, bool)
+        outside[win_lo:win_lo + W] = False
+        assert np.array_equal(got_masked[b, outside], before_masked[b, outside])
+
+
+# --------------------------------------------------------------------------
+def workload(cfg, seed=0, window=0, S=None, n_masked=None, all_masked=False, plant_rate=None):
+    w = bi.make_weights(cfg, seed)
+    pre = bi.make_prefix(cfg, seed)
+    st = bi.make_block_state(cfg, seed, window, S=S, n_masked=n_masked, all_masked=all_masked)
+    plant = carry_plant = None
+    if plant_rate is not None:
+        plant, carry_plant, _ = bi.make_plants(cfg, seed, w, st, plant_rate)
+    return w, pre, st, plant, carry_plant
+
+
+def gpu_decoder(cfg, w, pre, st, plant=None, carry_plant=None):
+    from block_diffusion_decoding_amd.decoder import BlockDecoder, Dims
+    dims = Dims(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.hidden, cfg.V, cfg.D, cfg.cap)
+    weights = {k: torch.from_numpy(getattr(w, k)) for k in ("E", "Wq", "Wk", "Wv", "Wo", "Wlm")}
+    dec = BlockDecoder(dims, weights, dtype=tdt(cfg.dtype), device=DEV)
+    if pre.kind == "prefill":
+        dec.prefill(pre.prompt)
+        for blk in range(pre.committed.shape[1] // cfg.D):
+            dec.set_block(pre.committed[:, blk * cfg.D:(blk + 1) * cfg.D], np.zeros((cfg.B, cfg.D), bool))
+            dec.commit()
+    else:
+        dec.set_synthetic_prefix(pre.kv_len, pre.cache_k, pre.cache_v, pre.carry)
+    dec.set_block(st.tokens, st.masked, plant, carry_offset=carry_plant)
+    return dec
+
+
+def oracle_seqs(cfg, w, pre, st, plant=None, carry_plant=None):
+    m = R.Model.from_weights(w, cfg)
+    return m, R.seqs_from_inputs(m, cfg, pre, st, plant, carry_plant)

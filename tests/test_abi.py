@@ -1,0 +1,143 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/bd.h declares, and rejects bad arguments on the host before any
+launch (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from block_diffusion_decoding_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libbd.so not built")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(bd_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_four_calls_and_support():
+    names = declared_functions()
+    for n in ["bd_block_attn", "bd_lmhead_confidence", "bd_threshold_unmask", "bd_kv_append",
+              "bd_embed_rows", "bd_linear", "bd_qkv_proj", "bd_block_attn_workspace_size",
+              "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) <= set(_lib.SIGNATURES), "binding lacks a signature"
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (bd_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.bd_version().startswith(b"libbd")
+    for s in range(5):
+        assert lib.bd_status_string(s)
+    assert lib.bd_last_hip_error() == 0
+
+
+FAKE = 0x100000  # 16-byte aligned fake device address; never dereferenced
+
+
+def attn(lib, **kw):
+    a = dict(dt=1, B=1, Hq=4, Hkv=2, d=128, D=32, q=FAKE, n_q=8, q_off=8, kc=FAKE, vc=FAKE, kv_len=FAKE,
+             cap=64, kb=FAKE, vb=FAKE, n_blk=32, scale=0.1, o=FAKE, lse=None, ws=FAKE, wsb=1 << 30, s=None)
+    a.update(kw)
+    return lib.bd_block_attn(a["dt"], a["B"], a["Hq"], a["Hkv"], a["d"], a["D"], a["q"], a["n_q"], a["q_off"],
+                             a["kc"], a["vc"], a["kv_len"], a["cap"], a["kb"], a["vb"], a["n_blk"], a["scale"],
+                             a["o"], a["lse"], a["ws"], a["wsb"], a["s"])
+
+
+def test_attn_argument_errors():
+    lib = _lib.load()
+    E, U = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED
+    assert attn(lib, B=0) == 0 and attn(lib, n_q=0) == 0          # empty work: no-op
+    assert attn(lib, Hkv=3) == E                                     # Hq % Hkv
+    assert attn(lib, q_off=30) == E                                  # q_off + n_q > n_blk
+    assert attn(lib, n_blk=48) == E                                  # n_blk % D
+    assert attn(lib, D=0) == E
+    assert attn(lib, d=96) == U
+    assert attn(lib, q=None) == E
+    assert attn(lib, q=FAKE + 2) == E                                # misaligned
+    assert attn(lib, dt=7) == E
+    assert attn(lib, scale=float("nan")) == E
+    need = lib.bd_block_attn_workspace_size(1, 32, 28, 4, 128, 8, 16416, 32)
+    assert need > 0
+    assert attn(lib, B=32, Hq=28, Hkv=4, n_q=8, cap=16416, wsb=need - 1) == E
+    assert lib.bd_block_attn_workspace_size(0, 1, 4, 2, 64, 8, 64, 32) == 0   # fp32: no workspace
+
+
+def test_lmhead_unmask_append_argument_errors():
+    lib = _lib.load()
+    E, U, C = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED, _lib.BD_ECAPACITY
+    ws = lib.bd_lmhead_workspace_size(1, 64, 3584, 152064)
+    assert ws >= 64 * 1188 * 12
+    lm = lambda **k: lib.bd_lmhead_confidence(k.get("dt", 1), k.get("M", 8), k.get("hidden", 1536), 151936,
+                                              FAKE, k.get("n_src", 9), k.get("ri", FAKE), FAKE, FAKE, FAKE,
+                                              None, None, None, FAKE, k.get("wsb", 1 << 30), None)
+    assert lm(M=0) == 0
+    assert lm(hidden=1000) == U
+    assert lm(ri=None, n_src=4) == E
+    assert lm(wsb=16) == E
+    um = lambda **k: lib.bd_threshold_unmask(1, k.get("D", 32), k.get("lo", 8), k.get("wl", 8), FAKE, FAKE,
+                                             k.get("t", 0.9), FAKE, FAKE, None, None, None)
+    assert um(D=65) == E and um(lo=30) == E and um(wl=0) == E and um(t=float("nan")) == E
+    h = np.array([16400, 16384], dtype=np.int32)
+    ap = lambda host, n=32, cap=16416: lib.bd_kv_append(1, 2, 4, 128, cap, FAKE, FAKE, FAKE, host,
+                                                        FAKE, FAKE, 32, n, None)
+    assert ap(h.ctypes.data) == C
+    assert ap(None, n=33) == E                                        # n_rows > n_blk
+    assert ap(h.ctypes.data, n=0) == 0
+
+
+def test_gemm_and_embed_argument_errors():
+    lib = _lib.load()
+    E, U = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED
+    R = _lib.BdRows
+    assert lib.bd_linear(1, 64, 3584, 3584, FAKE, R(64, 64, 0), FAKE, None, R(1, 1, 0), FAKE, R(0, 1, 0),
+                         None) == E                                    # group 0
+    assert lib.bd_linear(1, 64, 3584, 1000, FAKE, R(64, 64, 0), FAKE, None, R(1, 1, 0), FAKE, R(64, 64, 0),
+                         None) == U                                    # K % 256
+    assert lib.bd_linear(1, 0, 3584, 3584, FAKE, R(1, 1, 0), FAKE, None, R(1, 1, 0), FAKE, R(1, 1, 0),
+                         None) == 0
+    assert lib.bd_embed_rows(1, 1, 65, 0, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
+    assert lib.bd_embed_rows(1, 1, 32, 30, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
+
+
+def test_launch_without_gpu_reports_hip_error():
+    """With no GPU present a valid call returns BD_EHIP instead of crashing
+    (run in a child process so the HIP runtime state stays out of pytest)."""
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import torch
+if torch.cuda.device_count() != 0:
+    print("visible-gpu"); sys.exit(0)
+from block_diffusion_decoding_amd import _lib
+lib = _lib.load()
+st = lib.bd_threshold_unmask(1, 32, 0, 8, 0x100000, 0x100000, 0.9, 0x100000, 0x100000, None, None, None)
+print(st, lib.bd_last_hip_error())
+""" % ROOT
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, env=env)
+    if r.returncode != 0:
+        pytest.skip(f"child exited {r.returncode}: {r.stderr[-300:]}")
+    if "visible-gpu" in r.stdout:
+        pytest.skip("a GPU is visible; this check is for hosts without one")
+    st, err = map(int, r.stdout.split()[-2:])
+    assert st == _lib.BD_EHIP and err != 0

@@ -1,0 +1,231 @@
+"""GPU parity of each libbd call against the fp64 oracle on seeded inputs
+(bd_block_attn, bd_lmhead_confidence, bd_threshold_unmask, bd_kv_append and
+the support calls).  Sizes span several tiles and ragged tails; the largest
+cases run at the full 7B long-context shape on sampled sequences."""
+import numpy as np
+import pytest
+import torch
+
+import bd_inputs as bi
+from gpu_util import DEV, TOL, down, lm_stats_close, rows_close, say, tdt, up
+from oracle import refine as R
+
+pytestmark = pytest.mark.gpu
+
+
+def ops():
+    from block_diffusion_decoding_amd import ops as o
+    return o
+
+
+# --------------------------------------------------------------------------
+# bd_block_attn
+# --------------------------------------------------------------------------
+ATTN_CASES = {
+    # name: (dtype, B, Hq, Hkv, d, D, n_q, q_off, lens, n_blk, std_qk, sample_b)
+    "f32-tiny-dc": ("f32", 1, 4, 2, 64, 32, 8, 8, [64], 32, 0.02, None),
+    "f32-tiny-exact-96": ("f32", 1, 4, 2, 64, 32, 32, 0, [96], 32, 0.02, None),
+    "f32-prefill-2blk": ("f32", 2, 4, 2, 64, 32, 64, 0, [0, 0], 64, 1.0, None),
+    "bf16-1.5B-dc": ("bf16", 1, 12, 2, 128, 32, 8, 8, [2048], 32, 0.02, None),
+    "bf16-1.5B-exact": ("bf16", 1, 12, 2, 128, 32, 32, 0, [2048], 32, 0.02, None),
+    "bf16-7B-dc-ragged": ("bf16", 8, 28, 4, 128, 32, 8, 16, "c3", 32, 0.02, None),
+    "bf16-7B-exact-ragged": ("bf16", 8, 28, 4, 128, 32, 32, 0, "c3", 32, 0.02, None),
+    "bf16-ragged-tail": ("bf16", 4, 28, 4, 128, 32, 8, 24, [0, 1000, 77, 4097], 32, 0.02, None),
+    "bf16-sharp": ("bf16", 2, 12, 2, 128, 32, 8, 0, [3000, 1500], 32, 1.0, None),
+    "bf16-prefill-4blk": ("bf16", 2, 12, 2, 128, 32, 128, 0, [0, 0], 128, 1.0, None),
+    "bf16-d64": ("bf16", 2, 8, 2, 64, 32, 8, 8, [700, 1300], 32, 0.5, None),
+    "bf16-7B-long-dc": ("bf16", 32, 28, 4, 128, 32, 8, 8, [16384] * 32, 32, 0.02, [0, 13, 31]),
+    "bf16-7B-long-exact": ("bf16", 32, 28, 4, 128, 32, 32, 0, [16384] * 32, 32, 0.02, [5, 30]),
+}
+
+
+@pytest.mark.parametrize("name", list(ATTN_CASES))
+def test_block_attn(name):
+    dt, B, Hq, Hkv, d, D, n_q, q_off, lens, n_blk, sd, sample = ATTN_CASES[name]
+    say(f"[attn] {name}")
+    seed = 3
+    if lens == "c3":
+        lens = \
+            list((np.random.default_rng(7).integers(32, 129, size=B) * 32).astype(int))
+    lens = np.array(lens, dtype=np.int32)
+    cap = int(max(lens.max(), 1) + 64)
+    kc = bi.normal(seed, "cache_k", (B, Hkv, cap, d), sd, dt)
+    vc = bi.normal(seed, "cache_v", (B, Hkv, cap, d), 0.02 if sd < 1 else 1.0, dt)
+    q = bi.normal(seed, "q", (B, n_q, Hq, d), sd, dt)
+    kb = bi.normal(seed, "blk_k", (B, n_blk, Hkv, d), sd, dt)
+    vb = bi.normal(seed, "blk_v", (B, n_blk, Hkv, d), 0.02 if sd < 1 else 1.0, dt)
+    T = tdt(dt)
+    o = torch.zeros(B, n_q, Hq, d, dtype=T, device=DEV)
+    lse = torch.zeros(B, Hq, n_q, dtype=torch.float32, device=DEV)
+    ops().bd_block_attn(up(q, T), up(kc, T), up(vc, T), up(lens), up(kb, T), up(vb, T), o, D=D, q_off=q_off,
+                        lse=lse)
+    torch.cuda.synchronize()
+    bs = list(range(B)) if sample is None else sample
+    ro, rlse = R.block_attn(q[bs], kc[bs], vc[bs], lens[bs], kb[bs], vb[bs], q_off, D)
+    err = rows_close(down(o)[bs], ro, TOL[dt], f"attn {name}")
+    g_lse = down(lse)[bs]
+    assert np.all(np.abs(g_lse - rlse) <= TOL[dt] * np.maximum(1.0, np.abs(rlse))), f"lse {name}"
+    say(f"    max row rel err {err:.2e}")
+
+
+def test_block_attn_is_deterministic_and_order_free():
+    """Two runs are bitwise identical; permuting the committed rows changes the
+    result only within rounding."""
+    B, Hq, Hkv, d, L = 2, 28, 4, 128, 5000
+    kc = bi.normal(9, "cache_k", (B, Hkv, L, d), 0.3, "bf16")
+    vc = bi.normal(9, "cache_v", (B, Hkv, L, d), 0.3, "bf16")
+    q = bi.normal(9, "q", (B, 8, Hq, d), 0.3, "bf16")
+    kb = bi.normal(9, "blk_k", (B, 32, Hkv, d), 0.3, "bf16")
+    vb = bi.normal(9, "blk_v", (B, 32, Hkv, d), 0.3, "bf16")
+    T = torch.bfloat16
+    lens = up(np.array([L, L - 321], dtype=np.int32))
+    args = [up(q, T), up(kc, T), up(vc, T), lens, up(kb, T), up(vb, T)]
+    o1 = torch.zeros(B, 8, Hq, d, dtype=T, device=DEV)
+    o2 = torch.zeros_like(o1)
+    ops().bd_block_attn(*args, o1, D=32, q_off=8)
+    ops().bd_block_attn(*args, o2, D=32, q_off=8)
+    assert torch.equal(o1, o2)
+    perm = np.random.default_rng(1).permutation(L - 321)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[1, :, :L - 321] = kc[1, :, perm].transpose(1, 0, 2)
+    vc2[1, :, :L - 321] = vc[1, :, perm].transpose(1, 0, 2)
+    o3 = torch.zeros_like(o1)
+    ops().bd_block_attn(args[0], up(kc2, T), up(vc2, T), lens, args[4], args[5], o3, D=32, q_off=8)
+    rows_close(down(o3), down(o1), TOL["bf16"], "permuted keys")
+
+
+# --------------------------------------------------------------------------
+# bd_lmhead_confidence
+# --------------------------------------------------------------------------
+LM_CASES = {
+    # name: (dtype, M, n_src, hidden, V, w scale, h scale, logits dump)
+    "f32-tiny": ("f32", 24, 40, 256, 1024, 1666.0, 1.0, True),
+    "bf16-1.5B-M8": ("bf16", 8, 9, 1536, 151936, 1.0, 1.0, True),
+    "bf16-7B-M64": ("bf16", 64, 72, 3584, 152064, 1.0, 1.0, False),
+    "bf16-7B-M1": ("bf16", 1, 3, 3584, 152064, 1.0, 1.0, False),
+    "bf16-7B-M17-sharp": ("bf16", 17, 20, 3584, 152064, 1.0, 60.0, False),
+    "bf16-7B-M100": ("bf16", 100, 128, 3584, 152064, 1.0, 1.0, False),
+    "bf16-ragged-vocab": ("bf16", 33, 40, 512, 1000, 1.0, 30.0, True),
+}
+
+
+@pytest.mark.parametrize("name", list(LM_CASES))
+def test_lmhead_confidence(name):
+    dt, M, n_src, hidden, V, ws_, hs, dump = LM_CASES[name]
+    say(f"[lmhead] {name}")
+    w = bi.normal(1, "Wlm", (V, hidden), 0.02 * ws_, dt)
+    h = bi.normal(1, "h", (n_src, hidden), 0.02 * hs, dt)
+    ridx = np.random.default_rng(M).integers(0, n_src, size=M).astype(np.int32)
+    T = tdt(dt)
+    am = torch.zeros(M, dtype=torch.int32, device=DEV)
+    conf, mx, lse = (torch.zeros(M, dtype=torch.float32, device=DEV) for _ in range(3))
+    lg = torch.zeros(M, V, dtype=torch.float32, device=DEV) if dump else None
+    ops().bd_lmhead_confidence(up(h, T), up(ridx), up(w, T), am, conf, max_logit=mx, lse=lse, logits=lg)
+    torch.cuda.synchronize()
+    ref = R.lm_logits(w, h[ridx])
+    if dump:
+        rows_close(down(lg), ref, TOL[dt], f"logits {name}")
+    ex = lm_stats_close(am.cpu().numpy(), down(conf), down(mx), down(lse), ref, TOL[dt], name)
+    say(f"    exempt argmax rows: {ex}")
+
+
+def test_lmhead_invalid_row_index():
+    V, hidden = 512, 256
+    w = bi.normal(2, "Wlm", (V, hidden), 0.02, "bf16")
+    h = bi.normal(2, "h", (4, hidden), 0.02, "bf16")
+    ridx = np.array([0, 7, -1, 3], dtype=np.int32)
+    am = torch.zeros(4, dtype=torch.int32, device=DEV)
+    conf = torch.zeros(4, dtype=torch.float32, device=DEV)
+    ops().bd_lmhead_confidence(up(h, torch.bfloat16), up(ridx), up(w, torch.bfloat16), am, conf)
+    a, c = am.cpu().numpy(), conf.cpu().numpy()
+    assert a[1] == -1 and a[2] == -1 and np.isnan(c[1]) and np.isnan(c[2])
+    assert a[0] >= 0 and a[3] >= 0 and np.isfinite(c[[0, 3]]).all()
+
+
+# --------------------------------------------------------------------------
+# bd_threshold_unmask (bit-exact)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("D,S,win", [(32, 8, 0), (32, 8, 3), (32, 32, 0), (64, 8, 7), (64, 64, 0), (8, 4, 1)])
+@pytest.mark.parametrize("tau", [0.9, 1.0, 0.3])
+def test_threshold_unmask(D, S, win, tau):
+    say(f"[unmask] D={D} S={S} win={win} tau={tau}")
+    B = 37
+    rng = np.random.default_rng(D * 100 + S + win)
+    conf = rng.choice(np.array([0.05, 0.3, 0.9, 0.95, 0.99], np.float32), size=(B, S)).astype(np.float32)
+    conf[::5] = rng.random((len(conf[::5]), S)).astype(np.float32)
+    conf[3, :] = 0.9                       # exact threshold ties
+    am = rng.integers(0, 150000, size=(B, S)).astype(np.int32)
+    masked = rng.random((B, D)) < 0.5
+    masked[7, :] = False                   # no candidates
+    masked[8, :] = True
+    tokens = np.where(masked, 0, rng.integers(0, 150000, size=(B, D))).astype(np.int32)
+    t_tok, t_bits = up(tokens), up(bi.mask_bits(masked).view(np.int64))
+    n = torch.zeros(B, dtype=torch.int32, device=DEV)
+    pos = torch.zeros(B, S, dtype=torch.int32, device=DEV)
+    ops().bd_threshold_unmask(up(conf), up(am), t_tok, t_bits, win_lo=win * S, threshold=tau,
+                              n_unmasked=n, unmasked_pos=pos)
+    rt, rm, rn, rp = R.batch_threshold_unmask(conf, am, tokens, masked, win * S, np.float32(tau))
+    assert np.array_equal(t_tok.cpu().numpy(), rt)
+    assert np.array_equal(bi.bits_to_mask(t_bits.cpu().numpy().view(np.uint64), D), rm)
+    assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(pos.cpu().numpy(), rp)
+
+
+# --------------------------------------------------------------------------
+# bd_kv_append (bit-exact) and capacity
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_kv_append(dt):
+    say(f"[append] {dt}")
+    B, Hkv, d, cap, n_blk = 5, 4, 128, 300, 32
+    T = tdt(dt)
+    kc = bi.normal(4, "cache_k", (B, Hkv, cap, d), 0.02, dt)
+    vc = bi.normal(4, "cache_v", (B, Hkv, cap, d), 0.02, dt)
+    kb = bi.normal(4, "blk_k", (B, n_blk, Hkv, d), 0.02, dt)
+    vb = bi.normal(4, "blk_v", (B, n_blk, Hkv, d), 0.02, dt)
+    lens = np.array([0, 32, 100, 268, 7], dtype=np.int32)
+    gk, gv, gl = up(kc, T), up(vc, T), up(lens)
+    ops().bd_kv_append(gk, gv, gl, up(kb, T), up(vb, T), n_rows=32, kv_len_host=lens)
+    rk, rv, rl = R.kv_append(kc, vc, lens, kb, vb, 32)
+    assert np.array_equal(down(gk), rk) and np.array_equal(down(gv), rv)
+    assert np.array_equal(gl.cpu().numpy(), rl)
+    with pytest.raises(Exception):
+        ops().bd_kv_append(gk, gv, gl, up(kb, T), up(vb, T), n_rows=32, kv_len_host=rl)
+
+
+# --------------------------------------------------------------------------
+# support calls: input rows and projections
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [bi.C1, bi.C2], ids=["tiny-f32", "1.5B-bf16"])
+def test_embed_and_projections(cfg):
+    say(f"[support] {cfg.name}")
+    w = bi.make_weights(cfg, 5)
+    m = R.Model.from_weights(w, cfg)
+    st = bi.make_block_state(cfg, 5, 1, n_masked=4)
+    B, D, S = cfg.B, cfg.D, cfg.S
+    plant = bi.normal(5, "plant", (B, D, cfg.hidden), 0.05, cfg.dtype)
+    T = tdt(cfg.dtype)
+    o = ops()
+    E = up(w.E, T)
+    X = torch.zeros(B, S, cfg.hidden, dtype=T, device=DEV)
+    o.bd_embed_rows(E, up(st.tokens), up(bi.mask_bits(st.masked).view(np.int64)), X, row_off=S, n_rows=S,
+                    plant=up(plant, T))
+    rX = np.stack([R.embed(m, st.tokens[b, S:2 * S], st.masked[b, S:2 * S], plant[b, S:2 * S]) for b in range(B)])
+    rows_close(down(X), rX, TOL[cfg.dtype], "embed")
+    # projections from the GPU's own X rows (so only the GEMMs are compared)
+    Xh = down(X).reshape(B * S, cfg.hidden)
+    q = torch.zeros(B, S, cfg.Hq * cfg.d, dtype=T, device=DEV)
+    kb = torch.zeros(B, D, cfg.Hkv * cfg.d, dtype=T, device=DEV)
+    vb = torch.zeros_like(kb)
+    kr = o.rows(S, D, S)
+    o.bd_qkv_proj(X, o.dense(B * S), up(w.Wq, T), q, o.dense(B * S), up(w.Wk, T), up(w.Wv, T), kb, kr, vb, kr,
+                  M=B * S)
+    Q, K, V = R.project(m, Xh)
+    rows_close(down(q).reshape(B * S, -1), Q.reshape(B * S, -1), TOL[cfg.dtype], "q proj")
+    rows_close(down(kb)[:, S:2 * S].reshape(B * S, -1), K.reshape(B * S, -1), TOL[cfg.dtype], "k proj")
+    rows_close(down(vb)[:, S:2 * S].reshape(B * S, -1), V.reshape(B * S, -1), TOL[cfg.dtype], "v proj")
+    assert float(kb[:, :S].abs().max()) == 0.0 and float(kb[:, 2 * S:].abs().max()) == 0.0
+    # output projection + residual into rows 1 + S .. of a [B, 1 + D, hidden] buffer
+    H = torch.zeros(B, 1 + D, cfg.hidden, dtype=T, device=DEV)
+    o.bd_linear(q, o.dense(B * S), up(w.Wo, T), H, o.rows(S, 1 + D, 1 + S), M=B * S, res=X, rr=o.dense(B * S))
+    rH = R.output(m, Xh, down(q).reshape(B * S, cfg.Hq, cfg.d))
+    rows_close(down(H)[:, 1 + S:1 + 2 * S].reshape(B * S, -1), rH, TOL[cfg.dtype], "o proj")

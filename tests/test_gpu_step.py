@@ -1,0 +1,134 @@
+"""GPU parity of whole refinement steps and block loops (driver + all calls)
+against the fp64 oracle on the same seeded inputs.
+
+Multi-step comparisons use teacher forcing: after every step the GPU state is
+set to the oracle's unmask decisions, so exempt ties cannot make the two
+sides drift apart."""
+import numpy as np
+import pytest
+import torch
+
+import bd_inputs as bi
+from gpu_util import (TOL, down, gpu_decoder, lm_stats_close, oracle_seqs, rows_close, say, unmask_close,
+                      workload)
+from oracle import refine as R
+
+pytestmark = pytest.mark.gpu
+
+
+def compare_step(cfg, dec, m, seqs, results, kind, s, S, before_masked, what):
+    rtol = TOL[cfg.dtype]
+    B, D = cfg.B, cfg.D
+    w = dec.last
+    # output rows of this step
+    H = down(dec.H)
+    for b, r in enumerate(results):
+        rows = r.rows
+        rows_close(H[b, 1 + rows], r.H, rtol, f"{what} H seq {b}")
+    # LM-head statistics of the window rows
+    src = np.concatenate([r.src for r in results])
+    ref_logits = R.lm_logits(m.Wlm, src)
+    lm_stats_close(w["argmax"].cpu().numpy().reshape(-1), down(w["conf"]).reshape(-1),
+                   down(w["maxl"]).reshape(-1), down(w["lse"]).reshape(-1), ref_logits, rtol, f"{what} lm")
+    # unmask decisions
+    ref_masked = np.stack([q.masked for q in seqs])
+    unmask_close(dec.masked_host(), ref_masked, before_masked, [r.conf for r in results], s * S, cfg.tau, rtol,
+                 f"{what} unmask")
+    return [len(r.picked) for r in results]
+
+
+def force(dec, seqs):
+    dec.set_tokens(np.stack([q.tokens for q in seqs]), np.stack([q.masked for q in seqs]))
+
+
+@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96], ids=["tiny-64", "tiny-96"])
+def test_tiny_prefill_and_commit_equal_oracle_cache(cfg):
+    say(f"[step] prefill+commit {cfg.name}")
+    w, pre, st, _, _ = workload(cfg, 0, all_masked=True)
+    dec = gpu_decoder(cfg, w, pre, st)
+    m, seqs = oracle_seqs(cfg, w, pre, st)
+    for b, q in enumerate(seqs):
+        L = q.L
+        assert int(dec.kv_len[b]) == L
+        rows_close(down(dec.cache_k)[b, :, :L].transpose(1, 0, 2).reshape(L, -1), q.cache_k.reshape(L, -1),
+                   TOL[cfg.dtype], "cache k")
+        rows_close(down(dec.cache_v)[b, :, :L].transpose(1, 0, 2).reshape(L, -1), q.cache_v.reshape(L, -1),
+                   TOL[cfg.dtype], "cache v")
+        rows_close(down(dec.H)[b, 0], q.carry, TOL[cfg.dtype], "carry")
+
+
+@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96], ids=["tiny-64", "tiny-96"])
+@pytest.mark.parametrize("mode", ["exact", "dual"])
+def test_tiny_block_decode_teacher_forced(cfg, mode):
+    say(f"[step] tiny block loop {cfg.name} {mode}")
+    w, pre, st, _, _ = workload(cfg, 0, all_masked=True)
+    dec = gpu_decoder(cfg, w, pre, st)
+    m, seqs = oracle_seqs(cfg, w, pre, st)
+    D, S, tau = cfg.D, cfg.S, cfg.tau
+    n_steps, passes = 0, []
+    for s in range(D // S):
+        first = True
+        while any(q.masked[s * S:(s + 1) * S].any() for q in seqs):
+            kind = "E" if (first or mode == "exact") else "DC"
+            before = np.stack([q.masked for q in seqs])
+            res = [(R.e_step if kind == "E" else R.dc_step)(m, q, s, S, tau, D) for q in seqs]
+            (dec.e_step if kind == "E" else dec.dc_step)(s, S, tau)
+            passes += compare_step(cfg, dec, m, seqs, res, kind, s, S, before, f"{mode} step {n_steps} {kind}")
+            force(dec, seqs)
+            first = False
+            n_steps += 1
+    for q in seqs:
+        R.commit(m, q, D)
+    dec.commit()
+    for b, q in enumerate(seqs):
+        L = q.L
+        assert int(dec.kv_len[b]) == L
+        rows_close(down(dec.cache_k)[b, :, L - D:L].transpose(1, 0, 2).reshape(D, -1),
+                   q.cache_k[L - D:].reshape(D, -1), TOL[cfg.dtype], "appended k")
+        rows_close(down(dec.cache_v)[b, :, L - D:L].transpose(1, 0, 2).reshape(D, -1),
+                   q.cache_v[L - D:].reshape(D, -1), TOL[cfg.dtype], "appended v")
+        rows_close(down(dec.H)[b, 0], q.carry, TOL[cfg.dtype], "carry after commit")
+    say(f"    {n_steps} steps, tokens per step {passes}")
+    assert n_steps >= D // S and sum(passes) == cfg.B * D
+
+
+@pytest.mark.parametrize("cfg,rate", [(bi.C2, None), (bi.C3, 0.5), (bi.C3, 1.0)], ids=["1.5B", "7B-r0.5", "7B-r1"])
+def test_refresh_then_dualcache_steps(cfg, rate):
+    """Window 1: exact refresh step, then two DualCache steps (the second after
+    the first one's unmasking), against the oracle."""
+    say(f"[step] {cfg.name} rate={rate}")
+    w, pre, st, plant, carry_plant = workload(cfg, 0, window=1, plant_rate=rate)
+    dec = gpu_decoder(cfg, w, pre, st, plant, carry_plant)
+    m, seqs = oracle_seqs(cfg, w, pre, st, plant, carry_plant)
+    S, D, tau, s = cfg.S, cfg.D, cfg.tau, 1
+    tokens_per_step = []
+    n_cand0 = int(sum(q.masked[s * S:(s + 1) * S].sum() for q in seqs))
+    for k, kind in enumerate(["E", "DC", "DC"]):
+        if not any(q.masked[s * S:(s + 1) * S].any() for q in seqs):
+            break
+        before = np.stack([q.masked for q in seqs])
+        res = [(R.e_step if kind == "E" else R.dc_step)(m, q, s, S, tau, D) for q in seqs]
+        (dec.e_step if kind == "E" else dec.dc_step)(s, S, tau)
+        tokens_per_step.append(sum(compare_step(cfg, dec, m, seqs, res, kind, s, S, before, f"{cfg.name} {kind}{k}")))
+        force(dec, seqs)
+    say(f"    tokens unmasked per step {tokens_per_step}")
+    if rate == 1.0:                 # every candidate planted: all pass in the first step
+        assert tokens_per_step[0] == n_cand0
+
+
+def test_fixed_schedule_block_matches_oracle_loop():
+    """Fixed 8 steps per window (1 exact + 7 DualCache, no host sync) on a
+    fresh block gives the oracle's loop result: every step unmasks at least
+    one token, so 8 steps finish a window of 8."""
+    cfg = bi.C1
+    say("[step] fixed schedule")
+    w, pre, st, _, _ = workload(cfg, 1, all_masked=True)
+    dec = gpu_decoder(cfg, w, pre, st)
+    m, seqs = oracle_seqs(cfg, w, pre, st)
+    R.decode_block(m, seqs, cfg.D, cfg.S, 1.0, mode="dual")
+    dec.decode_block(cfg.S, 1.0, mode="dual", steps_per_window=cfg.S)
+    torch.cuda.synchronize()
+    got = dec.tokens.cpu().numpy()
+    ref = np.stack([q.tokens for q in seqs])
+    assert np.array_equal(got, ref)
+    assert int(dec.mask_bits[0]) == 0 and int(dec.kv_len[0]) == seqs[0].L
