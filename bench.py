@@ -1,0 +1,350 @@
+"""Benchmark of the block-diffusion refinement step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rate 0.5]
+
+Headline workload (7B shape): Qwen2.5-7B-shaped attention layer (28 query /
+4 KV heads of dim 128, hidden 3584) + LM head 3584 x 152064, bf16, batch 8
+with committed prefixes drawn uniformly from 1024..4096 tokens (block
+aligned), block 32, sub-block 8, threshold 0.9, planted peaked logits for a
+fraction `rate` of the masked rows.  The timed loop is a real lockstep block
+decode: every window starts with an exact step (which refreshes the DualCache
+snapshot), DualCache steps follow until no position of the window is masked
+in any sequence, and a finished block is committed (forward over the clean
+block + cache append) before the next one starts.  W untimed steps, then
+exactly K timed refinement steps; value = K / time (steps/s), and decoded
+tokens / time is reported beside it.
+
+Also measured in the same run (reported under "extra"):
+* attention alone at the long-context shape (batch 32, 16384 committed tokens,
+  28/4 heads) in DualCache (8 rows) and exact (32 rows) form, against 8 TB/s;
+* the LM head alone at batch 1 (1.5B shape, 8 rows) against 8 TB/s and at 1024
+  rows (7B shape) against the dense bf16 MFMA peak (2.5 PFLOP/s);
+* a fixed-schedule long-context block (32 sequences x 16384 prefix: 4 windows
+  x 8 steps + commit), decoded tokens/s.
+
+roofline: the dominant kernel of the headline step is the LM head (its
+weights are ~92% of the step's bytes); its launches are timed with HIP events
+on the launch stream inside the timed region.
+cpu_baseline: the fp64 oracle (oracle/), timed on this host on a bounded
+sample of the same workload (DualCache steps of the same 8 sequences).
+"""
+import os
+
+try:
+    _CORES = len(os.sched_getaffinity(0))
+except AttributeError:  # pragma: no cover
+    _CORES = os.cpu_count() or 1
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = str(_CORES)
+
+import argparse
+import hashlib
+import json
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import bd_inputs as bi  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "block-refine steps/s & decoded tokens/s at 7B shape; % of HBM/MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_diffusion_decoding_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def make_decoder(cfg, w, pre):
+    from block_diffusion_decoding_amd.decoder import BlockDecoder, Dims
+    dims = Dims(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.hidden, cfg.V, cfg.D, cfg.cap)
+    weights = {k: torch.from_numpy(getattr(w, k)) for k in ("E", "Wq", "Wk", "Wv", "Wo", "Wlm")}
+    dec = BlockDecoder(dims, weights, dtype=torch.bfloat16, device="cuda")
+    dec.set_synthetic_prefix(pre.kv_len, pre.cache_k, pre.cache_v, pre.carry)
+    return dec
+
+
+def block_plants(cfg, w, rate, seed, n_blocks):
+    """Planted offsets for fresh blocks: a seeded fraction `rate` of all D
+    positions j >= 1 get an offset on input row j - 1 (position 0 is never
+    planted, so the carry row stays as the model computed it)."""
+    out = []
+    for k in range(n_blocks):
+        st = bi.BlockState(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), 0, cfg.D)
+        st.masked[:, 0] = False
+        plant, _, _ = bi.make_plants(cfg, seed + 1000 + k, w, st, rate)
+        out.append(torch.from_numpy(plant).to("cuda", torch.bfloat16))
+    return out
+
+
+class Loop:
+    """Lockstep block decode, one refinement step per call of step()."""
+
+    def __init__(self, dec, cfg, plants):
+        self.dec, self.cfg, self.plants = dec, cfg, plants
+        self.blk = -1
+        self.s = 0
+        self.first = True
+        self.steps = self.tokens = self.commits = 0
+        self.bits = None
+        self._new_block()
+
+    def _new_block(self):
+        cfg = self.cfg
+        self.blk += 1
+        self.dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool),
+                           self.plants[self.blk % len(self.plants)])
+        self.s, self.first = 0, True
+        self.bits = np.full(cfg.B, (1 << cfg.D) - 1, dtype=np.uint64)
+
+    def step(self):
+        cfg, dec = self.cfg, self.dec
+        S = cfg.S
+        if self.first:
+            dec.e_step(self.s, S, cfg.tau)
+        else:
+            dec.dc_step(self.s, S, cfg.tau)
+        self.first = False
+        self.steps += 1
+        bits = dec.mask_bits.cpu().numpy().view(np.uint64)      # 8 bytes per sequence
+        self.tokens += int(sum(bin(int(a) ^ int(b)).count("1") for a, b in zip(self.bits, bits)))
+        self.bits = bits.copy()
+        wmask = np.uint64(((1 << S) - 1) << (self.s * S))
+        if not np.any(bits & wmask):
+            self.s += 1
+            self.first = True
+            if self.s == cfg.D // S:
+                dec.commit()
+                self.commits += 1
+                self._new_block()
+
+
+def time_call(fn, reps, warm=3):
+    for _ in range(warm):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    return float(np.median(t)), float(np.mean(t))
+
+
+def extras(w3, reps):
+    """Attention and LM head alone at the long-context / batched shapes."""
+    from block_diffusion_decoding_amd import ops
+    out = {}
+    T = torch.bfloat16
+    c4 = bi.C4
+    # ---- attention, batch 32 x 16384 committed tokens
+    log("[bench] long-context attention inputs")
+    pre4 = bi.make_prefix(c4, 0)
+    kc = torch.from_numpy(pre4.cache_k).to("cuda", T)
+    vc = torch.from_numpy(pre4.cache_v).to("cuda", T)
+    del pre4
+    lens = torch.full((c4.B,), 16384, dtype=torch.int32, device="cuda")
+    for n_q, name in ((8, "dualcache"), (32, "exact")):
+        q = torch.randn(c4.B, n_q, c4.Hq, c4.d, device="cuda", dtype=T) * 0.02
+        kb = torch.randn(c4.B, c4.D, c4.Hkv, c4.d, device="cuda", dtype=T) * 0.02
+        vb = torch.randn_like(kb) * 0.02
+        o = torch.empty_like(q)
+        med, mean = time_call(lambda: ops.bd_block_attn(q, kc, vc, lens, kb, vb, o, D=c4.D, q_off=0), reps)
+        nbytes = c4.B * (16384 + c4.D) * 2 * c4.Hkv * c4.d * 2 + 2 * c4.B * n_q * c4.Hq * c4.d * 2
+        flops = 4 * c4.B * n_q * c4.Hq * c4.d * (16384 + c4.D)
+        out[f"attn_long_{name}"] = {
+            "shape": f"B=32 L=16384 n_q={n_q} Hq=28 Hkv=4 d=128 bf16", "us": mean * 1e6, "us_median": med * 1e6,
+            "bytes": nbytes, "GB/s": nbytes / mean / 1e9, "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS,
+            "TFLOP/s": flops / mean / 1e12}
+        log(f"[bench] attention {name}: {mean * 1e6:.1f} us, {nbytes / mean / 1e9:.0f} GB/s")
+    del kc, vc
+    # ---- fixed-schedule long-context block: 4 windows x 8 steps + commit
+    log("[bench] long-context block loop")
+    cfg4 = c4
+    pre4 = bi.make_prefix(cfg4, 0)
+    dec4 = make_decoder(cfg4, w3, pre4)
+    del pre4
+    dec4.new_block()
+    dec4.decode_block(cfg4.S, cfg4.tau, steps_per_window=8)          # warm-up block
+    dec4.kv_len.fill_(16384)
+    dec4.kv_len_host[:] = 16384
+    dec4.new_block()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = dec4.decode_block(cfg4.S, cfg4.tau, steps_per_window=8)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    decoded = cfg4.B * cfg4.D - int(sum(bin(int(x)).count("1") for x in dec4.mask_bits.cpu().numpy().view(np.uint64)))
+    out["long_block_loop"] = {"shape": "B=32 L=16384 block 32 sub-block 8, 8 steps/window + commit",
+                              "ms": dt * 1e3, "steps": n, "decoded_tokens": decoded,
+                              "tokens_per_s": decoded / dt, "steps_per_s": n / dt}
+    log(f"[bench] long block: {dt * 1e3:.2f} ms, {decoded / dt:.0f} tokens/s")
+    del dec4
+    torch.cuda.empty_cache()
+    # ---- LM head alone: 1024 rows on the 7B head (MFMA bound)
+    Wlm = torch.from_numpy(w3.Wlm).to("cuda", T)
+    for M, key in ((1024, "lmhead_7B_M1024"), (64, "lmhead_7B_M64")):
+        h = torch.randn(M, 3584, device="cuda", dtype=T) * 0.05
+        am = torch.empty(M, dtype=torch.int32, device="cuda")
+        cf = torch.empty(M, dtype=torch.float32, device="cuda")
+        med, mean = time_call(lambda: ops.bd_lmhead_confidence(h, None, Wlm, am, cf), reps)
+        flops = 2.0 * M * 3584 * 152064
+        nbytes = 152064 * 3584 * 2 + M * 3584 * 2 + 16 * M
+        out[key] = {"us": mean * 1e6, "TFLOP/s": flops / mean / 1e12,
+                    "frac_mfma": flops / mean / 1e12 / BF16_PEAK_TFLOPS,
+                    "GB/s": nbytes / mean / 1e9, "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] lm head M={M}: {mean * 1e6:.1f} us, {flops / mean / 1e12:.0f} TFLOP/s, "
+            f"{nbytes / mean / 1e9:.0f} GB/s")
+    del Wlm
+    # ---- LM head alone: batch 1 on the 1.5B head (HBM bound)
+    c2 = bi.C2
+    W2 = torch.from_numpy(bi.normal(0, "Wlm", (c2.V, c2.hidden), 0.02, "bf16")).to("cuda", T)
+    h = torch.randn(8, c2.hidden, device="cuda", dtype=T) * 0.05
+    am = torch.empty(8, dtype=torch.int32, device="cuda")
+    cf = torch.empty(8, dtype=torch.float32, device="cuda")
+    med, mean = time_call(lambda: ops.bd_lmhead_confidence(h, None, W2, am, cf), reps)
+    nbytes = c2.V * c2.hidden * 2 + 8 * c2.hidden * 2 + 16 * 8
+    out["lmhead_1.5B_M8"] = {"us": mean * 1e6, "GB/s": nbytes / mean / 1e9,
+                             "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
+    log(f"[bench] lm head 1.5B M=8: {mean * 1e6:.1f} us, {nbytes / mean / 1e9:.0f} GB/s")
+    return out
+
+
+def cpu_baseline(cfg, w, pre, rate, n_steps):
+    """fp64 oracle on the same seeded inputs: DualCache steps of window 1 of
+    the same 8 sequences (the exact refresh step that builds the snapshot is
+    not timed)."""
+    from oracle import refine as R
+    st = bi.make_block_state(cfg, 0, 1)
+    plant, carry_plant, _ = bi.make_plants(cfg, 0, w, st, rate)
+    m = R.Model.from_weights(w, cfg)
+    seqs = R.seqs_from_inputs(m, cfg, pre, st, plant, carry_plant)
+    for q in seqs:
+        R.e_step(m, q, 1, cfg.S, cfg.tau, cfg.D)
+    times = []
+    for _ in range(n_steps):
+        for q, b in zip(seqs, range(cfg.B)):
+            q.tokens = st.tokens[b].astype(np.int64).copy()
+            q.masked = st.masked[b].copy()
+        t0 = time.perf_counter()
+        for q in seqs:
+            R.dc_step(m, q, 1, cfg.S, cfg.tau, cfg.D)
+        times.append(time.perf_counter() - t0)
+    sec = float(np.median(times))
+    try:
+        vendor = np.show_config(mode="dicts")["Build Dependencies"]["blas"]["name"]
+    except Exception:  # pragma: no cover
+        vendor = "unknown"
+    return {"value": 1.0 / sec, "unit": "steps/s", "cores": _CORES, "kind": "oracle",
+            "sample": f"{n_steps} DualCache refinement steps (window 1) of the same 8-sequence 7B-shape batch, "
+                      f"fp64 NumPy ({vendor}), median {sec:.2f} s/step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rate", type=float, default=0.5, help="planted pass rate of masked rows")
+    ap.add_argument("--reps", type=int, default=20, help="repetitions of the single-call measurements")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this implementation runs on a "
+              "single GPU and has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import block_diffusion_decoding_amd as pkg
+    pkg.load_library()
+
+    cfg = bi.C3
+    log("[bench] generating the 7B-shape workload")
+    w = bi.make_weights(cfg, 0)
+    pre = bi.make_prefix(cfg, 0)
+    n_blocks = 8
+    dec = make_decoder(cfg, w, pre)
+    plants = block_plants(cfg, w, args.rate, 0, n_blocks)
+    loop = Loop(dec, cfg, plants)
+    for _ in range(args.warmup):
+        loop.step()
+    torch.cuda.synchronize()
+    # timed region
+    s0, t0_tok, c0 = loop.steps, loop.tokens, loop.commits
+    dec.lm_events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        loop.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    lm_t = np.array([a.elapsed_time(b) for a, b in dec.lm_events]) * 1e-3
+    dec.lm_events = None
+    steps = loop.steps - s0
+    tokens = loop.tokens - t0_tok
+    steps_per_s = steps / elapsed
+    log(f"[bench] {steps} steps in {elapsed * 1e3:.1f} ms: {steps_per_s:.1f} steps/s, "
+        f"{tokens / elapsed:.0f} tokens/s, {loop.commits - c0} commits, LM head {lm_t.mean() * 1e6:.1f} us")
+
+    # roofline of the dominant kernel: LM head of the 7B step (B*S = 64 rows)
+    M = cfg.B * cfg.S
+    lm_bytes = cfg.V * cfg.hidden * 2 + M * cfg.hidden * 2 + 16 * M
+    lm_mean = float(lm_t.mean())
+    achieved = lm_bytes / lm_mean / 1e9
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "lmhead_7B_M64_traffic.json")
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath))
+        if rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "bd_lmhead_confidence (lm_bf16_kernel<4> + lm_merge_kernel), 64 rows x 152064 x 3584",
+                "algorithmic_bytes": lm_bytes, "launch_us_mean": round(lm_mean * 1e6, 2),
+                "launch_us_median": round(float(np.median(lm_t)) * 1e6, 2)}
+    extra = {}
+    if not args.no_extras:
+        del dec
+        torch.cuda.empty_cache()
+        extra = extras(w, args.reps)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(cfg, w, pre, args.rate, args.cpu_steps)
+        log(f"[bench] oracle: {cpu['value']:.3f} steps/s on {cpu['cores']} cores")
+    line = {
+        "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "7B-shape refinement loop: 28q/4kv heads d128, hidden 3584, LM head 3584x152064, "
+                               "batch 8, prefixes 1024-4096 (block-aligned), block 32, sub-block 8, tau 0.9, "
+                               f"planted pass rate {args.rate}",
+                   "global_batch": cfg.B, "block": cfg.D, "sub_block": cfg.S, "threshold": cfg.tau},
+        "decoded_tokens_per_s": round(tokens / elapsed, 1),
+        "tokens_per_step": round(tokens / steps, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

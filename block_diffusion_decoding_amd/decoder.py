@@ -75,6 +75,7 @@ class BlockDecoder:
         self.n_unmasked = torch.zeros(B, dtype=torch.int32, device=dev)
         self._win = {}
         self.last = None
+        self.lm_events = None   # list of (start, end) events around LM-head calls when set
 
     # ------------------------------------------------------------------ state
     def set_synthetic_prefix(self, kv_len, cache_k, cache_v, carry):
@@ -148,8 +149,15 @@ class BlockDecoder:
     def _lm_and_unmask(self, s: int, S: int, tau: float):
         w = self._window(s, S)
         dm = self.dims
+        ev = None
+        if self.lm_events is not None:
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev[0].record()
         ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"], w["conf"],
                                  max_logit=w["maxl"], lse=w["lse"])
+        if ev is not None:
+            ev[1].record()
+            self.lm_events.append(ev)
         ops.bd_threshold_unmask(w["conf"], w["argmax"], self.tokens, self.mask_bits, win_lo=s * S,
                                 threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
         self.last = w
