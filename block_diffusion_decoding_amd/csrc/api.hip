@@ -165,40 +165,58 @@ bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int 
   if (D < 1 || (mask_bits != nullptr && D > 64) || row_off < 0 || row_off + n_rows > D || hidden <= 0 || V <= 0 ||
       !E || !tokens || !x)
     return BD_EINVAL;
+  if (hidden % (dt == BD_BF16 ? 8 : 4) != 0 || !aligned16(E) || !aligned16(x) || (plant && !aligned16(plant)))
+    return BD_EUNSUPPORTED;
   return hip_status(bd_embed_launch(dt, B, D, row_off, n_rows, hidden, V, E, tokens, mask_bits, plant, x,
                                     static_cast<hipStream_t>(stream)));
 }
 
 static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const BdGemmSeg* segs, int nseg,
-                             void* stream) {
+                             void* workspace, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
   if (M == 0) return BD_OK;
   if (K <= 0 || !x || !valid_rows(xr)) return BD_EINVAL;
+  int N[3];
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].N <= 0 || !segs[i].w || !segs[i].y || !valid_rows(segs[i].yr)) return BD_EINVAL;
     if (segs[i].res && !valid_rows(segs[i].rr)) return BD_EINVAL;
+    N[i] = segs[i].N;
   }
   if (dt == BD_BF16) {
     if (K % 256 != 0 || !aligned16(x)) return BD_EUNSUPPORTED;
     for (int i = 0; i < nseg; ++i)
       if (!aligned16(segs[i].w)) return BD_EUNSUPPORTED;
   }
-  return hip_status(bd_gemm_launch(dt, M, K, x, xr, segs, nseg, static_cast<hipStream_t>(stream)));
+  const BdGemmPlan p = bd_gemm_plan(dt, M, K, N, nseg);
+  if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)))
+    return BD_EINVAL;
+  return hip_status(bd_gemm_launch(dt, p, M, K, x, xr, segs, nseg, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t bd_linear_workspace_size(bd_dtype dt, int M, int N, int K) {
+  if (!valid_dtype(dt) || M <= 0 || N <= 0 || K <= 0) return 0;
+  return bd_gemm_plan(dt, M, K, &N, 1).ws_bytes;
+}
+
+size_t bd_qkv_proj_workspace_size(bd_dtype dt, int M, int K, int Nq, int Nkv) {
+  if (!valid_dtype(dt) || M <= 0 || K <= 0 || Nq <= 0 || Nkv <= 0) return 0;
+  const int N[3] = {Nq, Nkv, Nkv};
+  return bd_gemm_plan(dt, M, K, N, 3).ws_bytes;
 }
 
 bd_status bd_linear(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr, const void* w, const void* res,
-                    bd_rows rr, void* y, bd_rows yr, void* stream) {
+                    bd_rows rr, void* y, bd_rows yr, void* workspace, size_t ws_bytes, void* stream) {
   BdGemmSeg seg{w, y, yr, res, rr, N};
-  return gemm_common(dt, M, K, x, xr, &seg, 1, stream);
+  return gemm_common(dt, M, K, x, xr, &seg, 1, workspace, ws_bytes, stream);
 }
 
 bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,
                       bd_rows qr, const void* wk, const void* wv, int Nkv, void* k, bd_rows kr, void* v, bd_rows vr,
-                      void* stream) {
+                      void* workspace, size_t ws_bytes, void* stream) {
   const bd_rows none{1, 1, 0};
   BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
                        {wv, v, vr, nullptr, none, Nkv}};
-  return gemm_common(dt, M, K, x, xr, segs, 3, stream);
+  return gemm_common(dt, M, K, x, xr, segs, 3, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -78,8 +78,18 @@ struct BdGemmSeg {
   int N;
 };
 
-hipError_t bd_gemm_launch(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
-                          const BdGemmSeg* segs, int nseg, hipStream_t s);
+struct BdGemmPlan {
+  int MT;                 // 16-row tiles per work-group
+  int nx, ny;             // column tiles (all segments) and row tiles
+  int ksplit;             // K slices per tile
+  size_t counters_bytes;  // workspace: arrival counters, then fp32 partial tiles
+  size_t ws_bytes;
+};
+
+BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg);
+
+hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
+                          const BdGemmSeg* segs, int nseg, void* workspace, hipStream_t s);
 
 hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
                            const void* E, const int32_t* tokens, const uint64_t* mask_bits,

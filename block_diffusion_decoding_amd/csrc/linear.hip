@@ -6,18 +6,29 @@
 // the in-block buffer, Key design 3) and the attention output projection
 // with its residual.
 //
-// bf16 projections use the skinny MFMA core of skinny_gemm.h with a plain
-// store epilogue; up to three weight matrices (Q, K, V) share one launch.
+// bf16 projections use the streaming MFMA core of stream_gemm.h with a plain
+// store epilogue (plus residual); up to three weight matrices (Q, K, V) share
+// one launch, and K is split over work-groups when the column tiles alone
+// cannot fill the GPU.
 #include "bd_device.h"
 #include "bd_launch.h"
-#include "skinny_gemm.h"
+#include "stream_gemm.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNT = 1;
-constexpr int kKC = 256;
+constexpr int kNTW = 4;        // 16-column tiles per work-group (64 columns)
+constexpr int kKSC = 2;        // 32-wide k-steps per pipeline stage
+constexpr int kNS = 3;         // pipeline stages
 constexpr int kMaxSeg = 3;
+constexpr int kTargetWGs = 512;
+constexpr int kMinChunksPerSplit = 4;
+// Arrival counters occupy a fixed region at the start of every GEMM workspace
+// (one int per tile, at most kMaxTiles tiles), so that calls with different
+// tilings can share one workspace: a call's partial sums never overlap the
+// counters of another call, and every counter is back at zero when a call ends.
+constexpr int kMaxTiles = 16384;
+constexpr size_t kCounterBytes = kMaxTiles * sizeof(int);
 
 struct GemmK {
   const uint16_t* x;
@@ -30,46 +41,77 @@ struct GemmK {
   bd_rows rr[kMaxSeg];
   int N[kMaxSeg];
   int wg_begin[kMaxSeg + 1];
+  int ksplit;
+  float* part;    // [tiles][ksplit][MT*16 x 64] fp32 partial sums (ksplit > 1)
+  int* counters;  // [tiles] arrival counters, zero between calls
 };
 
+__device__ __forceinline__ void gemm_store(const GemmK& a, int seg, int m, int col, float v) {
+  const int N = a.N[seg];
+  if (a.res[seg]) v += bd_bf2f(a.res[seg][(size_t)bd_map_row(a.rr[seg], m) * N + col]);
+  a.y[seg][(size_t)bd_map_row(a.yr[seg], m) * N + col] = (uint16_t)bd_f2bf(v);
+}
+
+// One (column tile, row tile, K slice) per work-group.  With a K split the
+// slices write fp32 partial tiles; the last slice to arrive (arrival counter)
+// adds them in slice order, so the result does not depend on timing.
 template <int MT>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmK a) {
-  using XS = bd_skinny::XStage<MT, kKC>;
-  __shared__ uint4 sX[2 * XS::LDS_U4];
+__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
+  using C = bd_stream::Cfg<MT, kNTW, kKSC, kNS>;
+  constexpr int TILE = MT * 16 * kNTW * 16;
+  __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
+  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
+  const int wm = wave % C::WM, wn = wave / C::WM;
   const int bx = blockIdx.x;
   const int seg = (a.nseg > 2 && bx >= a.wg_begin[2]) ? 2 : (a.nseg > 1 && bx >= a.wg_begin[1]) ? 1 : 0;
   const int N = a.N[seg];
-  const int col0 = ((bx - a.wg_begin[seg]) * 4 + wave) * kNT * 16;
+  const int n0 = (bx - a.wg_begin[seg]) * kNTW * 16;
   const int m0 = blockIdx.y * MT * 16;
+  const int z = blockIdx.z;
+  const int nch = a.K / C::KC;
+  const int c0 = z * nch / a.ksplit, c1 = (z + 1) * nch / a.ksplit;
 
   auto xrow = [&](int m) -> const uint16_t* {
     return m < a.M ? a.x + (size_t)bd_map_row(a.xr, m) * a.K : nullptr;
   };
-  bd_f32x4 acc[MT][kNT];
-  bd_skinny::mainloop<MT, kNT, kKC>(xrow, m0, a.w[seg], N, a.K, col0, sX, acc);
+  bd_f32x4 acc[C::NTP];
+  bd_stream::mainloop<C>(xrow, a.x, m0, a.w[seg], N, a.K, n0, sbuf, acc, c0 * C::KC, c1 - c0);
 
-  uint16_t* y = a.y[seg];
-  const uint16_t* res = a.res[seg];
-  const bd_rows yr = a.yr[seg], rr = a.rr[seg];
+  if (a.ksplit == 1) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int j = 0; j < C::NTP; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + mt * 16 + 4 * g + r;
-      if (m >= a.M) continue;
-      const size_t yrow = (size_t)bd_map_row(yr, m) * N;
-      const size_t rrow = res ? (size_t)bd_map_row(rr, m) * N : 0;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int col = col0 + nt * 16 + l16;
-        if (col >= N) continue;
-        float v = acc[mt][nt][r];
-        if (res) v += bd_bf2f(res[rrow + col]);
-        y[yrow + col] = (uint16_t)bd_f2bf(v);
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 16 + 4 * g + r;
+        const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+        if (m < a.M && col < N) gemm_store(a, seg, m, col, acc[j][r]);
       }
-    }
+    return;
+  }
+  const int tile = blockIdx.y * gridDim.x + bx;
+  float* pt = a.part + ((size_t)tile * a.ksplit + z) * TILE;
+#pragma unroll
+  for (int j = 0; j < C::NTP; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      pt[(wm * 16 + 4 * g + r) * (kNTW * 16) + (wn * C::NTP + j) * 16 + l16] = acc[j][r];
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[tile], 1) == a.ksplit - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float* p0 = a.part + (size_t)tile * a.ksplit * TILE;
+  for (int e = tid; e < TILE; e += kThreads) {
+    const int m = m0 + e / (kNTW * 16), col = n0 + e % (kNTW * 16);
+    if (m >= a.M || col >= N) continue;
+    float v = 0.f;
+    for (int zz = 0; zz < a.ksplit; ++zz) v += p0[(size_t)zz * TILE + e];
+    gemm_store(a, seg, m, col, v);
+  }
+  if (tid == 0) a.counters[tile] = 0;
 }
 
 struct GemmF {
@@ -108,24 +150,66 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(int D, int row_off, int
   const T* er = E + (size_t)(masked ? V : (ok ? tok : 0)) * hidden;
   const T* pr = plant ? plant + ((size_t)b * D + pos) * hidden : nullptr;
   T* xr = x + ((size_t)b * n_rows + i) * hidden;
-  for (int e = threadIdx.x; e < hidden; e += kThreads) {
-    float v;
+  constexpr int PER = 16 / sizeof(T);  // elements per 16-byte access
+  for (int e = threadIdx.x * PER; e < hidden; e += kThreads * PER) {
+    uint4 ev = *reinterpret_cast<const uint4*>(er + e);
+    uint4 out;
     if constexpr (sizeof(T) == 2) {
-      v = bd_bf2f(er[e]);
-      if (pr) v += bd_bf2f(pr[e]);
-      xr[e] = ok ? (T)bd_f2bf(v) : (T)0x7fc0u;
+      uint4 pv = pr ? *reinterpret_cast<const uint4*>(pr + e) : make_uint4(0, 0, 0, 0);
+      const uint32_t* ew = reinterpret_cast<const uint32_t*>(&ev);
+      const uint32_t* pw = reinterpret_cast<const uint32_t*>(&pv);
+      uint32_t* ow = reinterpret_cast<uint32_t*>(&out);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (!ok) {
+          ow[h] = 0x7fc07fc0u;
+        } else if (pr) {
+          ow[h] = bd_pack_bf2(bd_bf2f(ew[h] & 0xffffu) + bd_bf2f(pw[h] & 0xffffu),
+                              bd_bf2f(ew[h] >> 16) + bd_bf2f(pw[h] >> 16));
+        } else {
+          ow[h] = ew[h];
+        }
+      }
     } else {
-      v = er[e];
-      if (pr) v += pr[e];
-      xr[e] = ok ? v : __builtin_nanf("");
+      float4 f = __builtin_bit_cast(float4, ev);
+      if (pr) {
+        const float4 p = *reinterpret_cast<const float4*>(pr + e);
+        f.x += p.x; f.y += p.y; f.z += p.z; f.w += p.w;
+      }
+      if (!ok) f = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+      out = __builtin_bit_cast(uint4, f);
     }
+    *reinterpret_cast<uint4*>(xr + e) = out;
   }
 }
 
 }  // namespace
 
-hipError_t bd_gemm_launch(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const BdGemmSeg* segs,
-                          int nseg, hipStream_t s) {
+BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg) {
+  BdGemmPlan p{};
+  if (dt == BD_F32) return p;
+  const int mt = (M + 15) / 16;
+  p.MT = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+  p.nx = 0;
+  for (int i = 0; i < nseg; ++i) p.nx += (N[i] + kNTW * 16 - 1) / (kNTW * 16);
+  p.ny = (M + p.MT * 16 - 1) / (p.MT * 16);
+  const int nch = K / (kKSC * 32);
+  const long base = (long)p.nx * p.ny;
+  int ks = (int)((kTargetWGs + base - 1) / base);
+  const int maxks = nch / kMinChunksPerSplit;
+  ks = ks > maxks ? maxks : ks;
+  p.ksplit = ks < 1 ? 1 : ks;
+  const size_t tiles = (size_t)p.nx * p.ny;
+  if (tiles > (size_t)kMaxTiles) p.ksplit = 1;
+  if (p.ksplit > 1) {
+    p.counters_bytes = kCounterBytes;
+    p.ws_bytes = kCounterBytes + tiles * p.ksplit * p.MT * 16 * kNTW * 16 * sizeof(float);
+  }
+  return p;
+}
+
+hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
+                          const BdGemmSeg* segs, int nseg, void* workspace, hipStream_t s) {
   if (dt == BD_F32) {
     for (int i = 0; i < nseg; ++i) {
       GemmF a{static_cast<const float*>(x), xr, M, K, static_cast<const float*>(segs[i].w),
@@ -144,7 +228,6 @@ hipError_t bd_gemm_launch(bd_dtype dt, int M, int K, const void* x, bd_rows xr, 
   a.M = M;
   a.K = K;
   a.nseg = nseg;
-  const int cols_per_wg = 4 * kNT * 16;
   int wg = 0;
   for (int i = 0; i < nseg; ++i) {
     a.w[i] = static_cast<const uint16_t*>(segs[i].w);
@@ -154,16 +237,16 @@ hipError_t bd_gemm_launch(bd_dtype dt, int M, int K, const void* x, bd_rows xr, 
     a.rr[i] = segs[i].rr;
     a.N[i] = segs[i].N;
     a.wg_begin[i] = wg;
-    wg += (segs[i].N + cols_per_wg - 1) / cols_per_wg;
+    wg += (segs[i].N + kNTW * 16 - 1) / (kNTW * 16);
   }
   for (int i = nseg; i <= kMaxSeg; ++i) a.wg_begin[i] = wg;
-  const int mt = (M + 15) / 16;
-  const int MT = mt > 4 ? 4 : mt;
-  const dim3 grid(wg, (M + MT * 16 - 1) / (MT * 16));
-  switch (MT) {
+  a.ksplit = p.ksplit;
+  a.counters = p.ksplit > 1 ? static_cast<int*>(workspace) : nullptr;
+  a.part = p.ksplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.counters_bytes) : nullptr;
+  const dim3 grid(wg, p.ny, p.ksplit);
+  switch (p.MT) {
     case 1: hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(gemm_bf16_kernel<3>, grid, dim3(kThreads), 0, s, a); break;
     default: hipLaunchKernelGGL(gemm_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
   }
   return hipGetLastError();

@@ -13,19 +13,21 @@
 // of a row in a fixed order into argmax, max, log-sum-exp and
 // confidence = exp(max - lse).
 //
-// bf16: skinny MFMA GEMM (skinny_gemm.h), weights streamed once from HBM at
-// batch sizes up to 64 rows per work-group.  fp32: plain VALU kernel.
+// bf16: streaming MFMA GEMM (stream_gemm.h), weights streamed once from HBM
+// through a 3-stage asynchronous global->LDS pipeline, up to 64 rows per
+// work-group.  fp32: plain VALU kernel.
 #include <climits>
 
 #include "bd_device.h"
 #include "bd_launch.h"
-#include "skinny_gemm.h"
+#include "stream_gemm.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNT = 2;        // 16-column tiles per wave (bf16)
-constexpr int kKC = 256;      // K chunk (bf16)
+constexpr int kNTW = 8;       // 16-column tiles per work-group (bf16)
+constexpr int kKSC = 2;       // 32-wide k-steps per pipeline stage (bf16)
+constexpr int kNS = 3;        // pipeline stages (bf16)
 constexpr int kF32Rows = 16;  // rows per work-group (fp32)
 
 struct LmK {
@@ -48,58 +50,57 @@ __device__ __forceinline__ const uint16_t* lm_row(const LmK& a, int m) {
 }
 
 template <int MT>
-__global__ __launch_bounds__(kThreads) void lm_bf16_kernel(LmK a) {
-  using XS = bd_skinny::XStage<MT, kKC>;
-  __shared__ uint4 sX[2 * XS::LDS_U4];
-  __shared__ BdArgStat red[4][MT * 16];
+__global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
+  using C = bd_stream::Cfg<MT, kNTW, kKSC, kNS>;
+  __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
+  const int wm = wave % C::WM, wn = wave / C::WM;
   const int m0 = blockIdx.y * MT * 16;
-  const int col0 = (blockIdx.x * 4 + wave) * kNT * 16;
+  const int n0 = blockIdx.x * kNTW * 16;
 
-  bd_f32x4 acc[MT][kNT];
+  bd_f32x4 acc[C::NTP];
   auto xrow = [&](int m) { return lm_row(a, m); };
-  bd_skinny::mainloop<MT, kNT, kKC>(xrow, m0, a.w, a.V, a.hidden, col0, sX, acc);
+  bd_stream::mainloop<C>(xrow, a.h, m0, a.w, a.V, a.hidden, n0, sbuf, acc);
 
+  // rows m0 + wm*16 + 4g + r, columns n0 + (wn*NTP + j)*16 + l16
+  BdArgStat* red = reinterpret_cast<BdArgStat*>(sbuf);  // [WN][MT*16]
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int r = 0; r < 4; ++r) {
+    const int rl = wm * 16 + 4 * g + r;
+    BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = mt * 16 + 4 * g + r;
-      BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int col = col0 + nt * 16 + l16;
-        const float v = acc[mt][nt][r];
-        if (col < a.V && v > st.m) {
-          st.m = v;
-          st.i = col;
-        }
+    for (int j = 0; j < C::NTP; ++j) {
+      const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+      const float v = acc[j][r];
+      if (col < a.V && v > st.m) {
+        st.m = v;
+        st.i = col;
       }
-      float s = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int col = col0 + nt * 16 + l16;
-        if (col < a.V) s += bd_exp2((acc[mt][nt][r] - st.m) * BD_LOG2E);
-      }
-      st.s = s;
-      if (a.logits != nullptr && m0 + rl < a.M) {
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int col = col0 + nt * 16 + l16;
-          if (col < a.V) a.logits[(size_t)(m0 + rl) * a.V + col] = acc[mt][nt][r];
-        }
-      }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
-      if (l16 == 0) red[wave][rl] = st;
     }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < C::NTP; ++j) {
+      const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+      if (col < a.V) s += bd_exp2((acc[j][r] - st.m) * BD_LOG2E);
+    }
+    st.s = s;
+    if (a.logits != nullptr && m0 + rl < a.M) {
+#pragma unroll
+      for (int j = 0; j < C::NTP; ++j) {
+        const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+        if (col < a.V) a.logits[(size_t)(m0 + rl) * a.V + col] = acc[j][r];
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
+    if (l16 == 0) red[wn * (MT * 16) + rl] = st;
   }
   __syncthreads();
   if (tid < MT * 16 && m0 + tid < a.M) {
-    BdArgStat st = red[0][tid];
+    BdArgStat st = red[tid];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) st = bd_stat_combine(st, red[w][tid]);
+    for (int w = 1; w < C::WN; ++w) st = bd_stat_combine(st, red[w * (MT * 16) + tid]);
     const size_t pi = (size_t)(m0 + tid) * a.nvt + blockIdx.x;
     a.pmax[pi] = st.m;
     a.pidx[pi] = st.i;
@@ -170,21 +171,25 @@ __global__ __launch_bounds__(kThreads) void lm_f32_kernel(LmF a) {
   }
 }
 
-// Fold the tiles of each row in a fixed order; one wave per row.
+// Fold the tiles of each row in a fixed order; one work-group per row.
 __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_idx, int n_src, int M,
                                                             int nvt, const float* pmax, const int32_t* pidx,
                                                             const float* psum, int32_t* argmax, float* conf,
                                                             float* max_logit, float* lse) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (m >= M) return;
+  __shared__ BdArgStat red[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = blockIdx.x;
   BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
-  for (int t = lane; t < nvt; t += 64) {
+  for (int t = tid; t < nvt; t += kThreads) {
     const size_t pi = (size_t)m * nvt + t;
     st = bd_stat_combine(st, BdArgStat{pmax[pi], pidx[pi], psum[pi]});
   }
   for (int off = 32; off > 0; off >>= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
-  if (lane != 0) return;
+  if (lane == 0) red[wave] = st;
+  __syncthreads();
+  if (tid != 0) return;
+  st = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) st = bd_stat_combine(st, red[w]);
   const int src = row_idx ? row_idx[m] : m;
   const bool ok = src >= 0 && src < n_src && st.s > 0.f;
   const float nan = __builtin_nanf("");
@@ -202,9 +207,9 @@ BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
     p.cols_per_wg = kThreads;
     p.rows_per_wg = kF32Rows;
   } else {
-    p.cols_per_wg = 4 * kNT * 16;
+    p.cols_per_wg = kNTW * 16;
     const int mt = (M + 15) / 16;
-    p.rows_per_wg = 16 * (mt < 1 ? 1 : (mt > 4 ? 4 : mt));
+    p.rows_per_wg = 16 * (mt <= 1 ? 1 : (mt == 2 ? 2 : 4));
   }
   p.nvt = (V + p.cols_per_wg - 1) / p.cols_per_wg;
   p.nmb = (M + p.rows_per_wg - 1) / p.rows_per_wg;
@@ -225,13 +230,12 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
     switch (p.rows_per_wg / 16) {
       case 1: hipLaunchKernelGGL(lm_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
       case 2: hipLaunchKernelGGL(lm_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-      case 3: hipLaunchKernelGGL(lm_bf16_kernel<3>, grid, dim3(kThreads), 0, s, a); break;
       default: hipLaunchKernelGGL(lm_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lm_merge_kernel, dim3((x.M + 3) / 4), dim3(kThreads), 0, s, x.row_idx, x.n_src, x.M,
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(x.M), dim3(kThreads), 0, s, x.row_idx, x.n_src, x.M,
                      p.nvt, x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse);
   return hipGetLastError();
 }

@@ -153,19 +153,26 @@ def bd_embed_rows(E, tokens, mask_bits, x, *, row_off, n_rows, plant=None, strea
     _check("bd_embed_rows", st)
 
 
-def bd_linear(x, xr, w, y, yr, *, M, res=None, rr=None, stream=None):
+def bd_linear(x, xr, w, y, yr, *, M, res=None, rr=None, ws=None, stream=None):
     """y[yr(m)] = x[xr(m)] w^T (+ res[rr(m)]); w [N, K]."""
     lib = _lib.load()
     N, K = w.shape
-    st = lib.bd_linear(_dt(w), M, N, K, _p(x), xr, _p(w), _p(res), rr if rr is not None else dense(1), _p(y), yr,
-                       _stream(stream))
+    dt = _dt(w)
+    if ws is None:
+        ws = workspace(lib.bd_linear_workspace_size(dt, M, N, K), w.device, "gemm")
+    st = lib.bd_linear(dt, M, N, K, _p(x), xr, _p(w), _p(res), rr if rr is not None else dense(1), _p(y), yr,
+                       _p(ws), ws.numel(), _stream(stream))
     _check("bd_linear", st)
 
 
-def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, stream=None):
+def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, ws=None, stream=None):
+    """q[qr(m)] = x[xr(m)] wq^T, k[kr(m)] = x[xr(m)] wk^T, v[vr(m)] = x[xr(m)] wv^T."""
     lib = _lib.load()
     Nq, K = wq.shape
     Nkv = wk.shape[0]
-    st = lib.bd_qkv_proj(_dt(wq), M, K, _p(x), xr, _p(wq), Nq, _p(q), qr, _p(wk), _p(wv), Nkv, _p(k), kr, _p(v),
-                         vr, _stream(stream))
+    dt = _dt(wq)
+    if ws is None:
+        ws = workspace(lib.bd_qkv_proj_workspace_size(dt, M, K, Nq, Nkv), wq.device, "gemm")
+    st = lib.bd_qkv_proj(dt, M, K, _p(x), xr, _p(wq), Nq, _p(q), qr, _p(wk), _p(wv), Nkv, _p(k), kr, _p(v),
+                         vr, _p(ws), ws.numel(), _stream(stream))
     _check("bd_qkv_proj", st)

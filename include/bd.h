@@ -194,25 +194,35 @@ bd_status bd_kv_append(bd_dtype dt, int B, int Hkv, int d, int cap,
  *   position is masked (then D may exceed 64, e.g. a multi-block prompt);
  *   plant [B, D, hidden] or NULL: an additive offset per block row;
  *   x [B, n_rows, hidden] out: row i of sequence b is block position row_off + i.
- * A token id outside [0, V) on an unmasked position yields a NaN row. */
+ * A token id outside [0, V) on an unmasked position yields a NaN row.
+ * hidden must be a multiple of 8 (bf16) or 4 (fp32). */
 bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
                         const void* E, const int32_t* tokens, const uint64_t* mask_bits,
                         const void* plant, void* x, void* stream);
 
 /* y[yr(m), n] = sum_k x[xr(m), k] * w[n, k]  (+ res[rr(m), n] when res != NULL)
  * for m < M, n < N.  x rows hold K elements, y/res rows hold N elements;
- * w is [N, K] row-major.  bf16 uses MFMA with fp32 accumulation. */
+ * w is [N, K] row-major.  bf16 uses MFMA with fp32 accumulation and needs
+ * K % 256 == 0; when the column tiles alone cannot fill the GPU, K is split
+ * over work-groups and the slices are added in a fixed order through the
+ * workspace (bd_linear_workspace_size; 0 means none is needed).  Its first
+ * 64 KiB hold arrival counters that every call leaves at zero, so one
+ * workspace may serve every bd_linear / bd_qkv_proj call on a stream. */
+size_t bd_linear_workspace_size(bd_dtype dt, int M, int N, int K);
 bd_status bd_linear(bd_dtype dt, int M, int N, int K,
                     const void* x, bd_rows xr, const void* w,
-                    const void* res, bd_rows rr, void* y, bd_rows yr, void* stream);
+                    const void* res, bd_rows rr, void* y, bd_rows yr,
+                    void* workspace, size_t ws_bytes, void* stream);
 
 /* The three input projections of one attention layer in one launch:
  *   q[qr(m)] = x[xr(m)] Wq^T  (Nq columns), k[kr(m)] = x[xr(m)] Wk^T and
- *   v[vr(m)] = x[xr(m)] Wv^T  (Nkv columns each). */
+ *   v[vr(m)] = x[xr(m)] Wv^T  (Nkv columns each).  Workspace as bd_linear. */
+size_t bd_qkv_proj_workspace_size(bd_dtype dt, int M, int K, int Nq, int Nkv);
 bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
                       const void* wq, int Nq, void* q, bd_rows qr,
                       const void* wk, const void* wv, int Nkv,
-                      void* k, bd_rows kr, void* v, bd_rows vr, void* stream);
+                      void* k, bd_rows kr, void* v, bd_rows vr,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ def test_header_declares_the_four_calls_and_support():
     names = declared_functions()
     for n in ["bd_block_attn", "bd_lmhead_confidence", "bd_threshold_unmask", "bd_kv_append",
               "bd_embed_rows", "bd_linear", "bd_qkv_proj", "bd_block_attn_workspace_size",
+              "bd_linear_workspace_size", "bd_qkv_proj_workspace_size",
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version"]:
         assert n in names
 
@@ -109,12 +110,18 @@ def test_gemm_and_embed_argument_errors():
     lib = _lib.load()
     E, U = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED
     R = _lib.BdRows
+    big = 1 << 30
     assert lib.bd_linear(1, 64, 3584, 3584, FAKE, R(64, 64, 0), FAKE, None, R(1, 1, 0), FAKE, R(0, 1, 0),
-                         None) == E                                    # group 0
+                         FAKE, big, None) == E                         # group 0
     assert lib.bd_linear(1, 64, 3584, 1000, FAKE, R(64, 64, 0), FAKE, None, R(1, 1, 0), FAKE, R(64, 64, 0),
-                         None) == U                                    # K % 256
+                         FAKE, big, None) == U                         # K % 256
     assert lib.bd_linear(1, 0, 3584, 3584, FAKE, R(1, 1, 0), FAKE, None, R(1, 1, 0), FAKE, R(1, 1, 0),
-                         None) == 0
+                         None, 0, None) == 0
+    need = lib.bd_qkv_proj_workspace_size(1, 64, 3584, 3584, 512)
+    assert need > 0                                                    # the 7B projections split K
+    assert lib.bd_qkv_proj(1, 64, 3584, FAKE, R(64, 64, 0), FAKE, 3584, FAKE, R(64, 64, 0), FAKE, FAKE, 512,
+                           FAKE, R(8, 32, 8), FAKE, R(8, 32, 8), FAKE, need - 16, None) == E
+    assert lib.bd_linear_workspace_size(0, 64, 3584, 3584) == 0       # fp32: no workspace
     assert lib.bd_embed_rows(1, 1, 65, 0, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
     assert lib.bd_embed_rows(1, 1, 32, 30, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
 

@@ -229,3 +229,36 @@ def test_embed_and_projections(cfg):
     o.bd_linear(q, o.dense(B * S), up(w.Wo, T), H, o.rows(S, 1 + D, 1 + S), M=B * S, res=X, rr=o.dense(B * S))
     rH = R.output(m, Xh, down(q).reshape(B * S, cfg.Hq, cfg.d))
     rows_close(down(H)[:, 1 + S:1 + 2 * S].reshape(B * S, -1), rH, TOL[cfg.dtype], "o proj")
+
+
+def test_projection_workspace_shared_by_different_tilings():
+    """Split-K projections of different shapes share one workspace: every
+    call must leave the arrival counters at zero for the next one."""
+    say("[support] shared gemm workspace")
+    o = ops()
+    T = torch.bfloat16
+    K = 3584
+    wq = bi.normal(6, "Wq", (3584, K), 0.02, "bf16")
+    wk = bi.normal(6, "Wk", (512, K), 0.02, "bf16")
+    wv = bi.normal(6, "Wv", (512, K), 0.02, "bf16")
+    wo = bi.normal(6, "Wo", (3584, K), 0.02, "bf16")
+    gq, gk, gv, go = (up(w_, T) for w_ in (wq, wk, wv, wo))
+    need = max(o._lib.load().bd_qkv_proj_workspace_size(1, M, K, 3584, 512) for M in (8, 64, 256)) + \
+        max(o._lib.load().bd_linear_workspace_size(1, M, 3584, K) for M in (8, 64, 256))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for it, M in enumerate([256, 64, 256, 8, 64, 256, 64]):
+        x = bi.normal(100 + it, "h", (M, K), 0.5, "bf16")
+        gx = up(x, T)
+        q = torch.zeros(M, 3584, dtype=T, device=DEV)
+        k = torch.zeros(M, 512, dtype=T, device=DEV)
+        v = torch.zeros(M, 512, dtype=T, device=DEV)
+        y = torch.zeros(M, 3584, dtype=T, device=DEV)
+        o.bd_qkv_proj(gx, o.dense(M), gq, q, o.dense(M), gk, gv, k, o.dense(M), v, o.dense(M), M=M, ws=ws)
+        o.bd_linear(gx, o.dense(M), go, y, o.dense(M), M=M, res=gx, rr=o.dense(M), ws=ws)
+        torch.cuda.synchronize()
+        xf = x.astype(np.float64)
+        rows_close(down(q), xf @ wq.astype(np.float64).T, TOL["bf16"], f"q M={M} call {it}")
+        rows_close(down(k), xf @ wk.astype(np.float64).T, TOL["bf16"], f"k M={M} call {it}")
+        rows_close(down(v), xf @ wv.astype(np.float64).T, TOL["bf16"], f"v M={M} call {it}")
+        rows_close(down(y), xf + xf @ wo.astype(np.float64).T, TOL["bf16"], f"o M={M} call {it}")
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0      # counters left at zero
