@@ -10,13 +10,15 @@
 // bf16 path (MFMA): one work-group handles (sequence b, KV head, key chunk,
 // query-tile group).  The G query heads that share a KV head and the n_q fresh
 // block rows form R = n_q * G query rows; this is what turns the grouped-query
-// attention into a real contraction for v_mfma_f32_16x16x32_bf16.  K and V
-// tiles of KT keys are staged through LDS (K row-major with an XOR swizzle,
-// V transposed) with a register prefetch of the next tile; the scores are
-// computed transposed (S^T = K Q^T) so that the probabilities land in the B
-// operand layout of the P.V product without any data movement; the softmax is
-// an online (running max) softmax in base 2.  Key chunks of one (sequence, KV
-// head) are merged by a second kernel when a sequence needs more than one.
+// attention into a real contraction for v_mfma_f32_16x16x32_bf16.  Up to 16
+// query tiles share one work-group, so the key/value bytes of a chunk are read
+// from HBM once.  K and V tiles of KT keys stream into a multi-stage LDS
+// pipeline by asynchronous global->LDS loads (both land XOR-swizzled; V is
+// read transposed by ds_read_b64_tr_b16); the scores are computed transposed (S^T = K Q^T) so
+// that the probabilities land in the B operand layout of the P.V product
+// without any data movement; the softmax is an online (running max) softmax
+// in base 2.  Key chunks of one (sequence, KV head) are merged by a second
+// kernel when a sequence needs more than one.
 //
 // fp32 path: a plain VALU kernel (one work-group per query row and head),
 // used for the tiny fp32 workload.
@@ -28,10 +30,29 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKT = 64;         // keys per LDS tile (bf16 path)
-constexpr int kXcd = 8;         // work-groups are dispatched round-robin over 8 XCDs
-constexpr int kMinChunk = 512;  // keys per work item, lower bound
-constexpr int kTargetWGs = 1024;
+// Tuning constants; the defaults were chosen by measurement on MI355X and can
+// be overridden at build time (-DBD_ATTN_KT=...).
+#ifndef BD_ATTN_KT
+#define BD_ATTN_KT 32
+#endif
+#ifndef BD_ATTN_NS
+#define BD_ATTN_NS 5
+#endif
+#ifndef BD_ATTN_TARGET_WGS
+#define BD_ATTN_TARGET_WGS 512
+#endif
+#ifndef BD_ATTN_MIN_CHUNK
+#define BD_ATTN_MIN_CHUNK 256
+#endif
+#ifndef BD_ATTN_QPW_MAX
+#define BD_ATTN_QPW_MAX 2
+#endif
+constexpr int kKT = BD_ATTN_KT;                 // keys per LDS tile (bf16 path)
+constexpr int kNS = BD_ATTN_NS;                 // pipeline stages (bf16 path)
+constexpr int kXcd = 8;                         // work-groups are dispatched round-robin over 8 XCDs
+constexpr int kMinChunk = BD_ATTN_MIN_CHUNK;    // keys per work item, lower bound
+constexpr int kTargetWGs = BD_ATTN_TARGET_WGS;
+constexpr int kQpwMax = BD_ATTN_QPW_MAX;        // query tiles per wave, at most (1, 2 or 4)
 
 struct AttnK {
   const uint16_t* q;
@@ -49,24 +70,125 @@ struct AttnK {
   float scale_log2;
 };
 
-__device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
-  const uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
+__host__ __device__ constexpr int vm_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+typedef short bd_s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane j receives element
+// j % 4 of the 8-byte pieces addressed by lanes j/4, j/4 + 4, j/4 + 8 and
+// j/4 + 12.  With lanes 4t..4t+3 of a group pointing at four consecutive
+// 8-byte pieces of key row k_t, lane j gets V[k_0..k_3][d0 + j]: four keys of
+// one head-dim column, i.e. a transposed-V MFMA fragment, straight from the
+// row-major tile.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const bd_s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bd_s16x4*)p);
+  return make_uint2((uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
+                    (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16));
 }
 
-template <int DH, int KT, int QPW>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnK a) {
-  constexpr int KCH = DH / 8;         // 16-byte chunks per key row
-  constexpr int VP = KT + 4;          // row pitch (elements) of the transposed V tile
-  constexpr int NKL = KT * KCH / kThreads;
-  constexpr int NVT = (KT / 4) * KCH; // V tasks: 4 keys x 8 head-dim elements
-  constexpr int KS = DH / 32;         // MFMA K-steps over the head dim
-  constexpr int NKT = KT / 16;        // 16-key tiles per LDS tile
-  static_assert(NKL >= 1 && KT * KCH % kThreads == 0, "K tile split");
-  static_assert(NVT <= kThreads, "V tile split");
+// Fragment loads of one 32-key tile at head dim 128, as inline asm that waits
+// for its own results before the block ends.  The compiler cannot tell these
+// LDS reads from the stages still being filled by global_load_lds and would
+// otherwise put an s_waitcnt vmcnt(0) in front of them, draining the load
+// pipeline; the stage read here is complete (explicit vmcnt wait + barrier).
+typedef unsigned int bd_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int bd_u32x2 __attribute__((ext_vector_type(2)));
 
-  __shared__ uint4 sK[2][KT * KCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][DH * VP];
+// kf[kt][ks] = K fragment of 16-key tile kt, head-dim step ks; a[ks] is the
+// LDS byte address of (kt = 0, ks); kt = 1 is 4096 bytes further.
+__device__ __forceinline__ void lds_kfrags_128x32(const uint32_t (&a)[4], uint4 (&kf)[2][4]) {
+  bd_u32x4 r[8];
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %9 offset:4096\n\t"
+      "ds_read_b128 %6, %10 offset:4096\n\t"
+      "ds_read_b128 %7, %11 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kf[i / 4][i % 4] = make_uint4(r[i][0], r[i][1], r[i][2], r[i][3]);
+}
+
+// vf[dt] = transposed V fragment of head-dim tile dt (keys 4g..4g+3 from the
+// read at a[dt], keys 16+4g.. from 4096 bytes further).
+__device__ __forceinline__ void lds_vfrags_128x32(const uint32_t (&a)[8], uint4 (&vf)[8]) {
+  bd_u32x2 r[16];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+        "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) vf[dt] = make_uint4(r[2 * dt][0], r[2 * dt][1], r[2 * dt + 1][0], r[2 * dt + 1][1]);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+typedef __bf16 bd_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float bd_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((bd_f32x2){lo, hi}, bd_bf16x2));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Barrier without __syncthreads()' fences (they would wait for every
+// outstanding global load and drain the pipeline); the kernel waits for what
+// it needs with explicit s_waitcnt first.
+__device__ __forceinline__ void pipe_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Pipeline stage layout (per KT-key tile): the K tile and then the V tile,
+// each as rows of DH/8 16-byte chunks, XOR-swizzled (chunk c of key k at slot
+// k*KCH + (c ^ (k & (KCH-1)))) so that both the K fragment reads and the
+// transposing V reads hit distinct banks.  Both tiles arrive by
+// global_load_lds_dwordx4: instruction i of a tile writes 64 consecutive
+// 16-byte slots, and each lane's global address is chosen so that its slot
+// receives the right chunk.
+template <int DH, int KT, int QPW, int NS>
+__global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_kernel(AttnK a) {
+  constexpr int KCH = DH / 8;             // 16-byte chunks per key row
+  constexpr int TU4 = KT * KCH;           // 16-byte slots per K (or V) tile
+  constexpr int NI = TU4 / 64;            // DMA instructions per K (or V) tile
+  constexpr int LW = 2 * NI / 4;          // DMA instructions per wave per stage
+  constexpr int KS = DH / 32;             // MFMA K-steps over the head dim
+  constexpr int NKT = KT / 16;            // 16-key tiles per LDS tile
+  static_assert(TU4 % 64 == 0 && (2 * NI) % 4 == 0, "tile split");
+  static_assert(NS >= 2 && NS <= 5, "shape");
+
+  __shared__ uint4 sStage[NS][2 * TU4];
 
   // ---- work item (XCD-aware: the query groups of one key chunk share an XCD)
   const int wid = blockIdx.x;
@@ -103,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnK a) {
 
   // ---- this wave's query tiles, Q fragments kept in registers
   bool tact[QPW];
-  int qblk[QPW];
+  int qblk[QPW];  // visibility limit (exclusive) per query row
   uint4 qf[QPW][KS];
   float m_run[QPW], l_run[QPW];
   bd_f32x4 oacc[QPW][DH / 16];
@@ -115,7 +237,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnK a) {
     const bool rok = tact[j] && r < a.R;
     const int i = rok ? r / a.G : 0;
     const int hg = rok ? r % a.G : 0;
-    qblk[j] = rok ? (a.q_off + i) / a.D : INT_MAX;
+    // keys [0, vis_end) of the virtual sequence (cache rows, then in-block
+    // rows) are visible: every cache row and the in-block rows of blocks up
+    // to the query's own
+    qblk[j] = rok ? L + ((a.q_off + i) / a.D + 1) * a.D : INT_MAX;
     const uint16_t* qp = a.q + (((size_t)b * a.n_q + i) * a.Hq + kvh * a.G + hg) * DH;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -128,91 +253,147 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnK a) {
   bool any_active = false;
 #pragma unroll
   for (int j = 0; j < QPW; ++j) any_active |= tact[j];
+  // keys below vis_all are inside the chunk and visible to every row of this
+  // wave (a wave-uniform value)
+  int vis_all = kend;
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) vis_all = min(vis_all, qblk[j]);
+  for (int off = 32; off > 0; off >>= 1) vis_all = min(vis_all, __shfl_xor(vis_all, off));
 
-  // ---- tile loads (registers) and stores (LDS)
-  uint4 kreg[NKL];
-  uint4 vreg[4];
-  auto key_ptr = [&](const uint16_t* cache_bh, const uint16_t* blk_b, int key) -> const uint16_t* {
+  // ---- asynchronous tile loads: this wave issues instructions wave + 4*u of
+  // the stage (the first NI fill K, the next NI fill V)
+  auto key_row = [&](const uint16_t* cache_bh, const uint16_t* blk_b, int key) -> const uint16_t* {
+    key = key < kend ? key : kend - 1;  // rows past the chunk repeat a real row; their scores are masked
     return key < L ? cache_bh + (size_t)key * DH : blk_b + (size_t)(key - L) * blk_stride;
   };
-  auto load_tile = [&](int t) {
+  // per-lane element offset of the chunk this lane fetches, relative to the
+  // first row of a tile (row kk, logical chunk ch), for each instruction
+  int loff[LW];
+#pragma unroll
+  for (int u = 0; u < LW; ++u) {
+    const int ins = wave + 4 * u;
+    const int p = (ins >= NI ? ins - NI : ins) * 64 + lane;
+    const int kk = p / KCH, phys = p % KCH;
+    loff[u] = kk * DH + (phys ^ (kk & (KCH - 1))) * 8;
+  }
+  const int cache_end = min(L, kend);  // tiles below this read only cache rows, none past the chunk
+  auto issue = [&](int t) {
+    uint4* st = sStage[t % NS];
     const int kbase = kbeg + t * KT;
+    if (kbase + KT <= cache_end) {
 #pragma unroll
-    for (int u = 0; u < NKL; ++u) {
-      const int e = tid + kThreads * u;
-      const int key = kbase + e / KCH;
-      kreg[u] = key < kend ? *reinterpret_cast<const uint4*>(key_ptr(kc_bh, kb_b, key) + (e % KCH) * 8)
-                           : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < NVT) {
-      const int kg = tid / KCH, dc = tid % KCH;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = kbase + 4 * kg + jj;
-        vreg[jj] = key < kend ? *reinterpret_cast<const uint4*>(key_ptr(vc_bh, vb_b, key) + dc * 8)
-                              : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < LW; ++u) {
+        const int ins = wave + 4 * u;
+        const uint16_t* base = (ins >= NI ? vc_bh : kc_bh) + (size_t)kbase * DH;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(base + loff[u]),
+                                         (lds_void_t*)(st + (ins >= NI ? TU4 : 0) + (ins >= NI ? ins - NI : ins) * 64),
+                                         16, 0, 0);
       }
-    }
-  };
-  auto store_tile = [&](int sb) {
+    } else {
 #pragma unroll
-    for (int u = 0; u < NKL; ++u) {
-      const int e = tid + kThreads * u;
-      const int kk = e / KCH, ch = e % KCH;
-      sK[sb][kk * KCH + (ch ^ (kk & (KCH - 1)))] = kreg[u];
-    }
-    if (tid < NVT) {
-      const int kg = tid / KCH, dc = tid % KCH;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 pk;
-        pk.x = half16(vreg[0], e) | (half16(vreg[1], e) << 16);
-        pk.y = half16(vreg[2], e) | (half16(vreg[3], e) << 16);
-        *reinterpret_cast<uint2*>(&sV[sb][(dc * 8 + e) * VP + 4 * kg]) = pk;
+      for (int u = 0; u < LW; ++u) {
+        const int ins = wave + 4 * u;
+        const bool isv = ins >= NI;
+        const int kk = loff[u] / DH;
+        const uint16_t* src = isv ? key_row(vc_bh, vb_b, kbase + kk) : key_row(kc_bh, kb_b, kbase + kk);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(src + (loff[u] - kk * DH)),
+                                         (lds_void_t*)(st + (isv ? TU4 : 0) + (isv ? ins - NI : ins) * 64), 16, 0, 0);
       }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // the Q fragments (and every other global load so far) must be in
+  // registers before the pipeline starts, so that no register wait on them
+  // is left for the compiler to place inside the loop
+  __builtin_amdgcn_s_waitcnt(vm_imm(0));
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) issue(t);
 
   for (int t = 0; t < ntiles; ++t) {
-    const int sb = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    const int later = min(ntiles - t - 1, NS - 2);
+    if (later <= 0) __builtin_amdgcn_s_waitcnt(vm_imm(0));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vm_imm(LW));
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(vm_imm(2 * LW));
+    else __builtin_amdgcn_s_waitcnt(vm_imm(3 * LW));
+    pipe_barrier();  // tile t in LDS; every wave is done with tile t - 1
+    if (t + NS - 1 < ntiles) issue(t + NS - 1);
+    const uint4* sK = sStage[t % NS];
+    const uint16_t* sV = reinterpret_cast<const uint16_t*>(sStage[t % NS] + TU4);
     if (any_active) {
       const int kbase = kbeg + t * KT;
       // S^T = K Q^T: lane holds keys 16*kt + 4g + r of query column l16
       bd_f32x4 s[QPW][NKT];
+      constexpr bool kFast = (DH == 128 && KT == 32);
+      uint4 vfr[kFast ? 8 : 1];
+      auto load_vfrags = [&](uint4 (&out)[kFast ? 8 : 1]) {
+        if constexpr (kFast) {
+          uint32_t va[8];
+          const uint32_t vb = lds_addr(sV);
+          const int vrow = 4 * g + (l16 >> 2);
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
+          for (int dt = 0; dt < 8; ++dt)
+            va[dt] = vb + vrow * 256 + ((2 * dt + ((l16 & 3) >> 1)) ^ (vrow & 15)) * 16 + (l16 & 1) * 8;
+          lds_vfrags_128x32(va, out);
+        }
+      };
+      if constexpr (kFast) {
+        uint4 kfr[2][4];
+        uint32_t ka[4];
+        const uint32_t kb = lds_addr(sK);
 #pragma unroll
-        for (int j = 0; j < QPW; ++j) s[j][kt] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
-        const int kk = kt * 16 + l16;
+        for (int ks = 0; ks < 4; ++ks) ka[ks] = kb + (l16 * 16 + ((g + 4 * ks) ^ l16)) * 16;
+        lds_kfrags_128x32(ka, kfr);
+        if constexpr (QPW == 1) load_vfrags(vfr);  // else after the softmax (register pressure)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 kf = sK[sb][kk * KCH + ((g + 4 * ks) ^ (kk & (KCH - 1)))];
+        for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-          for (int j = 0; j < QPW; ++j)
-            if (tact[j]) s[j][kt] = bd_mfma16(kf, qf[j][ks], s[j][kt]);
+          for (int j = 0; j < QPW; ++j) s[j][kt] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < QPW; ++j)
+              s[j][kt] = bd_mfma16(kfr[kt][ks], qf[j][ks], s[j][kt]);
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+          for (int j = 0; j < QPW; ++j) s[j][kt] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+          const int kk = kt * 16 + l16;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const uint4 kf = sK[kk * KCH + ((g + 4 * ks) ^ (kk & (KCH - 1)))];
+#pragma unroll
+            for (int j = 0; j < QPW; ++j)
+              s[j][kt] = bd_mfma16(kf, qf[j][ks], s[j][kt]);
+          }
         }
       }
       // online softmax (base 2), probabilities packed as the B operand of P.V
       uint4 pf[QPW][KT / 32];
 #pragma unroll
       for (int j = 0; j < QPW; ++j) {
-        if (!tact[j]) continue;
         float mx = BD_NEG_INF;
+        if (kbase + KT <= vis_all) {  // whole tile visible to every row: no mask
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
+          for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kbase + kt * 16 + 4 * g + r;
-            const bool vis = key < kend && (key < L || (key - L) / a.D <= qblk[j]);
-            const float v = vis ? s[j][kt][r] * a.scale_log2 : BD_NEG_INF;
-            s[j][kt][r] = v;
-            mx = fmaxf(mx, v);
-          }
+            for (int r = 0; r < 4; ++r) {
+              s[j][kt][r] *= a.scale_log2;
+              mx = fmaxf(mx, s[j][kt][r]);
+            }
+        } else {
+          const int lim = min(kend, qblk[j]);
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = kbase + kt * 16 + 4 * g + r;
+              const float v = key < lim ? s[j][kt][r] * a.scale_log2 : BD_NEG_INF;
+              s[j][kt][r] = v;
+              mx = fmaxf(mx, v);
+            }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -227,35 +408,47 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnK a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const bd_f32x4 sv = s[j][2 * u + h];
-            const uint32_t b0 = bd_f2bf(bd_exp2(sv[0] - muse)), b1 = bd_f2bf(bd_exp2(sv[1] - muse));
-            const uint32_t b2 = bd_f2bf(bd_exp2(sv[2] - muse)), b3 = bd_f2bf(bd_exp2(sv[3] - muse));
-            ps += (bd_bf2f(b0) + bd_bf2f(b1)) + (bd_bf2f(b2) + bd_bf2f(b3));
-            w[2 * h] = b0 | (b1 << 16);
-            w[2 * h + 1] = b2 | (b3 << 16);
+            const float p0 = bd_exp2(sv[0] - muse), p1 = bd_exp2(sv[1] - muse);
+            const float p2 = bd_exp2(sv[2] - muse), p3 = bd_exp2(sv[3] - muse);
+            ps += (p0 + p1) + (p2 + p3);
+            w[2 * h] = cvt_pk_bf16(p0, p1);
+            w[2 * h + 1] = cvt_pk_bf16(p2, p3);
           }
           pf[j][u] = make_uint4(w[0], w[1], w[2], w[3]);
         }
         l_run[j] = l_run[j] * alpha + ps;
+        if (__ballot(alpha != 1.f) != 0) {  // the running max moved for some row
 #pragma unroll
-        for (int dt = 0; dt < DH / 16; ++dt) oacc[j][dt] *= alpha;
+          for (int dt = 0; dt < DH / 16; ++dt) oacc[j][dt] *= alpha;
+        }
       }
       // O^T += V^T P^T: V^T fragment = two 4-key runs of one head-dim row
+      if constexpr (kFast && QPW != 1) load_vfrags(vfr);
+      // lane (g, l16) points at key 32u + 4g + l16/4 (and +16), head dims
+      // 16dt + 4*(l16 % 4) .. +3; it receives keys 32u+4g..+3 (and +16..)
+      // of head dim 16dt + l16, the slot order of the probabilities above
+      const int vrow = 4 * g + (l16 >> 2);
 #pragma unroll
       for (int u = 0; u < KT / 32; ++u) {
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) {
-          const uint16_t* vr = &sV[sb][(dt * 16 + l16) * VP + 32 * u + 4 * g];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-          const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          uint4 vf;
+          if constexpr (kFast) {
+            vf = vfr[dt];
+          } else {
+            const int lch = 2 * dt + ((l16 & 3) >> 1);
+            const int half = (l16 & 1) * 4;
+            const int r0 = 32 * u + vrow, r1 = r0 + 16;
+            const uint2 lo = lds_read_tr16(sV + r0 * DH + (lch ^ (r0 & (KCH - 1))) * 8 + half);
+            const uint2 hi = lds_read_tr16(sV + r1 * DH + (lch ^ (r1 & (KCH - 1))) * 8 + half);
+            vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          }
 #pragma unroll
           for (int j = 0; j < QPW; ++j)
-            if (tact[j]) oacc[j][dt] = bd_mfma16(vf, pf[j][u], oacc[j][dt]);
+            oacc[j][dt] = bd_mfma16(vf, pf[j][u], oacc[j][dt]);
         }
       }
     }
-    if (t + 1 < ntiles) store_tile(sb ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: normalised output (single chunk) or partials
@@ -274,8 +467,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnK a) {
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt) {
         const bd_f32x4 v = oacc[j][dt] * inv;
-        *reinterpret_cast<uint2*>(op + dt * 16 + 4 * g) =
-            make_uint2(bd_pack_bf2(v[0], v[1]), bd_pack_bf2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(op + dt * 16 + 4 * g) = make_uint2(cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3]));
       }
       if (a.lse != nullptr && g == 0)
         a.lse[((size_t)b * a.Hq + kvh * a.G + hg) * a.n_q + i] = (m_run[j] + bd_log2(l)) * BD_LN2;
@@ -420,7 +612,8 @@ BdAttnPlan bd_attn_plan(bd_dtype dt, int B, int Hq, int Hkv, int d, int n_q, int
   const int G = Hq / Hkv;
   p.R = n_q * G;
   p.QT = (p.R + 15) / 16;
-  p.qpw = 1;
+  p.qpw = p.QT <= 4 ? 1 : (p.QT <= 8 ? 2 : 4);
+  p.qpw = p.qpw > kQpwMax ? kQpwMax : p.qpw;
   p.nqg = (p.QT + 4 * p.qpw - 1) / (4 * p.qpw);
   const int tmax = cap + n_blk;
   if (dt == BD_F32) {
@@ -471,10 +664,26 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
   a.n_units = x.B * x.Hkv * p.nchunks;
   a.scale_log2 = x.scale * BD_LOG2E;
   const int n_wg = kXcd * a.nqg * ((a.n_units + kXcd - 1) / kXcd);
-  if (x.d == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, kKT, 1>), dim3(n_wg), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<64, kKT, 1>), dim3(n_wg), dim3(kThreads), 0, s, a);
+#define BD_ATTN_LAUNCH(DH, QPW) \
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS>), dim3(n_wg), dim3(kThreads), 0, s, a)
+  if (x.d == 128) {
+    if (p.qpw == 1) BD_ATTN_LAUNCH(128, 1);
+#if BD_ATTN_QPW_MAX >= 2
+    else if (p.qpw == 2) BD_ATTN_LAUNCH(128, 2);
+#endif
+#if BD_ATTN_QPW_MAX >= 4
+    else BD_ATTN_LAUNCH(128, 4);
+#endif
+  } else {
+    if (p.qpw == 1) BD_ATTN_LAUNCH(64, 1);
+#if BD_ATTN_QPW_MAX >= 2
+    else if (p.qpw == 2) BD_ATTN_LAUNCH(64, 2);
+#endif
+#if BD_ATTN_QPW_MAX >= 4
+    else BD_ATTN_LAUNCH(64, 4);
+#endif
+  }
+#undef BD_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nchunks == 1) return e;
   const size_t total = (size_t)x.B * x.Hkv * p.R * (x.d / 4);

@@ -82,8 +82,7 @@ struct BdGemmPlan {
   int MT;                 // 16-row tiles per work-group
   int nx, ny;             // column tiles (all segments) and row tiles
   int ksplit;             // K slices per tile
-  size_t counters_bytes;  // workspace: arrival counters, then fp32 partial tiles
-  size_t ws_bytes;
+  size_t ws_bytes;        // workspace: fp32 partial tiles [tile][slice][rows x 64]
 };
 
 BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg);

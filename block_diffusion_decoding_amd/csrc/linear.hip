@@ -17,18 +17,22 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNTW = 4;        // 16-column tiles per work-group (64 columns)
-constexpr int kKSC = 2;        // 32-wide k-steps per pipeline stage
-constexpr int kNS = 3;         // pipeline stages
+// Tiling; defaults chosen by measurement, overridable at build time.
+#ifndef BD_GEMM_NTW
+#define BD_GEMM_NTW 4
+#endif
+#ifndef BD_GEMM_TARGET_WGS
+#define BD_GEMM_TARGET_WGS 512
+#endif
+#ifndef BD_GEMM_MIN_CHUNKS
+#define BD_GEMM_MIN_CHUNKS 4
+#endif
+constexpr int kNTW = BD_GEMM_NTW;        // 16-column tiles per work-group
+constexpr int kKSC = 2;                  // 32-wide k-steps per pipeline stage
+constexpr int kNS = 3;                   // pipeline stages
 constexpr int kMaxSeg = 3;
-constexpr int kTargetWGs = 512;
-constexpr int kMinChunksPerSplit = 4;
-// Arrival counters occupy a fixed region at the start of every GEMM workspace
-// (one int per tile, at most kMaxTiles tiles), so that calls with different
-// tilings can share one workspace: a call's partial sums never overlap the
-// counters of another call, and every counter is back at zero when a call ends.
-constexpr int kMaxTiles = 16384;
-constexpr size_t kCounterBytes = kMaxTiles * sizeof(int);
+constexpr int kTargetWGs = BD_GEMM_TARGET_WGS;
+constexpr int kMinChunksPerSplit = BD_GEMM_MIN_CHUNKS;
 
 struct GemmK {
   const uint16_t* x;
@@ -43,7 +47,6 @@ struct GemmK {
   int wg_begin[kMaxSeg + 1];
   int ksplit;
   float* part;    // [tiles][ksplit][MT*16 x 64] fp32 partial sums (ksplit > 1)
-  int* counters;  // [tiles] arrival counters, zero between calls
 };
 
 __device__ __forceinline__ void gemm_store(const GemmK& a, int seg, int m, int col, float v) {
@@ -53,14 +56,14 @@ __device__ __forceinline__ void gemm_store(const GemmK& a, int seg, int m, int c
 }
 
 // One (column tile, row tile, K slice) per work-group.  With a K split the
-// slices write fp32 partial tiles; the last slice to arrive (arrival counter)
-// adds them in slice order, so the result does not depend on timing.
+// slices write fp32 partial tiles that gemm_reduce_kernel adds in slice order
+// (a separate launch: cross-XCD visibility inside one kernel would need
+// device-scope fences, i.e. L2 write-backs, per work-group).
 template <int MT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
   using C = bd_stream::Cfg<MT, kNTW, kKSC, kNS>;
   constexpr int TILE = MT * 16 * kNTW * 16;
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
-  __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int wm = wave % C::WM, wn = wave / C::WM;
@@ -97,21 +100,36 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       pt[(wm * 16 + 4 * g + r) * (kNTW * 16) + (wn * C::NTP + j) * 16 + l16] = acc[j][r];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[tile], 1) == a.ksplit - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* p0 = a.part + (size_t)tile * a.ksplit * TILE;
-  for (int e = tid; e < TILE; e += kThreads) {
+}
+
+// Adds the K slices of every tile in slice order, then residual and store.
+template <int MT>
+__global__ __launch_bounds__(kThreads) void gemm_reduce_kernel(GemmK a) {
+  constexpr int TILE = MT * 16 * kNTW * 16;
+  const int bx = blockIdx.x;
+  const int seg = (a.nseg > 2 && bx >= a.wg_begin[2]) ? 2 : (a.nseg > 1 && bx >= a.wg_begin[1]) ? 1 : 0;
+  const int N = a.N[seg];
+  const int n0 = (bx - a.wg_begin[seg]) * kNTW * 16;
+  const int m0 = blockIdx.y * MT * 16;
+  const float* p0 = a.part + (size_t)(blockIdx.y * gridDim.x + bx) * a.ksplit * TILE;
+  // blockIdx.z: which 16-row group of the tile this work-group adds
+  for (int e = blockIdx.z * 16 * kNTW * 16 + threadIdx.x * 4; e < (blockIdx.z + 1) * 16 * kNTW * 16;
+       e += kThreads * 4) {
     const int m = m0 + e / (kNTW * 16), col = n0 + e % (kNTW * 16);
-    if (m >= a.M || col >= N) continue;
-    float v = 0.f;
-    for (int zz = 0; zz < a.ksplit; ++zz) v += p0[(size_t)zz * TILE + e];
-    gemm_store(a, seg, m, col, v);
+    if (m >= a.M) break;
+    float4 v = *reinterpret_cast<const float4*>(p0 + e);
+    for (int zz = 1; zz < a.ksplit; ++zz) {
+      const float4 w = *reinterpret_cast<const float4*>(p0 + (size_t)zz * TILE + e);
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (col + u < N) gemm_store(a, seg, m, col + u, vv[u]);
   }
-  if (tid == 0) a.counters[tile] = 0;
 }
 
 struct GemmF {
@@ -199,12 +217,7 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg) {
   const int maxks = nch / kMinChunksPerSplit;
   ks = ks > maxks ? maxks : ks;
   p.ksplit = ks < 1 ? 1 : ks;
-  const size_t tiles = (size_t)p.nx * p.ny;
-  if (tiles > (size_t)kMaxTiles) p.ksplit = 1;
-  if (p.ksplit > 1) {
-    p.counters_bytes = kCounterBytes;
-    p.ws_bytes = kCounterBytes + tiles * p.ksplit * p.MT * 16 * kNTW * 16 * sizeof(float);
-  }
+  if (p.ksplit > 1) p.ws_bytes = (size_t)p.nx * p.ny * p.ksplit * p.MT * 16 * kNTW * 16 * sizeof(float);
   return p;
 }
 
@@ -241,13 +254,20 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
   }
   for (int i = nseg; i <= kMaxSeg; ++i) a.wg_begin[i] = wg;
   a.ksplit = p.ksplit;
-  a.counters = p.ksplit > 1 ? static_cast<int*>(workspace) : nullptr;
-  a.part = p.ksplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.counters_bytes) : nullptr;
+  a.part = p.ksplit > 1 ? static_cast<float*>(workspace) : nullptr;
   const dim3 grid(wg, p.ny, p.ksplit);
   switch (p.MT) {
     case 1: hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
     default: hipLaunchKernelGGL(gemm_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.ksplit == 1) return e;
+  const dim3 rgrid(wg, p.ny, p.MT);
+  switch (p.MT) {
+    case 1: hipLaunchKernelGGL(gemm_reduce_kernel<1>, rgrid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(gemm_reduce_kernel<2>, rgrid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(gemm_reduce_kernel<4>, rgrid, dim3(kThreads), 0, s, a); break;
   }
   return hipGetLastError();
 }

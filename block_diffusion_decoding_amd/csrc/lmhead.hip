@@ -25,9 +25,19 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNTW = 8;       // 16-column tiles per work-group (bf16)
-constexpr int kKSC = 2;       // 32-wide k-steps per pipeline stage (bf16)
-constexpr int kNS = 3;        // pipeline stages (bf16)
+// bf16 tiling; defaults chosen by measurement, overridable at build time.
+#ifndef BD_LM_NTW
+#define BD_LM_NTW 8
+#endif
+#ifndef BD_LM_KSC
+#define BD_LM_KSC 2
+#endif
+#ifndef BD_LM_NS
+#define BD_LM_NS 3
+#endif
+constexpr int kNTW = BD_LM_NTW;  // 16-column tiles per work-group (bf16)
+constexpr int kKSC = BD_LM_KSC;  // 32-wide k-steps per pipeline stage (bf16)
+constexpr int kNS = BD_LM_NS;    // pipeline stages (bf16)
 constexpr int kF32Rows = 16;  // rows per work-group (fp32)
 
 struct LmK {

@@ -205,9 +205,8 @@ bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int 
  * w is [N, K] row-major.  bf16 uses MFMA with fp32 accumulation and needs
  * K % 256 == 0; when the column tiles alone cannot fill the GPU, K is split
  * over work-groups and the slices are added in a fixed order through the
- * workspace (bd_linear_workspace_size; 0 means none is needed).  Its first
- * 64 KiB hold arrival counters that every call leaves at zero, so one
- * workspace may serve every bd_linear / bd_qkv_proj call on a stream. */
+ * workspace (bd_linear_workspace_size; 0 means none is needed) by a second
+ * kernel of the same call. */
 size_t bd_linear_workspace_size(bd_dtype dt, int M, int N, int K);
 bd_status bd_linear(bd_dtype dt, int M, int N, int K,
                     const void* x, bd_rows xr, const void* w,
