@@ -487,43 +487,50 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_kernel
 }
 
 // Merge the key chunks of every (sequence, KV head) whose keys span more than
-// one chunk: o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// one chunk: o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.  One wave per
+// query row; lane e holds head dims DH/64 * e .. (a 512-byte row per chunk).
 template <int DH>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnK a) {
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  const size_t total = (size_t)a.B * a.Hkv * a.R * (DH / 4);
-  if (idx >= total) return;
-  const int d4 = idx % (DH / 4);
-  const int r = (idx / (DH / 4)) % a.R;
-  const int bh = (int)(idx / (DH / 4) / a.R);
+  constexpr int PER = DH / 64;  // head dims per lane
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (size_t)a.B * a.Hkv * a.R) return;
+  const int r = (int)(row % a.R);
+  const int bh = (int)(row / a.R);
   const int b = bh / a.Hkv, kvh = bh % a.Hkv;
   int L = a.kv_len[b];
   L = L < 0 ? 0 : (L > a.cap ? a.cap : L);
-  const int T = L + a.n_blk;
-  const int nc = (T + a.chunk - 1) / a.chunk;
+  const int nc = (L + a.n_blk + a.chunk - 1) / a.chunk;
   if (nc <= 1) return;
   const size_t rp = (size_t)a.QT * 16;
   float M = BD_NEG_INF;
   for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[2 * (((size_t)bh * a.nchunks + c) * rp + r)]);
   const float muse = (M == BD_NEG_INF) ? 0.f : M;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float lsum = 0.f;
   for (int c = 0; c < nc; ++c) {
     const size_t pi = ((size_t)bh * a.nchunks + c) * rp + r;
     const float w = bd_exp2(a.part_ml[2 * pi] - muse);
     lsum += w * a.part_ml[2 * pi + 1];
-    const float4 v = *reinterpret_cast<const float4*>(a.part_o + pi * DH + 4 * d4);
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+    const float* po = a.part_o + pi * DH + PER * lane;
+    if constexpr (PER == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(po);
+      acc[0] += w * v.x;
+      acc[1] += w * v.y;
+    } else {
+      acc[0] += w * po[0];
+    }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int i = r / a.G, hg = r % a.G;
-  uint16_t* op = a.o + (((size_t)b * a.n_q + i) * a.Hq + kvh * a.G + hg) * DH + 4 * d4;
-  *reinterpret_cast<uint2*>(op) = make_uint2(bd_pack_bf2(acc.x * inv, acc.y * inv),
-                                             bd_pack_bf2(acc.z * inv, acc.w * inv));
-  if (a.lse != nullptr && d4 == 0)
+  uint16_t* op = a.o + (((size_t)b * a.n_q + i) * a.Hq + kvh * a.G + hg) * DH + PER * lane;
+  if constexpr (PER == 2)
+    *reinterpret_cast<uint32_t*>(op) = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
+  else
+    op[0] = (uint16_t)(cvt_pk_bf16(acc[0] * inv, 0.f) & 0xffffu);
+  if (a.lse != nullptr && lane == 0)
     a.lse[((size_t)b * a.Hq + kvh * a.G + hg) * a.n_q + i] = (M + bd_log2(lsum)) * BD_LN2;
 }
 
@@ -686,8 +693,8 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
 #undef BD_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nchunks == 1) return e;
-  const size_t total = (size_t)x.B * x.Hkv * p.R * (x.d / 4);
-  const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
+  const size_t rows = (size_t)x.B * x.Hkv * p.R;
+  const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64)));
   if (x.d == 128)
     hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(kThreads), 0, s, a);
   else
