@@ -24,7 +24,8 @@ Also measured in the same run (reported under "extra"):
 
 roofline: the dominant kernel of the headline step is the LM head (its
 weights are ~92% of the step's bytes); its launches are timed with HIP events
-on the launch stream inside the timed region.
+on the launch stream, over a second timed pass of the same loop with eager
+launches (the headline pass replays each step as a captured HIP graph).
 cpu_baseline: the fp64 oracle (oracle/), timed on this host on a bounded
 sample of the same workload (DualCache steps of the same 8 sequences).
 """
@@ -262,6 +263,7 @@ def main():
     ap.add_argument("--rate", type=float, default=0.5, help="planted pass rate of masked rows")
     ap.add_argument("--reps", type=int, default=20, help="repetitions of the single-call measurements")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-graphs", action="store_true", help="launch every step's kernels eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     args = ap.parse_args()
@@ -282,26 +284,40 @@ def main():
     n_blocks = 8
     dec = make_decoder(cfg, w, pre)
     plants = block_plants(cfg, w, args.rate, 0, n_blocks)
+    if not args.no_graphs:
+        dec.capture(cfg.S, cfg.tau)
     loop = Loop(dec, cfg, plants)
     for _ in range(args.warmup):
         loop.step()
     torch.cuda.synchronize()
-    # timed region
+    # timed region: the headline loop (captured steps replayed as HIP graphs)
     s0, t0_tok, c0 = loop.steps, loop.tokens, loop.commits
-    dec.lm_events = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         loop.step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    lm_t = np.array([a.elapsed_time(b) for a, b in dec.lm_events]) * 1e-3
-    dec.lm_events = None
     steps = loop.steps - s0
     tokens = loop.tokens - t0_tok
     steps_per_s = steps / elapsed
     log(f"[bench] {steps} steps in {elapsed * 1e3:.1f} ms: {steps_per_s:.1f} steps/s, "
-        f"{tokens / elapsed:.0f} tokens/s, {loop.commits - c0} commits, LM head {lm_t.mean() * 1e6:.1f} us")
+        f"{tokens / elapsed:.0f} tokens/s, {loop.commits - c0} commits")
+    # second timed pass of the same loop with eager launches and HIP events
+    # around every LM-head launch (a kernel inside a graph replay cannot be
+    # timed by events): the dominant kernel's launch durations
+    dec.lm_events = []
+    s1 = loop.steps
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        loop.step()
+    torch.cuda.synchronize()
+    elapsed_eager = time.perf_counter() - t1
+    lm_t = np.array([a.elapsed_time(b) for a, b in dec.lm_events]) * 1e-3
+    dec.lm_events = None
+    log(f"[bench] eager pass: {(loop.steps - s1) / elapsed_eager:.1f} steps/s, LM head {lm_t.mean() * 1e6:.1f} us "
+        f"over {len(lm_t)} launches")
 
     # roofline of the dominant kernel: LM head of the 7B step (B*S = 64 rows)
     M = cfg.B * cfg.S
@@ -318,7 +334,9 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "bd_lmhead_confidence (lm_bf16_kernel<4> + lm_merge_kernel), 64 rows x 152064 x 3584",
                 "algorithmic_bytes": lm_bytes, "launch_us_mean": round(lm_mean * 1e6, 2),
-                "launch_us_median": round(float(np.median(lm_t)) * 1e6, 2)}
+                "launch_us_median": round(float(np.median(lm_t)) * 1e6, 2),
+                "timing": f"HIP events around each of {len(lm_t)} LM-head launches of a second timed pass of "
+                          "the same loop (eager launches) on the launch stream"}
     extra = {}
     if not args.no_extras:
         del dec
@@ -339,6 +357,8 @@ def main():
                    "global_batch": cfg.B, "block": cfg.D, "sub_block": cfg.S, "threshold": cfg.tau},
         "decoded_tokens_per_s": round(tokens / elapsed, 1),
         "tokens_per_step": round(tokens / steps, 3),
+        "graphs": not args.no_graphs,
+        "ms_per_step_eager": round(elapsed_eager / args.steps * 1e3, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

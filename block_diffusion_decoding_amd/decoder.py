@@ -56,7 +56,6 @@ class BlockDecoder:
         self.device = torch.device(device)
         dev, dt = self.device, dtype
         B, D, Hq, Hkv, d, hid = dims.B, dims.D, dims.Hq, dims.Hkv, dims.d, dims.hidden
-        assert Hq * d == hid or True
         self.W = {k: v.to(dev, dt).contiguous() for k, v in weights.items()}
         assert self.W["E"].shape == (dims.V + 1, hid)
         self.cache_k = torch.zeros(B, Hkv, dims.cap, d, dtype=dt, device=dev)
@@ -76,6 +75,7 @@ class BlockDecoder:
         self._win = {}
         self.last = None
         self.lm_events = None   # list of (start, end) events around LM-head calls when set
+        self.graphs = {}        # (kind, s) -> captured HIP graph of that step
 
     # ------------------------------------------------------------------ state
     def set_synthetic_prefix(self, kv_len, cache_k, cache_v, carry):
@@ -102,7 +102,17 @@ class BlockDecoder:
         """Current block: tokens [B, D], masked [B, D] bool, optional plant
         [B, D, hidden] (offset on the block's input rows) and carry offset."""
         self.set_tokens(tokens, masked)
-        self.plant = None if plant is None else torch.as_tensor(plant).to(self.device, self.dtype).contiguous()
+        if plant is None:
+            if self.graphs:
+                self.plant.zero_()   # captured steps read the persistent plant buffer
+            else:
+                self.plant = None
+        else:
+            src = torch.as_tensor(plant).to(self.device, self.dtype)
+            if self.plant is None:
+                self.plant = src.contiguous().clone()
+            else:
+                self.plant.copy_(src)
         if carry_offset is not None:
             self.H[:, 0] += torch.as_tensor(carry_offset).to(self.device, self.dtype)
 
@@ -162,8 +172,10 @@ class BlockDecoder:
                                 threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
         self.last = w
 
-    def e_step(self, s: int, S: int, tau: float):
+    def e_step(self, s: int, S: int, tau: float, eager: bool = False):
         """Exact step for window s; refreshes the DualCache snapshot."""
+        if not eager and self._replay("E", s, S, tau):
+            return
         dm = self.dims
         B, D = dm.B, dm.D
         X, o = self._forward_rows(0, D)
@@ -171,8 +183,10 @@ class BlockDecoder:
                       res=X, rr=dense(B * D))
         self._lm_and_unmask(s, S, tau)
 
-    def dc_step(self, s: int, S: int, tau: float):
+    def dc_step(self, s: int, S: int, tau: float, eager: bool = False):
         """DualCache step for window s (snapshot rows outside the window)."""
+        if not eager and self._replay("DC", s, S, tau):
+            return
         dm = self.dims
         B, D = dm.B, dm.D
         X, o = self._forward_rows(s * S, S)
@@ -180,15 +194,22 @@ class BlockDecoder:
                       res=X, rr=dense(B * S))
         self._lm_and_unmask(s, S, tau)
 
-    def commit(self, check_capacity: bool = True):
-        """Forward over the finished block, append its K/V, keep the carry."""
+    def _commit_kernels(self):
         dm = self.dims
         B, D = dm.B, dm.D
         X, o = self._forward_rows(0, D)
         ops.bd_linear(o, rows(1, D, D - 1), self.W["Wo"], self.H, rows(1, 1 + D, 0), M=B,
                       res=X, rr=rows(1, D, D - 1))
-        ops.bd_kv_append(self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, n_rows=D,
-                         kv_len_host=self.kv_len_host if check_capacity else None)
+        ops.bd_kv_append(self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, n_rows=self.dims.D)
+
+    def commit(self, check_capacity: bool = True):
+        """Forward over the finished block, append its K/V, keep the carry.
+        The capacity is checked on the host mirror of the lengths first."""
+        D = self.dims.D
+        if check_capacity and np.any(self.kv_len_host + D > self.dims.cap):
+            raise ops.BdError("bd_kv_append", 3)
+        if not self._replay("commit", 0, 0, 0.0):
+            self._commit_kernels()
         self.kv_len_host = self.kv_len_host + D
 
     def prefill(self, prompt):
@@ -217,6 +238,52 @@ class BlockDecoder:
         self.kv_len_host = np.zeros(B, dtype=np.int32)
         ops.bd_kv_append(self.cache_k, self.cache_v, self.kv_len, pk, pv, n_rows=P, kv_len_host=self.kv_len_host)
         self.kv_len_host = self.kv_len_host + P
+
+    # ---------------------------------------------------------------- graphs
+    def capture(self, S: int, tau: float):
+        """Capture the exact and DualCache step of every window and the commit
+        as HIP graphs (through torch's graph API).  Every buffer and workspace
+        the steps touch is sized first, so replays allocate nothing; a plant
+        buffer always exists (zeros when nothing is planted)."""
+        dm = self.dims
+        B, D = dm.B, dm.D
+        if self.plant is None:
+            self.plant = torch.zeros(B, D, dm.hidden, dtype=self.dtype, device=self.device)
+        dt = self.dtype
+        need = {"attn": max(ops.bd_block_attn_workspace_size(dt, B, dm.Hq, dm.Hkv, dm.d, n, dm.cap, D)
+                            for n in (S, D)),
+                "lm": ops.bd_lmhead_workspace_size(dt, B * S, dm.hidden, dm.V),
+                "gemm": max([ops.bd_qkv_proj_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d, dm.Hkv * dm.d)
+                             for M in (B * S, B * D)] +
+                            [ops.bd_linear_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d) for M in (B, B * S, B * D)])}
+        for tag, n in need.items():
+            ops.workspace(n, self.device, tag)
+        for s in range(D // S):
+            self._window(s, S)
+        torch.cuda.synchronize()
+        self.graphs = {}
+        for s in range(D // S):
+            for kind, fn in (("E", self.e_step), ("DC", self.dc_step)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn(s, S, tau, eager=True)
+                self.graphs[(kind, s)] = g
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self._commit_kernels()
+        self.graphs[("commit", 0)] = g
+        self._graph_S, self._graph_tau = S, tau
+        torch.cuda.synchronize()
+
+    def _replay(self, kind: str, s: int, S: int, tau: float) -> bool:
+        g = self.graphs.get((kind, s))
+        if g is None or self.lm_events is not None or (kind != "commit" and
+                                                        (S, tau) != (self._graph_S, self._graph_tau)):
+            return False
+        g.replay()
+        if kind != "commit":
+            self.last = self._window(s, S)
+        return True
 
     # ------------------------------------------------------------------ loop
     def decode_block(self, S: int, tau: float, mode: str = "dual", steps_per_window: int | None = None,

@@ -153,6 +153,14 @@ def bd_embed_rows(E, tokens, mask_bits, x, *, row_off, n_rows, plant=None, strea
     _check("bd_embed_rows", st)
 
 
+def bd_linear_workspace_size(dtype, M, N, K) -> int:
+    return int(_lib.load().bd_linear_workspace_size(_DT[dtype], M, N, K))
+
+
+def bd_qkv_proj_workspace_size(dtype, M, K, Nq, Nkv) -> int:
+    return int(_lib.load().bd_qkv_proj_workspace_size(_DT[dtype], M, K, Nq, Nkv))
+
+
 def bd_linear(x, xr, w, y, yr, *, M, res=None, rr=None, ws=None, stream=None):
     """y[yr(m)] = x[xr(m)] w^T (+ res[rr(m)]); w [N, K]."""
     lib = _lib.load()
