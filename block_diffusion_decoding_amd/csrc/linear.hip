@@ -28,7 +28,6 @@ constexpr int kThreads = 256;
 #define BD_GEMM_MIN_CHUNKS 4
 #endif
 constexpr int kNTW = BD_GEMM_NTW;        // 16-column tiles per work-group
-constexpr int kKSC = 2;                  // 32-wide k-steps per pipeline stage
 constexpr int kNS = 3;                   // pipeline stages
 constexpr int kMaxSeg = 3;
 constexpr int kTargetWGs = BD_GEMM_TARGET_WGS;
@@ -61,7 +60,7 @@ __device__ __forceinline__ void gemm_store(const GemmK& a, int seg, int m, int c
 // device-scope fences, i.e. L2 write-backs, per work-group).
 template <int MT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
-  using C = bd_stream::Cfg<MT, kNTW, kKSC, kNS>;
+  using C = bd_stream::Cfg<MT, kNTW, kNS>;
   constexpr int TILE = MT * 16 * kNTW * 16;
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -79,27 +78,31 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
   auto xrow = [&](int m) -> const uint16_t* {
     return m < a.M ? a.x + (size_t)bd_map_row(a.xr, m) * a.K : nullptr;
   };
-  bd_f32x4 acc[C::NTP];
+  bd_f32x4 acc[C::MTW][C::NTP];
   bd_stream::mainloop<C>(xrow, a.x, m0, a.w[seg], N, a.K, n0, sbuf, acc, c0 * C::KC, c1 - c0);
 
   if (a.ksplit == 1) {
 #pragma unroll
-    for (int j = 0; j < C::NTP; ++j)
+    for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 16 + 4 * g + r;
-        const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-        if (m < a.M && col < N) gemm_store(a, seg, m, col, acc[j][r]);
-      }
+      for (int j = 0; j < C::NTP; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+          const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+          if (m < a.M && col < N) gemm_store(a, seg, m, col, acc[i][j][r]);
+        }
     return;
   }
   const int tile = blockIdx.y * gridDim.x + bx;
   float* pt = a.part + ((size_t)tile * a.ksplit + z) * TILE;
 #pragma unroll
-  for (int j = 0; j < C::NTP; ++j)
+  for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      pt[(wm * 16 + 4 * g + r) * (kNTW * 16) + (wn * C::NTP + j) * 16 + l16] = acc[j][r];
+    for (int j = 0; j < C::NTP; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        pt[((wm * C::MTW + i) * 16 + 4 * g + r) * (kNTW * 16) + (wn * C::NTP + j) * 16 + l16] = acc[i][j][r];
 }
 
 // Adds the K slices of every tile in slice order, then residual and store.
@@ -211,7 +214,7 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg) {
   p.nx = 0;
   for (int i = 0; i < nseg; ++i) p.nx += (N[i] + kNTW * 16 - 1) / (kNTW * 16);
   p.ny = (M + p.MT * 16 - 1) / (p.MT * 16);
-  const int nch = K / (kKSC * 32);
+  const int nch = K / 64;
   const long base = (long)p.nx * p.ny;
   int ks = (int)((kTargetWGs + base - 1) / base);
   const int maxks = nch / kMinChunksPerSplit;

@@ -29,14 +29,10 @@ constexpr int kThreads = 256;
 #ifndef BD_LM_NTW
 #define BD_LM_NTW 8
 #endif
-#ifndef BD_LM_KSC
-#define BD_LM_KSC 2
-#endif
 #ifndef BD_LM_NS
 #define BD_LM_NS 3
 #endif
 constexpr int kNTW = BD_LM_NTW;  // 16-column tiles per work-group (bf16)
-constexpr int kKSC = BD_LM_KSC;  // 32-wide k-steps per pipeline stage (bf16)
 constexpr int kNS = BD_LM_NS;    // pipeline stages (bf16)
 constexpr int kF32Rows = 16;  // rows per work-group (fp32)
 
@@ -61,7 +57,7 @@ __device__ __forceinline__ const uint16_t* lm_row(const LmK& a, int m) {
 
 template <int MT>
 __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
-  using C = bd_stream::Cfg<MT, kNTW, kKSC, kNS>;
+  using C = bd_stream::Cfg<MT, kNTW, kNS>;
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -69,42 +65,45 @@ __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
   const int m0 = blockIdx.y * MT * 16;
   const int n0 = blockIdx.x * kNTW * 16;
 
-  bd_f32x4 acc[C::NTP];
+  bd_f32x4 acc[C::MTW][C::NTP];
   auto xrow = [&](int m) { return lm_row(a, m); };
   bd_stream::mainloop<C>(xrow, a.h, m0, a.w, a.V, a.hidden, n0, sbuf, acc);
 
-  // rows m0 + wm*16 + 4g + r, columns n0 + (wn*NTP + j)*16 + l16
+  // rows m0 + (wm*MTW + i)*16 + 4g + r, columns n0 + (wn*NTP + j)*16 + l16
   BdArgStat* red = reinterpret_cast<BdArgStat*>(sbuf);  // [WN][MT*16]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int rl = wm * 16 + 4 * g + r;
-    BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
+  for (int i = 0; i < C::MTW; ++i) {
 #pragma unroll
-    for (int j = 0; j < C::NTP; ++j) {
-      const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-      const float v = acc[j][r];
-      if (col < a.V && v > st.m) {
-        st.m = v;
-        st.i = col;
-      }
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < C::NTP; ++j) {
-      const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-      if (col < a.V) s += bd_exp2((acc[j][r] - st.m) * BD_LOG2E);
-    }
-    st.s = s;
-    if (a.logits != nullptr && m0 + rl < a.M) {
+    for (int r = 0; r < 4; ++r) {
+      const int rl = (wm * C::MTW + i) * 16 + 4 * g + r;
+      BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
 #pragma unroll
       for (int j = 0; j < C::NTP; ++j) {
         const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-        if (col < a.V) a.logits[(size_t)(m0 + rl) * a.V + col] = acc[j][r];
+        const float v = acc[i][j][r];
+        if (col < a.V && v > st.m) {
+          st.m = v;
+          st.i = col;
+        }
       }
-    }
+      float s = 0.f;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
-    if (l16 == 0) red[wn * (MT * 16) + rl] = st;
+      for (int j = 0; j < C::NTP; ++j) {
+        const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+        if (col < a.V) s += bd_exp2((acc[i][j][r] - st.m) * BD_LOG2E);
+      }
+      st.s = s;
+      if (a.logits != nullptr && m0 + rl < a.M) {
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j) {
+          const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+          if (col < a.V) a.logits[(size_t)(m0 + rl) * a.V + col] = acc[i][j][r];
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
+      if (l16 == 0) red[wn * (MT * 16) + rl] = st;
+    }
   }
   __syncthreads();
   if (tid < MT * 16 && m0 + tid < a.M) {

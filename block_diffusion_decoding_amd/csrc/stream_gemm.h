@@ -3,18 +3,26 @@
 // long weight matrix W [N, K] that is read exactly once from HBM.
 //
 // A work-group (4 waves) owns MT*16 rows (MT in {1, 2, 4}) and NTW*16
-// columns.  K is walked in chunks of KSC*32.  Every chunk is one pipeline
-// stage in LDS holding, in v_mfma_f32_16x16x32_bf16 fragment order, the W
-// fragments of all NTW column tiles and the X fragments of all MT row tiles;
-// one fragment is 1 KiB = one global_load_lds_dwordx4 per wave (lane l's 16
-// bytes land at base + 16*l), so the loads go from HBM/L2 straight into LDS
-// without passing through registers and NS stages are in flight at once.
-// Waves split the rows first (wave -> row tile) and the columns second, so a
-// W fragment in LDS is read by MT waves and an X fragment by 4/MT waves.
+// columns.  K is walked in chunks of 64; every chunk is one pipeline stage in
+// LDS holding the NTW column tiles of W and the MT row tiles of X, each tile
+// 16 rows x 64 k = 2 KiB.  The tiles arrive by global->LDS DMA
+// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), NS stages
+// in flight, without passing through registers.
 //
-// K slots: in k-step ks of a chunk, lane group g = lane / 16 supplies
-// k = chunk*KSC*32 + 32*ks + 8*g .. +7 for both operands (any common
-// permutation of the K slots leaves the product unchanged).
+// Load shape: one DMA instruction covers 8 rows x 128 B, i.e. whole 128-byte
+// lines; a 16-row tile is two instructions.  (Sixteen rows x 64 B per
+// instruction, the MFMA fragment shape, touches twice as many lines and
+// measured about 3x slower for L2-resident rows, which is what the shared X
+// rows of every work-group are.)  Lane l of an instruction loads row l/8 and
+// 16-byte k-block (l%8) ^ (l/8), so LDS slot 8r+p holds k-block p^r of row r:
+// the XOR swizzle makes the fragment reads below conflict-free.
+//
+// MFMA v_mfma_f32_16x16x32_bf16: in k-step ks (0, 1) of a chunk, lane L
+// supplies row L%16 and k-block 4*ks + L/16 of its tile, read with one
+// ds_read_b128 at a per-lane offset.  A wave computes MTW row tiles x NTP
+// column tiles (MTW = min(MT, 2)): at 64 rows a 32x64 sub-tile, reading
+// 2 X + 4 W fragments per k-step.  All fragments of a chunk are read in one
+// batch before its MFMAs, so the LDS latency is paid once per chunk.
 #pragma once
 
 #include "bd_device.h"
@@ -42,21 +50,20 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
 }
 
-template <int MT_, int NTW_, int KSC_, int NS_>
+template <int MT_, int NTW_, int NS_>
 struct Cfg {
   static constexpr int MT = MT_;        // row tiles per work-group
   static constexpr int NTW = NTW_;      // column tiles per work-group
-  static constexpr int KSC = KSC_;      // 32-wide k-steps per chunk
   static constexpr int NS = NS_;        // pipeline stages
-  static constexpr int WM = MT;         // waves along the rows
-  static constexpr int WN = 4 / MT;     // waves along the columns
+  static constexpr int MTW = MT < 2 ? MT : 2;  // row tiles per wave
+  static constexpr int WM = MT / MTW;   // waves along the rows
+  static constexpr int WN = 4 / WM;     // waves along the columns
   static constexpr int NTP = NTW / WN;  // column tiles per wave
-  static constexpr int WFR = NTW * KSC; // W fragments per stage
-  static constexpr int XFR = MT * KSC;  // X fragments per stage
-  static constexpr int FR = WFR + XFR;
-  static constexpr int LW = (FR + 3) / 4;  // fragments (load instructions) per wave per stage, at most
-  static constexpr int LW_LO = FR / 4;      // waves >= FR % 4 issue one fewer
-  static constexpr int KC = KSC * 32;
+  static constexpr int KSC = 2;         // 32-wide k-steps per chunk
+  static constexpr int KC = 64;         // k per chunk
+  static constexpr int FR = 2 * (NTW + MT);  // DMA instructions per stage (1 KiB each)
+  static constexpr int LW = (FR + 3) / 4;    // instructions per wave per stage, at most
+  static constexpr int LW_LO = FR / 4;       // waves >= FR % 4 issue one fewer
   static constexpr int STAGE_U4 = FR * 64;
   static constexpr int LDS_BYTES = NS * STAGE_U4 * 16;
   static_assert(MT == 1 || MT == 2 || MT == 4, "MT");
@@ -64,52 +71,63 @@ struct Cfg {
   static_assert(NS == 2 || NS == 3, "stages");
 };
 
+// Byte offset, inside a 2 KiB tile, of lane `lane`'s fragment for k-step ks.
+__device__ __forceinline__ int frag_offset(int lane, int ks) {
+  const int r = lane & 15, r7 = r & 7;
+  return (r >> 3) * 1024 + (r7 * 8 + ((4 * ks + (lane >> 4)) ^ r7)) * 16;
+}
+
 // Row pointers: xrow(m) gives row m of X (K elements) or nullptr for a row
 // that does not exist; such rows read row `xdummy` instead and their outputs
 // are never used.  Columns >= N read row 0 of W likewise.
 // K range: elements [k0, k0 + nch*KC) of rows of length K.
+// Output: acc[i][j] holds rows m0 + (wm*MTW + i)*16 + 4*(lane/16) + r (r = the
+// vector element) and columns n0 + (wn*NTP + j)*16 + lane%16, with
+// wm = wave % WM and wn = wave / WM.
 template <class C, class XRowF>
 __device__ __forceinline__ void mainloop(const XRowF& xrow, const uint16_t* xdummy, int m0,
                                          const uint16_t* __restrict__ W, int N, int K, int n0, uint4* sbuf,
-                                         bd_f32x4 (&acc)[C::NTP], int k0 = 0, int nch = -1) {
+                                         bd_f32x4 (&acc)[C::MTW][C::NTP], int k0 = 0, int nch = -1) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int g = lane >> 4;
-  const int l16 = lane & 15;
   const int wm = wave % C::WM;
   const int wn = wave / C::WM;
   if (nch < 0) nch = K / C::KC;
 
 #pragma unroll
-  for (int j = 0; j < C::NTP; ++j) acc[j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane source pointers of this wave's fragments (chunk 0)
+  // per-lane source pointers of this wave's DMA instructions (chunk 0):
+  // instruction f loads rows 8*(f%2) .. +7 of tile f/2
+  const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
   const uint16_t* src[C::LW];
 #pragma unroll
   for (int i = 0; i < C::LW; ++i) {
     const int f = wave + 4 * i;
+    const int t = f >> 1, r = 8 * (f & 1) + lrow;
     if (f >= C::FR) {
       src[i] = nullptr;
-    } else if (f < C::WFR) {
-      const int nt = f / C::KSC, ks = f % C::KSC;
-      const int col = n0 + nt * 16 + l16;
-      src[i] = W + (size_t)(col < N ? col : 0) * K + k0 + 32 * ks + 8 * g;
+    } else if (t < C::NTW) {
+      const int col = n0 + t * 16 + r;
+      src[i] = W + (size_t)(col < N ? col : 0) * K + k0 + 8 * lkb;
     } else {
-      const int mt = (f - C::WFR) / C::KSC, ks = (f - C::WFR) % C::KSC;
-      const uint16_t* p = xrow(m0 + mt * 16 + l16);
-      src[i] = (p ? p : xdummy) + k0 + 32 * ks + 8 * g;
+      const uint16_t* p = xrow(m0 + (t - C::NTW) * 16 + r);
+      src[i] = (p ? p : xdummy) + k0 + 8 * lkb;
     }
   }
   auto issue = [&](int ch) {
     uint4* st = sbuf + (ch % C::NS) * C::STAGE_U4;
 #pragma unroll
     for (int i = 0; i < C::LW; ++i)
-      if (wave + 4 * i < C::FR)
+      if (C::FR % 4 == 0 || wave + 4 * i < C::FR)
         __builtin_amdgcn_global_load_lds((glb_void_t*)(src[i] + (size_t)ch * C::KC),
                                          (lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, 0);
   };
   const bool more = wave < C::FR % 4;  // this wave issues LW (else LW_LO) loads per stage
+  const int fo0 = frag_offset(lane, 0) / 16, fo1 = frag_offset(lane, 1) / 16;
 
 #pragma unroll
   for (int c = 0; c < C::NS - 1; ++c)
@@ -124,15 +142,21 @@ __device__ __forceinline__ void mainloop(const XRowF& xrow, const uint16_t* xdum
     pipe_barrier();  // chunk ch is in LDS for every wave; slot of ch - 1 is free
     if (ch + C::NS - 1 < nch) issue(ch + C::NS - 1);
     const uint4* st = sbuf + (ch % C::NS) * C::STAGE_U4;
+    uint4 xa[C::KSC][C::MTW], wb[C::KSC][C::NTP];
 #pragma unroll
     for (int ks = 0; ks < C::KSC; ++ks) {
-      const uint4 a = st[(C::WFR + wm * C::KSC + ks) * 64 + lane];
+      const int fo = ks == 0 ? fo0 : fo1;
 #pragma unroll
-      for (int j = 0; j < C::NTP; ++j) {
-        const int nt = wn * C::NTP + j;
-        acc[j] = bd_mfma16(a, st[(nt * C::KSC + ks) * 64 + lane], acc[j]);
-      }
+      for (int i = 0; i < C::MTW; ++i) xa[ks][i] = st[(C::NTW + wm * C::MTW + i) * 128 + fo];
+#pragma unroll
+      for (int j = 0; j < C::NTP; ++j) wb[ks][j] = st[(wn * C::NTP + j) * 128 + fo];
     }
+#pragma unroll
+    for (int ks = 0; ks < C::KSC; ++ks)
+#pragma unroll
+      for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_mfma16(xa[ks][i], wb[ks][j], acc[i][j]);
   }
   __syncthreads();  // stages may be reused by the caller's epilogue
 }
