@@ -13,9 +13,11 @@
 // of a row in a fixed order into argmax, max, log-sum-exp and
 // confidence = exp(max - lse).
 //
-// bf16: streaming MFMA GEMM (stream_gemm.h), weights streamed once from HBM
-// through a 3-stage asynchronous global->LDS pipeline, up to 64 rows per
-// work-group.  fp32: plain VALU kernel.
+// bf16, up to 64 rows: streaming MFMA GEMM (stream_gemm.h), weights
+// streamed once from HBM through a 3-stage asynchronous global->LDS pipeline.
+// bf16, more rows (the exact step of a whole batch, where the product is
+// MFMA-bound): 256 x 256 work-group tiles, see lm_big_kernel.
+// fp32: plain VALU kernel.
 #include <climits>
 
 #include "bd_device.h"
@@ -111,6 +113,137 @@ __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
 #pragma unroll
     for (int w = 1; w < C::WN; ++w) st = bd_stat_combine(st, red[w * (MT * 16) + tid]);
     const size_t pi = (size_t)(m0 + tid) * a.nvt + blockIdx.x;
+    a.pmax[pi] = st.m;
+    a.pidx[pi] = st.i;
+    a.psum[pi] = st.s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large-M bf16 LM head: each work-group computes a 256-row x 256-column tile of
+// the logits with 8 waves (2 along the rows x 4 along the columns, 128 x 64
+// each, 32 MFMA accumulators per wave) and reduces it to per-row partials.
+// K is walked in 64-wide chunks through two 64 KiB LDS stages filled by
+// whole-line DMA (the tile layout of stream_gemm.h: a 16-row x 64-k tile is
+// 2 KiB, two instructions of 8 rows x 128 B, XOR-swizzled k-blocks).  Work
+// order: the row blocks of one column block are consecutive on one XCD, so a
+// W column block is fetched from HBM once and re-read from that XCD's L2.
+constexpr int kBigRows = 256, kBigCols = 256, kBigThreads = 512;
+constexpr int kBigTiles = (kBigRows + kBigCols) / 16;  // 16-row tiles per stage
+constexpr int kBigFR = 2 * kBigTiles;                   // DMA instructions per stage
+constexpr int kBigLW = kBigFR / 8;                      // per wave
+constexpr int kBigStageU4 = kBigFR * 64;
+
+__global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_count, int cb_count) {
+  __shared__ uint4 sbuf[2 * kBigStageU4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int wr = wave & 1, wc = wave >> 1;
+  // XCD-aware order: work-group w runs on XCD w % 8; the (w / 8)-th work-group
+  // of an XCD takes row block q % rb_count of column block 8 * (q / rb_count) + xcd.
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int rb = q % rb_count, cb = 8 * (q / rb_count) + xcd;
+  if (cb >= cb_count) return;
+  const int m0 = rb * kBigRows, n0 = cb * kBigCols;
+  const int nch = a.hidden / 64;
+
+  // DMA sources: instruction f covers rows 8*(f%2)..+7 of stage tile f/2;
+  // tiles 0..15 are X row tiles, 16..31 W column tiles.
+  const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
+  const uint16_t* src[kBigLW];
+#pragma unroll
+  for (int i = 0; i < kBigLW; ++i) {
+    const int f = wave + 8 * i, t = f >> 1, r = 8 * (f & 1) + lrow;
+    if (t < kBigRows / 16) {
+      const uint16_t* p = lm_row(a, m0 + t * 16 + r);
+      src[i] = (p ? p : a.h) + 8 * lkb;
+    } else {
+      const int col = n0 + (t - kBigRows / 16) * 16 + r;
+      src[i] = a.w + (size_t)(col < a.V ? col : 0) * a.hidden + 8 * lkb;
+    }
+  }
+  auto issue = [&](int ch) {
+    uint4* st = sbuf + (ch & 1) * kBigStageU4;
+#pragma unroll
+    for (int i = 0; i < kBigLW; ++i)
+      __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ch * 64),
+                                       (bd_stream::lds_void_t*)(st + (wave + 8 * i) * 64), 16, 0, 0);
+  };
+
+  bd_f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t sbase = bd_stream::lds_addr(sbuf);
+  const uint32_t fo[2] = {(uint32_t)bd_stream::frag_offset(lane, 0), (uint32_t)bd_stream::frag_offset(lane, 1)};
+  const uint32_t xt0 = wr * 8 * 2048, wt0 = (kBigRows / 16 + wc * 4) * 2048;  // this wave's first X / W tile
+
+  issue(0);
+  for (int ch = 0; ch < nch; ++ch) {
+    __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+    bd_stream::pipe_barrier();  // chunk ch in LDS everywhere; the other stage is free
+    if (ch + 1 < nch) issue(ch + 1);
+    const uint32_t st = sbase + (ch & 1) * kBigStageU4 * 16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 wb[4], xa[4];
+      bd_stream::lds_frags_4x4(st + xt0 + fo[ks], st + wt0 + fo[ks], xa, wb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+      bd_stream::lds_frags_4(st + xt0 + 4 * 2048 + fo[ks], xa);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 + i][j] = bd_mfma16(xa[i], wb[j], acc[4 + i][j]);
+    }
+  }
+  __syncthreads();  // the stages become the reduction buffer
+
+  // acc[i][j][r]: row m0 + wr*128 + 16i + 4g + r, column n0 + wc*64 + 16j + l16
+  BdArgStat* red = reinterpret_cast<BdArgStat*>(sbuf);  // [4 column waves][256 rows]
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rl = wr * 128 + 16 * i + 4 * g + r;
+      BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wc * 64 + 16 * j + l16;
+        const float v = acc[i][j][r];
+        if (col < a.V && v > st.m) {
+          st.m = v;
+          st.i = col;
+        }
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wc * 64 + 16 * j + l16;
+        if (col < a.V) sum += bd_exp2((acc[i][j][r] - st.m) * BD_LOG2E);
+      }
+      st.s = sum;
+      if (a.logits != nullptr && m0 + rl < a.M) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wc * 64 + 16 * j + l16;
+          if (col < a.V) a.logits[(size_t)(m0 + rl) * a.V + col] = acc[i][j][r];
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
+      if (l16 == 0) red[wc * kBigRows + rl] = st;
+    }
+  }
+  __syncthreads();
+  if (tid < kBigRows && m0 + tid < a.M) {
+    BdArgStat st = red[tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) st = bd_stat_combine(st, red[w * kBigRows + tid]);
+    const size_t pi = (size_t)(m0 + tid) * a.nvt + cb;
     a.pmax[pi] = st.m;
     a.pidx[pi] = st.i;
     a.psum[pi] = st.s;
@@ -215,6 +348,9 @@ BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
   if (dt == BD_F32) {
     p.cols_per_wg = kThreads;
     p.rows_per_wg = kF32Rows;
+  } else if (M > 64) {
+    p.cols_per_wg = kBigCols;
+    p.rows_per_wg = kBigRows;
   } else {
     p.cols_per_wg = kNTW * 16;
     const int mt = (M + 15) / 16;
@@ -237,6 +373,11 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
     LmK a{static_cast<const uint16_t*>(x.h), x.n_src, x.row_idx, static_cast<const uint16_t*>(x.w), x.logits,
           x.M, x.hidden, x.V, p.nvt, x.pmax, x.pidx, x.psum};
     switch (p.rows_per_wg / 16) {
+      case kBigRows / 16: {
+        const int cb8 = (p.nvt + 7) / 8 * 8;  // column blocks rounded up to whole XCD rounds
+        hipLaunchKernelGGL(lm_big_kernel, dim3(cb8 * p.nmb), dim3(kBigThreads), 0, s, a, p.nmb, p.nvt);
+        break;
+      }
       case 1: hipLaunchKernelGGL(lm_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
       case 2: hipLaunchKernelGGL(lm_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
       default: hipLaunchKernelGGL(lm_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a); break;

@@ -106,6 +106,9 @@ LM_CASES = {
     "bf16-7B-M17-sharp": ("bf16", 17, 20, 3584, 152064, 1.0, 60.0, False),
     "bf16-7B-M100": ("bf16", 100, 128, 3584, 152064, 1.0, 1.0, False),
     "bf16-ragged-vocab": ("bf16", 33, 40, 512, 1000, 1.0, 30.0, True),
+    # more than 64 rows: 256 x 256 tiles; two row blocks, the second ragged,
+    # and a ragged last vocabulary block
+    "bf16-big-ragged": ("bf16", 300, 310, 512, 5000, 1.0, 30.0, True),
 }
 
 
@@ -129,17 +132,43 @@ def test_lmhead_confidence(name):
     say(f"    exempt argmax rows: {ex}")
 
 
-def test_lmhead_invalid_row_index():
+@pytest.mark.parametrize("M", [4, 80])
+def test_lmhead_invalid_row_index(M):
     V, hidden = 512, 256
+    say(f"[lmhead] invalid row index M={M}")
     w = bi.normal(2, "Wlm", (V, hidden), 0.02, "bf16")
     h = bi.normal(2, "h", (4, hidden), 0.02, "bf16")
-    ridx = np.array([0, 7, -1, 3], dtype=np.int32)
-    am = torch.zeros(4, dtype=torch.int32, device=DEV)
-    conf = torch.zeros(4, dtype=torch.float32, device=DEV)
+    ridx = np.resize(np.array([0, 7, -1, 3], dtype=np.int32), M)
+    am = torch.zeros(M, dtype=torch.int32, device=DEV)
+    conf = torch.zeros(M, dtype=torch.float32, device=DEV)
     ops().bd_lmhead_confidence(up(h, torch.bfloat16), up(ridx), up(w, torch.bfloat16), am, conf)
     a, c = am.cpu().numpy(), conf.cpu().numpy()
-    assert a[1] == -1 and a[2] == -1 and np.isnan(c[1]) and np.isnan(c[2])
-    assert a[0] >= 0 and a[3] >= 0 and np.isfinite(c[[0, 3]]).all()
+    bad = (ridx < 0) | (ridx >= 4)
+    assert (a[bad] == -1).all() and np.isnan(c[bad]).all()
+    assert (a[~bad] >= 0).all() and np.isfinite(c[~bad]).all()
+    ref = R.lm_logits(w, h[np.clip(ridx, 0, 3)])
+    lm_stats_close(a[~bad], c[~bad], None, None, ref[~bad], TOL["bf16"], f"valid rows M={M}")
+
+
+def test_lmhead_7B_batched_sampled():
+    """The batched exact-step shape: 1024 rows on the 7B head (four 256-row
+    blocks), checked on sampled rows of every block against the oracle."""
+    M, n_src, hidden, V = 1024, 1100, 3584, 152064
+    say("[lmhead] 7B M=1024 sampled")
+    w = bi.normal(3, "Wlm", (V, hidden), 0.02, "bf16")
+    h = bi.normal(3, "h", (n_src, hidden), 0.02, "bf16")
+    ridx = np.random.default_rng(11).integers(0, n_src, size=M).astype(np.int32)
+    am = torch.zeros(M, dtype=torch.int32, device=DEV)
+    conf, mx, lse = (torch.zeros(M, dtype=torch.float32, device=DEV) for _ in range(3))
+    ops().bd_lmhead_confidence(up(h, torch.bfloat16), up(ridx), up(w, torch.bfloat16), am, conf, max_logit=mx,
+                               lse=lse)
+    torch.cuda.synchronize()
+    a, c = am.cpu().numpy(), down(conf)
+    assert ((a >= 0) & (a < V)).all() and np.isfinite(c).all() and ((c > 0) & (c <= 1)).all()
+    rows = np.concatenate([np.random.default_rng(12).choice(np.arange(b * 256, (b + 1) * 256), 6, replace=False)
+                           for b in range(4)] + [np.array([0, 255, 256, 1023])])
+    ref = R.lm_logits(w, h[ridx[rows]])
+    lm_stats_close(a[rows], c[rows], down(mx)[rows], down(lse)[rows], ref, TOL["bf16"], "7B M=1024 sampled")
 
 
 # --------------------------------------------------------------------------
