@@ -36,7 +36,7 @@ constexpr int kThreads = 256;
 #define BD_ATTN_KT 32
 #endif
 #ifndef BD_ATTN_NS
-#define BD_ATTN_NS 5
+#define BD_ATTN_NS 4
 #endif
 #ifndef BD_ATTN_TARGET_WGS
 #define BD_ATTN_TARGET_WGS 512
@@ -47,12 +47,16 @@ constexpr int kThreads = 256;
 #ifndef BD_ATTN_QPW_MAX
 #define BD_ATTN_QPW_MAX 2
 #endif
+#ifndef BD_ATTN_WG_PER_CU
+#define BD_ATTN_WG_PER_CU 2
+#endif
 constexpr int kKT = BD_ATTN_KT;                 // keys per LDS tile (bf16 path)
 constexpr int kNS = BD_ATTN_NS;                 // pipeline stages (bf16 path)
 constexpr int kXcd = 8;                         // work-groups are dispatched round-robin over 8 XCDs
 constexpr int kMinChunk = BD_ATTN_MIN_CHUNK;    // keys per work item, lower bound
 constexpr int kTargetWGs = BD_ATTN_TARGET_WGS;
 constexpr int kQpwMax = BD_ATTN_QPW_MAX;        // query tiles per wave, at most (1, 2 or 4)
+constexpr float kLazyMax = 8.f;                 // running-max slack (log2 units), see the softmax
 
 struct AttnK {
   const uint16_t* q;
@@ -178,7 +182,7 @@ __device__ __forceinline__ void pipe_barrier() {
 // 16-byte slots, and each lane's global address is chosen so that its slot
 // receives the right chunk.
 template <int DH, int KT, int QPW, int NS>
-__global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_kernel(AttnK a) {
+__global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void attn_bf16_kernel(AttnK a) {
   constexpr int KCH = DH / 8;             // 16-byte chunks per key row
   constexpr int TU4 = KT * KCH;           // 16-byte slots per K (or V) tile
   constexpr int NI = TU4 / 64;            // DMA instructions per K (or V) tile
@@ -374,16 +378,51 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_kernel
       uint4 pf[QPW][KT / 32];
 #pragma unroll
       for (int j = 0; j < QPW; ++j) {
-        float mx = BD_NEG_INF;
-        if (kbase + KT <= vis_all) {  // whole tile visible to every row: no mask
+        if (kbase + KT <= vis_all) {
+          // Whole tile visible to every row: no mask, and a lazy running max.
+          // Any common offset m gives the same softmax as long as every
+          // contribution to a row uses it, so m_run only moves when some
+          // score exceeds it by more than kLazyMax (probabilities stay below
+          // 2^kLazyMax); otherwise no cross-lane reduction and no rescale.
+          float mx = s[j][0][0];
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              s[j][kt][r] *= a.scale_log2;
-              mx = fmaxf(mx, s[j][kt][r]);
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][kt][r]);
+          const float smx = mx * a.scale_log2;
+          if (__ballot(smx > m_run[j] + kLazyMax) != 0) {
+            float mall = fmaxf(smx, __shfl_xor(smx, 16));
+            mall = fmaxf(mall, __shfl_xor(mall, 32));
+            const float mnew = fmaxf(m_run[j], mall);
+            const float alpha = bd_exp2(m_run[j] - mnew);
+            m_run[j] = mnew;
+            l_run[j] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DH / 16; ++dt) oacc[j][dt] *= alpha;
+          }
+          const float mneg = -m_run[j];
+          float ps = 0.f;
+#pragma unroll
+          for (int u = 0; u < KT / 32; ++u) {
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const bd_f32x4 sv = s[j][2 * u + h];
+              const float p0 = bd_exp2(__builtin_fmaf(sv[0], a.scale_log2, mneg));
+              const float p1 = bd_exp2(__builtin_fmaf(sv[1], a.scale_log2, mneg));
+              const float p2 = bd_exp2(__builtin_fmaf(sv[2], a.scale_log2, mneg));
+              const float p3 = bd_exp2(__builtin_fmaf(sv[3], a.scale_log2, mneg));
+              ps += (p0 + p1) + (p2 + p3);
+              w[2 * h] = cvt_pk_bf16(p0, p1);
+              w[2 * h + 1] = cvt_pk_bf16(p2, p3);
             }
-        } else {
+            pf[j][u] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+          l_run[j] += ps;
+          continue;
+        }
+        float mx = BD_NEG_INF;
+        {
           const int lim = min(kend, qblk[j]);
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt)
