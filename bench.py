@@ -61,12 +61,53 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+LM_SOURCES = ("lmhead.hip", "stream_gemm.h", "bd_device.h", "bd_launch.h")
+CALIB_BYTES = 1 << 30  # plain device copy that calibrates the HBM byte counters
+
+
 def kernel_source_hash() -> str:
+    """Hash of the sources the LM-head kernels are built from: a stored
+    counter reading is used only while they are unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_diffusion_decoding_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in LM_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def traffic_from(fetch_csv, write_csv):
+    """Turn two rocprofv3 --pmc counter files (FETCH_SIZE, then WRITE_SIZE, both
+    over `bench.py --section lm`) into the HBM bytes per launch of the 64-row
+    7B LM head. Each counter is scaled by what it reads for the 1 GiB plain
+    device copy that run makes (the copy reads and writes exactly CALIB_BYTES)."""
+    import csv
+
+    def rows(path, counter):
+        return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+    out = {"kernel_source_hash": kernel_source_hash(), "calibration_bytes": CALIB_BYTES,
+           "launch": "lm_bf16_kernel<4> + lm_merge_kernel (grid 64 x 256), 64 rows x 152064 x 3584"}
+    total = 0.0
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rs = rows(path, counter)
+        main = [float(r["Counter_Value"]) for r in rs if "lm_bf16_kernel<4>" in r["Kernel_Name"]]
+        merge = [float(r["Counter_Value"]) for r in rs
+                 if "lm_merge_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) == 64 * 256]
+        cp = [float(r["Counter_Value"]) for r in rs
+              if "copyBuffer" in r["Kernel_Name"] or "copy_kernel" in r["Kernel_Name"]]
+        if not main or not merge or not cp:
+            raise SystemExit(f"{path}: no {counter} reading for the LM head, its merge or the calibration copy")
+        kib = float(np.median(main)) + float(np.median(merge))
+        scale = CALIB_BYTES / (max(cp) * 1024.0)
+        out[counter] = {"kib_per_launch": kib, "main_kib": float(np.median(main)),
+                        "merge_kib": float(np.median(merge)), "dispatches": len(main), "copy_kib": max(cp),
+                        "scale": scale, "bytes_per_launch": kib * 1024.0 * scale}
+        total += kib * 1024.0 * scale
+    out["bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", "lmhead_7B_M64_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def make_decoder(cfg, w, pre):
@@ -146,12 +187,26 @@ def time_call(fn, reps, warm=3):
     return float(np.median(t)), float(np.mean(t))
 
 
-def extras(w3, reps):
-    """Attention and LM head alone at the long-context / batched shapes."""
+def extras(w3, reps, parts=("attn", "long", "lm"), graphs=True):
+    """Attention and LM head alone at the long-context / batched shapes, and
+    the long-context block loop."""
     from block_diffusion_decoding_amd import ops
     out = {}
     T = torch.bfloat16
     c4 = bi.C4
+    if "attn" in parts:
+        out.update(extras_attn(c4, reps))
+    if "long" in parts:
+        out.update(extras_long(c4, w3, graphs))
+    if "lm" in parts:
+        out.update(extras_lm(w3, reps))
+    return out
+
+
+def extras_attn(c4, reps):
+    from block_diffusion_decoding_amd import ops
+    out = {}
+    T = torch.bfloat16
     # ---- attention, batch 32 x 16384 committed tokens
     log("[bench] long-context attention inputs")
     pre4 = bi.make_prefix(c4, 0)
@@ -173,12 +228,19 @@ def extras(w3, reps):
             "TFLOP/s": flops / mean / 1e12}
         log(f"[bench] attention {name}: {mean * 1e6:.1f} us, {nbytes / mean / 1e9:.0f} GB/s")
     del kc, vc
+    return out
+
+
+def extras_long(c4, w3, graphs):
+    out = {}
     # ---- fixed-schedule long-context block: 4 windows x 8 steps + commit
     log("[bench] long-context block loop")
     cfg4 = c4
     pre4 = bi.make_prefix(cfg4, 0)
     dec4 = make_decoder(cfg4, w3, pre4)
     del pre4
+    if graphs:
+        dec4.capture(cfg4.S, cfg4.tau)
     dec4.new_block()
     dec4.decode_block(cfg4.S, cfg4.tau, steps_per_window=8)          # warm-up block
     dec4.kv_len.fill_(16384)
@@ -196,6 +258,21 @@ def extras(w3, reps):
     log(f"[bench] long block: {dt * 1e3:.2f} ms, {decoded / dt:.0f} tokens/s")
     del dec4
     torch.cuda.empty_cache()
+    return out
+
+
+def extras_lm(w3, reps):
+    from block_diffusion_decoding_amd import ops
+    out = {}
+    T = torch.bfloat16
+    # plain device copy of known size: calibrates the HBM byte counters of a
+    # profiling run of this section
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     # ---- LM head alone: 1024 rows on the 7B head (MFMA bound)
     Wlm = torch.from_numpy(w3.Wlm).to("cuda", T)
     for M, key in ((1024, "lmhead_7B_M1024"), (64, "lmhead_7B_M64")):
@@ -266,7 +343,16 @@ def main():
     ap.add_argument("--no-graphs", action="store_true", help="launch every step's kernels eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm"), default="all",
+                    help="attn/long/lm: run only that single-call or loop measurement (for profiling) and print "
+                         "its JSON instead of the bench line")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/lmhead_7B_M64_traffic.json from two rocprofv3 --pmc counter files of "
+                         "`--section lm` (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this implementation runs on a "
               "single GPU and has no multi-GPU path", file=sys.stderr)
@@ -280,6 +366,9 @@ def main():
     cfg = bi.C3
     log("[bench] generating the 7B-shape workload")
     w = bi.make_weights(cfg, 0)
+    if args.section != "all":
+        print(json.dumps(extras(w, args.reps, parts=(args.section,), graphs=not args.no_graphs)), flush=True)
+        return
     pre = bi.make_prefix(cfg, 0)
     n_blocks = 8
     dec = make_decoder(cfg, w, pre)
