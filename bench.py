@@ -275,7 +275,7 @@ def extras_lm(w3, reps):
     del src, dst
     # ---- LM head alone: 1024 rows on the 7B head (MFMA bound)
     Wlm = torch.from_numpy(w3.Wlm).to("cuda", T)
-    for M, key in ((1024, "lmhead_7B_M1024"), (64, "lmhead_7B_M64")):
+    for M, key in ((1024, "lmhead_7B_M1024"), (256, "lmhead_7B_M256"), (64, "lmhead_7B_M64")):
         h = torch.randn(M, 3584, device="cuda", dtype=T) * 0.05
         am = torch.empty(M, dtype=torch.int32, device="cuda")
         cf = torch.empty(M, dtype=torch.float32, device="cuda")

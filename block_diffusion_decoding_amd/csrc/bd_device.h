@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 #include "../../include/bd.h"
 
@@ -71,3 +72,55 @@ __device__ __forceinline__ BdArgStat bd_stat_shfl_xor(BdArgStat a, int mask) {
   b.s = __shfl_xor(a.s, mask);
   return b;
 }
+
+// Reductions over the 16 lanes of a row group (lanes 16k .. 16k+15) with DPP
+// row rotations: after rotating by 8, 4, 2 and 1 every lane holds the result
+// (the operations are commutative, and the fixed order makes them
+// deterministic).  VALU-speed, no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ int bd_dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float bd_dpp_f(float x) {
+  return __int_as_float(bd_dpp_i<CTRL>(__float_as_int(x)));
+}
+__device__ __forceinline__ float bd_row16_max(float x) {
+  x = fmaxf(x, bd_dpp_f<0x128>(x));  // row_ror:8
+  x = fmaxf(x, bd_dpp_f<0x124>(x));  // row_ror:4
+  x = fmaxf(x, bd_dpp_f<0x122>(x));  // row_ror:2
+  return fmaxf(x, bd_dpp_f<0x121>(x));  // row_ror:1
+}
+__device__ __forceinline__ float bd_row16_sum(float x) {
+  x += bd_dpp_f<0x128>(x);
+  x += bd_dpp_f<0x124>(x);
+  x += bd_dpp_f<0x122>(x);
+  return x + bd_dpp_f<0x121>(x);
+}
+__device__ __forceinline__ int bd_row16_min(int x) {
+  x = min(x, bd_dpp_i<0x128>(x));
+  x = min(x, bd_dpp_i<0x124>(x));
+  x = min(x, bd_dpp_i<0x122>(x));
+  return min(x, bd_dpp_i<0x121>(x));
+}
+
+// (max, lowest argmax, sum of exp(v - max)) of the N values v[] held by each
+// of the 16 lanes of a row group, at columns col[]; masked values are -inf.
+// The row max is found first, so every exponential uses it directly.
+template <int N>
+__device__ __forceinline__ BdArgStat bd_row16_stat(const float (&v)[N], const int (&col)[N]) {
+  float m = v[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) m = fmaxf(m, v[j]);
+  m = bd_row16_max(m);
+  const float mu = (m == BD_NEG_INF) ? 0.f : m;
+  float s = 0.f;
+  int idx = INT_MAX;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    s += bd_exp2((v[j] - mu) * BD_LOG2E);
+    if (v[j] == m && v[j] != BD_NEG_INF) idx = min(idx, col[j]);
+  }
+  return BdArgStat{m, bd_row16_min(idx), bd_row16_sum(s)};
+}
+

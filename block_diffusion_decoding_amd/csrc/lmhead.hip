@@ -72,39 +72,33 @@ __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
   bd_stream::mainloop<C>(xrow, a.h, m0, a.w, a.V, a.hidden, n0, sbuf, acc);
 
   // rows m0 + (wm*MTW + i)*16 + 4g + r, columns n0 + (wn*NTP + j)*16 + l16
+  if (a.logits != nullptr) {  // debug dump of the raw logits (tests only)
+#pragma unroll
+    for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j) {
+          const int col = n0 + (wn * C::NTP + j) * 16 + l16;
+          if (m < a.M && col < a.V) a.logits[(size_t)m * a.V + col] = acc[i][j][r];
+        }
+      }
+  }
+  const bool ragged = n0 + kNTW * 16 > a.V;  // only the last column block
+  int col[C::NTP];
+#pragma unroll
+  for (int j = 0; j < C::NTP; ++j) col[j] = n0 + (wn * C::NTP + j) * 16 + l16;
   BdArgStat* red = reinterpret_cast<BdArgStat*>(sbuf);  // [WN][MT*16]
 #pragma unroll
   for (int i = 0; i < C::MTW; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = (wm * C::MTW + i) * 16 + 4 * g + r;
-      BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
+      float v[C::NTP];
 #pragma unroll
-      for (int j = 0; j < C::NTP; ++j) {
-        const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-        const float v = acc[i][j][r];
-        if (col < a.V && v > st.m) {
-          st.m = v;
-          st.i = col;
-        }
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < C::NTP; ++j) {
-        const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-        if (col < a.V) s += bd_exp2((acc[i][j][r] - st.m) * BD_LOG2E);
-      }
-      st.s = s;
-      if (a.logits != nullptr && m0 + rl < a.M) {
-#pragma unroll
-        for (int j = 0; j < C::NTP; ++j) {
-          const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-          if (col < a.V) a.logits[(size_t)(m0 + rl) * a.V + col] = acc[i][j][r];
-        }
-      }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
-      if (l16 == 0) red[wn * (MT * 16) + rl] = st;
+      for (int j = 0; j < C::NTP; ++j) v[j] = (ragged && col[j] >= a.V) ? BD_NEG_INF : acc[i][j][r];
+      const BdArgStat st = bd_row16_stat(v, col);
+      if (l16 == 0) red[wn * (MT * 16) + (wm * C::MTW + i) * 16 + 4 * g + r] = st;
     }
   }
   __syncthreads();
@@ -120,39 +114,59 @@ __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-M bf16 LM head: each work-group computes a 256-row x 256-column tile of
-// the logits with 8 waves (2 along the rows x 4 along the columns, 128 x 64
-// each, 32 MFMA accumulators per wave) and reduces it to per-row partials.
-// K is walked in 64-wide chunks through two 64 KiB LDS stages filled by
-// whole-line DMA (the tile layout of stream_gemm.h: a 16-row x 64-k tile is
-// 2 KiB, two instructions of 8 rows x 128 B, XOR-swizzled k-blocks).  Work
-// order: the row blocks of one column block are consecutive on one XCD, so a
-// W column block is fetched from HBM once and re-read from that XCD's L2.
-constexpr int kBigRows = 256, kBigCols = 256, kBigThreads = 512;
-constexpr int kBigTiles = (kBigRows + kBigCols) / 16;  // 16-row tiles per stage
-constexpr int kBigFR = 2 * kBigTiles;                   // DMA instructions per stage
-constexpr int kBigLW = kBigFR / 8;                      // per wave
-constexpr int kBigStageU4 = kBigFR * 64;
+// Large-M bf16 LM head: each work-group computes a 256-row x (CT*16)-column
+// tile of the logits with 8 waves and reduces it to per-row partials.
+//   CT = 16 (more than 256 rows, MFMA-bound): 2 x 4 waves of 128 x 64, two
+//            64 KiB stages;
+//   CT = 8  (up to 256 rows, HBM-bound): 4 x 2 waves of 64 x 64, three
+//            48 KiB stages (two in flight) and twice the work-groups, so the
+//            weight stream has more bytes in flight and a shorter tail.
+// K is walked in 64-wide chunks filled by whole-line DMA (the tile layout of
+// stream_gemm.h: a 16-row x 64-k tile is 2 KiB, two instructions of 8 rows x
+// 128 B, XOR-swizzled k-blocks).  Work order: the row blocks of one column
+// block are consecutive on one XCD, so a W column block is fetched from HBM
+// once and re-read from that XCD's L2.
+constexpr int kBigRows = 256, kBigThreads = 512;
+#ifndef BD_LM_NARROW_MAX_ROWS
+#define BD_LM_NARROW_MAX_ROWS 256
+#endif
+constexpr int kNarrowMaxRows = BD_LM_NARROW_MAX_ROWS;  // up to this many rows: 256 x 128 tiles
 
+template <int CT>
+struct Big {
+  static constexpr int WR = CT == 16 ? 2 : 4;       // waves along the rows
+  static constexpr int WC = 8 / WR;                 // waves along the columns
+  static constexpr int MW = kBigRows / 16 / WR;     // row tiles per wave
+  static constexpr int NWT = CT / WC;               // column tiles per wave
+  static constexpr int NS = CT == 16 ? 2 : 3;       // stages
+  static constexpr int TILES = kBigRows / 16 + CT;  // 16-row tiles per stage
+  static constexpr int FR = 2 * TILES;              // DMA instructions per stage
+  static constexpr int LW = FR / 8;                 // per wave
+  static constexpr int STAGE_U4 = FR * 64;
+  static_assert(MW % 4 == 0 && NWT == 4 && FR % 8 == 0, "wave tiling");
+};
+
+template <int CT>
 __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_count, int cb_count) {
-  __shared__ uint4 sbuf[2 * kBigStageU4];
+  using P = Big<CT>;
+  __shared__ uint4 sbuf[P::NS * P::STAGE_U4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int wr = wave & 1, wc = wave >> 1;
+  const int wr = wave % P::WR, wc = wave / P::WR;
   // XCD-aware order: work-group w runs on XCD w % 8; the (w / 8)-th work-group
   // of an XCD takes row block q % rb_count of column block 8 * (q / rb_count) + xcd.
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int rb = q % rb_count, cb = 8 * (q / rb_count) + xcd;
   if (cb >= cb_count) return;
-  const int m0 = rb * kBigRows, n0 = cb * kBigCols;
+  const int m0 = rb * kBigRows, n0 = cb * CT * 16;
   const int nch = a.hidden / 64;
 
   // DMA sources: instruction f covers rows 8*(f%2)..+7 of stage tile f/2;
-  // tiles 0..15 are X row tiles, 16..31 W column tiles.
+  // tiles 0..15 are X row tiles, the next CT are W column tiles.
   const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
-  const uint16_t* src[kBigLW];
+  const uint16_t* src[P::LW];
 #pragma unroll
-  for (int i = 0; i < kBigLW; ++i) {
+  for (int i = 0; i < P::LW; ++i) {
     const int f = wave + 8 * i, t = f >> 1, r = 8 * (f & 1) + lrow;
     if (t < kBigRows / 16) {
       const uint16_t* p = lm_row(a, m0 + t * 16 + r);
@@ -163,28 +177,33 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
     }
   }
   auto issue = [&](int ch) {
-    uint4* st = sbuf + (ch & 1) * kBigStageU4;
+    uint4* st = sbuf + (ch % P::NS) * P::STAGE_U4;
 #pragma unroll
-    for (int i = 0; i < kBigLW; ++i)
+    for (int i = 0; i < P::LW; ++i)
       __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ch * 64),
                                        (bd_stream::lds_void_t*)(st + (wave + 8 * i) * 64), 16, 0, 0);
   };
 
-  bd_f32x4 acc[8][4];
+  bd_f32x4 acc[P::MW][P::NWT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < P::MW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < P::NWT; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t sbase = bd_stream::lds_addr(sbuf);
   const uint32_t fo[2] = {(uint32_t)bd_stream::frag_offset(lane, 0), (uint32_t)bd_stream::frag_offset(lane, 1)};
-  const uint32_t xt0 = wr * 8 * 2048, wt0 = (kBigRows / 16 + wc * 4) * 2048;  // this wave's first X / W tile
+  // this wave's first X / W tile, as a byte offset in a stage
+  const uint32_t xt0 = wr * P::MW * 2048, wt0 = (kBigRows / 16 + wc * P::NWT) * 2048;
 
-  issue(0);
+#pragma unroll
+  for (int c = 0; c < P::NS - 1; ++c)
+    if (c < nch) issue(c);
   for (int ch = 0; ch < nch; ++ch) {
-    __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
-    bd_stream::pipe_barrier();  // chunk ch in LDS everywhere; the other stage is free
-    if (ch + 1 < nch) issue(ch + 1);
-    const uint32_t st = sbase + (ch & 1) * kBigStageU4 * 16;
+    // chunks issued so far: min(nch, ch + NS - 1); keep the later ones in flight
+    if (P::NS == 3 && ch + 1 < nch) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(P::LW));
+    else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+    bd_stream::pipe_barrier();  // chunk ch in LDS everywhere; the slot of ch - 1 is free
+    if (ch + P::NS - 1 < nch) issue(ch + P::NS - 1);
+    const uint32_t st = sbase + (ch % P::NS) * P::STAGE_U4 * 16;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 wb[4], xa[4];
@@ -193,56 +212,53 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
-      bd_stream::lds_frags_4(st + xt0 + 4 * 2048 + fo[ks], xa);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i0 = 4; i0 < P::MW; i0 += 4) {
+        bd_stream::lds_frags_4(st + xt0 + i0 * 2048 + fo[ks], xa);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[4 + i][j] = bd_mfma16(xa[i], wb[j], acc[4 + i][j]);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i0 + i][j] = bd_mfma16(xa[i], wb[j], acc[i0 + i][j]);
+      }
     }
   }
   __syncthreads();  // the stages become the reduction buffer
 
-  // acc[i][j][r]: row m0 + wr*128 + 16i + 4g + r, column n0 + wc*64 + 16j + l16
-  BdArgStat* red = reinterpret_cast<BdArgStat*>(sbuf);  // [4 column waves][256 rows]
+  // acc[i][j][r]: row m0 + wr*MW*16 + 16i + 4g + r, column n0 + wc*NWT*16 + 16j + l16
+  if (a.logits != nullptr) {  // debug dump of the raw logits (tests only)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < P::MW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wr * P::MW * 16 + 16 * i + 4 * g + r;
+#pragma unroll
+        for (int j = 0; j < P::NWT; ++j) {
+          const int col = n0 + (wc * P::NWT + j) * 16 + l16;
+          if (m < a.M && col < a.V) a.logits[(size_t)m * a.V + col] = acc[i][j][r];
+        }
+      }
+  }
+  const bool ragged = n0 + CT * 16 > a.V;  // only the last column block
+  int col[P::NWT];
+#pragma unroll
+  for (int j = 0; j < P::NWT; ++j) col[j] = n0 + (wc * P::NWT + j) * 16 + l16;
+  BdArgStat* red = reinterpret_cast<BdArgStat*>(sbuf);  // [WC column waves][256 rows]
+#pragma unroll
+  for (int i = 0; i < P::MW; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = wr * 128 + 16 * i + 4 * g + r;
-      BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
+      float v[P::NWT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wc * 64 + 16 * j + l16;
-        const float v = acc[i][j][r];
-        if (col < a.V && v > st.m) {
-          st.m = v;
-          st.i = col;
-        }
-      }
-      float sum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wc * 64 + 16 * j + l16;
-        if (col < a.V) sum += bd_exp2((acc[i][j][r] - st.m) * BD_LOG2E);
-      }
-      st.s = sum;
-      if (a.logits != nullptr && m0 + rl < a.M) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wc * 64 + 16 * j + l16;
-          if (col < a.V) a.logits[(size_t)(m0 + rl) * a.V + col] = acc[i][j][r];
-        }
-      }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
-      if (l16 == 0) red[wc * kBigRows + rl] = st;
+      for (int j = 0; j < P::NWT; ++j) v[j] = (ragged && col[j] >= a.V) ? BD_NEG_INF : acc[i][j][r];
+      const BdArgStat st = bd_row16_stat(v, col);
+      if (l16 == 0) red[wc * kBigRows + wr * P::MW * 16 + 16 * i + 4 * g + r] = st;
     }
   }
   __syncthreads();
   if (tid < kBigRows && m0 + tid < a.M) {
     BdArgStat st = red[tid];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) st = bd_stat_combine(st, red[w * kBigRows + tid]);
+    for (int w = 1; w < P::WC; ++w) st = bd_stat_combine(st, red[w * kBigRows + tid]);
     const size_t pi = (size_t)(m0 + tid) * a.nvt + cb;
     a.pmax[pi] = st.m;
     a.pidx[pi] = st.i;
@@ -349,7 +365,7 @@ BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
     p.cols_per_wg = kThreads;
     p.rows_per_wg = kF32Rows;
   } else if (M > 64) {
-    p.cols_per_wg = kBigCols;
+    p.cols_per_wg = (M > kNarrowMaxRows ? 16 : 8) * 16;
     p.rows_per_wg = kBigRows;
   } else {
     p.cols_per_wg = kNTW * 16;
@@ -375,7 +391,10 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
     switch (p.rows_per_wg / 16) {
       case kBigRows / 16: {
         const int cb8 = (p.nvt + 7) / 8 * 8;  // column blocks rounded up to whole XCD rounds
-        hipLaunchKernelGGL(lm_big_kernel, dim3(cb8 * p.nmb), dim3(kBigThreads), 0, s, a, p.nmb, p.nvt);
+        if (p.cols_per_wg == 256)
+          hipLaunchKernelGGL(lm_big_kernel<16>, dim3(cb8 * p.nmb), dim3(kBigThreads), 0, s, a, p.nmb, p.nvt);
+        else
+          hipLaunchKernelGGL(lm_big_kernel<8>, dim3(cb8 * p.nmb), dim3(kBigThreads), 0, s, a, p.nmb, p.nvt);
         break;
       }
       case 1: hipLaunchKernelGGL(lm_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a); break;

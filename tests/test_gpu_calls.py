@@ -109,6 +109,8 @@ LM_CASES = {
     # more than 64 rows: 256 x 256 tiles; two row blocks, the second ragged,
     # and a ragged last vocabulary block
     "bf16-big-ragged": ("bf16", 300, 310, 512, 5000, 1.0, 30.0, True),
+    # 65..256 rows: 256 x 128 tiles, ragged rows and vocabulary
+    "bf16-big-narrow-ragged": ("bf16", 200, 230, 512, 5000, 1.0, 30.0, True),
 }
 
 
