@@ -161,7 +161,7 @@ class Loop:
             dec.dc_step(self.s, S, cfg.tau)
         self.first = False
         self.steps += 1
-        bits = dec.mask_bits.cpu().numpy().view(np.uint64)      # 8 bytes per sequence
+        bits = dec.mask_bits_host()      # 8 bytes per sequence, refreshed by the step itself
         self.tokens += int(sum(bin(int(a) ^ int(b)).count("1") for a, b in zip(self.bits, bits)))
         self.bits = bits.copy()
         wmask = np.uint64(((1 << S) - 1) << (self.s * S))

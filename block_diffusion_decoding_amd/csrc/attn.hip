@@ -542,24 +542,41 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnK a) {
   const int nc = (L + a.n_blk + a.chunk - 1) / a.chunk;
   if (nc <= 1) return;
   const size_t rp = (size_t)a.QT * 16;
+  const size_t base = (size_t)bh * a.nchunks * rp + r;  // partial index of chunk c: base + c * rp
+  // the running max of chunk c is read by lane c % 64, then a wave max
   float M = BD_NEG_INF;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[2 * (((size_t)bh * a.nchunks + c) * rp + r)]);
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, a.part_ml[2 * (base + (size_t)c * rp)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   const float muse = (M == BD_NEG_INF) ? 0.f : M;
+  // weighted sum, 8 chunks per batch so their loads are in flight together;
+  // chunk indices past the end are clamped and weighted 0
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float lsum = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const size_t pi = ((size_t)bh * a.nchunks + c) * rp + r;
-    const float w = bd_exp2(a.part_ml[2 * pi] - muse);
-    lsum += w * a.part_ml[2 * pi + 1];
-    const float* po = a.part_o + pi * DH + PER * lane;
-    if constexpr (PER == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(po);
-      acc[0] += w * v.x;
-      acc[1] += w * v.y;
-    } else {
-      acc[0] += w * po[0];
+  for (int c0 = 0; c0 < nc; c0 += 8) {
+    float mv[8], lv[8], ov[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t pi = base + (size_t)min(c0 + u, nc - 1) * rp;
+      mv[u] = a.part_ml[2 * pi];
+      lv[u] = a.part_ml[2 * pi + 1];
+      const float* po = a.part_o + pi * DH + PER * lane;
+      if constexpr (PER == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(po);
+        ov[u][0] = v.x;
+        ov[u][1] = v.y;
+      } else {
+        ov[u][0] = po[0];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = (c0 + u < nc) ? bd_exp2(mv[u] - muse) : 0.f;
+      lsum += w * lv[u];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += w * ov[u][e];
     }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;

@@ -28,7 +28,10 @@ constexpr int kThreads = 256;
 #define BD_GEMM_MIN_CHUNKS 4
 #endif
 constexpr int kNTW = BD_GEMM_NTW;        // 16-column tiles per work-group
-constexpr int kNS = 3;                   // pipeline stages
+#ifndef BD_GEMM_NS
+#define BD_GEMM_NS 3
+#endif
+constexpr int kNS = BD_GEMM_NS;          // pipeline stages
 constexpr int kMaxSeg = 3;
 constexpr int kTargetWGs = BD_GEMM_TARGET_WGS;
 constexpr int kMinChunksPerSplit = BD_GEMM_MIN_CHUNKS;

@@ -329,32 +329,84 @@ __global__ __launch_bounds__(kThreads) void lm_f32_kernel(LmF a) {
   }
 }
 
-// Fold the tiles of each row in a fixed order; one work-group per row.
+// Fold the tiles of each row; one work-group per row.  Each thread keeps up to
+// kMergePer of the row's tile statistics in registers: the row max is found
+// first, then every tile's sum is scaled with one exp2 and the argmax is the
+// lowest column among the tiles that reach the max.  The order of the sums
+// is fixed, so the result is deterministic.
+constexpr int kMergePer = 8;
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = sh[0];
+  for (int w = 1; w < kThreads / 64; ++w) v = fmaxf(v, sh[w]);
+  return v;
+}
+
 __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_idx, int n_src, int M,
                                                             int nvt, const float* pmax, const int32_t* pidx,
                                                             const float* psum, int32_t* argmax, float* conf,
                                                             float* max_logit, float* lse) {
-  __shared__ BdArgStat red[kThreads / 64];
+  __shared__ float shm[kThreads / 64];
+  __shared__ float shs[kThreads / 64];
+  __shared__ int shi[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = blockIdx.x;
-  BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
-  for (int t = tid; t < nvt; t += kThreads) {
-    const size_t pi = (size_t)m * nvt + t;
-    st = bd_stat_combine(st, BdArgStat{pmax[pi], pidx[pi], psum[pi]});
+  const size_t rowb = (size_t)m * nvt;
+  float mx = BD_NEG_INF, s = 0.f;
+  int idx = INT_MAX;
+  if (nvt <= kMergePer * kThreads) {
+    float pm[kMergePer], ps[kMergePer];
+    int pi[kMergePer];
+#pragma unroll
+    for (int u = 0; u < kMergePer; ++u) {
+      const int t = tid + u * kThreads;
+      const bool ok = t < nvt;
+      pm[u] = ok ? pmax[rowb + t] : BD_NEG_INF;
+      ps[u] = ok ? psum[rowb + t] : 0.f;
+      pi[u] = ok ? pidx[rowb + t] : INT_MAX;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergePer; ++u) mx = fmaxf(mx, pm[u]);
+    mx = block_max(mx, shm);
+    const float mu = (mx == BD_NEG_INF) ? 0.f : mx;
+#pragma unroll
+    for (int u = 0; u < kMergePer; ++u) {
+      s += ps[u] * bd_exp2((pm[u] - mu) * BD_LOG2E);
+      if (pm[u] == mx && pm[u] != BD_NEG_INF) idx = min(idx, pi[u]);
+    }
+  } else {  // very large vocabularies: pairwise combines over a strided loop
+    BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
+    for (int t = tid; t < nvt; t += kThreads) st = bd_stat_combine(st, BdArgStat{pmax[rowb + t], pidx[rowb + t], psum[rowb + t]});
+    mx = block_max(st.m, shm);
+    const float mu = (mx == BD_NEG_INF) ? 0.f : mx;
+    s = (st.m == BD_NEG_INF) ? 0.f : st.s * bd_exp2((st.m - mu) * BD_LOG2E);
+    if (st.m == mx && st.m != BD_NEG_INF) idx = st.i;
   }
-  for (int off = 32; off > 0; off >>= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
-  if (lane == 0) red[wave] = st;
+  for (int off = 32; off > 0; off >>= 1) {
+    s += __shfl_xor(s, off);
+    idx = min(idx, __shfl_xor(idx, off));
+  }
+  if (lane == 0) {
+    shs[wave] = s;
+    shi[wave] = idx;
+  }
   __syncthreads();
   if (tid != 0) return;
-  st = red[0];
-  for (int w = 1; w < kThreads / 64; ++w) st = bd_stat_combine(st, red[w]);
+  for (int w = 1; w < kThreads / 64; ++w) {
+    s += shs[w];
+    idx = min(idx, shi[w]);
+  }
   const int src = row_idx ? row_idx[m] : m;
-  const bool ok = src >= 0 && src < n_src && st.s > 0.f;
+  const bool ok = src >= 0 && src < n_src && s > 0.f;
   const float nan = __builtin_nanf("");
-  argmax[m] = ok ? st.i : -1;
-  conf[m] = ok ? 1.f / st.s : nan;
-  if (max_logit != nullptr) max_logit[m] = ok ? st.m : nan;
-  if (lse != nullptr) lse[m] = ok ? st.m + bd_log2(st.s) * BD_LN2 : nan;
+  argmax[m] = ok ? idx : -1;
+  conf[m] = ok ? 1.f / s : nan;
+  if (max_logit != nullptr) max_logit[m] = ok ? mx : nan;
+  if (lse != nullptr) lse[m] = ok ? mx + bd_log2(s) * BD_LN2 : nan;
 }
 
 }  // namespace

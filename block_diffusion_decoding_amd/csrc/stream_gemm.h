@@ -68,7 +68,7 @@ struct Cfg {
   static constexpr int LDS_BYTES = NS * STAGE_U4 * 16;
   static_assert(MT == 1 || MT == 2 || MT == 4, "MT");
   static_assert(NTW % WN == 0, "split");
-  static_assert(NS == 2 || NS == 3, "stages");
+  static_assert(NS >= 2 && NS <= 5, "stages");
 };
 
 // LDS byte address of a shared-memory pointer.
@@ -187,8 +187,16 @@ __device__ __forceinline__ void mainloop(const XRowF& xrow, const uint16_t* xdum
     // chunks issued so far: min(nch, ch + NS - 1); keep the later ones in flight
     const int later = min(nch - ch - 1, C::NS - 2);
     if (later == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    else if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LW));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LW_LO));
+    else if (later == 1) {
+      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LW_LO));
+    } else if (later == 2) {
+      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::LW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::LW_LO));
+    } else {
+      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * C::LW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * C::LW_LO));
+    }
     pipe_barrier();  // chunk ch is in LDS for every wave; slot of ch - 1 is free
     if (ch + C::NS - 1 < nch) issue(ch + C::NS - 1);
     const uint4* st = sbuf + (ch % C::NS) * C::STAGE_U4;

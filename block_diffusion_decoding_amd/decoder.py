@@ -70,11 +70,18 @@ class BlockDecoder:
         self.o = torch.zeros(B, D, Hq, d, dtype=dt, device=dev)
         self.tokens = torch.zeros(B, D, dtype=torch.int32, device=dev)
         self.mask_bits = torch.zeros(B, dtype=torch.int64, device=dev)
+        # host copy of the mask bits, refreshed by the last node of every step
+        # (pinned, so the copy is a plain DMA into it and the host only waits
+        # for the step's event)
+        self.bits_host = torch.zeros(B, dtype=torch.int64, pin_memory=True)
+        self._bits_ev = torch.cuda.Event()
+        self._bits_fresh = False
         self.plant = None
         self.n_unmasked = torch.zeros(B, dtype=torch.int32, device=dev)
         self._win = {}
         self.last = None
         self.lm_events = None   # list of (start, end) events around LM-head calls when set
+        self._capturing = False
         self.graphs = {}        # (kind, s) -> captured HIP graph of that step
 
     # ------------------------------------------------------------------ state
@@ -97,6 +104,7 @@ class BlockDecoder:
             bits |= m[:, j].astype(np.uint64) << np.uint64(j)
         self.tokens.copy_(torch.from_numpy(t).to(self.device))
         self.mask_bits.copy_(torch.from_numpy(bits.view(np.int64)).to(self.device))
+        self._bits_fresh = False
 
     def set_block(self, tokens, masked, plant=None, carry_offset=None):
         """Current block: tokens [B, D], masked [B, D] bool, optional plant
@@ -120,8 +128,16 @@ class BlockDecoder:
         B, D = self.dims.B, self.dims.D
         self.set_block(np.zeros((B, D), np.int32), np.ones((B, D), bool))
 
+    def mask_bits_host(self) -> np.ndarray:
+        """Mask bits [B] (uint64) after the last step, without a blocking
+        device-to-host copy when a step produced them."""
+        if not self._bits_fresh:
+            return self.mask_bits.cpu().numpy().view(np.uint64).copy()
+        self._bits_ev.synchronize()
+        return self.bits_host.numpy().view(np.uint64).copy()
+
     def masked_host(self) -> np.ndarray:
-        bits = self.mask_bits.cpu().numpy().view(np.uint64)
+        bits = self.mask_bits_host()
         return np.stack([(bits >> np.uint64(j)) & np.uint64(1) for j in range(self.dims.D)], 1).astype(bool)
 
     # ------------------------------------------------------------ step parts
@@ -170,29 +186,36 @@ class BlockDecoder:
             self.lm_events.append(ev)
         ops.bd_threshold_unmask(w["conf"], w["argmax"], self.tokens, self.mask_bits, win_lo=s * S,
                                 threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
+        self.bits_host.copy_(self.mask_bits, non_blocking=True)
         self.last = w
+
+    def _step_done(self):
+        self._bits_ev.record()
+        self._bits_fresh = True
 
     def e_step(self, s: int, S: int, tau: float, eager: bool = False):
         """Exact step for window s; refreshes the DualCache snapshot."""
-        if not eager and self._replay("E", s, S, tau):
-            return
-        dm = self.dims
-        B, D = dm.B, dm.D
-        X, o = self._forward_rows(0, D)
-        ops.bd_linear(o, dense(B * D), self.W["Wo"], self.H, rows(D, 1 + D, 1), M=B * D,
-                      res=X, rr=dense(B * D))
-        self._lm_and_unmask(s, S, tau)
+        if eager or not self._replay("E", s, S, tau):
+            dm = self.dims
+            B, D = dm.B, dm.D
+            X, o = self._forward_rows(0, D)
+            ops.bd_linear(o, dense(B * D), self.W["Wo"], self.H, rows(D, 1 + D, 1), M=B * D,
+                          res=X, rr=dense(B * D))
+            self._lm_and_unmask(s, S, tau)
+        if not self._capturing:
+            self._step_done()
 
     def dc_step(self, s: int, S: int, tau: float, eager: bool = False):
         """DualCache step for window s (snapshot rows outside the window)."""
-        if not eager and self._replay("DC", s, S, tau):
-            return
-        dm = self.dims
-        B, D = dm.B, dm.D
-        X, o = self._forward_rows(s * S, S)
-        ops.bd_linear(o, dense(B * S), self.W["Wo"], self.H, rows(S, 1 + D, 1 + s * S), M=B * S,
-                      res=X, rr=dense(B * S))
-        self._lm_and_unmask(s, S, tau)
+        if eager or not self._replay("DC", s, S, tau):
+            dm = self.dims
+            B, D = dm.B, dm.D
+            X, o = self._forward_rows(s * S, S)
+            ops.bd_linear(o, dense(B * S), self.W["Wo"], self.H, rows(S, 1 + D, 1 + s * S), M=B * S,
+                          res=X, rr=dense(B * S))
+            self._lm_and_unmask(s, S, tau)
+        if not self._capturing:
+            self._step_done()
 
     def _commit_kernels(self):
         dm = self.dims
@@ -262,12 +285,16 @@ class BlockDecoder:
             self._window(s, S)
         torch.cuda.synchronize()
         self.graphs = {}
-        for s in range(D // S):
-            for kind, fn in (("E", self.e_step), ("DC", self.dc_step)):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    fn(s, S, tau, eager=True)
-                self.graphs[(kind, s)] = g
+        self._capturing = True
+        try:
+            for s in range(D // S):
+                for kind, fn in (("E", self.e_step), ("DC", self.dc_step)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        fn(s, S, tau, eager=True)
+                    self.graphs[(kind, s)] = g
+        finally:
+            self._capturing = False
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             self._commit_kernels()
@@ -301,7 +328,7 @@ class BlockDecoder:
                     if k >= steps_per_window:
                         break
                 else:
-                    bits = self.mask_bits.cpu().numpy().view(np.uint64)
+                    bits = self.mask_bits_host()
                     wmask = np.uint64(((1 << S) - 1) << (s * S))
                     if not np.any(bits & wmask):
                         break

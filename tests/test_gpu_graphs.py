@@ -49,6 +49,9 @@ def test_captured_steps_replay_like_eager():
                 torch.cuda.synchronize()
                 for a, b in zip(state(eager), state(graph)):
                     assert torch.equal(a, b), f"block {blk} window {s} step {k} ({kind}) differs"
+                # the host copy of the mask bits that each step refreshes
+                want = eager.mask_bits.cpu().numpy().view(np.uint64)
+                assert np.array_equal(eager.mask_bits_host(), want) and np.array_equal(graph.mask_bits_host(), want)
                 n_cmp += 1
         eager.set_tokens(eager.tokens.cpu().numpy(), np.zeros((cfg.B, cfg.D), bool))
         graph.set_tokens(graph.tokens.cpu().numpy(), np.zeros((cfg.B, cfg.D), bool))
