@@ -142,6 +142,7 @@ class Loop:
         self.first = True
         self.steps = self.tokens = self.commits = 0
         self.bits = None
+        self.wmask = [np.uint64(((1 << cfg.S) - 1) << (w * cfg.S)) for w in range(cfg.D // cfg.S)]
         self._new_block()
 
     def _new_block(self):
@@ -162,10 +163,9 @@ class Loop:
         self.first = False
         self.steps += 1
         bits = dec.mask_bits_host()      # 8 bytes per sequence, refreshed by the step itself
-        self.tokens += int(sum(bin(int(a) ^ int(b)).count("1") for a, b in zip(self.bits, bits)))
-        self.bits = bits.copy()
-        wmask = np.uint64(((1 << S) - 1) << (self.s * S))
-        if not np.any(bits & wmask):
+        self.tokens += int(np.bitwise_count(self.bits ^ bits).sum())
+        self.bits = bits
+        if not (bits & self.wmask[self.s]).any():
             self.s += 1
             self.first = True
             if self.s == cfg.D // S:

@@ -27,7 +27,12 @@ constexpr int kThreads = 256;
 #ifndef BD_GEMM_MIN_CHUNKS
 #define BD_GEMM_MIN_CHUNKS 4
 #endif
-constexpr int kNTW = BD_GEMM_NTW;        // 16-column tiles per work-group
+#ifndef BD_GEMM_NTW_M64
+#define BD_GEMM_NTW_M64 4
+#endif
+// 16-column tiles per work-group: narrower at 64 rows (more column work-groups,
+// a smaller K split, half the partial sums to add)
+__host__ __device__ constexpr int ntw_for(int MT) { return MT == 4 ? BD_GEMM_NTW_M64 : BD_GEMM_NTW; }
 #ifndef BD_GEMM_NS
 #define BD_GEMM_NS 3
 #endif
@@ -63,6 +68,7 @@ __device__ __forceinline__ void gemm_store(const GemmK& a, int seg, int m, int c
 // device-scope fences, i.e. L2 write-backs, per work-group).
 template <int MT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
+  constexpr int kNTW = ntw_for(MT);
   using C = bd_stream::Cfg<MT, kNTW, kNS>;
   constexpr int TILE = MT * 16 * kNTW * 16;
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
@@ -111,6 +117,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
 // Adds the K slices of every tile in slice order, then residual and store.
 template <int MT>
 __global__ __launch_bounds__(kThreads) void gemm_reduce_kernel(GemmK a) {
+  constexpr int kNTW = ntw_for(MT);
   constexpr int TILE = MT * 16 * kNTW * 16;
   const int bx = blockIdx.x;
   const int seg = (a.nseg > 2 && bx >= a.wg_begin[2]) ? 2 : (a.nseg > 1 && bx >= a.wg_begin[1]) ? 1 : 0;
@@ -214,6 +221,7 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg) {
   if (dt == BD_F32) return p;
   const int mt = (M + 15) / 16;
   p.MT = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+  const int kNTW = ntw_for(p.MT);
   p.nx = 0;
   for (int i = 0; i < nseg; ++i) p.nx += (N[i] + kNTW * 16 - 1) / (kNTW * 16);
   p.ny = (M + p.MT * 16 - 1) / (p.MT * 16);
@@ -256,7 +264,7 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
     a.rr[i] = segs[i].rr;
     a.N[i] = segs[i].N;
     a.wg_begin[i] = wg;
-    wg += (segs[i].N + kNTW * 16 - 1) / (kNTW * 16);
+    wg += (segs[i].N + ntw_for(p.MT) * 16 - 1) / (ntw_for(p.MT) * 16);
   }
   for (int i = nseg; i <= kMaxSeg; ++i) a.wg_begin[i] = wg;
   a.ksplit = p.ksplit;
