@@ -95,10 +95,10 @@ size_t bd_lmhead_workspace_size(bd_dtype dt, int M, int hidden, int V) {
   return bd_lm_plan(dt, M, hidden, V).ws_bytes;
 }
 
-bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
-                               const int32_t* row_idx, const void* w, int32_t* argmax, float* conf,
-                               float* max_logit, float* lse, float* logits, void* workspace, size_t ws_bytes,
-                               void* stream) {
+static bd_status lm_common(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
+                           const int32_t* row_idx, const int32_t* out_pos, const int32_t* m_dev, int n_out,
+                           const void* w, int32_t* argmax, float* conf, float* max_logit, float* lse, float* logits,
+                           void* workspace, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
   if (M == 0) return BD_OK;
   if (hidden <= 0 || V <= 0 || n_src <= 0 || !h_src || !w || !argmax || !conf) return BD_EINVAL;
@@ -123,7 +123,39 @@ bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V, const void
   a.pmax = static_cast<float*>(workspace);
   a.psum = a.pmax + n;
   a.pidx = reinterpret_cast<int32_t*>(a.psum + n);
+  a.m_dev = m_dev;
+  a.out_pos = out_pos;
+  a.n_out = n_out;
   return hip_status(bd_lm_launch(dt, p, a, static_cast<hipStream_t>(stream)));
+}
+
+bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
+                               const int32_t* row_idx, const void* w, int32_t* argmax, float* conf,
+                               float* max_logit, float* lse, float* logits, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  return lm_common(dt, M, hidden, V, h_src, n_src, row_idx, nullptr, nullptr, 0, w, argmax, conf, max_logit, lse,
+                   logits, workspace, ws_bytes, stream);
+}
+
+bd_status bd_lmhead_confidence_rows(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
+                                    const int32_t* row_idx, const int32_t* out_pos, const int32_t* m_dev, int n_out,
+                                    const void* w, int32_t* argmax, float* conf, float* max_logit, float* lse,
+                                    float* logits, void* workspace, size_t ws_bytes, void* stream) {
+  if (M > 0 && (m_dev == nullptr || row_idx == nullptr || out_pos == nullptr || n_out < 0)) return BD_EINVAL;
+  return lm_common(dt, M, hidden, V, h_src, n_src, row_idx, out_pos, m_dev, n_out, w, argmax, conf, max_logit,
+                   lse, logits, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+bd_status bd_candidate_rows(int B, int win_lo, int win_len, const uint64_t* mask_bits, int rows_per_seq,
+                            int32_t* row_idx, int32_t* out_pos, int32_t* count, void* stream) {
+  if (B < 0) return BD_EINVAL;
+  if (B == 0) return BD_OK;
+  if (win_lo < 0 || win_len < 1 || win_len > 64 || win_lo + win_len > 64) return BD_EINVAL;
+  if (rows_per_seq < win_lo + win_len || (long)B * win_len > 4096) return BD_EINVAL;
+  if (!mask_bits || !row_idx || !out_pos || !count) return BD_EINVAL;
+  return hip_status(bd_candidates_launch(B, win_lo, win_len, mask_bits, rows_per_seq, row_idx, out_pos, count,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------

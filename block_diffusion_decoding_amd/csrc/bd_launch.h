@@ -64,9 +64,14 @@ struct BdLmArgs {
   float* pmax;
   int32_t* pidx;
   float* psum;
+  const int32_t* m_dev;    // device row count (rows >= it are skipped), or NULL = M
+  const int32_t* out_pos;  // output slot of row m, or NULL = m
+  int n_out;               // output slots when out_pos is given
 };
 
 hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& a, hipStream_t s);
+hipError_t bd_candidates_launch(int B, int win_lo, int win_len, const uint64_t* mask_bits, int rows_per_seq,
+                                int32_t* row_idx, int32_t* out_pos, int32_t* count, hipStream_t s);
 
 // ---- projections -------------------------------------------------------------
 struct BdGemmSeg {

@@ -48,10 +48,19 @@ struct LmK {
   float* pmax;
   int32_t* pidx;
   float* psum;
+  const int32_t* m_dev;  // device row count, or NULL
 };
 
-__device__ __forceinline__ const uint16_t* lm_row(const LmK& a, int m) {
-  if (m >= a.M) return nullptr;
+// Rows taken: min(M, *m_dev) when a device count is given (the row list of
+// the masked candidates), else M.
+__device__ __forceinline__ int lm_rows(const int32_t* m_dev, int M) {
+  if (m_dev == nullptr) return M;
+  const int c = *m_dev;
+  return c < 0 ? 0 : (c < M ? c : M);
+}
+
+__device__ __forceinline__ const uint16_t* lm_row(const LmK& a, int m, int Meff) {
+  if (m >= Meff) return nullptr;
   const int r = a.row_idx ? a.row_idx[m] : m;
   if (r < 0 || r >= a.n_src) return nullptr;
   return a.h + (size_t)r * a.hidden;
@@ -66,9 +75,11 @@ __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int m0 = blockIdx.y * MT * 16;
   const int n0 = blockIdx.x * kNTW * 16;
+  const int Meff = lm_rows(a.m_dev, a.M);
+  if (m0 >= Meff) return;  // the whole row block is past the row count
 
   bd_f32x4 acc[C::MTW][C::NTP];
-  auto xrow = [&](int m) { return lm_row(a, m); };
+  auto xrow = [&](int m) { return lm_row(a, m, Meff); };
   bd_stream::mainloop<C>(xrow, a.h, m0, a.w, a.V, a.hidden, n0, sbuf, acc);
 
   // rows m0 + (wm*MTW + i)*16 + 4g + r, columns n0 + (wn*NTP + j)*16 + l16
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
 #pragma unroll
         for (int j = 0; j < C::NTP; ++j) {
           const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-          if (m < a.M && col < a.V) a.logits[(size_t)m * a.V + col] = acc[i][j][r];
+          if (m < Meff && col < a.V) a.logits[(size_t)m * a.V + col] = acc[i][j][r];
         }
       }
   }
@@ -102,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
     }
   }
   __syncthreads();
-  if (tid < MT * 16 && m0 + tid < a.M) {
+  if (tid < MT * 16 && m0 + tid < Meff) {
     BdArgStat st = red[tid];
 #pragma unroll
     for (int w = 1; w < C::WN; ++w) st = bd_stat_combine(st, red[w * (MT * 16) + tid]);
@@ -160,6 +171,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
   if (cb >= cb_count) return;
   const int m0 = rb * kBigRows, n0 = cb * CT * 16;
   const int nch = a.hidden / 64;
+  const int Meff = lm_rows(a.m_dev, a.M);
+  if (m0 >= Meff) return;  // the whole row block is past the row count
 
   // DMA sources: instruction f covers rows 8*(f%2)..+7 of stage tile f/2;
   // tiles 0..15 are X row tiles, the next CT are W column tiles.
@@ -169,20 +182,47 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
   for (int i = 0; i < P::LW; ++i) {
     const int f = wave + 8 * i, t = f >> 1, r = 8 * (f & 1) + lrow;
     if (t < kBigRows / 16) {
-      const uint16_t* p = lm_row(a, m0 + t * 16 + r);
+      const uint16_t* p = lm_row(a, m0 + t * 16 + r, Meff);
       src[i] = (p ? p : a.h) + 8 * lkb;
     } else {
       const int col = n0 + (t - kBigRows / 16) * 16 + r;
       src[i] = a.w + (size_t)(col < a.V ? col : 0) * a.hidden + 8 * lkb;
     }
   }
+  // X tiles past the row count are not loaded (their MFMAs are skipped);
+  // the number of loads this wave issues per stage is then a wave-uniform
+  // value and the pipeline waits select the matching immediate.
+  const int live_tiles = (Meff - m0 + 15) / 16;
+  bool ld[P::LW];
+  int issued = 0;
+#pragma unroll
+  for (int i = 0; i < P::LW; ++i) {
+    const int t = (wave + 8 * i) >> 1;
+    ld[i] = t >= kBigRows / 16 || t < live_tiles;
+    issued += ld[i] ? 1 : 0;
+  }
   auto issue = [&](int ch) {
     uint4* st = sbuf + (ch % P::NS) * P::STAGE_U4;
 #pragma unroll
     for (int i = 0; i < P::LW; ++i)
-      __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ch * 64),
-                                       (bd_stream::lds_void_t*)(st + (wave + 8 * i) * 64), 16, 0, 0);
+      if (ld[i])
+        __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ch * 64),
+                                         (bd_stream::lds_void_t*)(st + (wave + 8 * i) * 64), 16, 0, 0);
   };
+  auto wait_later_stage = [&]() {  // vmcnt <= loads of one stage
+    switch (issued) {
+      case 0: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(1)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(2)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(3)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(4)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(5)); break;
+      case 6: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(6)); break;
+      case 7: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(7)); break;
+      default: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(8)); break;
+    }
+  };
+  static_assert(P::LW <= 8, "wait immediates");
 
   bd_f32x4 acc[P::MW][P::NWT];
 #pragma unroll
@@ -191,15 +231,21 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
     for (int j = 0; j < P::NWT; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t sbase = bd_stream::lds_addr(sbuf);
   const uint32_t fo[2] = {(uint32_t)bd_stream::frag_offset(lane, 0), (uint32_t)bd_stream::frag_offset(lane, 1)};
-  // this wave's first X / W tile, as a byte offset in a stage
-  const uint32_t xt0 = wr * P::MW * 2048, wt0 = (kBigRows / 16 + wc * P::NWT) * 2048;
+  // Row tiles are dealt to the row waves in turn (tile i of this wave is row
+  // tile i*WR + wr), so that the waves sharing a SIMD get equal shares when
+  // rows past the count are skipped.  First X / W tile as a byte offset.
+  const uint32_t xt0 = wr * 2048, wt0 = (kBigRows / 16 + wc * P::NWT) * 2048;
+  constexpr int XS = P::WR * 2048;  // byte stride between this wave's X tiles
+  // this wave's 16-row tiles that hold rows below the count (MFMAs of the
+  // others are skipped: the candidate rows are listed first)
+  const int live = min(P::MW, max(0, (live_tiles - wr + P::WR - 1) / P::WR));
 
 #pragma unroll
   for (int c = 0; c < P::NS - 1; ++c)
     if (c < nch) issue(c);
   for (int ch = 0; ch < nch; ++ch) {
     // chunks issued so far: min(nch, ch + NS - 1); keep the later ones in flight
-    if (P::NS == 3 && ch + 1 < nch) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(P::LW));
+    if (P::NS == 3 && ch + 1 < nch) wait_later_stage();
     else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
     bd_stream::pipe_barrier();  // chunk ch in LDS everywhere; the slot of ch - 1 is free
     if (ch + P::NS - 1 < nch) issue(ch + P::NS - 1);
@@ -207,34 +253,37 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 wb[4], xa[4];
-      bd_stream::lds_frags_4x4(st + xt0 + fo[ks], st + wt0 + fo[ks], xa, wb);
+      bd_stream::lds_frags_4x4<XS>(st + xt0 + fo[ks], st + wt0 + fo[ks], xa, wb);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        if (i < live)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
 #pragma unroll
       for (int i0 = 4; i0 < P::MW; i0 += 4) {
-        bd_stream::lds_frags_4(st + xt0 + i0 * 2048 + fo[ks], xa);
+        if (i0 >= live) break;
+        bd_stream::lds_frags_4<XS>(st + xt0 + i0 * XS + fo[ks], xa);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
+          if (i0 + i < live)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i0 + i][j] = bd_mfma16(xa[i], wb[j], acc[i0 + i][j]);
+            for (int j = 0; j < 4; ++j) acc[i0 + i][j] = bd_mfma16(xa[i], wb[j], acc[i0 + i][j]);
       }
     }
   }
   __syncthreads();  // the stages become the reduction buffer
 
-  // acc[i][j][r]: row m0 + wr*MW*16 + 16i + 4g + r, column n0 + wc*NWT*16 + 16j + l16
+  // acc[i][j][r]: row m0 + (i*WR + wr)*16 + 4g + r, column n0 + wc*NWT*16 + 16j + l16
   if (a.logits != nullptr) {  // debug dump of the raw logits (tests only)
 #pragma unroll
     for (int i = 0; i < P::MW; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wr * P::MW * 16 + 16 * i + 4 * g + r;
+        const int m = m0 + (i * P::WR + wr) * 16 + 4 * g + r;
 #pragma unroll
         for (int j = 0; j < P::NWT; ++j) {
           const int col = n0 + (wc * P::NWT + j) * 16 + l16;
-          if (m < a.M && col < a.V) a.logits[(size_t)m * a.V + col] = acc[i][j][r];
+          if (m < Meff && col < a.V) a.logits[(size_t)m * a.V + col] = acc[i][j][r];
         }
       }
   }
@@ -251,11 +300,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
 #pragma unroll
       for (int j = 0; j < P::NWT; ++j) v[j] = (ragged && col[j] >= a.V) ? BD_NEG_INF : acc[i][j][r];
       const BdArgStat st = bd_row16_stat(v, col);
-      if (l16 == 0) red[wc * kBigRows + wr * P::MW * 16 + 16 * i + 4 * g + r] = st;
+      if (l16 == 0) red[wc * kBigRows + (i * P::WR + wr) * 16 + 4 * g + r] = st;
     }
   }
   __syncthreads();
-  if (tid < kBigRows && m0 + tid < a.M) {
+  if (tid < kBigRows && m0 + tid < Meff) {
     BdArgStat st = red[tid];
 #pragma unroll
     for (int w = 1; w < P::WC; ++w) st = bd_stat_combine(st, red[w * kBigRows + tid]);
@@ -276,6 +325,7 @@ struct LmF {
   float* pmax;
   int32_t* pidx;
   float* psum;
+  const int32_t* m_dev;
 };
 
 __global__ __launch_bounds__(kThreads) void lm_f32_kernel(LmF a) {
@@ -284,11 +334,13 @@ __global__ __launch_bounds__(kThreads) void lm_f32_kernel(LmF a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = blockIdx.x * kThreads + tid;
   const int m0 = blockIdx.y * kF32Rows;
+  const int Meff = lm_rows(a.m_dev, a.M);
+  if (m0 >= Meff) return;
   const float* hrow[kF32Rows];
 #pragma unroll
   for (int r = 0; r < kF32Rows; ++r) {
     const int m = m0 + r;
-    const int src = (m < a.M) ? (a.row_idx ? a.row_idx[m] : m) : -1;
+    const int src = (m < Meff) ? (a.row_idx ? a.row_idx[m] : m) : -1;
     hrow[r] = (src >= 0 && src < a.n_src) ? a.h + (size_t)src * a.hidden : nullptr;
   }
   float acc[kF32Rows];
@@ -312,13 +364,13 @@ __global__ __launch_bounds__(kThreads) void lm_f32_kernel(LmF a) {
 #pragma unroll
   for (int r = 0; r < kF32Rows; ++r) {
     const int m = m0 + r;
-    if (a.logits != nullptr && m < a.M && col < a.V) a.logits[(size_t)m * a.V + col] = acc[r];
+    if (a.logits != nullptr && m < Meff && col < a.V) a.logits[(size_t)m * a.V + col] = acc[r];
     BdArgStat st = (col < a.V) ? BdArgStat{acc[r], col, 1.f} : BdArgStat{BD_NEG_INF, INT_MAX, 0.f};
     for (int off = 1; off < 64; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
     __syncthreads();
     if (lane == 0) red[wave] = st;
     __syncthreads();
-    if (tid == 0 && m < a.M) {
+    if (tid == 0 && m < Meff) {
       BdArgStat t = red[0];
       for (int w = 1; w < kThreads / 64; ++w) t = bd_stat_combine(t, red[w]);
       const size_t pi = (size_t)m * a.nvt + blockIdx.x;
@@ -349,12 +401,16 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
 __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_idx, int n_src, int M,
                                                             int nvt, const float* pmax, const int32_t* pidx,
                                                             const float* psum, int32_t* argmax, float* conf,
-                                                            float* max_logit, float* lse) {
+                                                            float* max_logit, float* lse, const int32_t* m_dev,
+                                                            const int32_t* out_pos, int n_out) {
   __shared__ float shm[kThreads / 64];
   __shared__ float shs[kThreads / 64];
   __shared__ int shi[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = blockIdx.x;
+  if (m >= lm_rows(m_dev, M)) return;
+  const int om = out_pos ? out_pos[m] : m;  // output slot of this row
+  if (out_pos != nullptr && (om < 0 || om >= n_out)) return;
   const size_t rowb = (size_t)m * nvt;
   float mx = BD_NEG_INF, s = 0.f;
   int idx = INT_MAX;
@@ -403,10 +459,10 @@ __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_i
   const int src = row_idx ? row_idx[m] : m;
   const bool ok = src >= 0 && src < n_src && s > 0.f;
   const float nan = __builtin_nanf("");
-  argmax[m] = ok ? idx : -1;
-  conf[m] = ok ? 1.f / s : nan;
-  if (max_logit != nullptr) max_logit[m] = ok ? mx : nan;
-  if (lse != nullptr) lse[m] = ok ? mx + bd_log2(s) * BD_LN2 : nan;
+  argmax[om] = ok ? idx : -1;
+  conf[om] = ok ? 1.f / s : nan;
+  if (max_logit != nullptr) max_logit[om] = ok ? mx : nan;
+  if (lse != nullptr) lse[om] = ok ? mx + bd_log2(s) * BD_LN2 : nan;
 }
 
 }  // namespace
@@ -435,11 +491,11 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
   const dim3 grid(p.nvt, p.nmb);
   if (dt == BD_F32) {
     LmF a{static_cast<const float*>(x.h), x.n_src, x.row_idx, static_cast<const float*>(x.w), x.logits,
-          x.M, x.hidden, x.V, p.nvt, x.pmax, x.pidx, x.psum};
+          x.M, x.hidden, x.V, p.nvt, x.pmax, x.pidx, x.psum, x.m_dev};
     hipLaunchKernelGGL(lm_f32_kernel, grid, dim3(kThreads), 0, s, a);
   } else {
     LmK a{static_cast<const uint16_t*>(x.h), x.n_src, x.row_idx, static_cast<const uint16_t*>(x.w), x.logits,
-          x.M, x.hidden, x.V, p.nvt, x.pmax, x.pidx, x.psum};
+          x.M, x.hidden, x.V, p.nvt, x.pmax, x.pidx, x.psum, x.m_dev};
     switch (p.rows_per_wg / 16) {
       case kBigRows / 16: {
         const int cb8 = (p.nvt + 7) / 8 * 8;  // column blocks rounded up to whole XCD rounds
@@ -457,6 +513,7 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lm_merge_kernel, dim3(x.M), dim3(kThreads), 0, s, x.row_idx, x.n_src, x.M,
-                     p.nvt, x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse);
+                     p.nvt, x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse, x.m_dev, x.out_pos,
+                     x.n_out);
   return hipGetLastError();
 }

@@ -79,25 +79,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Fragment reads written as asm with the wait inside the block: the compiler
 // then cannot guard them with a wait for every outstanding global->LDS DMA
 // (it cannot tell which LDS bytes a DMA writes), which would serialise the
-// next stage's loads with this stage's MFMAs.  x[i] from a + 2048*i, w[j] from
-// b + 2048*j (consecutive 2 KiB tiles), byte addresses.
+// next stage's loads with this stage's MFMAs.  Tiles are 2 KiB.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 as_uint4(u32x4_t r) { return make_uint4(r[0], r[1], r[2], r[3]); }
 
+// x[i] from a + XS*i, w[j] from b + 2048*j (byte addresses and strides).
+template <int XS = 2048>
 __device__ __forceinline__ void lds_frags_4x4(uint32_t a, uint32_t b, uint4 (&x)[4], uint4 (&w)[4]) {
   u32x4_t r[8];
   asm volatile(
       "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:2048\n\t"
-      "ds_read_b128 %2, %8 offset:4096\n\t"
-      "ds_read_b128 %3, %8 offset:6144\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
       "ds_read_b128 %4, %9\n\t"
       "ds_read_b128 %5, %9 offset:2048\n\t"
       "ds_read_b128 %6, %9 offset:4096\n\t"
       "ds_read_b128 %7, %9 offset:6144\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a), "v"(b)
+      : "v"(a), "v"(b), "i"(XS), "i"(2 * XS), "i"(3 * XS)
       : "memory");
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -106,16 +107,18 @@ __device__ __forceinline__ void lds_frags_4x4(uint32_t a, uint32_t b, uint4 (&x)
   }
 }
 
+// x[i] from a + XS*i.
+template <int XS = 2048>
 __device__ __forceinline__ void lds_frags_4(uint32_t a, uint4 (&x)[4]) {
   u32x4_t r[4];
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:2048\n\t"
-      "ds_read_b128 %2, %4 offset:4096\n\t"
-      "ds_read_b128 %3, %4 offset:6144\n\t"
+      "ds_read_b128 %1, %4 offset:%5\n\t"
+      "ds_read_b128 %2, %4 offset:%6\n\t"
+      "ds_read_b128 %3, %4 offset:%7\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(a)
+      : "v"(a), "i"(XS), "i"(2 * XS), "i"(3 * XS)
       : "memory");
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = as_uint4(r[i]);

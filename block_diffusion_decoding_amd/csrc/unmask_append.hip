@@ -9,6 +9,11 @@
 //
 // Append: Key design 3 and the v2 news article's hierarchical-cache
 // paragraph -- a finished block's K/V become read-only context.
+//
+// Candidate rows: Key design 3 (only masked positions of the active window
+// are predicted) and Key design 2 (candidate j reads the output row of
+// position j-1): the masked window positions of the whole batch are listed
+// in (sequence, position) order so that the LM head computes only them.
 #include "bd_device.h"
 #include "bd_launch.h"
 
@@ -71,7 +76,49 @@ __global__ __launch_bounds__(256) void append_kernel(int Hkv, int row_bytes, int
   if (threadIdx.x == 0) kv_len[b] = L + n_rows;
 }
 
+// One work-group of 256 threads walks the B*win_len window entries in
+// rounds of 256: a ballot per wave and the wave totals give each candidate
+// its slot; entries past the count are set to -1.
+__global__ __launch_bounds__(256) void candidates_kernel(int B, int win_lo, int win_len, const uint64_t* mask_bits,
+                                                        int rows_per_seq, int32_t* row_idx, int32_t* out_pos,
+                                                        int32_t* count) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = B * win_len;
+  int base = 0;
+  for (int e0 = 0; e0 < n; e0 += 256) {
+    const int e = e0 + tid;
+    const int b = e / win_len, r = e - b * win_len;
+    const int pos = win_lo + r;
+    const bool cand = e < n && ((mask_bits[b < B ? b : 0] >> pos) & 1ull);
+    const uint64_t bal = __ballot(cand);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (cand) {
+      row_idx[off + before] = b * rows_per_seq + pos;
+      out_pos[off + before] = e;
+    }
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  for (int e = base + tid; e < n; e += 256) {
+    row_idx[e] = -1;
+    out_pos[e] = -1;
+  }
+  if (tid == 0) *count = base;
+}
+
 }  // namespace
+
+hipError_t bd_candidates_launch(int B, int win_lo, int win_len, const uint64_t* mask_bits, int rows_per_seq,
+                                int32_t* row_idx, int32_t* out_pos, int32_t* count, hipStream_t s) {
+  hipLaunchKernelGGL(candidates_kernel, dim3(1), dim3(256), 0, s, B, win_lo, win_len, mask_bits, rows_per_seq,
+                     row_idx, out_pos, count);
+  return hipGetLastError();
+}
 
 hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* conf, const int32_t* argmax,
                             float threshold, int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,

@@ -50,8 +50,13 @@ class Dims:
 class BlockDecoder:
     """Owns the device state of a batch of sequences decoded block by block."""
 
-    def __init__(self, dims: Dims, weights: dict, dtype=torch.bfloat16, device="cuda"):
+    def __init__(self, dims: Dims, weights: dict, dtype=torch.bfloat16, device="cuda", compact=None):
+        """``compact``: run the LM head only on the masked candidates of the
+        window (bd_candidate_rows + bd_lmhead_confidence_rows); None = when a
+        window has more than 64 rows (B*S > 64), where the LM head is
+        MFMA-bound and skipped rows save time."""
         self.dims = dims
+        self.compact = compact
         self.dtype = dtype
         self.device = torch.device(device)
         dev, dt = self.device, dtype
@@ -149,6 +154,9 @@ class BlockDecoder:
             B, D = self.dims.B, self.dims.D
             idx = np.array([b * (1 + D) + s * S + r for b in range(B) for r in range(S)], dtype=np.int32)
             w = dict(row_idx=torch.from_numpy(idx).to(self.device),
+                     cand_rows=torch.zeros(B * S, dtype=torch.int32, device=self.device),
+                     cand_pos=torch.zeros(B * S, dtype=torch.int32, device=self.device),
+                     cand_count=torch.zeros(1, dtype=torch.int32, device=self.device),
                      argmax=torch.zeros(B, S, dtype=torch.int32, device=self.device),
                      conf=torch.zeros(B, S, dtype=torch.float32, device=self.device),
                      maxl=torch.zeros(B, S, dtype=torch.float32, device=self.device),
@@ -179,8 +187,16 @@ class BlockDecoder:
         if self.lm_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record()
-        ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"], w["conf"],
-                                 max_logit=w["maxl"], lse=w["lse"])
+        if self.uses_compaction(S):
+            # only the masked candidates: their conf/argmax land at their window
+            # slots; the other slots are not candidates and the unmask ignores them
+            ops.bd_candidate_rows(self.mask_bits, w["cand_rows"], w["cand_pos"], w["cand_count"], win_lo=s * S,
+                                  win_len=S, rows_per_seq=1 + dm.D)
+            ops.bd_lmhead_confidence_rows(self.H.view(-1, dm.hidden), w["cand_rows"], w["cand_pos"], w["cand_count"],
+                                          self.W["Wlm"], w["argmax"], w["conf"], max_logit=w["maxl"], lse=w["lse"])
+        else:
+            ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"],
+                                     w["conf"], max_logit=w["maxl"], lse=w["lse"])
         if ev is not None:
             ev[1].record()
             self.lm_events.append(ev)
@@ -188,6 +204,9 @@ class BlockDecoder:
                                 threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
         self.bits_host.copy_(self.mask_bits, non_blocking=True)
         self.last = w
+
+    def uses_compaction(self, S: int) -> bool:
+        return self.compact if self.compact is not None else self.dims.B * S > 64
 
     def _step_done(self):
         self._bits_ev.record()

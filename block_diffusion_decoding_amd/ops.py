@@ -117,6 +117,34 @@ def bd_lmhead_confidence(h_src, row_idx, w, argmax, conf, *, max_logit=None, lse
     _check("bd_lmhead_confidence", st)
 
 
+def bd_lmhead_confidence_rows(h_src, row_idx, out_pos, m_dev, w, argmax, conf, *, max_logit=None, lse=None,
+                              logits=None, ws=None, stream=None):
+    """Rows m < m_dev[0] of row_idx/out_pos (capacity M = row_idx.numel());
+    results of row m land at out_pos[m] of argmax/conf (and max_logit/lse)."""
+    lib = _lib.load()
+    hidden = h_src.shape[-1]
+    n_src = h_src.numel() // hidden
+    V = w.shape[0]
+    M = row_idx.numel()
+    dt = _dt(h_src)
+    need = lib.bd_lmhead_workspace_size(dt, M, hidden, V)
+    if ws is None:
+        ws = workspace(need, h_src.device, "lm")
+    st = lib.bd_lmhead_confidence_rows(dt, M, hidden, V, _p(h_src), n_src, _p(row_idx), _p(out_pos), _p(m_dev),
+                                       conf.numel(), _p(w), _p(argmax), _p(conf), _p(max_logit), _p(lse),
+                                       _p(logits), _p(ws), ws.numel(), _stream(stream))
+    _check("bd_lmhead_confidence_rows", st)
+
+
+def bd_candidate_rows(mask_bits, row_idx, out_pos, count, *, win_lo, win_len, rows_per_seq, stream=None):
+    """mask_bits [B] (64-bit); row_idx/out_pos [B*win_len] int32; count [1] int32."""
+    lib = _lib.load()
+    B = mask_bits.numel()
+    st = lib.bd_candidate_rows(B, win_lo, win_len, _p(mask_bits), rows_per_seq, _p(row_idx), _p(out_pos),
+                               _p(count), _stream(stream))
+    _check("bd_candidate_rows", st)
+
+
 def bd_threshold_unmask(conf, argmax, tokens, mask_bits, *, win_lo, threshold, n_unmasked=None,
                         unmasked_pos=None, stream=None):
     """conf/argmax [B, win_len]; tokens [B, D] int32; mask_bits [B] (64-bit)."""

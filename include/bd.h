@@ -11,6 +11,7 @@
  *   output projection + residual        bd_linear                    (support)
  *   LM head with token shift + softmax
  *     confidence / argmax               bd_lmhead_confidence
+ *     (only the masked candidates)      bd_candidate_rows + bd_lmhead_confidence_rows
  *   confidence-threshold unmasking      bd_threshold_unmask
  *   (block finished) cache append       bd_kv_append
  *
@@ -144,6 +145,46 @@ bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V,
                                int32_t* argmax, float* conf, float* max_logit, float* lse,
                                float* logits,
                                void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bd_candidate_rows -- the LM-head rows a refinement step needs: only masked
+ * positions of the active window are candidates ([v2 notes] Key design 3),
+ * and candidate j reads the output row of position j-1 ([v2 notes] Key
+ * design 2).  Lists them batch-wide in (sequence, position) order.
+ *
+ *   mask_bits [B] uint64 (device)  bit j set <=> position j still [MASK]
+ *   win_lo, win_len                window [win_lo, win_lo + win_len), win_len <= 64
+ *   rows_per_seq                   rows of the output-row buffer per sequence:
+ *                                  row b*rows_per_seq + j holds the output of
+ *                                  position j-1 (row 0 = the carry), so the
+ *                                  source row of candidate (b, j) is
+ *                                  b*rows_per_seq + j; needs rows_per_seq > win_lo + win_len - 1
+ *   row_idx  [B*win_len] int32     out: source row of the k-th candidate
+ *   out_pos  [B*win_len] int32     out: b*win_len + (j - win_lo) of the k-th candidate
+ *   count    [1] int32             out: number of candidates
+ * Entries k >= count are set to -1.  B*win_len <= 4096.
+ * ---------------------------------------------------------------------- */
+bd_status bd_candidate_rows(int B, int win_lo, int win_len, const uint64_t* mask_bits, int rows_per_seq,
+                            int32_t* row_idx, int32_t* out_pos, int32_t* count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bd_lmhead_confidence_rows -- bd_lmhead_confidence over a row list whose
+ * length is known only on the device (the candidates of bd_candidate_rows):
+ * only rows m < min(*m_dev, M) are computed, and row m's results are written
+ * at out_pos[m] of the output arrays, which hold n_out entries (an out_pos
+ * outside [0, n_out) drops that row's results).  M is the capacity of
+ * row_idx/out_pos and sizes the workspace (bd_lmhead_workspace_size(dt, M,
+ * ...)); the launch covers M rows, work beyond the count exits early.  Same
+ * statistics and argument rules as bd_lmhead_confidence otherwise; the
+ * debug dump, if given, is [M, V] in list order.
+ * ---------------------------------------------------------------------- */
+bd_status bd_lmhead_confidence_rows(bd_dtype dt, int M, int hidden, int V,
+                                    const void* h_src, int n_src, const int32_t* row_idx,
+                                    const int32_t* out_pos, const int32_t* m_dev, int n_out,
+                                    const void* w,
+                                    int32_t* argmax, float* conf, float* max_logit, float* lse,
+                                    float* logits,
+                                    void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * bd_threshold_unmask -- confidence-aware parallel unmasking in the active

@@ -114,11 +114,11 @@ def workload(cfg, seed=0, window=0, S=None, n_masked=None, all_masked=False, pla
     return w, pre, st, plant, carry_plant
 
 
-def gpu_decoder(cfg, w, pre, st, plant=None, carry_plant=None):
+def gpu_decoder(cfg, w, pre, st, plant=None, carry_plant=None, compact=None):
     from block_diffusion_decoding_amd.decoder import BlockDecoder, Dims
     dims = Dims(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.hidden, cfg.V, cfg.D, cfg.cap)
     weights = {k: torch.from_numpy(getattr(w, k)) for k in ("E", "Wq", "Wk", "Wv", "Wo", "Wlm")}
-    dec = BlockDecoder(dims, weights, dtype=tdt(cfg.dtype), device=DEV)
+    dec = BlockDecoder(dims, weights, dtype=tdt(cfg.dtype), device=DEV, compact=compact)
     if pre.kind == "prefill":
         dec.prefill(pre.prompt)
         for blk in range(pre.committed.shape[1] // cfg.D):

@@ -106,6 +106,22 @@ def test_lmhead_unmask_append_argument_errors():
     assert ap(h.ctypes.data, n=0) == 0
 
 
+def test_candidate_rows_argument_errors():
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    cr = lambda **k: lib.bd_candidate_rows(k.get("B", 4), k.get("lo", 8), k.get("wl", 8), k.get("bits", FAKE),
+                                           k.get("rps", 33), FAKE, FAKE, FAKE, None)
+    assert cr(B=0) == 0
+    assert cr(B=-1) == E and cr(wl=0) == E and cr(wl=65) == E and cr(lo=60) == E
+    assert cr(rps=15) == E                                            # row of position 15 would not exist
+    assert cr(B=513) == E                                             # more than 4096 window entries
+    assert cr(bits=None) == E
+    lmr = lambda **k: lib.bd_lmhead_confidence_rows(1, 64, 512, 5000, FAKE, 100, k.get("ri", FAKE),
+                                                    k.get("pos", FAKE), k.get("mdev", FAKE), 64, FAKE, FAKE, FAKE,
+                                                    None, None, None, FAKE, 1 << 30, None)
+    assert lmr(mdev=None) == E and lmr(pos=None) == E and lmr(ri=None) == E
+
+
 def test_gemm_and_embed_argument_errors():
     lib = _lib.load()
     E, U = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED
