@@ -15,9 +15,15 @@
 //
 // bf16, up to 64 rows: streaming MFMA GEMM (stream_gemm.h), weights
 // streamed once from HBM through a 3-stage asynchronous global->LDS pipeline.
-// bf16, more rows (the exact step of a whole batch, where the product is
-// MFMA-bound): 256 x 256 work-group tiles, see lm_big_kernel.
+// bf16, more rows (a whole batch's window or block, where the product is
+// MFMA-bound): 256-row work-group tiles, see lm_big_kernel.
 // fp32: plain VALU kernel.
+//
+// With a device-side row count (bd_lmhead_confidence_rows: the masked
+// candidates listed first by bd_candidate_rows) rows past the count are
+// skipped -- whole row blocks exit, and the 256-row kernel skips the loads
+// and MFMAs of its row tiles past the count -- and the merge writes each
+// row's statistics to its output slot.
 #include <climits>
 
 #include "bd_device.h"
