@@ -174,9 +174,18 @@ class Loop:
                 self._new_block()
 
 
-def time_call(fn, reps, warm=3):
-    for _ in range(warm):
+def time_call(fn, reps, warm=3, warm_s=0.1):
+    """Median and mean of `reps` calls, after at least `warm` calls and
+    `warm_s` seconds of the same call (the clocks take ~20 ms of sustained
+    load to settle after the host-side input generation left the GPU idle)."""
+    t_end = time.perf_counter() + warm_s
+    n = 0
+    while n < warm or time.perf_counter() < t_end:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
         a.record()

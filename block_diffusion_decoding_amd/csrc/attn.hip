@@ -10,11 +10,13 @@
 // bf16 path (MFMA): one work-group handles (sequence b, KV head, key chunk,
 // query-tile group).  The G query heads that share a KV head and the n_q fresh
 // block rows form R = n_q * G query rows; this is what turns the grouped-query
-// attention into a real contraction for v_mfma_f32_16x16x32_bf16.  Up to 16
-// query tiles share one work-group, so the key/value bytes of a chunk are read
-// from HBM once.  K and V tiles of KT keys stream into a multi-stage LDS
-// pipeline by asynchronous global->LDS loads (both land XOR-swizzled; V is
-// read transposed by ds_read_b64_tr_b16); the scores are computed transposed (S^T = K Q^T) so
+// attention into a real contraction for v_mfma_f32_16x16x32_bf16.  A
+// work-group has 8 waves and up to 16 query tiles, so the key/value bytes of a
+// chunk are read from HBM once; its 8-stage LDS ring (128 KiB) holds it to one
+// work-group per CU, and the key chunks are sized for one work-group per CU.
+// K and V tiles of KT keys stream into the ring by asynchronous global->LDS
+// loads (both land XOR-swizzled; V is read transposed by ds_read_b64_tr_b16,
+// issued while the score MFMAs run); the scores are computed transposed (S^T = K Q^T) so
 // that the probabilities land in the B operand layout of the P.V product
 // without any data movement; the softmax is an online (running max) softmax
 // in base 2.  Key chunks of one (sequence, KV head) are merged by a second
@@ -29,17 +31,20 @@
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // merge and fp32 kernels
 // Tuning constants; the defaults were chosen by measurement on MI355X and can
 // be overridden at build time (-DBD_ATTN_KT=...).
 #ifndef BD_ATTN_KT
 #define BD_ATTN_KT 32
 #endif
 #ifndef BD_ATTN_NS
-#define BD_ATTN_NS 4
+#define BD_ATTN_NS 8
+#endif
+#ifndef BD_ATTN_WAVES
+#define BD_ATTN_WAVES 8
 #endif
 #ifndef BD_ATTN_TARGET_WGS
-#define BD_ATTN_TARGET_WGS 512
+#define BD_ATTN_TARGET_WGS 256
 #endif
 #ifndef BD_ATTN_MIN_CHUNK
 #define BD_ATTN_MIN_CHUNK 256
@@ -47,14 +52,13 @@ constexpr int kThreads = 256;
 #ifndef BD_ATTN_QPW_MAX
 #define BD_ATTN_QPW_MAX 2
 #endif
-#ifndef BD_ATTN_WG_PER_CU
-#define BD_ATTN_WG_PER_CU 2
-#endif
 constexpr int kKT = BD_ATTN_KT;                 // keys per LDS tile (bf16 path)
 constexpr int kNS = BD_ATTN_NS;                 // pipeline stages (bf16 path)
+constexpr int kWaves = BD_ATTN_WAVES;           // waves per work-group (bf16 path)
+constexpr int kAttnThreads = 64 * kWaves;
 constexpr int kXcd = 8;                         // work-groups are dispatched round-robin over 8 XCDs
 constexpr int kMinChunk = BD_ATTN_MIN_CHUNK;    // keys per work item, lower bound
-constexpr int kTargetWGs = BD_ATTN_TARGET_WGS;
+constexpr int kTargetWGs = BD_ATTN_TARGET_WGS;  // one work-group per CU: the stage ring fills the LDS
 constexpr int kQpwMax = BD_ATTN_QPW_MAX;        // query tiles per wave, at most (1, 2 or 4)
 constexpr float kLazyMax = 8.f;                 // running-max slack (log2 units), see the softmax
 
@@ -174,6 +178,22 @@ __device__ __forceinline__ void pipe_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Wait until at most `later` stages of LW loads per wave are outstanding
+// (s_waitcnt takes an immediate, hence the switch).
+template <int LW, int NS>
+__device__ __forceinline__ void wait_stages(int later) {
+  switch (later) {
+    case 1: if constexpr (NS > 2) __builtin_amdgcn_s_waitcnt(vm_imm(1 * LW)); break;
+    case 2: if constexpr (NS > 3) __builtin_amdgcn_s_waitcnt(vm_imm(2 * LW)); break;
+    case 3: if constexpr (NS > 4) __builtin_amdgcn_s_waitcnt(vm_imm(3 * LW)); break;
+    case 4: if constexpr (NS > 5) __builtin_amdgcn_s_waitcnt(vm_imm(4 * LW)); break;
+    case 5: if constexpr (NS > 6) __builtin_amdgcn_s_waitcnt(vm_imm(5 * LW)); break;
+    case 6: if constexpr (NS > 7) __builtin_amdgcn_s_waitcnt(vm_imm(6 * LW)); break;
+    case 7: if constexpr (NS > 8) __builtin_amdgcn_s_waitcnt(vm_imm(7 * LW)); break;
+    default: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
+  }
+}
+
 // Pipeline stage layout (per KT-key tile): the K tile and then the V tile,
 // each as rows of DH/8 16-byte chunks, XOR-swizzled (chunk c of key k at slot
 // k*KCH + (c ^ (k & (KCH-1)))) so that both the K fragment reads and the
@@ -182,15 +202,15 @@ __device__ __forceinline__ void pipe_barrier() {
 // 16-byte slots, and each lane's global address is chosen so that its slot
 // receives the right chunk.
 template <int DH, int KT, int QPW, int NS>
-__global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void attn_bf16_kernel(AttnK a) {
+__global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_kernel(AttnK a) {
   constexpr int KCH = DH / 8;             // 16-byte chunks per key row
   constexpr int TU4 = KT * KCH;           // 16-byte slots per K (or V) tile
   constexpr int NI = TU4 / 64;            // DMA instructions per K (or V) tile
-  constexpr int LW = 2 * NI / 4;          // DMA instructions per wave per stage
+  constexpr int LW = 2 * NI / kWaves;     // DMA instructions per wave per stage
   constexpr int KS = DH / 32;             // MFMA K-steps over the head dim
   constexpr int NKT = KT / 16;            // 16-key tiles per LDS tile
-  static_assert(TU4 % 64 == 0 && (2 * NI) % 4 == 0, "tile split");
-  static_assert(NS >= 2 && NS <= 5, "shape");
+  static_assert(TU4 % 64 == 0 && (2 * NI) % kWaves == 0 && LW >= 1, "tile split");
+  static_assert(NS >= 2 && NS <= 9 && (NS - 1) * LW < 64, "shape");
 
   __shared__ uint4 sStage[NS][2 * TU4];
 
@@ -235,7 +255,7 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
   bd_f32x4 oacc[QPW][DH / 16];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
-    const int t = (qg * 4 + wave) * QPW + j;
+    const int t = (qg * kWaves + wave) * QPW + j;
     tact[j] = t < a.QT;
     const int r = t * 16 + l16;
     const bool rok = tact[j] && r < a.R;
@@ -264,8 +284,8 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
   for (int j = 0; j < QPW; ++j) vis_all = min(vis_all, qblk[j]);
   for (int off = 32; off > 0; off >>= 1) vis_all = min(vis_all, __shfl_xor(vis_all, off));
 
-  // ---- asynchronous tile loads: this wave issues instructions wave + 4*u of
-  // the stage (the first NI fill K, the next NI fill V)
+  // ---- asynchronous tile loads: this wave issues instructions wave + kWaves*u
+  // of the stage (the first NI fill K, the next NI fill V)
   auto key_row = [&](const uint16_t* cache_bh, const uint16_t* blk_b, int key) -> const uint16_t* {
     key = key < kend ? key : kend - 1;  // rows past the chunk repeat a real row; their scores are masked
     return key < L ? cache_bh + (size_t)key * DH : blk_b + (size_t)(key - L) * blk_stride;
@@ -275,7 +295,7 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
   int loff[LW];
 #pragma unroll
   for (int u = 0; u < LW; ++u) {
-    const int ins = wave + 4 * u;
+    const int ins = wave + kWaves * u;
     const int p = (ins >= NI ? ins - NI : ins) * 64 + lane;
     const int kk = p / KCH, phys = p % KCH;
     loff[u] = kk * DH + (phys ^ (kk & (KCH - 1))) * 8;
@@ -287,7 +307,7 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
     if (kbase + KT <= cache_end) {
 #pragma unroll
       for (int u = 0; u < LW; ++u) {
-        const int ins = wave + 4 * u;
+        const int ins = wave + kWaves * u;
         const uint16_t* base = (ins >= NI ? vc_bh : kc_bh) + (size_t)kbase * DH;
         __builtin_amdgcn_global_load_lds((glb_void_t*)(base + loff[u]),
                                          (lds_void_t*)(st + (ins >= NI ? TU4 : 0) + (ins >= NI ? ins - NI : ins) * 64),
@@ -296,7 +316,7 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
     } else {
 #pragma unroll
       for (int u = 0; u < LW; ++u) {
-        const int ins = wave + 4 * u;
+        const int ins = wave + kWaves * u;
         const bool isv = ins >= NI;
         const int kk = loff[u] / DH;
         const uint16_t* src = isv ? key_row(vc_bh, vb_b, kbase + kk) : key_row(kc_bh, kb_b, kbase + kk);
@@ -306,20 +326,18 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
     }
   };
 
-  // the Q fragments (and every other global load so far) must be in
+  // The Q fragments (and every other global load so far) must be in
   // registers before the pipeline starts, so that no register wait on them
-  // is left for the compiler to place inside the loop
+  // is left for the compiler to place inside the loop.  The prologue always
+  // issues NS-1 stages: in a chunk of fewer tiles the extra stages re-read
+  // the chunk's last rows (key_row clamps) into slots no tile uses, and the
+  // loop's waits, which count them as older loads, still drain every load
+  // before the work-group ends.
   __builtin_amdgcn_s_waitcnt(vm_imm(0));
 #pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < ntiles) issue(t);
-
+  for (int t = 0; t < NS - 1; ++t) issue(t);
   for (int t = 0; t < ntiles; ++t) {
-    const int later = min(ntiles - t - 1, NS - 2);
-    if (later <= 0) __builtin_amdgcn_s_waitcnt(vm_imm(0));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vm_imm(LW));
-    else if (later == 2) __builtin_amdgcn_s_waitcnt(vm_imm(2 * LW));
-    else __builtin_amdgcn_s_waitcnt(vm_imm(3 * LW));
+    wait_stages<LW, NS>(min(ntiles - t - 1, NS - 2));
     pipe_barrier();  // tile t in LDS; every wave is done with tile t - 1
     if (t + NS - 1 < ntiles) issue(t + NS - 1);
     const uint4* sK = sStage[t % NS];
@@ -348,7 +366,6 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) ka[ks] = kb + (l16 * 16 + ((g + 4 * ks) ^ l16)) * 16;
         lds_kfrags_128x32(ka, kfr);
-        if constexpr (QPW == 1) load_vfrags(vfr);  // else after the softmax (register pressure)
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
@@ -359,6 +376,8 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
             for (int j = 0; j < QPW; ++j)
               s[j][kt] = bd_mfma16(kfr[kt][ks], qf[j][ks], s[j][kt]);
         }
+        // the V reads go out while the score MFMAs are still in the matrix pipe
+        load_vfrags(vfr);
       } else {
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
@@ -462,7 +481,6 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
         }
       }
       // O^T += V^T P^T: V^T fragment = two 4-key runs of one head-dim row
-      if constexpr (kFast && QPW != 1) load_vfrags(vfr);
       // lane (g, l16) points at key 32u + 4g + l16/4 (and +16), head dims
       // 16dt + 4*(l16 % 4) .. +3; it receives keys 32u+4g..+3 (and +16..)
       // of head dim 16dt + l16, the slot order of the probabilities above
@@ -497,7 +515,7 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
     float l = l_run[j];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const int r = ((qg * 4 + wave) * QPW + j) * 16 + l16;
+    const int r = ((qg * kWaves + wave) * QPW + j) * 16 + l16;
     if (r >= a.R) continue;
     const int i = r / a.G, hg = r % a.G;
     if (single) {
@@ -517,10 +535,7 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
       for (int dt = 0; dt < DH / 16; ++dt)
         *reinterpret_cast<float4*>(po + dt * 16 + 4 * g) =
             make_float4(oacc[j][dt][0], oacc[j][dt][1], oacc[j][dt][2], oacc[j][dt][3]);
-      if (g == 0) {
-        a.part_ml[2 * pi] = m_run[j];
-        a.part_ml[2 * pi + 1] = l;
-      }
+      if (g == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * pi) = make_float2(m_run[j], l);
     }
   }
 }
@@ -528,7 +543,10 @@ __global__ __launch_bounds__(kThreads, (QPW == 4 ? 1 : BD_ATTN_WG_PER_CU)) void 
 // Merge the key chunks of every (sequence, KV head) whose keys span more than
 // one chunk: o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.  One wave per
 // query row; lane e holds head dims DH/64 * e .. (a 512-byte row per chunk).
-template <int DH>
+// Chunks are taken NB at a time with an online maximum, so every load of a
+// batch is in flight together and a row needs one round trip per batch;
+// chunk indices past the end are clamped and weighted 0.
+template <int DH, int NB>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnK a) {
   constexpr int PER = DH / 64;  // head dims per lane
   const int lane = threadIdx.x & 63;
@@ -543,25 +561,18 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnK a) {
   if (nc <= 1) return;
   const size_t rp = (size_t)a.QT * 16;
   const size_t base = (size_t)bh * a.nchunks * rp + r;  // partial index of chunk c: base + c * rp
-  // the running max of chunk c is read by lane c % 64, then a wave max
-  float M = BD_NEG_INF;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, a.part_ml[2 * (base + (size_t)c * rp)]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float muse = (M == BD_NEG_INF) ? 0.f : M;
-  // weighted sum, 8 chunks per batch so their loads are in flight together;
-  // chunk indices past the end are clamped and weighted 0
+  float M = BD_NEG_INF, lsum = 0.f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float lsum = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += 8) {
-    float mv[8], lv[8], ov[8][PER];
+  for (int c0 = 0; c0 < nc; c0 += NB) {
+    float mv[NB], lv[NB], ov[NB][PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const size_t pi = base + (size_t)min(c0 + u, nc - 1) * rp;
-      mv[u] = a.part_ml[2 * pi];
-      lv[u] = a.part_ml[2 * pi + 1];
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + 2 * pi);
+      mv[u] = ml.x;
+      lv[u] = ml.y;
       const float* po = a.part_o + pi * DH + PER * lane;
       if constexpr (PER == 2) {
         const float2 v = *reinterpret_cast<const float2*>(po);
@@ -571,13 +582,23 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnK a) {
         ov[u][0] = po[0];
       }
     }
+    float mb = M;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NB; ++u)
+      if (c0 + u < nc) mb = fmaxf(mb, mv[u]);
+    const float muse = (mb == BD_NEG_INF) ? 0.f : mb;
+    const float alpha = bd_exp2(M - muse);  // 0 while nothing has been seen
+    lsum *= alpha;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
       const float w = (c0 + u < nc) ? bd_exp2(mv[u] - muse) : 0.f;
       lsum += w * lv[u];
 #pragma unroll
       for (int e = 0; e < PER; ++e) acc[e] += w * ov[u][e];
     }
+    M = mb;
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int i = r / a.G, hg = r % a.G;
@@ -675,9 +696,9 @@ BdAttnPlan bd_attn_plan(bd_dtype dt, int B, int Hq, int Hkv, int d, int n_q, int
   const int G = Hq / Hkv;
   p.R = n_q * G;
   p.QT = (p.R + 15) / 16;
-  p.qpw = p.QT <= 4 ? 1 : (p.QT <= 8 ? 2 : 4);
+  p.qpw = p.QT <= kWaves ? 1 : (p.QT <= 2 * kWaves ? 2 : 4);
   p.qpw = p.qpw > kQpwMax ? kQpwMax : p.qpw;
-  p.nqg = (p.QT + 4 * p.qpw - 1) / (4 * p.qpw);
+  p.nqg = (p.QT + kWaves * p.qpw - 1) / (kWaves * p.qpw);
   const int tmax = cap + n_blk;
   if (dt == BD_F32) {
     p.chunk = tmax;
@@ -728,7 +749,7 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
   a.scale_log2 = x.scale * BD_LOG2E;
   const int n_wg = kXcd * a.nqg * ((a.n_units + kXcd - 1) / kXcd);
 #define BD_ATTN_LAUNCH(DH, QPW) \
-  hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS>), dim3(n_wg), dim3(kThreads), 0, s, a)
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS>), dim3(n_wg), dim3(kAttnThreads), 0, s, a)
   if (x.d == 128) {
     if (p.qpw == 1) BD_ATTN_LAUNCH(128, 1);
 #if BD_ATTN_QPW_MAX >= 2
@@ -751,9 +772,17 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
   if (e != hipSuccess || p.nchunks == 1) return e;
   const size_t rows = (size_t)x.B * x.Hkv * p.R;
   const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64)));
-  if (x.d == 128)
-    hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(kThreads), 0, s, a);
+#define BD_MERGE_LAUNCH(DH, NB) hipLaunchKernelGGL((attn_merge_kernel<DH, NB>), grid, dim3(kThreads), 0, s, a)
+  const int nb = p.nchunks <= 2 ? 2 : (p.nchunks <= 4 ? 4 : 8);
+  if (x.d == 128) {
+    if (nb == 2) BD_MERGE_LAUNCH(128, 2);
+    else if (nb == 4) BD_MERGE_LAUNCH(128, 4);
+    else BD_MERGE_LAUNCH(128, 8);
+  } else {
+    if (nb == 2) BD_MERGE_LAUNCH(64, 2);
+    else if (nb == 4) BD_MERGE_LAUNCH(64, 4);
+    else BD_MERGE_LAUNCH(64, 8);
+  }
+#undef BD_MERGE_LAUNCH
   return hipGetLastError();
 }
