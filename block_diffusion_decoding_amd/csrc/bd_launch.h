@@ -41,8 +41,9 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& a,
 
 // ---- LM head ---------------------------------------------------------------
 struct BdLmPlan {
-  int cols_per_wg;  // vocabulary columns per work-group
-  int nvt;          // vocabulary tiles (work-groups along V)
+  int cols_per_wg;  // vocabulary columns per work-group (at most, streaming kernel)
+  int nvt;          // work-groups along V (partials per row)
+  int passes;       // streaming kernel: passes over a work-group's column range
   int rows_per_wg;  // rows of h per work-group
   int nmb;          // row blocks
   size_t ws_bytes;  // partial (max, argmax, sum) per (row, tile)

@@ -84,11 +84,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
   const int nch = a.K / C::KC;
   const int c0 = z * nch / a.ksplit, c1 = (z + 1) * nch / a.ksplit;
 
-  auto xrow = [&](int m) -> const uint16_t* {
+  auto xidx = [](int m) { return m; };
+  auto xptr = [&](int m, int) -> const uint16_t* {
     return m < a.M ? a.x + (size_t)bd_map_row(a.xr, m) * a.K : nullptr;
   };
   bd_f32x4 acc[C::MTW][C::NTP];
-  bd_stream::mainloop<C>(xrow, a.x, m0, a.w[seg], N, a.K, n0, sbuf, acc, c0 * C::KC, c1 - c0);
+  bd_stream::mainloop<C>(xidx, xptr, a.x, m0, a.w[seg], N, a.K, n0, sbuf, acc, c0 * C::KC, c1 - c0);
 
   if (a.ksplit == 1) {
 #pragma unroll

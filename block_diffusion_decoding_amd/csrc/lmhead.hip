@@ -13,8 +13,9 @@
 // of a row in a fixed order into argmax, max, log-sum-exp and
 // confidence = exp(max - lse).
 //
-// bf16, up to 64 rows: streaming MFMA GEMM (stream_gemm.h), weights
-// streamed once from HBM through a 3-stage asynchronous global->LDS pipeline.
+// bf16, up to 64 rows: streaming MFMA GEMM, persistent over the vocabulary
+// (lm_stream_kernel): weights streamed once from HBM through a 3-stage
+// asynchronous global->LDS pipeline, every work-group an equal share.
 // bf16, more rows (a whole batch's window or block, where the product is
 // MFMA-bound): 256-row work-group tiles, see lm_big_kernel.
 // fp32: plain VALU kernel.
@@ -40,8 +41,14 @@ constexpr int kThreads = 256;
 #ifndef BD_LM_NS
 #define BD_LM_NS 3
 #endif
-constexpr int kNTW = BD_LM_NTW;  // 16-column tiles per work-group (bf16)
+#ifndef BD_LM_STREAM_WGS
+#define BD_LM_STREAM_WGS 512
+#endif
+constexpr int kNTW = BD_LM_NTW;  // 16-column tiles per pass (bf16, up to 64 rows)
 constexpr int kNS = BD_LM_NS;    // pipeline stages (bf16)
+constexpr int kStreamWGs = BD_LM_STREAM_WGS;  // work-groups of the streaming kernel: two per CU
+// s_waitcnt immediate waiting for lgkmcnt(0) only
+constexpr int kLgkm0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
 constexpr int kF32Rows = 16;  // rows per work-group (fp32)
 
 struct LmK {
@@ -65,68 +72,196 @@ __device__ __forceinline__ int lm_rows(const int32_t* m_dev, int M) {
   return c < 0 ? 0 : (c < M ? c : M);
 }
 
-__device__ __forceinline__ const uint16_t* lm_row(const LmK& a, int m, int Meff) {
-  if (m >= Meff) return nullptr;
-  const int r = a.row_idx ? a.row_idx[m] : m;
-  if (r < 0 || r >= a.n_src) return nullptr;
-  return a.h + (size_t)r * a.hidden;
+// Source row of row m, in two steps so that a wave's row-index loads can all
+// be in flight before any is used: lm_row_index clamps m into [0, M) (M >= 1)
+// so its load is always in bounds, lm_row_ptr rejects rows past the count
+// and out-of-range indices (their outputs are never used).
+__device__ __forceinline__ int lm_row_index(const LmK& a, int m) {
+  const int mc = m < a.M ? m : a.M - 1;
+  return a.row_idx ? a.row_idx[mc] : mc;
 }
 
+__device__ __forceinline__ const uint16_t* lm_row_ptr(const LmK& a, int m, int r, int Meff) {
+  return (m < Meff && r >= 0 && r < a.n_src) ? a.h + (size_t)r * a.hidden : nullptr;
+}
+
+// Streaming LM head for up to 64 rows, persistent over the vocabulary.
+// Work-group w of nwg owns the 16-column tiles [w*T/nwg, (w+1)*T/nwg),
+// T = ceil(V/16), and walks them in P passes of at most kNTW tiles (equal
+// splits of its range), so every work-group streams the same share of W and
+// all of them finish together.  The 64-wide K chunks of all its passes form
+// one stream of pipeline stages (stage s: pass s / nch, chunk s % nch): the
+// first stages of a pass are in flight while the previous pass finishes its
+// MFMAs and reduces its logits.  A pass's statistics are folded into one
+// running (max, argmax, sum) per row, stored once at the end.
+// Stage layout as in stream_gemm.h: kNTW W tiles then MT X tiles, each 16
+// rows x 64 k (2 KiB, two whole-line DMA instructions, XOR-swizzled).  A pass
+// with fewer than kNTW tiles fills its unused W slots from row 0 of h (an L2
+// hit), so every stage issues the same loads per wave and the waits count
+// exactly; the epilogue ignores the logits of those slots.
 template <int MT>
-__global__ __launch_bounds__(kThreads, 2) void lm_bf16_kernel(LmK a) {
+__global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
   using C = bd_stream::Cfg<MT, kNTW, kNS>;
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
+  __shared__ BdArgStat red[C::WN * MT * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int m0 = blockIdx.y * MT * 16;
-  const int n0 = blockIdx.x * kNTW * 16;
   const int Meff = lm_rows(a.m_dev, a.M);
   if (m0 >= Meff) return;  // the whole row block is past the row count
+  const int K = a.hidden, nch = K / C::KC, nst = P * nch;
+  const int T = (a.V + 15) >> 4;
+  const int t0 = (int)((long long)blockIdx.x * T / gridDim.x);
+  const int nt = (int)((long long)(blockIdx.x + 1) * T / gridDim.x) - t0;
+  auto pass_begin = [&](int p) { return t0 + p * nt / P; };  // first tile of pass p
+
+  // DMA instruction f = wave + 4i loads rows 8*(f%2)..+7 of stage tile f/2:
+  // tiles 0..kNTW-1 are W (per pass), the next MT are X (fixed).
+  const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
+  int xm[C::LW], xi[C::LW];
+#pragma unroll
+  for (int i = 0; i < C::LW; ++i) {  // row indices first: their loads are in flight together
+    const int f = wave + 4 * i, t = f >> 1;
+    xm[i] = m0 + (t - kNTW) * 16 + 8 * (f & 1) + lrow;
+    xi[i] = (f < C::FR && t >= kNTW) ? lm_row_index(a, xm[i]) : 0;
+  }
+  const uint16_t* const hdummy = a.h + 8 * lkb;
+  const uint16_t* src[C::LW];
+#pragma unroll
+  for (int i = 0; i < C::LW; ++i) {
+    const uint16_t* p = lm_row_ptr(a, xm[i], xi[i], Meff);
+    src[i] = p ? p + 8 * lkb : hdummy;  // X rows; W rows are set per pass
+  }
+  auto set_pass = [&](int p) {  // W sources of pass p
+    const int b = pass_begin(p), n = pass_begin(p + 1) - b;
+#pragma unroll
+    for (int i = 0; i < C::LW; ++i) {
+      const int f = wave + 4 * i, t = f >> 1;
+      if (f < C::FR && t < kNTW) {
+        const int col = (b + t) * 16 + 8 * (f & 1) + lrow;
+        src[i] = t >= n ? hdummy : a.w + (size_t)(col < a.V ? col : 0) * K + 8 * lkb;
+      }
+    }
+  };
+  int ip = 0, ich = 0, iss = 0;  // issue cursor: pass, chunk, stages issued
+  set_pass(0);
+  auto issue_next = [&]() {
+    uint4* st = sbuf + (iss % C::NS) * C::STAGE_U4;
+#pragma unroll
+    for (int i = 0; i < C::LW; ++i)
+      if (C::FR % 4 == 0 || wave + 4 * i < C::FR)
+        __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ich * C::KC),
+                                         (bd_stream::lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, 0);
+    ++iss;
+    if (++ich == nch) {
+      ich = 0;
+      if (++ip < P) set_pass(ip);
+    }
+  };
+  const bool more = wave < C::FR % 4;  // this wave issues LW (else LW_LO) loads per stage
+  const int fo0 = bd_stream::frag_offset(lane, 0) / 16, fo1 = bd_stream::frag_offset(lane, 1) / 16;
 
   bd_f32x4 acc[C::MTW][C::NTP];
-  auto xrow = [&](int m) { return lm_row(a, m, Meff); };
-  bd_stream::mainloop<C>(xrow, a.h, m0, a.w, a.V, a.hidden, n0, sbuf, acc);
+#pragma unroll
+  for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+  BdArgStat run{BD_NEG_INF, INT_MAX, 0.f};  // threads tid < MT*16: row m0 + tid over the passes so far
 
-  // rows m0 + (wm*MTW + i)*16 + 4g + r, columns n0 + (wn*NTP + j)*16 + l16
-  if (a.logits != nullptr) {  // debug dump of the raw logits (tests only)
+  // the row-index loads (and every other global load so far) complete before
+  // the pipeline starts, so no register wait is left for the loop
+  __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+#pragma unroll
+  for (int c = 0; c < C::NS - 1; ++c)
+    if (c < nst) issue_next();
+
+  int cp = 0, cch = 0;  // compute cursor: pass, chunk
+  for (int s = 0; s < nst; ++s) {
+    const int later = min(nst - s - 1, C::NS - 2);
+    if (later == 0) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+    else if (later == 1) {
+      if (more) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(C::LW));
+      else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(C::LW_LO));
+    } else if (later == 2) {
+      if (more) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(2 * C::LW));
+      else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(2 * C::LW_LO));
+    } else {
+      if (more) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(3 * C::LW));
+      else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(3 * C::LW_LO));
+    }
+    bd_stream::pipe_barrier();  // stage s is in LDS for every wave; the slot of s - 1 is free
+    if (s + C::NS - 1 < nst) issue_next();
+    // fragment reads: asm that waits inside the block (otherwise the compiler,
+    // unable to tell which LDS bytes the DMA in flight writes, puts a
+    // vmcnt(0) in front of them and drains the pipeline every stage)
+    const uint32_t sb = bd_stream::lds_addr(sbuf + (s % C::NS) * C::STAGE_U4);
+#pragma unroll
+    for (int ks = 0; ks < C::KSC; ++ks) {
+      const uint32_t fo = (ks == 0 ? fo0 : fo1) * 16;
+      uint4 xa[C::MTW], wb[C::NTP];
+      bd_stream::lds_frags_kstep<C::MTW, C::NTP>(sb + (kNTW + wm * C::MTW) * 2048 + fo,
+                                                 sb + wn * C::NTP * 2048 + fo, xa, wb);
+#pragma unroll
+      for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+    }
+    if (++cch < nch) continue;
+
+    // ---- end of pass cp: rows m0 + (wm*MTW + i)*16 + 4g + r, columns
+    // (b + wn*NTP + j)*16 + l16; slots past the pass and columns past V are out
+    const int b = pass_begin(cp), n = pass_begin(cp + 1) - b;
+    int col[C::NTP];
+    bool cok[C::NTP];
+#pragma unroll
+    for (int j = 0; j < C::NTP; ++j) {
+      col[j] = (b + wn * C::NTP + j) * 16 + l16;
+      cok[j] = wn * C::NTP + j < n && col[j] < a.V;
+    }
+    if (a.logits != nullptr) {  // debug dump of the raw logits (tests only)
+#pragma unroll
+      for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+#pragma unroll
+          for (int j = 0; j < C::NTP; ++j)
+            if (m < Meff && cok[j]) a.logits[(size_t)m * a.V + col[j]] = acc[i][j][r];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < C::MTW; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v[C::NTP];
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j) v[j] = cok[j] ? acc[i][j][r] : BD_NEG_INF;
+        const BdArgStat rs = bd_row16_stat(v, col);
+        if (l16 == 0) red[wn * (MT * 16) + (wm * C::MTW + i) * 16 + 4 * g + r] = rs;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+      for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+    // the stat writes must land before the barrier (it carries no fence, so
+    // the loads in flight are not drained); red is next written a whole pass
+    // later, after further barriers
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    bd_stream::pipe_barrier();
+    if (tid < MT * 16) {
 #pragma unroll
-        for (int j = 0; j < C::NTP; ++j) {
-          const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-          if (m < Meff && col < a.V) a.logits[(size_t)m * a.V + col] = acc[i][j][r];
-        }
-      }
-  }
-  const bool ragged = n0 + kNTW * 16 > a.V;  // only the last column block
-  int col[C::NTP];
-#pragma unroll
-  for (int j = 0; j < C::NTP; ++j) col[j] = n0 + (wn * C::NTP + j) * 16 + l16;
-  BdArgStat* red = reinterpret_cast<BdArgStat*>(sbuf);  // [WN][MT*16]
-#pragma unroll
-  for (int i = 0; i < C::MTW; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v[C::NTP];
-#pragma unroll
-      for (int j = 0; j < C::NTP; ++j) v[j] = (ragged && col[j] >= a.V) ? BD_NEG_INF : acc[i][j][r];
-      const BdArgStat st = bd_row16_stat(v, col);
-      if (l16 == 0) red[wn * (MT * 16) + (wm * C::MTW + i) * 16 + 4 * g + r] = st;
+      for (int w = 0; w < C::WN; ++w) run = bd_stat_combine(run, red[w * (MT * 16) + tid]);
     }
+    cch = 0;
+    ++cp;
   }
-  __syncthreads();
   if (tid < MT * 16 && m0 + tid < Meff) {
-    BdArgStat st = red[tid];
-#pragma unroll
-    for (int w = 1; w < C::WN; ++w) st = bd_stat_combine(st, red[w * (MT * 16) + tid]);
-    const size_t pi = (size_t)(m0 + tid) * a.nvt + blockIdx.x;
-    a.pmax[pi] = st.m;
-    a.pidx[pi] = st.i;
-    a.psum[pi] = st.s;
+    const size_t pi = (size_t)blockIdx.x * a.M + m0 + tid;  // [work-group][row]: whole cache lines
+    a.pmax[pi] = run.m;
+    a.pidx[pi] = run.i;
+    a.psum[pi] = run.s;
   }
 }
 
@@ -171,9 +306,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
   const int g = lane >> 4, l16 = lane & 15;
   const int wr = wave % P::WR, wc = wave / P::WR;
   // XCD-aware order: work-group w runs on XCD w % 8; the (w / 8)-th work-group
-  // of an XCD takes row block q % rb_count of column block 8 * (q / rb_count) + xcd.
+  // of an XCD takes row block q % rb_count of column block
+  // xcd * per_xcd + q / rb_count, so the row blocks of a column block share
+  // one L2 (W is fetched from HBM once).
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-  const int rb = q % rb_count, cb = 8 * (q / rb_count) + xcd;
+  const int per_xcd = (cb_count + 7) >> 3;
+  const int rb = q % rb_count, cb = xcd * per_xcd + q / rb_count;
   if (cb >= cb_count) return;
   const int m0 = rb * kBigRows, n0 = cb * CT * 16;
   const int nch = a.hidden / 64;
@@ -183,12 +321,18 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
   // DMA sources: instruction f covers rows 8*(f%2)..+7 of stage tile f/2;
   // tiles 0..15 are X row tiles, the next CT are W column tiles.
   const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
+  int xi[P::LW];  // row indices first: their loads are in flight together
+#pragma unroll
+  for (int i = 0; i < P::LW; ++i) {
+    const int f = wave + 8 * i, t = f >> 1, r = 8 * (f & 1) + lrow;
+    xi[i] = t < kBigRows / 16 ? lm_row_index(a, m0 + t * 16 + r) : 0;
+  }
   const uint16_t* src[P::LW];
 #pragma unroll
   for (int i = 0; i < P::LW; ++i) {
     const int f = wave + 8 * i, t = f >> 1, r = 8 * (f & 1) + lrow;
     if (t < kBigRows / 16) {
-      const uint16_t* p = lm_row(a, m0 + t * 16 + r, Meff);
+      const uint16_t* p = lm_row_ptr(a, m0 + t * 16 + r, xi[i], Meff);
       src[i] = (p ? p : a.h) + 8 * lkb;
     } else {
       const int col = n0 + (t - kBigRows / 16) * 16 + r;
@@ -314,7 +458,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_co
     BdArgStat st = red[tid];
 #pragma unroll
     for (int w = 1; w < P::WC; ++w) st = bd_stat_combine(st, red[w * kBigRows + tid]);
-    const size_t pi = (size_t)(m0 + tid) * a.nvt + cb;
+    const size_t pi = (size_t)(m0 + tid) * a.nvt + cb;  // [row][tile]: few, wide work-groups
     a.pmax[pi] = st.m;
     a.pidx[pi] = st.i;
     a.psum[pi] = st.s;
@@ -379,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void lm_f32_kernel(LmF a) {
     if (tid == 0 && m < Meff) {
       BdArgStat t = red[0];
       for (int w = 1; w < kThreads / 64; ++w) t = bd_stat_combine(t, red[w]);
-      const size_t pi = (size_t)m * a.nvt + blockIdx.x;
+      const size_t pi = (size_t)blockIdx.x * a.M + m;
       a.pmax[pi] = t.m;
       a.pidx[pi] = t.i;
       a.psum[pi] = t.s;
@@ -405,7 +549,8 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
 }
 
 __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_idx, int n_src, int M,
-                                                            int nvt, const float* pmax, const int32_t* pidx,
+                                                            int nvt, size_t ts, size_t rs, const float* pmax,
+                                                            const int32_t* pidx,
                                                             const float* psum, int32_t* argmax, float* conf,
                                                             float* max_logit, float* lse, const int32_t* m_dev,
                                                             const int32_t* out_pos, int n_out) {
@@ -417,7 +562,12 @@ __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_i
   if (m >= lm_rows(m_dev, M)) return;
   const int om = out_pos ? out_pos[m] : m;  // output slot of this row
   if (out_pos != nullptr && (om < 0 || om >= n_out)) return;
-  const size_t rowb = (size_t)m * nvt;
+  // partial (row m, tile t) is at t * ts + m * rs: [tile][row] from the
+  // streaming kernels (whose work-groups then store whole cache lines),
+  // [row][tile] from the 256-row kernel (whose merge rows read contiguously)
+  const float* pmr = pmax + (size_t)m * rs;
+  const float* psr = psum + (size_t)m * rs;
+  const int32_t* pir = pidx + (size_t)m * rs;
   float mx = BD_NEG_INF, s = 0.f;
   int idx = INT_MAX;
   if (nvt <= kMergePer * kThreads) {
@@ -427,9 +577,9 @@ __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_i
     for (int u = 0; u < kMergePer; ++u) {
       const int t = tid + u * kThreads;
       const bool ok = t < nvt;
-      pm[u] = ok ? pmax[rowb + t] : BD_NEG_INF;
-      ps[u] = ok ? psum[rowb + t] : 0.f;
-      pi[u] = ok ? pidx[rowb + t] : INT_MAX;
+      pm[u] = ok ? pmr[t * ts] : BD_NEG_INF;
+      ps[u] = ok ? psr[t * ts] : 0.f;
+      pi[u] = ok ? pir[t * ts] : INT_MAX;
     }
 #pragma unroll
     for (int u = 0; u < kMergePer; ++u) mx = fmaxf(mx, pm[u]);
@@ -442,7 +592,8 @@ __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_i
     }
   } else {  // very large vocabularies: pairwise combines over a strided loop
     BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
-    for (int t = tid; t < nvt; t += kThreads) st = bd_stat_combine(st, BdArgStat{pmax[rowb + t], pidx[rowb + t], psum[rowb + t]});
+    for (int t = tid; t < nvt; t += kThreads)
+      st = bd_stat_combine(st, BdArgStat{pmr[t * ts], pir[t * ts], psr[t * ts]});
     mx = block_max(st.m, shm);
     const float mu = (mx == BD_NEG_INF) ? 0.f : mx;
     s = (st.m == BD_NEG_INF) ? 0.f : st.s * bd_exp2((st.m - mu) * BD_LOG2E);
@@ -481,12 +632,16 @@ BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
   } else if (M > 64) {
     p.cols_per_wg = (M > kNarrowMaxRows ? 16 : 8) * 16;
     p.rows_per_wg = kBigRows;
-  } else {
-    p.cols_per_wg = kNTW * 16;
+  } else {  // streaming kernel: nvt work-groups, each a range of 16-column tiles in `passes` passes
     const int mt = (M + 15) / 16;
     p.rows_per_wg = 16 * (mt <= 1 ? 1 : (mt == 2 ? 2 : 4));
+    const int T = (V + 15) / 16;
+    p.nvt = T < kStreamWGs ? T : kStreamWGs;
+    const int per = (T + p.nvt - 1) / p.nvt;  // tiles of the largest range
+    p.passes = (per + kNTW - 1) / kNTW;
+    p.cols_per_wg = per * 16;
   }
-  p.nvt = (V + p.cols_per_wg - 1) / p.cols_per_wg;
+  if (dt == BD_F32 || M > 64) p.nvt = (V + p.cols_per_wg - 1) / p.cols_per_wg;
   p.nmb = (M + p.rows_per_wg - 1) / p.rows_per_wg;
   p.ws_bytes = (size_t)M * p.nvt * (2 * sizeof(float) + sizeof(int32_t));
   (void)hidden;
@@ -511,15 +666,16 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
           hipLaunchKernelGGL(lm_big_kernel<8>, dim3(cb8 * p.nmb), dim3(kBigThreads), 0, s, a, p.nmb, p.nvt);
         break;
       }
-      case 1: hipLaunchKernelGGL(lm_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
-      case 2: hipLaunchKernelGGL(lm_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-      default: hipLaunchKernelGGL(lm_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
+      case 1: hipLaunchKernelGGL(lm_stream_kernel<1>, grid, dim3(kThreads), 0, s, a, p.passes); break;
+      case 2: hipLaunchKernelGGL(lm_stream_kernel<2>, grid, dim3(kThreads), 0, s, a, p.passes); break;
+      default: hipLaunchKernelGGL(lm_stream_kernel<4>, grid, dim3(kThreads), 0, s, a, p.passes); break;
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lm_merge_kernel, dim3(x.M), dim3(kThreads), 0, s, x.row_idx, x.n_src, x.M,
-                     p.nvt, x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse, x.m_dev, x.out_pos,
+  const bool row_major = dt != BD_F32 && p.rows_per_wg == kBigRows;  // partial layout, see the merge
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(x.M), dim3(kThreads), 0, s, x.row_idx, x.n_src, x.M, p.nvt,
+                     row_major ? (size_t)1 : (size_t)x.M, row_major ? (size_t)p.nvt : (size_t)1, x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse, x.m_dev, x.out_pos,
                      x.n_out);
   return hipGetLastError();
 }

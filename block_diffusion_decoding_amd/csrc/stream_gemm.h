@@ -124,21 +124,83 @@ __device__ __forceinline__ void lds_frags_4(uint32_t a, uint4 (&x)[4]) {
   for (int i = 0; i < 4; ++i) x[i] = as_uint4(r[i]);
 }
 
+// One k-step's fragments of a wave: NX X fragments from xa + 2048*i and NW W
+// fragments from wa + 2048*j (byte addresses; tiles are 2 KiB apart).
+template <int NX, int NW>
+__device__ __forceinline__ void lds_frags_kstep(uint32_t xa, uint32_t wa, uint4 (&x)[NX], uint4 (&w)[NW]);
+
+template <>
+__device__ __forceinline__ void lds_frags_kstep<2, 4>(uint32_t xa, uint32_t wa, uint4 (&x)[2], uint4 (&w)[4]) {
+  u32x4_t r[6];
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:2048\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %7 offset:2048\n\t"
+      "ds_read_b128 %4, %7 offset:4096\n\t"
+      "ds_read_b128 %5, %7 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+      : "v"(xa), "v"(wa)
+      : "memory");
+  x[0] = as_uint4(r[0]);
+  x[1] = as_uint4(r[1]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = as_uint4(r[2 + j]);
+}
+
+template <>
+__device__ __forceinline__ void lds_frags_kstep<2, 2>(uint32_t xa, uint32_t wa, uint4 (&x)[2], uint4 (&w)[2]) {
+  u32x4_t r[4];
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:2048\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "ds_read_b128 %3, %5 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(xa), "v"(wa)
+      : "memory");
+  x[0] = as_uint4(r[0]);
+  x[1] = as_uint4(r[1]);
+  w[0] = as_uint4(r[2]);
+  w[1] = as_uint4(r[3]);
+}
+
+template <>
+__device__ __forceinline__ void lds_frags_kstep<1, 2>(uint32_t xa, uint32_t wa, uint4 (&x)[1], uint4 (&w)[2]) {
+  u32x4_t r[3];
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2])
+      : "v"(xa), "v"(wa)
+      : "memory");
+  x[0] = as_uint4(r[0]);
+  w[0] = as_uint4(r[1]);
+  w[1] = as_uint4(r[2]);
+}
+
 // Byte offset, inside a 2 KiB tile, of lane `lane`'s fragment for k-step ks.
 __device__ __forceinline__ int frag_offset(int lane, int ks) {
   const int r = lane & 15, r7 = r & 7;
   return (r >> 3) * 1024 + (r7 * 8 + ((4 * ks + (lane >> 4)) ^ r7)) * 16;
 }
 
-// Row pointers: xrow(m) gives row m of X (K elements) or nullptr for a row
-// that does not exist; such rows read row `xdummy` instead and their outputs
-// are never used.  Columns >= N read row 0 of W likewise.
+// Rows of X: xidx(m) gives the source row index of row m (it may load it
+// from a row list, so it must accept any m of the work-group's row tiles),
+// xptr(m, idx) the row (K elements) or nullptr for a row that does not exist;
+// such rows read row `xdummy` instead and their outputs are never used.  All
+// xidx calls of a wave are made before any xptr call, so row-index loads are
+// in flight together.  Columns >= N read row 0 of W likewise.
 // K range: elements [k0, k0 + nch*KC) of rows of length K.
 // Output: acc[i][j] holds rows m0 + (wm*MTW + i)*16 + 4*(lane/16) + r (r = the
 // vector element) and columns n0 + (wn*NTP + j)*16 + lane%16, with
 // wm = wave % WM and wn = wave / WM.
-template <class C, class XRowF>
-__device__ __forceinline__ void mainloop(const XRowF& xrow, const uint16_t* xdummy, int m0,
+template <class C, class XIdxF, class XPtrF>
+__device__ __forceinline__ void mainloop(const XIdxF& xidx, const XPtrF& xptr, const uint16_t* xdummy, int m0,
                                          const uint16_t* __restrict__ W, int N, int K, int n0, uint4* sbuf,
                                          bd_f32x4 (&acc)[C::MTW][C::NTP], int k0 = 0, int nch = -1) {
   const int tid = threadIdx.x;
@@ -156,6 +218,14 @@ __device__ __forceinline__ void mainloop(const XRowF& xrow, const uint16_t* xdum
   // per-lane source pointers of this wave's DMA instructions (chunk 0):
   // instruction f loads rows 8*(f%2) .. +7 of tile f/2
   const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
+  int xm[C::LW], xi[C::LW];
+#pragma unroll
+  for (int i = 0; i < C::LW; ++i) {
+    const int f = wave + 4 * i;
+    const int t = f >> 1, r = 8 * (f & 1) + lrow;
+    xm[i] = m0 + (t - C::NTW) * 16 + r;
+    xi[i] = (f < C::FR && t >= C::NTW) ? xidx(xm[i]) : 0;
+  }
   const uint16_t* src[C::LW];
 #pragma unroll
   for (int i = 0; i < C::LW; ++i) {
@@ -167,7 +237,7 @@ __device__ __forceinline__ void mainloop(const XRowF& xrow, const uint16_t* xdum
       const int col = n0 + t * 16 + r;
       src[i] = W + (size_t)(col < N ? col : 0) * K + k0 + 8 * lkb;
     } else {
-      const uint16_t* p = xrow(m0 + (t - C::NTW) * 16 + r);
+      const uint16_t* p = xptr(xm[i], xi[i]);
       src[i] = (p ? p : xdummy) + k0 + 8 * lkb;
     }
   }
