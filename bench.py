@@ -86,11 +86,11 @@ def traffic_from(fetch_csv, write_csv):
         return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
 
     out = {"kernel_source_hash": kernel_source_hash(), "calibration_bytes": CALIB_BYTES,
-           "launch": "lm_bf16_kernel<4> + lm_merge_kernel (grid 64 x 256), 64 rows x 152064 x 3584"}
+           "launch": "lm_stream_kernel<4> (512 work-groups) + lm_merge_kernel (grid 64 x 256), 64 rows x 152064 x 3584"}
     total = 0.0
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         rs = rows(path, counter)
-        main = [float(r["Counter_Value"]) for r in rs if "lm_bf16_kernel<4>" in r["Kernel_Name"]]
+        main = [float(r["Counter_Value"]) for r in rs if "lm_stream_kernel<4>" in r["Kernel_Name"]]
         merge = [float(r["Counter_Value"]) for r in rs
                  if "lm_merge_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) == 64 * 256]
         cp = [float(r["Counter_Value"]) for r in rs
@@ -430,7 +430,7 @@ def main():
             traffic = rec.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "bd_lmhead_confidence (lm_bf16_kernel<4> + lm_merge_kernel), 64 rows x 152064 x 3584",
+                "kernel": "bd_lmhead_confidence (lm_stream_kernel<4> + lm_merge_kernel), 64 rows x 152064 x 3584",
                 "algorithmic_bytes": lm_bytes, "launch_us_mean": round(lm_mean * 1e6, 2),
                 "launch_us_median": round(float(np.median(lm_t)) * 1e6, 2),
                 "timing": f"HIP events around each of {len(lm_t)} LM-head launches of a second timed pass of "
