@@ -41,7 +41,11 @@ TID = {
     "mask": 30, "plant": 40,
     # stand-alone operands for single-call tests
     "q": 50, "blk_k": 51, "blk_v": 52, "h": 53, "conf": 54,
+    # multi-layer model (layer l uses tensor id base + 16 * l)
+    "mE": 60, "mWlm": 61, "mprompt": 62, "x": 63, "pos": 64,
+    "mWq": 1000, "mWk": 1001, "mWv": 1002, "mWo": 1003, "mWg": 1004, "mWu": 1005, "mWd": 1006,
 }
+_LAYER_STRIDE = 16
 
 
 # --------------------------------------------------------------------------
@@ -136,9 +140,10 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return x
 
 
-def normal(seed: int, name: str, shape, std: float, dtype: str) -> np.ndarray:
-    """N(0, std^2) float32 array (bf16-representable when dtype == 'bf16')."""
-    tid = TID[name]
+def normal(seed: int, name: str, shape, std: float, dtype: str, layer: int = 0) -> np.ndarray:
+    """N(0, std^2) float32 array (bf16-representable when dtype == 'bf16');
+    ``layer`` selects the draw of a per-layer tensor."""
+    tid = TID[name] + _LAYER_STRIDE * layer
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
     nchunks = (n + _CHUNK - 1) // _CHUNK
@@ -336,3 +341,99 @@ def mask_bits(masked: np.ndarray) -> np.ndarray:
 def bits_to_mask(bits: np.ndarray, D: int) -> np.ndarray:
     bits = np.asarray(bits, dtype=np.uint64)
     return np.stack([(bits >> np.uint64(j)) & np.uint64(1) for j in range(D)], axis=1).astype(bool)
+
+
+# --------------------------------------------------------------------------
+# multi-layer model (end-to-end decode)
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class ModelConfig:
+    """A random-init Qwen2.5-shaped decoder for the end-to-end decode.
+
+    n_layers layers of hidden size Hq*d with GQA (Hq/Hkv heads of dim d) and
+    a SwiGLU MLP of width inter; vocab V (+ the [MASK] row of E).  B prompts
+    of prompt_len uniform token ids (a whole number of blocks), n_blocks
+    blocks of D generated in windows of S, threshold tau.  RMSNorm eps and
+    RoPE theta are the Qwen2.5 family's (the pages do not give them; any
+    values are valid for random weights).  cap = cache rows per sequence.
+    lm_scale scales the LM-head weights (tiny configs: so that some
+    candidates pass the threshold).
+    """
+    name: str
+    dtype: str
+    B: int
+    n_layers: int
+    Hq: int
+    Hkv: int
+    d: int
+    hidden: int
+    inter: int
+    V: int
+    prompt_len: int
+    n_blocks: int
+    D: int = 32
+    S: int = 8
+    tau: float = 0.9
+    std: float = 0.02
+    eps: float = 1e-6
+    theta: float = 1e6
+    lm_scale: float = 1.0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def cap(self) -> int:
+        return self.prompt_len + self.n_blocks * self.D
+
+
+# end-to-end Qwen2.5-1.5B shape: 16 prompts of 512 ids, 512 new tokens
+C5 = ModelConfig(name="c5", dtype="bf16", B=16, n_layers=28, Hq=12, Hkv=2, d=128, hidden=1536,
+                 inter=8960, V=151936, prompt_len=512, n_blocks=16)
+# small models the oracle runs in seconds (tests)
+M1 = ModelConfig(name="m1", dtype="f32", B=2, n_layers=2, Hq=4, Hkv=2, d=64, hidden=256, inter=512,
+                 V=1024, prompt_len=64, n_blocks=2, lm_scale=100.0)
+M2 = ModelConfig(name="m2", dtype="bf16", B=2, n_layers=2, Hq=4, Hkv=2, d=128, hidden=512, inter=768,
+                 V=2048, prompt_len=64, n_blocks=1, lm_scale=100.0)
+MODEL_CONFIGS = {c.name: c for c in (C5, M1, M2)}
+
+
+@dataclass
+class LayerWeights:
+    """Wq [Hq*d, hid], Wk/Wv [Hkv*d, hid], Wo [hid, Hq*d], Wg/Wu [inter,
+    hid], Wd [hid, inter] (out x in, row-major)."""
+    Wq: np.ndarray
+    Wk: np.ndarray
+    Wv: np.ndarray
+    Wo: np.ndarray
+    Wg: np.ndarray
+    Wu: np.ndarray
+    Wd: np.ndarray
+
+
+@dataclass
+class ModelWeights:
+    E: np.ndarray
+    layers: list
+    Wlm: np.ndarray
+
+
+def make_model_weights(cfg: ModelConfig, seed: int) -> ModelWeights:
+    dt, s = cfg.dtype, cfg.std
+    hq, hkv, hid, I = cfg.Hq * cfg.d, cfg.Hkv * cfg.d, cfg.hidden, cfg.inter
+    E = normal(seed, "mE", (cfg.V + 1, hid), s, dt)
+    layers = []
+    for l in range(cfg.n_layers):
+        layers.append(LayerWeights(
+            normal(seed, "mWq", (hq, hid), s, dt, l), normal(seed, "mWk", (hkv, hid), s, dt, l),
+            normal(seed, "mWv", (hkv, hid), s, dt, l), normal(seed, "mWo", (hid, hq), s, dt, l),
+            normal(seed, "mWg", (I, hid), s, dt, l), normal(seed, "mWu", (I, hid), s, dt, l),
+            normal(seed, "mWd", (hid, I), s, dt, l)))
+    Wlm = normal(seed, "mWlm", (cfg.V, hid), s * cfg.lm_scale, dt)
+    return ModelWeights(E, layers, Wlm)
+
+
+def make_prompts(cfg: ModelConfig, seed: int) -> np.ndarray:
+    """[B, prompt_len] int32 uniform token ids."""
+    return _rng(seed, TID["mprompt"]).integers(0, cfg.V, size=(cfg.B, cfg.prompt_len)).astype(np.int32)
