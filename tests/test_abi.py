@@ -87,7 +87,8 @@ def test_lmhead_unmask_append_argument_errors():
     lib = _lib.load()
     E, U, C = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED, _lib.BD_ECAPACITY
     ws = lib.bd_lmhead_workspace_size(1, 64, 3584, 152064)
-    assert ws >= 64 * 1188 * 12
+    assert ws >= 64 * 512 * 12          # one (max, argmax, sum) per row and streaming work-group
+    assert lib.bd_lmhead_workspace_size(1, 1024, 3584, 152064) >= 1024 * 594 * 12  # per row and 256-column block
     lm = lambda **k: lib.bd_lmhead_confidence(k.get("dt", 1), k.get("M", 8), k.get("hidden", 1536), 151936,
                                               FAKE, k.get("n_src", 9), k.get("ri", FAKE), FAKE, FAKE, FAKE,
                                               None, None, None, FAKE, k.get("wsb", 1 << 30), None)
