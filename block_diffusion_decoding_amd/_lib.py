@@ -56,6 +56,9 @@ SIGNATURES = {
                             c_void_p, c_int, c_void_p, BdRows,
                             c_void_p, c_void_p, c_int, c_void_p, BdRows, c_void_p, BdRows,
                             c_void_p, c_size_t, c_void_p]),
+    "bd_rmsnorm": (c_int, [c_int, c_int, c_int, c_void_p, BdRows, c_float, c_void_p, BdRows, c_void_p]),
+    "bd_rope": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, BdRows, c_void_p, c_int, c_float, c_void_p]),
+    "bd_swiglu": (c_int, [c_int, c_int, c_int, c_void_p, BdRows, c_void_p, BdRows, c_void_p]),
 }
 
 _lib = None

@@ -251,4 +251,30 @@ bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, cons
   return gemm_common(dt, M, K, x, xr, segs, 3, workspace, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+bd_status bd_rmsnorm(bd_dtype dt, int M, int hidden, const void* x, bd_rows xr, float eps, void* y, bd_rows yr,
+                     void* stream) {
+  if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
+  if (M == 0) return BD_OK;
+  if (hidden <= 0 || !x || !y || !valid_rows(xr) || !valid_rows(yr) || !(eps >= 0.f)) return BD_EINVAL;
+  return hip_status(bd_rmsnorm_launch(dt, M, hidden, x, xr, eps, y, yr, static_cast<hipStream_t>(stream)));
+}
+
+bd_status bd_rope(bd_dtype dt, int B, int n_rows, int H, int d, void* x, bd_rows xr, const int32_t* pos_base,
+                  int pos_off, float theta, void* stream) {
+  if (!valid_dtype(dt) || B < 0 || n_rows < 0) return BD_EINVAL;
+  if (B == 0 || n_rows == 0) return BD_OK;
+  if (H <= 0 || d <= 0 || d % 2 != 0 || pos_off < 0 || !x || !pos_base || !valid_rows(xr) || !(theta > 1.f))
+    return BD_EINVAL;
+  return hip_status(bd_rope_launch(dt, B, n_rows, H, d, x, xr, pos_base, pos_off, theta,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+bd_status bd_swiglu(bd_dtype dt, int M, int inter, const void* gu, bd_rows gr, void* a, bd_rows ar, void* stream) {
+  if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
+  if (M == 0) return BD_OK;
+  if (inter <= 0 || !gu || !a || !valid_rows(gr) || !valid_rows(ar)) return BD_EINVAL;
+  return hip_status(bd_swiglu_launch(dt, M, inter, gu, gr, a, ar, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -109,3 +109,11 @@ hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* 
 hipError_t bd_append_launch(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache,
                             void* v_cache, int32_t* kv_len, const void* k_blk, const void* v_blk,
                             int n_blk, int n_rows, hipStream_t s);
+
+// ---- layer pieces of the multi-layer model (model_ops.hip) --------------------
+hipError_t bd_rmsnorm_launch(bd_dtype dt, int M, int hidden, const void* x, bd_rows xr, float eps, void* y,
+                             bd_rows yr, hipStream_t s);
+hipError_t bd_rope_launch(bd_dtype dt, int B, int n_rows, int H, int d, void* x, bd_rows xr, const int32_t* pos_base,
+                          int pos_off, float theta, hipStream_t s);
+hipError_t bd_swiglu_launch(bd_dtype dt, int M, int inter, const void* gu, bd_rows gr, void* a, bd_rows ar,
+                            hipStream_t s);

@@ -291,14 +291,7 @@ class BlockDecoder:
         B, D = dm.B, dm.D
         if self.plant is None:
             self.plant = torch.zeros(B, D, dm.hidden, dtype=self.dtype, device=self.device)
-        dt = self.dtype
-        need = {"attn": max(ops.bd_block_attn_workspace_size(dt, B, dm.Hq, dm.Hkv, dm.d, n, dm.cap, D)
-                            for n in (S, D)),
-                "lm": ops.bd_lmhead_workspace_size(dt, B * S, dm.hidden, dm.V),
-                "gemm": max([ops.bd_qkv_proj_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d, dm.Hkv * dm.d)
-                             for M in (B * S, B * D)] +
-                            [ops.bd_linear_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d) for M in (B, B * S, B * D)])}
-        for tag, n in need.items():
+        for tag, n in self._workspace_needs(S).items():
             ops.workspace(n, self.device, tag)
         for s in range(D // S):
             self._window(s, S)
@@ -320,6 +313,17 @@ class BlockDecoder:
         self.graphs[("commit", 0)] = g
         self._graph_S, self._graph_tau = S, tau
         torch.cuda.synchronize()
+
+    def _workspace_needs(self, S: int) -> dict:
+        """Workspace bytes per tag that the steps and the commit use."""
+        dm = self.dims
+        B, D, dt = dm.B, dm.D, self.dtype
+        return {"attn": max(ops.bd_block_attn_workspace_size(dt, B, dm.Hq, dm.Hkv, dm.d, n, dm.cap, D)
+                            for n in (S, D)),
+                "lm": ops.bd_lmhead_workspace_size(dt, B * S, dm.hidden, dm.V),
+                "gemm": max([ops.bd_qkv_proj_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d, dm.Hkv * dm.d)
+                             for M in (B * S, B * D)] +
+                            [ops.bd_linear_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d) for M in (B, B * S, B * D)])}
 
     def _replay(self, kind: str, s: int, S: int, tau: float) -> bool:
         g = self.graphs.get((kind, s))

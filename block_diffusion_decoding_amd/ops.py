@@ -212,3 +212,24 @@ def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, ws=None, stream=No
     st = lib.bd_qkv_proj(dt, M, K, _p(x), xr, _p(wq), Nq, _p(q), qr, _p(wk), _p(wv), Nkv, _p(k), kr, _p(v),
                          vr, _p(ws), ws.numel(), _stream(stream))
     _check("bd_qkv_proj", st)
+
+
+def bd_rmsnorm(x, xr, y, yr, *, M, eps, stream=None):
+    """y[yr(m)] = rmsnorm(x[xr(m)]) (unit gains); rows of x.shape[-1] elements."""
+    st = _lib.load().bd_rmsnorm(_dt(x), M, x.shape[-1], _p(x), xr, float(eps), _p(y), yr, _stream(stream))
+    _check("bd_rmsnorm", st)
+
+
+def bd_rope(x, xr, pos_base, *, n_rows, H, d, pos_off=0, theta, stream=None):
+    """Rotary embedding in place on rows xr(b*n_rows + i) of x at positions
+    pos_base[b] + pos_off + i; B = pos_base.numel()."""
+    st = _lib.load().bd_rope(_dt(x), pos_base.numel(), n_rows, H, d, _p(x), xr, _p(pos_base), int(pos_off),
+                             float(theta), _stream(stream))
+    _check("bd_rope", st)
+
+
+def bd_swiglu(gu, gr, a, ar, *, M, inter, stream=None):
+    """a[ar(m)] = silu(gate) * up of the row gu[gr(m)] = [gate | up]."""
+    st = _lib.load().bd_swiglu(_dt(gu), M, inter, _p(gu), gr, _p(a), ar, _stream(stream))
+    _check("bd_swiglu", st)
+

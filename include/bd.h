@@ -264,6 +264,37 @@ bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
                       void* k, bd_rows kr, void* v, bd_rows vr,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Layer pieces of the multi-layer decode (support calls).  The pages name the
+ * model family ([v2 notes] main results: Qwen2.5-style decoders adapted to
+ * block diffusion) but not its layer equations; these are that family's
+ * usual pieces, applied in pre-norm layers.  bf16 or fp32 storage (dt),
+ * fp32 arithmetic; in place is allowed for bd_rmsnorm (x == y, same rows).
+ * Rows that the row maps send to the same buffer row are undefined.
+ * ---------------------------------------------------------------------- */
+
+/* RMSNorm with unit gains: y[yr(m)] = x[xr(m)] / sqrt(mean_k x[xr(m), k]^2 + eps)
+ * for m < M; rows hold `hidden` elements.  eps >= 0. */
+bd_status bd_rmsnorm(bd_dtype dt, int M, int hidden, const void* x, bd_rows xr, float eps, void* y,
+                     bd_rows yr, void* stream);
+
+/* Rotary position embedding (rotate-half form), in place.  Logical row
+ * m = b*n_rows + i (b < B, i < n_rows) is buffer row xr(m) of x, holding H
+ * heads of d elements; it sits at position pos_base[b] + pos_off + i
+ * (pos_base [B] int32 on the device, e.g. the committed lengths).  For each
+ * head and j < d/2 the pair (x_j, x_{j+d/2}) is rotated by the angle
+ * pos * theta^(-2j/d): (x_j cos - x_{j+d/2} sin, x_{j+d/2} cos + x_j sin).
+ * d even, theta > 1. */
+bd_status bd_rope(bd_dtype dt, int B, int n_rows, int H, int d, void* x, bd_rows xr, const int32_t* pos_base,
+                  int pos_off, float theta, void* stream);
+
+/* SwiGLU gate: a[ar(m), n] = silu(gu[gr(m), n]) * gu[gr(m), inter + n] for m < M,
+ * n < inter, silu(z) = z / (1 + exp(-z)); rows of gu hold the gate projection
+ * then the up projection (2*inter elements), rows of a hold inter; a must
+ * not overlap gu. */
+bd_status bd_swiglu(bd_dtype dt, int M, int inter, const void* gu, bd_rows gr, void* a, bd_rows ar,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

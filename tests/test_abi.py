@@ -165,3 +165,26 @@ print(st, lib.bd_last_hip_error())
         pytest.skip("a GPU is visible; this check is for hosts without one")
     st, err = map(int, r.stdout.split()[-2:])
     assert st == _lib.BD_EHIP and err != 0
+
+
+def test_layer_piece_argument_errors():
+    """RMSNorm, rotary embedding and SwiGLU reject bad shapes before any
+    launch; empty calls succeed."""
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    d1, bad = _lib.BdRows(1, 1, 0), _lib.BdRows(0, 1, 0)
+    assert lib.bd_rmsnorm(1, 0, 1536, FAKE, d1, 1e-6, FAKE, d1, None) == 0
+    assert lib.bd_rmsnorm(1, 4, 0, FAKE, d1, 1e-6, FAKE, d1, None) == E
+    assert lib.bd_rmsnorm(1, 4, 1536, None, d1, 1e-6, FAKE, d1, None) == E
+    assert lib.bd_rmsnorm(1, 4, 1536, FAKE, bad, 1e-6, FAKE, d1, None) == E
+    assert lib.bd_rmsnorm(1, 4, 1536, FAKE, d1, -1.0, FAKE, d1, None) == E
+    assert lib.bd_rmsnorm(7, 4, 1536, FAKE, d1, 1e-6, FAKE, d1, None) == E
+    assert lib.bd_rope(1, 2, 0, 12, 128, FAKE, d1, FAKE, 0, 1e6, None) == 0
+    assert lib.bd_rope(1, 2, 8, 12, 127, FAKE, d1, FAKE, 0, 1e6, None) == E
+    assert lib.bd_rope(1, 2, 8, 12, 128, FAKE, d1, None, 0, 1e6, None) == E
+    assert lib.bd_rope(1, 2, 8, 12, 128, FAKE, d1, FAKE, -1, 1e6, None) == E
+    assert lib.bd_rope(1, 2, 8, 12, 128, FAKE, d1, FAKE, 0, 1.0, None) == E
+    assert lib.bd_swiglu(1, 0, 8960, FAKE, d1, FAKE, d1, None) == 0
+    assert lib.bd_swiglu(1, 3, 0, FAKE, d1, FAKE, d1, None) == E
+    assert lib.bd_swiglu(1, 3, 8960, FAKE, d1, None, d1, None) == E
+    assert lib.bd_swiglu(1, 3, 8960, FAKE, bad, FAKE, d1, None) == E

@@ -1,0 +1,178 @@
+"""GPU parity of the multi-layer decode against the oracle (oracle/model.py):
+the layer-piece calls one by one, a small fp32 model's whole generation
+token for token, and single steps of a small bf16 model within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import bd_inputs as bi
+from gpu_util import DEV, TOL, down, lm_stats_close, rows_close, say, tdt, up
+from oracle import model as OM
+from oracle import refine as R
+
+pytestmark = pytest.mark.gpu
+
+
+def ops():
+    from block_diffusion_decoding_amd import ops as o
+    return o
+
+
+# --------------------------------------------------------------- layer pieces
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rmsnorm_rows_and_in_place(dtype):
+    say(f"[model] rmsnorm {dtype}")
+    o = ops()
+    x = bi.normal(1, "x", (5, 12, 1536), 0.7, dtype)
+    xt = up(x, tdt(dtype))
+    y = torch.zeros(5, 13, 1536, dtype=tdt(dtype), device=DEV)
+    # rows 2..9 of each of the 5 sequences -> rows 1..8 of y
+    o.bd_rmsnorm(xt, o.rows(8, 12, 2), y, o.rows(8, 13, 1), M=40, eps=1e-6)
+    ref = OM.rmsnorm(x[:, 2:10].astype(np.float64), 1e-6)
+    rows_close(down(y[:, 1:9]), ref, TOL[dtype], "rmsnorm")
+    assert not y[:, 0].any() and not y[:, 9:].any()
+    o.bd_rmsnorm(xt, o.dense(60), xt, o.dense(60), M=60, eps=1e-6)
+    rows_close(down(xt), OM.rmsnorm(x.astype(np.float64), 1e-6), TOL[dtype], "rmsnorm in place")
+
+
+@pytest.mark.parametrize("dtype,H,d", [("f32", 4, 64), ("bf16", 12, 128), ("bf16", 2, 128)])
+def test_rope_positions_from_lengths(dtype, H, d):
+    say(f"[model] rope {dtype} H{H} d{d}")
+    o = ops()
+    B, D, n, lo = 3, 32, 8, 16
+    x = bi.normal(2, "x", (B, D, H * d), 0.5, dtype)
+    lens = np.array([0, 512, 4064], dtype=np.int32)
+    xt = up(x, tdt(dtype))
+    o.bd_rope(xt, o.rows(n, D, lo), up(lens), n_rows=n, H=H, d=d, pos_off=lo, theta=1e6)
+    got = down(xt).reshape(B, D, H, d)
+    for b in range(B):
+        pos = lens[b] + lo + np.arange(n)
+        ref = OM.rope(x[b, lo:lo + n].astype(np.float64).reshape(n, H, d), pos, 1e6)
+        rows_close(got[b, lo:lo + n].reshape(n * H, d), ref.reshape(n * H, d), TOL[dtype], f"rope seq {b}")
+        outside = np.ones(D, bool)
+        outside[lo:lo + n] = False
+        assert np.array_equal(got[b, outside], down(up(x, tdt(dtype)))[b][outside].reshape(-1, H, d))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_swiglu(dtype):
+    say(f"[model] swiglu {dtype}")
+    o = ops()
+    M, I = 37, 8960
+    gu = bi.normal(3, "x", (M, 2 * I), 2.0, dtype)
+    a = torch.zeros(M, I, dtype=tdt(dtype), device=DEV)
+    o.bd_swiglu(up(gu, tdt(dtype)), o.dense(M), a, o.dense(M), M=M, inter=I)
+    g64 = gu.astype(np.float64)
+    ref = OM.silu(g64[:, :I]) * g64[:, I:]
+    rows_close(down(a), ref, TOL[dtype], "swiglu")
+
+
+# ------------------------------------------------------------- whole decode
+def _decoder(cfg, w):
+    from block_diffusion_decoding_amd.model import ModelDecoder, ModelDims
+    dims = ModelDims(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.hidden, cfg.V, cfg.D, cfg.cap,
+                     n_layers=cfg.n_layers, inter=cfg.inter, eps=cfg.eps, theta=cfg.theta)
+    t = lambda a: torch.from_numpy(a)
+    weights = {"E": t(w.E), "Wlm": t(w.Wlm),
+               "layers": [{k: t(getattr(l, k)) for k in ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd")} for l in w.layers]}
+    return ModelDecoder(dims, weights, dtype=tdt(cfg.dtype), device=DEV)
+
+
+def _oracle(cfg, w):
+    return OM.LM.from_weights(w, cfg)
+
+
+def test_small_fp32_model_generates_the_oracle_tokens():
+    """Two layers, two prompts of 64 ids, two blocks of 32 generated with the
+    threshold 0.9 (lm_scale makes some candidates pass): the same tokens,
+    step for step."""
+    cfg = bi.M1
+    say("[model] fp32 generate")
+    w = bi.make_model_weights(cfg, 0)
+    prompts = bi.make_prompts(cfg, 0)
+    m = _oracle(cfg, w)
+    ref_steps = []
+    seqs = OM.generate(m, prompts, cfg.n_blocks, cfg.D, cfg.S, cfg.tau,
+                       on_step=lambda i, s, kind, res: ref_steps.append((s, kind, [r.conf for r in res])))
+    ref = np.stack([np.asarray(q.history[cfg.prompt_len:]) for q in seqs])
+    # the comparison is meaningful only where the oracle's decisions are not
+    # near ties: every candidate confidence is 1e-4 away from the threshold
+    # and the fallback picks have a clear winner
+    for s, kind, confs in ref_steps:
+        for c in confs:
+            assert np.all(np.abs(np.asarray(c) - cfg.tau) > 1e-4)
+    dec = _decoder(cfg, w)
+    got = dec.generate(prompts, cfg.n_blocks, cfg.S, cfg.tau)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, ref), f"tokens differ at {np.argwhere(got != ref)[:5]}"
+    assert int(dec.kv_len[0, 0]) == cfg.cap and int(dec.kv_len[-1, -1]) == cfg.cap
+    # the caches hold the oracle's rotated K/V of every committed position
+    for l in (0, cfg.n_layers - 1):
+        rows_close(down(dec.cache_k[l, 1]).transpose(1, 0, 2).reshape(cfg.cap, -1),
+                   seqs[1].cache_k[l].reshape(cfg.cap, -1), TOL["f32"], f"cache_k layer {l}")
+
+
+def test_small_bf16_model_steps_match_the_oracle():
+    """Prefill, then an exact step and a DualCache step of window 1 on a bf16
+    model: final rows, LM-head statistics and unmask decisions."""
+    cfg = bi.M2
+    say("[model] bf16 steps")
+    w = bi.make_model_weights(cfg, 1)
+    prompts = bi.make_prompts(cfg, 1)
+    m = _oracle(cfg, w)
+    D, S = cfg.D, cfg.S
+    seqs = [OM.prefill(m, p, D) for p in prompts]
+    dec = _decoder(cfg, w)
+    dec.prefill(prompts)
+    rows_close(down(dec.H[:, 0]), np.stack([q.carry for q in seqs]), TOL["bf16"], "carry after prefill")
+    st = bi.make_block_state(bi.C1, 1, 1)   # window 1 state of a 32-block (tokens clipped to V)
+    tokens = np.minimum(st.tokens[:1].repeat(cfg.B, 0), cfg.V - 1)
+    masked = st.masked[:1].repeat(cfg.B, 0)
+    tokens[masked] = 0
+    for b, q in enumerate(seqs):
+        q.tokens, q.masked = tokens[b].astype(np.int64).copy(), masked[b].copy()
+    dec.set_tokens(tokens, masked)
+    tol = TOL["bf16"]
+    for kind in ("E", "DC"):
+        before = np.stack([q.masked for q in seqs])
+        res = [(OM.e_step if kind == "E" else OM.dc_step)(m, q, 1, S, cfg.tau, D) for q in seqs]
+        (dec.e_step if kind == "E" else dec.dc_step)(1, S, cfg.tau)
+        torch.cuda.synchronize()
+        rows = np.arange(D) if kind == "E" else np.arange(S, 2 * S)
+        rows_close(down(dec.H[:, 1 + rows]), np.stack([r.H for r in res]), tol, f"{kind} final rows")
+        srcs = np.stack([r.src for r in res]).reshape(-1, cfg.hidden)
+        logits = R.lm_logits(m.Wlm, srcs)
+        wl = dec.last
+        am, cf = wl["argmax"].cpu().numpy().reshape(-1), wl["conf"].cpu().numpy().reshape(-1)
+        cand = before[:, S:2 * S].reshape(-1)
+        lm_stats_close(am[cand], cf[cand], None, None, logits[cand], tol, f"{kind} LM head")
+        got_masked = dec.masked_host()
+        # the window's decisions: exact except near-threshold confidences
+        for b, q in enumerate(seqs):
+            ref_conf = res[b].conf
+            for r in range(S):
+                j = S + r
+                if before[b, j] and abs(ref_conf[r] - cfg.tau) > 1e-3:
+                    assert got_masked[b, j] == q.masked[j], f"{kind}: seq {b} position {j}"
+        dec.set_tokens(np.stack([q.tokens for q in seqs]), np.stack([q.masked for q in seqs]))
+
+
+def test_model_graph_replays_match_eager_launches():
+    """Captured steps of the multi-layer decoder replay bit for bit like
+    eager launches (two decoders side by side, one whole block)."""
+    cfg = bi.M2
+    say("[model] graphs")
+    w = bi.make_model_weights(cfg, 2)
+    prompts = bi.make_prompts(cfg, 2)
+    a, b = _decoder(cfg, w), _decoder(cfg, w)
+    for d in (a, b):
+        d.prefill(prompts)
+        d.new_block()
+    b.capture(cfg.S, cfg.tau)
+    na = a.decode_block(cfg.S, cfg.tau)
+    nb = b.decode_block(cfg.S, cfg.tau)
+    torch.cuda.synchronize()
+    assert na == nb
+    assert torch.equal(a.tokens, b.tokens)
+    assert torch.equal(a.cache_k, b.cache_k) and torch.equal(a.cache_v, b.cache_v)
+    assert torch.equal(a.H, b.H)
