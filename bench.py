@@ -196,9 +196,73 @@ def time_call(fn, reps, warm=3, warm_s=0.1):
     return float(np.median(t)), float(np.mean(t))
 
 
-def extras(w3, reps, parts=("attn", "long", "lm"), graphs=True):
-    """Attention and LM head alone at the long-context / batched shapes, and
-    the long-context block loop."""
+def extras_e2e(graphs=True, n_blocks=None):
+    """End-to-end decode of the random-init 1.5B-shaped model: B prompts of
+    prompt_len ids, prefill, then n_blocks blocks of D generated in windows of
+    S with threshold tau (steps replayed as captured HIP graphs).  The weights
+    are N(0, 0.02) drawn on the GPU from a seeded generator (no oracle runs at
+    this size)."""
+    from block_diffusion_decoding_amd.model import ModelDecoder, ModelDims
+    cfg = bi.C5
+    nb = cfg.n_blocks if n_blocks is None else n_blocks
+    log(f"[bench] end-to-end 1.5B-shape decode: {cfg.n_layers} layers, B {cfg.B}, prompt {cfg.prompt_len}, "
+        f"{nb} blocks")
+    dev, dt = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+
+    def rnd(*shape):
+        return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * cfg.std).to(dt)
+
+    hq, hkv, hid, I = cfg.Hq * cfg.d, cfg.Hkv * cfg.d, cfg.hidden, cfg.inter
+    weights = {"E": rnd(cfg.V + 1, hid), "Wlm": rnd(cfg.V, hid),
+               "layers": [{"Wq": rnd(hq, hid), "Wk": rnd(hkv, hid), "Wv": rnd(hkv, hid), "Wo": rnd(hid, hq),
+                           "Wg": rnd(I, hid), "Wu": rnd(I, hid), "Wd": rnd(hid, I)} for _ in range(cfg.n_layers)]}
+    dims = ModelDims(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, hid, cfg.V, cfg.D, cfg.prompt_len + nb * cfg.D,
+                     n_layers=cfg.n_layers, inter=I, eps=cfg.eps, theta=cfg.theta)
+    dec = ModelDecoder(dims, weights, dtype=dt, device=dev)
+    del weights
+    prompts = bi.make_prompts(cfg, 0)
+    n_weight_bytes = sum(t.numel() * 2 for lw in dec.layers for t in lw.values()) + 2 * dec.W["Wlm"].numel() * 2
+    # warm-up: a prefill and one block (also sizes every workspace), then capture
+    dec.prefill(prompts)
+    dec.new_block()
+    dec.decode_block(cfg.S, cfg.tau)
+    if graphs:
+        dec.capture(cfg.S, cfg.tau)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dec.prefill(prompts)
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t0
+    steps = []
+    t1 = time.perf_counter()
+    for _ in range(nb):
+        dec.new_block()
+        steps.append(dec.decode_block(cfg.S, cfg.tau))
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t1
+    tokens = cfg.B * nb * cfg.D
+    n_steps = int(sum(steps))
+    log(f"[bench] e2e: prefill {t_pre * 1e3:.1f} ms, decode {t_dec * 1e3:.1f} ms for {tokens} tokens "
+        f"({n_steps} refinement steps + {nb} commits): {tokens / t_dec:.0f} tokens/s decoding, "
+        f"{tokens / (t_pre + t_dec):.0f} tokens/s with the prefill")
+    out = {"e2e_1.5B": {"shape": f"{cfg.n_layers} layers, hidden {hid}, {cfg.Hq}q/{cfg.Hkv}kv heads d{cfg.d}, "
+                                 f"MLP {I}, vocab {cfg.V}; B {cfg.B}, prompt {cfg.prompt_len}, {nb} blocks of "
+                                 f"{cfg.D} (sub-block {cfg.S}), tau {cfg.tau}",
+                        "prefill_ms": t_pre * 1e3, "decode_ms": t_dec * 1e3, "tokens": tokens,
+                        "refinement_steps": n_steps, "commits": nb,
+                        "decode_tokens_per_s": tokens / t_dec, "tokens_per_s_with_prefill": tokens / (t_pre + t_dec),
+                        "ms_per_step": t_dec / (n_steps + nb) * 1e3, "weight_bytes_per_forward": n_weight_bytes,
+                        "graphs": graphs}}
+    del dec
+    torch.cuda.empty_cache()
+    return out
+
+
+def extras(w3, reps, parts=("attn", "long", "lm", "e2e"), graphs=True, e2e_blocks=None):
+    """Attention and LM head alone at the long-context / batched shapes, the
+    long-context block loop and the end-to-end multi-layer decode."""
     from block_diffusion_decoding_amd import ops
     out = {}
     T = torch.bfloat16
@@ -209,6 +273,8 @@ def extras(w3, reps, parts=("attn", "long", "lm"), graphs=True):
         out.update(extras_long(c4, w3, graphs))
     if "lm" in parts:
         out.update(extras_lm(w3, reps))
+    if "e2e" in parts:
+        out.update(extras_e2e(graphs, e2e_blocks))
     return out
 
 
@@ -352,9 +418,11 @@ def main():
     ap.add_argument("--no-graphs", action="store_true", help="launch every step's kernels eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
-    ap.add_argument("--section", choices=("all", "attn", "long", "lm"), default="all",
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e"), default="all",
                     help="attn/long/lm: run only that single-call or loop measurement (for profiling) and print "
                          "its JSON instead of the bench line")
+    ap.add_argument("--e2e-blocks", type=int, default=None,
+                    help="blocks generated by the end-to-end decode measurement (default: the workload's 16)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/lmhead_7B_M64_traffic.json from two rocprofv3 --pmc counter files of "
                          "`--section lm` (FETCH_SIZE, WRITE_SIZE) and exit")
@@ -373,6 +441,10 @@ def main():
     pkg.load_library()
 
     cfg = bi.C3
+    if args.section == "e2e":
+        print(json.dumps(extras(None, args.reps, parts=("e2e",), graphs=not args.no_graphs,
+                                e2e_blocks=args.e2e_blocks)), flush=True)
+        return
     log("[bench] generating the 7B-shape workload")
     w = bi.make_weights(cfg, 0)
     if args.section != "all":
@@ -439,7 +511,7 @@ def main():
     if not args.no_extras:
         del dec
         torch.cuda.empty_cache()
-        extra = extras(w, args.reps)
+        extra = extras(w, args.reps, e2e_blocks=args.e2e_blocks)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")

@@ -204,7 +204,7 @@ bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int 
 }
 
 static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const BdGemmSeg* segs, int nseg,
-                             void* workspace, size_t ws_bytes, void* stream) {
+                             int mode, const BdGemmRope* rope, void* workspace, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
   if (M == 0) return BD_OK;
   if (K <= 0 || !x || !valid_rows(xr)) return BD_EINVAL;
@@ -214,32 +214,45 @@ static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows x
     if (segs[i].res && !valid_rows(segs[i].rr)) return BD_EINVAL;
     N[i] = segs[i].N;
   }
+  if (mode == BD_GEMM_ROPE) {
+    const int d = rope->d;
+    if (d <= 0 || d % 8 != 0 || N[0] % d != 0 || N[1] % d != 0 || rope->n_rows <= 0 || M % rope->n_rows != 0 ||
+        rope->pos_off < 0 || !rope->pos_base || !(rope->theta > 1.f))
+      return BD_EINVAL;
+  }
   if (dt == BD_BF16) {
     if (K % 256 != 0 || !aligned16(x)) return BD_EUNSUPPORTED;
     for (int i = 0; i < nseg; ++i)
       if (!aligned16(segs[i].w)) return BD_EUNSUPPORTED;
   }
-  const BdGemmPlan p = bd_gemm_plan(dt, M, K, N, nseg);
+  const BdGemmPlan p = bd_gemm_plan(dt, M, K, N, nseg, mode);
   if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)))
     return BD_EINVAL;
-  return hip_status(bd_gemm_launch(dt, p, M, K, x, xr, segs, nseg, workspace, static_cast<hipStream_t>(stream)));
+  return hip_status(bd_gemm_launch(dt, p, M, K, x, xr, segs, nseg, mode, rope, workspace,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 size_t bd_linear_workspace_size(bd_dtype dt, int M, int N, int K) {
   if (!valid_dtype(dt) || M <= 0 || N <= 0 || K <= 0) return 0;
-  return bd_gemm_plan(dt, M, K, &N, 1).ws_bytes;
+  return bd_gemm_plan(dt, M, K, &N, 1, BD_GEMM_PLAIN).ws_bytes;
 }
 
 size_t bd_qkv_proj_workspace_size(bd_dtype dt, int M, int K, int Nq, int Nkv) {
   if (!valid_dtype(dt) || M <= 0 || K <= 0 || Nq <= 0 || Nkv <= 0) return 0;
   const int N[3] = {Nq, Nkv, Nkv};
-  return bd_gemm_plan(dt, M, K, N, 3).ws_bytes;
+  return bd_gemm_plan(dt, M, K, N, 3, BD_GEMM_PLAIN).ws_bytes;
+}
+
+size_t bd_qkv_proj_rope_workspace_size(bd_dtype dt, int M, int K, int Nq, int Nkv) {
+  if (!valid_dtype(dt) || M <= 0 || K <= 0 || Nq <= 0 || Nkv <= 0) return 0;
+  const int N[3] = {Nq, Nkv, Nkv};
+  return bd_gemm_plan(dt, M, K, N, 3, BD_GEMM_ROPE).ws_bytes;
 }
 
 bd_status bd_linear(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr, const void* w, const void* res,
                     bd_rows rr, void* y, bd_rows yr, void* workspace, size_t ws_bytes, void* stream) {
   BdGemmSeg seg{w, y, yr, res, rr, N};
-  return gemm_common(dt, M, K, x, xr, &seg, 1, workspace, ws_bytes, stream);
+  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_PLAIN, nullptr, workspace, ws_bytes, stream);
 }
 
 bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,
@@ -248,7 +261,25 @@ bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, cons
   const bd_rows none{1, 1, 0};
   BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
                        {wv, v, vr, nullptr, none, Nkv}};
-  return gemm_common(dt, M, K, x, xr, segs, 3, workspace, ws_bytes, stream);
+  return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_PLAIN, nullptr, workspace, ws_bytes, stream);
+}
+
+bd_status bd_qkv_proj_rope(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,
+                           bd_rows qr, const void* wk, const void* wv, int Nkv, void* k, bd_rows kr, void* v,
+                           bd_rows vr, int d, const int32_t* pos_base, int n_rows, int pos_off, float theta,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  const bd_rows none{1, 1, 0};
+  BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
+                       {wv, v, vr, nullptr, none, Nkv}};
+  const BdGemmRope rope{pos_base, n_rows, pos_off, d, theta};
+  return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_ROPE, &rope, workspace, ws_bytes, stream);
+}
+
+bd_status bd_gate_up_swiglu(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* w_gu, int inter,
+                            void* a, bd_rows ar, void* stream) {
+  const bd_rows none{1, 1, 0};
+  BdGemmSeg seg{w_gu, a, ar, nullptr, none, inter};
+  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_SWIGLU, nullptr, nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------------------

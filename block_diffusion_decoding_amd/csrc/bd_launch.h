@@ -84,17 +84,38 @@ struct BdGemmSeg {
   int N;
 };
 
-struct BdGemmPlan {
-  int MT;                 // 16-row tiles per work-group
-  int nx, ny;             // column tiles (all segments) and row tiles
-  int ksplit;             // K slices per tile
-  size_t ws_bytes;        // workspace: fp32 partial tiles [tile][slice][rows x 64]
+// Epilogue variants of the projection GEMM.
+enum BdGemmMode {
+  BD_GEMM_PLAIN = 0,   // y = x W^T (+ res)
+  BD_GEMM_ROPE = 1,    // segments 0 and 1 (q, k) rotated after the product
+  BD_GEMM_SWIGLU = 2,  // one segment: W = [gate; up] (2N rows), y = silu(x Wg^T) * (x Wu^T)
 };
 
-BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg);
+// Rotary embedding of the q and k segments (BD_GEMM_ROPE): logical row m is
+// at position pos_base[m / n_rows] + pos_off + m % n_rows; head dim d.
+struct BdGemmRope {
+  const int32_t* pos_base;
+  int n_rows, pos_off, d;
+  float theta;
+};
+
+struct BdGemmPlan {
+  int MT;                 // 16-row tiles per work-group
+  int NTW;                // 16-column tiles per pass
+  int ny;                 // row blocks
+  int T;                  // 16-column tiles over all segments
+  int G;                  // tiles per scheduling unit (2 in SwiGLU mode: a gate and an up tile)
+  int nwg;                // persistent work-groups per (row block, K slice)
+  int passes;             // passes per work-group
+  int ksplit;             // K slices
+  size_t ws_bytes;        // workspace: fp32 partial sums [ksplit][M][T*16]
+};
+
+BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int mode);
 
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
-                          const BdGemmSeg* segs, int nseg, void* workspace, hipStream_t s);
+                          const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope, void* workspace,
+                          hipStream_t s);
 
 hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
                            const void* E, const int32_t* tokens, const uint64_t* mask_bits,

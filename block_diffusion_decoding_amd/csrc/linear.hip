@@ -4,12 +4,20 @@
 // -- a masked position takes the learnable [MASK] embedding.  Projections:
 // the Q/K/V projections of the block rows (fresh rows write their K/V into
 // the in-block buffer, Key design 3) and the attention output projection
-// with its residual.
+// with its residual; for the multi-layer decoder also the gate/up projection
+// with the SwiGLU gate and the Q/K projections with the rotary embedding.
 //
-// bf16 projections use the streaming MFMA core of stream_gemm.h with a plain
-// store epilogue (plus residual); up to three weight matrices (Q, K, V) share
-// one launch, and K is split over work-groups when the column tiles alone
-// cannot fill the GPU.
+// bf16 projections: a persistent streaming GEMM on the MFMA core of
+// stream_gemm.h.  The 16-column tiles of all output segments (Q, K, V share
+// one launch) are dealt out to work-groups in balanced contiguous ranges; a
+// work-group walks its range in passes of up to NTW tiles while the
+// global->LDS DMA pipeline runs on across pass boundaries, so every weight
+// byte is read once from HBM with no per-tile pipeline fill and no tail of
+// short work-groups.  When the tiles alone cannot occupy the GPU, K is split
+// over slices that write fp32 partial sums, added by a second launch that
+// also applies the residual or the rotary embedding.
+#include <cmath>
+
 #include "bd_device.h"
 #include "bd_launch.h"
 #include "stream_gemm.h"
@@ -17,133 +25,355 @@
 namespace {
 
 constexpr int kThreads = 256;
-// Tiling; defaults chosen by measurement, overridable at build time.
-#ifndef BD_GEMM_NTW
-#define BD_GEMM_NTW 4
+// Tiling and scheduling; defaults chosen by measurement, overridable at build
+// time.
+#ifndef BD_GEMM_NS
+#define BD_GEMM_NS 3
 #endif
-#ifndef BD_GEMM_TARGET_WGS
-#define BD_GEMM_TARGET_WGS 512
+#ifndef BD_GEMM_MAX_MT
+#define BD_GEMM_MAX_MT 8
+#endif
+// resident work-groups (two per CU)
+#ifndef BD_GEMM_SLOTS
+#define BD_GEMM_SLOTS 512
 #endif
 #ifndef BD_GEMM_MIN_CHUNKS
 #define BD_GEMM_MIN_CHUNKS 4
 #endif
-#ifndef BD_GEMM_NTW_M64
-#define BD_GEMM_NTW_M64 4
+// Schedule cost model (ns, bytes per ns): a work-group's pipeline stage takes
+// at least STAGE_NS (two stages in flight against the memory latency), or
+// longer when the resident work-groups' stage bytes exceed what HBM (weight
+// tiles) and L2 (row tiles, empty weight slots) deliver; a K split adds a
+// reduction launch and its partial-sum traffic.
+#ifndef BD_GEMM_STAGE_NS
+#define BD_GEMM_STAGE_NS 700
 #endif
-// 16-column tiles per work-group: narrower at 64 rows (more column work-groups,
-// a smaller K split, half the partial sums to add)
-__host__ __device__ constexpr int ntw_for(int MT) { return MT == 4 ? BD_GEMM_NTW_M64 : BD_GEMM_NTW; }
-#ifndef BD_GEMM_NS
-#define BD_GEMM_NS 3
+#ifndef BD_GEMM_HBM_BPNS
+#define BD_GEMM_HBM_BPNS 5000
 #endif
-constexpr int kNS = BD_GEMM_NS;          // pipeline stages
+#ifndef BD_GEMM_L2_BPNS
+#define BD_GEMM_L2_BPNS 15000
+#endif
+#ifndef BD_GEMM_RED_NS
+#define BD_GEMM_RED_NS 2500
+#endif
+#ifndef BD_GEMM_PART_BPNS
+#define BD_GEMM_PART_BPNS 4000
+#endif
+constexpr int kNS = BD_GEMM_NS;  // pipeline stages
 constexpr int kMaxSeg = 3;
-constexpr int kTargetWGs = BD_GEMM_TARGET_WGS;
-constexpr int kMinChunksPerSplit = BD_GEMM_MIN_CHUNKS;
 
-struct GemmK {
+struct GemmS {
   const uint16_t* x;
   bd_rows xr;
-  int M, K, nseg;
+  int M, K, nseg, mode;
   const uint16_t* w[kMaxSeg];
   uint16_t* y[kMaxSeg];
   const uint16_t* res[kMaxSeg];
   bd_rows yr[kMaxSeg];
   bd_rows rr[kMaxSeg];
-  int N[kMaxSeg];
-  int wg_begin[kMaxSeg + 1];
+  int N[kMaxSeg];       // output columns per segment (SwiGLU: the gate width)
+  int tb[kMaxSeg + 1];  // first 16-column tile of each segment; T from nseg on
   int ksplit;
-  float* part;    // [tiles][ksplit][MT*16 x 64] fp32 partial sums (ksplit > 1)
+  float* part;          // [ksplit][M][T*16] fp32 partial sums (ksplit > 1)
+  const int32_t* pos_base;  // rotary embedding (BD_GEMM_ROPE)
+  int n_rows, pos_off, d;
+  double log2_theta;
 };
 
-__device__ __forceinline__ void gemm_store(const GemmK& a, int seg, int m, int col, float v) {
-  const int N = a.N[seg];
-  if (a.res[seg]) v += bd_bf2f(a.res[seg][(size_t)bd_map_row(a.rr[seg], m) * N + col]);
-  a.y[seg][(size_t)bd_map_row(a.yr[seg], m) * N + col] = (uint16_t)bd_f2bf(v);
+__device__ __forceinline__ int seg_of(const GemmS& a, int gt) {
+  return gt >= a.tb[2] ? 2 : (gt >= a.tb[1] ? 1 : 0);
 }
 
-// One (column tile, row tile, K slice) per work-group.  With a K split the
-// slices write fp32 partial tiles that gemm_reduce_kernel adds in slice order
-// (a separate launch: cross-XCD visibility inside one kernel would need
-// device-scope fences, i.e. L2 write-backs, per work-group).
-template <int MT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmK a) {
-  constexpr int kNTW = ntw_for(MT);
-  using C = bd_stream::Cfg<MT, kNTW, kNS>;
-  constexpr int TILE = MT * 16 * kNTW * 16;
+// Work-group (blockIdx.x, row block blockIdx.y, K slice blockIdx.z) owns
+// scheduling units [g0, g0 + ng) of the T/G units (G = 1: a 16-column tile;
+// G = 2 in SwiGLU mode: a gate tile and the matching up tile, adjacent in the
+// tile order so that one wave holds both) and walks them in P passes.
+// Epilogue per pass: bf16 store (+ residual), SwiGLU, or fp32 partial sums.
+template <int MT, int NTW>
+__global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P, int G) {
+  using C = bd_stream::Cfg<MT, NTW, kNS>;
+  static_assert(C::NTP % 2 == 0, "a wave holds whole gate/up tile pairs");
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int wm = wave % C::WM, wn = wave / C::WM;
-  const int bx = blockIdx.x;
-  const int seg = (a.nseg > 2 && bx >= a.wg_begin[2]) ? 2 : (a.nseg > 1 && bx >= a.wg_begin[1]) ? 1 : 0;
-  const int N = a.N[seg];
-  const int n0 = (bx - a.wg_begin[seg]) * kNTW * 16;
   const int m0 = blockIdx.y * MT * 16;
   const int z = blockIdx.z;
-  const int nch = a.K / C::KC;
-  const int c0 = z * nch / a.ksplit, c1 = (z + 1) * nch / a.ksplit;
+  const int K = a.K, nchK = K / C::KC;
+  const int c0 = (int)((long long)z * nchK / a.ksplit);
+  const int nch = (int)((long long)(z + 1) * nchK / a.ksplit) - c0;
+  const int T = a.tb[a.nseg];
+  const int Tg = T / G;
+  const int g0 = (int)((long long)blockIdx.x * Tg / gridDim.x);
+  const int ng = (int)((long long)(blockIdx.x + 1) * Tg / gridDim.x) - g0;
+  auto pass_begin = [&](int p) { return G * (g0 + p * ng / P); };  // first tile of pass p
+  const int nst = P * nch;
+  const size_t koff = (size_t)c0 * C::KC;
 
-  auto xidx = [](int m) { return m; };
-  auto xptr = [&](int m, int) -> const uint16_t* {
-    return m < a.M ? a.x + (size_t)bd_map_row(a.xr, m) * a.K : nullptr;
-  };
-  bd_f32x4 acc[C::MTW][C::NTP];
-  bd_stream::mainloop<C>(xidx, xptr, a.x, m0, a.w[seg], N, a.K, n0, sbuf, acc, c0 * C::KC, c1 - c0);
-
-  if (a.ksplit == 1) {
+  // DMA instruction f = wave + 4i loads rows 8*(f%2)..+7 of stage tile f/2:
+  // tiles 0..NTW-1 are W (per pass), the next MT are X (fixed).  Slots past
+  // the data read a valid row whose products are discarded.
+  const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
+  const uint16_t* const dummy = a.x + (size_t)bd_map_row(a.xr, 0) * K + koff + 8 * lkb;
+  const uint16_t* src[C::LW];
 #pragma unroll
-    for (int i = 0; i < C::MTW; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NTP; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
-          const int col = n0 + (wn * C::NTP + j) * 16 + l16;
-          if (m < a.M && col < N) gemm_store(a, seg, m, col, acc[i][j][r]);
-        }
-    return;
+  for (int i = 0; i < C::LW; ++i) {
+    const int f = wave + 4 * i, t = f >> 1;
+    const int m = m0 + (t - NTW) * 16 + 8 * (f & 1) + lrow;
+    src[i] = (f < C::FR && t >= NTW && m < a.M) ? a.x + (size_t)bd_map_row(a.xr, m) * K + koff + 8 * lkb : dummy;
   }
-  const int tile = blockIdx.y * gridDim.x + bx;
-  float* pt = a.part + ((size_t)tile * a.ksplit + z) * TILE;
+  auto set_pass = [&](int p) {  // W sources of pass p
+    const int b = pass_begin(p), n = pass_begin(p + 1) - b;
+#pragma unroll
+    for (int i = 0; i < C::LW; ++i) {
+      const int f = wave + 4 * i, t = f >> 1;
+      if (f < C::FR && t < NTW) {
+        const int r = 8 * (f & 1) + lrow;
+        const uint16_t* row = dummy;
+        if (t < n) {
+          const int gt = b + t;
+          if (a.mode == BD_GEMM_SWIGLU) {
+            int c = (gt >> 1) * 16 + r;
+            c = c < a.N[0] ? c : a.N[0] - 1;
+            row = a.w[0] + (size_t)((gt & 1) ? a.N[0] + c : c) * K + koff + 8 * lkb;
+          } else {
+            const int sg = seg_of(a, gt);
+            int c = (gt - a.tb[sg]) * 16 + r;
+            c = c < a.N[sg] ? c : a.N[sg] - 1;
+            row = a.w[sg] + (size_t)c * K + koff + 8 * lkb;
+          }
+        }
+        src[i] = row;
+      }
+    }
+  };
+  int ip = 0, ich = 0, iss = 0;  // issue cursor: pass, chunk, stages issued
+  set_pass(0);
+  auto issue_next = [&]() {
+    uint4* st = sbuf + (iss % C::NS) * C::STAGE_U4;
+#pragma unroll
+    for (int i = 0; i < C::LW; ++i)
+      if (C::FR % 4 == 0 || wave + 4 * i < C::FR)
+        __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ich * C::KC),
+                                         (bd_stream::lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, 0);
+    ++iss;
+    if (++ich == nch) {
+      ich = 0;
+      if (++ip < P) set_pass(ip);
+    }
+  };
+  const bool more = wave < C::FR % 4;  // this wave issues LW (else LW_LO) loads per stage
+  const int fo0 = bd_stream::frag_offset(lane, 0) / 16, fo1 = bd_stream::frag_offset(lane, 1) / 16;
+
+  bd_f32x4 acc[C::MTW][C::NTP];
 #pragma unroll
   for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NTP; ++j)
+    for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        pt[((wm * C::MTW + i) * 16 + 4 * g + r) * (kNTW * 16) + (wn * C::NTP + j) * 16 + l16] = acc[i][j][r];
+  for (int c = 0; c < C::NS - 1; ++c)
+    if (c < nst) issue_next();
+
+  int cp = 0, cch = 0;  // compute cursor: pass, chunk
+  for (int s = 0; s < nst; ++s) {
+    const int later = min(nst - s - 1, C::NS - 2);
+    if (later == 0) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+    else if (later == 1) {
+      if (more) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(C::LW));
+      else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(C::LW_LO));
+    } else if (later == 2) {
+      if (more) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(2 * C::LW));
+      else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(2 * C::LW_LO));
+    } else {
+      if (more) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(3 * C::LW));
+      else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(3 * C::LW_LO));
+    }
+    bd_stream::pipe_barrier();  // stage s is in LDS for every wave; the slot of s - 1 is free
+    if (s + C::NS - 1 < nst) issue_next();
+    // fragment reads as asm that waits inside the block (a plain LDS read
+    // would get a wait for every DMA in flight in front of it)
+    const uint32_t sb = bd_stream::lds_addr(sbuf + (s % C::NS) * C::STAGE_U4);
+#pragma unroll
+    for (int ks = 0; ks < C::KSC; ++ks) {
+      const uint32_t fo = (ks == 0 ? fo0 : fo1) * 16;
+      uint4 xa[C::MTW], wb[C::NTP];
+      bd_stream::lds_frags_kstep<C::MTW, C::NTP>(sb + (NTW + wm * C::MTW) * 2048 + fo,
+                                                 sb + wn * C::NTP * 2048 + fo, xa, wb);
+#pragma unroll
+      for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+    }
+    if (++cch < nch) continue;
+
+    // ---- end of pass cp: rows m0 + (wm*MTW + i)*16 + 4g + r, tile slots
+    // wn*NTP + j of the pass, column l16 of each
+    const int b = pass_begin(cp), n = pass_begin(cp + 1) - b;
+    if (a.mode == BD_GEMM_SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < C::NTP; j += 2) {
+        const int slot = wn * C::NTP + j;
+        const int col = ((b + slot) >> 1) * 16 + l16;
+        if (slot < n && col < a.N[0]) {
+#pragma unroll
+          for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+              if (m < a.M) {
+                const float zg = acc[i][j][r], u = acc[i][j + 1][r];
+                a.y[0][(size_t)bd_map_row(a.yr[0], m) * a.N[0] + col] =
+                    (uint16_t)bd_f2bf(zg / (1.f + __expf(-zg)) * u);
+              }
+            }
+        }
+      }
+    } else if (a.ksplit > 1) {
+      const size_t Nt = (size_t)T * 16;
+#pragma unroll
+      for (int j = 0; j < C::NTP; ++j) {
+        const int slot = wn * C::NTP + j;
+        if (slot < n) {
+          float* pz = a.part + (size_t)z * a.M * Nt + (size_t)(b + slot) * 16 + l16;
+#pragma unroll
+          for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+              if (m < a.M) pz[(size_t)m * Nt] = acc[i][j][r];
+            }
+        }
+      }
+    } else {
+      int sgj[C::NTP], colj[C::NTP];
+      bool okj[C::NTP];
+#pragma unroll
+      for (int j = 0; j < C::NTP; ++j) {
+        const int slot = wn * C::NTP + j;
+        const int gt = b + slot;
+        sgj[j] = seg_of(a, gt);
+        colj[j] = (gt - a.tb[sgj[j]]) * 16 + l16;
+        okj[j] = slot < n && colj[j] < a.N[sgj[j]];
+      }
+      // residual values first, all loads in flight together, then the stores
+      // (y may be res: a lane reads exactly the elements it writes)
+      float rv[C::MTW][C::NTP][4];
+#pragma unroll
+      for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+            const uint16_t* res = a.res[sgj[j]];
+            rv[i][j][r] = (okj[j] && m < a.M && res)
+                              ? bd_bf2f(res[(size_t)bd_map_row(a.rr[sgj[j]], m) * a.N[sgj[j]] + colj[j]])
+                              : 0.f;
+          }
+#pragma unroll
+      for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NTP; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
+            if (okj[j] && m < a.M)
+              a.y[sgj[j]][(size_t)bd_map_row(a.yr[sgj[j]], m) * a.N[sgj[j]] + colj[j]] =
+                  (uint16_t)bd_f2bf(acc[i][j][r] + rv[i][j][r]);
+          }
+    }
+#pragma unroll
+    for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+    cch = 0;
+    ++cp;
+  }
 }
 
-// Adds the K slices of every tile in slice order, then residual and store.
-template <int MT>
-__global__ __launch_bounds__(kThreads) void gemm_reduce_kernel(GemmK a) {
-  constexpr int kNTW = ntw_for(MT);
-  constexpr int TILE = MT * 16 * kNTW * 16;
-  const int bx = blockIdx.x;
-  const int seg = (a.nseg > 2 && bx >= a.wg_begin[2]) ? 2 : (a.nseg > 1 && bx >= a.wg_begin[1]) ? 1 : 0;
-  const int N = a.N[seg];
-  const int n0 = (bx - a.wg_begin[seg]) * kNTW * 16;
-  const int m0 = blockIdx.y * MT * 16;
-  const float* p0 = a.part + (size_t)(blockIdx.y * gridDim.x + bx) * a.ksplit * TILE;
-  // blockIdx.z: which 16-row group of the tile this work-group adds
-  for (int e = blockIdx.z * 16 * kNTW * 16 + threadIdx.x * 4; e < (blockIdx.z + 1) * 16 * kNTW * 16;
-       e += kThreads * 4) {
-    const int m = m0 + e / (kNTW * 16), col = n0 + e % (kNTW * 16);
-    if (m >= a.M) break;
-    float4 v = *reinterpret_cast<const float4*>(p0 + e);
-    for (int zz = 1; zz < a.ksplit; ++zz) {
-      const float4 w = *reinterpret_cast<const float4*>(p0 + (size_t)zz * TILE + e);
-      v.x += w.x;
-      v.y += w.y;
-      v.z += w.z;
-      v.w += w.w;
-    }
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (col + u < N) gemm_store(a, seg, m, col + u, vv[u]);
+// K-split reduction: y[m, col] = sum over slices of part[z][m][col] (+ res),
+// the slices added in order.  One thread per (row, 4 columns).  In a rotated
+// segment (BD_GEMM_ROPE, segments 0 and 1) the thread of columns j..j+3 in the
+// first half of a head also adds the partner columns j + d/2 .. and rotates
+// the pairs (position pos_base[m / n_rows] + pos_off + m % n_rows, angle
+// pos * theta^(-2j/d) in fp64, the rotation in fp32); the threads of the
+// second halves have nothing to do.
+__global__ __launch_bounds__(kThreads) void gemm_stream_reduce(GemmS a) {
+  const int T = a.tb[a.nseg];
+  const size_t Nt = (size_t)T * 16;
+  const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= (size_t)a.M * T * 4) return;
+  const int m = (int)(t / ((size_t)T * 4));
+  const int rem = (int)(t % ((size_t)T * 4));
+  const int gt = rem >> 2;
+  const int sg = seg_of(a, gt);
+  const int col = (gt - a.tb[sg]) * 16 + 4 * (rem & 3);
+  const int N = a.N[sg];
+  if (col >= N) return;
+  const bool rope = a.mode == BD_GEMM_ROPE && sg < 2;
+  const int half = a.d >> 1;
+  if (rope && col % a.d >= half) return;
+  const size_t zs = (size_t)a.M * Nt;
+  const float* p = a.part + (size_t)m * Nt + (size_t)gt * 16 + 4 * (rem & 3);
+  float lo[4], hi[4];
+  {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    lo[0] = v.x, lo[1] = v.y, lo[2] = v.z, lo[3] = v.w;
+    const float4 h = rope ? *reinterpret_cast<const float4*>(p + half) : make_float4(0.f, 0.f, 0.f, 0.f);
+    hi[0] = h.x, hi[1] = h.y, hi[2] = h.z, hi[3] = h.w;
   }
+  // slices in order; four slices' loads in flight at a time
+  int zz = 1;
+  for (; zz + 3 < a.ksplit; zz += 4) {
+    float4 v[4], h[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(p + (zz + u) * zs);
+    if (rope) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) h[u] = *reinterpret_cast<const float4*>(p + (zz + u) * zs + half);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lo[0] += v[u].x, lo[1] += v[u].y, lo[2] += v[u].z, lo[3] += v[u].w;
+      if (rope) hi[0] += h[u].x, hi[1] += h[u].y, hi[2] += h[u].z, hi[3] += h[u].w;
+    }
+  }
+  for (; zz < a.ksplit; ++zz) {
+    const float4 v = *reinterpret_cast<const float4*>(p + zz * zs);
+    lo[0] += v.x, lo[1] += v.y, lo[2] += v.z, lo[3] += v.w;
+    if (rope) {
+      const float4 h = *reinterpret_cast<const float4*>(p + zz * zs + half);
+      hi[0] += h.x, hi[1] += h.y, hi[2] += h.z, hi[3] += h.w;
+    }
+  }
+  uint16_t* yrow = a.y[sg] + (size_t)bd_map_row(a.yr[sg], m) * N;
+  if (rope) {
+    const int bq = m / a.n_rows, iq = m % a.n_rows;
+    const double pos = (double)(a.pos_base[bq] + a.pos_off + iq);
+    const int j0 = col % a.d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double ang = pos * exp2(-(2.0 * (j0 + e) / a.d) * a.log2_theta);
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      const float c = (float)cs, s = (float)sn;
+      const float x1 = lo[e], x2 = hi[e];
+      yrow[col + e] = (uint16_t)bd_f2bf(x1 * c - x2 * s);
+      yrow[col + half + e] = (uint16_t)bd_f2bf(x2 * c + x1 * s);
+    }
+    return;
+  }
+  if (a.res[sg]) {  // residual loads first, then the stores
+    const uint16_t* rrow = a.res[sg] + (size_t)bd_map_row(a.rr[sg], m) * N;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (col + e < N) lo[e] += bd_bf2f(rrow[col + e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (col + e < N) yrow[col + e] = (uint16_t)bd_f2bf(lo[e]);
 }
 
 struct GemmF {
@@ -157,7 +387,9 @@ struct GemmF {
   int N;
 };
 
-__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF a) {
+// fp32 projections: one thread per output element (small test shapes); in
+// SwiGLU mode the thread forms the gate and the up product of its column.
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF a, int swiglu) {
   const int n = blockIdx.x * kThreads + threadIdx.x;
   const int m = blockIdx.y;
   if (n >= a.N) return;
@@ -165,6 +397,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF a) {
   const float* wr = a.w + (size_t)n * a.K;
   float acc = 0.f;
   for (int k = 0; k < a.K; ++k) acc += xr[k] * wr[k];
+  if (swiglu) {
+    const float* ur = a.w + (size_t)(a.N + n) * a.K;
+    float up = 0.f;
+    for (int k = 0; k < a.K; ++k) up += xr[k] * ur[k];
+    acc = acc / (1.f + __expf(-acc)) * up;
+  }
   if (a.res) acc += a.res[(size_t)bd_map_row(a.rr, m) * a.N + n];
   a.y[(size_t)bd_map_row(a.yr, m) * a.N + n] = acc;
 }
@@ -217,74 +455,132 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(int D, int row_off, int
 
 }  // namespace
 
-BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg) {
-  BdGemmPlan p{};
-  if (dt == BD_F32) return p;
+BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int mode) {
+  BdGemmPlan best{};
+  if (dt == BD_F32 || M <= 0) return best;
   const int mt = (M + 15) / 16;
-  p.MT = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
-  const int kNTW = ntw_for(p.MT);
-  p.nx = 0;
-  for (int i = 0; i < nseg; ++i) p.nx += (N[i] + kNTW * 16 - 1) / (kNTW * 16);
-  p.ny = (M + p.MT * 16 - 1) / (p.MT * 16);
+  const int mt0 = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+  const int G = mode == BD_GEMM_SWIGLU ? 2 : 1;
+  int T = 0;
+  if (mode == BD_GEMM_SWIGLU)
+    T = 2 * ((N[0] + 15) / 16);
+  else
+    for (int i = 0; i < nseg; ++i) T += (N[i] + 15) / 16;
+  const int Tg = T / G;
   const int nch = K / 64;
-  const long base = (long)p.nx * p.ny;
-  int ks = (int)((kTargetWGs + base - 1) / base);
-  const int maxks = nch / kMinChunksPerSplit;
-  ks = ks > maxks ? maxks : ks;
-  p.ksplit = ks < 1 ? 1 : ks;
-  if (p.ksplit > 1) p.ws_bytes = (size_t)p.nx * p.ny * p.ksplit * p.MT * 16 * kNTW * 16 * sizeof(float);
-  return p;
+  int maxks = nch / BD_GEMM_MIN_CHUNKS;
+  if (maxks < 1 || mode == BD_GEMM_SWIGLU) maxks = 1;
+  double best_ns = -1;
+  // candidates: row tile (16 .. 64 rows, or 128 above 64 rows), K slices, and
+  // the number of passes per work-group (work-groups = units / pass size)
+  for (int MT = mt0; MT <= (mt > 4 && BD_GEMM_MAX_MT >= 8 ? 8 : mt0); MT *= 2) {
+    const int NTW = MT <= 2 ? 8 : 4;
+    const int ny = (M + MT * 16 - 1) / (MT * 16);
+    const int upp = NTW / G;  // units per pass
+    for (int ks = 1; ks <= maxks; ++ks) {
+      const int chunks = (nch + ks - 1) / ks;
+      for (int k = 1; k <= 64; ++k) {
+        const int nwg = (Tg + k * upp - 1) / (k * upp);
+        if (k > 1 && nwg == (Tg + (k - 1) * upp - 1) / ((k - 1) * upp)) continue;  // same split as k - 1
+        const long total = (long)nwg * ny * ks;
+        const int passes = ((Tg + nwg - 1) / nwg * G + NTW - 1) / NTW;
+        const double real = (double)T / ((double)nwg * passes);  // weight tiles per stage, on average
+        const double per_wg = real * 2048.0 / BD_GEMM_HBM_BPNS + (MT + NTW - real) * 2048.0 / BD_GEMM_L2_BPNS;
+        const double resident = (double)(total < BD_GEMM_SLOTS ? total : BD_GEMM_SLOTS);
+        double stage = resident * per_wg;
+        stage = stage > BD_GEMM_STAGE_NS ? stage : BD_GEMM_STAGE_NS;
+        const double waves = (double)((total + BD_GEMM_SLOTS - 1) / BD_GEMM_SLOTS);
+        double est = waves * passes * chunks * stage;
+        if (ks > 1)
+          est += BD_GEMM_RED_NS + (double)ks * M * T * 16 * 8 / BD_GEMM_PART_BPNS;
+        else if (mode == BD_GEMM_ROPE)
+          est += BD_GEMM_RED_NS;
+        if (best_ns < 0 || est < best_ns) {
+          best_ns = est;
+          best.MT = MT;
+          best.NTW = NTW;
+          best.ny = ny;
+          best.T = T;
+          best.G = G;
+          best.nwg = nwg;
+          best.passes = passes;
+          best.ksplit = ks;
+        }
+        if (nwg == 1) break;
+      }
+    }
+  }
+  best.ws_bytes = best.ksplit > 1 ? (size_t)best.ksplit * M * T * 16 * sizeof(float) : 0;
+  return best;
 }
 
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
-                          const BdGemmSeg* segs, int nseg, void* workspace, hipStream_t s) {
+                          const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope, void* workspace,
+                          hipStream_t s) {
   if (dt == BD_F32) {
     for (int i = 0; i < nseg; ++i) {
       GemmF a{static_cast<const float*>(x), xr, M, K, static_cast<const float*>(segs[i].w),
               static_cast<float*>(segs[i].y), static_cast<const float*>(segs[i].res), segs[i].yr, segs[i].rr,
               segs[i].N};
       hipLaunchKernelGGL(gemm_f32_kernel, dim3((segs[i].N + kThreads - 1) / kThreads, M), dim3(kThreads), 0, s,
-                         a);
+                         a, mode == BD_GEMM_SWIGLU ? 1 : 0);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    return hipSuccess;
+  } else {
+    GemmS a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.xr = xr;
+    a.M = M;
+    a.K = K;
+    a.nseg = nseg;
+    a.mode = mode;
+    int t = 0;
+    for (int i = 0; i < nseg; ++i) {
+      a.w[i] = static_cast<const uint16_t*>(segs[i].w);
+      a.y[i] = static_cast<uint16_t*>(segs[i].y);
+      a.res[i] = static_cast<const uint16_t*>(segs[i].res);
+      a.yr[i] = segs[i].yr;
+      a.rr[i] = segs[i].rr;
+      a.N[i] = segs[i].N;
+      a.tb[i] = t;
+      t += mode == BD_GEMM_SWIGLU ? 2 * ((segs[i].N + 15) / 16) : (segs[i].N + 15) / 16;
+    }
+    for (int i = nseg; i <= kMaxSeg; ++i) a.tb[i] = t;
+    a.ksplit = p.ksplit;
+    a.part = p.ksplit > 1 ? static_cast<float*>(workspace) : nullptr;
+    if (mode == BD_GEMM_ROPE) {
+      a.pos_base = rope->pos_base;
+      a.n_rows = rope->n_rows;
+      a.pos_off = rope->pos_off;
+      a.d = rope->d;
+      a.log2_theta = std::log2((double)rope->theta);
+    }
+    const dim3 grid(p.nwg, p.ny, p.ksplit);
+    switch (p.MT) {
+      case 1: hipLaunchKernelGGL((gemm_stream_kernel<1, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+      case 2: hipLaunchKernelGGL((gemm_stream_kernel<2, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+      case 4: hipLaunchKernelGGL((gemm_stream_kernel<4, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+      default: hipLaunchKernelGGL((gemm_stream_kernel<8, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.ksplit > 1) {
+      const size_t n = (size_t)M * p.T * 4;
+      hipLaunchKernelGGL(gemm_stream_reduce, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                         a);
+      return hipGetLastError();
+    }
   }
-  GemmK a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.xr = xr;
-  a.M = M;
-  a.K = K;
-  a.nseg = nseg;
-  int wg = 0;
-  for (int i = 0; i < nseg; ++i) {
-    a.w[i] = static_cast<const uint16_t*>(segs[i].w);
-    a.y[i] = static_cast<uint16_t*>(segs[i].y);
-    a.res[i] = static_cast<const uint16_t*>(segs[i].res);
-    a.yr[i] = segs[i].yr;
-    a.rr[i] = segs[i].rr;
-    a.N[i] = segs[i].N;
-    a.wg_begin[i] = wg;
-    wg += (segs[i].N + ntw_for(p.MT) * 16 - 1) / (ntw_for(p.MT) * 16);
+  // rotary embedding as its own pass where the projection had no reduction
+  if (mode == BD_GEMM_ROPE && (dt == BD_F32 || p.ksplit == 1)) {
+    for (int i = 0; i < 2 && i < nseg; ++i) {
+      hipError_t e = bd_rope_launch(dt, M / rope->n_rows, rope->n_rows, segs[i].N / rope->d, rope->d, segs[i].y,
+                                    segs[i].yr, rope->pos_base, rope->pos_off, rope->theta, s);
+      if (e != hipSuccess) return e;
+    }
   }
-  for (int i = nseg; i <= kMaxSeg; ++i) a.wg_begin[i] = wg;
-  a.ksplit = p.ksplit;
-  a.part = p.ksplit > 1 ? static_cast<float*>(workspace) : nullptr;
-  const dim3 grid(wg, p.ny, p.ksplit);
-  switch (p.MT) {
-    case 1: hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(gemm_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.ksplit == 1) return e;
-  const dim3 rgrid(wg, p.ny, p.MT);
-  switch (p.MT) {
-    case 1: hipLaunchKernelGGL(gemm_reduce_kernel<1>, rgrid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(gemm_reduce_kernel<2>, rgrid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(gemm_reduce_kernel<4>, rgrid, dim3(kThreads), 0, s, a); break;
-  }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V, const void* E,

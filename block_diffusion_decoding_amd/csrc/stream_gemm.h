@@ -2,7 +2,7 @@
 // for a handful of rows m (the fresh block rows of a refinement step) and a
 // long weight matrix W [N, K] that is read exactly once from HBM.
 //
-// A work-group (4 waves) owns MT*16 rows (MT in {1, 2, 4}) and NTW*16
+// A work-group (4 waves) owns MT*16 rows (MT in {1, 2, 4, 8}) and NTW*16
 // columns.  K is walked in chunks of 64; every chunk is one pipeline stage in
 // LDS holding the NTW column tiles of W and the MT row tiles of X, each tile
 // 16 rows x 64 k = 2 KiB.  The tiles arrive by global->LDS DMA
@@ -66,7 +66,7 @@ struct Cfg {
   static constexpr int LW_LO = FR / 4;       // waves >= FR % 4 issue one fewer
   static constexpr int STAGE_U4 = FR * 64;
   static constexpr int LDS_BYTES = NS * STAGE_U4 * 16;
-  static_assert(MT == 1 || MT == 2 || MT == 4, "MT");
+  static_assert(MT == 1 || MT == 2 || MT == 4 || MT == 8, "MT");
   static_assert(NTW % WN == 0, "split");
   static_assert(NS >= 2 && NS <= 5, "stages");
 };
@@ -187,109 +187,6 @@ __device__ __forceinline__ void lds_frags_kstep<1, 2>(uint32_t xa, uint32_t wa, 
 __device__ __forceinline__ int frag_offset(int lane, int ks) {
   const int r = lane & 15, r7 = r & 7;
   return (r >> 3) * 1024 + (r7 * 8 + ((4 * ks + (lane >> 4)) ^ r7)) * 16;
-}
-
-// Rows of X: xidx(m) gives the source row index of row m (it may load it
-// from a row list, so it must accept any m of the work-group's row tiles),
-// xptr(m, idx) the row (K elements) or nullptr for a row that does not exist;
-// such rows read row `xdummy` instead and their outputs are never used.  All
-// xidx calls of a wave are made before any xptr call, so row-index loads are
-// in flight together.  Columns >= N read row 0 of W likewise.
-// K range: elements [k0, k0 + nch*KC) of rows of length K.
-// Output: acc[i][j] holds rows m0 + (wm*MTW + i)*16 + 4*(lane/16) + r (r = the
-// vector element) and columns n0 + (wn*NTP + j)*16 + lane%16, with
-// wm = wave % WM and wn = wave / WM.
-template <class C, class XIdxF, class XPtrF>
-__device__ __forceinline__ void mainloop(const XIdxF& xidx, const XPtrF& xptr, const uint16_t* xdummy, int m0,
-                                         const uint16_t* __restrict__ W, int N, int K, int n0, uint4* sbuf,
-                                         bd_f32x4 (&acc)[C::MTW][C::NTP], int k0 = 0, int nch = -1) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave % C::WM;
-  const int wn = wave / C::WM;
-  if (nch < 0) nch = K / C::KC;
-
-#pragma unroll
-  for (int i = 0; i < C::MTW; ++i)
-#pragma unroll
-    for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // per-lane source pointers of this wave's DMA instructions (chunk 0):
-  // instruction f loads rows 8*(f%2) .. +7 of tile f/2
-  const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
-  int xm[C::LW], xi[C::LW];
-#pragma unroll
-  for (int i = 0; i < C::LW; ++i) {
-    const int f = wave + 4 * i;
-    const int t = f >> 1, r = 8 * (f & 1) + lrow;
-    xm[i] = m0 + (t - C::NTW) * 16 + r;
-    xi[i] = (f < C::FR && t >= C::NTW) ? xidx(xm[i]) : 0;
-  }
-  const uint16_t* src[C::LW];
-#pragma unroll
-  for (int i = 0; i < C::LW; ++i) {
-    const int f = wave + 4 * i;
-    const int t = f >> 1, r = 8 * (f & 1) + lrow;
-    if (f >= C::FR) {
-      src[i] = nullptr;
-    } else if (t < C::NTW) {
-      const int col = n0 + t * 16 + r;
-      src[i] = W + (size_t)(col < N ? col : 0) * K + k0 + 8 * lkb;
-    } else {
-      const uint16_t* p = xptr(xm[i], xi[i]);
-      src[i] = (p ? p : xdummy) + k0 + 8 * lkb;
-    }
-  }
-  auto issue = [&](int ch) {
-    uint4* st = sbuf + (ch % C::NS) * C::STAGE_U4;
-#pragma unroll
-    for (int i = 0; i < C::LW; ++i)
-      if (C::FR % 4 == 0 || wave + 4 * i < C::FR)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(src[i] + (size_t)ch * C::KC),
-                                         (lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, 0);
-  };
-  const bool more = wave < C::FR % 4;  // this wave issues LW (else LW_LO) loads per stage
-  const int fo0 = frag_offset(lane, 0) / 16, fo1 = frag_offset(lane, 1) / 16;
-
-#pragma unroll
-  for (int c = 0; c < C::NS - 1; ++c)
-    if (c < nch) issue(c);
-
-  for (int ch = 0; ch < nch; ++ch) {
-    // chunks issued so far: min(nch, ch + NS - 1); keep the later ones in flight
-    const int later = min(nch - ch - 1, C::NS - 2);
-    if (later == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    else if (later == 1) {
-      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LW));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::LW_LO));
-    } else if (later == 2) {
-      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::LW));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * C::LW_LO));
-    } else {
-      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * C::LW));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * C::LW_LO));
-    }
-    pipe_barrier();  // chunk ch is in LDS for every wave; slot of ch - 1 is free
-    if (ch + C::NS - 1 < nch) issue(ch + C::NS - 1);
-    const uint4* st = sbuf + (ch % C::NS) * C::STAGE_U4;
-    uint4 xa[C::KSC][C::MTW], wb[C::KSC][C::NTP];
-#pragma unroll
-    for (int ks = 0; ks < C::KSC; ++ks) {
-      const int fo = ks == 0 ? fo0 : fo1;
-#pragma unroll
-      for (int i = 0; i < C::MTW; ++i) xa[ks][i] = st[(C::NTW + wm * C::MTW + i) * 128 + fo];
-#pragma unroll
-      for (int j = 0; j < C::NTP; ++j) wb[ks][j] = st[(wn * C::NTP + j) * 128 + fo];
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::KSC; ++ks)
-#pragma unroll
-      for (int i = 0; i < C::MTW; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_mfma16(xa[ks][i], wb[ks][j], acc[i][j]);
-  }
-  __syncthreads();  // stages may be reused by the caller's epilogue
 }
 
 }  // namespace bd_stream

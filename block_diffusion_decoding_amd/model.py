@@ -66,33 +66,31 @@ class ModelDecoder(BlockDecoder):
         self.blk_k = torch.zeros(Lr, B, D, Hkv, d, dtype=dt, device=dev)
         self.blk_v = torch.zeros_like(self.blk_k)
         self.hbuf = torch.zeros(B * D, hid, dtype=dt, device=dev)
-        self.gu = torch.zeros(B * D, 2 * I, dtype=dt, device=dev)
         self.act = torch.zeros(B * D, I, dtype=dt, device=dev)
 
     # ------------------------------------------------------------------ layers
-    def _layers(self, X, h, q, o, gu, a, M, n, lo, kr, attn_kv, layer_ids):
+    def _layers(self, X, h, q, o, a, M, n, lo, kr, attn_kv, layer_ids):
         """Layers ``layer_ids`` over M = B*n fresh rows X (block rows
-        lo .. lo+n-1 of every sequence).  attn_kv(l) gives layer l's
-        (k_cache, v_cache, kv_len, k_blk, v_blk); the fresh K/V go to rows kr
-        of k_blk/v_blk, rotated at positions kv_len[b] + lo + i."""
+        lo .. lo+n-1 of every sequence), the residual stream, updated in
+        place.  attn_kv(l) gives layer l's (k_cache, v_cache, kv_len, k_blk,
+        v_blk); the fresh K/V go to rows kr of k_blk/v_blk, rotated at
+        positions kv_len[b] + lo + i."""
         dm = self.dims
         for l in layer_ids:
             lw = self.layers[l]
             kc, vc, kvl, kb, vb = attn_kv(l)
             ops.bd_rmsnorm(X, dense(M), h, dense(M), M=M, eps=dm.eps)
-            ops.bd_qkv_proj(h, dense(M), lw["Wq"], q, dense(M), lw["Wk"], lw["Wv"], kb, kr, vb, kr, M=M)
-            ops.bd_rope(q, dense(M), kvl, n_rows=n, H=dm.Hq, d=dm.d, pos_off=lo, theta=dm.theta)
-            ops.bd_rope(kb, kr, kvl, n_rows=n, H=dm.Hkv, d=dm.d, pos_off=lo, theta=dm.theta)
+            ops.bd_qkv_proj_rope(h, dense(M), lw["Wq"], q, dense(M), lw["Wk"], lw["Wv"], kb, kr, vb, kr, kvl, M=M,
+                                 d=dm.d, n_rows=n, pos_off=lo, theta=dm.theta)
             ops.bd_block_attn(q, kc, vc, kvl, kb, vb, o, D=dm.D, q_off=lo)
             ops.bd_linear(o, dense(M), lw["Wo"], X, dense(M), M=M, res=X, rr=dense(M))
             ops.bd_rmsnorm(X, dense(M), h, dense(M), M=M, eps=dm.eps)
-            ops.bd_linear(h, dense(M), lw["Wgu"], gu, dense(M), M=M)
-            ops.bd_swiglu(gu, dense(M), a, dense(M), M=M, inter=dm.inter)
+            ops.bd_gate_up_swiglu(h, dense(M), lw["Wgu"], a, dense(M), M=M)
             ops.bd_linear(a, dense(M), lw["Wd"], X, dense(M), M=M, res=X, rr=dense(M))
 
     def _forward_block_rows(self, lo: int, n: int):
-        """Block rows [lo, lo + n) of every sequence through all layers; the
-        final normalised rows land in H rows 1 + lo .. lo + n."""
+        """Block rows [lo, lo + n) of every sequence through all layers;
+        returns the residual stream X [B, n, hidden] after the last layer."""
         dm = self.dims
         B, D = dm.B, dm.D
         M = B * n
@@ -100,7 +98,7 @@ class ModelDecoder(BlockDecoder):
         q = self.q.view(-1)[: M * dm.Hq * dm.d].view(B, n, dm.Hq, dm.d)
         o = self.o.view(-1)[: M * dm.Hq * dm.d].view(B, n, dm.Hq, dm.d)
         ops.bd_embed_rows(self.W["E"], self.tokens, self.mask_bits, X, row_off=lo, n_rows=n)
-        self._layers(X, self.hbuf, q, o, self.gu, self.act, M, n, lo, rows(n, D, lo),
+        self._layers(X, self.hbuf, q, o, self.act, M, n, lo, rows(n, D, lo),
                      lambda l: (self.cache_k[l], self.cache_v[l], self.kv_len[l], self.blk_k[l], self.blk_v[l]),
                      range(dm.n_layers))
         return X
@@ -156,7 +154,6 @@ class ModelDecoder(BlockDecoder):
         h = torch.empty(M, dm.hidden, dtype=dt, device=dev)
         q = torch.empty(B, P, dm.Hq, dm.d, dtype=dt, device=dev)
         o = torch.empty_like(q)
-        gu = torch.empty(M, 2 * dm.inter, dtype=dt, device=dev)
         a = torch.empty(M, dm.inter, dtype=dt, device=dev)
         pk = torch.empty(B, P, dm.Hkv, dm.d, dtype=dt, device=dev)
         pv = torch.empty_like(pk)
@@ -165,7 +162,7 @@ class ModelDecoder(BlockDecoder):
         # one K/V buffer serves every layer: layer l's rows are appended to
         # its cache (and its length moves to P) before layer l + 1 writes them
         for l in range(dm.n_layers):
-            self._layers(X, h, q, o, gu, a, M, P, 0, dense(M),
+            self._layers(X, h, q, o, a, M, P, 0, dense(M),
                          lambda l: (self.cache_k[l], self.cache_v[l], self.kv_len[l], pk, pv), (l,))
             ops.bd_kv_append(self.cache_k[l], self.cache_v[l], self.kv_len[l], pk, pv, n_rows=P)
         ops.bd_rmsnorm(X, rows(1, P, P - 1), self.H, rows(1, 1 + D, 0), M=B, eps=dm.eps)
@@ -176,9 +173,9 @@ class ModelDecoder(BlockDecoder):
         dm = self.dims
         B, D, dt = dm.B, dm.D, self.dtype
         Ms = (B * S, B * D)
-        gemm = [ops.bd_qkv_proj_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d, dm.Hkv * dm.d) for M in Ms]
+        gemm = [ops.bd_qkv_proj_rope_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d, dm.Hkv * dm.d) for M in Ms]
         gemm += [ops.bd_linear_workspace_size(dt, M, N, K) for M in Ms
-                 for N, K in ((dm.hidden, dm.Hq * dm.d), (2 * dm.inter, dm.hidden), (dm.hidden, dm.inter))]
+                 for N, K in ((dm.hidden, dm.Hq * dm.d), (dm.hidden, dm.inter))]
         return {"attn": max(ops.bd_block_attn_workspace_size(dt, B, dm.Hq, dm.Hkv, dm.d, n, dm.cap, D) for n in (S, D)),
                 "lm": ops.bd_lmhead_workspace_size(dt, B * S, dm.hidden, dm.V),
                 "gemm": max(gemm)}

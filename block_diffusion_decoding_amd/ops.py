@@ -214,6 +214,35 @@ def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, ws=None, stream=No
     _check("bd_qkv_proj", st)
 
 
+def bd_qkv_proj_rope_workspace_size(dtype, M, K, Nq, Nkv) -> int:
+    return int(_lib.load().bd_qkv_proj_rope_workspace_size(_DT[dtype], M, K, Nq, Nkv))
+
+
+def bd_qkv_proj_rope(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, pos_base, *, M, d, n_rows, pos_off=0, theta,
+                     ws=None, stream=None):
+    """bd_qkv_proj, then q and k rotated at positions pos_base[m // n_rows] +
+    pos_off + m % n_rows (heads of d elements)."""
+    lib = _lib.load()
+    Nq, K = wq.shape
+    Nkv = wk.shape[0]
+    dt = _dt(wq)
+    if ws is None:
+        ws = workspace(lib.bd_qkv_proj_rope_workspace_size(dt, M, K, Nq, Nkv), wq.device, "gemm")
+    st = lib.bd_qkv_proj_rope(dt, M, K, _p(x), xr, _p(wq), Nq, _p(q), qr, _p(wk), _p(wv), Nkv, _p(k), kr, _p(v),
+                              vr, int(d), _p(pos_base), int(n_rows), int(pos_off), float(theta), _p(ws), ws.numel(),
+                              _stream(stream))
+    _check("bd_qkv_proj_rope", st)
+
+
+def bd_gate_up_swiglu(x, xr, w_gu, a, ar, *, M, stream=None):
+    """a[ar(m)] = silu(x[xr(m)] Wg^T) * (x[xr(m)] Wu^T) with w_gu = [Wg; Wu]
+    ([2*inter, K])."""
+    inter2, K = w_gu.shape
+    st = _lib.load().bd_gate_up_swiglu(_dt(w_gu), M, K, _p(x), xr, _p(w_gu), inter2 // 2, _p(a), ar,
+                                       _stream(stream))
+    _check("bd_gate_up_swiglu", st)
+
+
 def bd_rmsnorm(x, xr, y, yr, *, M, eps, stream=None):
     """y[yr(m)] = rmsnorm(x[xr(m)]) (unit gains); rows of x.shape[-1] elements."""
     st = _lib.load().bd_rmsnorm(_dt(x), M, x.shape[-1], _p(x), xr, float(eps), _p(y), yr, _stream(stream))

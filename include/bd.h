@@ -247,7 +247,8 @@ bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int 
  * K % 256 == 0; when the column tiles alone cannot fill the GPU, K is split
  * over work-groups and the slices are added in a fixed order through the
  * workspace (bd_linear_workspace_size; 0 means none is needed) by a second
- * kernel of the same call. */
+ * kernel of the same call.  y may be res (same rows): each element is read
+ * before it is written. */
 size_t bd_linear_workspace_size(bd_dtype dt, int M, int N, int K);
 bd_status bd_linear(bd_dtype dt, int M, int N, int K,
                     const void* x, bd_rows xr, const void* w,
@@ -263,6 +264,29 @@ bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
                       const void* wk, const void* wv, int Nkv,
                       void* k, bd_rows kr, void* v, bd_rows vr,
                       void* workspace, size_t ws_bytes, void* stream);
+
+/* bd_qkv_proj followed by the rotary embedding of q and k (as bd_rope, with
+ * H = Nq/d resp. Nkv/d heads; logical row m = b*n_rows + i sits at position
+ * pos_base[b] + pos_off + i), in the same call: where K is split the rotation
+ * is applied by the reduction kernel to the fp32 sums, otherwise by a rotary
+ * pass over q and k.  d % 8 == 0, Nq and Nkv multiples of d, M a multiple of
+ * n_rows, theta > 1.  Workspace: bd_qkv_proj_rope_workspace_size. */
+size_t bd_qkv_proj_rope_workspace_size(bd_dtype dt, int M, int K, int Nq, int Nkv);
+bd_status bd_qkv_proj_rope(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
+                           const void* wq, int Nq, void* q, bd_rows qr,
+                           const void* wk, const void* wv, int Nkv,
+                           void* k, bd_rows kr, void* v, bd_rows vr,
+                           int d, const int32_t* pos_base, int n_rows, int pos_off, float theta,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Gate/up projection of a SwiGLU MLP with the gate applied in the epilogue:
+ *   a[ar(m), n] = silu(x[xr(m)] . w_gu[n]) * (x[xr(m)] . w_gu[inter + n])
+ * for m < M, n < inter; w_gu [2*inter, K] holds the gate rows, then the up
+ * rows; silu(z) = z / (1 + exp(-z)) in fp32 on the fp32 sums.  The gate and
+ * up tile of the same columns are computed by one wave, so the [M, 2*inter]
+ * projection is never stored.  No workspace. */
+bd_status bd_gate_up_swiglu(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* w_gu, int inter,
+                            void* a, bd_rows ar, void* stream);
 
 /* ------------------------------------------------------------------------
  * Layer pieces of the multi-layer decode (support calls).  The pages name the

@@ -29,7 +29,8 @@ def test_header_declares_the_four_calls_and_support():
     for n in ["bd_block_attn", "bd_lmhead_confidence", "bd_threshold_unmask", "bd_kv_append",
               "bd_embed_rows", "bd_linear", "bd_qkv_proj", "bd_block_attn_workspace_size",
               "bd_linear_workspace_size", "bd_qkv_proj_workspace_size",
-              "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version"]:
+              "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
+              "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu"]:
         assert n in names
 
 
@@ -134,10 +135,13 @@ def test_gemm_and_embed_argument_errors():
                          FAKE, big, None) == U                         # K % 256
     assert lib.bd_linear(1, 0, 3584, 3584, FAKE, R(1, 1, 0), FAKE, None, R(1, 1, 0), FAKE, R(1, 1, 0),
                          None, 0, None) == 0
-    need = lib.bd_qkv_proj_workspace_size(1, 64, 3584, 3584, 512)
-    assert need > 0                                                    # the 7B projections split K
-    assert lib.bd_qkv_proj(1, 64, 3584, FAKE, R(64, 64, 0), FAKE, 3584, FAKE, R(64, 64, 0), FAKE, FAKE, 512,
+    need = lib.bd_qkv_proj_workspace_size(1, 64, 8960, 1536, 256)
+    assert need > 0                                                    # a long K with few columns splits K
+    assert lib.bd_qkv_proj(1, 64, 8960, FAKE, R(64, 64, 0), FAKE, 1536, FAKE, R(64, 64, 0), FAKE, FAKE, 256,
                            FAKE, R(8, 32, 8), FAKE, R(8, 32, 8), FAKE, need - 16, None) == E
+    # the split writes one fp32 partial sum per slice, row and 16-column tile column
+    assert need % (64 * (1536 + 2 * 256) * 4) == 0
+    assert lib.bd_linear_workspace_size(1, 128, 17920, 1536) == 0     # enough column tiles: no split
     assert lib.bd_linear_workspace_size(0, 64, 3584, 3584) == 0       # fp32: no workspace
     assert lib.bd_embed_rows(1, 1, 65, 0, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
     assert lib.bd_embed_rows(1, 1, 32, 30, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
@@ -188,3 +192,23 @@ def test_layer_piece_argument_errors():
     assert lib.bd_swiglu(1, 3, 0, FAKE, d1, FAKE, d1, None) == E
     assert lib.bd_swiglu(1, 3, 8960, FAKE, d1, None, d1, None) == E
     assert lib.bd_swiglu(1, 3, 8960, FAKE, bad, FAKE, d1, None) == E
+
+
+def test_fused_layer_call_argument_errors():
+    """The fused projections check their shapes before any launch."""
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    d1 = _lib.BdRows(1, 1, 0)
+    big = 1 << 30
+    rope = lambda **k: lib.bd_qkv_proj_rope(1, k.get("M", 128), 1536, FAKE, d1, FAKE, k.get("Nq", 1536), FAKE, d1,
+                                            FAKE, FAKE, 256, FAKE, d1, FAKE, d1, k.get("d", 128),
+                                            k.get("pos", FAKE), k.get("n", 8), k.get("off", 0), k.get("theta", 1e6),
+                                            FAKE, big, None)
+    assert rope(d=100) == E          # d % 8
+    assert rope(Nq=1500) == E        # Nq % d
+    assert rope(M=100) == E          # M % n_rows
+    assert rope(pos=None) == E and rope(off=-1) == E and rope(theta=0.5) == E and rope(n=0) == E
+    assert lib.bd_qkv_proj_rope_workspace_size(1, 128, 1536, 1536, 256) > 0   # rotation in the reduction
+    assert lib.bd_gate_up_swiglu(1, 128, 1000, FAKE, d1, FAKE, 8960, FAKE, d1, None) == _lib.BD_EUNSUPPORTED
+    assert lib.bd_gate_up_swiglu(1, 128, 1536, FAKE, d1, None, 8960, FAKE, d1, None) == E
+    assert lib.bd_gate_up_swiglu(1, 0, 1536, FAKE, d1, FAKE, 8960, FAKE, d1, None) == 0

@@ -277,7 +277,7 @@ def test_projection_workspace_shared_by_different_tilings():
     need = max(o._lib.load().bd_qkv_proj_workspace_size(1, M, K, 3584, 512) for M in (8, 64, 256)) + \
         max(o._lib.load().bd_linear_workspace_size(1, M, 3584, K) for M in (8, 64, 256))
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
-    for it, M in enumerate([256, 64, 256, 8, 64, 256, 64]):
+    for it, M in enumerate([256, 64, 256, 8, 64, 100, 256, 64]):
         x = bi.normal(100 + it, "h", (M, K), 0.5, "bf16")
         gx = up(x, T)
         q = torch.zeros(M, 3584, dtype=T, device=DEV)
@@ -292,3 +292,30 @@ def test_projection_workspace_shared_by_different_tilings():
         rows_close(down(k), xf @ wk.astype(np.float64).T, TOL["bf16"], f"k M={M} call {it}")
         rows_close(down(v), xf @ wv.astype(np.float64).T, TOL["bf16"], f"v M={M} call {it}")
         rows_close(down(y), xf + xf @ wo.astype(np.float64).T, TOL["bf16"], f"o M={M} call {it}")
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 1536, 1536), (32, 2048, 512), (50, 1536, 8960), (128, 1536, 8960),
+                                   (100, 17920, 256), (512, 8192, 512), (512, 1536, 1536), (16, 1000, 512)])
+def test_linear_in_place_residual_tilings(M, N, K):
+    """y = x W^T + y in place through row maps, for row counts that take
+    every row tile (16 .. 128 rows, ragged tails) with and without a K split:
+    the residual rows are read before the same rows are written."""
+    say(f"[support] linear M{M} N{N} K{K}")
+    o = ops()
+    T = torch.bfloat16
+    x = bi.normal(7, "h", (M, K), 0.5, "bf16")
+    w = bi.normal(7, "Wo", (N, K), 0.02, "bf16")
+    r = bi.normal(8, "h", (M, N), 0.5, "bf16")
+    # rows of y live at buffer rows 2 + 3*(m // 5) ... (groups of 5, stride 7)
+    G = (M + 4) // 5
+    buf = torch.zeros(G * 7 + 2, N, dtype=T, device=DEV)
+    idx = np.array([(m // 5) * 7 + 2 + m % 5 for m in range(M)])
+    buf[torch.from_numpy(idx).to(DEV)] = up(r, T)
+    yr = o.rows(5, 7, 2)
+    o.bd_linear(up(x, T), o.dense(M), up(w, T), buf, yr, M=M, res=buf, rr=yr)
+    torch.cuda.synchronize()
+    got = down(buf)
+    ref = r.astype(np.float64) + x.astype(np.float64) @ w.astype(np.float64).T
+    rows_close(got[idx], ref, TOL["bf16"], f"linear M{M}")
+    untouched = np.setdiff1d(np.arange(buf.shape[0]), idx)
+    assert not got[untouched].any()

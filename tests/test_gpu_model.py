@@ -35,7 +35,7 @@ def test_rmsnorm_rows_and_in_place(dtype):
     rows_close(down(xt), OM.rmsnorm(x.astype(np.float64), 1e-6), TOL[dtype], "rmsnorm in place")
 
 
-@pytest.mark.parametrize("dtype,H,d", [("f32", 4, 64), ("bf16", 12, 128), ("bf16", 2, 128)])
+@pytest.mark.parametrize("dtype,H,d", [("f32", 4, 64), ("bf16", 12, 128), ("bf16", 2, 128), ("bf16", 7, 64)])
 def test_rope_positions_from_lengths(dtype, H, d):
     say(f"[model] rope {dtype} H{H} d{d}")
     o = ops()
@@ -65,6 +65,77 @@ def test_swiglu(dtype):
     g64 = gu.astype(np.float64)
     ref = OM.silu(g64[:, :I]) * g64[:, I:]
     rows_close(down(a), ref, TOL[dtype], "swiglu")
+
+
+@pytest.mark.parametrize("dtype,hidden,inter", [("bf16", 4100, 1001), ("f32", 12, 6), ("bf16", 8200, 8)])
+def test_row_ops_at_widths_off_the_vector_path(dtype, hidden, inter):
+    """Widths that are not whole 16-byte vectors, or rows longer than the
+    one-pass register budget, take the general loops: same results."""
+    say(f"[model] row ops {dtype} hidden {hidden} inter {inter}")
+    o = ops()
+    M = 9
+    x = bi.normal(4, "x", (M, hidden), 0.7, dtype)
+    y = torch.zeros(M, hidden, dtype=tdt(dtype), device=DEV)
+    o.bd_rmsnorm(up(x, tdt(dtype)), o.dense(M), y, o.dense(M), M=M, eps=1e-6)
+    rows_close(down(y), OM.rmsnorm(x.astype(np.float64), 1e-6), TOL[dtype], "rmsnorm")
+    gu = bi.normal(5, "x", (M, 2 * inter), 2.0, dtype)
+    a = torch.zeros(M, inter, dtype=tdt(dtype), device=DEV)
+    o.bd_swiglu(up(gu, tdt(dtype)), o.dense(M), a, o.dense(M), M=M, inter=inter)
+    g64 = gu.astype(np.float64)
+    rows_close(down(a), OM.silu(g64[:, :inter]) * g64[:, inter:], TOL[dtype], "swiglu")
+
+
+@pytest.mark.parametrize("dtype,B,n,Hq,Hkv,d,K", [("bf16", 16, 8, 12, 2, 128, 1536), ("bf16", 3, 8, 4, 2, 64, 512),
+                                                  ("bf16", 2, 4, 4, 2, 64, 256), ("f32", 3, 8, 4, 2, 64, 256),
+                                                  ("bf16", 16, 32, 12, 2, 128, 1536)])
+def test_qkv_proj_rope_matches_projection_then_rotation(dtype, B, n, Hq, Hkv, d, K):
+    """q and k rotated at their absolute positions, v plain; the K-split path
+    rotates in the reduction, the others in a rotary pass."""
+    say(f"[model] qkv+rope {dtype} B{B} n{n} Hq{Hq} Hkv{Hkv} d{d} K{K}")
+    o = ops()
+    T = tdt(dtype)
+    M = B * n
+    D = 32
+    x = bi.normal(13, "x", (M, K), 0.5, dtype)
+    wq = bi.normal(13, "mWq", (Hq * d, K), 0.05, dtype)
+    wk = bi.normal(13, "mWk", (Hkv * d, K), 0.05, dtype)
+    wv = bi.normal(13, "mWv", (Hkv * d, K), 0.05, dtype)
+    lens = (np.arange(B, dtype=np.int32) * 97) % 2048
+    lo = D - n if n < D else 0
+    q = torch.zeros(M, Hq * d, dtype=T, device=DEV)
+    kb = torch.zeros(B, D, Hkv * d, dtype=T, device=DEV)
+    vb = torch.zeros_like(kb)
+    kr = o.rows(n, D, lo)
+    o.bd_qkv_proj_rope(up(x, T), o.dense(M), up(wq, T), q, o.dense(M), up(wk, T), up(wv, T), kb, kr, vb, kr,
+                       up(lens), M=M, d=d, n_rows=n, pos_off=lo, theta=1e6)
+    x64 = x.astype(np.float64)
+    pos = (lens[:, None] + lo + np.arange(n)[None, :]).reshape(-1)
+    Q = OM.rope((x64 @ wq.astype(np.float64).T).reshape(M, Hq, d), pos, 1e6)
+    Kr = OM.rope((x64 @ wk.astype(np.float64).T).reshape(M, Hkv, d), pos, 1e6)
+    V = x64 @ wv.astype(np.float64).T
+    rows_close(down(q).reshape(M * Hq, d), Q.reshape(M * Hq, d), TOL[dtype], "q")
+    rows_close(down(kb)[:, lo:lo + n].reshape(M * Hkv, d), Kr.reshape(M * Hkv, d), TOL[dtype], "k")
+    rows_close(down(vb)[:, lo:lo + n].reshape(M, -1), V, TOL[dtype], "v")
+    if n < D:
+        assert not kb[:, :lo].any() and not vb[:, :lo].any()
+
+
+@pytest.mark.parametrize("dtype,M,K,inter", [("bf16", 128, 1536, 8960), ("bf16", 5, 512, 1000),
+                                             ("bf16", 37, 256, 520), ("bf16", 300, 512, 256),
+                                             ("f32", 9, 256, 100)])
+def test_gate_up_swiglu_matches_projections_then_gate(dtype, M, K, inter):
+    say(f"[model] gate/up+swiglu {dtype} M{M} K{K} inter{inter}")
+    o = ops()
+    T = tdt(dtype)
+    x = bi.normal(14, "x", (M, K), 0.5, dtype)
+    w = bi.normal(14, "mWg", (2 * inter, K), 0.05, dtype)
+    a = torch.zeros(M + 3, inter, dtype=T, device=DEV)
+    o.bd_gate_up_swiglu(up(x, T), o.dense(M), up(w, T), a, o.rows(M, M + 3, 2), M=M)
+    x64, w64 = x.astype(np.float64), w.astype(np.float64)
+    ref = OM.silu(x64 @ w64[:inter].T) * (x64 @ w64[inter:].T)
+    got = down(a)
+    rows_close(got[2:2 + M], ref, TOL[dtype], "swiglu projection")
+    assert not got[:2].any() and not got[2 + M:].any()
 
 
 # ------------------------------------------------------------- whole decode
