@@ -44,6 +44,8 @@ TID = {
     # multi-layer model (layer l uses tensor id base + 16 * l)
     "mE": 60, "mWlm": 61, "mprompt": 62, "x": 63, "pos": 64,
     "mWq": 1000, "mWk": 1001, "mWv": 1002, "mWo": 1003, "mWg": 1004, "mWu": 1005, "mWd": 1006,
+    # training form
+    "tx0": 70, "tmask": 71,
 }
 _LAYER_STRIDE = 16
 
@@ -437,3 +439,48 @@ def make_model_weights(cfg: ModelConfig, seed: int) -> ModelWeights:
 def make_prompts(cfg: ModelConfig, seed: int) -> np.ndarray:
     """[B, prompt_len] int32 uniform token ids."""
     return _rng(seed, TID["mprompt"]).integers(0, cfg.V, size=(cfg.B, cfg.prompt_len)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# training form (forward pass and loss value of the 2L layout)
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class TrainConfig:
+    """A batch of S training sequences of L tokens for the one-layer model
+    (fields as Config); each sample also enters in its complementary view,
+    so 2S sequences of 2L rows are attended.  mask_p: probability that a
+    position is masked in the first view."""
+    name: str
+    dtype: str
+    S: int
+    L: int
+    Hq: int
+    Hkv: int
+    d: int
+    hidden: int
+    V: int
+    D: int = 32
+    mask_p: float = 0.5
+    std: float = 0.02
+    lm_scale: float = 1.0
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+# small cases the oracle runs in seconds (tests; lm_scale makes the logits
+# O(1) so that a wrong source row or target changes the loss visibly) and
+# the 1.5B-shaped layer the benchmark times (L 2048, 4 samples = 8 views)
+T1 = TrainConfig(name="t1", dtype="f32", S=2, L=96, Hq=4, Hkv=2, d=64, hidden=256, V=1024, lm_scale=300.0)
+T2 = TrainConfig(name="t2", dtype="bf16", S=2, L=128, Hq=12, Hkv=2, d=128, hidden=1536, V=4096, lm_scale=100.0)
+T3 = TrainConfig(name="t3", dtype="bf16", S=4, L=2048, Hq=12, Hkv=2, d=128, hidden=1536, V=151936)
+TRAIN_CONFIGS = {c.name: c for c in (T1, T2, T3)}
+
+
+def make_train_batch(cfg: TrainConfig, seed: int):
+    """x0 [S, L] int32 uniform token ids; m [S, L] bool, Bernoulli(mask_p):
+    the first view's mask (the second view masks the complement)."""
+    x0 = _rng(seed, TID["tx0"]).integers(0, cfg.V, size=(cfg.S, cfg.L)).astype(np.int32)
+    m = _rng(seed, TID["tmask"]).random((cfg.S, cfg.L)) < cfg.mask_p
+    return x0, m

@@ -260,7 +260,66 @@ def extras_e2e(graphs=True, n_blocks=None):
     return out
 
 
-def extras(w3, reps, parts=("attn", "long", "lm", "e2e"), graphs=True, e2e_blocks=None):
+def train_attn_flops(cfg) -> float:
+    """Algorithmic FLOPs of one 2L-layout attention call: every visible
+    (query, key) pair costs a d-long dot product for the score and one for
+    the output (2 flops per multiply-add each).  Per view sequence and query
+    head, block b's D noisy and D clean rows each see (b + 1) * D keys."""
+    nb = cfg.L // cfg.D
+    pairs = 2 * sum(cfg.D * (b + 1) * cfg.D for b in range(nb))
+    return 4.0 * cfg.d * pairs * cfg.Hq * 2 * cfg.S
+
+
+def extras_train(reps):
+    """Training form (forward pass and loss value) of the 1.5B-shaped layer:
+    S samples of L tokens in both complementary views, i.e. 2S sequences of
+    2L rows; the 2L attention alone and the whole forward + loss."""
+    from block_diffusion_decoding_amd import ops
+    from block_diffusion_decoding_amd.train import TrainForward
+    cfg = bi.T3
+    log(f"[bench] training form: {cfg.S} samples x L {cfg.L} in 2 views, {cfg.Hq}q/{cfg.Hkv}kv heads d{cfg.d}, "
+        f"hidden {cfg.hidden}, vocab {cfg.V}")
+    dev, dt = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+
+    def rnd(*shape):
+        return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * cfg.std).to(dt)
+
+    hq, hkv, hid = cfg.Hq * cfg.d, cfg.Hkv * cfg.d, cfg.hidden
+    W = {"E": rnd(cfg.V + 1, hid), "Wq": rnd(hq, hid), "Wk": rnd(hkv, hid), "Wv": rnd(hkv, hid),
+         "Wo": rnd(hid, hq), "Wlm": rnd(cfg.V, hid)}
+    tf = TrainForward(W, cfg.Hq, cfg.Hkv, cfg.d, cfg.D, dtype=dt, device=dev)
+    del W
+    x0, m = bi.make_train_batch(cfg, 0)
+    plan = tf.plan(x0, m)
+    res = tf.forward(x0, m, plan)
+    t_fwd, _ = time_call(lambda: tf.forward(x0, m, plan), max(3, reps // 4))
+    n = res["count"]
+    S2, L2 = 2 * cfg.S, 2 * cfg.L
+    q = tf._bufs["q"].view(S2, L2, cfg.Hq, cfg.d)
+    k = tf._bufs["k"].view(S2, L2, cfg.Hkv, cfg.d)
+    v = tf._bufs["v"].view(S2, L2, cfg.Hkv, cfg.d)
+    o = tf._bufs["o"].view(S2, L2, cfg.Hq, cfg.d)
+    t_att, t_att_mean = time_call(lambda: ops.bd_train_attn(q, k, v, o, L=cfg.L, D=cfg.D), reps)
+    fl = train_attn_flops(cfg)
+    loss = float(res["loss_sum"].cpu()[0])
+    log(f"[bench] training form: forward + loss {t_fwd * 1e3:.2f} ms for {n} supervised tokens "
+        f"({n / t_fwd:.0f} tokens/s), mean loss {loss / n:.4f}; 2L attention {t_att * 1e6:.1f} us = "
+        f"{fl / t_att / 1e15:.3f} PFLOP/s ({fl / t_att / 2.5e15 * 100:.1f}% of the bf16 MFMA peak)")
+    out = {"train_1.5B_layer": {
+        "shape": f"{cfg.S} samples x L {cfg.L} (D {cfg.D}), 2 complementary views = {S2} sequences of {L2} rows; "
+                 f"{cfg.Hq}q/{cfg.Hkv}kv heads d{cfg.d}, hidden {hid}, vocab {cfg.V}",
+        "forward_and_loss_ms": t_fwd * 1e3, "supervised_tokens": n, "supervised_tokens_per_s": n / t_fwd,
+        "mean_loss": loss / n,
+        "attention_us_median": t_att * 1e6, "attention_us_mean": t_att_mean * 1e6, "attention_flops": fl,
+        "attention_pflops": fl / t_att / 1e15, "attention_frac_of_bf16_mfma_peak": fl / t_att / 2.5e15}}
+    del tf
+    torch.cuda.empty_cache()
+    return out
+
+
+def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train"), graphs=True, e2e_blocks=None):
     """Attention and LM head alone at the long-context / batched shapes, the
     long-context block loop and the end-to-end multi-layer decode."""
     from block_diffusion_decoding_amd import ops
@@ -275,6 +334,8 @@ def extras(w3, reps, parts=("attn", "long", "lm", "e2e"), graphs=True, e2e_block
         out.update(extras_lm(w3, reps))
     if "e2e" in parts:
         out.update(extras_e2e(graphs, e2e_blocks))
+    if "train" in parts:
+        out.update(extras_train(reps))
     return out
 
 
@@ -418,8 +479,8 @@ def main():
     ap.add_argument("--no-graphs", action="store_true", help="launch every step's kernels eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
-    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e"), default="all",
-                    help="attn/long/lm: run only that single-call or loop measurement (for profiling) and print "
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train"), default="all",
+                    help="attn/long/lm/e2e/train: run only that measurement (for profiling) and print "
                          "its JSON instead of the bench line")
     ap.add_argument("--e2e-blocks", type=int, default=None,
                     help="blocks generated by the end-to-end decode measurement (default: the workload's 16)")
@@ -441,8 +502,8 @@ def main():
     pkg.load_library()
 
     cfg = bi.C3
-    if args.section == "e2e":
-        print(json.dumps(extras(None, args.reps, parts=("e2e",), graphs=not args.no_graphs,
+    if args.section in ("e2e", "train"):
+        print(json.dumps(extras(None, args.reps, parts=(args.section,), graphs=not args.no_graphs,
                                 e2e_blocks=args.e2e_blocks)), flush=True)
         return
     log("[bench] generating the 7B-shape workload")

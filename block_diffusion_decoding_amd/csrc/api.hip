@@ -85,6 +85,7 @@ bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const
   a.q_off = q_off;
   a.cap = cap;
   a.n_blk = n_blk;
+  a.epc = 1;
   a.scale = scale;
   return hip_status(bd_attn_launch(dt, p, a, static_cast<hipStream_t>(stream)));
 }
@@ -306,6 +307,39 @@ bd_status bd_swiglu(bd_dtype dt, int M, int inter, const void* gu, bd_rows gr, v
   if (M == 0) return BD_OK;
   if (inter <= 0 || !gu || !a || !valid_rows(gr) || !valid_rows(ar)) return BD_EINVAL;
   return hip_status(bd_swiglu_launch(dt, M, inter, gu, gr, a, ar, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+size_t bd_train_attn_workspace_size(bd_dtype dt, int S, int L, int D, int Hq, int Hkv, int d) {
+  if (!valid_dtype(dt) || S <= 0 || L <= 0 || D < 1 || L % D != 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+      (d != 64 && d != 128))
+    return 0;
+  return bd_train_plan(dt, S, L, D, Hq, Hkv, d).ws_bytes;
+}
+
+bd_status bd_train_attn(bd_dtype dt, int S, int L, int D, int Hq, int Hkv, int d, const void* q, const void* k,
+                        const void* v, float scale, void* o, void* workspace, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dt) || S < 0 || L < 0) return BD_EINVAL;
+  if (S == 0 || L == 0) return BD_OK;
+  if (D < 1 || L % D != 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !q || !k || !v || !o || !(scale == scale))
+    return BD_EINVAL;
+  if (d != 64 && d != 128) return BD_EUNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BD_EINVAL;
+  const BdTrainPlan p = bd_train_plan(dt, S, L, D, Hq, Hkv, d);
+  if (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)) return BD_EINVAL;
+  return hip_status(bd_train_attn_launch(dt, p, S, L, D, Hq, Hkv, d, q, k, v, scale, o, workspace,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+bd_status bd_masked_nll(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src, const int32_t* row_idx,
+                        const void* w, const int32_t* target, const float* lse, float* nll, float* loss_sum,
+                        void* stream) {
+  if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
+  if (M == 0) return BD_OK;
+  if (hidden <= 0 || V <= 0 || n_src <= 0 || !h_src || !w || !target || !lse || !nll) return BD_EINVAL;
+  if (hidden % (dt == BD_BF16 ? 8 : 4) != 0 || !aligned16(h_src) || !aligned16(w)) return BD_EUNSUPPORTED;
+  return hip_status(bd_nll_launch(dt, M, hidden, V, h_src, n_src, row_idx, w, target, lse, nll, loss_sum,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

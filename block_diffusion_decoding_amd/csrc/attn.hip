@@ -74,6 +74,7 @@ struct AttnK {
   float* part_o;
   float* part_ml;
   int B, Hq, Hkv, G, D, n_q, q_off, cap, n_blk;
+  int epc;  // entries (b) per cache slab: entry b reads cache slab b / epc
   int R, QT, nqg, chunk, nchunks, n_units;
   float scale_log2;
 };
@@ -241,8 +242,9 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_ke
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
-  const uint16_t* kc_bh = a.kc + (size_t)bh * a.cap * DH;
-  const uint16_t* vc_bh = a.vc + (size_t)bh * a.cap * DH;
+  const size_t slab = (size_t)(b / a.epc) * a.Hkv + kvh;
+  const uint16_t* kc_bh = a.kc + slab * a.cap * DH;
+  const uint16_t* vc_bh = a.vc + slab * a.cap * DH;
   const uint16_t* kb_b = a.kb + ((size_t)b * a.n_blk * a.Hkv + kvh) * DH;
   const uint16_t* vb_b = a.vb + ((size_t)b * a.n_blk * a.Hkv + kvh) * DH;
   const size_t blk_stride = (size_t)a.Hkv * DH;
@@ -621,7 +623,7 @@ struct AttnF {
   const float* vb;
   float* o;
   float* lse;
-  int Hq, Hkv, G, d, D, n_q, q_off, cap, n_blk;
+  int Hq, Hkv, G, d, D, n_q, q_off, cap, n_blk, epc;
   float scale;
 };
 
@@ -652,9 +654,9 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnF a) {
   __shared__ float red[kThreads / 64];
   if (tid < a.d) sq[tid] = a.q[(((size_t)b * a.n_q + i) * a.Hq + h) * a.d + tid];
   __syncthreads();
-  const size_t bh = (size_t)b * a.Hkv + kvh;
+  const size_t slab = (size_t)(b / a.epc) * a.Hkv + kvh;
   auto kp = [&](const float* cache, const float* blk, int key) -> const float* {
-    return key < L ? cache + (bh * a.cap + key) * a.d
+    return key < L ? cache + (slab * a.cap + key) * a.d
                    : blk + (((size_t)b * a.n_blk + (key - L)) * a.Hkv + kvh) * a.d;
   };
   float m = -__builtin_inff(), l = 0.f, acc = 0.f;
@@ -727,7 +729,7 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
     AttnF a{static_cast<const float*>(x.q), static_cast<const float*>(x.k_cache),
             static_cast<const float*>(x.v_cache), x.kv_len, static_cast<const float*>(x.k_blk),
             static_cast<const float*>(x.v_blk), static_cast<float*>(x.o), x.lse,
-            x.Hq, x.Hkv, x.G, x.d, x.D, x.n_q, x.q_off, x.cap, x.n_blk, x.scale};
+            x.Hq, x.Hkv, x.G, x.d, x.D, x.n_q, x.q_off, x.cap, x.n_blk, x.epc, x.scale};
     hipLaunchKernelGGL(attn_f32_kernel, dim3(x.n_q, x.Hq, x.B), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
@@ -743,7 +745,7 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
   a.part_o = x.part_o;
   a.part_ml = x.part_ml;
   a.B = x.B; a.Hq = x.Hq; a.Hkv = x.Hkv; a.G = x.G; a.D = x.D; a.n_q = x.n_q; a.q_off = x.q_off;
-  a.cap = x.cap; a.n_blk = x.n_blk;
+  a.cap = x.cap; a.n_blk = x.n_blk; a.epc = x.epc;
   a.R = p.R; a.QT = p.QT; a.nqg = p.nqg; a.chunk = p.chunk; a.nchunks = p.nchunks;
   a.n_units = x.B * x.Hkv * p.nchunks;
   a.scale_log2 = x.scale * BD_LOG2E;

@@ -34,6 +34,7 @@ struct BdAttnArgs {
   float* part_o;
   float* part_ml;
   int B, Hq, Hkv, G, d, D, n_q, q_off, cap, n_blk;
+  int epc;  // entries per cache slab (1: entry b owns slab b)
   float scale;
 };
 
@@ -130,6 +131,23 @@ hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* 
 hipError_t bd_append_launch(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache,
                             void* v_cache, int32_t* kv_len, const void* k_blk, const void* v_blk,
                             int n_blk, int n_rows, hipStream_t s);
+
+// ---- training form (train.hip) ------------------------------------------------
+struct BdTrainPlan {
+  BdAttnPlan attn;      // the step kernel over S*2*(L/D) entries
+  size_t cache_bytes;   // one of the clean K / V caches [S, Hkv, L, d]
+  size_t len_off;       // int32 cached length per entry
+  size_t attn_off;      // attention partials
+  size_t ws_bytes;
+};
+
+BdTrainPlan bd_train_plan(bd_dtype dt, int S, int L, int D, int Hq, int Hkv, int d);
+hipError_t bd_train_attn_launch(bd_dtype dt, const BdTrainPlan& p, int S, int L, int D, int Hq, int Hkv, int d,
+                                const void* q, const void* k, const void* v, float scale, void* o,
+                                void* workspace, hipStream_t s);
+hipError_t bd_nll_launch(bd_dtype dt, int M, int hidden, int V, const void* h, int n_src, const int32_t* row_idx,
+                         const void* w, const int32_t* target, const float* lse, float* nll, float* loss,
+                         hipStream_t s);
 
 // ---- layer pieces of the multi-layer model (model_ops.hip) --------------------
 hipError_t bd_rmsnorm_launch(bd_dtype dt, int M, int hidden, const void* x, bd_rows xr, float eps, void* y,

@@ -262,3 +262,32 @@ def bd_swiglu(gu, gr, a, ar, *, M, inter, stream=None):
     st = _lib.load().bd_swiglu(_dt(gu), M, inter, _p(gu), gr, _p(a), ar, _stream(stream))
     _check("bd_swiglu", st)
 
+
+
+def bd_train_attn_workspace_size(dtype, S, L, D, Hq, Hkv, d) -> int:
+    return int(_lib.load().bd_train_attn_workspace_size(_DT[dtype], S, L, D, Hq, Hkv, d))
+
+
+def bd_train_attn(q, k, v, o, *, L, D, scale=None, ws=None, stream=None):
+    """Attention of the 2L training layout: q [S, 2L, Hq, d], k/v [S, 2L, Hkv, d]
+    (rows 0..L-1 noisy, L..2L-1 clean) -> o like q."""
+    lib = _lib.load()
+    S, L2, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert L2 == 2 * L
+    dt = _dt(q)
+    if ws is None:
+        ws = workspace(lib.bd_train_attn_workspace_size(dt, S, L, D, Hq, Hkv, d), q.device, "train")
+    sc = d ** -0.5 if scale is None else float(scale)
+    st = lib.bd_train_attn(dt, S, L, D, Hq, Hkv, d, _p(q), _p(k), _p(v), sc, _p(o), _p(ws), ws.numel(),
+                           _stream(stream))
+    _check("bd_train_attn", st)
+
+
+def bd_masked_nll(h_src, row_idx, w, target, lse, nll, loss_sum=None, *, M, stream=None):
+    """nll[m] = lse[m] - h_src[row_idx[m]] . w[target[m]]; loss_sum[0] = sum."""
+    V, hidden = w.shape
+    n_src = h_src.numel() // hidden
+    st = _lib.load().bd_masked_nll(_dt(w), M, hidden, V, _p(h_src), n_src, _p(row_idx), _p(w), _p(target),
+                                   _p(lse), _p(nll), _p(loss_sum), _stream(stream))
+    _check("bd_masked_nll", st)

@@ -319,6 +319,42 @@ bd_status bd_rope(bd_dtype dt, int B, int n_rows, int H, int d, void* x, bd_rows
 bd_status bd_swiglu(bd_dtype dt, int M, int inter, const void* gu, bd_rows gr, void* a, bd_rows ar,
                     void* stream);
 
+/* ------------------------------------------------------------------------
+ * Training form (forward pass and loss value only).  [v2 notes] Key design 2:
+ * the noisy sequence x_t (masked positions -> [MASK]) and the clean x_0 of a
+ * sample are concatenated into 2L positions and attended under one hybrid
+ * mask; each sample appears twice, with a mask m and its complement; the
+ * loss is the cross-entropy of the masked tokens, each predicted from the
+ * logits of the position before it.
+ * ---------------------------------------------------------------------- */
+
+/* Attention over the 2L layout of S sequences (S counts every view):
+ *   q [S, 2L, Hq, d], k/v [S, 2L, Hkv, d]; within a sequence rows 0..L-1 are
+ *   x_t, rows L..2L-1 are x_0; block of row p = (p mod L) / D.
+ *   A noisy row of block b sees the noisy rows of block b and the clean rows
+ *   of blocks < b; a clean row of block b sees the clean rows of blocks <= b;
+ *   clean rows never see noisy rows.  o [S, 2L, Hq, d]; scale usually 1/sqrt(d).
+ * Each (sequence, half, block) is run as a block over a prefix cache (the
+ * clean rows of earlier blocks), with the block's own rows as in-block keys:
+ * the workspace (bd_train_attn_workspace_size, always > 0) receives the
+ * clean K/V in cache layout and the per-block lengths.  L % D == 0,
+ * d in {64, 128}; Hq % Hkv == 0. */
+size_t bd_train_attn_workspace_size(bd_dtype dt, int S, int L, int D, int Hq, int Hkv, int d);
+bd_status bd_train_attn(bd_dtype dt, int S, int L, int D, int Hq, int Hkv, int d,
+                        const void* q, const void* k, const void* v, float scale, void* o,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* Cross-entropy terms of the supervised positions:
+ *   nll[m] = lse[m] - h_src[row_idx[m]] . w[target[m]]      (m < M)
+ * with lse from bd_lmhead_confidence on the same rows (row_idx = the
+ * token-shift source rows; NULL = identity) and w the LM head [V, hidden];
+ * the dot product in fp32.  loss_sum (optional) [1] = sum_m nll[m], added in
+ * a fixed order in fp64.  A row index outside [0, n_src) or a target
+ * outside [0, V) gives a NaN term.  hidden % 8 == 0 (bf16) or % 4 (fp32). */
+bd_status bd_masked_nll(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
+                        const int32_t* row_idx, const void* w, const int32_t* target, const float* lse,
+                        float* nll, float* loss_sum, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,8 @@ def test_header_declares_the_four_calls_and_support():
               "bd_embed_rows", "bd_linear", "bd_qkv_proj", "bd_block_attn_workspace_size",
               "bd_linear_workspace_size", "bd_qkv_proj_workspace_size",
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
-              "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu"]:
+              "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu",
+              "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll"]:
         assert n in names
 
 
@@ -212,3 +213,22 @@ def test_fused_layer_call_argument_errors():
     assert lib.bd_gate_up_swiglu(1, 128, 1000, FAKE, d1, FAKE, 8960, FAKE, d1, None) == _lib.BD_EUNSUPPORTED
     assert lib.bd_gate_up_swiglu(1, 128, 1536, FAKE, d1, None, 8960, FAKE, d1, None) == E
     assert lib.bd_gate_up_swiglu(1, 0, 1536, FAKE, d1, FAKE, 8960, FAKE, d1, None) == 0
+
+
+def test_training_form_argument_errors():
+    """The 2L attention and the cross-entropy terms check their shapes
+    before any launch."""
+    lib = _lib.load()
+    E, U = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED
+    need = lib.bd_train_attn_workspace_size(1, 8, 2048, 32, 12, 2, 128)
+    # two bf16 clean caches of 8 x 2 x 2048 x 128 plus 1024 entry lengths
+    assert need >= 2 * 8 * 2 * 2048 * 128 * 2 + 1024 * 4
+    assert lib.bd_train_attn_workspace_size(1, 8, 2000, 32, 12, 2, 128) == 0        # L % D
+    ta = lambda **k: lib.bd_train_attn(1, k.get("S", 8), k.get("L", 2048), k.get("D", 32), k.get("Hq", 12), 2,
+                                       k.get("d", 128), FAKE, FAKE, FAKE, 0.088, FAKE, k.get("ws", FAKE),
+                                       k.get("wsb", need), None)
+    assert ta(L=2000) == E and ta(Hq=13) == E and ta(d=96) == U and ta(ws=None) == E and ta(wsb=need - 16) == E
+    assert ta(S=0) == 0
+    nl = lambda **k: lib.bd_masked_nll(1, k.get("M", 10), k.get("hid", 1536), 151936, FAKE, 100, FAKE, FAKE,
+                                       k.get("tg", FAKE), FAKE, FAKE, None, None)
+    assert nl(hid=1530) == U and nl(tg=None) == E and nl(M=0) == 0

@@ -1,0 +1,93 @@
+"""GPU parity of the training form (2L layout) against the oracle
+(oracle/train.py): the 2L hybrid-mask attention alone, and the forward pass
+with the token-shift masked cross-entropy of both complementary views."""
+import numpy as np
+import pytest
+import torch
+
+import bd_inputs as bi
+from gpu_util import DEV, TOL, down, rows_close, say, tdt, up
+from oracle import refine as R
+from oracle import train as TR
+
+pytestmark = pytest.mark.gpu
+
+
+def ops():
+    from block_diffusion_decoding_amd import ops as o
+    return o
+
+
+@pytest.mark.parametrize("dtype,S,L,D,Hq,Hkv,d", [("f32", 2, 96, 32, 4, 2, 64), ("bf16", 2, 128, 32, 12, 2, 128),
+                                                  ("bf16", 3, 64, 32, 28, 4, 128), ("bf16", 2, 64, 8, 4, 2, 64),
+                                                  ("bf16", 1, 512, 32, 12, 2, 128)])
+def test_train_attn_matches_masked_attention(dtype, S, L, D, Hq, Hkv, d):
+    say(f"[train] attention {dtype} S{S} L{L} D{D} Hq{Hq} Hkv{Hkv} d{d}")
+    o = ops()
+    T = tdt(dtype)
+    q = bi.normal(20, "q", (S, 2 * L, Hq, d), 1.0, dtype)
+    k = bi.normal(20, "blk_k", (S, 2 * L, Hkv, d), 1.0, dtype)
+    v = bi.normal(20, "blk_v", (S, 2 * L, Hkv, d), 1.0, dtype)
+    out = torch.zeros(S, 2 * L, Hq, d, dtype=T, device=DEV)
+    o.bd_train_attn(up(q, T), up(k, T), up(v, T), out, L=L, D=D)
+    torch.cuda.synchronize()
+    A = TR.mask_2L(L, D)
+    got = down(out)
+    for s in range(S):
+        ref, _ = R.attention(q[s].astype(np.float64), k[s].astype(np.float64), v[s].astype(np.float64), A, Hq // Hkv)
+        rows_close(got[s].reshape(-1, d), ref.reshape(-1, d), TOL[dtype], f"sequence {s}")
+
+
+def _decoder_weights(cfg, w):
+    return {k: torch.from_numpy(getattr(w, k)) for k in ("E", "Wq", "Wk", "Wv", "Wo", "Wlm")}
+
+
+@pytest.mark.parametrize("cfg", [bi.T1, bi.T2], ids=["tiny-f32", "1.5B-layer-bf16"])
+def test_training_forward_matches_the_oracle(cfg):
+    """Every supervised position's cross-entropy and the summed loss of both
+    views, against the oracle on the same seeded batch."""
+    say(f"[train] forward + loss {cfg.name}")
+    from block_diffusion_decoding_amd.train import TrainForward
+    w = bi.make_weights(cfg, 3)
+    x0, m = bi.make_train_batch(cfg, 3)
+    model = R.Model.from_weights(w, cfg)
+    tf = TrainForward(_decoder_weights(cfg, w), cfg.Hq, cfg.Hkv, cfg.d, cfg.D, dtype=tdt(cfg.dtype), device=DEV)
+    res = tf.forward(x0, m)
+    torch.cuda.synchronize()
+    nll = res["nll"].cpu().numpy().astype(np.float64)
+    pos = res["pos"]
+    rtol = TOL[cfg.dtype]
+    ref_total, ref_count = 0.0, 0
+    for s in range(cfg.S):
+        ref_total += TR.sample_loss(model, x0[s], m[s], cfg.D)[0]
+        ref_count += cfg.L - 1
+        for vi, view in enumerate(TR.complementary_views(m[s])):
+            p_ref, rows, nll_ref, H = TR.view_nll(model, x0[s], view, cfg.D)
+            logits = R.lm_logits(model.Wlm, H[rows])
+            rms = np.sqrt((logits ** 2).mean(axis=1))
+            sel = pos[:, 0] == 2 * s + vi
+            assert np.array_equal(pos[sel, 1], p_ref)
+            err = np.abs(nll[sel] - nll_ref)
+            bound = 2 * rtol * np.maximum(1.0, rms)
+            assert np.all(err <= bound), f"sample {s} view {vi}: max nll error {err.max():.3g}"
+    assert res["count"] == ref_count
+    got_total = float(res["loss_sum"].cpu()[0])
+    assert abs(got_total - ref_total) <= rtol * abs(ref_total), (got_total, ref_total)
+
+
+def test_masked_nll_flags_invalid_rows_and_targets():
+    say("[train] nll bounds")
+    o = ops()
+    T = torch.bfloat16
+    h = up(bi.normal(21, "h", (6, 512), 0.5, "bf16"), T)
+    w = up(bi.normal(21, "Wlm", (100, 512), 0.05, "bf16"), T)
+    ri = torch.tensor([0, 5, 6, -1, 2], dtype=torch.int32, device=DEV)
+    tg = torch.tensor([3, 99, 1, 1, 100], dtype=torch.int32, device=DEV)
+    lse = torch.zeros(5, dtype=torch.float32, device=DEV)
+    nll = torch.zeros(5, dtype=torch.float32, device=DEV)
+    o.bd_masked_nll(h, ri, w, tg, lse, nll, M=5)
+    got = nll.cpu().numpy()
+    assert np.isfinite(got[:2]).all() and np.isnan(got[2:]).all()
+    hf = down(h).astype(np.float64)
+    wf = down(w).astype(np.float64)
+    np.testing.assert_allclose(got[:2], [-(hf[0] @ wf[3]), -(hf[5] @ wf[99])], rtol=1e-5, atol=1e-5)
