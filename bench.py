@@ -44,6 +44,8 @@ import json
 import sys
 import time
 
+from dataclasses import replace
+
 import numpy as np
 import torch
 
@@ -319,7 +321,39 @@ def extras_train(reps):
     return out
 
 
-def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train"), graphs=True, e2e_blocks=None):
+def extras_subblock(w3, graphs, steps=40, warmup=10):
+    """The headline loop (7B shape, planted pass rate 0.5) at sub-block sizes
+    4, 8, 16 and 32 (= the block: every step recomputes all D rows): the pages
+    call the best sub-block size task-dependent."""
+    out = {}
+    pre = None
+    for S in (4, 8, 16, 32):
+        cfg = replace(bi.C3, S=S)
+        if pre is None:
+            pre = bi.make_prefix(cfg, 0)
+        dec = make_decoder(cfg, w3, pre)
+        plants = block_plants(cfg, w3, 0.5, 0, 8)
+        if graphs:
+            dec.capture(cfg.S, cfg.tau)
+        loop = Loop(dec, cfg, plants)
+        for _ in range(warmup):
+            loop.step()
+        torch.cuda.synchronize()
+        s0, t0_tok = loop.steps, loop.tokens
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            loop.step()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        n, tok = loop.steps - s0, loop.tokens - t0_tok
+        log(f"[bench] sub-block {S}: {n / el:.1f} steps/s, {tok / el:.0f} tokens/s ({tok / n:.2f} tokens per step)")
+        out[f"S{S}"] = {"steps_per_s": n / el, "tokens_per_s": tok / el, "tokens_per_step": tok / n}
+        del dec, plants, loop
+        torch.cuda.empty_cache()
+    return {"subblock_sweep_7B": out}
+
+
+def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock"), graphs=True, e2e_blocks=None):
     """Attention and LM head alone at the long-context / batched shapes, the
     long-context block loop and the end-to-end multi-layer decode."""
     from block_diffusion_decoding_amd import ops
@@ -336,6 +370,8 @@ def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train"), graphs=True, 
         out.update(extras_e2e(graphs, e2e_blocks))
     if "train" in parts:
         out.update(extras_train(reps))
+    if "subblock" in parts:
+        out.update(extras_subblock(w3, graphs))
     return out
 
 
@@ -479,8 +515,8 @@ def main():
     ap.add_argument("--no-graphs", action="store_true", help="launch every step's kernels eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
-    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train"), default="all",
-                    help="attn/long/lm/e2e/train: run only that measurement (for profiling) and print "
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock"), default="all",
+                    help="attn/long/lm/e2e/train/subblock: run only that measurement (for profiling) and print "
                          "its JSON instead of the bench line")
     ap.add_argument("--e2e-blocks", type=int, default=None,
                     help="blocks generated by the end-to-end decode measurement (default: the workload's 16)")

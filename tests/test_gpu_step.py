@@ -4,6 +4,8 @@ against the fp64 oracle on the same seeded inputs.
 Multi-step comparisons use teacher forcing: after every step the GPU state is
 set to the oracle's unmask decisions, so exempt ties cannot make the two
 sides drift apart."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -57,7 +59,8 @@ def test_tiny_prefill_and_commit_equal_oracle_cache(cfg):
         rows_close(down(dec.H)[b, 0], q.carry, TOL[cfg.dtype], "carry")
 
 
-@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96], ids=["tiny-64", "tiny-96"])
+@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96, replace(bi.C1, S=4), replace(bi.C1_96, S=16)],
+                         ids=["tiny-64", "tiny-96", "tiny-64-S4", "tiny-96-S16"])
 @pytest.mark.parametrize("mode", ["exact", "dual"])
 def test_tiny_block_decode_teacher_forced(cfg, mode):
     say(f"[step] tiny block loop {cfg.name} {mode}")
