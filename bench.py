@@ -353,7 +353,48 @@ def extras_subblock(w3, graphs, steps=40, warmup=10):
     return {"subblock_sweep_7B": out}
 
 
-def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock"), graphs=True, e2e_blocks=None):
+def extras_v1():
+    """v1-style decoding of a full-attention model (one 1.5B-shaped layer +
+    the 1.5B head) with the block-wise DualCache, against the same decode
+    with an exact full forward pass every step: 4 prompts of 256 ids, 256
+    generated tokens in blocks of 32, tau 0.9, eager launches (the prefix and
+    suffix lengths change every block)."""
+    from block_diffusion_decoding_amd.v1 import FullAttnDecoder
+    cfg = bi.T3
+    B, P, gen = 4, 256, 256
+    log(f"[bench] v1 full-attention decode: B {B}, prompt {P}, {gen} new tokens, {cfg.Hq}q/{cfg.Hkv}kv d{cfg.d}, "
+        f"hidden {cfg.hidden}, vocab {cfg.V}")
+    dev, dt = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+
+    def rnd(*shape):
+        return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * cfg.std).to(dt)
+
+    hq, hkv, hid = cfg.Hq * cfg.d, cfg.Hkv * cfg.d, cfg.hidden
+    W = {"E": rnd(cfg.V + 1, hid), "Wq": rnd(hq, hid), "Wk": rnd(hkv, hid), "Wv": rnd(hkv, hid),
+         "Wo": rnd(hid, hq), "Wlm": rnd(cfg.V, hid)}
+    dec = FullAttnDecoder(W, B, P, gen, cfg.Hq, cfg.Hkv, cfg.d, cfg.D, dtype=dt, device=dev)
+    del W
+    prompts = bi.make_train_batch(replace(cfg, S=B, L=P), 9)[0]
+    out = {}
+    for mode in ("dual", "exact"):
+        dec.generate(prompts[:, :P], 0.9, mode)          # warm-up pass
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, steps = dec.generate(prompts[:, :P], 0.9, mode)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        log(f"[bench] v1 {mode}: {steps} steps in {el * 1e3:.1f} ms, {B * gen / el:.0f} tokens/s")
+        out[mode] = {"steps": steps, "ms": el * 1e3, "tokens_per_s": B * gen / el}
+    out["dual_speedup"] = out["exact"]["ms"] / out["dual"]["ms"]
+    del dec
+    torch.cuda.empty_cache()
+    return {"v1_full_attention_1.5B_layer": out}
+
+
+def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "v1"), graphs=True,
+           e2e_blocks=None):
     """Attention and LM head alone at the long-context / batched shapes, the
     long-context block loop and the end-to-end multi-layer decode."""
     from block_diffusion_decoding_amd import ops
@@ -372,6 +413,8 @@ def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock"), g
         out.update(extras_train(reps))
     if "subblock" in parts:
         out.update(extras_subblock(w3, graphs))
+    if "v1" in parts:
+        out.update(extras_v1())
     return out
 
 
@@ -515,8 +558,8 @@ def main():
     ap.add_argument("--no-graphs", action="store_true", help="launch every step's kernels eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
-    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock"), default="all",
-                    help="attn/long/lm/e2e/train/subblock: run only that measurement (for profiling) and print "
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "v1"),
+                    default="all", help="attn/long/lm/e2e/train/subblock/v1: run only that measurement (for profiling) and print "
                          "its JSON instead of the bench line")
     ap.add_argument("--e2e-blocks", type=int, default=None,
                     help="blocks generated by the end-to-end decode measurement (default: the workload's 16)")
@@ -538,7 +581,7 @@ def main():
     pkg.load_library()
 
     cfg = bi.C3
-    if args.section in ("e2e", "train"):
+    if args.section in ("e2e", "train", "v1"):
         print(json.dumps(extras(None, args.reps, parts=(args.section,), graphs=not args.no_graphs,
                                 e2e_blocks=args.e2e_blocks)), flush=True)
         return

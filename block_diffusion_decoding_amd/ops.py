@@ -80,7 +80,10 @@ def bd_block_attn(q, k_cache, v_cache, kv_len, k_blk, v_blk, o, *, D, q_off=0, s
     o [B, n_q, Hq, d]; lse [B, Hq, n_q] fp32 or None."""
     lib = _lib.load()
     B, n_q, Hq, d = q.shape
-    _, Hkv, cap, _ = k_cache.shape
+    if k_cache is None:         # no cache rows: only the in-block keys
+        Hkv, cap = k_blk.shape[2], 0
+    else:
+        _, Hkv, cap, _ = k_cache.shape
     n_blk = k_blk.shape[1]
     if scale is None:
         scale = d ** -0.5
@@ -156,18 +159,22 @@ def bd_threshold_unmask(conf, argmax, tokens, mask_bits, *, win_lo, threshold, n
     _check("bd_threshold_unmask", st)
 
 
-def bd_kv_append(k_cache, v_cache, kv_len, k_blk, v_blk, *, n_rows, kv_len_host=None, stream=None):
-    """k/v_cache [B, Hkv, cap, d]; kv_len [B] int32 (in/out); k/v_blk [B, n_blk, Hkv, d]."""
+def bd_kv_append(k_cache, v_cache, kv_len, k_blk, v_blk, *, n_rows, kv_len_host=None, row_off=0, stream=None):
+    """k/v_cache [B, Hkv, cap, d]; kv_len [B] int32 (in/out); k/v_blk [B, n_blk, Hkv, d];
+    appends rows row_off .. row_off + n_rows - 1 of each sequence's k/v_blk."""
     lib = _lib.load()
     B, Hkv, cap, d = k_cache.shape
     n_blk = k_blk.shape[1]
+    assert 0 <= row_off and row_off + n_rows <= n_blk
     host = None
     if kv_len_host is not None:
         import numpy as np
         host = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+    off = row_off * Hkv * d * k_blk.element_size()
+    kp, vp = _p(k_blk), _p(v_blk)
     st = lib.bd_kv_append(_dt(k_cache), B, Hkv, d, cap, _p(k_cache), _p(v_cache), _p(kv_len),
-                          None if host is None else host.ctypes.data, _p(k_blk), _p(v_blk), n_blk, n_rows,
-                          _stream(stream))
+                          None if host is None else host.ctypes.data, kp + off, vp + off, n_blk,
+                          n_rows, _stream(stream))
     _check("bd_kv_append", st)
 
 
