@@ -33,20 +33,22 @@ constexpr int kThreads = 256;
 #ifndef BD_GEMM_MAX_MT
 #define BD_GEMM_MAX_MT 8
 #endif
-// resident work-groups (two per CU)
-#ifndef BD_GEMM_SLOTS
-#define BD_GEMM_SLOTS 512
+// 16-column tiles per pass at 128-row tiles (4 or 8)
+#ifndef BD_GEMM_NTW_M128
+#define BD_GEMM_NTW_M128 4
 #endif
+constexpr int kCUs = 256;
+constexpr int kLdsPerCU = 160 * 1024;
 #ifndef BD_GEMM_MIN_CHUNKS
 #define BD_GEMM_MIN_CHUNKS 4
 #endif
 // Schedule cost model (ns, bytes per ns): a work-group's pipeline stage takes
-// at least STAGE_NS (two stages in flight against the memory latency), or
-// longer when the resident work-groups' stage bytes exceed what HBM (weight
-// tiles) and L2 (row tiles, empty weight slots) deliver; a K split adds a
-// reduction launch and its partial-sum traffic.
-#ifndef BD_GEMM_STAGE_NS
-#define BD_GEMM_STAGE_NS 700
+// at least LAT_NS / (NS - 1) (NS - 1 stages in flight against the memory
+// latency), or longer when the resident work-groups' stage bytes exceed what
+// HBM (weight tiles) and L2 (row tiles, empty weight slots) deliver; a K
+// split adds a reduction launch and its partial-sum traffic.
+#ifndef BD_GEMM_LAT_NS
+#define BD_GEMM_LAT_NS 1400
 #endif
 #ifndef BD_GEMM_HBM_BPNS
 #define BD_GEMM_HBM_BPNS 5000
@@ -474,7 +476,11 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
   // candidates: row tile (16 .. 64 rows, or 128 above 64 rows), K slices, and
   // the number of passes per work-group (work-groups = units / pass size)
   for (int MT = mt0; MT <= (mt > 4 && BD_GEMM_MAX_MT >= 8 ? 8 : mt0); MT *= 2) {
-    const int NTW = MT <= 2 ? 8 : 4;
+    const int NTW = MT <= 2 ? 8 : (MT == 8 ? BD_GEMM_NTW_M128 : 4);
+    // resident work-groups: at most two per CU, fewer when the stages fill the LDS
+    const int lds = kNS * 2 * (NTW + MT) * 1024;
+    const int per_cu = kLdsPerCU / lds >= 2 ? 2 : 1;
+    const int SLOTS = kCUs * per_cu;
     const int ny = (M + MT * 16 - 1) / (MT * 16);
     const int upp = NTW / G;  // units per pass
     for (int ks = 1; ks <= maxks; ++ks) {
@@ -486,10 +492,11 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
         const int passes = ((Tg + nwg - 1) / nwg * G + NTW - 1) / NTW;
         const double real = (double)T / ((double)nwg * passes);  // weight tiles per stage, on average
         const double per_wg = real * 2048.0 / BD_GEMM_HBM_BPNS + (MT + NTW - real) * 2048.0 / BD_GEMM_L2_BPNS;
-        const double resident = (double)(total < BD_GEMM_SLOTS ? total : BD_GEMM_SLOTS);
+        const double resident = (double)(total < SLOTS ? total : SLOTS);
         double stage = resident * per_wg;
-        stage = stage > BD_GEMM_STAGE_NS ? stage : BD_GEMM_STAGE_NS;
-        const double waves = (double)((total + BD_GEMM_SLOTS - 1) / BD_GEMM_SLOTS);
+        const double floor_ns = (double)BD_GEMM_LAT_NS / (kNS - 1);
+        stage = stage > floor_ns ? stage : floor_ns;
+        const double waves = (double)((total + SLOTS - 1) / SLOTS);
         double est = waves * passes * chunks * stage;
         if (ks > 1)
           est += BD_GEMM_RED_NS + (double)ks * M * T * 16 * 8 / BD_GEMM_PART_BPNS;
@@ -561,7 +568,9 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
       case 1: hipLaunchKernelGGL((gemm_stream_kernel<1, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
       case 2: hipLaunchKernelGGL((gemm_stream_kernel<2, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
       case 4: hipLaunchKernelGGL((gemm_stream_kernel<4, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
-      default: hipLaunchKernelGGL((gemm_stream_kernel<8, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+      default: hipLaunchKernelGGL((gemm_stream_kernel<8, BD_GEMM_NTW_M128>), grid, dim3(kThreads), 0, s, a, p.passes,
+                                  p.G);
+        break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
