@@ -102,6 +102,8 @@ class FullAttnDecoder:
                                                 np.arange(self.D)[None, :]).astype(np.int32).reshape(-1)))
 
     def _sync_block(self):
+        if self.block < 0:          # no block begun since the prompts were set
+            return
         lo = self.P + self.block * self.D
         self.tok_full[:, lo:lo + self.D].copy_(self.tok_blk)
         self.bits_full[:, lo // self.D].copy_(self.bits_blk)
