@@ -33,10 +33,6 @@ constexpr int kThreads = 256;
 #ifndef BD_GEMM_MAX_MT
 #define BD_GEMM_MAX_MT 8
 #endif
-// 16-column tiles per pass at 128-row tiles (4 or 8)
-#ifndef BD_GEMM_NTW_M128
-#define BD_GEMM_NTW_M128 4
-#endif
 constexpr int kCUs = 256;
 constexpr int kLdsPerCU = 160 * 1024;
 #ifndef BD_GEMM_MIN_CHUNKS
@@ -476,7 +472,7 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
   // candidates: row tile (16 .. 64 rows, or 128 above 64 rows), K slices, and
   // the number of passes per work-group (work-groups = units / pass size)
   for (int MT = mt0; MT <= (mt > 4 && BD_GEMM_MAX_MT >= 8 ? 8 : mt0); MT *= 2) {
-    const int NTW = MT <= 2 ? 8 : (MT == 8 ? BD_GEMM_NTW_M128 : 4);
+    const int NTW = MT <= 2 ? 8 : 4;
     // resident work-groups: at most two per CU, fewer when the stages fill the LDS
     const int lds = kNS * 2 * (NTW + MT) * 1024;
     const int per_cu = kLdsPerCU / lds >= 2 ? 2 : 1;
@@ -568,9 +564,7 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
       case 1: hipLaunchKernelGGL((gemm_stream_kernel<1, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
       case 2: hipLaunchKernelGGL((gemm_stream_kernel<2, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
       case 4: hipLaunchKernelGGL((gemm_stream_kernel<4, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
-      default: hipLaunchKernelGGL((gemm_stream_kernel<8, BD_GEMM_NTW_M128>), grid, dim3(kThreads), 0, s, a, p.passes,
-                                  p.G);
-        break;
+      default: hipLaunchKernelGGL((gemm_stream_kernel<8, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

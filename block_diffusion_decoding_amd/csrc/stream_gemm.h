@@ -150,31 +150,6 @@ __device__ __forceinline__ void lds_frags_kstep<2, 4>(uint32_t xa, uint32_t wa, 
 }
 
 template <>
-__device__ __forceinline__ void lds_frags_kstep<2, 8>(uint32_t xa, uint32_t wa, uint4 (&x)[2], uint4 (&w)[8]) {
-  u32x4_t r[10];
-  asm volatile(
-      "ds_read_b128 %0, %10\n\t"
-      "ds_read_b128 %1, %10 offset:2048\n\t"
-      "ds_read_b128 %2, %11\n\t"
-      "ds_read_b128 %3, %11 offset:2048\n\t"
-      "ds_read_b128 %4, %11 offset:4096\n\t"
-      "ds_read_b128 %5, %11 offset:6144\n\t"
-      "ds_read_b128 %6, %11 offset:8192\n\t"
-      "ds_read_b128 %7, %11 offset:10240\n\t"
-      "ds_read_b128 %8, %11 offset:12288\n\t"
-      "ds_read_b128 %9, %11 offset:14336\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
-        "=&v"(r[8]), "=&v"(r[9])
-      : "v"(xa), "v"(wa)
-      : "memory");
-  x[0] = as_uint4(r[0]);
-  x[1] = as_uint4(r[1]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = as_uint4(r[2 + j]);
-}
-
-template <>
 __device__ __forceinline__ void lds_frags_kstep<2, 2>(uint32_t xa, uint32_t wa, uint4 (&x)[2], uint4 (&w)[2]) {
   u32x4_t r[4];
   asm volatile(
