@@ -44,6 +44,8 @@ SIGNATURES = {
     "bd_candidate_rows": (c_int, [c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "bd_threshold_unmask": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_float,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "bd_threshold_unmask_tau": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "bd_kv_append": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_int, c_int, c_void_p]),
     "bd_embed_rows": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,

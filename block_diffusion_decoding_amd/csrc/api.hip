@@ -167,7 +167,18 @@ bd_status bd_threshold_unmask(int B, int D, int win_lo, int win_len, const float
   if (B == 0) return BD_OK;
   if (D < 1 || D > 64 || win_lo < 0 || win_len < 1 || win_len > 64 || win_lo + win_len > D) return BD_EINVAL;
   if (!conf || !argmax || !tokens || !mask_bits || !(threshold == threshold)) return BD_EINVAL;
-  return hip_status(bd_unmask_launch(B, D, win_lo, win_len, conf, argmax, threshold, tokens, mask_bits,
+  return hip_status(bd_unmask_launch(B, D, win_lo, win_len, conf, argmax, threshold, nullptr, tokens, mask_bits,
+                                     n_unmasked, unmasked_pos, static_cast<hipStream_t>(stream)));
+}
+
+bd_status bd_threshold_unmask_tau(int B, int D, int win_lo, int win_len, const float* conf, const int32_t* argmax,
+                                  const float* threshold, int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
+                                  int32_t* unmasked_pos, void* stream) {
+  if (B < 0) return BD_EINVAL;
+  if (B == 0) return BD_OK;
+  if (D < 1 || D > 64 || win_lo < 0 || win_len < 1 || win_len > 64 || win_lo + win_len > D) return BD_EINVAL;
+  if (!conf || !argmax || !tokens || !mask_bits || !threshold) return BD_EINVAL;
+  return hip_status(bd_unmask_launch(B, D, win_lo, win_len, conf, argmax, 0.f, threshold, tokens, mask_bits,
                                      n_unmasked, unmasked_pos, static_cast<hipStream_t>(stream)));
 }
 

@@ -124,9 +124,9 @@ hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, i
 
 // ---- unmask / append ---------------------------------------------------------
 hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* conf,
-                            const int32_t* argmax, float threshold, int32_t* tokens,
-                            uint64_t* mask_bits, int32_t* n_unmasked, int32_t* unmasked_pos,
-                            hipStream_t s);
+                            const int32_t* argmax, float threshold, const float* threshold_dev,
+                            int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
+                            int32_t* unmasked_pos, hipStream_t s);
 
 hipError_t bd_append_launch(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache,
                             void* v_cache, int32_t* kv_len, const void* k_blk, const void* v_blk,

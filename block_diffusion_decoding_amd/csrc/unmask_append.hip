@@ -20,11 +20,12 @@
 namespace {
 
 __global__ __launch_bounds__(64) void unmask_kernel(int D, int win_lo, int win_len, const float* conf,
-                                                    const int32_t* argmax, float thr, int32_t* tokens,
-                                                    uint64_t* mask_bits, int32_t* n_unmasked,
+                                                    const int32_t* argmax, float thr, const float* thr_dev,
+                                                    int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
                                                     int32_t* unmasked_pos) {
   const int b = blockIdx.x;
   const int r = threadIdx.x;
+  if (thr_dev != nullptr) thr = thr_dev[b];  // per-sequence threshold from device memory
   const int pos = win_lo + r;
   const uint64_t bits = mask_bits[b];
   const bool cand = r < win_len && ((bits >> pos) & 1ull);
@@ -121,10 +122,10 @@ hipError_t bd_candidates_launch(int B, int win_lo, int win_len, const uint64_t* 
 }
 
 hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* conf, const int32_t* argmax,
-                            float threshold, int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
-                            int32_t* unmasked_pos, hipStream_t s) {
-  hipLaunchKernelGGL(unmask_kernel, dim3(B), dim3(64), 0, s, D, win_lo, win_len, conf, argmax, threshold, tokens,
-                     mask_bits, n_unmasked, unmasked_pos);
+                            float threshold, const float* threshold_dev, int32_t* tokens, uint64_t* mask_bits,
+                            int32_t* n_unmasked, int32_t* unmasked_pos, hipStream_t s) {
+  hipLaunchKernelGGL(unmask_kernel, dim3(B), dim3(64), 0, s, D, win_lo, win_len, conf, argmax, threshold,
+                     threshold_dev, tokens, mask_bits, n_unmasked, unmasked_pos);
   return hipGetLastError();
 }
 

@@ -282,11 +282,13 @@ class BlockDecoder:
         self.kv_len_host = self.kv_len_host + P
 
     # ---------------------------------------------------------------- graphs
-    def capture(self, S: int, tau: float):
+    def capture(self, S: int, tau):
         """Capture the exact and DualCache step of every window and the commit
         as HIP graphs (through torch's graph API).  Every buffer and workspace
         the steps touch is sized first, so replays allocate nothing; a plant
-        buffer always exists (zeros when nothing is planted)."""
+        buffer always exists (zeros when nothing is planted).  tau: a float
+        (fixed in the graphs) or a [B] fp32 device tensor whose values the
+        replays read (a threshold schedule without re-capture)."""
         dm = self.dims
         B, D = dm.B, dm.D
         if self.plant is None:
@@ -327,9 +329,15 @@ class BlockDecoder:
 
     def _replay(self, kind: str, s: int, S: int, tau: float) -> bool:
         g = self.graphs.get((kind, s))
-        if g is None or self.lm_events is not None or (kind != "commit" and
-                                                        (S, tau) != (self._graph_S, self._graph_tau)):
+        if g is None or self.lm_events is not None:
             return False
+        if kind != "commit":
+            # a threshold tensor is read by the replayed kernels: the same
+            # tensor (whatever values it holds now) matches the capture
+            same_tau = (tau is self._graph_tau) if isinstance(tau, torch.Tensor) or \
+                isinstance(self._graph_tau, torch.Tensor) else tau == self._graph_tau
+            if S != self._graph_S or not same_tau:
+                return False
         g.replay()
         if kind != "commit":
             self.last = self._window(s, S)

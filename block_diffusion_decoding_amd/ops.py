@@ -150,10 +150,17 @@ def bd_candidate_rows(mask_bits, row_idx, out_pos, count, *, win_lo, win_len, ro
 
 def bd_threshold_unmask(conf, argmax, tokens, mask_bits, *, win_lo, threshold, n_unmasked=None,
                         unmasked_pos=None, stream=None):
-    """conf/argmax [B, win_len]; tokens [B, D] int32; mask_bits [B] (64-bit)."""
+    """conf/argmax [B, win_len]; tokens [B, D] int32; mask_bits [B] (64-bit);
+    threshold: a float, or a [B] fp32 device tensor read when the kernel runs."""
     lib = _lib.load()
     B, win_len = conf.shape
     D = tokens.shape[1]
+    if isinstance(threshold, torch.Tensor):
+        assert threshold.dtype == torch.float32 and threshold.numel() == B
+        st = lib.bd_threshold_unmask_tau(B, D, win_lo, win_len, _p(conf), _p(argmax), _p(threshold), _p(tokens),
+                                         _p(mask_bits), _p(n_unmasked), _p(unmasked_pos), _stream(stream))
+        _check("bd_threshold_unmask_tau", st)
+        return
     st = lib.bd_threshold_unmask(B, D, win_lo, win_len, _p(conf), _p(argmax), float(threshold), _p(tokens),
                                  _p(mask_bits), _p(n_unmasked), _p(unmasked_pos), _stream(stream))
     _check("bd_threshold_unmask", st)

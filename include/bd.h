@@ -208,6 +208,16 @@ bd_status bd_threshold_unmask(int B, int D, int win_lo, int win_len,
                               int32_t* tokens, uint64_t* mask_bits,
                               int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
 
+/* The same rule with a per-sequence threshold read from device memory
+ * (threshold [B] fp32) when the kernel runs: a captured step graph can then
+ * follow a threshold schedule (the pages leave adaptive thresholds to future
+ * work; the value is the caller's).  A NaN threshold passes no candidate
+ * (the fallback still unmasks one). */
+bd_status bd_threshold_unmask_tau(int B, int D, int win_lo, int win_len,
+                                  const float* conf, const int32_t* argmax, const float* threshold,
+                                  int32_t* tokens, uint64_t* mask_bits,
+                                  int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
+
 /* ------------------------------------------------------------------------
  * bd_kv_append -- commit a finished block to the block-level cache ([v2
  * notes] Key design 3: a decoded block's K/V become read-only context; [v2

@@ -31,7 +31,7 @@ def test_header_declares_the_four_calls_and_support():
               "bd_linear_workspace_size", "bd_qkv_proj_workspace_size",
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
               "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu",
-              "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll"]:
+              "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau"]:
         assert n in names
 
 
@@ -232,3 +232,12 @@ def test_training_form_argument_errors():
     nl = lambda **k: lib.bd_masked_nll(1, k.get("M", 10), k.get("hid", 1536), 151936, FAKE, 100, FAKE, FAKE,
                                        k.get("tg", FAKE), FAKE, FAKE, None, None)
     assert nl(hid=1530) == U and nl(tg=None) == E and nl(M=0) == 0
+
+
+def test_device_threshold_unmask_argument_errors():
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    call = lambda **k: lib.bd_threshold_unmask_tau(k.get("B", 4), k.get("D", 32), k.get("lo", 8), 8, FAKE, FAKE,
+                                                   k.get("tau", FAKE), FAKE, FAKE, None, None, None)
+    assert call(tau=None) == E and call(D=65) == E and call(lo=30) == E and call(B=-1) == E
+    assert call(B=0) == 0

@@ -201,6 +201,32 @@ def test_threshold_unmask(D, S, win, tau):
     assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(pos.cpu().numpy(), rp)
 
 
+@pytest.mark.parametrize("D,S,win", [(32, 8, 1), (64, 64, 0)])
+def test_threshold_unmask_per_sequence_threshold(D, S, win):
+    """Thresholds read from device memory, one per sequence (NaN passes
+    nothing): each sequence decides as the oracle does with its own value."""
+    say(f"[unmask] per-sequence thresholds D={D} S={S}")
+    B = 24
+    rng = np.random.default_rng(D + S + win)
+    conf = rng.choice(np.array([0.05, 0.3, 0.5, 0.9, 0.95, 0.99], np.float32), size=(B, S)).astype(np.float32)
+    am = rng.integers(0, 150000, size=(B, S)).astype(np.int32)
+    masked = rng.random((B, D)) < 0.6
+    tokens = np.where(masked, 0, rng.integers(0, 150000, size=(B, D))).astype(np.int32)
+    taus = rng.choice(np.array([0.3, 0.5, 0.9, 1.0, np.nan], np.float32), size=B).astype(np.float32)
+    t_tok, t_bits = up(tokens), up(bi.mask_bits(masked).view(np.int64))
+    n = torch.zeros(B, dtype=torch.int32, device=DEV)
+    pos = torch.zeros(B, S, dtype=torch.int32, device=DEV)
+    ops().bd_threshold_unmask(up(conf), up(am), t_tok, t_bits, win_lo=win * S, threshold=up(taus),
+                              n_unmasked=n, unmasked_pos=pos)
+    got_bits = bi.bits_to_mask(t_bits.cpu().numpy().view(np.uint64), D)
+    for b in range(B):
+        rt, rm, rn, rp = R.batch_threshold_unmask(conf[b:b + 1], am[b:b + 1], tokens[b:b + 1], masked[b:b + 1],
+                                                  win * S, taus[b])
+        assert np.array_equal(t_tok.cpu().numpy()[b], rt[0]), f"sequence {b} (tau {taus[b]})"
+        assert np.array_equal(got_bits[b], rm[0])
+        assert n.cpu().numpy()[b] == rn[0] and np.array_equal(pos.cpu().numpy()[b], rp[0])
+
+
 # --------------------------------------------------------------------------
 # bd_kv_append (bit-exact) and capacity
 # --------------------------------------------------------------------------

@@ -61,3 +61,35 @@ def test_captured_steps_replay_like_eager():
         for a, b in zip(state(eager), state(graph)):
             assert torch.equal(a, b), f"commit of block {blk} differs"
     assert n_cmp == 2 * (cfg.D // S) * 3
+
+
+def test_captured_steps_follow_a_device_threshold_schedule():
+    """Graphs captured with a threshold tensor replay with the values it holds
+    at each replay: a schedule (here lowered every step, one value per
+    sequence) gives the same results as eager steps with those thresholds."""
+    say("[graphs] device threshold schedule")
+    cfg = MID
+    w, pre, st, _, _ = workload(cfg, 0, all_masked=True, plant_rate=None)
+    eager = gpu_decoder(cfg, w, pre, st)
+    graph = gpu_decoder(cfg, w, pre, st)
+    S = cfg.S
+    tau_dev = torch.full((cfg.B,), 0.9, dtype=torch.float32, device="cuda")
+    graph.capture(S, tau_dev)
+    plant = bi.normal(3, "plant", (cfg.B, cfg.D, cfg.hidden), 0.5, "bf16")
+    for d in (eager, graph):
+        d.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plant)
+    step = 0
+    for s in range(cfg.D // S):
+        for k in range(3):
+            kind = "E" if k == 0 else "DC"
+            taus = np.float32(0.9 - 0.1 * step) + np.float32(0.05) * np.arange(cfg.B, dtype=np.float32)
+            tau_e = torch.from_numpy(taus).cuda()
+            (eager.e_step if kind == "E" else eager.dc_step)(s, S, tau_e, eager=True)
+            torch.cuda.synchronize()
+            tau_dev.copy_(torch.from_numpy(taus))
+            (graph.e_step if kind == "E" else graph.dc_step)(s, S, tau_dev)
+            torch.cuda.synchronize()
+            for a, b in zip(state(eager), state(graph)):
+                assert torch.equal(a, b), f"window {s} step {k} ({kind}) differs"
+            step += 1
+    assert len(graph.graphs) > 0
