@@ -91,3 +91,39 @@ def test_masked_nll_flags_invalid_rows_and_targets():
     hf = down(h).astype(np.float64)
     wf = down(w).astype(np.float64)
     np.testing.assert_allclose(got[:2], [-(hf[0] @ wf[3]), -(hf[5] @ wf[99])], rtol=1e-5, atol=1e-5)
+
+
+def test_train_attn_full_size_sampled():
+    """The benchmark's shape (4 samples x L 2048 in both views = 8 sequences
+    of 4096 rows, 12q/2kv heads d 128), in the benchmark's launch
+    configuration, on 48 sampled (sequence, row, head) outputs computed one
+    by one in fp64 over the keys the 2L mask lets that row see."""
+    cfg = bi.T3
+    say("[train] attention full size, sampled")
+    o = ops()
+    S2, L, D, Hq, Hkv, d = 2 * cfg.S, cfg.L, cfg.D, cfg.Hq, cfg.Hkv, cfg.d
+    g = torch.Generator(device=DEV)
+    g.manual_seed(21)
+    q = torch.randn(S2, 2 * L, Hq, d, generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn(S2, 2 * L, Hkv, d, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(S2, 2 * L, Hkv, d, generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.zeros_like(q)
+    o.bd_train_attn(q, k, v, out, L=L, D=D)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(21)
+    samples = [(int(rng.integers(S2)), int(rng.integers(2 * L)), int(rng.integers(Hq))) for _ in range(44)]
+    samples += [(0, 0, 0), (1, L - 1, 5), (S2 - 1, L, 11), (S2 - 1, 2 * L - 1, 3)]   # block edges
+    for s, p, h in samples:
+        b = (p % L) // D
+        if p < L:   # noisy: own noisy block, clean blocks < b
+            keys = np.concatenate([np.arange(b * D, (b + 1) * D), L + np.arange(b * D)])
+        else:       # clean: clean blocks <= b
+            keys = L + np.arange((b + 1) * D)
+        kvh = h // (Hq // Hkv)
+        qv = q[s, p, h].float().cpu().numpy().astype(np.float64)
+        K = k[s, keys, kvh].float().cpu().numpy().astype(np.float64)
+        V = v[s, keys, kvh].float().cpu().numpy().astype(np.float64)
+        sc = K @ qv / np.sqrt(d)
+        pr = np.exp(sc - sc.max())
+        ref = (pr / pr.sum()) @ V
+        rows_close(out[s, p, h].float().cpu().numpy()[None], ref[None], TOL["bf16"], f"sequence {s} row {p} head {h}")

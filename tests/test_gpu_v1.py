@@ -61,3 +61,32 @@ def test_v1_generation_teacher_forced(case, mode):
     got_tokens = dec.tokens_host()
     for b, q in enumerate(seqs):
         assert np.array_equal(got_tokens[b], q.tokens.astype(np.int32))
+
+
+def test_whole_sequence_attention_at_the_benchmark_shape_sampled():
+    """The refresh pass of the v1 benchmark (4 sequences of 512 positions,
+    12q/2kv heads d 128: one block spanning the sequence, no cache) on sampled
+    (sequence, row, head) outputs computed one by one in fp64 over all keys."""
+    from block_diffusion_decoding_amd import ops
+    say("[v1] whole-sequence attention, sampled")
+    B, T, Hq, Hkv, d = 4, 512, 12, 2, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(22)
+    q = torch.randn(B, T, Hq, d, generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn(B, T, Hkv, d, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(B, T, Hkv, d, generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.zeros_like(q)
+    ops.bd_block_attn(q, None, None, torch.zeros(B, dtype=torch.int32, device=DEV), k, v, out, D=T, q_off=0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(22)
+    for s, p, h in [(int(rng.integers(B)), int(rng.integers(T)), int(rng.integers(Hq))) for _ in range(32)]:
+        kvh = h // (Hq // Hkv)
+        qv = q[s, p, h].float().cpu().numpy().astype(np.float64)
+        K = k[s, :, kvh].float().cpu().numpy().astype(np.float64)
+        V = v[s, :, kvh].float().cpu().numpy().astype(np.float64)
+        sc = K @ qv / np.sqrt(d)
+        pr = np.exp(sc - sc.max())
+        ref = (pr / pr.sum()) @ V
+        got = out[s, p, h].float().cpu().numpy().astype(np.float64)
+        err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert err <= TOL["bf16"], f"sequence {s} row {p} head {h}: rel err {err:.3g}"
