@@ -53,6 +53,8 @@ SIGNATURES = {
     "bd_linear_workspace_size": (c_size_t, [c_int] * 4),
     "bd_linear": (c_int, [c_int, c_int, c_int, c_int, c_void_p, BdRows, c_void_p,
                           c_void_p, BdRows, c_void_p, BdRows, c_void_p, c_size_t, c_void_p]),
+    "bd_linear_residual_rmsnorm": (c_int, [c_int, c_int, c_int, c_int, c_void_p, BdRows, c_void_p, c_void_p,
+                                           BdRows, c_float, c_void_p, BdRows, c_void_p, c_size_t, c_void_p]),
     "bd_qkv_proj_workspace_size": (c_size_t, [c_int] * 5),
     "bd_qkv_proj": (c_int, [c_int, c_int, c_int, c_void_p, BdRows,
                             c_void_p, c_int, c_void_p, BdRows,

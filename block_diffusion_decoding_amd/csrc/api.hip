@@ -216,7 +216,8 @@ bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int 
 }
 
 static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const BdGemmSeg* segs, int nseg,
-                             int mode, const BdGemmRope* rope, void* workspace, size_t ws_bytes, void* stream) {
+                             int mode, const BdGemmRope* rope, const BdGemmNorm* post_norm, void* workspace,
+                             size_t ws_bytes, void* stream) {
   if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
   if (M == 0) return BD_OK;
   if (K <= 0 || !x || !valid_rows(xr)) return BD_EINVAL;
@@ -240,7 +241,7 @@ static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows x
   const BdGemmPlan p = bd_gemm_plan(dt, M, K, N, nseg, mode);
   if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)))
     return BD_EINVAL;
-  return hip_status(bd_gemm_launch(dt, p, M, K, x, xr, segs, nseg, mode, rope, workspace,
+  return hip_status(bd_gemm_launch(dt, p, M, K, x, xr, segs, nseg, mode, rope, post_norm, workspace,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -264,7 +265,16 @@ size_t bd_qkv_proj_rope_workspace_size(bd_dtype dt, int M, int K, int Nq, int Nk
 bd_status bd_linear(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr, const void* w, const void* res,
                     bd_rows rr, void* y, bd_rows yr, void* workspace, size_t ws_bytes, void* stream) {
   BdGemmSeg seg{w, y, yr, res, rr, N};
-  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_PLAIN, nullptr, workspace, ws_bytes, stream);
+  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_PLAIN, nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+bd_status bd_linear_residual_rmsnorm(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr, const void* w,
+                                     void* y, bd_rows yr, float eps, void* h, bd_rows hr, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  if (!h || !valid_rows(hr) || !(eps >= 0.f)) return BD_EINVAL;
+  BdGemmSeg seg{w, y, yr, y, yr, N};
+  const BdGemmNorm norm{h, hr, eps};
+  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_PLAIN, nullptr, &norm, workspace, ws_bytes, stream);
 }
 
 bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,
@@ -273,7 +283,7 @@ bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, cons
   const bd_rows none{1, 1, 0};
   BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
                        {wv, v, vr, nullptr, none, Nkv}};
-  return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_PLAIN, nullptr, workspace, ws_bytes, stream);
+  return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_PLAIN, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
 bd_status bd_qkv_proj_rope(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,
@@ -284,14 +294,14 @@ bd_status bd_qkv_proj_rope(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
   BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
                        {wv, v, vr, nullptr, none, Nkv}};
   const BdGemmRope rope{pos_base, n_rows, pos_off, d, theta};
-  return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_ROPE, &rope, workspace, ws_bytes, stream);
+  return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_ROPE, &rope, nullptr, workspace, ws_bytes, stream);
 }
 
 bd_status bd_gate_up_swiglu(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* w_gu, int inter,
                             void* a, bd_rows ar, void* stream) {
   const bd_rows none{1, 1, 0};
   BdGemmSeg seg{w_gu, a, ar, nullptr, none, inter};
-  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_SWIGLU, nullptr, nullptr, 0, stream);
+  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_SWIGLU, nullptr, nullptr, nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -114,9 +114,17 @@ struct BdGemmPlan {
 
 BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int mode);
 
+// RMSNorm (unit gains) of a one-segment projection's output rows, after the
+// residual: h[hr(m)] = y[yr(m)] / sqrt(mean y^2 + eps).
+struct BdGemmNorm {
+  void* h;
+  bd_rows hr;
+  float eps;
+};
+
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
-                          const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope, void* workspace,
-                          hipStream_t s);
+                          const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope,
+                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s);
 
 hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
                            const void* E, const int32_t* tokens, const uint64_t* mask_bits,

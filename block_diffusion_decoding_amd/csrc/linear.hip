@@ -374,6 +374,75 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_reduce(GemmS a) {
     if (col + e < N) yrow[col + e] = (uint16_t)bd_f2bf(lo[e]);
 }
 
+// K-split reduction of a one-segment projection fused with the residual and
+// the RMSNorm that follows it in a pre-norm layer:
+//   y[yr(m)] = sum over slices of part[z][m] + res[rr(m)]   (stored in bf16)
+//   h[hr(m)] = y[yr(m)] / sqrt(mean y^2 + eps)             (of the stored y)
+// One work-group per row; thread t holds the 4-column groups t, t + 256, ...
+// (rows up to kNormGroups * 1024 columns).  The row's sum of squares is added
+// in a fixed order (wave sums, then the waves in order).
+constexpr int kNormGroups = 4;
+__global__ __launch_bounds__(kThreads) void gemm_reduce_norm(GemmS a, float eps, uint16_t* h, bd_rows hr) {
+  __shared__ float red[kThreads / 64];
+  const int m = blockIdx.x;
+  const int N = a.N[0];
+  const size_t Nt = (size_t)a.tb[a.nseg] * 16;
+  const size_t zs = (size_t)a.M * Nt;
+  const float* prow = a.part + (size_t)m * Nt;
+  const uint16_t* rrow = a.res[0] ? a.res[0] + (size_t)bd_map_row(a.rr[0], m) * N : nullptr;
+  uint16_t* yrow = a.y[0] + (size_t)bd_map_row(a.yr[0], m) * N;
+  float v[kNormGroups][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int g = 0; g < kNormGroups; ++g) {
+    const int col = (g * kThreads + (int)threadIdx.x) * 4;
+    if (col >= N) continue;
+    const float* p = prow + col;
+    float4 acc = *reinterpret_cast<const float4*>(p);
+    int zz = 1;
+    for (; zz + 3 < a.ksplit; zz += 4) {  // slices in order, four loads in flight
+      float4 t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t[u] = *reinterpret_cast<const float4*>(p + (zz + u) * zs);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc.x += t[u].x, acc.y += t[u].y, acc.z += t[u].z, acc.w += t[u].w;
+    }
+    for (; zz < a.ksplit; ++zz) {
+      const float4 t = *reinterpret_cast<const float4*>(p + zz * zs);
+      acc.x += t.x, acc.y += t.y, acc.z += t.z, acc.w += t.w;
+    }
+    v[g][0] = acc.x, v[g][1] = acc.y, v[g][2] = acc.z, v[g][3] = acc.w;
+    if (rrow) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[g][e] += bd_bf2f(rrow[col + e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[g][e] = bd_bf2f(bd_f2bf(v[g][e]));  // the stored value is what gets normalised
+      ss += v[g][e] * v[g][e];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
+  const float inv = 1.f / __builtin_sqrtf(tot / (float)N + eps);
+  uint16_t* hrow = h + (size_t)bd_map_row(hr, m) * N;
+#pragma unroll
+  for (int g = 0; g < kNormGroups; ++g) {
+    const int col = (g * kThreads + (int)threadIdx.x) * 4;
+    if (col >= N) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      yrow[col + e] = (uint16_t)bd_f2bf(v[g][e]);
+      hrow[col + e] = (uint16_t)bd_f2bf(v[g][e] * inv);
+    }
+  }
+}
+
 struct GemmF {
   const float* x;
   bd_rows xr;
@@ -518,8 +587,12 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
 }
 
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
-                          const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope, void* workspace,
-                          hipStream_t s) {
+                          const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope,
+                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s) {
+  // the RMSNorm after a one-segment projection rides on its K-split reduction
+  // when there is one and the row fits a work-group's registers
+  const bool fused_norm = post_norm != nullptr && dt == BD_BF16 && nseg == 1 && p.ksplit > 1 &&
+                          segs[0].N % 4 == 0 && segs[0].N <= kNormGroups * kThreads * 4;
   if (dt == BD_F32) {
     for (int i = 0; i < nseg; ++i) {
       GemmF a{static_cast<const float*>(x), xr, M, K, static_cast<const float*>(segs[i].w),
@@ -568,13 +641,21 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (fused_norm) {
+      hipLaunchKernelGGL(gemm_reduce_norm, dim3(M), dim3(kThreads), 0, s, a, post_norm->eps,
+                         static_cast<uint16_t*>(post_norm->h), post_norm->hr);
+      return hipGetLastError();
+    }
     if (p.ksplit > 1) {
       const size_t n = (size_t)M * p.T * 4;
       hipLaunchKernelGGL(gemm_stream_reduce, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
                          a);
-      return hipGetLastError();
+      hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess || post_norm == nullptr) return e2;
     }
   }
+  if (post_norm != nullptr && !fused_norm)
+    return bd_rmsnorm_launch(dt, M, segs[0].N, segs[0].y, segs[0].yr, post_norm->eps, post_norm->h, post_norm->hr, s);
   // rotary embedding as its own pass where the projection had no reduction
   if (mode == BD_GEMM_ROPE && (dt == BD_F32 || p.ksplit == 1)) {
     for (int i = 0; i < 2 && i < nseg; ++i) {

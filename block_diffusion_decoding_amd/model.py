@@ -69,28 +69,40 @@ class ModelDecoder(BlockDecoder):
         self.act = torch.zeros(B * D, I, dtype=dt, device=dev)
 
     # ------------------------------------------------------------------ layers
-    def _layers(self, X, h, q, o, a, M, n, lo, kr, attn_kv, layer_ids):
+    def _layers(self, X, h, q, o, a, M, n, lo, kr, attn_kv, layer_ids, final=None):
         """Layers ``layer_ids`` over M = B*n fresh rows X (block rows
         lo .. lo+n-1 of every sequence), the residual stream, updated in
         place.  attn_kv(l) gives layer l's (k_cache, v_cache, kv_len, k_blk,
         v_blk); the fresh K/V go to rows kr of k_blk/v_blk, rotated at
-        positions kv_len[b] + lo + i."""
+        positions kv_len[b] + lo + i.  h holds rmsnorm(X) for the next
+        sublayer: each projection into the residual stream also normalises
+        its result (bd_linear_residual_rmsnorm).  After the last layer that
+        norm goes to ``final`` = (buffer, row map) when given (the final
+        RMSNorm in front of the LM head), else it is not taken."""
         dm = self.dims
-        for l in layer_ids:
+        ids = list(layer_ids)
+        ops.bd_rmsnorm(X, dense(M), h, dense(M), M=M, eps=dm.eps)
+        for idx, l in enumerate(ids):
             lw = self.layers[l]
             kc, vc, kvl, kb, vb = attn_kv(l)
-            ops.bd_rmsnorm(X, dense(M), h, dense(M), M=M, eps=dm.eps)
             ops.bd_qkv_proj_rope(h, dense(M), lw["Wq"], q, dense(M), lw["Wk"], lw["Wv"], kb, kr, vb, kr, kvl, M=M,
                                  d=dm.d, n_rows=n, pos_off=lo, theta=dm.theta)
             ops.bd_block_attn(q, kc, vc, kvl, kb, vb, o, D=dm.D, q_off=lo)
-            ops.bd_linear(o, dense(M), lw["Wo"], X, dense(M), M=M, res=X, rr=dense(M))
-            ops.bd_rmsnorm(X, dense(M), h, dense(M), M=M, eps=dm.eps)
+            ops.bd_linear_residual_rmsnorm(o, dense(M), lw["Wo"], X, dense(M), h, dense(M), M=M, eps=dm.eps)
             ops.bd_gate_up_swiglu(h, dense(M), lw["Wgu"], a, dense(M), M=M)
-            ops.bd_linear(a, dense(M), lw["Wd"], X, dense(M), M=M, res=X, rr=dense(M))
+            if idx < len(ids) - 1:
+                ops.bd_linear_residual_rmsnorm(a, dense(M), lw["Wd"], X, dense(M), h, dense(M), M=M, eps=dm.eps)
+            elif final is not None:
+                ops.bd_linear_residual_rmsnorm(a, dense(M), lw["Wd"], X, dense(M), final[0], final[1], M=M,
+                                               eps=dm.eps)
+            else:
+                ops.bd_linear(a, dense(M), lw["Wd"], X, dense(M), M=M, res=X, rr=dense(M))
 
-    def _forward_block_rows(self, lo: int, n: int):
+    def _forward_block_rows(self, lo: int, n: int, final=None):
         """Block rows [lo, lo + n) of every sequence through all layers;
-        returns the residual stream X [B, n, hidden] after the last layer."""
+        returns the residual stream X [B, n, hidden] after the last layer
+        (with ``final`` = (buffer, row map) the final RMSNorm is written
+        there on the way)."""
         dm = self.dims
         B, D = dm.B, dm.D
         M = B * n
@@ -100,17 +112,15 @@ class ModelDecoder(BlockDecoder):
         ops.bd_embed_rows(self.W["E"], self.tokens, self.mask_bits, X, row_off=lo, n_rows=n)
         self._layers(X, self.hbuf, q, o, self.act, M, n, lo, rows(n, D, lo),
                      lambda l: (self.cache_k[l], self.cache_v[l], self.kv_len[l], self.blk_k[l], self.blk_v[l]),
-                     range(dm.n_layers))
+                     range(dm.n_layers), final)
         return X
 
     # ------------------------------------------------------------------ steps
     def e_step(self, s: int, S: int, tau: float, eager: bool = False):
         """Exact step for window s; refreshes every layer's DualCache snapshot."""
         if eager or not self._replay("E", s, S, tau):
-            dm = self.dims
-            B, D = dm.B, dm.D
-            X = self._forward_block_rows(0, D)
-            ops.bd_rmsnorm(X, dense(B * D), self.H, rows(D, 1 + D, 1), M=B * D, eps=dm.eps)
+            D = self.dims.D
+            self._forward_block_rows(0, D, final=(self.H, rows(D, 1 + D, 1)))
             self._lm_and_unmask(s, S, tau)
         if not self._capturing:
             self._step_done()
@@ -119,10 +129,8 @@ class ModelDecoder(BlockDecoder):
         """DualCache step for window s (every layer's snapshot rows outside the
         window; the row feeding the window's first position stays in H)."""
         if eager or not self._replay("DC", s, S, tau):
-            dm = self.dims
-            B, D = dm.B, dm.D
-            X = self._forward_block_rows(s * S, S)
-            ops.bd_rmsnorm(X, dense(B * S), self.H, rows(S, 1 + D, 1 + s * S), M=B * S, eps=dm.eps)
+            D = self.dims.D
+            self._forward_block_rows(s * S, S, final=(self.H, rows(S, 1 + D, 1 + s * S)))
             self._lm_and_unmask(s, S, tau)
         if not self._capturing:
             self._step_done()

@@ -215,6 +215,18 @@ def bd_linear(x, xr, w, y, yr, *, M, res=None, rr=None, ws=None, stream=None):
     _check("bd_linear", st)
 
 
+def bd_linear_residual_rmsnorm(x, xr, w, y, yr, h, hr, *, M, eps, ws=None, stream=None):
+    """y[yr(m)] += x[xr(m)] w^T, then h[hr(m)] = rmsnorm(y[yr(m)]) (unit gains)."""
+    lib = _lib.load()
+    N, K = w.shape
+    dt = _dt(w)
+    if ws is None:
+        ws = workspace(lib.bd_linear_workspace_size(dt, M, N, K), w.device, "gemm")
+    st = lib.bd_linear_residual_rmsnorm(dt, M, N, K, _p(x), xr, _p(w), _p(y), yr, float(eps), _p(h), hr, _p(ws),
+                                        ws.numel(), _stream(stream))
+    _check("bd_linear_residual_rmsnorm", st)
+
+
 def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, ws=None, stream=None):
     """q[qr(m)] = x[xr(m)] wq^T, k[kr(m)] = x[xr(m)] wk^T, v[vr(m)] = x[xr(m)] wv^T."""
     lib = _lib.load()

@@ -265,6 +265,19 @@ bd_status bd_linear(bd_dtype dt, int M, int N, int K,
                     const void* res, bd_rows rr, void* y, bd_rows yr,
                     void* workspace, size_t ws_bytes, void* stream);
 
+/* A projection into the residual stream followed by the RMSNorm of the
+ * result (a pre-norm layer's output projection or down projection and the
+ * norm in front of the next sublayer):
+ *   y[yr(m)] += x[xr(m)] W^T                     (y: residual stream, in place)
+ *   h[hr(m)]  = y[yr(m)] / sqrt(mean_k y^2 + eps)  (unit gains, of the stored y)
+ * Where K is split, the norm is taken by the reduction kernel (one
+ * work-group per row, bf16, N % 4 == 0 and N <= 4096); otherwise a RMSNorm
+ * pass follows.  h must not overlap y.  Workspace: bd_linear_workspace_size. */
+bd_status bd_linear_residual_rmsnorm(bd_dtype dt, int M, int N, int K,
+                                     const void* x, bd_rows xr, const void* w,
+                                     void* y, bd_rows yr, float eps, void* h, bd_rows hr,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
 /* The three input projections of one attention layer in one launch:
  *   q[qr(m)] = x[xr(m)] Wq^T  (Nq columns), k[kr(m)] = x[xr(m)] Wk^T and
  *   v[vr(m)] = x[xr(m)] Wv^T  (Nkv columns each).  Workspace as bd_linear. */

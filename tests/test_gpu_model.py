@@ -138,6 +138,32 @@ def test_gate_up_swiglu_matches_projections_then_gate(dtype, M, K, inter):
     assert not got[:2].any() and not got[2 + M:].any()
 
 
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 128, 1536, 1536), ("bf16", 128, 1536, 8960),
+                                         ("bf16", 512, 1536, 8960), ("bf16", 8, 1536, 1536),
+                                         ("bf16", 100, 4608, 512), ("bf16", 256, 8192, 512), ("f32", 9, 256, 512)])
+def test_linear_residual_rmsnorm(dtype, M, N, K):
+    """y += x W^T in place, then h = rmsnorm(y): fused into the K-split
+    reduction where there is one (rows up to 4096 columns), else a norm pass."""
+    say(f"[model] linear + residual + rmsnorm {dtype} M{M} N{N} K{K}")
+    o = ops()
+    T = tdt(dtype)
+    x = bi.normal(15, "x", (M, K), 0.5, dtype)
+    w = bi.normal(15, "mWo", (N, K), 0.05, dtype)
+    r = bi.normal(16, "x", (M, N), 0.7, dtype)
+    y = torch.zeros(M + 2, N, dtype=T, device=DEV)
+    y[1:M + 1] = up(r, T)
+    h = torch.zeros(M, N, dtype=T, device=DEV)
+    o.bd_linear_residual_rmsnorm(up(x, T), o.dense(M), up(w, T), y, o.rows(M, M + 2, 1), h, o.dense(M), M=M,
+                                 eps=1e-6)
+    ref_y = r.astype(np.float64) + x.astype(np.float64) @ w.astype(np.float64).T
+    got_y = down(y)
+    rows_close(got_y[1:M + 1], ref_y, TOL[dtype], "residual stream")
+    rows_close(down(h), OM.rmsnorm(ref_y, 1e-6), TOL[dtype], "normalised rows")
+    assert not got_y[0].any() and not got_y[M + 1].any()
+    # h is the norm of the stored y
+    rows_close(down(h), OM.rmsnorm(got_y[1:M + 1].astype(np.float64), 1e-6), TOL[dtype] / 4, "norm of stored y")
+
+
 # ------------------------------------------------------------- whole decode
 def _decoder(cfg, w):
     from block_diffusion_decoding_amd.model import ModelDecoder, ModelDims
