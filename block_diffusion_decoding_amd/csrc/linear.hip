@@ -59,6 +59,7 @@ constexpr int kLdsPerCU = 160 * 1024;
 #define BD_GEMM_PART_BPNS 4000
 #endif
 constexpr int kNS = BD_GEMM_NS;  // pipeline stages
+constexpr int kSliceBatch = 8;   // K slices whose partial sums a reduction thread loads at once
 constexpr int kMaxSeg = 3;
 
 struct GemmS {
@@ -315,36 +316,22 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_reduce(GemmS a) {
   if (rope && col % a.d >= half) return;
   const size_t zs = (size_t)a.M * Nt;
   const float* p = a.part + (size_t)m * Nt + (size_t)gt * 16 + 4 * (rem & 3);
-  float lo[4], hi[4];
-  {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    lo[0] = v.x, lo[1] = v.y, lo[2] = v.z, lo[3] = v.w;
-    const float4 h = rope ? *reinterpret_cast<const float4*>(p + half) : make_float4(0.f, 0.f, 0.f, 0.f);
-    hi[0] = h.x, hi[1] = h.y, hi[2] = h.z, hi[3] = h.w;
-  }
-  // slices in order; four slices' loads in flight at a time
-  int zz = 1;
-  for (; zz + 3 < a.ksplit; zz += 4) {
-    float4 v[4], h[4];
+  // slices in order; up to kSliceBatch slices' loads in flight at a time
+  float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < a.ksplit; z0 += kSliceBatch) {
+    float4 v[kSliceBatch], h[kSliceBatch];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(p + (zz + u) * zs);
-    if (rope) {
+    for (int u = 0; u < kSliceBatch; ++u)
+      if (z0 + u < a.ksplit) {
+        v[u] = *reinterpret_cast<const float4*>(p + (z0 + u) * zs);
+        if (rope) h[u] = *reinterpret_cast<const float4*>(p + (z0 + u) * zs + half);
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) h[u] = *reinterpret_cast<const float4*>(p + (zz + u) * zs + half);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      lo[0] += v[u].x, lo[1] += v[u].y, lo[2] += v[u].z, lo[3] += v[u].w;
-      if (rope) hi[0] += h[u].x, hi[1] += h[u].y, hi[2] += h[u].z, hi[3] += h[u].w;
-    }
-  }
-  for (; zz < a.ksplit; ++zz) {
-    const float4 v = *reinterpret_cast<const float4*>(p + zz * zs);
-    lo[0] += v.x, lo[1] += v.y, lo[2] += v.z, lo[3] += v.w;
-    if (rope) {
-      const float4 h = *reinterpret_cast<const float4*>(p + zz * zs + half);
-      hi[0] += h.x, hi[1] += h.y, hi[2] += h.z, hi[3] += h.w;
-    }
+    for (int u = 0; u < kSliceBatch; ++u)
+      if (z0 + u < a.ksplit) {
+        lo[0] += v[u].x, lo[1] += v[u].y, lo[2] += v[u].z, lo[3] += v[u].w;
+        if (rope) hi[0] += h[u].x, hi[1] += h[u].y, hi[2] += h[u].z, hi[3] += h[u].w;
+      }
   }
   uint16_t* yrow = a.y[sg] + (size_t)bd_map_row(a.yr[sg], m) * N;
   if (rope) {
@@ -392,26 +379,34 @@ __global__ __launch_bounds__(kThreads) void gemm_reduce_norm(GemmS a, float eps,
   const uint16_t* rrow = a.res[0] ? a.res[0] + (size_t)bd_map_row(a.rr[0], m) * N : nullptr;
   uint16_t* yrow = a.y[0] + (size_t)bd_map_row(a.yr[0], m) * N;
   float v[kNormGroups][4];
+#pragma unroll
+  for (int g = 0; g < kNormGroups; ++g) v[g][0] = v[g][1] = v[g][2] = v[g][3] = 0.f;
+  // slices in order; the loads of every column group of a batch of slices
+  // are in flight together
+  constexpr int ZB = kSliceBatch / 2;
+  for (int z0 = 0; z0 < a.ksplit; z0 += ZB) {
+    float4 t[kNormGroups][ZB];
+#pragma unroll
+    for (int g = 0; g < kNormGroups; ++g) {
+      const int col = (g * kThreads + (int)threadIdx.x) * 4;
+#pragma unroll
+      for (int u = 0; u < ZB; ++u)
+        if (col < N && z0 + u < a.ksplit) t[g][u] = *reinterpret_cast<const float4*>(prow + col + (z0 + u) * zs);
+    }
+#pragma unroll
+    for (int g = 0; g < kNormGroups; ++g) {
+      const int col = (g * kThreads + (int)threadIdx.x) * 4;
+#pragma unroll
+      for (int u = 0; u < ZB; ++u)
+        if (col < N && z0 + u < a.ksplit)
+          v[g][0] += t[g][u].x, v[g][1] += t[g][u].y, v[g][2] += t[g][u].z, v[g][3] += t[g][u].w;
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int g = 0; g < kNormGroups; ++g) {
     const int col = (g * kThreads + (int)threadIdx.x) * 4;
     if (col >= N) continue;
-    const float* p = prow + col;
-    float4 acc = *reinterpret_cast<const float4*>(p);
-    int zz = 1;
-    for (; zz + 3 < a.ksplit; zz += 4) {  // slices in order, four loads in flight
-      float4 t[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = *reinterpret_cast<const float4*>(p + (zz + u) * zs);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc.x += t[u].x, acc.y += t[u].y, acc.z += t[u].z, acc.w += t[u].w;
-    }
-    for (; zz < a.ksplit; ++zz) {
-      const float4 t = *reinterpret_cast<const float4*>(p + zz * zs);
-      acc.x += t.x, acc.y += t.y, acc.z += t.z, acc.w += t.w;
-    }
-    v[g][0] = acc.x, v[g][1] = acc.y, v[g][2] = acc.z, v[g][3] = acc.w;
     if (rrow) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[g][e] += bd_bf2f(rrow[col + e]);
