@@ -109,6 +109,7 @@ struct BdGemmPlan {
   int nwg;                // persistent work-groups per (row block, K slice)
   int passes;             // passes per work-group
   int ksplit;             // K slices
+  int big_ct;             // > 0: 256-row x (big_ct*16)-column tiles instead (large M)
   size_t ws_bytes;        // workspace: fp32 partial sums [ksplit][M][T*16]
 };
 

@@ -74,6 +74,7 @@ struct GemmS {
   int N[kMaxSeg];       // output columns per segment (SwiGLU: the gate width)
   int tb[kMaxSeg + 1];  // first 16-column tile of each segment; T from nseg on
   int ksplit;
+  int vec_out;          // every output width % 4 == 0, y/res 8-byte aligned: vector stores
   float* part;          // [ksplit][M][T*16] fp32 partial sums (ksplit > 1)
   const int32_t* pos_base;  // rotary embedding (BD_GEMM_ROPE)
   int n_rows, pos_off, d;
@@ -289,6 +290,270 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
       for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
     cch = 0;
     ++cp;
+  }
+}
+
+// Large-M projections (prompt prefill, exact steps of big batches, the
+// training form): 256-row x (CT*16)-column tiles with 8 waves, the tile
+// machinery of the batched LM head.  CT = 16: 2 x 4 waves of 128 x 64, two
+// 64 KiB stages; CT = 8: 4 x 2 waves of 64 x 64, three 48 KiB stages.  The
+// CT column tiles of a block are consecutive tiles of the segment order (in
+// SwiGLU mode gate and up tiles alternate, so a wave holds whole pairs).  No
+// K split (there are enough tiles); rows past M are neither loaded nor
+// multiplied.  Work order: the larger operand is fetched from HBM once per
+// block and the smaller one re-read from L2: with more weight columns than
+// rows, the row blocks of a column block are consecutive on one XCD; with
+// more rows (row_major), the column blocks of a row block are.
+constexpr int kBigRows = 256, kBigThreads = 512;
+template <int CT>
+struct GBig {
+  static constexpr int WR = CT == 16 ? 2 : 4;       // waves along the rows
+  static constexpr int WC = 8 / WR;                 // waves along the columns
+  static constexpr int MW = kBigRows / 16 / WR;     // row tiles per wave
+  static constexpr int NWT = CT / WC;               // column tiles per wave
+  static constexpr int NS = CT == 16 ? 2 : 3;       // stages
+  static constexpr int TILES = kBigRows / 16 + CT;  // 16-row tiles per stage
+  static constexpr int FR = 2 * TILES;              // DMA instructions per stage
+  static constexpr int LW = FR / 8;                 // per wave
+  static constexpr int STAGE_U4 = FR * 64;
+  static_assert(MW % 4 == 0 && NWT == 4 && FR % 8 == 0 && LW <= 8, "wave tiling");
+};
+
+template <int CT>
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int rb_count, int cb_count,
+                                                                   int row_major) {
+  using P = GBig<CT>;
+  __shared__ uint4 sbuf[P::NS * P::STAGE_U4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int wr = wave % P::WR, wc = wave / P::WR;
+  // work-group w runs on XCD w % 8; its (w / 8)-th work-group takes the next
+  // inner block of that XCD's outer blocks
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  int rb, cb;
+  if (row_major) {
+    const int per_xcd = (rb_count + 7) >> 3;
+    cb = q % cb_count;
+    rb = xcd * per_xcd + q / cb_count;
+    if (rb >= rb_count) return;
+  } else {
+    const int per_xcd = (cb_count + 7) >> 3;
+    rb = q % rb_count;
+    cb = xcd * per_xcd + q / rb_count;
+    if (cb >= cb_count) return;
+  }
+  const int m0 = rb * kBigRows;
+  const int K = a.K, nch = K / 64;
+  const int T = a.tb[a.nseg];
+  const bool swiglu = a.mode == BD_GEMM_SWIGLU;
+
+  // DMA sources: instruction f covers rows 8*(f%2)..+7 of stage tile f/2;
+  // tiles 0..15 are X row tiles, the next CT are W column tiles.
+  const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
+  const uint16_t* src[P::LW];
+  const int live_tiles = min(kBigRows / 16, (a.M - m0 + 15) / 16);
+  bool ld[P::LW];
+  int issued = 0;
+#pragma unroll
+  for (int i = 0; i < P::LW; ++i) {
+    const int f = wave + 8 * i, t = f >> 1, r = 8 * (f & 1) + lrow;
+    if (t < kBigRows / 16) {
+      const int m = m0 + t * 16 + r;
+      src[i] = a.x + (size_t)bd_map_row(a.xr, m < a.M ? m : a.M - 1) * K + 8 * lkb;
+      ld[i] = t < live_tiles;
+    } else {
+      int gt = cb * CT + (t - kBigRows / 16);
+      gt = gt < T ? gt : T - 1;  // past the last tile: a valid row, products unused
+      size_t wrow;
+      const uint16_t* w;
+      if (swiglu) {
+        int c = (gt >> 1) * 16 + r;
+        c = c < a.N[0] ? c : a.N[0] - 1;
+        w = a.w[0];
+        wrow = (size_t)((gt & 1) ? a.N[0] + c : c);
+      } else {
+        const int sg = seg_of(a, gt);
+        int c = (gt - a.tb[sg]) * 16 + r;
+        c = c < a.N[sg] ? c : a.N[sg] - 1;
+        w = a.w[sg];
+        wrow = (size_t)c;
+      }
+      src[i] = w + wrow * K + 8 * lkb;
+      ld[i] = true;
+    }
+    issued += ld[i] ? 1 : 0;
+  }
+  auto issue = [&](int ch) {
+    uint4* st = sbuf + (ch % P::NS) * P::STAGE_U4;
+#pragma unroll
+    for (int i = 0; i < P::LW; ++i)
+      if (ld[i])
+        __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ch * 64),
+                                         (bd_stream::lds_void_t*)(st + (wave + 8 * i) * 64), 16, 0, 0);
+  };
+  auto wait_later_stage = [&]() {  // vmcnt <= loads of one stage
+    switch (issued) {
+      case 0: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(1)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(2)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(3)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(4)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(5)); break;
+      case 6: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(6)); break;
+      case 7: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(7)); break;
+      default: __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(8)); break;
+    }
+  };
+
+  bd_f32x4 acc[P::MW][P::NWT];
+#pragma unroll
+  for (int i = 0; i < P::MW; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NWT; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t sbase = bd_stream::lds_addr(sbuf);
+  const uint32_t fo[2] = {(uint32_t)bd_stream::frag_offset(lane, 0), (uint32_t)bd_stream::frag_offset(lane, 1)};
+  // row tile i of this wave is row tile i*WR + wr of the block
+  const uint32_t xt0 = wr * 2048, wt0 = (kBigRows / 16 + wc * P::NWT) * 2048;
+  constexpr int XS = P::WR * 2048;
+  const int live = min(P::MW, max(0, (live_tiles - wr + P::WR - 1) / P::WR));
+
+#pragma unroll
+  for (int c = 0; c < P::NS - 1; ++c)
+    if (c < nch) issue(c);
+  for (int ch = 0; ch < nch; ++ch) {
+    if (P::NS == 3 && ch + 1 < nch) wait_later_stage();
+    else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+    bd_stream::pipe_barrier();  // chunk ch in LDS everywhere; the slot of ch - 1 is free
+    if (ch + P::NS - 1 < nch) issue(ch + P::NS - 1);
+    const uint32_t st = sbase + (ch % P::NS) * P::STAGE_U4 * 16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 wb[4], xa[4];
+      bd_stream::lds_frags_4x4<XS>(st + xt0 + fo[ks], st + wt0 + fo[ks], xa, wb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < live)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+#pragma unroll
+      for (int i0 = 4; i0 < P::MW; i0 += 4) {
+        if (i0 >= live) break;
+        bd_stream::lds_frags_4<XS>(st + xt0 + i0 * XS + fo[ks], xa);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i0 + i < live)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i0 + i][j] = bd_mfma16(xa[i], wb[j], acc[i0 + i][j]);
+      }
+    }
+  }
+
+  // acc[i][j][r]: row m0 + (i*WR + wr)*16 + 4g + r, tile cb*CT + wc*NWT + j, column l16
+  const int gt0 = cb * CT + wc * P::NWT;
+  if (a.vec_out) {
+    // Stores through LDS: in rounds of 64 rows the fp32 results (after the
+    // SwiGLU gate) are staged as rows, then written out as 4-column vectors
+    // (the residual added in fp32 on the way), so a wave writes whole row
+    // segments instead of 2-byte scattered elements.  Row pitch TW + 16
+    // floats: the four 16-lane groups of a write land in distinct banks.
+    constexpr int TW = CT * 16, PITCH = TW + 16, RR = 64;
+    float* lt = reinterpret_cast<float*>(sbuf);
+    const int ow = swiglu ? TW / 2 : TW;  // output columns of the block
+    for (int h = 0; h < kBigRows / RR; ++h) {
+      if (m0 + h * RR >= a.M) break;  // the same for the whole work-group
+      __syncthreads();                // the stages (or the previous round) are free
+#pragma unroll
+      for (int i = 0; i < P::MW; ++i) {
+        const int rt = (i * P::WR + wr) * 16;
+        if (rt / RR != h) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* lrow = lt + (rt - h * RR + 4 * g + r) * PITCH;
+          if (swiglu) {
+#pragma unroll
+            for (int j = 0; j < P::NWT; j += 2) {
+              const float zg = acc[i][j][r], u = acc[i][j + 1][r];
+              lrow[((wc * P::NWT + j) >> 1) * 16 + l16] = zg / (1.f + __expf(-zg)) * u;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < P::NWT; ++j) lrow[(wc * P::NWT + j) * 16 + l16] = acc[i][j][r];
+          }
+        }
+      }
+      __syncthreads();
+      for (int c = tid; c < RR * (ow / 4); c += kBigThreads) {
+        const int row = c / (ow / 4), c4 = (c % (ow / 4)) * 4;
+        const int m = m0 + h * RR + row;
+        if (m >= a.M) continue;
+        int sg = 0, col, N;
+        if (swiglu) {
+          col = cb * (TW / 2) + c4;
+          N = a.N[0];
+        } else {
+          const int gt = cb * CT + c4 / 16;
+          if (gt >= T) continue;
+          sg = seg_of(a, gt);
+          col = (gt - a.tb[sg]) * 16 + c4 % 16;
+          N = a.N[sg];
+        }
+        if (col >= N) continue;  // N % 4 == 0: a vector is wholly inside or outside
+        const float4 v = *reinterpret_cast<const float4*>(lt + row * PITCH + c4);
+        float vv[4] = {v.x, v.y, v.z, v.w};
+        if (!swiglu && a.res[sg]) {
+          const uint2 rv = *reinterpret_cast<const uint2*>(a.res[sg] + (size_t)bd_map_row(a.rr[sg], m) * N + col);
+          vv[0] += bd_bf2f(rv.x & 0xffffu);
+          vv[1] += bd_bf2f(rv.x >> 16);
+          vv[2] += bd_bf2f(rv.y & 0xffffu);
+          vv[3] += bd_bf2f(rv.y >> 16);
+        }
+        *reinterpret_cast<uint2*>(a.y[sg] + (size_t)bd_map_row(a.yr[sg], m) * N + col) =
+            make_uint2(bd_pack_bf2(vv[0], vv[1]), bd_pack_bf2(vv[2], vv[3]));
+      }
+    }
+    return;
+  }
+  if (swiglu) {
+#pragma unroll
+    for (int j = 0; j < P::NWT; j += 2) {
+      const int col = ((gt0 + j) >> 1) * 16 + l16;
+      if (gt0 + j >= T || col >= a.N[0]) continue;
+#pragma unroll
+      for (int i = 0; i < P::MW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + (i * P::WR + wr) * 16 + 4 * g + r;
+          if (m < a.M) {
+            const float zg = acc[i][j][r], u = acc[i][j + 1][r];
+            a.y[0][(size_t)bd_map_row(a.yr[0], m) * a.N[0] + col] = (uint16_t)bd_f2bf(zg / (1.f + __expf(-zg)) * u);
+          }
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < P::NWT; ++j) {
+    const int gt = gt0 + j;
+    if (gt >= T) continue;
+    const int sg = seg_of(a, gt);
+    const int col = (gt - a.tb[sg]) * 16 + l16;
+    if (col >= a.N[sg]) continue;
+    const int N = a.N[sg];
+    const uint16_t* res = a.res[sg];
+#pragma unroll
+    for (int i = 0; i < P::MW; ++i) {
+      float rv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {  // residual values first, then the stores
+        const int m = m0 + (i * P::WR + wr) * 16 + 4 * g + r;
+        rv[r] = (res && m < a.M) ? bd_bf2f(res[(size_t)bd_map_row(a.rr[sg], m) * N + col]) : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + (i * P::WR + wr) * 16 + 4 * g + r;
+        if (m < a.M) a.y[sg][(size_t)bd_map_row(a.yr[sg], m) * N + col] = (uint16_t)bd_f2bf(acc[i][j][r] + rv[r]);
+      }
+    }
   }
 }
 
@@ -578,6 +843,17 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
     }
   }
   best.ws_bytes = best.ksplit > 1 ? (size_t)best.ksplit * M * T * 16 * sizeof(float) : 0;
+  // large M: 256-row tiles when their blocks alone fill the GPU
+  const int rbk = (M + kBigRows - 1) / kBigRows;
+  for (int ct = 16; ct >= 8 && M >= kBigRows; ct /= 2) {
+    const int cbk = (T + ct - 1) / ct;
+    if ((long)rbk * cbk >= kCUs) {
+      best.big_ct = ct;
+      best.ksplit = 1;
+      best.ws_bytes = 0;
+      break;
+    }
+  }
   return best;
 }
 
@@ -618,6 +894,11 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
       t += mode == BD_GEMM_SWIGLU ? 2 * ((segs[i].N + 15) / 16) : (segs[i].N + 15) / 16;
     }
     for (int i = nseg; i <= kMaxSeg; ++i) a.tb[i] = t;
+    a.vec_out = 1;
+    for (int i = 0; i < nseg; ++i)
+      if (segs[i].N % 4 != 0 || (reinterpret_cast<uintptr_t>(segs[i].y) & 7) != 0 ||
+          (segs[i].res != nullptr && (reinterpret_cast<uintptr_t>(segs[i].res) & 7) != 0))
+        a.vec_out = 0;
     a.ksplit = p.ksplit;
     a.part = p.ksplit > 1 ? static_cast<float*>(workspace) : nullptr;
     if (mode == BD_GEMM_ROPE) {
@@ -627,26 +908,38 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
       a.d = rope->d;
       a.log2_theta = std::log2((double)rope->theta);
     }
-    const dim3 grid(p.nwg, p.ny, p.ksplit);
-    switch (p.MT) {
-      case 1: hipLaunchKernelGGL((gemm_stream_kernel<1, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
-      case 2: hipLaunchKernelGGL((gemm_stream_kernel<2, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
-      case 4: hipLaunchKernelGGL((gemm_stream_kernel<4, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
-      default: hipLaunchKernelGGL((gemm_stream_kernel<8, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (fused_norm) {
-      hipLaunchKernelGGL(gemm_reduce_norm, dim3(M), dim3(kThreads), 0, s, a, post_norm->eps,
-                         static_cast<uint16_t*>(post_norm->h), post_norm->hr);
-      return hipGetLastError();
-    }
-    if (p.ksplit > 1) {
-      const size_t n = (size_t)M * p.T * 4;
-      hipLaunchKernelGGL(gemm_stream_reduce, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                         a);
-      hipError_t e2 = hipGetLastError();
-      if (e2 != hipSuccess || post_norm == nullptr) return e2;
+    if (p.big_ct != 0) {  // 256-row tiles, no K split
+      const int rbk = (M + kBigRows - 1) / kBigRows, cbk = (p.T + p.big_ct - 1) / p.big_ct;
+      const int row_major = rbk * kBigRows > cbk * p.big_ct * 16 ? 1 : 0;  // more rows than weight columns
+      const dim3 bgrid((unsigned)(row_major ? 8 * ((rbk + 7) / 8) * cbk : 8 * ((cbk + 7) / 8) * rbk));
+      if (p.big_ct == 16)
+        hipLaunchKernelGGL(gemm_big_kernel<16>, bgrid, dim3(kBigThreads), 0, s, a, rbk, cbk, row_major);
+      else
+        hipLaunchKernelGGL(gemm_big_kernel<8>, bgrid, dim3(kBigThreads), 0, s, a, rbk, cbk, row_major);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      const dim3 grid(p.nwg, p.ny, p.ksplit);
+      switch (p.MT) {
+        case 1: hipLaunchKernelGGL((gemm_stream_kernel<1, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+        case 2: hipLaunchKernelGGL((gemm_stream_kernel<2, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+        case 4: hipLaunchKernelGGL((gemm_stream_kernel<4, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+        default: hipLaunchKernelGGL((gemm_stream_kernel<8, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (fused_norm) {
+        hipLaunchKernelGGL(gemm_reduce_norm, dim3(M), dim3(kThreads), 0, s, a, post_norm->eps,
+                           static_cast<uint16_t*>(post_norm->h), post_norm->hr);
+        return hipGetLastError();
+      }
+      if (p.ksplit > 1) {
+        const size_t n = (size_t)M * p.T * 4;
+        hipLaunchKernelGGL(gemm_stream_reduce, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                           a);
+        hipError_t e2 = hipGetLastError();
+        if (e2 != hipSuccess || post_norm == nullptr) return e2;
+      }
     }
   }
   if (post_norm != nullptr && !fused_norm)

@@ -321,11 +321,14 @@ def test_projection_workspace_shared_by_different_tilings():
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 1536, 1536), (32, 2048, 512), (50, 1536, 8960), (128, 1536, 8960),
-                                   (100, 17920, 256), (512, 8192, 512), (512, 1536, 1536), (16, 1000, 512)])
+                                   (100, 17920, 256), (512, 8192, 512), (512, 1536, 1536), (16, 1000, 512),
+                                   (1000, 8192, 512), (4096, 4096, 512)])
 def test_linear_in_place_residual_tilings(M, N, K):
     """y = x W^T + y in place through row maps, for row counts that take
-    every row tile (16 .. 128 rows, ragged tails) with and without a K split:
-    the residual rows are read before the same rows are written."""
+    every row tile (16 .. 128 rows, ragged tails) with and without a K split,
+    and the 256-row tiles of large M (1000 rows: 128-column tiles, ragged;
+    4096 rows: 256-column tiles): the residual rows are read before the same
+    rows are written."""
     say(f"[support] linear M{M} N{N} K{K}")
     o = ops()
     T = torch.bfloat16

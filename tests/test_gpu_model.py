@@ -87,10 +87,12 @@ def test_row_ops_at_widths_off_the_vector_path(dtype, hidden, inter):
 
 @pytest.mark.parametrize("dtype,B,n,Hq,Hkv,d,K", [("bf16", 16, 8, 12, 2, 128, 1536), ("bf16", 3, 8, 4, 2, 64, 512),
                                                   ("bf16", 2, 4, 4, 2, 64, 256), ("f32", 3, 8, 4, 2, 64, 256),
-                                                  ("bf16", 16, 32, 12, 2, 128, 1536)])
+                                                  ("bf16", 16, 32, 12, 2, 128, 1536),
+                                                  ("bf16", 128, 32, 12, 2, 128, 512)])
 def test_qkv_proj_rope_matches_projection_then_rotation(dtype, B, n, Hq, Hkv, d, K):
     """q and k rotated at their absolute positions, v plain; the K-split path
-    rotates in the reduction, the others in a rotary pass."""
+    rotates in the reduction, the others (one slice; 256-row tiles at 4096
+    rows) in a rotary pass."""
     say(f"[model] qkv+rope {dtype} B{B} n{n} Hq{Hq} Hkv{Hkv} d{d} K{K}")
     o = ops()
     T = tdt(dtype)
@@ -122,7 +124,8 @@ def test_qkv_proj_rope_matches_projection_then_rotation(dtype, B, n, Hq, Hkv, d,
 
 @pytest.mark.parametrize("dtype,M,K,inter", [("bf16", 128, 1536, 8960), ("bf16", 5, 512, 1000),
                                              ("bf16", 37, 256, 520), ("bf16", 300, 512, 256),
-                                             ("f32", 9, 256, 100)])
+                                             ("f32", 9, 256, 100), ("bf16", 512, 1536, 8960),
+                                             ("bf16", 1100, 512, 4096)])
 def test_gate_up_swiglu_matches_projections_then_gate(dtype, M, K, inter):
     say(f"[model] gate/up+swiglu {dtype} M{M} K{K} inter{inter}")
     o = ops()
