@@ -642,7 +642,8 @@ def main():
             traffic = rec.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "bd_lmhead_confidence (lm_stream_kernel<4> + lm_merge_kernel), 64 rows x 152064 x 3584",
+                "kernel": "bd_lmhead_unmask (lm_stream_kernel<4> + lm_merge_unmask_kernel: the LM head's final reduction "
+                          "with the threshold unmask), 64 rows x 152064 x 3584",
                 "algorithmic_bytes": lm_bytes, "launch_us_mean": round(lm_mean * 1e6, 2),
                 "launch_us_median": round(float(np.median(lm_t)) * 1e6, 2),
                 "timing": f"HIP events around each of {len(lm_t)} LM-head launches of a second timed pass of "

@@ -41,6 +41,11 @@ SIGNATURES = {
                                           c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                           c_void_p, c_size_t, c_void_p]),
+    "bd_lmhead_unmask": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                 c_void_p, c_int, c_void_p, c_void_p, c_float, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_size_t, c_void_p]),
     "bd_candidate_rows": (c_int, [c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "bd_threshold_unmask": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_float,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -99,7 +99,7 @@ size_t bd_lmhead_workspace_size(bd_dtype dt, int M, int hidden, int V) {
 static bd_status lm_common(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
                            const int32_t* row_idx, const int32_t* out_pos, const int32_t* m_dev, int n_out,
                            const void* w, int32_t* argmax, float* conf, float* max_logit, float* lse, float* logits,
-                           void* workspace, size_t ws_bytes, void* stream) {
+                           void* workspace, size_t ws_bytes, void* stream, const BdLmUnmask* um = nullptr) {
   if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
   if (M == 0) return BD_OK;
   if (hidden <= 0 || V <= 0 || n_src <= 0 || !h_src || !w || !argmax || !conf) return BD_EINVAL;
@@ -127,7 +127,7 @@ static bd_status lm_common(bd_dtype dt, int M, int hidden, int V, const void* h_
   a.m_dev = m_dev;
   a.out_pos = out_pos;
   a.n_out = n_out;
-  return hip_status(bd_lm_launch(dt, p, a, static_cast<hipStream_t>(stream)));
+  return hip_status(bd_lm_launch(dt, p, a, static_cast<hipStream_t>(stream), um));
 }
 
 bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,
@@ -136,6 +136,22 @@ bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V, const void
                                void* stream) {
   return lm_common(dt, M, hidden, V, h_src, n_src, row_idx, nullptr, nullptr, 0, w, argmax, conf, max_logit, lse,
                    logits, workspace, ws_bytes, stream);
+}
+
+bd_status bd_lmhead_unmask(bd_dtype dt, int B, int D, int win_lo, int win_len, int hidden, int V, const void* h_src,
+                           int n_src, const int32_t* row_idx, const void* w, float threshold,
+                           const float* threshold_dev, int32_t* argmax, float* conf, float* max_logit, float* lse,
+                           int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked, int32_t* unmasked_pos,
+                           uint64_t* mask_bits_host, void* workspace, size_t ws_bytes, void* stream) {
+  if (B < 0) return BD_EINVAL;
+  if (B == 0) return BD_OK;
+  if (D < 1 || D > 64 || win_lo < 0 || win_len < 1 || win_len > 64 || win_lo + win_len > D) return BD_EINVAL;
+  if ((long)B * win_len > 64 || !tokens || !mask_bits) return BD_EINVAL;
+  if (threshold_dev == nullptr && !(threshold == threshold)) return BD_EINVAL;
+  BdLmUnmask um{B, D, win_lo, win_len, threshold, threshold_dev, tokens, mask_bits, n_unmasked, unmasked_pos,
+                mask_bits_host};
+  return lm_common(dt, B * win_len, hidden, V, h_src, n_src, row_idx, nullptr, nullptr, 0, w, argmax, conf,
+                   max_logit, lse, nullptr, workspace, ws_bytes, stream, &um);
 }
 
 bd_status bd_lmhead_confidence_rows(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,

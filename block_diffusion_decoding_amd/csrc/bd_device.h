@@ -124,3 +124,43 @@ __device__ __forceinline__ BdArgStat bd_row16_stat(const float (&v)[N], const in
   return BdArgStat{m, bd_row16_min(idx), bd_row16_sum(s)};
 }
 
+
+// Confidence-threshold unmasking of one sequence's window by one wavefront
+// ("Fast-dLLM v2: Efficient Block-Diffusion LLM" notes, Key design 3; the v1
+// article, Core technique 2).  Lane r holds window entry r: its confidence c
+// and argmax am (ignored past win_len).  Candidates are the masked window
+// positions; every candidate with c > thr is unmasked, and when candidates
+// exist but none passes, the most confident one (lowest position on ties).
+// A NaN confidence never passes and ranks last.  Writes the picked tokens,
+// the new mask bits (also to bits_out when given: a second copy, e.g. in
+// host memory the device can write), the count and the ascending positions.
+__device__ inline void bd_unmask_wave(int r, int b, int D, int win_lo, int win_len, uint64_t bits, float c, int32_t am,
+                                      float thr, int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
+                                      int32_t* unmasked_pos, uint64_t* bits_out) {
+  const int pos = win_lo + r;
+  const bool cand = r < win_len && ((bits >> pos) & 1ull);
+  c = cand ? c : BD_NEG_INF;
+  if (c != c) c = BD_NEG_INF;
+  uint64_t pick = __ballot(cand && c > thr);
+  const uint64_t cands = __ballot(cand);
+  if (pick == 0 && cands != 0) {
+    float best = c;
+    for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+    const uint64_t eq = __ballot(cand && c == best);
+    pick = eq & (~eq + 1ull);  // lowest position among the most confident
+  }
+  const bool mine = (pick >> r) & 1ull;
+  if (mine) tokens[(size_t)b * D + pos] = am;
+  const int n = __popcll(pick);
+  if (unmasked_pos != nullptr && r < win_len) {
+    const int rank = __popcll(pick & ((1ull << r) - 1ull));
+    if (mine) unmasked_pos[(size_t)b * win_len + rank] = pos;
+    if (r >= n) unmasked_pos[(size_t)b * win_len + r] = -1;
+  }
+  if (r == 0) {
+    const uint64_t left = bits & ~(pick << win_lo);
+    mask_bits[b] = left;
+    if (bits_out != nullptr) bits_out[b] = left;
+    if (n_unmasked != nullptr) n_unmasked[b] = n;
+  }
+}

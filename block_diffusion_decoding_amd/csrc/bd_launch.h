@@ -71,7 +71,23 @@ struct BdLmArgs {
   int n_out;               // output slots when out_pos is given
 };
 
-hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& a, hipStream_t s);
+// Threshold unmask fused into the LM head's merge: rows m = b * win_len + r
+// (window entry r of sequence b), one work-group per sequence.
+struct BdLmUnmask {
+  int B, D, win_lo, win_len;
+  float threshold;
+  const float* threshold_dev;  // [B] per-sequence threshold, or NULL = threshold
+  int32_t* tokens;
+  uint64_t* mask_bits;
+  int32_t* n_unmasked;
+  int32_t* unmasked_pos;
+  uint64_t* bits_out;          // second copy of the new mask bits, or NULL
+};
+
+// um != NULL: the merge also applies the threshold rule (a.M = B * win_len,
+// no row list compaction).
+hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& a, hipStream_t s,
+                        const BdLmUnmask* um = nullptr);
 hipError_t bd_candidates_launch(int B, int win_lo, int win_len, const uint64_t* mask_bits, int rows_per_seq,
                                 int32_t* row_idx, int32_t* out_pos, int32_t* count, hipStream_t s);
 

@@ -537,6 +537,8 @@ __global__ __launch_bounds__(kThreads) void lm_f32_kernel(LmF a) {
 // lowest column among the tiles that reach the max.  The order of the sums
 // is fixed, so the result is deterministic.
 constexpr int kMergePer = 8;
+constexpr int kFuseThreads = 512;  // merge fused with the unmask: 8 waves, one row each at a time
+constexpr int kFusePer = 8;        // partials per lane held in registers (up to 512 per row)
 
 __device__ __forceinline__ float block_max(float v, float* sh) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -622,6 +624,80 @@ __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_i
   if (lse != nullptr) lse[om] = ok ? mx + bd_log2(s) * BD_LN2 : nan;
 }
 
+// Merge fused with the threshold unmask: one work-group per sequence.  The
+// sequence's win_len rows are padded to RP (a power of two) lanes, so one
+// load instruction of a wave covers 64 / RP tiles x RP consecutive rows
+// (short runs of whole partial rows instead of 64 scattered words; the
+// partials are [tile][row]).  Lane (q, r) folds tiles q + (64 / RP) * (wave
+// + 8 u) of row r in batches held in registers; lanes of one row, then the 8
+// waves (through LDS), combine their (max, argmax, sum) in a fixed order.
+// Wave 0 lane r then holds row r: it writes the statistics and the wave
+// applies the threshold rule.  Saves the unmask launch of the step.
+__global__ __launch_bounds__(kFuseThreads) void lm_merge_unmask_kernel(const int32_t* row_idx, int n_src, int nvt,
+                                                                      const float* pmax, const int32_t* pidx,
+                                                                      const float* psum, int32_t* argmax, float* conf,
+                                                                      float* max_logit, float* lse, int M, int RP,
+                                                                      BdLmUnmask u) {
+  constexpr int NW = kFuseThreads / 64;
+  __shared__ BdArgStat sh[NW][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int r = lane & (RP - 1);
+  const int q = lane / RP;
+  const int tpi = 64 / RP;                // tiles per wave instruction
+  const bool live = r < u.win_len;
+  const int m = b * u.win_len + (live ? r : 0);
+  BdArgStat st{BD_NEG_INF, INT_MAX, 0.f};
+  for (int t0 = q + tpi * wave; t0 < nvt; t0 += tpi * NW * kFusePer) {
+    float pm[kFusePer], ps[kFusePer];
+    int pi[kFusePer];
+#pragma unroll
+    for (int k = 0; k < kFusePer; ++k) {
+      const int t = t0 + tpi * NW * k;
+      const bool ok = live && t < nvt;
+      const size_t at = (size_t)t * M + m;
+      pm[k] = ok ? pmax[at] : BD_NEG_INF;
+      ps[k] = ok ? psum[at] : 0.f;
+      pi[k] = ok ? pidx[at] : INT_MAX;
+    }
+    float bm = pm[0];
+#pragma unroll
+    for (int k = 1; k < kFusePer; ++k) bm = fmaxf(bm, pm[k]);
+    const float mu = (bm == BD_NEG_INF) ? 0.f : bm;
+    float bs = 0.f;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < kFusePer; ++k) {
+      bs += ps[k] * bd_exp2((pm[k] - mu) * BD_LOG2E);
+      if (pm[k] == bm && pm[k] != BD_NEG_INF) bi = min(bi, pi[k]);
+    }
+    st = bd_stat_combine(st, BdArgStat{bm, bi, bs});
+  }
+  for (int off = RP; off < 64; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
+  if (q == 0) sh[wave][r] = st;
+  __syncthreads();
+  if (wave != 0) return;
+  if (q == 0)
+    for (int w = 1; w < NW; ++w) st = bd_stat_combine(st, sh[w][r]);
+  float c = BD_NEG_INF;
+  int32_t am = -1;
+  if (live && q == 0) {
+    const int src = row_idx ? row_idx[m] : m;
+    const bool ok = src >= 0 && src < n_src && st.s > 0.f;
+    const float nan = __builtin_nanf("");
+    c = ok ? 1.f / st.s : nan;
+    am = ok ? st.i : -1;
+    argmax[m] = am;
+    conf[m] = c;
+    if (max_logit != nullptr) max_logit[m] = ok ? st.m : nan;
+    if (lse != nullptr) lse[m] = ok ? st.m + bd_log2(st.s) * BD_LN2 : nan;
+  }
+  // lane r (< RP, so q == 0) holds window entry r
+  const float thr = u.threshold_dev != nullptr ? u.threshold_dev[b] : u.threshold;
+  bd_unmask_wave(lane, b, u.D, u.win_lo, u.win_len, u.mask_bits[b], lane < RP ? c : BD_NEG_INF,
+                 lane < RP ? am : -1, thr, u.tokens, u.mask_bits, u.n_unmasked, u.unmasked_pos, u.bits_out);
+}
+
 }  // namespace
 
 BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
@@ -648,7 +724,7 @@ BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
   return p;
 }
 
-hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipStream_t s) {
+hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipStream_t s, const BdLmUnmask* um) {
   const dim3 grid(p.nvt, p.nmb);
   if (dt == BD_F32) {
     LmF a{static_cast<const float*>(x.h), x.n_src, x.row_idx, static_cast<const float*>(x.w), x.logits,
@@ -674,6 +750,14 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool row_major = dt != BD_F32 && p.rows_per_wg == kBigRows;  // partial layout, see the merge
+  if (um != nullptr) {  // [tile][row] partials: the streaming and fp32 kernels (at most 64 rows)
+    if (row_major || x.M != um->B * um->win_len) return hipErrorInvalidValue;
+    int rp = 1;
+    while (rp < um->win_len) rp <<= 1;
+    hipLaunchKernelGGL(lm_merge_unmask_kernel, dim3(um->B), dim3(kFuseThreads), 0, s, x.row_idx, x.n_src, p.nvt,
+                       x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse, x.M, rp, *um);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(lm_merge_kernel, dim3(x.M), dim3(kThreads), 0, s, x.row_idx, x.n_src, x.M, p.nvt,
                      row_major ? (size_t)1 : (size_t)x.M, row_major ? (size_t)p.nvt : (size_t)1, x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse, x.m_dev, x.out_pos,
                      x.n_out);

@@ -26,31 +26,11 @@ __global__ __launch_bounds__(64) void unmask_kernel(int D, int win_lo, int win_l
   const int b = blockIdx.x;
   const int r = threadIdx.x;
   if (thr_dev != nullptr) thr = thr_dev[b];  // per-sequence threshold from device memory
-  const int pos = win_lo + r;
   const uint64_t bits = mask_bits[b];
-  const bool cand = r < win_len && ((bits >> pos) & 1ull);
-  float c = cand ? conf[(size_t)b * win_len + r] : BD_NEG_INF;
-  if (c != c) c = BD_NEG_INF;  // a NaN confidence never passes and ranks last
-  uint64_t pick = __ballot(cand && c > thr);
-  const uint64_t cands = __ballot(cand);
-  if (pick == 0 && cands != 0) {
-    float best = cand ? c : BD_NEG_INF;
-    for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
-    const uint64_t eq = __ballot(cand && c == best);
-    pick = eq & (~eq + 1ull);  // lowest position among the most confident
-  }
-  const bool mine = (pick >> r) & 1ull;
-  if (mine) tokens[(size_t)b * D + pos] = argmax[(size_t)b * win_len + r];
-  const int n = __popcll(pick);
-  if (unmasked_pos != nullptr && r < win_len) {
-    const int rank = __popcll(pick & ((1ull << r) - 1ull));
-    if (mine) unmasked_pos[(size_t)b * win_len + rank] = pos;
-    if (r >= n) unmasked_pos[(size_t)b * win_len + r] = -1;
-  }
-  if (r == 0) {
-    mask_bits[b] = bits & ~(pick << win_lo);
-    if (n_unmasked != nullptr) n_unmasked[b] = n;
-  }
+  const bool in = r < win_len;
+  const float c = in ? conf[(size_t)b * win_len + r] : BD_NEG_INF;
+  const int32_t am = in ? argmax[(size_t)b * win_len + r] : -1;
+  bd_unmask_wave(r, b, D, win_lo, win_len, bits, c, am, thr, tokens, mask_bits, n_unmasked, unmasked_pos, nullptr);
 }
 
 // One work-group per sequence: copy n_rows in-block rows behind the committed

@@ -75,9 +75,9 @@ class BlockDecoder:
         self.o = torch.zeros(B, D, Hq, d, dtype=dt, device=dev)
         self.tokens = torch.zeros(B, D, dtype=torch.int32, device=dev)
         self.mask_bits = torch.zeros(B, dtype=torch.int64, device=dev)
-        # host copy of the mask bits, refreshed by the last node of every step
-        # (pinned, so the copy is a plain DMA into it and the host only waits
-        # for the step's event)
+        # host copy of the mask bits, refreshed by every step (written by the
+        # unmask itself, or by a copy behind it; pinned, so the host only
+        # waits for the step's event)
         self.bits_host = torch.zeros(B, dtype=torch.int64, pin_memory=True)
         self._bits_ev = torch.cuda.Event()
         self._bits_fresh = False
@@ -187,6 +187,7 @@ class BlockDecoder:
         if self.lm_events is not None:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             ev[0].record()
+        fused = False
         if self.uses_compaction(S):
             # only the masked candidates: their conf/argmax land at their window
             # slots; the other slots are not candidates and the unmask ignores them
@@ -194,15 +195,24 @@ class BlockDecoder:
                                   win_len=S, rows_per_seq=1 + dm.D)
             ops.bd_lmhead_confidence_rows(self.H.view(-1, dm.hidden), w["cand_rows"], w["cand_pos"], w["cand_count"],
                                           self.W["Wlm"], w["argmax"], w["conf"], max_logit=w["maxl"], lse=w["lse"])
+        elif dm.B * S <= 64:
+            # one call: the LM head, then its final reduction fused with the
+            # threshold rule, which also writes the new bits to host memory
+            ops.bd_lmhead_unmask(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"], w["conf"],
+                                 self.tokens, self.mask_bits, win_lo=s * S, threshold=tau, max_logit=w["maxl"],
+                                 lse=w["lse"], n_unmasked=self.n_unmasked, unmasked_pos=w["pos"],
+                                 mask_bits_host=self.bits_host)
+            fused = True
         else:
             ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"],
                                      w["conf"], max_logit=w["maxl"], lse=w["lse"])
         if ev is not None:
             ev[1].record()
             self.lm_events.append(ev)
-        ops.bd_threshold_unmask(w["conf"], w["argmax"], self.tokens, self.mask_bits, win_lo=s * S,
-                                threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
-        self.bits_host.copy_(self.mask_bits, non_blocking=True)
+        if not fused:
+            ops.bd_threshold_unmask(w["conf"], w["argmax"], self.tokens, self.mask_bits, win_lo=s * S,
+                                    threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
+            self.bits_host.copy_(self.mask_bits, non_blocking=True)
         self.last = w
 
     def uses_compaction(self, S: int) -> bool:

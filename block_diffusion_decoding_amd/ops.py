@@ -139,6 +139,36 @@ def bd_lmhead_confidence_rows(h_src, row_idx, out_pos, m_dev, w, argmax, conf, *
     _check("bd_lmhead_confidence_rows", st)
 
 
+def bd_lmhead_unmask(h_src, row_idx, w, argmax, conf, tokens, mask_bits, *, win_lo, threshold, max_logit=None,
+                     lse=None, n_unmasked=None, unmasked_pos=None, mask_bits_host=None, ws=None, stream=None):
+    """LM head with fused confidence and the threshold unmask in one call:
+    argmax/conf [B, win_len] (row b * win_len + r predicts position
+    win_lo + r); tokens [B, D] int32, mask_bits [B] (64-bit) in/out;
+    threshold a float or a [B] fp32 device tensor; mask_bits_host an
+    optional pinned host tensor [B] (64-bit) that receives the new bits."""
+    lib = _lib.load()
+    hidden = h_src.shape[-1]
+    n_src = h_src.numel() // hidden
+    V = w.shape[0]
+    B, win_len = conf.shape
+    D = tokens.shape[1]
+    dt = _dt(h_src)
+    if mask_bits_host is not None:
+        assert mask_bits_host.device.type == "cpu" and mask_bits_host.is_pinned() and mask_bits_host.numel() == B
+    tau_dev = None
+    if isinstance(threshold, torch.Tensor):
+        assert threshold.dtype == torch.float32 and threshold.numel() == B
+        tau_dev, threshold = threshold, 0.0
+    need = lib.bd_lmhead_workspace_size(dt, B * win_len, hidden, V)
+    if ws is None:
+        ws = workspace(need, h_src.device, "lm")
+    st = lib.bd_lmhead_unmask(dt, B, D, win_lo, win_len, hidden, V, _p(h_src), n_src, _p(row_idx), _p(w),
+                              float(threshold), _p(tau_dev), _p(argmax), _p(conf), _p(max_logit), _p(lse),
+                              _p(tokens), _p(mask_bits), _p(n_unmasked), _p(unmasked_pos), _p(mask_bits_host),
+                              _p(ws), ws.numel(), _stream(stream))
+    _check("bd_lmhead_unmask", st)
+
+
 def bd_candidate_rows(mask_bits, row_idx, out_pos, count, *, win_lo, win_len, rows_per_seq, stream=None):
     """mask_bits [B] (64-bit); row_idx/out_pos [B*win_len] int32; count [1] int32."""
     lib = _lib.load()

@@ -13,6 +13,7 @@
  *     confidence / argmax               bd_lmhead_confidence
  *     (only the masked candidates)      bd_candidate_rows + bd_lmhead_confidence_rows
  *   confidence-threshold unmasking      bd_threshold_unmask
+ *     (LM head + unmask, one call)      bd_lmhead_unmask
  *   (block finished) cache append       bd_kv_append
  *
  * Sources, by page title and section:
@@ -217,6 +218,39 @@ bd_status bd_threshold_unmask_tau(int B, int D, int win_lo, int win_len,
                                   const float* conf, const int32_t* argmax, const float* threshold,
                                   int32_t* tokens, uint64_t* mask_bits,
                                   int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bd_lmhead_unmask -- bd_lmhead_confidence followed by bd_threshold_unmask
+ * in one call, for a lockstep window of at most 64 rows ([v2 notes] Key
+ * designs 2 and 3: the confidences of the window's rows decide which of its
+ * masked positions are decoded).  The LM head's final reduction and the
+ * threshold rule share one kernel (one work-group per sequence), which saves
+ * a launch per refinement step.
+ *
+ *   row m = b * win_len + r predicts position win_lo + r of sequence b; its
+ *   source row is h_src[row_idx[m]] (row_idx may be NULL = m)
+ *   argmax, conf, max_logit, lse [B, win_len]: as bd_lmhead_confidence
+ *   (max_logit and lse may be NULL); the fold order of the per-tile partials
+ *   differs from bd_lmhead_confidence, so conf and lse may differ from it in
+ *   the last bits
+ *   threshold / threshold_dev: a fixed threshold, or (threshold_dev != NULL)
+ *   a per-sequence [B] fp32 threshold read from device memory
+ *   tokens, mask_bits, n_unmasked, unmasked_pos: as bd_threshold_unmask
+ *   mask_bits_host [B] or NULL: the new mask bits are also written here.
+ *     It must be pinned host memory from hipHostMalloc (the device writes it
+ *     directly; no copy is enqueued); the values are valid on the host once
+ *     the stream has passed this call (e.g. after an event recorded behind
+ *     it has completed).
+ *   workspace: bd_lmhead_workspace_size(dt, B * win_len, hidden, V) bytes.
+ * Requires B * win_len <= 64 and the rules of both calls.
+ * ---------------------------------------------------------------------- */
+bd_status bd_lmhead_unmask(bd_dtype dt, int B, int D, int win_lo, int win_len, int hidden, int V,
+                           const void* h_src, int n_src, const int32_t* row_idx, const void* w,
+                           float threshold, const float* threshold_dev,
+                           int32_t* argmax, float* conf, float* max_logit, float* lse,
+                           int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
+                           int32_t* unmasked_pos, uint64_t* mask_bits_host,
+                           void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * bd_kv_append -- commit a finished block to the block-level cache ([v2

@@ -31,7 +31,8 @@ def test_header_declares_the_four_calls_and_support():
               "bd_linear_workspace_size", "bd_qkv_proj_workspace_size",
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
               "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu",
-              "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau"]:
+              "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau",
+              "bd_lmhead_unmask"]:
         assert n in names
 
 
@@ -240,4 +241,20 @@ def test_device_threshold_unmask_argument_errors():
     call = lambda **k: lib.bd_threshold_unmask_tau(k.get("B", 4), k.get("D", 32), k.get("lo", 8), 8, FAKE, FAKE,
                                                    k.get("tau", FAKE), FAKE, FAKE, None, None, None)
     assert call(tau=None) == E and call(D=65) == E and call(lo=30) == E and call(B=-1) == E
+    assert call(B=0) == 0
+
+
+def test_lmhead_unmask_argument_errors():
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    need = lib.bd_lmhead_workspace_size(1, 64, 3584, 152064)
+    call = lambda **k: lib.bd_lmhead_unmask(1, k.get("B", 8), k.get("D", 32), k.get("lo", 8), k.get("win", 8), 3584,
+                                            152064, FAKE, 300, FAKE, FAKE, k.get("tau", 0.9), k.get("tdev", None),
+                                            FAKE, FAKE, None, None, k.get("tok", FAKE), k.get("bits", FAKE), None,
+                                            None, None, FAKE, k.get("wsb", need), None)
+    assert call(B=9) == E                       # more than 64 rows
+    assert call(win=16, B=4, lo=24) == E        # window past D
+    assert call(D=65) == E and call(tok=None) == E and call(bits=None) == E
+    assert call(tau=float("nan")) == E          # a NaN fixed threshold
+    assert call(wsb=need - 16) == E
     assert call(B=0) == 0

@@ -228,6 +228,88 @@ def test_threshold_unmask_per_sequence_threshold(D, S, win):
 
 
 # --------------------------------------------------------------------------
+# bd_lmhead_unmask: the LM head and the threshold rule in one call
+# --------------------------------------------------------------------------
+FUSE_CASES = {
+    # name: (dtype, B, S, D, win, hidden, V, h scale, tau; "dev" = per-sequence device thresholds)
+    "f32-tiny": ("f32", 3, 8, 32, 1, 256, 1024, 40.0, 0.5),
+    "bf16-7B-B8-S8": ("bf16", 8, 8, 32, 2, 3584, 152064, 60.0, 0.9),
+    "bf16-1.5B-B1-S8": ("bf16", 1, 8, 32, 3, 1536, 151936, 60.0, 0.9),
+    "bf16-B16-S4-dev": ("bf16", 16, 4, 32, 5, 512, 5000, 30.0, "dev"),
+    "bf16-B2-S32": ("bf16", 2, 32, 64, 1, 512, 5000, 30.0, 0.5),
+    # fp32 head of 140000 columns: 547 partials per row (the strided merge)
+    "f32-wide-vocab": ("f32", 2, 8, 32, 0, 256, 140000, 40.0, 0.5),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSE_CASES))
+def test_lmhead_unmask(name):
+    """bd_lmhead_unmask against the oracle (statistics per row, then the
+    threshold rule applied by the oracle to the call's own confidences, so
+    both sides decide in fp32 from the same values), against the two-call
+    path (bd_lmhead_confidence + bd_threshold_unmask: same argmax and max,
+    conf/lse up to the partials' fold order, same decisions), and the host
+    copy of the new mask bits."""
+    dt, B, S, D, win, hidden, V, hs, tau = FUSE_CASES[name]
+    say(f"[lmhead+unmask] {name}")
+    T = tdt(dt)
+    M = B * S
+    n_src = B * (1 + D)
+    w = bi.normal(4, "Wlm", (V, hidden), 0.02, dt)
+    h = bi.normal(4, "h", (n_src, hidden), 0.02 * hs, dt)
+    rng = np.random.default_rng(M + V)
+    ridx = np.array([b * (1 + D) + win * S + r for b in range(B) for r in range(S)], dtype=np.int32)
+    masked = rng.random((B, D)) < 0.6
+    masked[0, win * S:(win + 1) * S] = True
+    tokens = np.where(masked, 0, rng.integers(0, V, size=(B, D))).astype(np.int32)
+    taus = rng.choice(np.array([0.3, 0.6, 0.9, 1.0], np.float32), size=B).astype(np.float32)
+    thr = up(taus) if tau == "dev" else tau
+    outs = []
+    for fused in (True, False):
+        am = torch.zeros(B, S, dtype=torch.int32, device=DEV)
+        conf, mx, lse = (torch.zeros(B, S, dtype=torch.float32, device=DEV) for _ in range(3))
+        t_tok, t_bits = up(tokens), up(bi.mask_bits(masked).view(np.int64))
+        n = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        pos = torch.full((B, S), -7, dtype=torch.int32, device=DEV)
+        host = torch.zeros(B, dtype=torch.int64, pin_memory=True)
+        if fused:
+            ops().bd_lmhead_unmask(up(h, T), up(ridx), up(w, T), am, conf, t_tok, t_bits, win_lo=win * S,
+                                   threshold=thr, max_logit=mx, lse=lse, n_unmasked=n, unmasked_pos=pos,
+                                   mask_bits_host=host)
+        else:
+            ops().bd_lmhead_confidence(up(h, T), up(ridx), up(w, T), am.view(-1), conf.view(-1),
+                                       max_logit=mx.view(-1), lse=lse.view(-1))
+            ops().bd_threshold_unmask(conf, am, t_tok, t_bits, win_lo=win * S, threshold=thr, n_unmasked=n,
+                                      unmasked_pos=pos)
+        torch.cuda.synchronize()
+        outs.append(dict(am=am.cpu().numpy(), conf=down(conf), mx=down(mx), lse=down(lse),
+                         tok=t_tok.cpu().numpy(), bits=t_bits.cpu().numpy().view(np.uint64),
+                         n=n.cpu().numpy(), pos=pos.cpu().numpy(), host=host.numpy().view(np.uint64).copy()))
+    f, u = outs
+    # the oracle: statistics of every row, then the rule on the call's own conf/argmax
+    ref = R.lm_logits(w, h[ridx])
+    lm_stats_close(f["am"].reshape(-1), f["conf"].reshape(-1), f["mx"].reshape(-1), f["lse"].reshape(-1), ref,
+                   TOL[dt], name)
+    for b in range(B):
+        tb = np.float32(taus[b]) if tau == "dev" else np.float32(tau)
+        rt, rm, rn, rp = R.batch_threshold_unmask(f["conf"][b:b + 1], f["am"][b:b + 1], tokens[b:b + 1],
+                                                  masked[b:b + 1], win * S, tb)
+        assert np.array_equal(f["tok"][b], rt[0]), f"{name}: tokens of sequence {b}"
+        assert np.array_equal(bi.bits_to_mask(f["bits"][b:b + 1], D)[0], rm[0]), f"{name}: mask of sequence {b}"
+        assert f["n"][b] == rn[0] and np.array_equal(f["pos"][b], rp[0]), f"{name}: positions of sequence {b}"
+    assert np.array_equal(f["host"], f["bits"]), "host copy of the mask bits"
+    assert f["n"].sum() >= 1
+    # the two-call path: identical argmax / max; conf and lse up to the fold order
+    assert np.array_equal(f["am"], u["am"]) and np.array_equal(f["mx"], u["mx"])
+    assert np.allclose(f["conf"], u["conf"], rtol=1e-5, atol=0) and np.allclose(f["lse"], u["lse"], rtol=1e-5, atol=1e-5)
+    taus_b = taus if tau == "dev" else np.full(B, tau, np.float32)
+    near = (np.abs(f["conf"] - taus_b[:, None]) <= 1e-5 * np.maximum(1.0, taus_b[:, None])).any(axis=1)
+    same = ~near
+    for key in ("tok", "bits", "n", "pos"):
+        assert np.array_equal(f[key][same], u[key][same]), f"{name}: {key} differs from the two-call path"
+
+
+# --------------------------------------------------------------------------
 # bd_kv_append (bit-exact) and capacity
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
