@@ -168,12 +168,42 @@ class Loop:
         self.tokens += int(np.bitwise_count(self.bits ^ bits).sum())
         self.bits = bits
         if not (bits & self.wmask[self.s]).any():
-            self.s += 1
-            self.first = True
-            if self.s == cfg.D // S:
-                dec.commit()
-                self.commits += 1
-                self._new_block()
+            self._next_window()
+
+    def _next_window(self):
+        self.s += 1
+        self.first = True
+        if self.s == self.cfg.D // self.cfg.S:
+            self.dec.commit()
+            self.commits += 1
+            self._new_block()
+
+    def window(self) -> int:
+        """The current window from its exact step on, as one captured graph of
+        S step slots and one wait; returns the refinement steps it took (the
+        slots before which a masked position of the window was left)."""
+        assert self.first
+        ring = self.dec.run_window(self.s, self.cfg.S, self.cfg.tau)
+        wm = self.wmask[self.s]
+        before = np.concatenate([self.bits[None], ring[:-1]])
+        steps = int(((before & wm) != 0).any(axis=1).sum())
+        self.tokens += int(np.bitwise_count(self.bits ^ ring[-1]).sum())
+        self.bits = ring[-1]
+        self.steps += steps
+        assert not (self.bits & wm).any()
+        self._next_window()
+        return steps
+
+    def run(self, n: int, windows: bool):
+        """Exactly n refinement steps: whole windows while at least S steps
+        remain (with window graphs), single steps otherwise."""
+        left = n
+        while left > 0:
+            if windows and self.first and left >= self.cfg.S:
+                left -= self.window()
+            else:
+                self.step()
+                left -= 1
 
 
 def time_call(fn, reps, warm=3, warm_s=0.1):
@@ -336,13 +366,11 @@ def extras_subblock(w3, graphs, steps=40, warmup=10):
         if graphs:
             dec.capture(cfg.S, cfg.tau)
         loop = Loop(dec, cfg, plants)
-        for _ in range(warmup):
-            loop.step()
+        loop.run(warmup, graphs)
         torch.cuda.synchronize()
         s0, t0_tok = loop.steps, loop.tokens
         t0 = time.perf_counter()
-        for _ in range(steps):
-            loop.step()
+        loop.run(steps, graphs)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         n, tok = loop.steps - s0, loop.tokens - t0_tok
@@ -556,6 +584,9 @@ def main():
     ap.add_argument("--reps", type=int, default=20, help="repetitions of the single-call measurements")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-graphs", action="store_true", help="launch every step's kernels eagerly")
+    ap.add_argument("--no-window-graphs", action="store_true",
+                    help="replay one captured step at a time (a host wait after every step) instead of one "
+                         "captured graph per window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "v1"),
@@ -597,15 +628,14 @@ def main():
     if not args.no_graphs:
         dec.capture(cfg.S, cfg.tau)
     loop = Loop(dec, cfg, plants)
-    for _ in range(args.warmup):
-        loop.step()
+    windows = not args.no_graphs and not args.no_window_graphs
+    loop.run(args.warmup, windows)
     torch.cuda.synchronize()
-    # timed region: the headline loop (captured steps replayed as HIP graphs)
+    # timed region: the headline loop (captured windows replayed as HIP graphs)
     s0, t0_tok, c0 = loop.steps, loop.tokens, loop.commits
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        loop.step()
+    loop.run(args.steps, windows)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     steps = loop.steps - s0
@@ -668,7 +698,7 @@ def main():
                    "global_batch": cfg.B, "block": cfg.D, "sub_block": cfg.S, "threshold": cfg.tau},
         "decoded_tokens_per_s": round(tokens / elapsed, 1),
         "tokens_per_step": round(tokens / steps, 3),
-        "graphs": not args.no_graphs,
+        "graphs": ("one per window" if windows else "one per step") if not args.no_graphs else None,
         "ms_per_step_eager": round(elapsed_eager / args.steps * 1e3, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -62,6 +62,13 @@ struct LmK {
   int32_t* pidx;
   float* psum;
   const int32_t* m_dev;  // device row count, or NULL
+  // optional skip test (the LM head fused with the unmask): the launch does
+  // nothing when no sequence b < skip_B has a bit of skip_mask set in
+  // skip_bits[b], i.e. no masked position is left in the window
+  const uint64_t* skip_bits;
+  uint64_t skip_mask;
+  int skip_B;
+  int32_t* ran;  // with the skip test: 1 when the launch computed, else 0
 };
 
 // Rows taken: min(M, *m_dev) when a device count is given (the row list of
@@ -169,9 +176,17 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
     for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
   BdArgStat run{BD_NEG_INF, INT_MAX, 0.f};  // threads tid < MT*16: row m0 + tid over the passes so far
 
+  // the skip test's bits load with the row indices (at most 64 sequences)
+  uint64_t skip_word = 0;
+  if (a.skip_bits != nullptr && lane < a.skip_B) skip_word = a.skip_bits[lane];
   // the row-index loads (and every other global load so far) complete before
   // the pipeline starts, so no register wait is left for the loop
   __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+  if (a.skip_bits != nullptr) {
+    const bool go = __ballot((skip_word & a.skip_mask) != 0) != 0;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *a.ran = go ? 1 : 0;  // for the merge
+    if (!go) return;  // no masked position left in the window: nothing to predict
+  }
 #pragma unroll
   for (int c = 0; c < C::NS - 1; ++c)
     if (c < nst) issue_next();
@@ -624,6 +639,11 @@ __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_i
   if (lse != nullptr) lse[om] = ok ? mx + bd_log2(s) * BD_LN2 : nan;
 }
 
+// The fused call's skip flag: 16 bytes after the partials.
+int32_t* lm_ran_flag(const BdLmPlan& p, const BdLmArgs& x) {
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(x.pmax) + p.ws_bytes - 16);
+}
+
 // Merge fused with the threshold unmask: one work-group per sequence.  The
 // sequence's win_len rows are padded to RP (a power of two) lanes, so one
 // load instruction of a wave covers 64 / RP tiles x RP consecutive rows
@@ -631,17 +651,24 @@ __global__ __launch_bounds__(kThreads) void lm_merge_kernel(const int32_t* row_i
 // partials are [tile][row]).  Lane (q, r) folds tiles q + (64 / RP) * (wave
 // + 8 u) of row r in batches held in registers; lanes of one row, then the 8
 // waves (through LDS), combine their (max, argmax, sum) in a fixed order.
-// Wave 0 lane r then holds row r: it writes the statistics and the wave
-// applies the threshold rule.  Saves the unmask launch of the step.
+// Wave 0 lane r then holds row r: it writes the statistics (unless the LM
+// head skipped its work: no masked position in the window of any sequence)
+// and the wave applies the threshold rule.
+// Saves the unmask launch of the step.
 __global__ __launch_bounds__(kFuseThreads) void lm_merge_unmask_kernel(const int32_t* row_idx, int n_src, int nvt,
                                                                       const float* pmax, const int32_t* pidx,
                                                                       const float* psum, int32_t* argmax, float* conf,
                                                                       float* max_logit, float* lse, int M, int RP,
-                                                                      BdLmUnmask u) {
+                                                                      const int32_t* ran, BdLmUnmask u) {
   constexpr int NW = kFuseThreads / 64;
   __shared__ BdArgStat sh[NW][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
+  // this sequence's bits before the unmask below (only this work-group writes
+  // them) and whether the LM head computed (it skips a window with no masked
+  // position in any sequence: then the statistics are left as they were)
+  const uint64_t bits0 = u.mask_bits[b];
+  const bool computed = ran == nullptr || *ran != 0;
   const int r = lane & (RP - 1);
   const int q = lane / RP;
   const int tpi = 64 / RP;                // tiles per wave instruction
@@ -681,7 +708,7 @@ __global__ __launch_bounds__(kFuseThreads) void lm_merge_unmask_kernel(const int
     for (int w = 1; w < NW; ++w) st = bd_stat_combine(st, sh[w][r]);
   float c = BD_NEG_INF;
   int32_t am = -1;
-  if (live && q == 0) {
+  if (live && q == 0 && computed) {
     const int src = row_idx ? row_idx[m] : m;
     const bool ok = src >= 0 && src < n_src && st.s > 0.f;
     const float nan = __builtin_nanf("");
@@ -694,7 +721,7 @@ __global__ __launch_bounds__(kFuseThreads) void lm_merge_unmask_kernel(const int
   }
   // lane r (< RP, so q == 0) holds window entry r
   const float thr = u.threshold_dev != nullptr ? u.threshold_dev[b] : u.threshold;
-  bd_unmask_wave(lane, b, u.D, u.win_lo, u.win_len, u.mask_bits[b], lane < RP ? c : BD_NEG_INF,
+  bd_unmask_wave(lane, b, u.D, u.win_lo, u.win_len, bits0, lane < RP ? c : BD_NEG_INF,
                  lane < RP ? am : -1, thr, u.tokens, u.mask_bits, u.n_unmasked, u.unmasked_pos, u.bits_out);
 }
 
@@ -720,6 +747,7 @@ BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
   if (dt == BD_F32 || M > 64) p.nvt = (V + p.cols_per_wg - 1) / p.cols_per_wg;
   p.nmb = (M + p.rows_per_wg - 1) / p.rows_per_wg;
   p.ws_bytes = (size_t)M * p.nvt * (2 * sizeof(float) + sizeof(int32_t));
+  p.ws_bytes = (p.ws_bytes + 15) / 16 * 16 + 16;  // then the skip flag of the fused call
   (void)hidden;
   return p;
 }
@@ -732,7 +760,13 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
     hipLaunchKernelGGL(lm_f32_kernel, grid, dim3(kThreads), 0, s, a);
   } else {
     LmK a{static_cast<const uint16_t*>(x.h), x.n_src, x.row_idx, static_cast<const uint16_t*>(x.w), x.logits,
-          x.M, x.hidden, x.V, p.nvt, x.pmax, x.pidx, x.psum, x.m_dev};
+          x.M, x.hidden, x.V, p.nvt, x.pmax, x.pidx, x.psum, x.m_dev, nullptr, 0, 0, nullptr};
+    if (um != nullptr && p.rows_per_wg != kBigRows) {  // the fused call: skip when the window has no candidate
+      a.skip_bits = um->mask_bits;
+      a.skip_mask = (um->win_len >= 64 ? ~0ull : ((1ull << um->win_len) - 1ull)) << um->win_lo;
+      a.skip_B = um->B;
+      a.ran = lm_ran_flag(p, x);
+    }
     switch (p.rows_per_wg / 16) {
       case kBigRows / 16: {
         const int cb8 = (p.nvt + 7) / 8 * 8;  // column blocks rounded up to whole XCD rounds
@@ -755,7 +789,8 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
     int rp = 1;
     while (rp < um->win_len) rp <<= 1;
     hipLaunchKernelGGL(lm_merge_unmask_kernel, dim3(um->B), dim3(kFuseThreads), 0, s, x.row_idx, x.n_src, p.nvt,
-                       x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse, x.M, rp, *um);
+                       x.pmax, x.pidx, x.psum, x.argmax, x.conf, x.max_logit, x.lse, x.M, rp,
+                       dt == BD_F32 ? nullptr : lm_ran_flag(p, x), *um);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(lm_merge_kernel, dim3(x.M), dim3(kThreads), 0, s, x.row_idx, x.n_src, x.M, p.nvt,

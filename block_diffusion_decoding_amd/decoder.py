@@ -87,7 +87,8 @@ class BlockDecoder:
         self.last = None
         self.lm_events = None   # list of (start, end) events around LM-head calls when set
         self._capturing = False
-        self.graphs = {}        # (kind, s) -> captured HIP graph of that step
+        self.graphs = {}        # (kind, s) -> captured HIP graph of that step ("W": whole window)
+        self._rings = {}        # S -> [S, B] pinned: mask bits after each step slot of a window
 
     # ------------------------------------------------------------------ state
     def set_synthetic_prefix(self, kv_len, cache_k, cache_v, carry):
@@ -180,7 +181,10 @@ class BlockDecoder:
                           D=D, q_off=lo)
         return X, o
 
-    def _lm_and_unmask(self, s: int, S: int, tau: float):
+    def _lm_and_unmask(self, s: int, S: int, tau: float, bits_out=None):
+        """LM head on the window's rows, then the threshold rule; the new mask
+        bits also land in the pinned host tensor bits_out (default bits_host)."""
+        bits_out = self.bits_host if bits_out is None else bits_out
         w = self._window(s, S)
         dm = self.dims
         ev = None
@@ -201,7 +205,7 @@ class BlockDecoder:
             ops.bd_lmhead_unmask(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"], w["conf"],
                                  self.tokens, self.mask_bits, win_lo=s * S, threshold=tau, max_logit=w["maxl"],
                                  lse=w["lse"], n_unmasked=self.n_unmasked, unmasked_pos=w["pos"],
-                                 mask_bits_host=self.bits_host)
+                                 mask_bits_host=bits_out)
             fused = True
         else:
             ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"],
@@ -212,7 +216,7 @@ class BlockDecoder:
         if not fused:
             ops.bd_threshold_unmask(w["conf"], w["argmax"], self.tokens, self.mask_bits, win_lo=s * S,
                                     threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
-            self.bits_host.copy_(self.mask_bits, non_blocking=True)
+            bits_out.copy_(self.mask_bits, non_blocking=True)
         self.last = w
 
     def uses_compaction(self, S: int) -> bool:
@@ -222,7 +226,7 @@ class BlockDecoder:
         self._bits_ev.record()
         self._bits_fresh = True
 
-    def e_step(self, s: int, S: int, tau: float, eager: bool = False):
+    def e_step(self, s: int, S: int, tau: float, eager: bool = False, bits_out=None):
         """Exact step for window s; refreshes the DualCache snapshot."""
         if eager or not self._replay("E", s, S, tau):
             dm = self.dims
@@ -230,11 +234,11 @@ class BlockDecoder:
             X, o = self._forward_rows(0, D)
             ops.bd_linear(o, dense(B * D), self.W["Wo"], self.H, rows(D, 1 + D, 1), M=B * D,
                           res=X, rr=dense(B * D))
-            self._lm_and_unmask(s, S, tau)
+            self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
             self._step_done()
 
-    def dc_step(self, s: int, S: int, tau: float, eager: bool = False):
+    def dc_step(self, s: int, S: int, tau: float, eager: bool = False, bits_out=None):
         """DualCache step for window s (snapshot rows outside the window)."""
         if eager or not self._replay("DC", s, S, tau):
             dm = self.dims
@@ -242,7 +246,7 @@ class BlockDecoder:
             X, o = self._forward_rows(s * S, S)
             ops.bd_linear(o, dense(B * S), self.W["Wo"], self.H, rows(S, 1 + D, 1 + s * S), M=B * S,
                           res=X, rr=dense(B * S))
-            self._lm_and_unmask(s, S, tau)
+            self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
             self._step_done()
 
@@ -319,6 +323,22 @@ class BlockDecoder:
                     self.graphs[(kind, s)] = g
         finally:
             self._capturing = False
+        # a whole window in one graph: its exact step and S - 1 DualCache steps
+        # (a window never needs more: every step decodes at least one masked
+        # position of each sequence that has one), each step writing its new
+        # mask bits to its own row of the pinned ring.  Steps past the end of
+        # the window find no candidate and their LM head does no work.
+        ring = self._ring(S)
+        self._capturing = True
+        try:
+            for s in range(D // S):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(S):
+                        (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[i])
+                self.graphs[("W", s)] = g
+        finally:
+            self._capturing = False
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             self._commit_kernels()
@@ -337,21 +357,52 @@ class BlockDecoder:
                              for M in (B * S, B * D)] +
                             [ops.bd_linear_workspace_size(dt, M, dm.hidden, dm.Hq * dm.d) for M in (B, B * S, B * D)])}
 
+    def _replay_ok(self, S: int, tau) -> bool:
+        """Whether the captured steps match (S, tau): a threshold tensor is read
+        by the replayed kernels, so the same tensor (whatever values it holds
+        now) matches the capture."""
+        if self.lm_events is not None:
+            return False
+        same_tau = (tau is self._graph_tau) if isinstance(tau, torch.Tensor) or \
+            isinstance(self._graph_tau, torch.Tensor) else tau == self._graph_tau
+        return S == self._graph_S and same_tau
+
     def _replay(self, kind: str, s: int, S: int, tau: float) -> bool:
         g = self.graphs.get((kind, s))
         if g is None or self.lm_events is not None:
             return False
-        if kind != "commit":
-            # a threshold tensor is read by the replayed kernels: the same
-            # tensor (whatever values it holds now) matches the capture
-            same_tau = (tau is self._graph_tau) if isinstance(tau, torch.Tensor) or \
-                isinstance(self._graph_tau, torch.Tensor) else tau == self._graph_tau
-            if S != self._graph_S or not same_tau:
-                return False
+        if kind != "commit" and not self._replay_ok(S, tau):
+            return False
         g.replay()
         if kind != "commit":
             self.last = self._window(s, S)
         return True
+
+    def _ring(self, S: int):
+        """Pinned [S, B] mask-bit ring of windows of S positions (kept for the
+        decoder's lifetime: captured window graphs write into it)."""
+        r = self._rings.get(S)
+        if r is None:
+            r = self._rings[S] = torch.zeros(S, self.dims.B, dtype=torch.int64, pin_memory=True)
+        return r
+
+    def run_window(self, s: int, S: int, tau) -> np.ndarray:
+        """Window s from its exact step on: S step slots (one graph replay when
+        captured), then one wait.  Returns the mask bits after every slot
+        [S, B] (uint64); slot i was a refinement step iff some sequence still
+        had a masked position of the window before it."""
+        g = self.graphs.get(("W", s))
+        ring = self._ring(S)
+        if g is not None and self._replay_ok(S, tau):
+            g.replay()
+            self.last = self._window(s, S)
+        else:
+            for i in range(S):
+                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[i])
+        self._bits_ev.record()
+        self._bits_ev.synchronize()
+        self._bits_fresh = False
+        return ring.numpy().view(np.uint64).copy()
 
     # ------------------------------------------------------------------ loop
     def decode_block(self, S: int, tau: float, mode: str = "dual", steps_per_window: int | None = None,

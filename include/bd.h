@@ -242,6 +242,10 @@ bd_status bd_threshold_unmask_tau(int B, int D, int win_lo, int win_len,
  *     the stream has passed this call (e.g. after an event recorded behind
  *     it has completed).
  *   workspace: bd_lmhead_workspace_size(dt, B * win_len, hidden, V) bytes.
+ * When no sequence has a masked position in the window the LM head does no
+ * work: tokens, bits and the statistics are left as they were and only
+ * mask_bits_host is written.  A captured step can thus be replayed past the
+ * end of its window at the cost of its other kernels.
  * Requires B * win_len <= 64 and the rules of both calls.
  * ---------------------------------------------------------------------- */
 bd_status bd_lmhead_unmask(bd_dtype dt, int B, int D, int win_lo, int win_len, int hidden, int V,

@@ -261,13 +261,15 @@ def test_lmhead_unmask(name):
     ridx = np.array([b * (1 + D) + win * S + r for b in range(B) for r in range(S)], dtype=np.int32)
     masked = rng.random((B, D)) < 0.6
     masked[0, win * S:(win + 1) * S] = True
+    if B > 1:
+        masked[B - 1, win * S:(win + 1) * S] = False   # a sequence with no candidate
     tokens = np.where(masked, 0, rng.integers(0, V, size=(B, D))).astype(np.int32)
     taus = rng.choice(np.array([0.3, 0.6, 0.9, 1.0], np.float32), size=B).astype(np.float32)
     thr = up(taus) if tau == "dev" else tau
     outs = []
     for fused in (True, False):
-        am = torch.zeros(B, S, dtype=torch.int32, device=DEV)
-        conf, mx, lse = (torch.zeros(B, S, dtype=torch.float32, device=DEV) for _ in range(3))
+        am = torch.full((B, S), -5, dtype=torch.int32, device=DEV)
+        conf, mx, lse = (torch.full((B, S), -5.0, dtype=torch.float32, device=DEV) for _ in range(3))
         t_tok, t_bits = up(tokens), up(bi.mask_bits(masked).view(np.int64))
         n = torch.full((B,), -7, dtype=torch.int32, device=DEV)
         pos = torch.full((B, S), -7, dtype=torch.int32, device=DEV)
@@ -286,10 +288,12 @@ def test_lmhead_unmask(name):
                          tok=t_tok.cpu().numpy(), bits=t_bits.cpu().numpy().view(np.uint64),
                          n=n.cpu().numpy(), pos=pos.cpu().numpy(), host=host.numpy().view(np.uint64).copy()))
     f, u = outs
+    # every row has statistics (some sequence had a candidate)
+    has = np.ones(B, bool)
     # the oracle: statistics of every row, then the rule on the call's own conf/argmax
-    ref = R.lm_logits(w, h[ridx])
-    lm_stats_close(f["am"].reshape(-1), f["conf"].reshape(-1), f["mx"].reshape(-1), f["lse"].reshape(-1), ref,
-                   TOL[dt], name)
+    ref = R.lm_logits(w, h[ridx]).reshape(B, S, -1)[has].reshape(-1, V)
+    lm_stats_close(f["am"][has].reshape(-1), f["conf"][has].reshape(-1), f["mx"][has].reshape(-1),
+                   f["lse"][has].reshape(-1), ref, TOL[dt], name)
     for b in range(B):
         tb = np.float32(taus[b]) if tau == "dev" else np.float32(tau)
         rt, rm, rn, rp = R.batch_threshold_unmask(f["conf"][b:b + 1], f["am"][b:b + 1], tokens[b:b + 1],
@@ -300,13 +304,45 @@ def test_lmhead_unmask(name):
     assert np.array_equal(f["host"], f["bits"]), "host copy of the mask bits"
     assert f["n"].sum() >= 1
     # the two-call path: identical argmax / max; conf and lse up to the fold order
-    assert np.array_equal(f["am"], u["am"]) and np.array_equal(f["mx"], u["mx"])
-    assert np.allclose(f["conf"], u["conf"], rtol=1e-5, atol=0) and np.allclose(f["lse"], u["lse"], rtol=1e-5, atol=1e-5)
+    assert np.array_equal(f["am"][has], u["am"][has]) and np.array_equal(f["mx"][has], u["mx"][has])
+    assert np.allclose(f["conf"][has], u["conf"][has], rtol=1e-5, atol=0)
+    assert np.allclose(f["lse"][has], u["lse"][has], rtol=1e-5, atol=1e-5)
     taus_b = taus if tau == "dev" else np.full(B, tau, np.float32)
     near = (np.abs(f["conf"] - taus_b[:, None]) <= 1e-5 * np.maximum(1.0, taus_b[:, None])).any(axis=1)
     same = ~near
     for key in ("tok", "bits", "n", "pos"):
         assert np.array_equal(f[key][same], u[key][same]), f"{name}: {key} differs from the two-call path"
+
+
+def test_lmhead_unmask_window_without_candidates():
+    """No sequence has a masked position in the window: the call changes no
+    token, bit or statistic (the LM head is skipped) and still writes the
+    host copy of the bits; the next window of the same batch then decodes."""
+    say("[lmhead+unmask] empty window")
+    B, S, D, hidden, V = 8, 8, 32, 512, 5000
+    w = bi.normal(5, "Wlm", (V, hidden), 0.02, "bf16")
+    h = bi.normal(5, "h", (B * (1 + D), hidden), 0.6, "bf16")
+    masked = np.zeros((B, D), bool)
+    masked[:, 16:] = True                      # window 1 ([8, 16)) is fully decoded
+    tokens = np.arange(B * D, dtype=np.int32).reshape(B, D)
+    T = torch.bfloat16
+    am = torch.full((B, S), -5, dtype=torch.int32, device=DEV)
+    conf = torch.full((B, S), -5.0, dtype=torch.float32, device=DEV)
+    t_tok, t_bits = up(tokens), up(bi.mask_bits(masked).view(np.int64))
+    n = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    host = torch.zeros(B, dtype=torch.int64, pin_memory=True)
+    for win in (1, 2):
+        ridx = np.array([b * (1 + D) + win * S + r for b in range(B) for r in range(S)], dtype=np.int32)
+        ops().bd_lmhead_unmask(up(h, T), up(ridx), up(w, T), am, conf, t_tok, t_bits, win_lo=win * S,
+                               threshold=0.9, n_unmasked=n, mask_bits_host=host)
+        torch.cuda.synchronize()
+        if win == 1:
+            assert (am.cpu().numpy() == -5).all() and (conf.cpu().numpy() == -5.0).all()
+            assert np.array_equal(t_tok.cpu().numpy(), tokens) and (n.cpu().numpy() == 0).all()
+            assert np.array_equal(host.numpy(), bi.mask_bits(masked).view(np.int64))
+    # window 2 had candidates in every sequence: at least one token each
+    assert (n.cpu().numpy() >= 1).all() and (am.cpu().numpy() >= 0).all()
+    assert np.array_equal(host.numpy(), t_bits.cpu().numpy())
 
 
 # --------------------------------------------------------------------------

@@ -93,3 +93,52 @@ def test_captured_steps_follow_a_device_threshold_schedule():
                 assert torch.equal(a, b), f"window {s} step {k} ({kind}) differs"
             step += 1
     assert len(graph.graphs) > 0
+
+
+@pytest.mark.parametrize("compact", [None, True])
+def test_window_graphs_decode_like_single_steps(compact):
+    """One captured graph per window (its exact step and S - 1 DualCache
+    step slots) against single eager steps taken until the window is
+    decoded: the same mask bits after every refinement step, the same tokens
+    after every window, the same committed cache and carry after every block.
+    Slots past the end of the window change no token and no bit.  compact:
+    the LM head over the masked candidates only (row list, device count);
+    None here: the LM head fused with the unmask."""
+    say(f"[graphs] window graphs vs single steps (compact={compact})")
+    cfg = MID
+    w, pre, st, _, _ = workload(cfg, 0, all_masked=True, plant_rate=None)
+    eager = gpu_decoder(cfg, w, pre, st, compact=compact)
+    graph = gpu_decoder(cfg, w, pre, st, compact=compact)
+    S, tau = cfg.S, 0.6
+    graph.capture(S, tau)
+    rng = np.random.default_rng(5)
+    wins = cfg.D // S
+    n_steps = 0
+    for blk in range(2):
+        plant = bi.normal(10 + blk, "plant", (cfg.B, cfg.D, cfg.hidden), 0.5, "bf16")
+        plant[rng.random((cfg.B, cfg.D)) < 0.5] = 0.0
+        for d in (eager, graph):
+            d.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plant)
+        for s in range(wins):
+            wmask = np.uint64(((1 << S) - 1) << (s * S))
+            seen = []
+            k = 0
+            while k == 0 or (eager.mask_bits_host() & wmask).any():
+                (eager.e_step if k == 0 else eager.dc_step)(s, S, tau)
+                seen.append(eager.mask_bits_host())
+                k += 1
+            assert k <= S
+            ring = graph.run_window(s, S, tau)
+            assert ring.shape == (S, cfg.B)
+            for i in range(S):
+                want = seen[i] if i < k else seen[-1]
+                assert np.array_equal(ring[i], want), f"block {blk} window {s} slot {i}"
+            assert torch.equal(eager.tokens, graph.tokens) and torch.equal(eager.mask_bits, graph.mask_bits)
+            assert np.array_equal(graph.mask_bits_host(), seen[-1])
+            n_steps += k
+        for d in (eager, graph):
+            d.commit()
+        torch.cuda.synchronize()
+        assert torch.equal(eager.cache_k, graph.cache_k) and torch.equal(eager.cache_v, graph.cache_v)
+        assert torch.equal(eager.kv_len, graph.kv_len) and torch.equal(eager.H[:, 0], graph.H[:, 0])
+    assert n_steps > 2 * wins
