@@ -80,7 +80,7 @@ def kernel_source_hash() -> str:
 def traffic_from(fetch_csv, write_csv):
     """Turn two rocprofv3 --pmc counter files (FETCH_SIZE, then WRITE_SIZE, both
     over `bench.py --section lm`) into the HBM bytes per launch of the 64-row
-    7B LM head. Each counter is scaled by what it reads for the 1 GiB plain
+    7B LM head fused with the unmask (the refinement step's call). Each counter is scaled by what it reads for the 1 GiB plain
     device copy that run makes (the copy reads and writes exactly CALIB_BYTES)."""
     import csv
 
@@ -88,13 +88,13 @@ def traffic_from(fetch_csv, write_csv):
         return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
 
     out = {"kernel_source_hash": kernel_source_hash(), "calibration_bytes": CALIB_BYTES,
-           "launch": "lm_stream_kernel<4> (512 work-groups) + lm_merge_kernel (grid 64 x 256), 64 rows x 152064 x 3584"}
+           "launch": "bd_lmhead_unmask: lm_stream_kernel<4> (512 work-groups) + lm_merge_unmask_kernel (8 "
+                     "work-groups x 512), 64 rows x 152064 x 3584 (8 sequences x window of 8)"}
     total = 0.0
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         rs = rows(path, counter)
         main = [float(r["Counter_Value"]) for r in rs if "lm_stream_kernel<4>" in r["Kernel_Name"]]
-        merge = [float(r["Counter_Value"]) for r in rs
-                 if "lm_merge_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) == 64 * 256]
+        merge = [float(r["Counter_Value"]) for r in rs if "lm_merge_unmask_kernel" in r["Kernel_Name"]]
         cp = [float(r["Counter_Value"]) for r in rs
               if "copyBuffer" in r["Kernel_Name"] or "copy_kernel" in r["Kernel_Name"]]
         if not main or not merge or not cp:
@@ -132,6 +132,33 @@ def block_plants(cfg, w, rate, seed, n_blocks):
         plant, _, _ = bi.make_plants(cfg, seed + 1000 + k, w, st, rate)
         out.append(torch.from_numpy(plant).to("cuda", torch.bfloat16))
     return out
+
+
+class LaunchTimer:
+    """HIP events around launches on the current stream.  Before each start
+    event a short spin kernel is queued, so the host has queued the timed
+    launch before the GPU reaches the event: the interval holds GPU time only
+    (without it, a GPU that has caught up with the host would wait inside the
+    interval for the launch to be submitted)."""
+
+    SPIN_CYCLES = 200000
+
+    def __init__(self):
+        self.events = []
+
+    def start(self):
+        torch.cuda._sleep(self.SPIN_CYCLES)
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.events.append([ev, None])
+
+    def stop(self):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.events[-1][1] = ev
+
+    def seconds(self) -> np.ndarray:
+        return np.array([a.elapsed_time(b) for a, b in self.events]) * 1e-3
 
 
 class Loop:
@@ -530,6 +557,28 @@ def extras_lm(w3, reps):
                     "GB/s": nbytes / mean / 1e9, "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
         log(f"[bench] lm head M={M}: {mean * 1e6:.1f} us, {flops / mean / 1e12:.0f} TFLOP/s, "
             f"{nbytes / mean / 1e9:.0f} GB/s")
+    # ---- the refinement step's call: the 64-row LM head fused with the
+    # threshold unmask (8 sequences x window of 8); the window's mask bits are
+    # restored before every call (one 64-byte device copy, timed with it), or
+    # the calls would decode the window and then skip the LM head
+    B, S, D = 8, 8, 32
+    h = torch.randn(B * (1 + D), 3584, device="cuda", dtype=T) * 0.05
+    ridx = torch.tensor([b * (1 + D) + 8 + r for b in range(B) for r in range(S)], dtype=torch.int32, device="cuda")
+    am = torch.empty(B, S, dtype=torch.int32, device="cuda")
+    cf = torch.empty(B, S, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(B, D, dtype=torch.int32, device="cuda")
+    bits0 = torch.full((B,), -1, dtype=torch.int64, device="cuda")
+    bits = bits0.clone()
+    host = torch.zeros(B, dtype=torch.int64, pin_memory=True)
+
+    def fused():
+        bits.copy_(bits0)
+        ops.bd_lmhead_unmask(h, ridx, Wlm, am, cf, tok, bits, win_lo=8, threshold=0.9, mask_bits_host=host)
+    med, mean = time_call(fused, reps)
+    nbytes = 152064 * 3584 * 2 + 64 * 3584 * 2 + 16 * 64
+    out["lmhead_unmask_7B_B8_S8"] = {"us_with_bits_reset": mean * 1e6, "GB/s": nbytes / mean / 1e9,
+                                     "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
+    log(f"[bench] lm head + unmask B=8 S=8: {mean * 1e6:.1f} us with the bits reset, {nbytes / mean / 1e9:.0f} GB/s")
     del Wlm
     # ---- LM head alone: batch 1 on the 1.5B head (HBM bound)
     c2 = bi.C2
@@ -643,21 +692,19 @@ def main():
     steps_per_s = steps / elapsed
     log(f"[bench] {steps} steps in {elapsed * 1e3:.1f} ms: {steps_per_s:.1f} steps/s, "
         f"{tokens / elapsed:.0f} tokens/s, {loop.commits - c0} commits")
-    # second timed pass of the same loop with eager launches and HIP events
+    # second pass of the same loop, steps launched one by one, with HIP events
     # around every LM-head launch (a kernel inside a graph replay cannot be
     # timed by events): the dominant kernel's launch durations
-    dec.lm_events = []
-    s1 = loop.steps
+    timer = LaunchTimer()
+    dec.lm_timer = timer
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     for _ in range(args.steps):
         loop.step()
     torch.cuda.synchronize()
-    elapsed_eager = time.perf_counter() - t1
-    lm_t = np.array([a.elapsed_time(b) for a, b in dec.lm_events]) * 1e-3
-    dec.lm_events = None
-    log(f"[bench] eager pass: {(loop.steps - s1) / elapsed_eager:.1f} steps/s, LM head {lm_t.mean() * 1e6:.1f} us "
-        f"over {len(lm_t)} launches")
+    lm_t = timer.seconds()
+    dec.lm_timer = None
+    log(f"[bench] LM head (bd_lmhead_unmask) {lm_t.mean() * 1e6:.1f} us mean, {np.median(lm_t) * 1e6:.1f} us median "
+        f"over {len(lm_t)} launches of the loop")
 
     # roofline of the dominant kernel: LM head of the 7B step (B*S = 64 rows)
     M = cfg.B * cfg.S
@@ -676,8 +723,9 @@ def main():
                           "with the threshold unmask), 64 rows x 152064 x 3584",
                 "algorithmic_bytes": lm_bytes, "launch_us_mean": round(lm_mean * 1e6, 2),
                 "launch_us_median": round(float(np.median(lm_t)) * 1e6, 2),
-                "timing": f"HIP events around each of {len(lm_t)} LM-head launches of a second timed pass of "
-                          "the same loop (eager launches) on the launch stream"}
+                "timing": f"HIP events around each of {len(lm_t)} LM-head launches of a second pass of the same "
+                          "loop (steps launched one by one) on the launch stream; a spin kernel before each start "
+                          "event keeps the host ahead of the GPU, so no interval holds host launch time"}
     extra = {}
     if not args.no_extras:
         del dec
@@ -699,7 +747,6 @@ def main():
         "decoded_tokens_per_s": round(tokens / elapsed, 1),
         "tokens_per_step": round(tokens / steps, 3),
         "graphs": ("one per window" if windows else "one per step") if not args.no_graphs else None,
-        "ms_per_step_eager": round(elapsed_eager / args.steps * 1e3, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -50,6 +50,11 @@ class Dims:
 class BlockDecoder:
     """Owns the device state of a batch of sequences decoded block by block."""
 
+    # capture() also records one graph per window (run_window): worth it when a
+    # step slot past the end of a window (whose LM head does no work) costs
+    # less than a host wait
+    window_graphs = True
+
     def __init__(self, dims: Dims, weights: dict, dtype=torch.bfloat16, device="cuda", compact=None):
         """``compact``: run the LM head only on the masked candidates of the
         window (bd_candidate_rows + bd_lmhead_confidence_rows); None = when a
@@ -85,7 +90,7 @@ class BlockDecoder:
         self.n_unmasked = torch.zeros(B, dtype=torch.int32, device=dev)
         self._win = {}
         self.last = None
-        self.lm_events = None   # list of (start, end) events around LM-head calls when set
+        self.lm_timer = None    # object whose start() / stop() bracket every LM-head call when set
         self._capturing = False
         self.graphs = {}        # (kind, s) -> captured HIP graph of that step ("W": whole window)
         self._rings = {}        # S -> [S, B] pinned: mask bits after each step slot of a window
@@ -187,10 +192,8 @@ class BlockDecoder:
         bits_out = self.bits_host if bits_out is None else bits_out
         w = self._window(s, S)
         dm = self.dims
-        ev = None
-        if self.lm_events is not None:
-            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            ev[0].record()
+        if self.lm_timer is not None:
+            self.lm_timer.start()
         fused = False
         if self.uses_compaction(S):
             # only the masked candidates: their conf/argmax land at their window
@@ -210,9 +213,8 @@ class BlockDecoder:
         else:
             ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"],
                                      w["conf"], max_logit=w["maxl"], lse=w["lse"])
-        if ev is not None:
-            ev[1].record()
-            self.lm_events.append(ev)
+        if self.lm_timer is not None:
+            self.lm_timer.stop()
         if not fused:
             ops.bd_threshold_unmask(w["conf"], w["argmax"], self.tokens, self.mask_bits, win_lo=s * S,
                                     threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=w["pos"])
@@ -331,7 +333,7 @@ class BlockDecoder:
         ring = self._ring(S)
         self._capturing = True
         try:
-            for s in range(D // S):
+            for s in range(D // S if self.window_graphs else 0):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
                     for i in range(S):
@@ -361,7 +363,7 @@ class BlockDecoder:
         """Whether the captured steps match (S, tau): a threshold tensor is read
         by the replayed kernels, so the same tensor (whatever values it holds
         now) matches the capture."""
-        if self.lm_events is not None:
+        if self.lm_timer is not None:
             return False
         same_tau = (tau is self._graph_tau) if isinstance(tau, torch.Tensor) or \
             isinstance(self._graph_tau, torch.Tensor) else tau == self._graph_tau
@@ -369,7 +371,7 @@ class BlockDecoder:
 
     def _replay(self, kind: str, s: int, S: int, tau: float) -> bool:
         g = self.graphs.get((kind, s))
-        if g is None or self.lm_events is not None:
+        if g is None or self.lm_timer is not None:
             return False
         if kind != "commit" and not self._replay_ok(S, tau):
             return False

@@ -43,6 +43,9 @@ class ModelDecoder(BlockDecoder):
     "Wo", "Wg", "Wu", "Wd"}, ...]} (out x in); gate and up are stored as one
     [2*inter, hid] matrix so that one GEMM makes both."""
 
+    # a step slot past the end of a window still runs every layer: no window graphs
+    window_graphs = False
+
     def __init__(self, dims: ModelDims, weights: dict, dtype=torch.bfloat16, device="cuda", compact=None):
         top = {"E": weights["E"], "Wlm": weights["Wlm"]}
         # BlockDecoder's single-layer buffers are replaced below; give it the
@@ -116,22 +119,22 @@ class ModelDecoder(BlockDecoder):
         return X
 
     # ------------------------------------------------------------------ steps
-    def e_step(self, s: int, S: int, tau: float, eager: bool = False):
+    def e_step(self, s: int, S: int, tau: float, eager: bool = False, bits_out=None):
         """Exact step for window s; refreshes every layer's DualCache snapshot."""
         if eager or not self._replay("E", s, S, tau):
             D = self.dims.D
             self._forward_block_rows(0, D, final=(self.H, rows(D, 1 + D, 1)))
-            self._lm_and_unmask(s, S, tau)
+            self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
             self._step_done()
 
-    def dc_step(self, s: int, S: int, tau: float, eager: bool = False):
+    def dc_step(self, s: int, S: int, tau: float, eager: bool = False, bits_out=None):
         """DualCache step for window s (every layer's snapshot rows outside the
         window; the row feeding the window's first position stays in H)."""
         if eager or not self._replay("DC", s, S, tau):
             D = self.dims.D
             self._forward_block_rows(s * S, S, final=(self.H, rows(S, 1 + D, 1 + s * S)))
-            self._lm_and_unmask(s, S, tau)
+            self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
             self._step_done()
 
