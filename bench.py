@@ -206,9 +206,10 @@ class Loop:
             self._new_block()
 
     def window(self) -> int:
-        """The current window from its exact step on, as one captured graph of
-        S step slots and one wait; returns the refinement steps it took (the
-        slots before which a masked position of the window was left)."""
+        """The current window's first steps (from its exact step on) as one
+        captured graph of slots(S) step slots and one wait; returns the
+        refinement steps they took (the slots before which a masked position
+        of the window was left)."""
         assert self.first
         ring = self.dec.run_window(self.s, self.cfg.S, self.cfg.tau)
         wm = self.wmask[self.s]
@@ -217,16 +218,18 @@ class Loop:
         self.tokens += int(np.bitwise_count(self.bits ^ ring[-1]).sum())
         self.bits = ring[-1]
         self.steps += steps
-        assert not (self.bits & wm).any()
-        self._next_window()
+        self.first = False
+        if not (self.bits & wm).any():
+            self._next_window()
         return steps
 
     def run(self, n: int, windows: bool):
-        """Exactly n refinement steps: whole windows while at least S steps
-        remain (with window graphs), single steps otherwise."""
+        """Exactly n refinement steps: window graphs while at least a graph's
+        slots remain, single steps otherwise."""
         left = n
+        slots = self.dec.slots(self.cfg.S)
         while left > 0:
-            if windows and self.first and left >= self.cfg.S:
+            if windows and self.first and left >= slots:
                 left -= self.window()
             else:
                 self.step()

@@ -52,8 +52,17 @@ class BlockDecoder:
 
     # capture() also records one graph per window (run_window): worth it when a
     # step slot past the end of a window (whose LM head does no work) costs
-    # less than a host wait
+    # less than a host wait.  A window graph holds at most window_slots step
+    # slots: a window of S positions needs at most S steps, but a slot past its
+    # end still runs the step's other kernels (~75 us at the 7B shape, a host
+    # wait ~37 us), so wide windows run their first steps as one graph and the
+    # rest one by one.
     window_graphs = True
+    window_slots = 8
+
+    def slots(self, S: int) -> int:
+        """Step slots of a window graph for windows of S positions."""
+        return min(S, self.window_slots)
 
     def __init__(self, dims: Dims, weights: dict, dtype=torch.bfloat16, device="cuda", compact=None):
         """``compact``: run the LM head only on the masked candidates of the
@@ -325,18 +334,19 @@ class BlockDecoder:
                     self.graphs[(kind, s)] = g
         finally:
             self._capturing = False
-        # a whole window in one graph: its exact step and S - 1 DualCache steps
-        # (a window never needs more: every step decodes at least one masked
-        # position of each sequence that has one), each step writing its new
-        # mask bits to its own row of the pinned ring.  Steps past the end of
-        # the window find no candidate and their LM head does no work.
+        # a window's first steps in one graph: its exact step and slots(S) - 1
+        # DualCache steps (a window never needs more than S: every step decodes
+        # at least one masked position of each sequence that has one), each step
+        # writing its new mask bits to its own row of the pinned ring.  Steps
+        # past the end of the window find no candidate and their LM head does
+        # no work.
         ring = self._ring(S)
         self._capturing = True
         try:
             for s in range(D // S if self.window_graphs else 0):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
-                    for i in range(S):
+                    for i in range(self.slots(S)):
                         (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[i])
                 self.graphs[("W", s)] = g
         finally:
@@ -381,25 +391,27 @@ class BlockDecoder:
         return True
 
     def _ring(self, S: int):
-        """Pinned [S, B] mask-bit ring of windows of S positions (kept for the
-        decoder's lifetime: captured window graphs write into it)."""
+        """Pinned [slots(S), B] mask-bit ring of windows of S positions (kept
+        for the decoder's lifetime: captured window graphs write into it)."""
         r = self._rings.get(S)
         if r is None:
-            r = self._rings[S] = torch.zeros(S, self.dims.B, dtype=torch.int64, pin_memory=True)
+            r = self._rings[S] = torch.zeros(self.slots(S), self.dims.B, dtype=torch.int64, pin_memory=True)
         return r
 
     def run_window(self, s: int, S: int, tau) -> np.ndarray:
-        """Window s from its exact step on: S step slots (one graph replay when
-        captured), then one wait.  Returns the mask bits after every slot
-        [S, B] (uint64); slot i was a refinement step iff some sequence still
-        had a masked position of the window before it."""
+        """Window s from its exact step on: slots(S) step slots (one graph
+        replay when captured), then one wait.  Returns the mask bits after
+        every slot [slots(S), B] (uint64); slot i was a refinement step iff some
+        sequence still had a masked position of the window before it.  When
+        slots(S) < S the window may still have masked positions afterwards:
+        its next steps are DualCache steps."""
         g = self.graphs.get(("W", s))
         ring = self._ring(S)
         if g is not None and self._replay_ok(S, tau):
             g.replay()
             self.last = self._window(s, S)
         else:
-            for i in range(S):
+            for i in range(self.slots(S)):
                 (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[i])
         self._bits_ev.record()
         self._bits_ev.synchronize()

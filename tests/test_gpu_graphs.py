@@ -95,22 +95,26 @@ def test_captured_steps_follow_a_device_threshold_schedule():
     assert len(graph.graphs) > 0
 
 
-@pytest.mark.parametrize("compact", [None, True])
-def test_window_graphs_decode_like_single_steps(compact):
-    """One captured graph per window (its exact step and S - 1 DualCache
-    step slots) against single eager steps taken until the window is
+@pytest.mark.parametrize("compact,S", [(None, 8), (True, 8), (None, 16)])
+def test_window_graphs_decode_like_single_steps(compact, S):
+    """One captured graph per window (its exact step and slots(S) - 1
+    DualCache step slots, then single DualCache steps while the window has
+    masked positions) against single eager steps taken until the window is
     decoded: the same mask bits after every refinement step, the same tokens
     after every window, the same committed cache and carry after every block.
     Slots past the end of the window change no token and no bit.  compact:
     the LM head over the masked candidates only (row list, device count);
-    None here: the LM head fused with the unmask."""
-    say(f"[graphs] window graphs vs single steps (compact={compact})")
-    cfg = MID
+    None here: the LM head fused with the unmask.  S = 16: a window graph
+    holds 8 of the window's up to 16 steps."""
+    say(f"[graphs] window graphs vs single steps (compact={compact}, S={S})")
+    cfg = replace(MID, S=S)
     w, pre, st, _, _ = workload(cfg, 0, all_masked=True, plant_rate=None)
     eager = gpu_decoder(cfg, w, pre, st, compact=compact)
     graph = gpu_decoder(cfg, w, pre, st, compact=compact)
-    S, tau = cfg.S, 0.6
+    tau = 0.6 if S <= 8 else 1.0     # 1.0: one token per step, so a wide window outlasts its graph
     graph.capture(S, tau)
+    slots = graph.slots(S)
+    longest = 0
     rng = np.random.default_rng(5)
     wins = cfg.D // S
     n_steps = 0
@@ -128,11 +132,15 @@ def test_window_graphs_decode_like_single_steps(compact):
                 seen.append(eager.mask_bits_host())
                 k += 1
             assert k <= S
+            longest = max(longest, k)
             ring = graph.run_window(s, S, tau)
-            assert ring.shape == (S, cfg.B)
-            for i in range(S):
+            assert ring.shape == (slots, cfg.B)
+            for i in range(slots):
                 want = seen[i] if i < k else seen[-1]
                 assert np.array_equal(ring[i], want), f"block {blk} window {s} slot {i}"
+            for i in range(slots, k):       # the rest of a wide window, one step at a time
+                graph.dc_step(s, S, tau)
+                assert np.array_equal(graph.mask_bits_host(), seen[i]), f"block {blk} window {s} step {i}"
             assert torch.equal(eager.tokens, graph.tokens) and torch.equal(eager.mask_bits, graph.mask_bits)
             assert np.array_equal(graph.mask_bits_host(), seen[-1])
             n_steps += k
@@ -142,3 +150,4 @@ def test_window_graphs_decode_like_single_steps(compact):
         assert torch.equal(eager.cache_k, graph.cache_k) and torch.equal(eager.cache_v, graph.cache_v)
         assert torch.equal(eager.kv_len, graph.kv_len) and torch.equal(eager.H[:, 0], graph.H[:, 0])
     assert n_steps > 2 * wins
+    assert S <= slots or longest > slots
