@@ -239,6 +239,9 @@ FUSE_CASES = {
     "bf16-B2-S32": ("bf16", 2, 32, 64, 1, 512, 5000, 30.0, 0.5),
     # fp32 head of 140000 columns: 547 partials per row (the strided merge)
     "f32-wide-vocab": ("f32", 2, 8, 32, 0, 256, 140000, 40.0, 0.5),
+    # windows that are not a power of two (lanes padded to 8) and a 64-wide window
+    "bf16-B5-S6": ("bf16", 5, 6, 36, 2, 512, 5000, 30.0, 0.5),
+    "bf16-B1-S64": ("bf16", 1, 64, 64, 0, 512, 5000, 30.0, 0.5),
 }
 
 
