@@ -285,7 +285,9 @@ def extras_e2e(graphs=True, n_blocks=None):
     dec = ModelDecoder(dims, weights, dtype=dt, device=dev)
     del weights
     prompts = bi.make_prompts(cfg, 0)
-    n_weight_bytes = sum(t.numel() * 2 for lw in dec.layers for t in lw.values()) + 2 * dec.W["Wlm"].numel() * 2
+    layer_bytes = sum(t.numel() * 2 for lw in dec.layers for t in lw.values())
+    lm_bytes = dec.W["Wlm"].numel() * 2
+    n_weight_bytes = layer_bytes + 2 * lm_bytes   # layers, LM head and embedding table
     # warm-up: a prefill and one block (also sizes every workspace), then capture
     dec.prefill(prompts)
     dec.new_block()
@@ -316,6 +318,12 @@ def extras_e2e(graphs=True, n_blocks=None):
                         "refinement_steps": n_steps, "commits": nb,
                         "decode_tokens_per_s": tokens / t_dec, "tokens_per_s_with_prefill": tokens / (t_pre + t_dec),
                         "ms_per_step": t_dec / (n_steps + nb) * 1e3, "weight_bytes_per_forward": n_weight_bytes,
+                        # a refinement step streams every layer's weights and the LM head once, a
+                        # commit the layers' weights: those bytes per second of the decode against
+                        # the 8 TB/s spec
+                        "weight_GB_per_s": (n_steps * (layer_bytes + lm_bytes) + nb * layer_bytes) / t_dec / 1e9,
+                        "frac_hbm_weights": (n_steps * (layer_bytes + lm_bytes) + nb * layer_bytes) / t_dec / 1e9
+                        / HBM_PEAK_GBS,
                         "graphs": graphs}}
     del dec
     torch.cuda.empty_cache()
