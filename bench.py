@@ -728,6 +728,18 @@ def main():
         rec = json.load(open(tpath))
         if rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("bytes_per_launch")
+    # the whole DualCache step against HBM: every byte it must read once (LM head and projection
+    # weights, the committed K/V of the batch at the loop's starting lengths plus the in-block rows)
+    attn_bytes = int(sum((int(L) + cfg.D) * 2 * cfg.Hkv * cfg.d * 2 for L in pre.kv_len))
+    proj_bytes = (cfg.Hq * cfg.d + 2 * cfg.Hkv * cfg.d) * cfg.hidden * 2 + cfg.hidden * cfg.Hq * cfg.d * 2
+    step_bytes = cfg.V * cfg.hidden * 2 + proj_bytes + attn_bytes
+    floor_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    step_roofline = {"bound": "hbm", "bytes_per_dualcache_step": step_bytes, "floor_us_at_peak": round(floor_us, 1),
+                     "us_per_step": round(elapsed / steps * 1e6, 1),
+                     "frac": round(floor_us / (elapsed / steps * 1e6), 4),
+                     "note": "LM head + QKV/O weights + the batch's K/V at the starting lengths, read once, "
+                             "against the whole loop's time per step (exact steps, window ends and host waits "
+                             "included)"}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "bd_lmhead_unmask (lm_stream_kernel<4> + lm_merge_unmask_kernel: the LM head's final reduction "
@@ -759,6 +771,7 @@ def main():
         "tokens_per_step": round(tokens / steps, 3),
         "graphs": ("one per window" if windows else "one per step") if not args.no_graphs else None,
         "roofline": roofline,
+        "step_roofline": step_roofline,
         "cpu_baseline": cpu,
         "extra": extra,
     }
