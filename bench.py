@@ -172,6 +172,12 @@ class Loop:
         self.steps = self.tokens = self.commits = 0
         self.bits = None
         self.wmask = [np.uint64(((1 << cfg.S) - 1) << (w * cfg.S)) for w in range(cfg.D // cfg.S)]
+        # steps each sequence needed on its own (it had a masked position of the
+        # window before the step), per block: the schedule a per-sequence
+        # window progression would follow (identical tokens, pinned in the oracle)
+        self.own = np.zeros(cfg.B, np.int64)
+        self.block_steps = 0
+        self.done_blocks = []            # (lockstep steps, max over sequences of own steps)
         self._new_block()
 
     def _new_block(self):
@@ -191,6 +197,8 @@ class Loop:
             dec.dc_step(self.s, S, cfg.tau)
         self.first = False
         self.steps += 1
+        self.block_steps += 1
+        self.own += (self.bits & self.wmask[self.s]) != 0
         bits = dec.mask_bits_host()      # 8 bytes per sequence, refreshed by the step itself
         self.tokens += int(np.bitwise_count(self.bits ^ bits).sum())
         self.bits = bits
@@ -203,6 +211,9 @@ class Loop:
         if self.s == self.cfg.D // self.cfg.S:
             self.dec.commit()
             self.commits += 1
+            self.done_blocks.append((self.block_steps, int(self.own.max())))
+            self.own[:] = 0
+            self.block_steps = 0
             self._new_block()
 
     def window(self) -> int:
@@ -214,7 +225,10 @@ class Loop:
         ring = self.dec.run_window(self.s, self.cfg.S, self.cfg.tau)
         wm = self.wmask[self.s]
         before = np.concatenate([self.bits[None], ring[:-1]])
-        steps = int(((before & wm) != 0).any(axis=1).sum())
+        had = (before & wm) != 0                     # [slots, B]
+        steps = int(had.any(axis=1).sum())
+        self.own += had.sum(axis=0)
+        self.block_steps += steps
         self.tokens += int(np.bitwise_count(self.bits ^ ring[-1]).sum())
         self.bits = ring[-1]
         self.steps += steps
@@ -728,6 +742,14 @@ def main():
         rec = json.load(open(tpath))
         if rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("bytes_per_launch")
+    # lockstep against a per-sequence window progression over the blocks the
+    # loop finished (warm-up and timed): steps the batch took vs the most steps
+    # any one sequence needed on its own schedule (what per-sequence progression
+    # would take if a step mixing exact and DualCache rows cost the same)
+    lock = sum(b[0] for b in loop.done_blocks)
+    own = sum(b[1] for b in loop.done_blocks)
+    progression = {"blocks": len(loop.done_blocks), "lockstep_steps": lock, "per_sequence_steps_bound": own,
+                   "saving_bound": round(1 - own / lock, 4) if lock else None}
     # the whole DualCache step against HBM: every byte it must read once (LM head and projection
     # weights, the committed K/V of the batch at the loop's starting lengths plus the in-block rows)
     attn_bytes = int(sum((int(L) + cfg.D) * 2 * cfg.Hkv * cfg.d * 2 for L in pre.kv_len))
@@ -772,6 +794,7 @@ def main():
         "graphs": ("one per window" if windows else "one per step") if not args.no_graphs else None,
         "roofline": roofline,
         "step_roofline": step_roofline,
+        "per_sequence_progression": progression,
         "cpu_baseline": cpu,
         "extra": extra,
     }
