@@ -151,3 +151,29 @@ def test_window_graphs_decode_like_single_steps(compact, S):
         assert torch.equal(eager.kv_len, graph.kv_len) and torch.equal(eager.H[:, 0], graph.H[:, 0])
     assert n_steps > 2 * wins
     assert S <= slots or longest > slots
+
+
+def test_window_graphs_follow_a_device_threshold_schedule():
+    """Window graphs captured with a threshold tensor read the values it holds
+    at each replay: per-sequence thresholds changed between windows give the
+    same mask bits after every slot as eager single steps with those values."""
+    say("[graphs] window graphs, device threshold schedule")
+    cfg = MID
+    w, pre, st, _, _ = workload(cfg, 0, all_masked=True, plant_rate=None)
+    eager = gpu_decoder(cfg, w, pre, st)
+    graph = gpu_decoder(cfg, w, pre, st)
+    S = cfg.S
+    tau_dev = torch.full((cfg.B,), 0.9, dtype=torch.float32, device="cuda")
+    graph.capture(S, tau_dev)
+    plant = bi.normal(4, "plant", (cfg.B, cfg.D, cfg.hidden), 0.5, "bf16")
+    for d in (eager, graph):
+        d.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plant)
+    for s in range(cfg.D // S):
+        taus = np.float32(0.3 + 0.2 * s) + np.float32(0.1) * np.arange(cfg.B, dtype=np.float32)
+        tau_e = torch.from_numpy(taus).cuda()
+        tau_dev.copy_(torch.from_numpy(taus))
+        ring = graph.run_window(s, S, tau_dev)
+        for i in range(graph.slots(S)):
+            (eager.e_step if i == 0 else eager.dc_step)(s, S, tau_e, eager=True)
+            assert np.array_equal(ring[i], eager.mask_bits_host()), f"window {s} slot {i}"
+        assert torch.equal(eager.tokens, graph.tokens)
