@@ -51,6 +51,9 @@ SIGNATURES = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "bd_threshold_unmask_tau": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "bd_threshold_unmask_windows": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_float,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "bd_copy_rows": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "bd_kv_append": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_int, c_int, c_void_p]),
     "bd_embed_rows": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,

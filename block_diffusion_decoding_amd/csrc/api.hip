@@ -198,6 +198,29 @@ bd_status bd_threshold_unmask_tau(int B, int D, int win_lo, int win_len, const f
                                      n_unmasked, unmasked_pos, static_cast<hipStream_t>(stream)));
 }
 
+bd_status bd_threshold_unmask_windows(int B, int D, int win_len, const int32_t* win_lo, const float* conf,
+                                      const int32_t* argmax, float threshold, int32_t* tokens, uint64_t* mask_bits,
+                                      int32_t* n_unmasked, int32_t* unmasked_pos, void* stream) {
+  if (B < 0) return BD_EINVAL;
+  if (B == 0) return BD_OK;
+  if (D < 1 || D > 64 || win_len < 1 || win_len > D) return BD_EINVAL;
+  if (!win_lo || !conf || !argmax || !tokens || !mask_bits || !(threshold == threshold)) return BD_EINVAL;
+  return hip_status(bd_unmask_launch(B, D, 0, win_len, conf, argmax, threshold, nullptr, tokens, mask_bits,
+                                     n_unmasked, unmasked_pos, static_cast<hipStream_t>(stream), win_lo));
+}
+
+// ---------------------------------------------------------------------------
+bd_status bd_copy_rows(int B, int n_rows, int row_bytes, const uint64_t* row_mask, const void* src0, void* dst0,
+                       const void* src1, void* dst1, void* stream) {
+  if (B < 0 || n_rows < 0) return BD_EINVAL;
+  if (B == 0 || n_rows == 0) return BD_OK;
+  if (n_rows > 64 || row_bytes <= 0 || row_bytes % 16 != 0 || !row_mask || !src0 || !dst0) return BD_EINVAL;
+  if ((src1 == nullptr) != (dst1 == nullptr)) return BD_EINVAL;
+  if (!aligned16(src0) || !aligned16(dst0) || (src1 && (!aligned16(src1) || !aligned16(dst1)))) return BD_EINVAL;
+  return hip_status(bd_copy_rows_launch(B, n_rows, row_bytes, row_mask, src0, dst0, src1, dst1,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------------------
 bd_status bd_kv_append(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache, void* v_cache, int32_t* kv_len,
                        const int32_t* kv_len_host, const void* k_blk, const void* v_blk, int n_blk, int n_rows,

@@ -151,7 +151,9 @@ hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, i
 hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* conf,
                             const int32_t* argmax, float threshold, const float* threshold_dev,
                             int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
-                            int32_t* unmasked_pos, hipStream_t s);
+                            int32_t* unmasked_pos, hipStream_t s, const int32_t* win_lo_dev = nullptr);
+hipError_t bd_copy_rows_launch(int B, int n_rows, int row_bytes, const uint64_t* row_mask, const void* src0,
+                               void* dst0, const void* src1, void* dst1, hipStream_t s);
 
 hipError_t bd_append_launch(bd_dtype dt, int B, int Hkv, int d, int cap, void* k_cache,
                             void* v_cache, int32_t* kv_len, const void* k_blk, const void* v_blk,

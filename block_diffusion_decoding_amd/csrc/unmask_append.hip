@@ -21,16 +21,43 @@ namespace {
 
 __global__ __launch_bounds__(64) void unmask_kernel(int D, int win_lo, int win_len, const float* conf,
                                                     const int32_t* argmax, float thr, const float* thr_dev,
-                                                    int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
-                                                    int32_t* unmasked_pos) {
+                                                    const int32_t* win_lo_dev, int32_t* tokens, uint64_t* mask_bits,
+                                                    int32_t* n_unmasked, int32_t* unmasked_pos) {
   const int b = blockIdx.x;
   const int r = threadIdx.x;
   if (thr_dev != nullptr) thr = thr_dev[b];  // per-sequence threshold from device memory
+  if (win_lo_dev != nullptr) {               // per-sequence window; one outside the block changes nothing
+    win_lo = win_lo_dev[b];
+    if (win_lo < 0 || win_lo + win_len > D) {
+      if (r == 0 && n_unmasked != nullptr) n_unmasked[b] = 0;
+      if (unmasked_pos != nullptr && r < win_len) unmasked_pos[(size_t)b * win_len + r] = -1;
+      return;
+    }
+  }
   const uint64_t bits = mask_bits[b];
   const bool in = r < win_len;
   const float c = in ? conf[(size_t)b * win_len + r] : BD_NEG_INF;
   const int32_t am = in ? argmax[(size_t)b * win_len + r] : -1;
   bd_unmask_wave(r, b, D, win_lo, win_len, bits, c, am, thr, tokens, mask_bits, n_unmasked, unmasked_pos, nullptr);
+}
+
+// One work-group per sequence: copy the rows r < n_rows whose bit r is set in
+// row_mask[b] from src to dst (and from src1 to dst1 when given), in 16-byte
+// pieces; layouts [B, n_rows, row_bytes].
+__global__ __launch_bounds__(256) void copy_rows_kernel(int n_rows, int row_bytes, const uint64_t* row_mask,
+                                                        const uint8_t* src0, uint8_t* dst0, const uint8_t* src1,
+                                                        uint8_t* dst1) {
+  const int b = blockIdx.x;
+  const uint64_t mask = row_mask[b];
+  if (mask == 0) return;
+  const int pieces = row_bytes / 16;
+  for (int e = threadIdx.x; e < n_rows * pieces; e += blockDim.x) {
+    const int r = e / pieces;
+    if (!((mask >> r) & 1ull)) continue;
+    const size_t at = ((size_t)b * n_rows + r) * row_bytes + (size_t)(e % pieces) * 16;
+    *reinterpret_cast<uint4*>(dst0 + at) = *reinterpret_cast<const uint4*>(src0 + at);
+    if (src1 != nullptr) *reinterpret_cast<uint4*>(dst1 + at) = *reinterpret_cast<const uint4*>(src1 + at);
+  }
 }
 
 // One work-group per sequence: copy n_rows in-block rows behind the committed
@@ -103,9 +130,17 @@ hipError_t bd_candidates_launch(int B, int win_lo, int win_len, const uint64_t* 
 
 hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* conf, const int32_t* argmax,
                             float threshold, const float* threshold_dev, int32_t* tokens, uint64_t* mask_bits,
-                            int32_t* n_unmasked, int32_t* unmasked_pos, hipStream_t s) {
+                            int32_t* n_unmasked, int32_t* unmasked_pos, hipStream_t s, const int32_t* win_lo_dev) {
   hipLaunchKernelGGL(unmask_kernel, dim3(B), dim3(64), 0, s, D, win_lo, win_len, conf, argmax, threshold,
-                     threshold_dev, tokens, mask_bits, n_unmasked, unmasked_pos);
+                     threshold_dev, win_lo_dev, tokens, mask_bits, n_unmasked, unmasked_pos);
+  return hipGetLastError();
+}
+
+hipError_t bd_copy_rows_launch(int B, int n_rows, int row_bytes, const uint64_t* row_mask, const void* src0,
+                               void* dst0, const void* src1, void* dst1, hipStream_t s) {
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(B), dim3(256), 0, s, n_rows, row_bytes, row_mask,
+                     static_cast<const uint8_t*>(src0), static_cast<uint8_t*>(dst0),
+                     static_cast<const uint8_t*>(src1), static_cast<uint8_t*>(dst1));
   return hipGetLastError();
 }
 

@@ -196,6 +196,29 @@ def bd_threshold_unmask(conf, argmax, tokens, mask_bits, *, win_lo, threshold, n
     _check("bd_threshold_unmask", st)
 
 
+def bd_threshold_unmask_windows(conf, argmax, tokens, mask_bits, win_lo, *, threshold, n_unmasked=None,
+                                unmasked_pos=None, stream=None):
+    """conf/argmax [B, win_len]; win_lo [B] int32 device: each sequence's window start."""
+    lib = _lib.load()
+    B, win_len = conf.shape
+    D = tokens.shape[1]
+    st = lib.bd_threshold_unmask_windows(B, D, win_len, _p(win_lo), _p(conf), _p(argmax), float(threshold),
+                                         _p(tokens), _p(mask_bits), _p(n_unmasked), _p(unmasked_pos),
+                                         _stream(stream))
+    _check("bd_threshold_unmask_windows", st)
+
+
+def bd_copy_rows(row_mask, src0, dst0, src1=None, dst1=None, *, stream=None):
+    """src/dst [B, n_rows, ...] contiguous, same shape; row_mask [B] (64-bit) device."""
+    lib = _lib.load()
+    B, n_rows = src0.shape[0], src0.shape[1]
+    row_bytes = src0[0, 0].numel() * src0.element_size()
+    assert dst0.shape == src0.shape and (src1 is None or (src1.shape == src0.shape and dst1.shape == src0.shape))
+    st = lib.bd_copy_rows(B, n_rows, row_bytes, _p(row_mask), _p(src0), _p(dst0), _p(src1), _p(dst1),
+                          _stream(stream))
+    _check("bd_copy_rows", st)
+
+
 def bd_kv_append(k_cache, v_cache, kv_len, k_blk, v_blk, *, n_rows, kv_len_host=None, row_off=0, stream=None):
     """k/v_cache [B, Hkv, cap, d]; kv_len [B] int32 (in/out); k/v_blk [B, n_blk, Hkv, d];
     appends rows row_off .. row_off + n_rows - 1 of each sequence's k/v_blk."""

@@ -1,0 +1,208 @@
+"""Per-sequence window progression on one GPU ("Fast-dLLM v2: Efficient
+Block-Diffusion LLM" notes, Key designs 3-4: windows of S positions decoded
+left to right, each opened by an exact step that refreshes the DualCache
+snapshot).
+
+In the lockstep decoder a window ends for the whole batch when its slowest
+sequence has decoded it.  Here every sequence moves to its next window as soon
+as it has decoded its own, so one batched step mixes sequences that open a
+window (an exact step: all D rows recomputed, snapshot refreshed) with
+sequences inside one (a DualCache step: their window rows fresh, the other
+in-block rows from their snapshot).  The tokens are those of the lockstep
+schedule (a sequence without candidates changes no state); the batch needs
+fewer steps when the sequences decode at different rates.
+
+One step, every arithmetic part a libbd call:
+  * input rows, Q/K/V and output rows of all D block rows of every sequence
+    (the exact step's work, for every sequence);
+  * before the attention, a DualCache sequence's K/V rows outside its window
+    are restored from its snapshot (bd_copy_rows), so its queries see the
+    snapshot there, as in a DualCache step;
+  * the LM head over each sequence's own window rows, the token shift read
+    through the row list (a DualCache sequence's first window position reads
+    its snapshot row, as in a DualCache step), then the threshold rule on each
+    sequence's own window (bd_threshold_unmask_windows);
+  * the sequences that opened a window save their K/V and output rows as
+    their new snapshot (bd_copy_rows).
+Row buffers: Hcat [2, B, 1 + D, hidden]: Hcat[0] holds this step's output rows,
+Hcat[1] the snapshot rows (row 0 = carry).  The step is captured as one HIP
+graph; the host writes the per-sequence windows, row lists and row masks
+before each replay.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import ops
+from .decoder import BlockDecoder, Dims
+from .ops import dense, rows
+
+
+class PerSequenceDecoder(BlockDecoder):
+    window_graphs = False
+
+    def __init__(self, dims: Dims, weights: dict, S: int, dtype=torch.bfloat16, device="cuda"):
+        super().__init__(dims, weights, dtype=dtype, device=device, compact=False)
+        B, D, hid = dims.B, dims.D, dims.hidden
+        assert D % S == 0 and D <= 63
+        self.S = S
+        dev = self.device
+        self.Hcat = torch.zeros(2, B, 1 + D, hid, dtype=dtype, device=dev)
+        self.Hcat[1].copy_(self.H)
+        self.H = self.Hcat[1]                    # carry and snapshot rows: what the commit writes
+        self.snap_k = torch.zeros_like(self.blk_k)
+        self.snap_v = torch.zeros_like(self.blk_v)
+        self.argmax = torch.zeros(B, S, dtype=torch.int32, device=dev)
+        self.conf = torch.zeros(B, S, dtype=torch.float32, device=dev)
+        self.maxl = torch.zeros(B, S, dtype=torch.float32, device=dev)
+        self.lse = torch.zeros(B, S, dtype=torch.float32, device=dev)
+        self.pos = torch.zeros(B, S, dtype=torch.int32, device=dev)
+        # per-step host-written inputs: row list, windows, restore / save masks
+        self.row_idx = torch.zeros(B * S, dtype=torch.int32, device=dev)
+        self.win_lo = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.restore = torch.zeros(B, dtype=torch.int64, device=dev)
+        self.save = torch.zeros(B, dtype=torch.int64, device=dev)
+        self.save_h = torch.zeros(B, dtype=torch.int64, device=dev)
+        self._stage32 = torch.zeros(B * S + B, dtype=torch.int32, pin_memory=True)
+        self._stage64 = torch.zeros(3 * B, dtype=torch.int64, pin_memory=True)
+        self._graph = None
+        self.win = np.zeros(B, np.int64)         # current window per sequence (D // S = block done)
+        self.opening = np.ones(B, bool)          # next step opens the window (exact step)
+        self.own_steps = np.zeros(B, np.int64)
+
+    # ------------------------------------------------------------ host side
+    def begin_block(self):
+        self.win[:] = 0
+        self.opening[:] = True
+        self.own_steps[:] = 0
+
+    def _inputs(self):
+        """Row list, windows and masks of the next step from the host state."""
+        B, D, S = self.dims.B, self.dims.D, self.S
+        nw = D // S
+        full = (1 << D) - 1
+        ridx = np.zeros((B, S), np.int64)
+        lo = np.zeros(B, np.int64)
+        restore = np.zeros(B, np.uint64)
+        save = np.zeros(B, np.uint64)
+        save_h = np.zeros(B, np.uint64)
+        idx = lambda buf, b, row: (buf * B + b) * (1 + D) + row
+        for b in range(B):
+            if self.win[b] >= nw:                # block done: a window outside the block, a no-op
+                lo[b] = D
+                ridx[b] = idx(1, b, 0)
+                continue
+            w0 = int(self.win[b]) * S
+            lo[b] = w0
+            for r in range(S):
+                q = w0 + r - 1                   # the token shift: position p reads row p - 1
+                if q < 0:
+                    ridx[b, r] = idx(1, b, 0)    # carry
+                elif self.opening[b] or q >= w0:
+                    ridx[b, r] = idx(0, b, q + 1)
+                else:
+                    ridx[b, r] = idx(1, b, q + 1)    # DualCache: the snapshot row before the window
+            win_bits = ((1 << S) - 1) << w0
+            if self.opening[b]:
+                save[b] = full
+                save_h[b] = ((1 << (D + 1)) - 1) ^ 1      # output rows 1 .. D
+            else:
+                restore[b] = full & ~win_bits
+        s32, s64 = self._stage32.numpy(), self._stage64.numpy()
+        s32[:B * S] = ridx.reshape(-1)
+        s32[B * S:] = lo
+        s64[:B] = restore.view(np.int64)
+        s64[B:2 * B] = save.view(np.int64)
+        s64[2 * B:] = save_h.view(np.int64)
+        t32, t64 = self._stage32, self._stage64
+        self.row_idx.copy_(t32[:B * S], non_blocking=True)
+        self.win_lo.copy_(t32[B * S:], non_blocking=True)
+        self.restore.copy_(t64[:B], non_blocking=True)
+        self.save.copy_(t64[B:2 * B], non_blocking=True)
+        self.save_h.copy_(t64[2 * B:], non_blocking=True)
+
+    # ---------------------------------------------------------------- step
+    def _kernels(self, tau):
+        dm, W = self.dims, self.W
+        B, D, S, hid = dm.B, dm.D, self.S, dm.hidden
+        X = self.X
+        ops.bd_embed_rows(W["E"], self.tokens, self.mask_bits, X, row_off=0, n_rows=D, plant=self.plant)
+        kr = rows(D, D, 0)
+        ops.bd_qkv_proj(X, dense(B * D), W["Wq"], self.q, dense(B * D), W["Wk"], W["Wv"], self.blk_k, kr,
+                        self.blk_v, kr, M=B * D)
+        ops.bd_copy_rows(self.restore, self.snap_k, self.blk_k, self.snap_v, self.blk_v)
+        ops.bd_block_attn(self.q, self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, self.o,
+                          D=D, q_off=0)
+        ops.bd_linear(self.o, dense(B * D), W["Wo"], self.Hcat[0], rows(D, 1 + D, 1), M=B * D, res=X,
+                      rr=dense(B * D))
+        ops.bd_lmhead_confidence(self.Hcat.view(-1, hid), self.row_idx, W["Wlm"], self.argmax.view(-1),
+                                 self.conf.view(-1), max_logit=self.maxl.view(-1), lse=self.lse.view(-1))
+        ops.bd_threshold_unmask_windows(self.conf, self.argmax, self.tokens, self.mask_bits, self.win_lo,
+                                        threshold=tau, n_unmasked=self.n_unmasked, unmasked_pos=self.pos)
+        ops.bd_copy_rows(self.save, self.blk_k, self.snap_k, self.blk_v, self.snap_v)
+        ops.bd_copy_rows(self.save_h, self.Hcat[0], self.Hcat[1])
+        self.bits_host.copy_(self.mask_bits, non_blocking=True)
+
+    def capture_step(self, tau: float):
+        """Capture the step as one HIP graph (every workspace sized first)."""
+        dm = self.dims
+        B, D = dm.B, dm.D
+        if self.plant is None:
+            self.plant = torch.zeros(B, D, dm.hidden, dtype=self.dtype, device=self.device)
+        for tag, n in {"attn": ops.bd_block_attn_workspace_size(self.dtype, B, dm.Hq, dm.Hkv, dm.d, D, dm.cap, D),
+                       "lm": ops.bd_lmhead_workspace_size(self.dtype, B * self.S, dm.hidden, dm.V),
+                       "gemm": max(ops.bd_qkv_proj_workspace_size(self.dtype, B * D, dm.hidden, dm.Hq * dm.d,
+                                                                  dm.Hkv * dm.d),
+                                   ops.bd_linear_workspace_size(self.dtype, B * D, dm.hidden, dm.Hq * dm.d),
+                                   ops.bd_linear_workspace_size(self.dtype, B, dm.hidden, dm.Hq * dm.d))}.items():
+            ops.workspace(n, self.device, tag)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self._kernels(tau)
+        self._graph, self._graph_tau_ps = g, tau
+        torch.cuda.synchronize()
+
+    def _advance(self, bits):
+        """Move every sequence past the windows it has finished (from the
+        current mask bits); a sequence entering a window opens it."""
+        nw = self.dims.D // self.S
+        for b in range(self.dims.B):
+            while self.win[b] < nw and not (bits[b] & np.uint64(((1 << self.S) - 1) << (int(self.win[b]) * self.S))):
+                self.win[b] += 1
+                self.opening[b] = True
+
+    def done(self) -> bool:
+        self._advance(self.mask_bits_host())
+        return bool((self.win >= self.dims.D // self.S).all())
+
+    def step(self, tau: float) -> bool:
+        """One batched step: every sequence with a masked position left in the
+        block opens or continues its own window.  Returns False (and does
+        nothing) when every sequence has finished the block.  last_kinds[b]
+        is (window, "E" or "DC") of sequence b in this step, or None."""
+        if self.done():
+            return False
+        nw = self.dims.D // self.S
+        self.last_kinds = [(int(self.win[b]), "E" if self.opening[b] else "DC") if self.win[b] < nw else None
+                           for b in range(self.dims.B)]
+        self.own_steps += self.win < nw
+        self._inputs()
+        if self._graph is not None and tau == self._graph_tau_ps:
+            self._graph.replay()
+        else:
+            self._kernels(tau)
+        self._step_done()
+        self.opening[self.win < nw] = False
+        return True
+
+    def decode_block(self, tau: float) -> int:
+        """Decode the current block, every sequence on its own windows, then
+        commit it; returns the number of batched steps."""
+        self.begin_block()
+        n = 0
+        while self.step(tau):
+            n += 1
+        self.commit()
+        return n

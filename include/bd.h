@@ -219,6 +219,29 @@ bd_status bd_threshold_unmask_tau(int B, int D, int win_lo, int win_len,
                                   int32_t* tokens, uint64_t* mask_bits,
                                   int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
 
+/* The same rule with each sequence's own window (per-sequence window
+ * progression, where every sequence advances through its block on its own
+ * schedule; the tokens are those of the lockstep schedule, since a sequence
+ * with no candidate changes no state):
+ *   win_lo [B] int32 (device)   window of sequence b = [win_lo[b], win_lo[b] + win_len);
+ *                               a window outside [0, D) leaves the sequence as
+ *                               it is (n_unmasked 0, unmasked_pos -1)
+ * Requires 1 <= win_len <= D <= 64. */
+bd_status bd_threshold_unmask_windows(int B, int D, int win_len, const int32_t* win_lo,
+                                      const float* conf, const int32_t* argmax, float threshold,
+                                      int32_t* tokens, uint64_t* mask_bits,
+                                      int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
+
+/* Per-sequence masked row copy (support for per-sequence window progression:
+ * restoring a sequence's DualCache snapshot rows outside its window, saving
+ * the rows of an exact step as the new snapshot):
+ *   for every sequence b and row r < n_rows with bit r of row_mask[b] set:
+ *     dst0[b, r, :] = src0[b, r, :]   (and dst1 from src1 when both are given)
+ *   layouts [B, n_rows, row_bytes], row_mask [B] uint64 (device)
+ * Requires n_rows <= 64, row_bytes % 16 == 0 and 16-byte aligned pointers. */
+bd_status bd_copy_rows(int B, int n_rows, int row_bytes, const uint64_t* row_mask,
+                       const void* src0, void* dst0, const void* src1, void* dst1, void* stream);
+
 /* ------------------------------------------------------------------------
  * bd_lmhead_unmask -- bd_lmhead_confidence followed by bd_threshold_unmask
  * in one call, for a lockstep window of at most 64 rows ([v2 notes] Key

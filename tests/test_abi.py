@@ -32,7 +32,7 @@ def test_header_declares_the_four_calls_and_support():
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
               "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu",
               "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau",
-              "bd_lmhead_unmask"]:
+              "bd_lmhead_unmask", "bd_threshold_unmask_windows", "bd_copy_rows"]:
         assert n in names
 
 
@@ -258,3 +258,18 @@ def test_lmhead_unmask_argument_errors():
     assert call(tau=float("nan")) == E          # a NaN fixed threshold
     assert call(wsb=need - 16) == E
     assert call(B=0) == 0
+
+
+def test_per_sequence_window_calls_argument_errors():
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    un = lambda **k: lib.bd_threshold_unmask_windows(k.get("B", 4), k.get("D", 32), k.get("win", 8),
+                                                     k.get("lo", FAKE), FAKE, FAKE, k.get("tau", 0.9), FAKE, FAKE,
+                                                     None, None, None)
+    assert un(lo=None) == E and un(D=65) == E and un(win=33) == E and un(tau=float("nan")) == E
+    assert un(B=0) == 0
+    cp = lambda **k: lib.bd_copy_rows(k.get("B", 4), k.get("n", 33), k.get("rb", 3072), k.get("mask", FAKE),
+                                      FAKE, FAKE, k.get("s1", None), k.get("d1", None), None)
+    assert cp(n=65) == E and cp(rb=3000) == E and cp(mask=None) == E and cp(s1=FAKE) == E
+    assert cp(s1=FAKE + 8, d1=FAKE) == E          # misaligned
+    assert cp(B=0) == 0 and cp(n=0) == 0
