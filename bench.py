@@ -433,6 +433,66 @@ def extras_subblock(w3, graphs, steps=40, warmup=10):
     return {"subblock_sweep_7B": out}
 
 
+def extras_persequence(w3, n_blocks=4):
+    """The headline workload (7B shape, planted pass rate 0.5) decoded block by
+    block with per-sequence window progression (one captured mixed step per
+    batched step) against the lockstep loop (window graphs), same blocks."""
+    from block_diffusion_decoding_amd.decoder import Dims
+    from block_diffusion_decoding_amd.persequence import PerSequenceDecoder
+    cfg = bi.C3
+    pre = bi.make_prefix(cfg, 0)
+    plants = block_plants(cfg, w3, 0.5, 0, n_blocks + 1)
+    dims = Dims(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.hidden, cfg.V, cfg.D, cfg.cap)
+    weights = {k: torch.from_numpy(getattr(w3, k)) for k in ("E", "Wq", "Wk", "Wv", "Wo", "Wlm")}
+    out = {}
+    # per-sequence progression
+    dec = PerSequenceDecoder(dims, weights, cfg.S, dtype=torch.bfloat16, device="cuda")
+    dec.set_synthetic_prefix(pre.kv_len, pre.cache_k, pre.cache_v, pre.carry)
+    dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plants[0])
+    dec.capture_step(cfg.tau)
+    dec.decode_block(cfg.tau)                     # warm-up block
+    torch.cuda.synchronize()
+    steps = 0
+    t0 = time.perf_counter()
+    for k in range(n_blocks):
+        dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plants[1 + k])
+        steps += dec.decode_block(cfg.tau)
+    torch.cuda.synchronize()
+    t_ps = time.perf_counter() - t0
+    del dec
+    torch.cuda.empty_cache()
+    # lockstep (window graphs), the same blocks from the same context
+    dec = make_decoder(cfg, w3, pre)
+    dec.capture(cfg.S, cfg.tau)
+    loop = Loop(dec, cfg, plants)
+
+    def advance():
+        if loop.first:
+            loop.window()
+        else:
+            loop.step()
+    while loop.blk < 1:                           # warm-up block
+        advance()
+    torch.cuda.synchronize()
+    s0 = loop.steps
+    t0 = time.perf_counter()
+    while loop.blk < 1 + n_blocks:
+        advance()
+    torch.cuda.synchronize()
+    t_ls = time.perf_counter() - t0
+    tokens = n_blocks * cfg.B * cfg.D
+    out["per_sequence_7B"] = {"blocks": n_blocks, "tokens": tokens,
+                              "per_sequence": {"steps": steps, "ms": t_ps * 1e3, "tokens_per_s": tokens / t_ps,
+                                               "ms_per_step": t_ps / steps * 1e3},
+                              "lockstep": {"steps": loop.steps - s0, "ms": t_ls * 1e3, "tokens_per_s": tokens / t_ls,
+                                           "ms_per_step": t_ls / (loop.steps - s0) * 1e3}}
+    log(f"[bench] per-sequence progression: {steps} steps, {tokens / t_ps:.0f} tokens/s; lockstep "
+        f"{loop.steps - s0} steps, {tokens / t_ls:.0f} tokens/s ({n_blocks} blocks)")
+    del dec, loop
+    torch.cuda.empty_cache()
+    return out
+
+
 def extras_v1():
     """v1-style decoding of a full-attention model (one 1.5B-shaped layer +
     the 1.5B head) with the block-wise DualCache, against the same decode
@@ -473,7 +533,7 @@ def extras_v1():
     return {"v1_full_attention_1.5B_layer": out}
 
 
-def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "v1"), graphs=True,
+def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "persequence", "v1"), graphs=True,
            e2e_blocks=None):
     """Attention and LM head alone at the long-context / batched shapes, the
     long-context block loop and the end-to-end multi-layer decode."""
@@ -493,6 +553,8 @@ def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "v
         out.update(extras_train(reps))
     if "subblock" in parts:
         out.update(extras_subblock(w3, graphs))
+    if "persequence" in parts:
+        out.update(extras_persequence(w3))
     if "v1" in parts:
         out.update(extras_v1())
     return out
@@ -663,8 +725,8 @@ def main():
                          "captured graph per window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
-    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "v1"),
-                    default="all", help="attn/long/lm/e2e/train/subblock/v1: run only that measurement (for profiling) and print "
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "persequence", "v1"),
+                    default="all", help="attn/long/lm/e2e/train/subblock/persequence/v1: run only that measurement (for profiling) and print "
                          "its JSON instead of the bench line")
     ap.add_argument("--e2e-blocks", type=int, default=None,
                     help="blocks generated by the end-to-end decode measurement (default: the workload's 16)")

@@ -58,14 +58,14 @@ class PerSequenceDecoder(BlockDecoder):
         self.maxl = torch.zeros(B, S, dtype=torch.float32, device=dev)
         self.lse = torch.zeros(B, S, dtype=torch.float32, device=dev)
         self.pos = torch.zeros(B, S, dtype=torch.int32, device=dev)
-        # per-step host-written inputs: row list, windows, restore / save masks
-        self.row_idx = torch.zeros(B * S, dtype=torch.int32, device=dev)
-        self.win_lo = torch.zeros(B, dtype=torch.int32, device=dev)
-        self.restore = torch.zeros(B, dtype=torch.int64, device=dev)
-        self.save = torch.zeros(B, dtype=torch.int64, device=dev)
-        self.save_h = torch.zeros(B, dtype=torch.int64, device=dev)
-        self._stage32 = torch.zeros(B * S + B, dtype=torch.int32, pin_memory=True)
-        self._stage64 = torch.zeros(3 * B, dtype=torch.int64, pin_memory=True)
+        # per-step host-written inputs, one buffer (one copy per step): restore /
+        # save masks [3, B] (64-bit), then the row list [B * S] and windows [B] (int32)
+        n64 = 3 * B + (B * S + B + 1) // 2
+        self._inbuf = torch.zeros(n64, dtype=torch.int64, device=dev)
+        self._stage = torch.zeros(n64, dtype=torch.int64, pin_memory=True)
+        self.restore, self.save, self.save_h = self._inbuf[:B], self._inbuf[B:2 * B], self._inbuf[2 * B:3 * B]
+        i32 = self._inbuf[3 * B:].view(torch.int32)
+        self.row_idx, self.win_lo = i32[:B * S], i32[B * S:B * S + B]
         self._graph = None
         self.win = np.zeros(B, np.int64)         # current window per sequence (D // S = block done)
         self.opening = np.ones(B, bool)          # next step opens the window (exact step)
@@ -81,46 +81,29 @@ class PerSequenceDecoder(BlockDecoder):
         """Row list, windows and masks of the next step from the host state."""
         B, D, S = self.dims.B, self.dims.D, self.S
         nw = D // S
-        full = (1 << D) - 1
-        ridx = np.zeros((B, S), np.int64)
-        lo = np.zeros(B, np.int64)
-        restore = np.zeros(B, np.uint64)
-        save = np.zeros(B, np.uint64)
-        save_h = np.zeros(B, np.uint64)
-        idx = lambda buf, b, row: (buf * B + b) * (1 + D) + row
-        for b in range(B):
-            if self.win[b] >= nw:                # block done: a window outside the block, a no-op
-                lo[b] = D
-                ridx[b] = idx(1, b, 0)
-                continue
-            w0 = int(self.win[b]) * S
-            lo[b] = w0
-            for r in range(S):
-                q = w0 + r - 1                   # the token shift: position p reads row p - 1
-                if q < 0:
-                    ridx[b, r] = idx(1, b, 0)    # carry
-                elif self.opening[b] or q >= w0:
-                    ridx[b, r] = idx(0, b, q + 1)
-                else:
-                    ridx[b, r] = idx(1, b, q + 1)    # DualCache: the snapshot row before the window
-            win_bits = ((1 << S) - 1) << w0
-            if self.opening[b]:
-                save[b] = full
-                save_h[b] = ((1 << (D + 1)) - 1) ^ 1      # output rows 1 .. D
-            else:
-                restore[b] = full & ~win_bits
-        s32, s64 = self._stage32.numpy(), self._stage64.numpy()
+        b = np.arange(B)[:, None]
+        active = self.win < nw
+        w0 = np.where(active, self.win * S, 0)
+        q = w0[:, None] + np.arange(S)[None, :] - 1     # the token shift: position p reads row p - 1
+        fresh = self.opening[:, None] | (q >= w0[:, None])
+        # Hcat row of (buffer, sequence, row): buffer 0 = this step's rows, 1 = snapshot (row 0 = carry);
+        # a DualCache sequence's first window position reads its snapshot row
+        ridx = np.where(fresh, b * (1 + D) + q + 1, (B + b) * (1 + D) + q + 1)
+        ridx = np.where((q < 0) | ~active[:, None], (B + b) * (1 + D), ridx)
+        lo = np.where(active, w0, D)                     # a finished sequence: a window outside the block
+        full = np.uint64((1 << D) - 1)
+        win_bits = np.uint64((1 << S) - 1) << w0.astype(np.uint64)
+        restore = np.where(active & ~self.opening, full & ~win_bits, np.uint64(0))
+        save = np.where(active & self.opening, full, np.uint64(0))
+        save_h = np.where(active & self.opening, np.uint64(((1 << (D + 1)) - 1) ^ 1), np.uint64(0))  # rows 1 .. D
+        st = self._stage.numpy()
+        st[:B] = restore.view(np.int64)
+        st[B:2 * B] = save.view(np.int64)
+        st[2 * B:3 * B] = save_h.view(np.int64)
+        s32 = st[3 * B:].view(np.int32)
         s32[:B * S] = ridx.reshape(-1)
-        s32[B * S:] = lo
-        s64[:B] = restore.view(np.int64)
-        s64[B:2 * B] = save.view(np.int64)
-        s64[2 * B:] = save_h.view(np.int64)
-        t32, t64 = self._stage32, self._stage64
-        self.row_idx.copy_(t32[:B * S], non_blocking=True)
-        self.win_lo.copy_(t32[B * S:], non_blocking=True)
-        self.restore.copy_(t64[:B], non_blocking=True)
-        self.save.copy_(t64[B:2 * B], non_blocking=True)
-        self.save_h.copy_(t64[2 * B:], non_blocking=True)
+        s32[B * S:B * S + B] = lo
+        self._inbuf.copy_(self._stage, non_blocking=True)
 
     # ---------------------------------------------------------------- step
     def _kernels(self, tau):
