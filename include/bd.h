@@ -14,6 +14,7 @@
  *     (only the masked candidates)      bd_candidate_rows + bd_lmhead_confidence_rows
  *   confidence-threshold unmasking      bd_threshold_unmask
  *     (LM head + unmask, one call)      bd_lmhead_unmask
+ *     (per-sequence windows)            bd_threshold_unmask_windows, bd_copy_rows
  *   (block finished) cache append       bd_kv_append
  *
  * Sources, by page title and section:
