@@ -41,22 +41,18 @@ __global__ __launch_bounds__(64) void unmask_kernel(int D, int win_lo, int win_l
   bd_unmask_wave(r, b, D, win_lo, win_len, bits, c, am, thr, tokens, mask_bits, n_unmasked, unmasked_pos, nullptr);
 }
 
-// One work-group per sequence: copy the rows r < n_rows whose bit r is set in
-// row_mask[b] from src to dst (and from src1 to dst1 when given), in 16-byte
-// pieces; layouts [B, n_rows, row_bytes].
+// One work-group per (sequence b, row r < n_rows): copies the row when bit r
+// of row_mask[b] is set, from src to dst (and from src1 to dst1 when given),
+// in 16-byte pieces; layouts [B, n_rows, row_bytes].
 __global__ __launch_bounds__(256) void copy_rows_kernel(int n_rows, int row_bytes, const uint64_t* row_mask,
                                                         const uint8_t* src0, uint8_t* dst0, const uint8_t* src1,
                                                         uint8_t* dst1) {
-  const int b = blockIdx.x;
-  const uint64_t mask = row_mask[b];
-  if (mask == 0) return;
-  const int pieces = row_bytes / 16;
-  for (int e = threadIdx.x; e < n_rows * pieces; e += blockDim.x) {
-    const int r = e / pieces;
-    if (!((mask >> r) & 1ull)) continue;
-    const size_t at = ((size_t)b * n_rows + r) * row_bytes + (size_t)(e % pieces) * 16;
-    *reinterpret_cast<uint4*>(dst0 + at) = *reinterpret_cast<const uint4*>(src0 + at);
-    if (src1 != nullptr) *reinterpret_cast<uint4*>(dst1 + at) = *reinterpret_cast<const uint4*>(src1 + at);
+  const int b = blockIdx.x, r = blockIdx.y;
+  if (!((row_mask[b] >> r) & 1ull)) return;
+  const size_t row = ((size_t)b * n_rows + r) * row_bytes;
+  for (int e = threadIdx.x * 16; e < row_bytes; e += blockDim.x * 16) {
+    *reinterpret_cast<uint4*>(dst0 + row + e) = *reinterpret_cast<const uint4*>(src0 + row + e);
+    if (src1 != nullptr) *reinterpret_cast<uint4*>(dst1 + row + e) = *reinterpret_cast<const uint4*>(src1 + row + e);
   }
 }
 
@@ -138,7 +134,7 @@ hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* 
 
 hipError_t bd_copy_rows_launch(int B, int n_rows, int row_bytes, const uint64_t* row_mask, const void* src0,
                                void* dst0, const void* src1, void* dst1, hipStream_t s) {
-  hipLaunchKernelGGL(copy_rows_kernel, dim3(B), dim3(256), 0, s, n_rows, row_bytes, row_mask,
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(B, n_rows), dim3(256), 0, s, n_rows, row_bytes, row_mask,
                      static_cast<const uint8_t*>(src0), static_cast<uint8_t*>(dst0),
                      static_cast<const uint8_t*>(src1), static_cast<uint8_t*>(dst1));
   return hipGetLastError();
