@@ -724,7 +724,8 @@ def main():
                     help="replay one captured step at a time (a host wait after every step) instead of one "
                          "captured graph per window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=32,
+                    help="DualCache steps of the oracle timed for cpu_baseline (about 10 s of host work)")
     ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "persequence", "v1"),
                     default="all", help="attn/long/lm/e2e/train/subblock/persequence/v1: run only that measurement (for profiling) and print "
                          "its JSON instead of the bench line")
