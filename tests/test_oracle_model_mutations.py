@@ -56,7 +56,32 @@ def _forward_rows_ignores_snapshot(model, seq, X, rows, D, snap_k=None, snap_v=N
     return _forward_rows(model, seq, X, rows, D, snap_k, snap_v)
 
 
+def _forward_rows_window_keeps_snapshot(model, seq, X, rows, D, snap_k=None, snap_v=None):
+    """DualCache pass whose window rows attend with the snapshot's K/V
+    instead of their fresh ones."""
+    if snap_k is None:
+        return _forward_rows(model, seq, X, rows, D)
+    rows = np.asarray(rows)
+    pos = seq.L + rows
+    Ks, Vs = [], []
+    for li, layer in enumerate(model.layers):
+        Q, K, V = OM.layer_qkv(model, layer, X, pos)
+        Kc = np.concatenate([seq.cache_k[li], snap_k[li]], axis=0)
+        Vc = np.concatenate([seq.cache_v[li], snap_v[li]], axis=0)
+        O, _ = OM.attention(Q, Kc, Vc, OM.visible(pos, np.arange(seq.L + D), D), model.G)
+        X = OM.layer_rest(model, layer, X, O)
+        Ks.append(K)
+        Vs.append(V)
+    return OM._norm(model, X), Ks, Vs
+
+
+def _embed_token_id_when_masked(model, tokens, masked):
+    return model.E[np.asarray(tokens)].astype(np.float64)
+
+
 MUTANTS = [
+    ("forward_rows", _forward_rows_window_keeps_snapshot, P.test_dualcache_whole_block_window_equals_exact_step_on_any_state),
+    ("embed", _embed_token_id_when_masked, P.test_masked_positions_take_the_mask_embedding),
     ("rope", _rope_interleaved, P.test_rope_hand_example_fixes_pairing_and_sign),
     ("rope", _rope_negative, P.test_rope_hand_example_fixes_pairing_and_sign),
     ("rope", _rope_freq_d2, P.test_rope_hand_example_fixes_pairing_and_sign),

@@ -140,6 +140,58 @@ def test_dualcache_pass_with_current_snapshot_equals_exact_pass():
     np.testing.assert_allclose(Hw, H[rows], rtol=1e-11, atol=1e-14)
 
 
+def test_dualcache_whole_block_window_equals_exact_step_on_any_state():
+    """S = D: every in-block row is a window row, so a DualCache step
+    recomputes all of them through every layer and must equal the exact step
+    on the current state, including after unmasking since the refresh."""
+    cfg, m, prompts = _small(8)
+    D = cfg.D
+    rng = np.random.default_rng(21)
+    q = OM.prefill(m, prompts[0], D)
+    OM.new_block(q, D)
+    OM.e_step(m, q, 0, D, 2.0, D)                         # refresh
+    idx = rng.choice(np.flatnonzero(q.masked), size=5, replace=False)
+    q.tokens[idx] = rng.integers(0, cfg.V, size=5)
+    q.masked[idx] = False
+    state = (q.tokens.copy(), q.masked.copy())
+    dc = OM.dc_step(m, q, 0, D, 2.0, D)
+    q.tokens, q.masked = state[0].copy(), state[1].copy()
+    e = OM.e_step(m, q, 0, D, 2.0, D)
+    np.testing.assert_allclose(dc.H, e.H, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dc.src, e.src, rtol=1e-11, atol=1e-14)
+    for l in range(cfg.n_layers):
+        np.testing.assert_allclose(dc.K[l], e.K[l], rtol=1e-11, atol=1e-14)
+    assert dc.picked == e.picked
+
+
+def test_masked_positions_take_the_mask_embedding():
+    """v2 notes, Key design 2: masked positions enter as row V of E whatever
+    id they hold; the step changes when E[V] changes."""
+    cfg, m, prompts = _small(9)
+    D, S = cfg.D, cfg.S
+    rng = np.random.default_rng(22)
+    base_q = OM.prefill(m, prompts[0], D)
+    OM.new_block(base_q, D)
+    base_q.tokens[:S] = rng.integers(0, cfg.V, S)
+    base_q.masked[:S] = False
+
+    def run(model, tokens):
+        q = OM.MSeq(base_q.cache_k, base_q.cache_v, base_q.carry, list(base_q.history), tokens.copy(),
+                    base_q.masked.copy())
+        e = OM.e_step(model, q, 1, S, 2.0, D)
+        d = OM.dc_step(model, q, 1, S, 2.0, D)
+        return np.concatenate([e.H.ravel(), d.H.ravel(), e.conf, d.conf])
+
+    base = run(m, base_q.tokens)
+    t2 = base_q.tokens.copy()
+    t2[base_q.masked] = rng.integers(0, cfg.V, int(base_q.masked.sum()))
+    np.testing.assert_array_equal(run(m, t2), base)
+    E2 = m.E.copy()
+    E2[cfg.V] += 0.05 * rng.standard_normal(E2.shape[1])
+    m2 = OM.LM(E2, m.layers, m.Wlm, m.Hq, m.Hkv, m.d, m.eps, m.theta)
+    assert np.abs(run(m2, base_q.tokens) - base).max() > 1e-6 * np.abs(base).max()
+
+
 def test_prefill_of_longer_prompt_equals_prefill_then_commit():
     cfg, m, prompts = _small(6)
     D = cfg.D

@@ -75,7 +75,27 @@ def _commit_stale(model, seq, D):
     return H
 
 
+def _dc_step_window_keeps_snapshot_kv(model, seq, s, S, tau, D):
+    """DualCache step whose window rows attend with the snapshot's K/V
+    instead of the K/V of their current tokens."""
+    lo = s * S
+    rows = np.arange(lo, lo + S)
+    X = R.embed(model, seq.tokens[rows], seq.masked[rows], seq.plant[rows])
+    _, Kw, Vw = R.project(model, X)
+    H = R._block_forward(model, seq, rows, seq.snap_k, seq.snap_v, X, D)
+    src = np.stack([H[j - 1 - lo] if j - 1 >= lo else seq.snap_h for j in range(lo, lo + S)])
+    am, mx, lse, conf, picked = R._decide(model, seq, s, S, tau, src)
+    return R.StepResult(H, rows, src, am, mx, lse, conf, picked, Kw, Vw)
+
+
+def _embed_token_id_when_masked(model, tokens, masked, plant=None):
+    X = model.E[np.asarray(tokens)].astype(np.float64)
+    return X if plant is None else X + np.asarray(plant, dtype=np.float64)
+
+
 MUTATIONS = {
+    "dualcache_window_keeps_snapshot_kv": ("dc_step", _dc_step_window_keeps_snapshot_kv),
+    "masked_rows_embed_their_token_id": ("embed", _embed_token_id_when_masked),
     "gqa_head_modulo": ("kv_head", lambda h, G: h % G),
     "mask_causal_inside_block": ("visible", lambda q, k, D: np.asarray(k)[None, :] <= np.asarray(q)[:, None]),
     "mask_everything_visible": ("visible", lambda q, k, D: np.ones((len(q), len(k)), bool)),
@@ -108,7 +128,17 @@ PINS = [
     lambda: P.test_p2_threshold_one_unmasks_one_token_per_step("dual"),
     lambda: P.test_p1_block_cache_equals_full_recompute(P.TINY, "dual"),
     P.test_p7_prefill_then_commit_equals_multi_block_prefill,
+    P.test_p4_dualcache_whole_block_window_equals_exact_step_on_any_state,
+    P.test_p4_dualcache_window_rows_are_exact_in_one_layer,
+    P.test_p10_masked_positions_take_the_mask_embedding,
 ]
+
+# the pin written for each mistake must catch it by itself
+TARGETED = {
+    "dualcache_window_keeps_snapshot_kv": [P.test_p4_dualcache_whole_block_window_equals_exact_step_on_any_state,
+                                           P.test_p4_dualcache_window_rows_are_exact_in_one_layer],
+    "masked_rows_embed_their_token_id": [P.test_p10_masked_positions_take_the_mask_embedding],
+}
 
 
 def test_pins_pass_unmutated():
@@ -127,3 +157,12 @@ def test_mutation_is_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught.append(getattr(pin, "__name__", "pin"))
     assert caught, f"mutation {name} slipped through every pin"
+
+
+@pytest.mark.parametrize("name", sorted(TARGETED))
+def test_targeted_pin_catches_its_mutation(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(R, attr, fn)
+    for pin in TARGETED[name]:
+        with pytest.raises(AssertionError):
+            pin()

@@ -14,6 +14,10 @@ P6  unmask rule against enumeration of every subset of a tiny window
 P7  after a commit the cache rows equal the K/V of a full recomputation
 P8  lockstep and per-sequence window progression give identical results
 P9  permuting the committed keys leaves attention unchanged
+P10 a masked position enters as the [MASK] embedding, whatever id it holds
+P4 also covers the DualCache window rows: a DualCache step whose window is the
+whole block equals the exact step on any token state, and in one layer every
+window row of a DualCache step is exact (a row's K/V depend on its own token)
 """
 import itertools
 import math
@@ -211,6 +215,91 @@ def test_p4_dualcache_refreshed_every_step_equals_exact_mode():
     for a, b in zip(exact, dual):
         assert np.array_equal(a.tokens, b.tokens)
         assert rel(a.cache_k, b.cache_k) < 1e-12 and rel(a.carry, b.carry) < 1e-12
+
+
+def _decode_since_refresh(q, lo, hi, n, rng, V):
+    """Unmask n masked positions of [lo, hi) to random ids, as the steps that
+    follow a refresh would."""
+    idx = rng.choice(np.flatnonzero(q.masked[lo:hi]) + lo, size=n, replace=False)
+    q.tokens[idx] = rng.integers(0, V, size=n)
+    q.masked[idx] = False
+
+
+def test_p4_dualcache_whole_block_window_equals_exact_step_on_any_state():
+    """S = D: the window is the whole block, so no in-block row lies outside
+    it and a DualCache step recomputes all of them.  After any unmasking
+    since the refresh it must equal the exact step on the current state."""
+    cfg = replace(TINY, B=2, S=TINY.D)
+    m, seqs = tiny_seqs(cfg, seed=6)
+    rng = np.random.default_rng(13)
+    for q in seqs:
+        R.e_step(m, q, 0, cfg.S, 2.0, cfg.D)                 # refresh
+        _decode_since_refresh(q, 0, cfg.D, 3, rng, cfg.V)
+        state = (q.tokens.copy(), q.masked.copy())
+        dc = R.dc_step(m, q, 0, cfg.S, 2.0, cfg.D)
+        q.tokens, q.masked = state[0].copy(), state[1].copy()
+        e = R.e_step(m, q, 0, cfg.S, 2.0, cfg.D)
+        assert rel(dc.H, e.H) < 1e-12 and rel(dc.src, e.src) < 1e-12
+        assert rel(dc.K, e.K) < 1e-12 and rel(dc.V, e.V) < 1e-12
+        assert np.array_equal(dc.argmax, e.argmax) and dc.picked == e.picked
+
+
+def test_p4_dualcache_window_rows_are_exact_in_one_layer():
+    """In a one-layer model a row's K/V are a projection of its own input row,
+    and between a refresh and a DualCache step only window positions change,
+    so the snapshot K/V of the other rows still equal fresh ones.  The
+    DualCache step must then equal the exact step on the current state at
+    every window row; only the row feeding the window's first position
+    differs: it is the snapshot row, taken before the window changed."""
+    cfg = replace(TINY, B=2)
+    m, seqs = tiny_seqs(cfg, seed=7, window=1)
+    rng = np.random.default_rng(14)
+    s, S, D = 1, cfg.S, cfg.D
+    lo = s * S
+    for q in seqs:
+        refresh = R.e_step(m, q, s, S, 2.0, D)
+        _decode_since_refresh(q, lo, lo + S, 2, rng, cfg.V)
+        state = (q.tokens.copy(), q.masked.copy())
+        dc = R.dc_step(m, q, s, S, 2.0, D)
+        q.tokens, q.masked = state[0].copy(), state[1].copy()
+        e = R.e_step(m, q, s, S, 2.0, D)
+        assert rel(dc.H, e.H[lo:lo + S]) < 1e-12
+        assert rel(dc.src[1:], e.src[1:]) < 1e-12
+        assert rel(dc.src[0], refresh.H[lo - 1]) < 1e-12
+        assert rel(dc.src[0], e.H[lo - 1]) > 1e-9
+
+
+# --------------------------------------------------------------------------
+# P10: a masked position enters as the [MASK] embedding
+# --------------------------------------------------------------------------
+def test_p10_masked_positions_take_the_mask_embedding():
+    """v2 notes, Key design 2: a masked position's input is the learnable
+    [MASK] embedding (row V of E), whatever id is stored at that position.
+    Exact and DualCache steps are unchanged when the ids at masked positions
+    change, and change when E[V] changes."""
+    cfg = replace(TINY, B=1)
+    m, (q0,) = tiny_seqs(cfg, seed=8, window=1, all_masked=False)
+    assert q0.masked.sum() >= 2 and (~q0.masked).sum() >= 2
+    rng = np.random.default_rng(15)
+
+    def run(model, tokens):
+        q = R.Seq(q0.cache_k, q0.cache_v, q0.carry, None, tokens.copy(), q0.masked.copy(), q0.plant)
+        e = R.e_step(model, q, 1, cfg.S, 2.0, cfg.D)
+        d = R.dc_step(model, q, 1, cfg.S, 2.0, cfg.D)
+        return np.concatenate([e.H.ravel(), e.K.ravel(), d.H.ravel(), e.conf, d.conf])
+
+    base = run(m, q0.tokens)
+    t2 = q0.tokens.copy()
+    t2[q0.masked] = rng.integers(0, cfg.V, int(q0.masked.sum()))
+    assert np.array_equal(run(m, t2), base)
+    E2 = m.E.copy()
+    E2[cfg.V] += 0.05 * rng.standard_normal(cfg.hidden)
+    assert rel(run(replace(m, E=E2), q0.tokens), base) > 1e-6
+    # an unmasked position is a lookup of its own id
+    t3 = q0.tokens.copy()
+    j = int(np.flatnonzero(~q0.masked)[0])
+    t3[j] = (t3[j] + 1) % cfg.V
+    assert rel(run(m, t3), base) > 1e-6
 
 
 # --------------------------------------------------------------------------
