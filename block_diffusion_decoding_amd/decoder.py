@@ -102,6 +102,7 @@ class BlockDecoder:
         self.lm_timer = None    # object whose start() / stop() bracket every LM-head call when set
         self._capturing = False
         self.graphs = {}        # (kind, s) -> captured HIP graph of that step ("W": whole window)
+        self._held_ws = {}      # tag -> workspace the captured graphs point into
         self._rings = {}        # S -> [S, B] pinned: mask bits after each step slot of a window
 
     # ------------------------------------------------------------------ state
@@ -131,7 +132,7 @@ class BlockDecoder:
         [B, D, hidden] (offset on the block's input rows) and carry offset."""
         self.set_tokens(tokens, masked)
         if plant is None:
-            if self.graphs:
+            if self.has_graphs():
                 self.plant.zero_()   # captured steps read the persistent plant buffer
             else:
                 self.plant = None
@@ -143,6 +144,17 @@ class BlockDecoder:
                 self.plant.copy_(src)
         if carry_offset is not None:
             self.H[:, 0] += torch.as_tensor(carry_offset).to(self.device, self.dtype)
+
+    def has_graphs(self) -> bool:
+        """Whether captured graphs hold pointers into this decoder's buffers."""
+        return bool(self.graphs)
+
+    def hold_workspaces(self, needs: dict):
+        """Size the shared workspaces for ``needs`` ({tag: bytes}) and keep
+        references to them: captured graphs hold their raw pointers, and a
+        later, larger call anywhere in the process replaces the shared
+        workspace of that tag, which must not free the one the graphs use."""
+        self._held_ws = {tag: ops.workspace(n, self.device, tag) for tag, n in needs.items()}
 
     def new_block(self):
         B, D = self.dims.B, self.dims.D
@@ -318,8 +330,7 @@ class BlockDecoder:
         B, D = dm.B, dm.D
         if self.plant is None:
             self.plant = torch.zeros(B, D, dm.hidden, dtype=self.dtype, device=self.device)
-        for tag, n in self._workspace_needs(S).items():
-            ops.workspace(n, self.device, tag)
+        self.hold_workspaces(self._workspace_needs(S))
         for s in range(D // S):
             self._window(s, S)
         torch.cuda.synchronize()

@@ -71,6 +71,9 @@ class PerSequenceDecoder(BlockDecoder):
         self.opening = np.ones(B, bool)          # next step opens the window (exact step)
         self.own_steps = np.zeros(B, np.int64)
 
+    def has_graphs(self) -> bool:
+        return self._graph is not None or super().has_graphs()
+
     # ------------------------------------------------------------ host side
     def begin_block(self):
         self.win[:] = 0
@@ -133,13 +136,12 @@ class PerSequenceDecoder(BlockDecoder):
         B, D = dm.B, dm.D
         if self.plant is None:
             self.plant = torch.zeros(B, D, dm.hidden, dtype=self.dtype, device=self.device)
-        for tag, n in {"attn": ops.bd_block_attn_workspace_size(self.dtype, B, dm.Hq, dm.Hkv, dm.d, D, dm.cap, D),
-                       "lm": ops.bd_lmhead_workspace_size(self.dtype, B * self.S, dm.hidden, dm.V),
-                       "gemm": max(ops.bd_qkv_proj_workspace_size(self.dtype, B * D, dm.hidden, dm.Hq * dm.d,
-                                                                  dm.Hkv * dm.d),
-                                   ops.bd_linear_workspace_size(self.dtype, B * D, dm.hidden, dm.Hq * dm.d),
-                                   ops.bd_linear_workspace_size(self.dtype, B, dm.hidden, dm.Hq * dm.d))}.items():
-            ops.workspace(n, self.device, tag)
+        self.hold_workspaces({
+            "attn": ops.bd_block_attn_workspace_size(self.dtype, B, dm.Hq, dm.Hkv, dm.d, D, dm.cap, D),
+            "lm": ops.bd_lmhead_workspace_size(self.dtype, B * self.S, dm.hidden, dm.V),
+            "gemm": max(ops.bd_qkv_proj_workspace_size(self.dtype, B * D, dm.hidden, dm.Hq * dm.d, dm.Hkv * dm.d),
+                        ops.bd_linear_workspace_size(self.dtype, B * D, dm.hidden, dm.Hq * dm.d),
+                        ops.bd_linear_workspace_size(self.dtype, B, dm.hidden, dm.Hq * dm.d))})
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):

@@ -80,8 +80,14 @@ def lm_stats_close(argmax, conf, mx, lse, ref_logits, rtol, what=""):
 
 
 def unmask_close(got_masked, ref_masked, before_masked, ref_conf_win, win_lo, tau, rtol, what=""):
-    """Compare unmask decisions of one window (bool arrays [B, D])."""
+    """Compare unmask decisions of one window (bool arrays [B, D]).
+
+    Returns (decisions compared, fallback ties).  On a fallback tie (no
+    candidate passes and the best two oracle confidences lie within
+    rtol * conf) the window must still unmask exactly one candidate, and
+    that one must lie within the tie band of the best."""
     B, D = ref_masked.shape
+    n_cmp = n_tie = 0
     for b in range(B):
         W = len(ref_conf_win[b])
         cand = [r for r in range(W) if before_masked[b, win_lo + r]]
@@ -92,15 +98,24 @@ def unmask_close(got_masked, ref_masked, before_masked, ref_conf_win, win_lo, ta
         if not passing and len(cand) >= 2:
             cs = sorted((conf[r] for r in cand), reverse=True)
             fallback_tie = cs[0] - cs[1] <= rtol * cs[0]
+        if fallback_tie:
+            n_tie += 1
+            if not near:
+                best = max(conf[r] for r in cand)
+                got = [r for r in cand if not got_masked[b, win_lo + r]]
+                assert len(got) == 1, f"{what}: seq {b} fallback tie unmasked {len(got)} positions"
+                assert best - conf[got[0]] <= rtol * best, f"{what}: seq {b} fallback pick outside the tie band"
         for r in range(W):
-            if r in near or (fallback_tie and not passing):
+            if r in near or fallback_tie:
                 continue
             j = win_lo + r
             assert got_masked[b, j] == ref_masked[b, j], f"{what}: seq {b} position {j} unmask decision differs"
+            n_cmp += r in cand
         # outside the window nothing changes
         outside = np.ones(D, bool)
         outside[win_lo:win_lo + W] = False
         assert np.array_equal(got_masked[b, outside], before_masked[b, outside])
+    return n_cmp, n_tie
 
 
 # --------------------------------------------------------------------------

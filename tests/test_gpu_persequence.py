@@ -82,3 +82,130 @@ def test_per_sequence_progression_teacher_forced(graph):
         rows_close(down(dec.H)[b, 0], q.carry, rtol, "carry after commit")
     say(f"    {n} batched steps, own steps per sequence {own.tolist()}, {mixed} mixed steps")
     assert n == own.max() and mixed > 0
+
+
+# --------------------------------------------------------------------------
+# the two calls of the per-sequence step, one by one
+# --------------------------------------------------------------------------
+def ops():
+    from block_diffusion_decoding_amd import ops as o
+    return o
+
+
+@pytest.mark.parametrize("D,S", [(32, 8), (32, 4), (64, 16)])
+@pytest.mark.parametrize("tau", [0.9, 0.3])
+def test_threshold_unmask_windows_against_oracle_rule(D, S, tau):
+    """Each sequence applies the threshold rule to its own window (the
+    oracle's rule per sequence, decided in fp32 on both sides); a window at
+    D (a sequence that has finished the block) changes nothing.  Tokens,
+    mask bits, counts and compacted positions are compared bit for bit."""
+    from gpu_util import up
+    say(f"[per-sequence] unmask windows D={D} S={S} tau={tau}")
+    B = 40
+    rng = np.random.default_rng(D * 7 + S)
+    conf = rng.choice(np.array([0.05, 0.3, 0.9, 0.95, 0.99], np.float32), size=(B, S)).astype(np.float32)
+    conf[::6] = rng.random((len(conf[::6]), S)).astype(np.float32)
+    conf[3] = 0.9                                    # exact threshold ties
+    conf[4] = 0.25                                   # fallback ties: lowest position wins
+    am = rng.integers(0, 150000, size=(B, S)).astype(np.int32)
+    masked = rng.random((B, D)) < 0.5
+    masked[5] = False                                # no candidates anywhere
+    masked[6] = True
+    tokens = np.where(masked, 0, rng.integers(0, 150000, size=(B, D))).astype(np.int32)
+    win_lo = (rng.integers(0, D // S + 1, size=B) * S).astype(np.int32)
+    win_lo[:4] = [D, 0, D - S, D]                    # finished sequences among them
+    t_tok, t_bits = up(tokens), up(bi.mask_bits(masked).view(np.int64))
+    n = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    pos = torch.full((B, S), -9, dtype=torch.int32, device=DEV)
+    ops().bd_threshold_unmask_windows(up(conf), up(am), t_tok, t_bits, up(win_lo), threshold=tau,
+                                      n_unmasked=n, unmasked_pos=pos)
+    got_t, got_m = t_tok.cpu().numpy(), bi.bits_to_mask(t_bits.cpu().numpy().view(np.uint64), D)
+    got_n, got_p = n.cpu().numpy(), pos.cpu().numpy()
+    for b in range(B):
+        if win_lo[b] >= D:
+            rt, rm, rn, rp = tokens[b:b + 1], masked[b:b + 1], [0], -np.ones((1, S), np.int64)
+        else:
+            rt, rm, rn, rp = R.batch_threshold_unmask(conf[b:b + 1], am[b:b + 1], tokens[b:b + 1], masked[b:b + 1],
+                                                      int(win_lo[b]), np.float32(tau))
+        what = f"sequence {b} window {win_lo[b]}"
+        assert np.array_equal(got_t[b], rt[0]) and np.array_equal(got_m[b], rm[0]), what
+        assert got_n[b] == rn[0] and np.array_equal(got_p[b], rp[0]), what
+
+
+@pytest.mark.parametrize("n_rows,row_shape,dt,pair", [(32, (4, 128), torch.bfloat16, True),
+                                                      (33, (1536,), torch.bfloat16, False),
+                                                      (64, (4,), torch.float32, True),
+                                                      (7, (2, 64), torch.float32, False)])
+def test_copy_rows_random_masks(n_rows, row_shape, dt, pair):
+    """dst[b, r] = src[b, r] exactly where bit r of row_mask[b] is set; every
+    other row of dst is left as it was (one or two tensor pairs)."""
+    say(f"[per-sequence] copy rows {n_rows} x {row_shape} {dt} pair={pair}")
+    B = 19
+    g = torch.Generator().manual_seed(n_rows)
+    mk = lambda: torch.randn(B, n_rows, *row_shape, generator=g).to(DEV, dt)
+    src0, dst0, src1, dst1 = mk(), mk(), mk(), mk()
+    rng = np.random.default_rng(n_rows)
+    keep = rng.random((B, n_rows)) < 0.4
+    keep[0] = False
+    keep[1] = True
+    bits = np.zeros(B, np.uint64)
+    for r in range(n_rows):
+        bits |= keep[:, r].astype(np.uint64) << np.uint64(r)
+    want0, want1 = dst0.clone(), dst1.clone()
+    kt = torch.from_numpy(keep).to(DEV)
+    want0[kt] = src0[kt]
+    want1[kt] = src1[kt]
+    mask = torch.from_numpy(bits.view(np.int64)).to(DEV)
+    if pair:
+        ops().bd_copy_rows(mask, src0, dst0, src1, dst1)
+    else:
+        ops().bd_copy_rows(mask, src0, dst0)
+        want1 = dst1
+    torch.cuda.synchronize()
+    assert torch.equal(dst0, want0) and torch.equal(dst1, want1)
+
+
+def test_graph_keeps_plant_and_workspaces_after_reset_and_growth():
+    """A captured per-sequence step keeps reading its plant buffer after
+    new_block() (no plant: the buffer is zeroed, not freed), and its
+    workspaces stay alive after larger calls elsewhere replace the shared
+    ones: replayed steps equal the steps of a decoder that never captured."""
+    cfg = MID
+    say("[per-sequence] graph after new_block and workspace growth")
+    w, pre, st, plant, _ = workload(cfg, 1, all_masked=True, plant_rate=1.0)
+    a = make_decoder(cfg, w, pre, st, None)
+    b = make_decoder(cfg, w, pre, st, plant)
+    b.capture_step(cfg.tau)
+    held = {tag: t.data_ptr() for tag, t in b._held_ws.items()}
+    assert set(held) == {"attn", "lm", "gemm"}
+    # a larger call anywhere in the process replaces the shared workspace of its
+    # tag (ops.workspace grows it); the graph's buffers must survive that
+    o = ops()
+    for tag, t in b._held_ws.items():
+        grown = o.workspace(t.numel() + (1 << 20), b.device, tag)
+        assert grown.data_ptr() != held[tag] and o.workspace(0, b.device, tag) is grown
+    # and calls through the grown workspaces run
+    Bg, cap = 8, 2048
+    q = torch.zeros(Bg, 8, 12, 128, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(Bg, 2, cap, 128, dtype=torch.bfloat16, device=DEV)
+    kb = torch.zeros(Bg, 32, 2, 128, dtype=torch.bfloat16, device=DEV)
+    lens = torch.full((Bg,), cap - 32, dtype=torch.int32, device=DEV)
+    o.bd_block_attn(q, kc, kc, lens, kb, kb, torch.zeros_like(q), D=32, q_off=8)
+    del q, kc, kb
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    for d in (a, b):
+        d.new_block()
+        d.begin_block()
+    n = 0
+    while True:
+        ra, rb = a.step(cfg.tau), b.step(cfg.tau)
+        assert ra == rb
+        if not ra:
+            break
+        torch.cuda.synchronize()
+        for x, y in ((a.tokens, b.tokens), (a.mask_bits, b.mask_bits), (a.Hcat, b.Hcat), (a.blk_k, b.blk_k)):
+            assert torch.equal(x, y), f"step {n}"
+        n += 1
+        assert n < 4 * cfg.D
+    say(f"    {n} steps replayed, bit-identical to eager")

@@ -18,24 +18,31 @@ from oracle import refine as R
 pytestmark = pytest.mark.gpu
 
 
-def compare_step(cfg, dec, m, seqs, results, kind, s, S, before_masked, what):
+def compare_step(cfg, dec, m, seqs, results, kind, s, S, before_masked, what, seq_ids=None):
+    """One step of the GPU decoder against the oracle's results for the
+    sequences ``seq_ids`` (default: all).  With candidate compaction the LM
+    head writes only the masked candidates' window slots, so the statistics
+    are compared there; otherwise at every window slot."""
     rtol = TOL[cfg.dtype]
-    B, D = cfg.B, cfg.D
+    D = cfg.D
+    ids = list(range(cfg.B)) if seq_ids is None else list(seq_ids)
     w = dec.last
     # output rows of this step
     H = down(dec.H)
-    for b, r in enumerate(results):
-        rows = r.rows
-        rows_close(H[b, 1 + rows], r.H, rtol, f"{what} H seq {b}")
+    for b, r in zip(ids, results):
+        rows_close(H[b, 1 + r.rows], r.H, rtol, f"{what} H seq {b}")
     # LM-head statistics of the window rows
-    src = np.concatenate([r.src for r in results])
+    sel = np.ones((len(ids), S), bool)
+    if dec.uses_compaction(S):
+        sel = before_masked[:, s * S:(s + 1) * S].copy()
+    src = np.stack([r.src for r in results])[sel]
     ref_logits = R.lm_logits(m.Wlm, src)
-    lm_stats_close(w["argmax"].cpu().numpy().reshape(-1), down(w["conf"]).reshape(-1),
-                   down(w["maxl"]).reshape(-1), down(w["lse"]).reshape(-1), ref_logits, rtol, f"{what} lm")
+    stat = lambda k: down(w[k])[ids][sel] if k != "argmax" else w[k].cpu().numpy()[ids][sel]
+    lm_stats_close(stat("argmax"), stat("conf"), stat("maxl"), stat("lse"), ref_logits, rtol, f"{what} lm")
     # unmask decisions
     ref_masked = np.stack([q.masked for q in seqs])
-    unmask_close(dec.masked_host(), ref_masked, before_masked, [r.conf for r in results], s * S, cfg.tau, rtol,
-                 f"{what} unmask")
+    n_cmp, n_tie = unmask_close(dec.masked_host()[ids], ref_masked, before_masked, [r.conf for r in results], s * S,
+                                cfg.tau, rtol, f"{what} unmask")
     return [len(r.picked) for r in results]
 
 
@@ -95,13 +102,17 @@ def test_tiny_block_decode_teacher_forced(cfg, mode):
     assert n_steps >= D // S and sum(passes) == cfg.B * D
 
 
-@pytest.mark.parametrize("cfg,rate", [(bi.C2, None), (bi.C3, 0.5), (bi.C3, 1.0)], ids=["1.5B", "7B-r0.5", "7B-r1"])
-def test_refresh_then_dualcache_steps(cfg, rate):
+@pytest.mark.parametrize("cfg,rate,compact", [(bi.C2, None, None), (bi.C3, 0.5, None), (bi.C3, 1.0, None),
+                                              (bi.C3, 0.5, True)],
+                         ids=["1.5B", "7B-r0.5", "7B-r1", "7B-r0.5-candidates"])
+def test_refresh_then_dualcache_steps(cfg, rate, compact):
     """Window 1: exact refresh step, then two DualCache steps (the second after
-    the first one's unmasking), against the oracle."""
-    say(f"[step] {cfg.name} rate={rate}")
+    the first one's unmasking), against the oracle; with ``compact`` the LM
+    head runs on the masked candidates only."""
+    say(f"[step] {cfg.name} rate={rate} compact={compact}")
     w, pre, st, plant, carry_plant = workload(cfg, 0, window=1, plant_rate=rate)
-    dec = gpu_decoder(cfg, w, pre, st, plant, carry_plant)
+    dec = gpu_decoder(cfg, w, pre, st, plant, carry_plant, compact=compact)
+    assert dec.uses_compaction(cfg.S) == bool(compact)
     m, seqs = oracle_seqs(cfg, w, pre, st, plant, carry_plant)
     S, D, tau, s = cfg.S, cfg.D, cfg.tau, 1
     tokens_per_step = []
