@@ -9,7 +9,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbd.so")
 
-BD_OK, BD_EINVAL, BD_EUNSUPPORTED, BD_ECAPACITY, BD_EHIP = 0, 1, 2, 3, 4
+BD_OK, BD_EINVAL, BD_EUNSUPPORTED, BD_ECAPACITY, BD_EHIP, BD_ESCRATCH = 0, 1, 2, 3, 4, 5
 BD_F32, BD_BF16 = 0, 1
 
 c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
@@ -32,6 +32,12 @@ SIGNATURES = {
                               c_void_p, c_void_p, c_int,
                               c_float, c_void_p, c_void_p,
                               c_void_p, c_size_t, c_void_p]),
+    "bd_block_attn_noalloc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_void_p, c_int, c_int,
+                                      c_void_p, c_void_p, c_void_p, c_int,
+                                      c_void_p, c_void_p, c_int,
+                                      c_float, c_void_p, c_void_p, c_void_p]),
+    "bd_block_attn_noalloc_scratch_bytes": (c_size_t, []),
     "bd_lmhead_workspace_size": (c_size_t, [c_int] * 4),
     "bd_lmhead_confidence": (c_int, [c_int, c_int, c_int, c_int,
                                      c_void_p, c_int, c_void_p, c_void_p,

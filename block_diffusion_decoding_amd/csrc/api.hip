@@ -8,11 +8,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-bd_status hip_status(hipError_t e) {
-  if (e == hipSuccess) return BD_OK;
-  g_last_hip_error = static_cast<int>(e);
-  return BD_EHIP;
-}
+bd_status hip_status(hipError_t e) { return bd_hip_status(e); }
 
 bool valid_dtype(bd_dtype dt) { return dt == BD_F32 || dt == BD_BF16; }
 
@@ -21,6 +17,29 @@ bool valid_rows(const bd_rows& r) { return r.group >= 1 && r.stride >= 0 && r.of
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
+
+bd_status bd_hip_status(hipError_t e) {
+  if (e == hipSuccess) return BD_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return BD_EHIP;
+}
+
+bd_status bd_block_attn_check(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const void* q, int n_q, int q_off,
+                              const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
+                              const void* k_blk, const void* v_blk, int n_blk, float scale, const void* o) {
+  if (!valid_dtype(dt) || B < 0 || n_q < 0) return BD_EINVAL;
+  if (B == 0 || n_q == 0) return BD_OK;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D < 1 || n_blk < 1 || n_blk % D != 0 || q_off < 0 ||
+      q_off + n_q > n_blk || cap < 0)
+    return BD_EINVAL;
+  if (d != 64 && d != 128) return BD_EUNSUPPORTED;
+  if (!q || !kv_len || !k_blk || !v_blk || !o || (cap > 0 && (!k_cache || !v_cache))) return BD_EINVAL;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
+      (cap > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return BD_EINVAL;
+  if (!(scale == scale)) return BD_EINVAL;
+  return BD_OK;
+}
 
 extern "C" {
 
@@ -33,6 +52,7 @@ const char* bd_status_string(bd_status s) {
     case BD_EUNSUPPORTED: return "unsupported";
     case BD_ECAPACITY: return "cache capacity exceeded";
     case BD_EHIP: return "HIP runtime error";
+    case BD_ESCRATCH: return "needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }
@@ -50,17 +70,9 @@ bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const
                         const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
                         const void* k_blk, const void* v_blk, int n_blk, float scale, void* o, float* lse,
                         void* workspace, size_t ws_bytes, void* stream) {
-  if (!valid_dtype(dt) || B < 0 || n_q < 0) return BD_EINVAL;
-  if (B == 0 || n_q == 0) return BD_OK;
-  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D < 1 || n_blk < 1 || n_blk % D != 0 || q_off < 0 ||
-      q_off + n_q > n_blk || cap < 0)
-    return BD_EINVAL;
-  if (d != 64 && d != 128) return BD_EUNSUPPORTED;
-  if (!q || !kv_len || !k_blk || !v_blk || !o || (cap > 0 && (!k_cache || !v_cache))) return BD_EINVAL;
-  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
-      (cap > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
-    return BD_EINVAL;
-  if (!(scale == scale)) return BD_EINVAL;
+  const bd_status chk = bd_block_attn_check(dt, B, Hq, Hkv, d, D, q, n_q, q_off, k_cache, v_cache, kv_len, cap,
+                                            k_blk, v_blk, n_blk, scale, o);
+  if (chk != BD_OK || B == 0 || n_q == 0) return chk;
   const BdAttnPlan p = bd_attn_plan(dt, B, Hq, Hkv, d, n_q, cap, n_blk);
   if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)))
     return BD_EINVAL;

@@ -7,6 +7,16 @@
 
 #include "../../include/bd.h"
 
+// ---- shared by the C-ABI files --------------------------------------------
+// BD_OK for hipSuccess; otherwise records the error for bd_last_hip_error()
+// and returns BD_EHIP.
+bd_status bd_hip_status(hipError_t e);
+
+// Host-side argument checks of bd_block_attn (BD_OK also for empty work).
+bd_status bd_block_attn_check(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const void* q, int n_q, int q_off,
+                              const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
+                              const void* k_blk, const void* v_blk, int n_blk, float scale, const void* o);
+
 // ---- attention -----------------------------------------------------------
 struct BdAttnPlan {
   int R;          // query rows per (sequence, KV head) = n_q * G

@@ -98,6 +98,25 @@ def bd_block_attn(q, k_cache, v_cache, kv_len, k_blk, v_blk, o, *, D, q_off=0, s
     return o
 
 
+def bd_block_attn_noalloc(q, k_cache, v_cache, kv_len, k_blk, v_blk, o, *, D, q_off=0, scale=None, lse=None,
+                          stream=None):
+    """bd_block_attn with its partials in the library's static device buffer
+    (no workspace; nothing allocated); same tensors as bd_block_attn."""
+    lib = _lib.load()
+    B, n_q, Hq, d = q.shape
+    if k_cache is None:
+        Hkv, cap = k_blk.shape[2], 0
+    else:
+        _, Hkv, cap, _ = k_cache.shape
+    if scale is None:
+        scale = d ** -0.5
+    st = lib.bd_block_attn_noalloc(_dt(q), B, Hq, Hkv, d, D, _p(q), n_q, q_off, _p(k_cache), _p(v_cache),
+                                   _p(kv_len), cap, _p(k_blk), _p(v_blk), k_blk.shape[1], float(scale), _p(o),
+                                   _p(lse), _stream(stream))
+    _check("bd_block_attn_noalloc", st)
+    return o
+
+
 def bd_lmhead_workspace_size(dtype, M, hidden, V) -> int:
     return int(_lib.load().bd_lmhead_workspace_size(_DT[dtype], M, hidden, V))
 

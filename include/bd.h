@@ -63,7 +63,9 @@ typedef enum bd_status {
   BD_EINVAL = 1,        /* bad argument (null pointer, shape, small workspace) */
   BD_EUNSUPPORTED = 2,  /* valid but not implemented (e.g. head dim) */
   BD_ECAPACITY = 3,     /* a cache append would exceed its capacity */
-  BD_EHIP = 4           /* a HIP runtime call failed */
+  BD_EHIP = 4,          /* a HIP runtime call failed */
+  BD_ESCRATCH = 5       /* needs more scratch than the static buffer of
+                           bd_block_attn_noalloc holds */
 } bd_status;
 
 typedef enum bd_dtype { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
@@ -119,6 +121,29 @@ bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D,
                         const void* k_blk, const void* v_blk, int n_blk,
                         float scale, void* o, float* lse,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/* bd_block_attn_noalloc -- bd_block_attn without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * layouts, mask, results and error checks as bd_block_attn; the split-key
+ * partials live in a static device buffer of the library instead
+ * (bd_block_attn_noalloc_scratch_bytes() bytes, 32 MiB, one per GPU the
+ * library runs on, held until the process ends).  The call allocates and frees
+ * nothing: the buffer's address is looked up once per device (with that device
+ * current) on the first call there.
+ *   Returns BD_ESCRATCH, before any launch, when the problem needs more than
+ *   the buffer holds (bd_block_attn_workspace_size() of the same arguments;
+ *   every refinement step of the 7B workloads up to 32 sequences x 16384
+ *   committed rows fits; a multi-block prefill may not).
+ *   The stream must belong to the current device.  Every call on a GPU shares
+ *   that GPU's buffer: calls that can overlap on one GPU (different streams,
+ *   threads or processes sharing a context) race and must be serialised by
+ *   the caller.  Nothing in the buffer needs clearing between calls. */
+bd_status bd_block_attn_noalloc(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const void* q, int n_q,
+                                int q_off, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                                int cap, const void* k_blk, const void* v_blk, int n_blk, float scale, void* o,
+                                float* lse, void* stream);
+size_t bd_block_attn_noalloc_scratch_bytes(void);
 
 /* ------------------------------------------------------------------------
  * bd_lmhead_confidence -- LM head with token shift and fused softmax

@@ -32,7 +32,7 @@ def test_header_declares_the_four_calls_and_support():
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
               "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu",
               "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau",
-              "bd_lmhead_unmask", "bd_threshold_unmask_windows", "bd_copy_rows"]:
+              "bd_lmhead_unmask", "bd_threshold_unmask_windows", "bd_copy_rows", "bd_block_attn_noalloc"]:
         assert n in names
 
 
@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     lib = _lib.load()
     assert lib.bd_version().startswith(b"libbd")
-    for s in range(5):
+    for s in range(6):
         assert lib.bd_status_string(s)
     assert lib.bd_last_hip_error() == 0
 
@@ -147,6 +147,40 @@ def test_gemm_and_embed_argument_errors():
     assert lib.bd_linear_workspace_size(0, 64, 3584, 3584) == 0       # fp32: no workspace
     assert lib.bd_embed_rows(1, 1, 65, 0, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
     assert lib.bd_embed_rows(1, 1, 32, 30, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
+
+
+def noalloc(lib, **kw):
+    a = dict(dt=1, B=1, Hq=4, Hkv=2, d=128, D=32, q=FAKE, n_q=8, q_off=8, kc=FAKE, vc=FAKE, kv_len=FAKE,
+             cap=64, kb=FAKE, vb=FAKE, n_blk=32, scale=0.1, o=FAKE, lse=None, s=None)
+    a.update(kw)
+    return lib.bd_block_attn_noalloc(a["dt"], a["B"], a["Hq"], a["Hkv"], a["d"], a["D"], a["q"], a["n_q"],
+                                     a["q_off"], a["kc"], a["vc"], a["kv_len"], a["cap"], a["kb"], a["vb"],
+                                     a["n_blk"], a["scale"], a["o"], a["lse"], a["s"])
+
+
+def test_noalloc_attn_argument_errors_and_scratch_limit():
+    """The static-scratch attention checks its arguments like bd_block_attn and
+    refuses a problem whose partials exceed its buffer, all before any HIP
+    call (so no device is needed here)."""
+    lib = _lib.load()
+    E, U = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED
+    assert lib.bd_block_attn_noalloc_scratch_bytes() == 32 << 20
+    assert noalloc(lib, B=0) == 0 and noalloc(lib, n_q=0) == 0
+    assert noalloc(lib, Hkv=3) == E
+    assert noalloc(lib, q_off=30) == E
+    assert noalloc(lib, n_blk=48) == E
+    assert noalloc(lib, d=96) == U
+    assert noalloc(lib, q=None) == E
+    assert noalloc(lib, o=FAKE + 4) == E
+    assert noalloc(lib, scale=float("nan")) == E
+    # one sequence, an 8-block prefill over 4160 cached rows: its partials do not fit in 32 MiB
+    need = lib.bd_block_attn_workspace_size(1, 1, 28, 4, 128, 256, 4160, 256)
+    assert need > lib.bd_block_attn_noalloc_scratch_bytes()
+    assert noalloc(lib, B=1, Hq=28, Hkv=4, n_q=256, q_off=0, n_blk=256, cap=4160) == _lib.BD_ESCRATCH
+    # every refinement step of the long-context workload fits (32 x 16384 rows, exact step)
+    assert lib.bd_block_attn_workspace_size(1, 32, 28, 4, 128, 32, 16416, 32) <= \
+        lib.bd_block_attn_noalloc_scratch_bytes()
+    assert lib.bd_last_hip_error() == 0
 
 
 def test_launch_without_gpu_reports_hip_error():
