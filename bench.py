@@ -45,6 +45,7 @@ import sys
 import time
 
 from dataclasses import replace
+from typing import NamedTuple
 
 import numpy as np
 import torch
@@ -63,50 +64,80 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-LM_SOURCES = ("lmhead.hip", "stream_gemm.h", "bd_device.h", "bd_launch.h")
 CALIB_BYTES = 1 << 30  # plain device copy that calibrates the HBM byte counters
 
+# Measured HBM traffic records (profiles/*.json), one per counted launch: the
+# launch's main kernel (its template instance, as rocprofv3 names it) and the
+# kernel that follows it in the same call, the section of this script whose
+# profiling run counts them, and the sources the kernels are built from (a
+# stored reading is used only while they are unchanged).
+TRAFFIC = {
+    "lm": {"file": "lmhead_7B_M64_traffic.json", "section": "lm",
+           "sources": ("lmhead.hip", "stream_gemm.h", "bd_device.h", "bd_launch.h"),
+           "main": "lm_stream_kernel<4>", "then": "lm_merge_unmask_kernel",
+           "launch": "bd_lmhead_unmask: lm_stream_kernel<4> (512 work-groups) + lm_merge_unmask_kernel (8 "
+                     "work-groups x 512), 64 rows x 152064 x 3584 (8 sequences x window of 8)"},
+    "attn_dualcache": {"file": "attention_long_context_dualcache_traffic.json", "section": "attn",
+                       "sources": ("attn.hip", "bd_device.h", "bd_launch.h"),
+                       "main": "attn_bf16_kernel<128, 32, 1,", "then": "attn_merge_kernel",
+                       "launch": "bd_block_attn DualCache step: attn_bf16_kernel<128, 32, 1, 8> + "
+                                 "attn_merge_kernel<128, 2>, 32 sequences x 16384 cached rows, 8 fresh rows x 28 "
+                                 "query heads, 4 KV heads, d 128"},
+    "attn_exact": {"file": "attention_long_context_exact_traffic.json", "section": "attn",
+                   "sources": ("attn.hip", "bd_device.h", "bd_launch.h"),
+                   "main": "attn_bf16_kernel<128, 32, 2,", "then": "attn_merge_kernel",
+                   "launch": "bd_block_attn exact step: attn_bf16_kernel<128, 32, 2, 8> + attn_merge_kernel<128, 2>, "
+                             "32 sequences x 16384 cached rows, 32 fresh rows x 28 query heads, 4 KV heads, d 128"},
+}
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the LM-head kernels are built from: a stored
-    counter reading is used only while they are unchanged."""
+
+def kernel_source_hash(kind: str = "lm") -> str:
+    """Hash of the sources a counted launch's kernels are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_diffusion_decoding_amd", "csrc")
-    for f in LM_SOURCES:
+    for f in TRAFFIC[kind]["sources"]:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from(fetch_csv, write_csv):
-    """Turn two rocprofv3 --pmc counter files (FETCH_SIZE, then WRITE_SIZE, both
-    over `bench.py --section lm`) into the HBM bytes per launch of the 64-row
-    7B LM head fused with the unmask (the refinement step's call). Each counter is scaled by what it reads for the 1 GiB plain
-    device copy that run makes (the copy reads and writes exactly CALIB_BYTES)."""
+def traffic_from(kind, fetch_csv, write_csv):
+    """Turn two rocprofv3 --pmc counter files (FETCH_SIZE, then WRITE_SIZE,
+    both over `bench.py --section <section of kind>`) into the HBM bytes per
+    launch of the counted call: every dispatch of its main kernel plus the
+    dispatch of its second kernel that follows it.  Each counter is scaled by
+    what it reads for the plain device copy of CALIB_BYTES the section makes
+    first (the copy reads and writes exactly CALIB_BYTES)."""
     import csv
+    spec = TRAFFIC[kind]
 
     def rows(path, counter):
-        return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rs = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        key = "Dispatch_Id" if rs and "Dispatch_Id" in rs[0] else "Correlation_Id"
+        return sorted(rs, key=lambda r: int(r[key])), key
 
-    out = {"kernel_source_hash": kernel_source_hash(), "calibration_bytes": CALIB_BYTES,
-           "launch": "bd_lmhead_unmask: lm_stream_kernel<4> (512 work-groups) + lm_merge_unmask_kernel (8 "
-                     "work-groups x 512), 64 rows x 152064 x 3584 (8 sequences x window of 8)"}
+    out = {"kernel_source_hash": kernel_source_hash(kind), "calibration_bytes": CALIB_BYTES, "launch": spec["launch"]}
     total = 0.0
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
-        rs = rows(path, counter)
-        main = [float(r["Counter_Value"]) for r in rs if "lm_stream_kernel<4>" in r["Kernel_Name"]]
-        merge = [float(r["Counter_Value"]) for r in rs if "lm_merge_unmask_kernel" in r["Kernel_Name"]]
+        rs, key = rows(path, counter)
+        main, then = [], []
+        for i, r in enumerate(rs):
+            if spec["main"] in r["Kernel_Name"]:
+                nxt = next((x for x in rs[i + 1:] if spec["then"] in x["Kernel_Name"]), None)
+                if nxt is not None:
+                    main.append(float(r["Counter_Value"]))
+                    then.append(float(nxt["Counter_Value"]))
         cp = [float(r["Counter_Value"]) for r in rs
               if "copyBuffer" in r["Kernel_Name"] or "copy_kernel" in r["Kernel_Name"]]
-        if not main or not merge or not cp:
-            raise SystemExit(f"{path}: no {counter} reading for the LM head, its merge or the calibration copy")
-        kib = float(np.median(main)) + float(np.median(merge))
+        if not main or not cp:
+            raise SystemExit(f"{path}: no {counter} reading for {spec['main']} + {spec['then']} or the calibration copy")
+        kib = float(np.median(main)) + float(np.median(then))
         scale = CALIB_BYTES / (max(cp) * 1024.0)
         out[counter] = {"kib_per_launch": kib, "main_kib": float(np.median(main)),
-                        "merge_kib": float(np.median(merge)), "dispatches": len(main), "copy_kib": max(cp),
+                        "then_kib": float(np.median(then)), "dispatches": len(main), "copy_kib": max(cp),
                         "scale": scale, "bytes_per_launch": kib * 1024.0 * scale}
         total += kib * 1024.0 * scale
     out["bytes_per_launch"] = total
-    path = os.path.join(ROOT, "profiles", "lmhead_7B_M64_traffic.json")
+    path = os.path.join(ROOT, "profiles", spec["file"])
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -250,9 +281,22 @@ class Loop:
                 left -= 1
 
 
-def time_call(fn, reps, warm=3, warm_s=0.1):
-    """Median and mean of `reps` calls, after at least `warm` calls and
-    `warm_s` seconds of the same call (the clocks take ~20 ms of sustained
+class Timing(NamedTuple):
+    median: float
+    mean: float
+    p10: float
+    p90: float
+
+    def record(self) -> dict:
+        """Microsecond fields of a single-call record."""
+        return {"us": self.mean * 1e6, "us_median": self.median * 1e6, "us_p10": self.p10 * 1e6,
+                "us_p90": self.p90 * 1e6}
+
+
+def time_call(fn, reps, warm=3, warm_s=0.1) -> Timing:
+    """Median, mean, 10th and 90th percentile (seconds) of `reps` calls, each
+    bracketed by HIP events on the current stream, after at least `warm` calls
+    and `warm_s` seconds of the same call (the clocks take ~20 ms of sustained
     load to settle after the host-side input generation left the GPU idle)."""
     t_end = time.perf_counter() + warm_s
     n = 0
@@ -269,7 +313,7 @@ def time_call(fn, reps, warm=3, warm_s=0.1):
         b.record()
     torch.cuda.synchronize()
     t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
-    return float(np.median(t)), float(np.mean(t))
+    return Timing(float(np.median(t)), float(np.mean(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90)))
 
 
 def extras_e2e(graphs=True, n_blocks=None):
@@ -378,14 +422,14 @@ def extras_train(reps):
     x0, m = bi.make_train_batch(cfg, 0)
     plan = tf.plan(x0, m)
     res = tf.forward(x0, m, plan)
-    t_fwd, _ = time_call(lambda: tf.forward(x0, m, plan), max(3, reps // 4))
+    t_fwd = time_call(lambda: tf.forward(x0, m, plan), max(3, reps // 4)).median
     n = res["count"]
     S2, L2 = 2 * cfg.S, 2 * cfg.L
     q = tf._bufs["q"].view(S2, L2, cfg.Hq, cfg.d)
     k = tf._bufs["k"].view(S2, L2, cfg.Hkv, cfg.d)
     v = tf._bufs["v"].view(S2, L2, cfg.Hkv, cfg.d)
     o = tf._bufs["o"].view(S2, L2, cfg.Hq, cfg.d)
-    t_att, t_att_mean = time_call(lambda: ops.bd_train_attn(q, k, v, o, L=cfg.L, D=cfg.D), reps)
+    t_att, t_att_mean = time_call(lambda: ops.bd_train_attn(q, k, v, o, L=cfg.L, D=cfg.D), reps)[:2]
     fl = train_attn_flops(cfg)
     loss = float(res["loss_sum"].cpu()[0])
     log(f"[bench] training form: forward + loss {t_fwd * 1e3:.2f} ms for {n} supervised tokens "
@@ -560,10 +604,32 @@ def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "p
     return out
 
 
+def calibration_copy():
+    """Plain device copy of CALIB_BYTES: what the HBM byte counters read for
+    it calibrates them in a profiling run of a section."""
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def stored_traffic(kind: str):
+    """Measured HBM bytes per launch from profiles/, while the kernel's
+    sources still hash to the recorded value (else None)."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC[kind]["file"])
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    return rec.get("bytes_per_launch") if rec.get("kernel_source_hash") == kernel_source_hash(kind) else None
+
+
 def extras_attn(c4, reps):
     from block_diffusion_decoding_amd import ops
     out = {}
     T = torch.bfloat16
+    calibration_copy()
     # ---- attention, batch 32 x 16384 committed tokens
     log("[bench] long-context attention inputs")
     pre4 = bi.make_prefix(c4, 0)
@@ -576,13 +642,14 @@ def extras_attn(c4, reps):
         kb = torch.randn(c4.B, c4.D, c4.Hkv, c4.d, device="cuda", dtype=T) * 0.02
         vb = torch.randn_like(kb) * 0.02
         o = torch.empty_like(q)
-        med, mean = time_call(lambda: ops.bd_block_attn(q, kc, vc, lens, kb, vb, o, D=c4.D, q_off=0), reps)
+        t = time_call(lambda: ops.bd_block_attn(q, kc, vc, lens, kb, vb, o, D=c4.D, q_off=0), reps)
+        mean = t.mean
         nbytes = c4.B * (16384 + c4.D) * 2 * c4.Hkv * c4.d * 2 + 2 * c4.B * n_q * c4.Hq * c4.d * 2
         flops = 4 * c4.B * n_q * c4.Hq * c4.d * (16384 + c4.D)
         out[f"attn_long_{name}"] = {
-            "shape": f"B=32 L=16384 n_q={n_q} Hq=28 Hkv=4 d=128 bf16", "us": mean * 1e6, "us_median": med * 1e6,
+            "shape": f"B=32 L=16384 n_q={n_q} Hq=28 Hkv=4 d=128 bf16", **t.record(),
             "bytes": nbytes, "GB/s": nbytes / mean / 1e9, "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS,
-            "TFLOP/s": flops / mean / 1e12}
+            "TFLOP/s": flops / mean / 1e12, "traffic": stored_traffic(f"attn_{name}")}
         log(f"[bench] attention {name}: {mean * 1e6:.1f} us, {nbytes / mean / 1e9:.0f} GB/s")
     del kc, vc
     return out
@@ -622,28 +689,33 @@ def extras_lm(w3, reps):
     from block_diffusion_decoding_amd import ops
     out = {}
     T = torch.bfloat16
-    # plain device copy of known size: calibrates the HBM byte counters of a
-    # profiling run of this section
-    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
+    calibration_copy()
     # ---- LM head alone: 1024 rows on the 7B head (MFMA bound)
     Wlm = torch.from_numpy(w3.Wlm).to("cuda", T)
     for M, key in ((1024, "lmhead_7B_M1024"), (256, "lmhead_7B_M256"), (64, "lmhead_7B_M64")):
         h = torch.randn(M, 3584, device="cuda", dtype=T) * 0.05
         am = torch.empty(M, dtype=torch.int32, device="cuda")
         cf = torch.empty(M, dtype=torch.float32, device="cuda")
-        med, mean = time_call(lambda: ops.bd_lmhead_confidence(h, None, Wlm, am, cf), reps)
+        t = time_call(lambda: ops.bd_lmhead_confidence(h, None, Wlm, am, cf), reps)
+        mean = t.mean
         flops = 2.0 * M * 3584 * 152064
         nbytes = 152064 * 3584 * 2 + M * 3584 * 2 + 16 * M
-        out[key] = {"us": mean * 1e6, "TFLOP/s": flops / mean / 1e12,
+        out[key] = {**t.record(), "TFLOP/s": flops / mean / 1e12,
                     "frac_mfma": flops / mean / 1e12 / BF16_PEAK_TFLOPS,
                     "GB/s": nbytes / mean / 1e9, "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
         log(f"[bench] lm head M={M}: {mean * 1e6:.1f} us, {flops / mean / 1e12:.0f} TFLOP/s, "
             f"{nbytes / mean / 1e9:.0f} GB/s")
+        if M == 1024:
+            # the same product through the vendor GEMM (hipBLASLt via torch), logits
+            # stored and no epilogue: a reference for the MFMA rate on this part
+            y = torch.empty(M, 152064, device="cuda", dtype=T)
+            tb = time_call(lambda: torch.matmul(h, Wlm.t(), out=y), reps)
+            out["vendor_gemm_7B_M1024"] = {
+                **tb.record(), "what": "torch.matmul(h [1024, 3584], Wlm^T) bf16 -> [1024, 152064] bf16 "
+                                      "(hipBLASLt), the batched LM head's product without its epilogue",
+                "TFLOP/s": flops / tb.mean / 1e12, "frac_mfma": flops / tb.mean / 1e12 / BF16_PEAK_TFLOPS}
+            log(f"[bench] vendor GEMM M={M}: {tb.mean * 1e6:.1f} us, {flops / tb.mean / 1e12:.0f} TFLOP/s")
+            del y
     # ---- the refinement step's call: the 64-row LM head fused with the
     # threshold unmask (8 sequences x window of 8); the window's mask bits are
     # restored before every call (one 64-byte device copy, timed with it), or
@@ -661,9 +733,10 @@ def extras_lm(w3, reps):
     def fused():
         bits.copy_(bits0)
         ops.bd_lmhead_unmask(h, ridx, Wlm, am, cf, tok, bits, win_lo=8, threshold=0.9, mask_bits_host=host)
-    med, mean = time_call(fused, reps)
+    t = time_call(fused, reps)
+    mean = t.mean
     nbytes = 152064 * 3584 * 2 + 64 * 3584 * 2 + 16 * 64
-    out["lmhead_unmask_7B_B8_S8"] = {"us_with_bits_reset": mean * 1e6, "GB/s": nbytes / mean / 1e9,
+    out["lmhead_unmask_7B_B8_S8"] = {"us_with_bits_reset": mean * 1e6, **t.record(), "GB/s": nbytes / mean / 1e9,
                                      "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
     log(f"[bench] lm head + unmask B=8 S=8: {mean * 1e6:.1f} us with the bits reset, {nbytes / mean / 1e9:.0f} GB/s")
     del Wlm
@@ -673,9 +746,10 @@ def extras_lm(w3, reps):
     h = torch.randn(8, c2.hidden, device="cuda", dtype=T) * 0.05
     am = torch.empty(8, dtype=torch.int32, device="cuda")
     cf = torch.empty(8, dtype=torch.float32, device="cuda")
-    med, mean = time_call(lambda: ops.bd_lmhead_confidence(h, None, W2, am, cf), reps)
+    t = time_call(lambda: ops.bd_lmhead_confidence(h, None, W2, am, cf), reps)
+    mean = t.mean
     nbytes = c2.V * c2.hidden * 2 + 8 * c2.hidden * 2 + 16 * 8
-    out["lmhead_1.5B_M8"] = {"us": mean * 1e6, "GB/s": nbytes / mean / 1e9,
+    out["lmhead_1.5B_M8"] = {**t.record(), "GB/s": nbytes / mean / 1e9,
                              "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
     log(f"[bench] lm head 1.5B M=8: {mean * 1e6:.1f} us, {nbytes / mean / 1e9:.0f} GB/s")
     return out
@@ -732,11 +806,12 @@ def main():
     ap.add_argument("--e2e-blocks", type=int, default=None,
                     help="blocks generated by the end-to-end decode measurement (default: the workload's 16)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/lmhead_7B_M64_traffic.json from two rocprofv3 --pmc counter files of "
-                         "`--section lm` (FETCH_SIZE, WRITE_SIZE) and exit")
+                    help="write the traffic record of --traffic-kind (profiles/*_traffic.json) from two rocprofv3 "
+                         "--pmc counter files of its section (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--traffic-kind", choices=sorted(TRAFFIC), default="lm")
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_from(*args.traffic_from)
+        traffic_from(args.traffic_kind, *args.traffic_from)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this implementation runs on a "
@@ -799,12 +874,7 @@ def main():
     lm_bytes = cfg.V * cfg.hidden * 2 + M * cfg.hidden * 2 + 16 * M
     lm_mean = float(lm_t.mean())
     achieved = lm_bytes / lm_mean / 1e9
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "lmhead_7B_M64_traffic.json")
-    if os.path.exists(tpath):
-        rec = json.load(open(tpath))
-        if rec.get("kernel_source_hash") == kernel_source_hash():
-            traffic = rec.get("bytes_per_launch")
+    traffic = stored_traffic("lm")
     # lockstep against a per-sequence window progression over the blocks the
     # loop finished (warm-up and timed): steps the batch took vs the most steps
     # any one sequence needed on its own schedule (what per-sequence progression
