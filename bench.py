@@ -715,7 +715,19 @@ def extras_lm(w3, reps):
                                       "(hipBLASLt), the batched LM head's product without its epilogue",
                 "TFLOP/s": flops / tb.mean / 1e12, "frac_mfma": flops / tb.mean / 1e12 / BF16_PEAK_TFLOPS}
             log(f"[bench] vendor GEMM M={M}: {tb.mean * 1e6:.1f} us, {flops / tb.mean / 1e12:.0f} TFLOP/s")
-            del y
+            # both on all-zero operands: the same instructions and memory traffic,
+            # far less switching activity in the matrix units
+            hz, Wz = torch.zeros_like(h), torch.zeros_like(Wlm)
+            tz = time_call(lambda: ops.bd_lmhead_confidence(hz, None, Wz, am, cf), reps)
+            tzb = time_call(lambda: torch.matmul(hz, Wz.t(), out=y), reps)
+            out["lmhead_7B_M1024_zero_operands"] = {
+                **tz.record(), "TFLOP/s": flops / tz.mean / 1e12, "frac_mfma": flops / tz.mean / 1e12 / BF16_PEAK_TFLOPS,
+                "vendor_us": tzb.mean * 1e6,
+                "vendor_TFLOP/s": flops / tzb.mean / 1e12,
+                "what": "the 1024-row LM head and the vendor GEMM on all-zero h and W (same work, same bytes)"}
+            log(f"[bench] zero operands M={M}: lm head {tz.mean * 1e6:.1f} us ({flops / tz.mean / 1e12:.0f} TFLOP/s), "
+                f"vendor GEMM {tzb.mean * 1e6:.1f} us ({flops / tzb.mean / 1e12:.0f} TFLOP/s)")
+            del y, hz, Wz
     # ---- the refinement step's call: the 64-row LM head fused with the
     # threshold unmask (8 sequences x window of 8); the window's mask bits are
     # restored before every call (one 64-byte device copy, timed with it), or

@@ -4,7 +4,8 @@
 
 Every .hip file under csrc/ is compiled for gfx950 into _build/, then linked
 into block_diffusion_decoding_amd/libbd.so.  Packed fp32 instructions are
-disabled for every file (-packed-fp32-ops).
+disabled for every file (-packed-fp32-ops).  BD_DEFINES (environment) adds
+-D options that override the kernels' tuning constants.
 """
 from __future__ import annotations
 
@@ -23,6 +24,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]
+# tuning constants of the kernels (e.g. "-DBD_LM_WIDE_PF=3"); only -D options are taken
+FLAGS += [f for f in os.environ.get("BD_DEFINES", "").split() if f.startswith("-D")]
 
 
 def _run(cmd):

@@ -106,9 +106,11 @@ LM_CASES = {
     "bf16-7B-M17-sharp": ("bf16", 17, 20, 3584, 152064, 1.0, 60.0, False),
     "bf16-7B-M100": ("bf16", 100, 128, 3584, 152064, 1.0, 1.0, False),
     "bf16-ragged-vocab": ("bf16", 33, 40, 512, 1000, 1.0, 30.0, True),
-    # more than 64 rows: 256 x 256 tiles; two row blocks, the second ragged,
-    # and a ragged last vocabulary block
+    # more than 256 rows: 256 x 256 tiles; two row blocks, the second ragged
+    # (by one row in -257), and a ragged last vocabulary block
     "bf16-big-ragged": ("bf16", 300, 310, 512, 5000, 1.0, 30.0, True),
+    "bf16-big-257": ("bf16", 257, 260, 768, 7001, 1.0, 30.0, True),
+    "bf16-big-600": ("bf16", 600, 640, 1536, 20000, 1.0, 30.0, False),
     # 65..256 rows: 256 x 128 tiles, ragged rows and vocabulary
     "bf16-big-narrow-ragged": ("bf16", 200, 230, 512, 5000, 1.0, 30.0, True),
 }
@@ -134,7 +136,7 @@ def test_lmhead_confidence(name):
     say(f"    exempt argmax rows: {ex}")
 
 
-@pytest.mark.parametrize("M", [4, 80])
+@pytest.mark.parametrize("M", [4, 80, 300])
 def test_lmhead_invalid_row_index(M):
     V, hidden = 512, 256
     say(f"[lmhead] invalid row index M={M}")
