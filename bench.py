@@ -241,19 +241,21 @@ class Loop:
         self.first = True
         if self.s == self.cfg.D // self.cfg.S:
             self.dec.commit()
-            self.commits += 1
-            self.done_blocks.append((self.block_steps, int(self.own.max())))
-            self.own[:] = 0
-            self.block_steps = 0
-            self._new_block()
+            self._block_done()
 
-    def window(self) -> int:
-        """The current window's first steps (from its exact step on) as one
-        captured graph of slots(S) step slots and one wait; returns the
-        refinement steps they took (the slots before which a masked position
-        of the window was left)."""
-        assert self.first
-        ring = self.dec.run_window(self.s, self.cfg.S, self.cfg.tau)
+    def _block_done(self):
+        """Book a committed block and set up the next one."""
+        self.first = True
+        self.commits += 1
+        self.done_blocks.append((self.block_steps, int(self.own.max())))
+        self.own[:] = 0
+        self.block_steps = 0
+        self._new_block()
+
+    def _account(self, ring) -> int:
+        """Book the slots of the current window's graph run (mask bits after
+        each slot, [slots, B]); returns the refinement steps among them (the
+        slots before which a masked position of the window was left)."""
         wm = self.wmask[self.s]
         before = np.concatenate([self.bits[None], ring[:-1]])
         had = (before & wm) != 0                     # [slots, B]
@@ -263,19 +265,56 @@ class Loop:
         self.tokens += int(np.bitwise_count(self.bits ^ ring[-1]).sum())
         self.bits = ring[-1]
         self.steps += steps
+        return steps
+
+    def window(self) -> int:
+        """The current window's first steps (from its exact step on) as one
+        captured graph of slots(S) step slots and one wait; returns the
+        refinement steps they took."""
+        assert self.first
+        steps = self._account(self.dec.run_window(self.s, self.cfg.S, self.cfg.tau))
         self.first = False
-        if not (self.bits & wm).any():
+        if not (self.bits & self.wmask[self.s]).any():
             self._next_window()
+        return steps
+
+    def windows(self, budget: int) -> int:
+        """Whole windows from the current one to at most the end of the
+        block, as many as `budget` steps surely cover, launched back to back
+        as captured graphs (and the commit when the block ends) with one wait
+        after the last: a window's S slots always finish it, so no launch
+        waits for the previous window's result.  Returns the steps taken."""
+        assert self.first
+        cfg, dec = self.cfg, self.dec
+        nw = cfg.D // cfg.S
+        first = self.s
+        last = min(nw, first + budget // cfg.S)
+        for s in range(first, last):
+            dec.run_window(s, cfg.S, cfg.tau, wait=False)
+        if last == nw:
+            dec.commit()
+        dec.wait()
+        steps = 0
+        for s in range(first, last):
+            self.s = s
+            steps += self._account(dec.window_bits(s, cfg.S))
+            assert not (self.bits & self.wmask[s]).any()
+        self.s = last
+        if last == nw:
+            self._block_done()
         return steps
 
     def run(self, n: int, windows: bool):
         """Exactly n refinement steps: window graphs while at least a graph's
-        slots remain, single steps otherwise."""
+        slots remain (whole windows back to back when their slots always
+        finish them), single steps otherwise."""
         left = n
-        slots = self.dec.slots(self.cfg.S)
+        S = self.cfg.S
+        slots = self.dec.slots(S)
+        piped = self.dec.windows_complete(S)
         while left > 0:
             if windows and self.first and left >= slots:
-                left -= self.window()
+                left -= self.windows(left) if piped else self.window()
             else:
                 self.step()
                 left -= 1
@@ -477,6 +516,104 @@ def extras_subblock(w3, graphs, steps=40, warmup=10):
     return {"subblock_sweep_7B": out}
 
 
+def timed_loop(dec, cfg, plants, graphs, steps, warmup):
+    """Steps/s and tokens/s of the lockstep loop over `plants` after `warmup`
+    steps (window graphs replayed when `graphs`)."""
+    loop = Loop(dec, cfg, plants)
+    loop.run(warmup, graphs)
+    torch.cuda.synchronize()
+    s0, t0_tok, c0 = loop.steps, loop.tokens, loop.commits
+    t0 = time.perf_counter()
+    loop.run(steps, graphs)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    n, tok = loop.steps - s0, loop.tokens - t0_tok
+    return {"steps": n, "steps_per_s": n / el, "tokens_per_s": tok / el, "tokens_per_step": tok / n,
+            "ms_per_step": el / n * 1e3, "commits": loop.commits - c0}
+
+
+def step_floor_bytes(cfg, kv_len) -> int:
+    """Bytes a DualCache step must read once: LM head and projection weights
+    and the batch's committed plus in-block K/V."""
+    attn = int(sum((int(L) + cfg.D) * 2 * cfg.Hkv * cfg.d * 2 for L in kv_len))
+    proj = (cfg.Hq * cfg.d + 2 * cfg.Hkv * cfg.d) * cfg.hidden * 2 + cfg.hidden * cfg.Hq * cfg.d * 2
+    return cfg.V * cfg.hidden * 2 + proj + attn
+
+
+def extras_rates(w3, graphs, rates=(0.0, 0.25, 0.5, 0.75, 1.0), steps=40, warmup=10):
+    """The headline loop at planted pass rates 0 .. 1 of the masked rows: the
+    threshold rule trades steps for tokens ("Fast-dLLM v2" notes, key findings
+    on the threshold); at rate 0 every step unmasks only the fallback token."""
+    cfg = bi.C3
+    pre = bi.make_prefix(cfg, 0)
+    dec = make_decoder(cfg, w3, pre)
+    if graphs:
+        dec.capture(cfg.S, cfg.tau)
+    out = {}
+    for r in rates:
+        plants = block_plants(cfg, w3, r, 0, 8)
+        rec = timed_loop(dec, cfg, plants, graphs, steps, warmup)
+        dec.set_synthetic_prefix(pre.kv_len, pre.cache_k, pre.cache_v, pre.carry)   # same context for every rate
+        log(f"[bench] pass rate {r}: {rec['steps_per_s']:.1f} steps/s, {rec['tokens_per_s']:.0f} tokens/s "
+            f"({rec['tokens_per_step']:.2f} tokens per step)")
+        out[f"r{r}"] = rec
+        del plants
+    del dec
+    torch.cuda.empty_cache()
+    return {"pass_rate_sweep_7B": out}
+
+
+def extras_step_small(graphs, steps=60, warmup=10):
+    """Whole refinement steps at the 1.5B shape (batch 1, one attention layer
+    and the 1536 x 151936 LM head, prefix 2048, planted pass rate 0.5)."""
+    cfg = bi.C2
+    w2 = bi.make_weights(cfg, 0)
+    pre = bi.make_prefix(cfg, 0)
+    dec = make_decoder(cfg, w2, pre)
+    if graphs:
+        dec.capture(cfg.S, cfg.tau)
+    rec = timed_loop(dec, cfg, block_plants(cfg, w2, 0.5, 0, 8), graphs, steps, warmup)
+    fb = step_floor_bytes(cfg, pre.kv_len)
+    rec.update({"bytes_per_dualcache_step": fb, "floor_us_at_peak": fb / (HBM_PEAK_GBS * 1e9) * 1e6,
+                "frac_of_floor": fb / (HBM_PEAK_GBS * 1e9) / (rec["ms_per_step"] * 1e-3)})
+    log(f"[bench] 1.5B-shape step loop: {rec['steps_per_s']:.1f} steps/s, {rec['tokens_per_s']:.0f} tokens/s, "
+        f"{rec['ms_per_step'] * 1e3:.1f} us/step")
+    del dec
+    torch.cuda.empty_cache()
+    return {"step_1.5B": rec}
+
+
+def oracle_one_thread(n_steps=3):
+    """The fp64 oracle on one host thread: DualCache steps (window 1) of the
+    tiny fp32 workload and of the 1.5B-shape workload."""
+    from threadpoolctl import threadpool_limits
+    from oracle import refine as R
+    out = {}
+    for cfg in (bi.C1, bi.C2):
+        w = bi.make_weights(cfg, 0)
+        pre = bi.make_prefix(cfg, 0)
+        st = bi.make_block_state(cfg, 0, 1)
+        plant, carry_plant, _ = bi.make_plants(cfg, 0, w, st, 0.5)
+        with threadpool_limits(limits=1):
+            m = R.Model.from_weights(w, cfg)
+            seqs = R.seqs_from_inputs(m, cfg, pre, st, plant, carry_plant)
+            for q in seqs:
+                R.e_step(m, q, 1, cfg.S, cfg.tau, cfg.D)
+            times = []
+            for _ in range(n_steps if cfg is bi.C2 else 10 * n_steps):
+                for q, b in zip(seqs, range(cfg.B)):
+                    q.tokens = st.tokens[b].astype(np.int64).copy()
+                    q.masked = st.masked[b].copy()
+                t0 = time.perf_counter()
+                for q in seqs:
+                    R.dc_step(m, q, 1, cfg.S, cfg.tau, cfg.D)
+                times.append(time.perf_counter() - t0)
+        sec = float(np.median(times))
+        out[cfg.name] = {"steps_per_s": 1.0 / sec, "s_per_step_median": sec, "threads": 1, "steps": len(times)}
+        log(f"[bench] oracle, one thread, {cfg.name}: {sec * 1e3:.1f} ms per DualCache step")
+    return {"oracle_one_thread": out}
+
+
 def extras_persequence(w3, n_blocks=4):
     """The headline workload (7B shape, planted pass rate 0.5) decoded block by
     block with per-sequence window progression (one captured mixed step per
@@ -512,7 +649,10 @@ def extras_persequence(w3, n_blocks=4):
 
     def advance():
         if loop.first:
-            loop.window()
+            if dec.windows_complete(cfg.S):
+                loop.windows(cfg.D)
+            else:
+                loop.window()
         else:
             loop.step()
     while loop.blk < 1:                           # warm-up block
@@ -577,7 +717,8 @@ def extras_v1():
     return {"v1_full_attention_1.5B_layer": out}
 
 
-def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "persequence", "v1"), graphs=True,
+def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "rates", "small", "persequence", "v1"),
+           graphs=True,
            e2e_blocks=None):
     """Attention and LM head alone at the long-context / batched shapes, the
     long-context block loop and the end-to-end multi-layer decode."""
@@ -597,6 +738,10 @@ def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "p
         out.update(extras_train(reps))
     if "subblock" in parts:
         out.update(extras_subblock(w3, graphs))
+    if "rates" in parts:
+        out.update(extras_rates(w3, graphs))
+    if "small" in parts:
+        out.update(extras_step_small(graphs))
     if "persequence" in parts:
         out.update(extras_persequence(w3))
     if "v1" in parts:
@@ -812,9 +957,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=32,
                     help="DualCache steps of the oracle timed for cpu_baseline (about 10 s of host work)")
-    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "persequence", "v1"),
-                    default="all", help="attn/long/lm/e2e/train/subblock/persequence/v1: run only that measurement (for profiling) and print "
-                         "its JSON instead of the bench line")
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "rates", "small",
+                                          "persequence", "v1", "oracle1"),
+                    default="all", help="run only that measurement (for profiling) and print its JSON instead of the "
+                                        "bench line (oracle1: the one-thread oracle, no GPU)")
     ap.add_argument("--e2e-blocks", type=int, default=None,
                     help="blocks generated by the end-to-end decode measurement (default: the workload's 16)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -824,6 +970,9 @@ def main():
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_kind, *args.traffic_from)
+        return
+    if args.section == "oracle1":
+        print(json.dumps(oracle_one_thread()), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this implementation runs on a "
@@ -836,7 +985,7 @@ def main():
     pkg.load_library()
 
     cfg = bi.C3
-    if args.section in ("e2e", "train", "v1"):
+    if args.section in ("e2e", "train", "v1", "small"):
         print(json.dumps(extras(None, args.reps, parts=(args.section,), graphs=not args.no_graphs,
                                 e2e_blocks=args.e2e_blocks)), flush=True)
         return
@@ -897,9 +1046,7 @@ def main():
                    "saving_bound": round(1 - own / lock, 4) if lock else None}
     # the whole DualCache step against HBM: every byte it must read once (LM head and projection
     # weights, the committed K/V of the batch at the loop's starting lengths plus the in-block rows)
-    attn_bytes = int(sum((int(L) + cfg.D) * 2 * cfg.Hkv * cfg.d * 2 for L in pre.kv_len))
-    proj_bytes = (cfg.Hq * cfg.d + 2 * cfg.Hkv * cfg.d) * cfg.hidden * 2 + cfg.hidden * cfg.Hq * cfg.d * 2
-    step_bytes = cfg.V * cfg.hidden * 2 + proj_bytes + attn_bytes
+    step_bytes = step_floor_bytes(cfg, pre.kv_len)
     floor_us = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
     step_roofline = {"bound": "hbm", "bytes_per_dualcache_step": step_bytes, "floor_us_at_peak": round(floor_us, 1),
                      "us_per_step": round(elapsed / steps * 1e6, 1),
@@ -926,6 +1073,7 @@ def main():
         log("[bench] cpu baseline (fp64 oracle)")
         cpu = cpu_baseline(cfg, w, pre, args.rate, args.cpu_steps)
         log(f"[bench] oracle: {cpu['value']:.3f} steps/s on {cpu['cores']} cores")
+        cpu.update(oracle_one_thread())
     line = {
         "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / steps * 1e3, 4),

@@ -103,7 +103,7 @@ class BlockDecoder:
         self._capturing = False
         self.graphs = {}        # (kind, s) -> captured HIP graph of that step ("W": whole window)
         self._held_ws = {}      # tag -> workspace the captured graphs point into
-        self._rings = {}        # S -> [S, B] pinned: mask bits after each step slot of a window
+        self._rings = {}        # S -> [D // S, slots(S), B] pinned: mask bits after each step slot of each window
 
     # ------------------------------------------------------------------ state
     def set_synthetic_prefix(self, kv_len, cache_k, cache_v, carry):
@@ -123,8 +123,10 @@ class BlockDecoder:
         bits = np.zeros(self.dims.B, dtype=np.uint64)
         for j in range(D):
             bits |= m[:, j].astype(np.uint64) << np.uint64(j)
-        self.tokens.copy_(torch.from_numpy(t).to(self.device))
-        self.mask_bits.copy_(torch.from_numpy(bits.view(np.int64)).to(self.device))
+        # pinned copies queued on the stream: no wait for the queued steps
+        # (the pinned blocks are not reused before their copies have run)
+        self.tokens.copy_(torch.from_numpy(t).pin_memory(), non_blocking=True)
+        self.mask_bits.copy_(torch.from_numpy(bits.view(np.int64)).pin_memory(), non_blocking=True)
         self._bits_fresh = False
 
     def set_block(self, tokens, masked, plant=None, carry_offset=None):
@@ -358,7 +360,7 @@ class BlockDecoder:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
                     for i in range(self.slots(S)):
-                        (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[i])
+                        (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[s, i])
                 self.graphs[("W", s)] = g
         finally:
             self._capturing = False
@@ -402,20 +404,32 @@ class BlockDecoder:
         return True
 
     def _ring(self, S: int):
-        """Pinned [slots(S), B] mask-bit ring of windows of S positions (kept
-        for the decoder's lifetime: captured window graphs write into it)."""
+        """Pinned [D // S, slots(S), B] mask-bit rings of the windows of S
+        positions (kept for the decoder's lifetime: captured window graphs
+        write into them), one ring per window so that the windows of a block
+        can run back to back before the host reads any of them."""
         r = self._rings.get(S)
         if r is None:
-            r = self._rings[S] = torch.zeros(self.slots(S), self.dims.B, dtype=torch.int64, pin_memory=True)
+            r = self._rings[S] = torch.zeros(self.dims.D // S, self.slots(S), self.dims.B, dtype=torch.int64,
+                                             pin_memory=True)
         return r
 
-    def run_window(self, s: int, S: int, tau) -> np.ndarray:
+    def windows_complete(self, S: int) -> bool:
+        """Whether a window's slots always finish it: every step unmasks at
+        least one masked position of the window in each sequence that has one
+        (the fallback of the threshold rule), so S steps always do."""
+        return self.slots(S) >= S
+
+    def run_window(self, s: int, S: int, tau, wait: bool = True):
         """Window s from its exact step on: slots(S) step slots (one graph
         replay when captured), then one wait.  Returns the mask bits after
         every slot [slots(S), B] (uint64); slot i was a refinement step iff some
         sequence still had a masked position of the window before it.  When
         slots(S) < S the window may still have masked positions afterwards:
-        its next steps are DualCache steps."""
+        its next steps are DualCache steps.  wait=False only queues the
+        window and returns None: window_bits(s, S) reads its ring after a
+        later wait (windows_complete(S) makes the next window's launch valid
+        without looking)."""
         g = self.graphs.get(("W", s))
         ring = self._ring(S)
         if g is not None and self._replay_ok(S, tau):
@@ -423,13 +437,46 @@ class BlockDecoder:
             self.last = self._window(s, S)
         else:
             for i in range(self.slots(S)):
-                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[i])
+                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[s, i])
         self._bits_ev.record()
-        self._bits_ev.synchronize()
         self._bits_fresh = False
-        return ring.numpy().view(np.uint64).copy()
+        if not wait:
+            return None
+        self._bits_ev.synchronize()
+        return self.window_bits(s, S)
+
+    def wait(self):
+        """Wait for the queued steps (their mask bits are then on the host)."""
+        self._bits_ev.synchronize()
+
+    def window_bits(self, s: int, S: int) -> np.ndarray:
+        """Mask bits after every slot of window s's last run [slots(S), B]
+        (uint64); valid once that run has finished (run_window or wait)."""
+        return self._ring(S)[s].numpy().view(np.uint64).copy()
 
     # ------------------------------------------------------------------ loop
+    def decode_block_windows(self, S: int, tau) -> int:
+        """Decode the current block as its captured window graphs launched
+        back to back, then commit, with one wait at the end (needs capture(S,
+        tau) and windows_complete(S)).  Returns the refinement steps taken:
+        the slots before which some sequence had a masked position of the
+        window."""
+        assert self.windows_complete(S) and self._replay_ok(S, tau) and ("W", 0) in self.graphs
+        bits = self.mask_bits_host()
+        n_win = self.dims.D // S
+        for s in range(n_win):
+            self.run_window(s, S, tau, wait=False)
+        self.commit()
+        self.wait()
+        n = 0
+        for s in range(n_win):
+            ring = self.window_bits(s, S)
+            wm = np.uint64(((1 << S) - 1) << (s * S))
+            before = np.concatenate([bits[None], ring[:-1]])
+            n += int(((before & wm) != 0).any(axis=1).sum())
+            bits = ring[-1]
+        return n
+
     def decode_block(self, S: int, tau: float, mode: str = "dual", steps_per_window: int | None = None,
                      on_step=None):
         """Decode the current block window by window (lockstep over the batch),

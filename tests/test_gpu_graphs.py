@@ -177,3 +177,35 @@ def test_window_graphs_follow_a_device_threshold_schedule():
             (eager.e_step if i == 0 else eager.dc_step)(s, S, tau_e, eager=True)
             assert np.array_equal(ring[i], eager.mask_bits_host()), f"window {s} slot {i}"
         assert torch.equal(eager.tokens, graph.tokens)
+
+
+@pytest.mark.parametrize("compact,S,tau", [(None, 8, 0.6), (True, 8, 0.6), (None, 4, 1.0)])
+def test_block_windows_back_to_back_decode_like_single_steps(compact, S, tau):
+    """A block decoded as its window graphs launched back to back with one
+    wait at the end (decode_block_windows) against the eager block loop that
+    waits for the mask bits after every step: the same steps, tokens,
+    committed cache and carry, over two blocks.  tau = 1.0: about one token
+    per sequence and step, so the windows use most of their S slots."""
+    say(f"[graphs] back-to-back window graphs vs eager block loop (compact={compact}, S={S}, tau={tau})")
+    cfg = replace(MID, S=S)
+    w, pre, st, _, _ = workload(cfg, 0, all_masked=True, plant_rate=None)
+    eager = gpu_decoder(cfg, w, pre, st, compact=compact)
+    graph = gpu_decoder(cfg, w, pre, st, compact=compact)
+    graph.capture(S, tau)
+    assert graph.windows_complete(S)
+    rng = np.random.default_rng(8)
+    for blk in range(2):
+        plant = bi.normal(20 + blk, "plant", (cfg.B, cfg.D, cfg.hidden), 0.5, "bf16")
+        plant[rng.random((cfg.B, cfg.D)) < 0.5] = 0.0
+        for d in (eager, graph):
+            d.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plant)
+        tok_before = eager.tokens.clone()
+        n_e = eager.decode_block(S, tau)
+        n_g = graph.decode_block_windows(S, tau)
+        torch.cuda.synchronize()
+        assert n_e == n_g, f"block {blk}: {n_e} eager steps, {n_g} in the window graphs"
+        assert cfg.D // S <= n_g <= cfg.D
+        assert torch.equal(eager.tokens, graph.tokens) and not torch.equal(tok_before, graph.tokens)
+        assert int(graph.mask_bits_host().max()) == 0
+        assert torch.equal(eager.cache_k, graph.cache_k) and torch.equal(eager.cache_v, graph.cache_v)
+        assert torch.equal(eager.kv_len, graph.kv_len) and torch.equal(eager.H[:, 0], graph.H[:, 0])
