@@ -49,6 +49,11 @@ constexpr int kThreads = 256;  // merge and fp32 kernels
 #ifndef BD_ATTN_MIN_CHUNK
 #define BD_ATTN_MIN_CHUNK 256
 #endif
+// committed K/V of a call larger than this stream through with the
+// non-temporal hint (they cannot stay cached until the next step anyway)
+#ifndef BD_ATTN_NT_MIN_BYTES
+#define BD_ATTN_NT_MIN_BYTES (256ll << 20)
+#endif
 #ifndef BD_ATTN_QPW_MAX
 #define BD_ATTN_QPW_MAX 2
 #endif
@@ -202,7 +207,7 @@ __device__ __forceinline__ void wait_stages(int later) {
 // global_load_lds_dwordx4: instruction i of a tile writes 64 consecutive
 // 16-byte slots, and each lane's global address is chosen so that its slot
 // receives the right chunk.
-template <int DH, int KT, int QPW, int NS>
+template <int DH, int KT, int QPW, int NS, int CAUX>
 __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_kernel(AttnK a) {
   constexpr int KCH = DH / 8;             // 16-byte chunks per key row
   constexpr int TU4 = KT * KCH;           // 16-byte slots per K (or V) tile
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_ke
         const uint16_t* base = (ins >= NI ? vc_bh : kc_bh) + (size_t)kbase * DH;
         __builtin_amdgcn_global_load_lds((glb_void_t*)(base + loff[u]),
                                          (lds_void_t*)(st + (ins >= NI ? TU4 : 0) + (ins >= NI ? ins - NI : ins) * 64),
-                                         16, 0, 0);
+                                         16, 0, CAUX);
       }
     } else {
 #pragma unroll
@@ -702,6 +707,7 @@ BdAttnPlan bd_attn_plan(bd_dtype dt, int B, int Hq, int Hkv, int d, int n_q, int
   p.qpw = p.qpw > kQpwMax ? kQpwMax : p.qpw;
   p.nqg = (p.QT + kWaves * p.qpw - 1) / (kWaves * p.qpw);
   const int tmax = cap + n_blk;
+  p.stream_nt = (long long)B * Hkv * cap * d * 2 * (dt == BD_F32 ? 4 : 2) >= BD_ATTN_NT_MIN_BYTES;
   if (dt == BD_F32) {
     p.chunk = tmax;
     p.nchunks = 1;
@@ -750,8 +756,13 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
   a.n_units = x.B * x.Hkv * p.nchunks;
   a.scale_log2 = x.scale * BD_LOG2E;
   const int n_wg = kXcd * a.nqg * ((a.n_units + kXcd - 1) / kXcd);
-#define BD_ATTN_LAUNCH(DH, QPW) \
-  hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS>), dim3(n_wg), dim3(kAttnThreads), 0, s, a)
+#define BD_ATTN_LAUNCH(DH, QPW)                                                                           \
+  do {                                                                                                    \
+    if (p.stream_nt)                                                                                      \
+      hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS, 2>), dim3(n_wg), dim3(kAttnThreads), 0, s, a); \
+    else                                                                                                  \
+      hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS, 0>), dim3(n_wg), dim3(kAttnThreads), 0, s, a); \
+  } while (0)
   if (x.d == 128) {
     if (p.qpw == 1) BD_ATTN_LAUNCH(128, 1);
 #if BD_ATTN_QPW_MAX >= 2

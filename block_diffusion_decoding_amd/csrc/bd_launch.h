@@ -25,6 +25,7 @@ struct BdAttnPlan {
   int nqg;        // query-tile groups (work items along the query rows)
   int chunk;      // keys per work item
   int nchunks;    // key chunks (max over sequences)
+  int stream_nt;  // committed K/V loaded with the non-temporal hint (bf16)
   size_t part_o;  // workspace offsets / sizes in bytes
   size_t part_ml;
   size_t ws_bytes;
@@ -136,6 +137,8 @@ struct BdGemmPlan {
   int passes;             // passes per work-group
   int ksplit;             // K slices
   int big_ct;             // > 0: 256-row x (big_ct*16)-column tiles instead (large M)
+  int kw_nt;              // > 0: K split over the waves of a work-group, kw_nt tiles and kw_mt row tiles each
+  int kw_mt;
   size_t ws_bytes;        // workspace: fp32 partial sums [ksplit][M][T*16]
 };
 

@@ -55,10 +55,16 @@ constexpr int kLdsPerCU = 160 * 1024;
 #ifndef BD_GEMM_RED_NS
 #define BD_GEMM_RED_NS 2500
 #endif
+// 0: never split K over the waves of a work-group; 1: for projections whose
+// streaming plan needs a K-split reduction; 2: wherever it fits
+#ifndef BD_GEMM_KWAVE
+#define BD_GEMM_KWAVE 1
+#endif
 #ifndef BD_GEMM_PART_BPNS
 #define BD_GEMM_PART_BPNS 4000
 #endif
 constexpr int kNS = BD_GEMM_NS;  // pipeline stages
+constexpr int kXcdGemm = 8;      // work-groups are dispatched round-robin over 8 XCDs
 constexpr int kSliceBatch = 8;   // K slices whose partial sums a reduction thread loads at once
 constexpr int kMaxSeg = 3;
 
@@ -290,6 +296,169 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
       for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
     cch = 0;
     ++cp;
+  }
+}
+
+// Projections with few 16-column tiles (the fresh rows of a refinement step
+// against a 3584-wide weight, say): split over work-groups by K, they would
+// need a reduction launch after the GEMM.  Here the K range is split over the
+// four waves of a work-group instead.  Work-group (tile group, row block)
+// owns NT consecutive tiles (in SwiGLU mode NT = 2: a gate and its up tile)
+// and 16*MT rows; wave w walks the 64-wide K chunks [w*nch/4, (w+1)*nch/4)
+// through a ring of NS stages of its own (stage: the NT W tiles, then the MT
+// X tiles, 2 KiB each, loaded by global->LDS DMA in whole 128-byte lines,
+// XOR-swizzled, as in stream_gemm.h), with no work-group barrier in the loop.
+// (W fragments loaded straight into registers, 16 rows x 64 bytes per
+// instruction, measured slower from HBM than these whole-line DMA tiles.)
+// The waves' accumulators then meet in LDS and are added in wave order, so
+// results do not depend on timing.  Grid: 8 x ceil(groups / 8) x ny
+// work-groups, the row blocks of one tile group consecutive on one XCD (they
+// read the same W tiles, the second time from L2).  One work-group per CU
+// (the rings take up to 144 KiB of LDS).
+template <int MT, int NT, int NS>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kwave_kernel(GemmS a, int ny) {
+  constexpr int FRW = 2 * (NT + MT);  // DMA instructions per stage (one wave's)
+  constexpr int STAGE_U4 = FRW * 64;
+  static_assert(NS >= 2 && (NS - 2) * FRW < 64 && NS <= 8, "stages");
+  static_assert(4 * MT * NT * 64 <= 4 * NS * STAGE_U4, "reduction area");
+  __shared__ uint4 sbuf[4 * NS * STAGE_U4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int xcd = blockIdx.x % kXcdGemm, t8 = blockIdx.x / kXcdGemm;
+  const int rb = t8 % ny;
+  const int tg = (t8 / ny) * kXcdGemm + xcd;
+  const int T = a.tb[a.nseg];
+  const int t0 = tg * NT;
+  if (t0 >= T) return;
+  const int n = T - t0 < NT ? T - t0 : NT;  // real tiles of this group
+  const int m0 = rb * MT * 16;
+  const int K = a.K, nchK = K / 64;
+  const int cb = wave * nchK / 4, nch = (wave + 1) * nchK / 4 - cb;
+  const bool swiglu = a.mode == BD_GEMM_SWIGLU;
+
+  // instruction f loads rows 8*(f%2)..+7 of stage tile f/2 (W tiles first);
+  // past the data: a valid X row whose products are discarded
+  const int lrow = lane >> 3, lkb = (lane & 7) ^ lrow;
+  const size_t koff = (size_t)cb * 64 + 8 * lkb;
+  const uint16_t* const dummy = a.x + (size_t)bd_map_row(a.xr, 0) * K + koff;
+  const uint16_t* src[FRW];
+#pragma unroll
+  for (int f = 0; f < FRW; ++f) {
+    const int t = f >> 1, r = 8 * (f & 1) + lrow;
+    const uint16_t* row = dummy;
+    if (t < NT) {
+      if (t < n) {
+        const int gt = t0 + t;
+        if (swiglu) {
+          int c = (gt >> 1) * 16 + r;
+          c = c < a.N[0] ? c : a.N[0] - 1;
+          row = a.w[0] + (size_t)((gt & 1) ? a.N[0] + c : c) * K + koff;
+        } else {
+          const int sg = seg_of(a, gt);
+          int c = (gt - a.tb[sg]) * 16 + r;
+          c = c < a.N[sg] ? c : a.N[sg] - 1;
+          row = a.w[sg] + (size_t)c * K + koff;
+        }
+      }
+    } else {
+      const int m = m0 + (t - NT) * 16 + r;
+      if (m < a.M) row = a.x + (size_t)bd_map_row(a.xr, m) * K + koff;
+    }
+    src[f] = row;
+  }
+  uint4* const ring = sbuf + wave * NS * STAGE_U4;
+  auto issue = [&](int c) {
+    uint4* st = ring + (c % NS) * STAGE_U4;
+#pragma unroll
+    for (int f = 0; f < FRW; ++f)
+      __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[f] + (size_t)c * 64),
+                                       (bd_stream::lds_void_t*)(st + f * 64), 16, 0, 0);
+  };
+  const int fo0 = bd_stream::frag_offset(lane, 0), fo1 = bd_stream::frag_offset(lane, 1);
+
+  bd_f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nch) issue(c);
+  for (int s = 0; s < nch; ++s) {
+    // stage s complete: at most `later` younger stages still in flight
+    const int later = min(nch - s - 1, NS - 2);
+    if (later <= 0) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(FRW));
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(NS > 3 ? 2 * FRW : 0));
+    else if (later == 3) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(NS > 4 ? 3 * FRW : 0));
+    else if (later == 4) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(NS > 5 ? 4 * FRW : 0));
+    else if (later == 5) __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(NS > 6 ? 5 * FRW : 0));
+    else __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(NS > 7 ? 6 * FRW : 0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (s + NS - 1 < nch) issue(s + NS - 1);  // into the slot read at s - 1 (its reads have completed)
+    const uint32_t sb = bd_stream::lds_addr(ring + (s % NS) * STAGE_U4);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t fo = ks == 0 ? fo0 : fo1;
+      uint4 xa[MT], wb[NT];
+      bd_stream::lds_frags_kstep<MT, NT>(sb + NT * 2048 + fo, sb + fo, xa, wb);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+    }
+  }
+
+  // ---- the waves' sums meet in LDS: red[w][i*NT + j][lane]
+  __syncthreads();
+  bd_f32x4* red = reinterpret_cast<bd_f32x4*>(sbuf);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) red[(wave * MT * NT + i * NT + j) * 64 + lane] = acc[i][j];
+  __syncthreads();
+  auto total = [&](int p) {  // tile pair p summed over the waves, in wave order
+    bd_f32x4 v = red[p * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[(w * MT * NT + p) * 64 + lane];
+    return v;
+  };
+  if (swiglu) {
+    // wave w: row tiles i = w, w + 4, ... of the (gate, up) pair
+    for (int i = wave; i < MT; i += 4) {
+      const int col = (t0 >> 1) * 16 + l16;
+      if (n < 2 || col >= a.N[0]) continue;
+      const bd_f32x4 zg = total(i * NT), u = total(i * NT + 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + i * 16 + 4 * g + r;
+        if (m < a.M)
+          a.y[0][(size_t)bd_map_row(a.yr[0], m) * a.N[0] + col] =
+              (uint16_t)bd_f2bf(zg[r] / (1.f + __expf(-zg[r])) * u[r]);
+      }
+    }
+    return;
+  }
+  for (int p = wave; p < MT * NT; p += 4) {
+    const int i = p / NT, j = p % NT;
+    if (j >= n) continue;
+    const int gt = t0 + j, sg = seg_of(a, gt);
+    const int col = (gt - a.tb[sg]) * 16 + l16;
+    if (col >= a.N[sg]) continue;
+    const bd_f32x4 v = total(p);
+    const uint16_t* res = a.res[sg];
+    float rv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + i * 16 + 4 * g + r;
+      rv[r] = (m < a.M && res) ? bd_bf2f(res[(size_t)bd_map_row(a.rr[sg], m) * a.N[sg] + col]) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + i * 16 + 4 * g + r;
+      if (m < a.M) a.y[sg][(size_t)bd_map_row(a.yr[sg], m) * a.N[sg] + col] = (uint16_t)bd_f2bf(v[r] + rv[r]);
+    }
   }
 }
 
@@ -843,12 +1012,29 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
     }
   }
   best.ws_bytes = best.ksplit > 1 ? (size_t)best.ksplit * M * T * 16 * sizeof(float) : 0;
+  // few tiles: K split over the waves of a work-group (no reduction launch),
+  // one work-group per CU
+  if (BD_GEMM_KWAVE > 0 && nch >= 4 && (BD_GEMM_KWAVE > 1 || best.ksplit > 1)) {
+    const int kmt = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+    const long kny = (M + kmt * 16 - 1) / (kmt * 16);
+    for (int nt = G; nt <= 2; nt += G) {
+      if ((long)(T + nt - 1) / nt * kny <= kCUs) {
+        best.kw_nt = nt;
+        best.kw_mt = kmt;
+        best.ny = (int)kny;
+        best.ksplit = 1;
+        best.ws_bytes = 0;
+        break;
+      }
+    }
+  }
   // large M: 256-row tiles when their blocks alone fill the GPU
   const int rbk = (M + kBigRows - 1) / kBigRows;
   for (int ct = 16; ct >= 8 && M >= kBigRows; ct /= 2) {
     const int cbk = (T + ct - 1) / ct;
     if ((long)rbk * cbk >= kCUs) {
       best.big_ct = ct;
+      best.kw_nt = 0;
       best.ksplit = 1;
       best.ws_bytes = 0;
       break;
@@ -908,7 +1094,23 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
       a.d = rope->d;
       a.log2_theta = std::log2((double)rope->theta);
     }
-    if (p.big_ct != 0) {  // 256-row tiles, no K split
+    if (p.kw_nt != 0) {  // K split over the waves
+      const int groups = (p.T + p.kw_nt - 1) / p.kw_nt;
+      const dim3 kgrid((unsigned)(kXcdGemm * ((groups + kXcdGemm - 1) / kXcdGemm) * p.ny));
+#define BD_KWAVE(MT, NT, NS) hipLaunchKernelGGL((gemm_kwave_kernel<MT, NT, NS>), kgrid, dim3(kThreads), 0, s, a, p.ny)
+      const int key = p.kw_mt * 10 + p.kw_nt;
+      switch (key) {  // stages: the four rings fill at most 144 KiB of LDS
+        case 11: BD_KWAVE(1, 1, 8); break;
+        case 12: BD_KWAVE(1, 2, 6); break;
+        case 21: BD_KWAVE(2, 1, 6); break;
+        case 22: BD_KWAVE(2, 2, 4); break;
+        case 41: BD_KWAVE(4, 1, 3); break;
+        default: BD_KWAVE(4, 2, 3); break;
+      }
+#undef BD_KWAVE
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else if (p.big_ct != 0) {  // 256-row tiles, no K split
       const int rbk = (M + kBigRows - 1) / kBigRows, cbk = (p.T + p.big_ct - 1) / p.big_ct;
       const int row_major = rbk * kBigRows > cbk * p.big_ct * 16 ? 1 : 0;  // more rows than weight columns
       const dim3 bgrid((unsigned)(row_major ? 8 * ((rbk + 7) / 8) * cbk : 8 * ((cbk + 7) / 8) * rbk));

@@ -44,6 +44,14 @@ constexpr int kThreads = 256;
 #ifndef BD_LM_STREAM_WGS
 #define BD_LM_STREAM_WGS 512
 #endif
+// Cache policy of the streaming kernel's W loads: 2 = non-temporal.  The
+// LM-head weights are read once per step and are far larger than the caches;
+// streamed with the non-temporal hint they run faster and leave the smaller
+// tensors of the step (projection weights, committed K/V) in the
+// memory-side cache for the next step.
+#ifndef BD_LM_AUX
+#define BD_LM_AUX 2
+#endif
 constexpr int kNTW = BD_LM_NTW;  // 16-column tiles per pass (bf16, up to 64 rows)
 constexpr int kNS = BD_LM_NS;    // pipeline stages (bf16)
 constexpr int kStreamWGs = BD_LM_STREAM_WGS;  // work-groups of the streaming kernel: two per CU
@@ -155,8 +163,14 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
   set_pass(0);
   auto issue_next = [&]() {
     uint4* st = sbuf + (iss % C::NS) * C::STAGE_U4;
+    // instructions i < kNTW/2 load W tiles (for every wave), the rest X rows
+    static_assert(kNTW % 2 == 0, "W instructions per wave");
 #pragma unroll
-    for (int i = 0; i < C::LW; ++i)
+    for (int i = 0; i < kNTW / 2; ++i)
+      __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ich * C::KC),
+                                       (bd_stream::lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, BD_LM_AUX);
+#pragma unroll
+    for (int i = kNTW / 2; i < C::LW; ++i)
       if (C::FR % 4 == 0 || wave + 4 * i < C::FR)
         __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ich * C::KC),
                                          (bd_stream::lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, 0);

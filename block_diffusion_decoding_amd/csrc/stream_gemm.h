@@ -183,6 +183,104 @@ __device__ __forceinline__ void lds_frags_kstep<1, 2>(uint32_t xa, uint32_t wa, 
   w[1] = as_uint4(r[2]);
 }
 
+template <>
+__device__ __forceinline__ void lds_frags_kstep<1, 1>(uint32_t xa, uint32_t wa, uint4 (&x)[1], uint4 (&w)[1]) {
+  u32x4_t r[2];
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(xa), "v"(wa)
+      : "memory");
+  x[0] = as_uint4(r[0]);
+  w[0] = as_uint4(r[1]);
+}
+
+template <>
+__device__ __forceinline__ void lds_frags_kstep<2, 1>(uint32_t xa, uint32_t wa, uint4 (&x)[2], uint4 (&w)[1]) {
+  u32x4_t r[3];
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %3 offset:2048\n\t"
+      "ds_read_b128 %2, %4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2])
+      : "v"(xa), "v"(wa)
+      : "memory");
+  x[0] = as_uint4(r[0]);
+  x[1] = as_uint4(r[1]);
+  w[0] = as_uint4(r[2]);
+}
+
+template <>
+__device__ __forceinline__ void lds_frags_kstep<4, 1>(uint32_t xa, uint32_t wa, uint4 (&x)[4], uint4 (&w)[1]) {
+  u32x4_t r[5];
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:2048\n\t"
+      "ds_read_b128 %2, %5 offset:4096\n\t"
+      "ds_read_b128 %3, %5 offset:6144\n\t"
+      "ds_read_b128 %4, %6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4])
+      : "v"(xa), "v"(wa)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = as_uint4(r[i]);
+  w[0] = as_uint4(r[4]);
+}
+
+template <>
+__device__ __forceinline__ void lds_frags_kstep<4, 2>(uint32_t xa, uint32_t wa, uint4 (&x)[4], uint4 (&w)[2]) {
+  u32x4_t r[6];
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:2048\n\t"
+      "ds_read_b128 %2, %6 offset:4096\n\t"
+      "ds_read_b128 %3, %6 offset:6144\n\t"
+      "ds_read_b128 %4, %7\n\t"
+      "ds_read_b128 %5, %7 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+      : "v"(xa), "v"(wa)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = as_uint4(r[i]);
+  w[0] = as_uint4(r[4]);
+  w[1] = as_uint4(r[5]);
+}
+
+// N fragments from a + 2048*i (consecutive 2 KiB tiles).
+template <int N>
+__device__ __forceinline__ void lds_frags(uint32_t a, uint4 (&x)[N]);
+
+template <>
+__device__ __forceinline__ void lds_frags<1>(uint32_t a, uint4 (&x)[1]) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(a) : "memory");
+  x[0] = as_uint4(r);
+}
+
+template <>
+__device__ __forceinline__ void lds_frags<2>(uint32_t a, uint4 (&x)[2]) {
+  u32x4_t r[2];
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %2 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(a)
+      : "memory");
+  x[0] = as_uint4(r[0]);
+  x[1] = as_uint4(r[1]);
+}
+
+template <>
+__device__ __forceinline__ void lds_frags<4>(uint32_t a, uint4 (&x)[4]) {
+  lds_frags_4<2048>(a, x);
+}
+
 // Byte offset, inside a 2 KiB tile, of lane `lane`'s fragment for k-step ks.
 __device__ __forceinline__ int frag_offset(int lane, int ks) {
   const int r = lane & 15, r7 = r & 7;

@@ -36,6 +36,11 @@ ATTN_CASES = {
     "bf16-d64": ("bf16", 2, 8, 2, 64, 32, 8, 8, [700, 1300], 32, 0.5, None),
     "bf16-7B-long-dc": ("bf16", 32, 28, 4, 128, 32, 8, 8, [16384] * 32, 32, 0.02, [0, 13, 31]),
     "bf16-7B-long-exact": ("bf16", 32, 28, 4, 128, 32, 32, 0, [16384] * 32, 32, 0.02, [5, 30]),
+    # long key streams of few (sequence, KV head) items: many key chunks per
+    # item; ragged lengths with 14 query tiles per item
+    "bf16-long-few-items": ("bf16", 2, 12, 2, 128, 32, 8, 8, [9000, 8300], 32, 0.02, None),
+    "bf16-long-ragged-exact": ("bf16", 16, 28, 4, 128, 32, 32, 0, [8300 - 41 * i for i in range(16)], 32, 0.02,
+                               [0, 6, 15]),
 }
 
 
@@ -444,11 +449,14 @@ def test_projection_workspace_shared_by_different_tilings():
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 1536, 1536), (32, 2048, 512), (50, 1536, 8960), (128, 1536, 8960),
+                                   (24, 640, 4352), (64, 3584, 3584), (200, 1536, 1536),
                                    (100, 17920, 256), (512, 8192, 512), (512, 1536, 1536), (16, 1000, 512),
                                    (1000, 8192, 512), (4096, 4096, 512)])
 def test_linear_in_place_residual_tilings(M, N, K):
     """y = x W^T + y in place through row maps, for row counts that take
-    every row tile (16 .. 128 rows, ragged tails) with and without a K split,
+    every row tile (16 .. 128 rows, ragged tails) with and without a K split
+    (over work-groups, or over the four waves of a work-group: 4352 = 4 x 17
+    chunks of 64),
     and the 256-row tiles of large M (1000 rows: 128-column tiles, ragged;
     4096 rows: 256-column tiles): the residual rows are read before the same
     rows are written."""
