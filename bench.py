@@ -193,16 +193,19 @@ class LaunchTimer:
 
 
 class Loop:
-    """Lockstep block decode, one refinement step per call of step()."""
+    """Lockstep block decode, one refinement step per call of step(), or
+    many steps per call of run()."""
 
     def __init__(self, dec, cfg, plants):
         self.dec, self.cfg, self.plants = dec, cfg, plants
         self.blk = -1
         self.s = 0
         self.first = True
+        self.slot = 0                    # next slot of the current window (run's queued path)
         self.steps = self.tokens = self.commits = 0
         self.bits = None
         self.wmask = [np.uint64(((1 << cfg.S) - 1) << (w * cfg.S)) for w in range(cfg.D // cfg.S)]
+        self.full = np.full(cfg.B, (1 << cfg.D) - 1, dtype=np.uint64)
         # steps each sequence needed on its own (it had a masked position of the
         # window before the step), per block: the schedule a per-sequence
         # window progression would follow (identical tokens, pinned in the oracle)
@@ -216,8 +219,8 @@ class Loop:
         self.blk += 1
         self.dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool),
                            self.plants[self.blk % len(self.plants)])
-        self.s, self.first = 0, True
-        self.bits = np.full(cfg.B, (1 << cfg.D) - 1, dtype=np.uint64)
+        self.s, self.first, self.slot = 0, True, 0
+        self.bits = self.full.copy()
 
     def step(self):
         cfg, dec = self.cfg, self.dec
@@ -233,37 +236,41 @@ class Loop:
         bits = dec.mask_bits_host()      # 8 bytes per sequence, refreshed by the step itself
         self.tokens += int(np.bitwise_count(self.bits ^ bits).sum())
         self.bits = bits
+        self.slot += 1
         if not (bits & self.wmask[self.s]).any():
             self._next_window()
 
     def _next_window(self):
         self.s += 1
         self.first = True
+        self.slot = 0
         if self.s == self.cfg.D // self.cfg.S:
             self.dec.commit()
             self._block_done()
 
-    def _block_done(self):
-        """Book a committed block and set up the next one."""
-        self.first = True
+    def _book_block(self):
+        """Book a committed block."""
         self.commits += 1
         self.done_blocks.append((self.block_steps, int(self.own.max())))
         self.own[:] = 0
         self.block_steps = 0
+
+    def _block_done(self):
+        """Book a committed block and set up the next one."""
+        self._book_block()
         self._new_block()
 
-    def _account(self, ring) -> int:
-        """Book the slots of the current window's graph run (mask bits after
-        each slot, [slots, B]); returns the refinement steps among them (the
+    def _account(self, ring, s, before) -> int:
+        """Book slots of window s (mask bits after each slot, [n, B], and the
+        bits before the first); returns the refinement steps among them (the
         slots before which a masked position of the window was left)."""
-        wm = self.wmask[self.s]
-        before = np.concatenate([self.bits[None], ring[:-1]])
-        had = (before & wm) != 0                     # [slots, B]
+        wm = self.wmask[s]
+        prev = np.concatenate([before[None], ring[:-1]])
+        had = (prev & wm) != 0                       # [n, B]
         steps = int(had.any(axis=1).sum())
         self.own += had.sum(axis=0)
         self.block_steps += steps
-        self.tokens += int(np.bitwise_count(self.bits ^ ring[-1]).sum())
-        self.bits = ring[-1]
+        self.tokens += int(np.bitwise_count(before ^ ring[-1]).sum())
         self.steps += steps
         return steps
 
@@ -272,49 +279,82 @@ class Loop:
         captured graph of slots(S) step slots and one wait; returns the
         refinement steps they took."""
         assert self.first
-        steps = self._account(self.dec.run_window(self.s, self.cfg.S, self.cfg.tau))
+        ring = self.dec.run_window(self.s, self.cfg.S, self.cfg.tau)
+        steps = self._account(ring, self.s, self.bits)
+        self.bits = ring[-1]
         self.first = False
+        self.slot = len(ring)
         if not (self.bits & self.wmask[self.s]).any():
             self._next_window()
         return steps
 
-    def windows(self, budget: int) -> int:
-        """Whole windows from the current one to at most the end of the
-        block, as many as `budget` steps surely cover, launched back to back
-        as captured graphs (and the commit when the block ends) with one wait
-        after the last: a window's S slots always finish it, so no launch
-        waits for the previous window's result.  Returns the steps taken."""
-        assert self.first
+    def queued(self, budget: int) -> int:
+        """At most `budget` refinement steps queued with one wait at the end.
+        At a window start with a window's S slots left in the budget: whole
+        windows back to back (a window's S slots always finish it), with
+        their commits and the next block's set-up, over at most two blocks
+        (the two ring parities); otherwise the slots of the current window
+        from the next one on, at most `budget` of them.  Returns the steps
+        taken (slots past the end of a window are not steps)."""
         cfg, dec = self.cfg, self.dec
-        nw = cfg.D // cfg.S
-        first = self.s
-        last = min(nw, first + budget // cfg.S)
-        for s in range(first, last):
-            dec.run_window(s, cfg.S, cfg.tau, wait=False)
-        if last == nw:
-            dec.commit()
+        S, nw = cfg.S, cfg.D // cfg.S
+        units = []                       # (block, window, first slot, end slot, bits before the first slot or None)
+        whole = self.slot == 0 and budget >= S
+        if whole:
+            blk0 = self.blk
+            while self.slot == 0 and budget >= S and self.blk < blk0 + 2:
+                before = self.bits if (not units or self.s == 0) else None   # else: the previous window's last bits
+                dec.run_window(self.s, S, cfg.tau, wait=False, parity=self.blk % 2)
+                units.append((self.blk, self.s, 0, S, before))
+                budget -= S
+                self.s += 1
+                if self.s == nw:
+                    dec.commit()
+                    self._new_block()        # queued copies; its bookkeeping follows the wait
+        else:
+            k = min(budget, S - self.slot)
+            dec.run_slots(self.s, S, cfg.tau, self.slot, self.slot + k, parity=self.blk % 2)
+            units.append((self.blk, self.s, self.slot, self.slot + k, self.bits))
         dec.wait()
         steps = 0
-        for s in range(first, last):
-            self.s = s
-            steps += self._account(dec.window_bits(s, cfg.S))
-            assert not (self.bits & self.wmask[s]).any()
-        self.s = last
-        if last == nw:
-            self._block_done()
+        prev_blk, cur = units[0][0], None
+        for blk, s, i0, i1, before in units:
+            if blk != prev_blk:              # the previous block ended with its last window
+                self._book_block()
+                prev_blk = blk
+            ring = dec.window_bits(s, S, blk % 2)[i0:i1]
+            steps += self._account(ring, s, cur if before is None else before)
+            cur = ring[-1]
+            if whole and (cur & self.wmask[s]).any():
+                raise RuntimeError(f"window {s} still has masked positions after its {S} slots")
+        if whole:
+            if self.s == 0:                  # the last window ended a block
+                self._book_block()
+            else:
+                self.bits = cur
+                self.first, self.slot = True, 0
+        else:
+            self.bits = cur
+            self.first = False
+            self.slot = units[0][3]
+            if not (cur & self.wmask[self.s]).any():
+                self._next_window()
         return steps
 
     def run(self, n: int, windows: bool):
-        """Exactly n refinement steps: window graphs while at least a graph's
-        slots remain (whole windows back to back when their slots always
-        finish them), single steps otherwise."""
+        """Exactly n refinement steps.  With window graphs: queued runs
+        (whole windows back to back, or slots of one window) with one wait
+        each when a window's slots always finish it, else window graphs while
+        at least a graph's slots remain; single steps otherwise."""
         left = n
         S = self.cfg.S
         slots = self.dec.slots(S)
-        piped = self.dec.windows_complete(S)
+        piped = windows and self.dec.windows_complete(S)
         while left > 0:
-            if windows and self.first and left >= slots:
-                left -= self.windows(left) if piped else self.window()
+            if piped:
+                left -= self.queued(left)
+            elif windows and self.first and left >= slots:
+                left -= self.window()
             else:
                 self.step()
                 left -= 1
@@ -648,11 +688,10 @@ def extras_persequence(w3, n_blocks=4):
     loop = Loop(dec, cfg, plants)
 
     def advance():
-        if loop.first:
-            if dec.windows_complete(cfg.S):
-                loop.windows(cfg.D)
-            else:
-                loop.window()
+        if dec.windows_complete(cfg.S):
+            loop.queued(cfg.D)
+        elif loop.first:
+            loop.window()
         else:
             loop.step()
     while loop.blk < 1:                           # warm-up block

@@ -101,9 +101,11 @@ class BlockDecoder:
         self.last = None
         self.lm_timer = None    # object whose start() / stop() bracket every LM-head call when set
         self._capturing = False
-        self.graphs = {}        # (kind, s) -> captured HIP graph of that step ("W": whole window)
+        # captured HIP graphs: ("E" | "DC", s) one step, ("W", s, parity) a window's
+        # slots, ("P", s, slot, parity) one slot, ("commit", 0) the commit
+        self.graphs = {}
         self._held_ws = {}      # tag -> workspace the captured graphs point into
-        self._rings = {}        # S -> [D // S, slots(S), B] pinned: mask bits after each step slot of each window
+        self._rings = {}        # S -> [2, D // S, slots(S), B] pinned: mask bits after each step slot of each window
 
     # ------------------------------------------------------------------ state
     def set_synthetic_prefix(self, kv_len, cache_k, cache_v, carry):
@@ -353,15 +355,25 @@ class BlockDecoder:
         # writing its new mask bits to its own row of the pinned ring.  Steps
         # past the end of the window find no candidate and their LM head does
         # no work.
+        # Two sets (ring parities) so that the windows of the next block can
+        # be queued before the host has read this block's rings; with
+        # windows_complete(S), also every slot as a graph of its own, for
+        # runs that start or stop inside a window.
         ring = self._ring(S)
         self._capturing = True
         try:
-            for s in range(D // S if self.window_graphs else 0):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in range(self.slots(S)):
-                        (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[s, i])
-                self.graphs[("W", s)] = g
+            for par in range(2 if self.window_graphs else 0):
+                for s in range(D // S):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        for i in range(self.slots(S)):
+                            (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[par, s, i])
+                    self.graphs[("W", s, par)] = g
+                    for i in range(self.slots(S) if self.windows_complete(S) else 0):
+                        g = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(g):
+                            (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[par, s, i])
+                        self.graphs[("P", s, i, par)] = g
         finally:
             self._capturing = False
         g = torch.cuda.CUDAGraph()
@@ -404,13 +416,14 @@ class BlockDecoder:
         return True
 
     def _ring(self, S: int):
-        """Pinned [D // S, slots(S), B] mask-bit rings of the windows of S
+        """Pinned [2, D // S, slots(S), B] mask-bit rings of the windows of S
         positions (kept for the decoder's lifetime: captured window graphs
-        write into them), one ring per window so that the windows of a block
-        can run back to back before the host reads any of them."""
+        write into them), one ring per window and parity so that the windows
+        of a block, and of the next block, can run back to back before the
+        host reads any of them."""
         r = self._rings.get(S)
         if r is None:
-            r = self._rings[S] = torch.zeros(self.dims.D // S, self.slots(S), self.dims.B, dtype=torch.int64,
+            r = self._rings[S] = torch.zeros(2, self.dims.D // S, self.slots(S), self.dims.B, dtype=torch.int64,
                                              pin_memory=True)
         return r
 
@@ -420,7 +433,7 @@ class BlockDecoder:
         (the fallback of the threshold rule), so S steps always do."""
         return self.slots(S) >= S
 
-    def run_window(self, s: int, S: int, tau, wait: bool = True):
+    def run_window(self, s: int, S: int, tau, wait: bool = True, parity: int = 0):
         """Window s from its exact step on: slots(S) step slots (one graph
         replay when captured), then one wait.  Returns the mask bits after
         every slot [slots(S), B] (uint64); slot i was a refinement step iff some
@@ -429,30 +442,46 @@ class BlockDecoder:
         its next steps are DualCache steps.  wait=False only queues the
         window and returns None: window_bits(s, S) reads its ring after a
         later wait (windows_complete(S) makes the next window's launch valid
-        without looking)."""
-        g = self.graphs.get(("W", s))
+        without looking).  parity: which of the two rings (and graph sets)."""
+        g = self.graphs.get(("W", s, parity))
         ring = self._ring(S)
         if g is not None and self._replay_ok(S, tau):
             g.replay()
             self.last = self._window(s, S)
         else:
             for i in range(self.slots(S)):
-                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[s, i])
+                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[parity, s, i])
         self._bits_ev.record()
         self._bits_fresh = False
         if not wait:
             return None
         self._bits_ev.synchronize()
-        return self.window_bits(s, S)
+        return self.window_bits(s, S, parity)
+
+    def run_slots(self, s: int, S: int, tau, i0: int, i1: int, parity: int = 0):
+        """Slots i0 .. i1-1 of window s (slot 0: its exact step; the others
+        DualCache steps), queued without a wait; slot i writes its mask bits
+        to row i of the window's ring (window_bits after a wait)."""
+        ring = self._ring(S)
+        ok = self._replay_ok(S, tau)
+        for i in range(i0, i1):
+            g = self.graphs.get(("P", s, i, parity))
+            if g is not None and ok:
+                g.replay()
+            else:
+                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[parity, s, i])
+        self.last = self._window(s, S)
+        self._bits_ev.record()
+        self._bits_fresh = False
 
     def wait(self):
         """Wait for the queued steps (their mask bits are then on the host)."""
         self._bits_ev.synchronize()
 
-    def window_bits(self, s: int, S: int) -> np.ndarray:
+    def window_bits(self, s: int, S: int, parity: int = 0) -> np.ndarray:
         """Mask bits after every slot of window s's last run [slots(S), B]
         (uint64); valid once that run has finished (run_window or wait)."""
-        return self._ring(S)[s].numpy().view(np.uint64).copy()
+        return self._ring(S)[parity, s].numpy().view(np.uint64).copy()
 
     # ------------------------------------------------------------------ loop
     def decode_block_windows(self, S: int, tau) -> int:
@@ -461,7 +490,7 @@ class BlockDecoder:
         tau) and windows_complete(S)).  Returns the refinement steps taken:
         the slots before which some sequence had a masked position of the
         window."""
-        assert self.windows_complete(S) and self._replay_ok(S, tau) and ("W", 0) in self.graphs
+        assert self.windows_complete(S) and self._replay_ok(S, tau) and ("W", 0, 0) in self.graphs
         bits = self.mask_bits_host()
         n_win = self.dims.D // S
         for s in range(n_win):

@@ -1,0 +1,122 @@
+"""Host logic of bench.py's decode loop, on the CPU with a stand-in decoder
+whose steps unmask positions deterministically from the mask bits alone:
+queued runs (whole windows back to back over two blocks with two ring
+parities, or slots of one window, one wait each) book exactly the steps,
+tokens, commits and per-block schedules of the same loop taken one step at
+a time."""
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+
+import bench
+
+
+class FakeDecoder:
+    """Mask-bit state of B sequences; a step of window s unmasks, in every
+    sequence with masked positions there, 1 to 3 of the lowest ones (a count
+    fixed by the block, window, sequence and bits), so that any order of
+    launching the same steps gives the same bits."""
+
+    def __init__(self, B, D, S):
+        self.B, self.D, self.S = B, D, S
+        self.bits = np.zeros(B, np.uint64)
+        self.blk = -1
+        self.rings = np.zeros((2, D // S, S, B), np.uint64)
+        self.commits = 0
+        self.log = []
+
+    def slots(self, S):
+        return S
+
+    def windows_complete(self, S):
+        return True
+
+    def set_block(self, tokens, masked, plant=None):
+        self.blk += 1
+        self.bits = np.full(self.B, (1 << self.D) - 1, np.uint64)
+
+    def _step(self, s):
+        self.log.append(("step", self.blk, s))
+        wm = ((1 << self.S) - 1) << (s * self.S)
+        for b in range(self.B):
+            m = int(self.bits[b]) & wm
+            if m:
+                k = 1 + (self.blk * 7 + s * 3 + b + bin(m).count("1")) % 3
+                for _ in range(k):
+                    if m:
+                        low = m & -m
+                        m ^= low
+                        self.bits[b] = np.uint64(int(self.bits[b]) & ~low)
+
+    def e_step(self, s, S, tau):
+        self._step(s)
+
+    def dc_step(self, s, S, tau):
+        self._step(s)
+
+    def mask_bits_host(self):
+        return self.bits.copy()
+
+    def commit(self):
+        self.commits += 1
+        self.log.append(("commit", self.blk))
+
+    def run_window(self, s, S, tau, wait=True, parity=0):
+        for i in range(S):
+            self._step(s)
+            self.rings[parity, s, i] = self.bits
+        return self.rings[parity, s].copy() if wait else None
+
+    def run_slots(self, s, S, tau, i0, i1, parity=0):
+        for i in range(i0, i1):
+            self._step(s)
+            self.rings[parity, s, i] = self.bits
+
+    def wait(self):
+        pass
+
+    def window_bits(self, s, S, parity=0):
+        return self.rings[parity, s].copy()
+
+
+def _state(loop):
+    return (loop.steps, loop.tokens, loop.commits, list(loop.done_blocks), loop.blk, loop.s, loop.first,
+            loop.bits.tolist(), loop.own.tolist(), loop.block_steps)
+
+
+@pytest.mark.parametrize("B,S", [(8, 8), (3, 4), (5, 16)])
+def test_queued_runs_book_like_single_steps(B, S):
+    cfg = SimpleNamespace(B=B, D=32, S=S, tau=0.9)
+    a = bench.Loop(FakeDecoder(B, 32, S), cfg, [None])
+    b = bench.Loop(FakeDecoder(B, 32, S), cfg, [None])
+    for n in [10, 60, 7, 1, 33, 64, 5, 120, 3]:
+        a.run(n, windows=True)            # queued runs
+        b.run(n, windows=False)           # one step and one wait at a time
+        assert _state(a) == _state(b), n
+        assert a.dec.commits == b.dec.commits == a.commits
+        # the same real steps on the device, in order (queued runs add only
+        # slots past the end of a window)
+        assert b.dec.log == _real_steps(a.dec.log, b.dec.log)
+    assert a.commits >= 3
+
+
+def _real_steps(log_a, log_b):
+    """log_a without the dead slots: the entries of log_b, matched in order."""
+    out, j = [], 0
+    for e in log_a:
+        if j < len(log_b) and e == log_b[j]:
+            out.append(e)
+            j += 1
+    assert j == len(log_b)
+    return out
+
+
+def test_queued_runs_stop_at_the_second_block():
+    """One queued run never starts the windows of a block whose ring parity
+    is still unread (at most two blocks per run)."""
+    cfg = SimpleNamespace(B=2, D=32, S=8, tau=0.9)
+    dec = FakeDecoder(2, 32, 8)
+    loop = bench.Loop(dec, cfg, [None])
+    loop.queued(10 ** 6)
+    assert loop.commits == 2 and loop.blk == 2 and dec.blk == 2 and loop.s == 0
