@@ -1013,10 +1013,14 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
   }
   best.ws_bytes = best.ksplit > 1 ? (size_t)best.ksplit * M * T * 16 * sizeof(float) : 0;
   // few tiles: K split over the waves of a work-group (no reduction launch),
-  // one work-group per CU
-  if (BD_GEMM_KWAVE > 0 && nch >= 4 && (BD_GEMM_KWAVE > 1 || best.ksplit > 1)) {
-    const int kmt = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
-    const long kny = (M + kmt * 16 - 1) / (kmt * 16);
+  // one work-group per CU.  Every work-group reads all K of its rows of X
+  // from L2, so long K rows stay with the K split over work-groups: measured
+  // (cold caches) faster up to 4096-wide rows for one row block, up to 2048
+  // for several.
+  const int kmt = mt <= 1 ? 1 : (mt == 2 ? 2 : 4);
+  const long kny = (M + kmt * 16 - 1) / (kmt * 16);
+  const bool kw_fit = K <= 2048 || (K <= 4096 && kny == 1);
+  if (BD_GEMM_KWAVE > 0 && nch >= 4 && (BD_GEMM_KWAVE > 1 || (best.ksplit > 1 && kw_fit))) {
     for (int nt = G; nt <= 2; nt += G) {
       if ((long)(T + nt - 1) / nt * kny <= kCUs) {
         best.kw_nt = nt;

@@ -137,15 +137,14 @@ def test_gemm_and_embed_argument_errors():
                          FAKE, big, None) == U                         # K % 256
     assert lib.bd_linear(1, 0, 3584, 3584, FAKE, R(1, 1, 0), FAKE, None, R(1, 1, 0), FAKE, R(1, 1, 0),
                          None, 0, None) == 0
-    # a long K, few columns and 256 rows: K split over work-groups (with 64
-    # rows it is split over the waves of a work-group and needs no workspace)
-    assert lib.bd_qkv_proj_workspace_size(1, 64, 8960, 1536, 256) == 0
-    need = lib.bd_qkv_proj_workspace_size(1, 256, 8960, 3584, 512)
-    assert need > 0
-    assert lib.bd_qkv_proj(1, 256, 8960, FAKE, R(256, 256, 0), FAKE, 3584, FAKE, R(256, 256, 0), FAKE, FAKE, 512,
+    # a short K with few columns: K split over the waves of a work-group, no workspace
+    assert lib.bd_qkv_proj_workspace_size(1, 64, 1536, 1536, 256) == 0
+    need = lib.bd_qkv_proj_workspace_size(1, 64, 8960, 1536, 256)
+    assert need > 0                                                    # a long K with few columns splits K
+    assert lib.bd_qkv_proj(1, 64, 8960, FAKE, R(64, 64, 0), FAKE, 1536, FAKE, R(64, 64, 0), FAKE, FAKE, 256,
                            FAKE, R(8, 32, 8), FAKE, R(8, 32, 8), FAKE, need - 16, None) == E
     # the split writes one fp32 partial sum per slice, row and 16-column tile column
-    assert need % (256 * (3584 + 2 * 512) * 4) == 0
+    assert need % (64 * (1536 + 2 * 256) * 4) == 0
     assert lib.bd_linear_workspace_size(1, 128, 17920, 1536) == 0     # enough column tiles: no split
     assert lib.bd_linear_workspace_size(0, 64, 3584, 3584) == 0       # fp32: no workspace
     assert lib.bd_embed_rows(1, 1, 65, 0, 8, 64, 10, FAKE, FAKE, FAKE, None, FAKE, None) == E
