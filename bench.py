@@ -75,19 +75,21 @@ TRAFFIC = {
     "lm": {"file": "lmhead_7B_M64_traffic.json", "section": "lm",
            "sources": ("lmhead.hip", "stream_gemm.h", "bd_device.h", "bd_launch.h"),
            "main": "lm_stream_kernel<4>", "then": "lm_merge_unmask_kernel",
-           "launch": "bd_lmhead_unmask: lm_stream_kernel<4> (512 work-groups) + lm_merge_unmask_kernel (8 "
-                     "work-groups x 512), 64 rows x 152064 x 3584 (8 sequences x window of 8)"},
+           "launch": "bd_lmhead_unmask: lm_stream_kernel<4> (512 work-groups, weight tiles with the "
+                     "non-temporal hint) + lm_merge_unmask_kernel (8 work-groups x 512), 64 rows x 152064 x 3584 "
+                     "(8 sequences x window of 8)"},
     "attn_dualcache": {"file": "attention_long_context_dualcache_traffic.json", "section": "attn",
                        "sources": ("attn.hip", "bd_device.h", "bd_launch.h"),
                        "main": "attn_bf16_kernel<128, 32, 1,", "then": "attn_merge_kernel",
-                       "launch": "bd_block_attn DualCache step: attn_bf16_kernel<128, 32, 1, 8> + "
-                                 "attn_merge_kernel<128, 2>, 32 sequences x 16384 cached rows, 8 fresh rows x 28 "
-                                 "query heads, 4 KV heads, d 128"},
+                       "launch": "bd_block_attn DualCache step: attn_bf16_kernel<128, 32, 1, 8, 2> (committed "
+                                 "K/V with the non-temporal hint) + attn_merge_kernel<128, 2>, 32 sequences x 16384 "
+                                 "cached rows, 8 fresh rows x 28 query heads, 4 KV heads, d 128"},
     "attn_exact": {"file": "attention_long_context_exact_traffic.json", "section": "attn",
                    "sources": ("attn.hip", "bd_device.h", "bd_launch.h"),
                    "main": "attn_bf16_kernel<128, 32, 2,", "then": "attn_merge_kernel",
-                   "launch": "bd_block_attn exact step: attn_bf16_kernel<128, 32, 2, 8> + attn_merge_kernel<128, 2>, "
-                             "32 sequences x 16384 cached rows, 32 fresh rows x 28 query heads, 4 KV heads, d 128"},
+                   "launch": "bd_block_attn exact step: attn_bf16_kernel<128, 32, 2, 8, 2> (committed K/V with "
+                             "the non-temporal hint) + attn_merge_kernel<128, 2>, 32 sequences x 16384 cached rows, "
+                             "32 fresh rows x 28 query heads, 4 KV heads, d 128"},
 }
 
 
