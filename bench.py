@@ -374,11 +374,12 @@ class Timing(NamedTuple):
                 "us_p90": self.p90 * 1e6}
 
 
-def time_call(fn, reps, warm=3, warm_s=0.1) -> Timing:
+def time_call(fn, reps, warm=3, warm_s=0.1, before=None) -> Timing:
     """Median, mean, 10th and 90th percentile (seconds) of `reps` calls, each
     bracketed by HIP events on the current stream, after at least `warm` calls
     and `warm_s` seconds of the same call (the clocks take ~20 ms of sustained
-    load to settle after the host-side input generation left the GPU idle)."""
+    load to settle after the host-side input generation left the GPU idle).
+    before(): queued ahead of every timed call, outside its interval."""
     t_end = time.perf_counter() + warm_s
     n = 0
     while n < warm or time.perf_counter() < t_end:
@@ -389,6 +390,8 @@ def time_call(fn, reps, warm=3, warm_s=0.1) -> Timing:
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
+        if before is not None:
+            before()
         a.record()
         fn()
         b.record()
@@ -556,6 +559,55 @@ def extras_subblock(w3, graphs, steps=40, warmup=10):
         del dec, plants, loop
         torch.cuda.empty_cache()
     return {"subblock_sweep_7B": out}
+
+
+def extras_proj(reps):
+    """The projections of the refinement steps one call at a time, each after
+    1 GiB of other reads has passed through the caches (as in a step, where
+    the LM head's weight stream comes between two uses of a projection's
+    weights): the 7B QKV and output projections at the 7B DualCache (64
+    rows) and exact (256 rows) steps, and the 1.5B layer's four projections at
+    the 28-layer decode's DualCache step (128 rows)."""
+    from block_diffusion_decoding_amd import ops
+    from block_diffusion_decoding_amd.ops import dense
+    T = torch.bfloat16
+    flush_src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush_dst = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+
+    def cold(fn):
+        def run():
+            flush_dst.copy_(flush_src[: 1 << 29])
+            flush_dst.copy_(flush_src[1 << 29:])
+            torch.cuda._sleep(20000)
+        return time_call(fn, reps, warm_s=0.02, before=run)
+
+    def rnd(*shape, s=1.0):
+        return (torch.randn(*shape, device="cuda") * s).to(T)
+    out = {}
+    for M, K, Nq, Nkv, inter, tag in ((64, 3584, 3584, 512, None, "7B_M64"), (256, 3584, 3584, 512, None, "7B_M256"),
+                                      (128, 1536, 1536, 256, 8960, "1.5B_M128")):
+        x, wq, wk, wv = rnd(M, K), rnd(Nq, K, s=.02), rnd(Nkv, K, s=.02), rnd(Nkv, K, s=.02)
+        q, k, v = rnd(M, Nq), rnd(M, Nkv), rnd(M, Nkv)
+        t = cold(lambda: ops.bd_qkv_proj(x, dense(M), wq, q, dense(M), wk, wv, k, dense(M), v, dense(M), M=M))
+        by = (Nq + 2 * Nkv) * K * 2
+        out[f"qkv_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
+        wo, y = rnd(K, Nq, s=.02), rnd(M, K)
+        t = cold(lambda: ops.bd_linear(q, dense(M), wo, y, dense(M), M=M, res=x, rr=dense(M)))
+        by = K * Nq * 2
+        out[f"o_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
+        if inter:
+            wgu, a = rnd(2 * inter, K, s=.02), rnd(M, inter)
+            t = cold(lambda: ops.bd_gate_up_swiglu(x, dense(M), wgu, a, dense(M), M=M))
+            by = 2 * inter * K * 2
+            out[f"gate_up_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
+            wd = rnd(K, inter, s=.02)
+            t = cold(lambda: ops.bd_linear(a, dense(M), wd, y, dense(M), M=M, res=y, rr=dense(M)))
+            by = K * inter * 2
+            out[f"down_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
+    log("[bench] projections (cold caches): " + ", ".join(f"{k} {v['us']:.1f} us" for k, v in out.items()))
+    del flush_src, flush_dst
+    torch.cuda.empty_cache()
+    return {"projections": out}
 
 
 def timed_loop(dec, cfg, plants, graphs, steps, warmup):
@@ -758,7 +810,8 @@ def extras_v1():
     return {"v1_full_attention_1.5B_layer": out}
 
 
-def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "rates", "small", "persequence", "v1"),
+def extras(w3, reps, parts=("attn", "long", "lm", "proj", "e2e", "train", "subblock", "rates", "small", "persequence",
+                            "v1"),
            graphs=True,
            e2e_blocks=None):
     """Attention and LM head alone at the long-context / batched shapes, the
@@ -773,6 +826,8 @@ def extras(w3, reps, parts=("attn", "long", "lm", "e2e", "train", "subblock", "r
         out.update(extras_long(c4, w3, graphs))
     if "lm" in parts:
         out.update(extras_lm(w3, reps))
+    if "proj" in parts:
+        out.update(extras_proj(reps))
     if "e2e" in parts:
         out.update(extras_e2e(graphs, e2e_blocks))
     if "train" in parts:
@@ -876,6 +931,24 @@ def extras_lm(w3, reps):
     out = {}
     T = torch.bfloat16
     calibration_copy()
+    # ---- vendor ceilings for streaming HBM traffic on this part: a 1 GiB
+    # device copy (torch copy_, reads and writes 1 GiB) and a 1 GiB fp32 sum
+    # (torch sum, reads 1 GiB): what a plain library streaming kernel reaches
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    tc = time_call(lambda: dst.copy_(src), reps)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    ts = time_call(lambda: torch.sum(src, dim=0, out=acc), reps)
+    out["hbm_stream_ceiling"] = {
+        "what": "vendor streaming kernels on 1 GiB: torch copy_ (1 GiB read + 1 GiB written) and torch.sum over "
+                "fp32 (1 GiB read)",
+        "copy_us": tc.mean * 1e6, "copy_GB/s": 2 * (1 << 30) / tc.mean / 1e9,
+        "sum_us": ts.mean * 1e6, "sum_read_GB/s": (1 << 30) / ts.mean / 1e9,
+        "frac_hbm_copy": 2 * (1 << 30) / tc.mean / 1e9 / HBM_PEAK_GBS,
+        "frac_hbm_sum": (1 << 30) / ts.mean / 1e9 / HBM_PEAK_GBS}
+    log(f"[bench] streaming ceilings: copy {2 * (1 << 30) / tc.mean / 1e9:.0f} GB/s, "
+        f"sum {(1 << 30) / ts.mean / 1e9:.0f} GB/s")
+    del src, dst
     # ---- LM head alone: 1024 rows on the 7B head (MFMA bound)
     Wlm = torch.from_numpy(w3.Wlm).to("cuda", T)
     for M, key in ((1024, "lmhead_7B_M1024"), (256, "lmhead_7B_M256"), (64, "lmhead_7B_M64")):
@@ -998,8 +1071,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=32,
                     help="DualCache steps of the oracle timed for cpu_baseline (about 10 s of host work)")
-    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "e2e", "train", "subblock", "rates", "small",
-                                          "persequence", "v1", "oracle1"),
+    ap.add_argument("--section", choices=("all", "attn", "long", "lm", "proj", "e2e", "train", "subblock", "rates",
+                                          "small", "persequence", "v1", "oracle1"),
                     default="all", help="run only that measurement (for profiling) and print its JSON instead of the "
                                         "bench line (oracle1: the one-thread oracle, no GPU)")
     ap.add_argument("--e2e-blocks", type=int, default=None,
@@ -1026,7 +1099,7 @@ def main():
     pkg.load_library()
 
     cfg = bi.C3
-    if args.section in ("e2e", "train", "v1", "small"):
+    if args.section in ("e2e", "train", "v1", "small", "proj"):
         print(json.dumps(extras(None, args.reps, parts=(args.section,), graphs=not args.no_graphs,
                                 e2e_blocks=args.e2e_blocks)), flush=True)
         return
