@@ -20,6 +20,12 @@ class BdRows(ctypes.Structure):
     _fields_ = [("group", ctypes.c_int32), ("stride", ctypes.c_int32), ("offset", ctypes.c_int32)]
 
 
+class BdGuard(ctypes.Structure):
+    """Device-side condition of a call: it does nothing when no bits[b], b < n,
+    has a bit of mask set."""
+    _fields_ = [("bits", ctypes.c_void_p), ("mask", ctypes.c_uint64), ("n", ctypes.c_int32)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "bd_version": (ctypes.c_char_p, []),
@@ -32,6 +38,12 @@ SIGNATURES = {
                               c_void_p, c_void_p, c_int,
                               c_float, c_void_p, c_void_p,
                               c_void_p, c_size_t, c_void_p]),
+    "bd_block_attn_guarded": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_void_p, c_int, c_int,
+                                      c_void_p, c_void_p, c_void_p, c_int,
+                                      c_void_p, c_void_p, c_int,
+                                      c_float, c_void_p, c_void_p,
+                                      c_void_p, c_size_t, ctypes.POINTER(BdGuard), c_void_p]),
     "bd_block_attn_noalloc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_void_p, c_int, c_int,
                                       c_void_p, c_void_p, c_void_p, c_int,
@@ -67,6 +79,9 @@ SIGNATURES = {
     "bd_linear_workspace_size": (c_size_t, [c_int] * 4),
     "bd_linear": (c_int, [c_int, c_int, c_int, c_int, c_void_p, BdRows, c_void_p,
                           c_void_p, BdRows, c_void_p, BdRows, c_void_p, c_size_t, c_void_p]),
+    "bd_linear_guarded": (c_int, [c_int, c_int, c_int, c_int, c_void_p, BdRows, c_void_p,
+                                  c_void_p, BdRows, c_void_p, BdRows, c_void_p, c_size_t, ctypes.POINTER(BdGuard),
+                                  c_void_p]),
     "bd_linear_residual_rmsnorm": (c_int, [c_int, c_int, c_int, c_int, c_void_p, BdRows, c_void_p, c_void_p,
                                            BdRows, c_float, c_void_p, BdRows, c_void_p, c_size_t, c_void_p]),
     "bd_qkv_proj_workspace_size": (c_size_t, [c_int] * 5),
@@ -74,6 +89,10 @@ SIGNATURES = {
                             c_void_p, c_int, c_void_p, BdRows,
                             c_void_p, c_void_p, c_int, c_void_p, BdRows, c_void_p, BdRows,
                             c_void_p, c_size_t, c_void_p]),
+    "bd_qkv_proj_guarded": (c_int, [c_int, c_int, c_int, c_void_p, BdRows,
+                                    c_void_p, c_int, c_void_p, BdRows,
+                                    c_void_p, c_void_p, c_int, c_void_p, BdRows, c_void_p, BdRows,
+                                    c_void_p, c_size_t, ctypes.POINTER(BdGuard), c_void_p]),
     "bd_qkv_proj_rope_workspace_size": (c_size_t, [c_int] * 5),
     "bd_qkv_proj_rope": (c_int, [c_int, c_int, c_int, c_void_p, BdRows,
                                  c_void_p, c_int, c_void_p, BdRows,

@@ -16,6 +16,12 @@ bool valid_rows(const bd_rows& r) { return r.group >= 1 && r.stride >= 0 && r.of
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A guard is optional; when given its words must be there and aligned.
+bool valid_guard(const bd_guard* g) {
+  return g == nullptr || (g->bits != nullptr && (reinterpret_cast<uintptr_t>(g->bits) & 7u) == 0 && g->n >= 1 &&
+                          g->n <= 4096);
+}
+
 }  // namespace
 
 bd_status bd_hip_status(hipError_t e) {
@@ -70,6 +76,15 @@ bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const
                         const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
                         const void* k_blk, const void* v_blk, int n_blk, float scale, void* o, float* lse,
                         void* workspace, size_t ws_bytes, void* stream) {
+  return bd_block_attn_guarded(dt, B, Hq, Hkv, d, D, q, n_q, q_off, k_cache, v_cache, kv_len, cap, k_blk, v_blk,
+                               n_blk, scale, o, lse, workspace, ws_bytes, nullptr, stream);
+}
+
+bd_status bd_block_attn_guarded(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const void* q, int n_q,
+                                int q_off, const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
+                                const void* k_blk, const void* v_blk, int n_blk, float scale, void* o, float* lse,
+                                void* workspace, size_t ws_bytes, const bd_guard* guard, void* stream) {
+  if (!valid_guard(guard)) return BD_EINVAL;
   const bd_status chk = bd_block_attn_check(dt, B, Hq, Hkv, d, D, q, n_q, q_off, k_cache, v_cache, kv_len, cap,
                                             k_blk, v_blk, n_blk, scale, o);
   if (chk != BD_OK || B == 0 || n_q == 0) return chk;
@@ -99,6 +114,7 @@ bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D, const
   a.n_blk = n_blk;
   a.epc = 1;
   a.scale = scale;
+  a.guard = guard;
   return hip_status(bd_attn_launch(dt, p, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -268,8 +284,8 @@ bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int 
 
 static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const BdGemmSeg* segs, int nseg,
                              int mode, const BdGemmRope* rope, const BdGemmNorm* post_norm, void* workspace,
-                             size_t ws_bytes, void* stream) {
-  if (!valid_dtype(dt) || M < 0) return BD_EINVAL;
+                             size_t ws_bytes, void* stream, const bd_guard* guard = nullptr) {
+  if (!valid_dtype(dt) || M < 0 || !valid_guard(guard)) return BD_EINVAL;
   if (M == 0) return BD_OK;
   if (K <= 0 || !x || !valid_rows(xr)) return BD_EINVAL;
   int N[3];
@@ -293,7 +309,7 @@ static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows x
   if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)))
     return BD_EINVAL;
   return hip_status(bd_gemm_launch(dt, p, M, K, x, xr, segs, nseg, mode, rope, post_norm, workspace,
-                                   static_cast<hipStream_t>(stream)));
+                                   static_cast<hipStream_t>(stream), guard));
 }
 
 size_t bd_linear_workspace_size(bd_dtype dt, int M, int N, int K) {
@@ -319,6 +335,13 @@ bd_status bd_linear(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr,
   return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_PLAIN, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
+bd_status bd_linear_guarded(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr, const void* w,
+                            const void* res, bd_rows rr, void* y, bd_rows yr, void* workspace, size_t ws_bytes,
+                            const bd_guard* guard, void* stream) {
+  BdGemmSeg seg{w, y, yr, res, rr, N};
+  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_PLAIN, nullptr, nullptr, workspace, ws_bytes, stream, guard);
+}
+
 bd_status bd_linear_residual_rmsnorm(bd_dtype dt, int M, int N, int K, const void* x, bd_rows xr, const void* w,
                                      void* y, bd_rows yr, float eps, void* h, bd_rows hr, void* workspace,
                                      size_t ws_bytes, void* stream) {
@@ -335,6 +358,15 @@ bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr, cons
   BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
                        {wv, v, vr, nullptr, none, Nkv}};
   return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_PLAIN, nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+bd_status bd_qkv_proj_guarded(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,
+                              bd_rows qr, const void* wk, const void* wv, int Nkv, void* k, bd_rows kr, void* v,
+                              bd_rows vr, void* workspace, size_t ws_bytes, const bd_guard* guard, void* stream) {
+  const bd_rows none{1, 1, 0};
+  BdGemmSeg segs[3] = {{wq, q, qr, nullptr, none, Nq}, {wk, k, kr, nullptr, none, Nkv},
+                       {wv, v, vr, nullptr, none, Nkv}};
+  return gemm_common(dt, M, K, x, xr, segs, 3, BD_GEMM_PLAIN, nullptr, nullptr, workspace, ws_bytes, stream, guard);
 }
 
 bd_status bd_qkv_proj_rope(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* wq, int Nq, void* q,

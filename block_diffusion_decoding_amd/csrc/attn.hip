@@ -82,6 +82,9 @@ struct AttnK {
   int epc;  // entries (b) per cache slab: entry b reads cache slab b / epc
   int R, QT, nqg, chunk, nchunks, n_units;
   float scale_log2;
+  const uint64_t* g_bits;  // guard (bd_guard): nothing is done when no g_bits[b],
+  uint64_t g_mask;         // b < g_n, has a bit of g_mask set
+  int g_n;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -343,6 +346,11 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_ke
   __builtin_amdgcn_s_waitcnt(vm_imm(0));
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t) issue(t);
+  // the guard's words load while the first stages are in flight
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) {
+    __builtin_amdgcn_s_waitcnt(vm_imm(0));  // no DMA into this LDS after the work-group ends
+    return;
+  }
   for (int t = 0; t < ntiles; ++t) {
     wait_stages<LW, NS>(min(ntiles - t - 1, NS - 2));
     pipe_barrier();  // tile t in LDS; every wave is done with tile t - 1
@@ -555,6 +563,7 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_ke
 // chunk indices past the end are clamped and weighted 0.
 template <int DH, int NB>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnK a) {
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) return;
   constexpr int PER = DH / 64;  // head dims per lane
   const int lane = threadIdx.x & 63;
   const size_t row = (size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -630,6 +639,9 @@ struct AttnF {
   float* lse;
   int Hq, Hkv, G, d, D, n_q, q_off, cap, n_blk, epc;
   float scale;
+  const uint64_t* g_bits;
+  uint64_t g_mask;
+  int g_n;
 };
 
 __device__ float block_reduce(float v, bool is_max, float* red) {
@@ -647,6 +659,7 @@ __device__ float block_reduce(float v, bool is_max, float* red) {
 }
 
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnF a) {
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) return;
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int kvh = h / a.G;
@@ -735,7 +748,8 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
     AttnF a{static_cast<const float*>(x.q), static_cast<const float*>(x.k_cache),
             static_cast<const float*>(x.v_cache), x.kv_len, static_cast<const float*>(x.k_blk),
             static_cast<const float*>(x.v_blk), static_cast<float*>(x.o), x.lse,
-            x.Hq, x.Hkv, x.G, x.d, x.D, x.n_q, x.q_off, x.cap, x.n_blk, x.epc, x.scale};
+            x.Hq, x.Hkv, x.G, x.d, x.D, x.n_q, x.q_off, x.cap, x.n_blk, x.epc, x.scale,
+            x.guard ? x.guard->bits : nullptr, x.guard ? x.guard->mask : 0, x.guard ? x.guard->n : 0};
     hipLaunchKernelGGL(attn_f32_kernel, dim3(x.n_q, x.Hq, x.B), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
@@ -755,6 +769,9 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
   a.R = p.R; a.QT = p.QT; a.nqg = p.nqg; a.chunk = p.chunk; a.nchunks = p.nchunks;
   a.n_units = x.B * x.Hkv * p.nchunks;
   a.scale_log2 = x.scale * BD_LOG2E;
+  a.g_bits = x.guard ? x.guard->bits : nullptr;
+  a.g_mask = x.guard ? x.guard->mask : 0;
+  a.g_n = x.guard ? x.guard->n : 0;
   const int n_wg = kXcd * a.nqg * ((a.n_units + kXcd - 1) / kXcd);
 #define BD_ATTN_LAUNCH(DH, QPW)                                                                           \
   do {                                                                                                    \

@@ -43,6 +43,26 @@ __device__ __forceinline__ float bd_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float bd_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Row maps (see bd_rows in bd.h).
+// The guard of a call (bd_guard): true when no bits[b], b < n, has a bit of
+// mask set (the call then does nothing).  The words were written before the
+// kernel started and do not change while it runs, so they are read through
+// the constant address space: scalar loads, eight at a time, that leave the
+// vector-memory counter to the kernel's own loads.
+typedef const __attribute__((address_space(4))) uint64_t* bd_const_u64_ptr;
+__device__ __forceinline__ bool bd_guard_dead(const uint64_t* bits, uint64_t mask, int n) {
+  if (bits == nullptr) return false;
+  const bd_const_u64_ptr p = (bd_const_u64_ptr)bits;
+  uint64_t any = 0;
+  for (int b0 = 0; b0 < n; b0 += 8) {
+    uint64_t w[8];  // all eight loads in flight before the first is used
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = p[b0 + u < n ? b0 + u : n - 1];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) any |= w[u];
+  }
+  return (any & mask) == 0;
+}
+
 __device__ __forceinline__ int bd_map_row(const bd_rows& m, int r) {
   return (r / m.group) * m.stride + m.offset + (r % m.group);
 }

@@ -47,6 +47,7 @@ struct BdAttnArgs {
   int B, Hq, Hkv, G, d, D, n_q, q_off, cap, n_blk;
   int epc;  // entries per cache slab (1: entry b owns slab b)
   float scale;
+  const bd_guard* guard;  // optional (bd_guard)
 };
 
 hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& a, hipStream_t s);
@@ -152,9 +153,11 @@ struct BdGemmNorm {
   float eps;
 };
 
+// guard: optional (bd_guard), honoured by every kernel of the launch.
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
                           const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope,
-                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s);
+                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s,
+                          const bd_guard* guard = nullptr);
 
 hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
                            const void* E, const int32_t* tokens, const uint64_t* mask_bits,

@@ -31,7 +31,7 @@ constexpr int kThreads = 256;
 #define BD_GEMM_NS 3
 #endif
 #ifndef BD_GEMM_MAX_MT
-#define BD_GEMM_MAX_MT 8
+#define BD_GEMM_MAX_MT 4
 #endif
 constexpr int kCUs = 256;
 constexpr int kLdsPerCU = 160 * 1024;
@@ -85,6 +85,9 @@ struct GemmS {
   const int32_t* pos_base;  // rotary embedding (BD_GEMM_ROPE)
   int n_rows, pos_off, d;
   double log2_theta;
+  const uint64_t* g_bits;   // guard (bd_guard): the launch does nothing when no
+  uint64_t g_mask;          // g_bits[b], b < g_n, has a bit of g_mask set
+  int g_n;
 };
 
 __device__ __forceinline__ int seg_of(const GemmS& a, int gt) {
@@ -181,6 +184,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
 #pragma unroll
   for (int c = 0; c < C::NS - 1; ++c)
     if (c < nst) issue_next();
+  // the guard's words load while the first stages are in flight
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) {
+    __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));  // no DMA into this LDS after the work-group ends
+    return;
+  }
 
   int cp = 0, cch = 0;  // compute cursor: pass, chunk
   for (int s = 0; s < nst; ++s) {
@@ -385,6 +393,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kwave_kernel(GemmS a, int ny
 #pragma unroll
   for (int c = 0; c < NS - 1; ++c)
     if (c < nch) issue(c);
+  // the guard's words load while the first stages are in flight
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) {
+    __builtin_amdgcn_s_waitcnt(bd_stream::vmcnt_imm(0));  // no DMA into this LDS after the work-group ends
+    return;
+  }
   for (int s = 0; s < nch; ++s) {
     // stage s complete: at most `later` younger stages still in flight
     const int later = min(nch - s - 1, NS - 2);
@@ -493,6 +506,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
                                                                    int row_major) {
   using P = GBig<CT>;
   __shared__ uint4 sbuf[P::NS * P::STAGE_U4];
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int wr = wave % P::WR, wc = wave / P::WR;
@@ -734,6 +748,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
 // pos * theta^(-2j/d) in fp64, the rotation in fp32); the threads of the
 // second halves have nothing to do.
 __global__ __launch_bounds__(kThreads) void gemm_stream_reduce(GemmS a) {
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) return;
   const int T = a.tb[a.nseg];
   const size_t Nt = (size_t)T * 16;
   const size_t t = (size_t)blockIdx.x * kThreads + threadIdx.x;
@@ -804,6 +819,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_reduce(GemmS a) {
 // in a fixed order (wave sums, then the waves in order).
 constexpr int kNormGroups = 4;
 __global__ __launch_bounds__(kThreads) void gemm_reduce_norm(GemmS a, float eps, uint16_t* h, bd_rows hr) {
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) return;
   __shared__ float red[kThreads / 64];
   const int m = blockIdx.x;
   const int N = a.N[0];
@@ -881,11 +897,15 @@ struct GemmF {
   const float* res;
   bd_rows yr, rr;
   int N;
+  const uint64_t* g_bits;
+  uint64_t g_mask;
+  int g_n;
 };
 
 // fp32 projections: one thread per output element (small test shapes); in
 // SwiGLU mode the thread forms the gate and the up product of its column.
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF a, int swiglu) {
+  if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) return;
   const int n = blockIdx.x * kThreads + threadIdx.x;
   const int m = blockIdx.y;
   if (n >= a.N) return;
@@ -970,7 +990,7 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
   // candidates: row tile (16 .. 64 rows, or 128 above 64 rows), K slices, and
   // the number of passes per work-group (work-groups = units / pass size)
   for (int MT = mt0; MT <= (mt > 4 && BD_GEMM_MAX_MT >= 8 ? 8 : mt0); MT *= 2) {
-    const int NTW = MT <= 2 ? 8 : 4;
+    const int NTW = MT <= 4 ? 8 : 4;
     // resident work-groups: at most two per CU, fewer when the stages fill the LDS
     const int lds = kNS * 2 * (NTW + MT) * 1024;
     const int per_cu = kLdsPerCU / lds >= 2 ? 2 : 1;
@@ -1049,7 +1069,10 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
 
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
                           const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope,
-                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s) {
+                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s, const bd_guard* guard) {
+  const uint64_t* g_bits = guard ? guard->bits : nullptr;
+  const uint64_t g_mask = guard ? guard->mask : 0;
+  const int g_n = guard ? guard->n : 0;
   // the RMSNorm after a one-segment projection rides on its K-split reduction
   // when there is one and the row fits a work-group's registers
   const bool fused_norm = post_norm != nullptr && dt == BD_BF16 && nseg == 1 && p.ksplit > 1 &&
@@ -1058,7 +1081,7 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
     for (int i = 0; i < nseg; ++i) {
       GemmF a{static_cast<const float*>(x), xr, M, K, static_cast<const float*>(segs[i].w),
               static_cast<float*>(segs[i].y), static_cast<const float*>(segs[i].res), segs[i].yr, segs[i].rr,
-              segs[i].N};
+              segs[i].N, g_bits, g_mask, g_n};
       hipLaunchKernelGGL(gemm_f32_kernel, dim3((segs[i].N + kThreads - 1) / kThreads, M), dim3(kThreads), 0, s,
                          a, mode == BD_GEMM_SWIGLU ? 1 : 0);
       hipError_t e = hipGetLastError();
@@ -1068,6 +1091,9 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
     GemmS a{};
     a.x = static_cast<const uint16_t*>(x);
     a.xr = xr;
+    a.g_bits = g_bits;
+    a.g_mask = g_mask;
+    a.g_n = g_n;
     a.M = M;
     a.K = K;
     a.nseg = nseg;
@@ -1129,7 +1155,12 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
       switch (p.MT) {
         case 1: hipLaunchKernelGGL((gemm_stream_kernel<1, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
         case 2: hipLaunchKernelGGL((gemm_stream_kernel<2, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
-        case 4: hipLaunchKernelGGL((gemm_stream_kernel<4, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
+        case 4:
+          if (p.NTW == 8)
+            hipLaunchKernelGGL((gemm_stream_kernel<4, 8>), grid, dim3(kThreads), 0, s, a, p.passes, p.G);
+          else
+            hipLaunchKernelGGL((gemm_stream_kernel<4, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G);
+          break;
         default: hipLaunchKernelGGL((gemm_stream_kernel<8, 4>), grid, dim3(kThreads), 0, s, a, p.passes, p.G); break;
       }
       hipError_t e = hipGetLastError();

@@ -105,6 +105,7 @@ class BlockDecoder:
         # slots, ("P", s, slot, parity) one slot, ("commit", 0) the commit
         self.graphs = {}
         self._held_ws = {}      # tag -> workspace the captured graphs point into
+        self._guard = None      # (bits, mask, n): the step's projections and attention skip a finished window
         self._rings = {}        # S -> [2, D // S, slots(S), B] pinned: mask bits after each step slot of each window
 
     # ------------------------------------------------------------------ state
@@ -206,9 +207,9 @@ class BlockDecoder:
         ops.bd_embed_rows(W["E"], self.tokens, self.mask_bits, X, row_off=lo, n_rows=n, plant=self.plant)
         kr = rows(n, D, lo)
         ops.bd_qkv_proj(X, dense(B * n), W["Wq"], q, dense(B * n), W["Wk"], W["Wv"], self.blk_k, kr,
-                        self.blk_v, kr, M=B * n)
+                        self.blk_v, kr, M=B * n, guard=self._guard)
         ops.bd_block_attn(q, self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, o,
-                          D=D, q_off=lo)
+                          D=D, q_off=lo, guard=self._guard)
         return X, o
 
     def _lm_and_unmask(self, s: int, S: int, tau: float, bits_out=None):
@@ -260,7 +261,7 @@ class BlockDecoder:
             B, D = dm.B, dm.D
             X, o = self._forward_rows(0, D)
             ops.bd_linear(o, dense(B * D), self.W["Wo"], self.H, rows(D, 1 + D, 1), M=B * D,
-                          res=X, rr=dense(B * D))
+                          res=X, rr=dense(B * D), guard=self._guard)
             self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
             self._step_done()
@@ -272,7 +273,7 @@ class BlockDecoder:
             B, D = dm.B, dm.D
             X, o = self._forward_rows(s * S, S)
             ops.bd_linear(o, dense(B * S), self.W["Wo"], self.H, rows(S, 1 + D, 1 + s * S), M=B * S,
-                          res=X, rr=dense(B * S))
+                          res=X, rr=dense(B * S), guard=self._guard)
             self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
             self._step_done()
@@ -364,6 +365,9 @@ class BlockDecoder:
         try:
             for par in range(2 if self.window_graphs else 0):
                 for s in range(D // S):
+                    # a slot past the end of its window skips its projections and
+                    # attention (its LM head skips itself), so dead slots cost little
+                    self._guard = (self.mask_bits, ((1 << S) - 1) << (s * S), B)
                     g = torch.cuda.CUDAGraph()
                     with torch.cuda.graph(g):
                         for i in range(self.slots(S)):
@@ -376,6 +380,7 @@ class BlockDecoder:
                         self.graphs[("P", s, i, par)] = g
         finally:
             self._capturing = False
+            self._guard = None
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             self._commit_kernels()
@@ -449,8 +454,12 @@ class BlockDecoder:
             g.replay()
             self.last = self._window(s, S)
         else:
-            for i in range(self.slots(S)):
-                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[parity, s, i])
+            self._guard = (self.mask_bits, ((1 << S) - 1) << (s * S), self.dims.B)
+            try:
+                for i in range(self.slots(S)):
+                    (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[parity, s, i])
+            finally:
+                self._guard = None
         self._bits_ev.record()
         self._bits_fresh = False
         if not wait:
@@ -469,7 +478,11 @@ class BlockDecoder:
             if g is not None and ok:
                 g.replay()
             else:
-                (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[parity, s, i])
+                self._guard = (self.mask_bits, ((1 << S) - 1) << (s * S), self.dims.B)
+                try:
+                    (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[parity, s, i])
+                finally:
+                    self._guard = None
         self.last = self._window(s, S)
         self._bits_ev.record()
         self._bits_fresh = False

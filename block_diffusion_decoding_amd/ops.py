@@ -6,6 +6,8 @@ kernels.  A non-OK status raises ``BdError``.  Shapes follow include/bd.h.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -74,10 +76,19 @@ def bd_block_attn_workspace_size(dtype, B, Hq, Hkv, d, n_q, cap, n_blk) -> int:
     return int(_lib.load().bd_block_attn_workspace_size(_DT[dtype], B, Hq, Hkv, d, n_q, cap, n_blk))
 
 
+def _guard(guard):
+    """(bits [n] int64 tensor, mask, n) -> a BdGuard the call reads (None: no guard)."""
+    if guard is None:
+        return None
+    bits, mask, n = guard
+    return ctypes.byref(_lib.BdGuard(_p(bits), ctypes.c_uint64(int(mask) & (2 ** 64 - 1)), int(n)))
+
+
 def bd_block_attn(q, k_cache, v_cache, kv_len, k_blk, v_blk, o, *, D, q_off=0, scale=None, lse=None,
-                  ws=None, stream=None):
+                  ws=None, stream=None, guard=None):
     """q [B, n_q, Hq, d]; k/v_cache [B, Hkv, cap, d]; kv_len [B] int32; k/v_blk [B, n_blk, Hkv, d];
-    o [B, n_q, Hq, d]; lse [B, Hq, n_q] fp32 or None."""
+    o [B, n_q, Hq, d]; lse [B, Hq, n_q] fp32 or None.  guard: (bits, mask, n) or None
+    (bd_block_attn_guarded: nothing is done when no bits[b] has a bit of mask set)."""
     lib = _lib.load()
     B, n_q, Hq, d = q.shape
     if k_cache is None:         # no cache rows: only the in-block keys
@@ -91,10 +102,12 @@ def bd_block_attn(q, k_cache, v_cache, kv_len, k_blk, v_blk, o, *, D, q_off=0, s
     need = lib.bd_block_attn_workspace_size(dt, B, Hq, Hkv, d, n_q, cap, n_blk)
     if ws is None:
         ws = workspace(need, q.device, "attn")
-    st = lib.bd_block_attn(dt, B, Hq, Hkv, d, D, _p(q), n_q, q_off, _p(k_cache), _p(v_cache), _p(kv_len), cap,
-                           _p(k_blk), _p(v_blk), n_blk, float(scale), _p(o), _p(lse), _p(ws), ws.numel(),
-                           _stream(stream))
-    _check("bd_block_attn", st)
+    args = (dt, B, Hq, Hkv, d, D, _p(q), n_q, q_off, _p(k_cache), _p(v_cache), _p(kv_len), cap,
+            _p(k_blk), _p(v_blk), n_blk, float(scale), _p(o), _p(lse), _p(ws), ws.numel())
+    if guard is None:
+        _check("bd_block_attn", lib.bd_block_attn(*args, _stream(stream)))
+    else:
+        _check("bd_block_attn_guarded", lib.bd_block_attn_guarded(*args, _guard(guard), _stream(stream)))
     return o
 
 
@@ -275,16 +288,19 @@ def bd_qkv_proj_workspace_size(dtype, M, K, Nq, Nkv) -> int:
     return int(_lib.load().bd_qkv_proj_workspace_size(_DT[dtype], M, K, Nq, Nkv))
 
 
-def bd_linear(x, xr, w, y, yr, *, M, res=None, rr=None, ws=None, stream=None):
-    """y[yr(m)] = x[xr(m)] w^T (+ res[rr(m)]); w [N, K]."""
+def bd_linear(x, xr, w, y, yr, *, M, res=None, rr=None, ws=None, stream=None, guard=None):
+    """y[yr(m)] = x[xr(m)] w^T (+ res[rr(m)]); w [N, K].  guard: as bd_block_attn."""
     lib = _lib.load()
     N, K = w.shape
     dt = _dt(w)
     if ws is None:
         ws = workspace(lib.bd_linear_workspace_size(dt, M, N, K), w.device, "gemm")
-    st = lib.bd_linear(dt, M, N, K, _p(x), xr, _p(w), _p(res), rr if rr is not None else dense(1), _p(y), yr,
-                       _p(ws), ws.numel(), _stream(stream))
-    _check("bd_linear", st)
+    args = (dt, M, N, K, _p(x), xr, _p(w), _p(res), rr if rr is not None else dense(1), _p(y), yr,
+            _p(ws), ws.numel())
+    if guard is None:
+        _check("bd_linear", lib.bd_linear(*args, _stream(stream)))
+    else:
+        _check("bd_linear_guarded", lib.bd_linear_guarded(*args, _guard(guard), _stream(stream)))
 
 
 def bd_linear_residual_rmsnorm(x, xr, w, y, yr, h, hr, *, M, eps, ws=None, stream=None):
@@ -299,17 +315,21 @@ def bd_linear_residual_rmsnorm(x, xr, w, y, yr, h, hr, *, M, eps, ws=None, strea
     _check("bd_linear_residual_rmsnorm", st)
 
 
-def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, ws=None, stream=None):
-    """q[qr(m)] = x[xr(m)] wq^T, k[kr(m)] = x[xr(m)] wk^T, v[vr(m)] = x[xr(m)] wv^T."""
+def bd_qkv_proj(x, xr, wq, q, qr, wk, wv, k, kr, v, vr, *, M, ws=None, stream=None, guard=None):
+    """q[qr(m)] = x[xr(m)] wq^T, k[kr(m)] = x[xr(m)] wk^T, v[vr(m)] = x[xr(m)] wv^T.  guard: as
+    bd_block_attn."""
     lib = _lib.load()
     Nq, K = wq.shape
     Nkv = wk.shape[0]
     dt = _dt(wq)
     if ws is None:
         ws = workspace(lib.bd_qkv_proj_workspace_size(dt, M, K, Nq, Nkv), wq.device, "gemm")
-    st = lib.bd_qkv_proj(dt, M, K, _p(x), xr, _p(wq), Nq, _p(q), qr, _p(wk), _p(wv), Nkv, _p(k), kr, _p(v),
-                         vr, _p(ws), ws.numel(), _stream(stream))
-    _check("bd_qkv_proj", st)
+    args = (dt, M, K, _p(x), xr, _p(wq), Nq, _p(q), qr, _p(wk), _p(wv), Nkv, _p(k), kr, _p(v),
+            vr, _p(ws), ws.numel())
+    if guard is None:
+        _check("bd_qkv_proj", lib.bd_qkv_proj(*args, _stream(stream)))
+    else:
+        _check("bd_qkv_proj_guarded", lib.bd_qkv_proj_guarded(*args, _guard(guard), _stream(stream)))
 
 
 def bd_qkv_proj_rope_workspace_size(dtype, M, K, Nq, Nkv) -> int:

@@ -81,6 +81,20 @@ typedef struct bd_rows {
   int32_t offset;
 } bd_rows;
 
+/* An optional condition on a call, tested on the device when its kernels run:
+ * the call does nothing (its outputs keep their contents) when no bits[b],
+ * 0 <= b < n, has a bit of mask set.  In a refinement step: bits = the
+ * batch's mask bits, mask = the window's positions, so that a step slot past
+ * the end of its window (queued before the host knows the window is done)
+ * skips its work.  The struct is read on the host during the call; bits is a
+ * device pointer (8-byte aligned), 1 <= n <= 4096.  Calls that take a guard
+ * pointer accept NULL (always run). */
+typedef struct bd_guard {
+  const uint64_t* bits;
+  uint64_t mask;
+  int32_t n;
+} bd_guard;
+
 const char* bd_version(void);
 const char* bd_status_string(bd_status s);
 /* hipError_t of the last failed HIP call on this thread (0 if none). */
@@ -121,6 +135,14 @@ bd_status bd_block_attn(bd_dtype dt, int B, int Hq, int Hkv, int d, int D,
                         const void* k_blk, const void* v_blk, int n_blk,
                         float scale, void* o, float* lse,
                         void* workspace, size_t ws_bytes, void* stream);
+/* bd_block_attn with a guard (see bd_guard): nothing is computed or written
+ * when the guard's condition fails on the device. */
+bd_status bd_block_attn_guarded(bd_dtype dt, int B, int Hq, int Hkv, int d, int D,
+                                const void* q, int n_q, int q_off,
+                                const void* k_cache, const void* v_cache, const int32_t* kv_len, int cap,
+                                const void* k_blk, const void* v_blk, int n_blk,
+                                float scale, void* o, float* lse,
+                                void* workspace, size_t ws_bytes, const bd_guard* guard, void* stream);
 
 /* bd_block_attn_noalloc -- bd_block_attn without a workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture,
@@ -351,6 +373,11 @@ bd_status bd_linear(bd_dtype dt, int M, int N, int K,
                     const void* x, bd_rows xr, const void* w,
                     const void* res, bd_rows rr, void* y, bd_rows yr,
                     void* workspace, size_t ws_bytes, void* stream);
+/* bd_linear with a guard (see bd_guard). */
+bd_status bd_linear_guarded(bd_dtype dt, int M, int N, int K,
+                            const void* x, bd_rows xr, const void* w,
+                            const void* res, bd_rows rr, void* y, bd_rows yr,
+                            void* workspace, size_t ws_bytes, const bd_guard* guard, void* stream);
 
 /* A projection into the residual stream followed by the RMSNorm of the
  * result (a pre-norm layer's output projection or down projection and the
@@ -374,6 +401,12 @@ bd_status bd_qkv_proj(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
                       const void* wk, const void* wv, int Nkv,
                       void* k, bd_rows kr, void* v, bd_rows vr,
                       void* workspace, size_t ws_bytes, void* stream);
+/* bd_qkv_proj with a guard (see bd_guard). */
+bd_status bd_qkv_proj_guarded(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
+                              const void* wq, int Nq, void* q, bd_rows qr,
+                              const void* wk, const void* wv, int Nkv,
+                              void* k, bd_rows kr, void* v, bd_rows vr,
+                              void* workspace, size_t ws_bytes, const bd_guard* guard, void* stream);
 
 /* bd_qkv_proj followed by the rotary embedding of q and k (as bd_rope, with
  * H = Nq/d resp. Nkv/d heads; logical row m = b*n_rows + i sits at position

@@ -312,3 +312,26 @@ def test_per_sequence_window_calls_argument_errors():
     assert cp(n=65) == E and cp(rb=3000) == E and cp(mask=None) == E and cp(s1=FAKE) == E
     assert cp(s1=FAKE + 8, d1=FAKE) == E          # misaligned
     assert cp(B=0) == 0 and cp(n=0) == 0
+
+
+def test_guard_argument_errors():
+    """A guard's words must be given, 8-byte aligned and 1..4096 of them;
+    errors come back before any launch (no GPU touched)."""
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    R = _lib.BdRows
+    big = 1 << 30
+    G = _lib.BdGuard
+    for g in (G(None, 1, 4), G(FAKE + 4, 1, 4), G(FAKE, 1, 0), G(FAKE, 1, 4097)):
+        ref = ctypes.byref(g)
+        assert lib.bd_linear_guarded(1, 64, 3584, 3584, FAKE, R(64, 64, 0), FAKE, None, R(1, 1, 0), FAKE,
+                                     R(64, 64, 0), FAKE, big, ref, None) == E
+        assert lib.bd_qkv_proj_guarded(1, 64, 3584, FAKE, R(64, 64, 0), FAKE, 3584, FAKE, R(64, 64, 0), FAKE, FAKE,
+                                       512, FAKE, R(64, 64, 0), FAKE, R(64, 64, 0), FAKE, big, ref, None) == E
+        assert lib.bd_block_attn_guarded(1, 2, 28, 4, 128, 32, FAKE, 8, 8, FAKE, FAKE, FAKE, 64, FAKE, FAKE, 32,
+                                         0.1, FAKE, None, FAKE, big, ref, None) == E
+    # a valid guard on an empty problem is fine (nothing to launch)
+    ok = ctypes.byref(G(FAKE, 1, 4))
+    assert lib.bd_linear_guarded(1, 0, 3584, 3584, FAKE, R(1, 1, 0), FAKE, None, R(1, 1, 0), FAKE, R(1, 1, 0),
+                                 None, 0, ok, None) == 0
+    assert lib.bd_last_hip_error() == 0

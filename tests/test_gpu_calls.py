@@ -479,3 +479,73 @@ def test_linear_in_place_residual_tilings(M, N, K):
     rows_close(got[idx], ref, TOL["bf16"], f"linear M{M}")
     untouched = np.setdiff1d(np.arange(buf.shape[0]), idx)
     assert not got[untouched].any()
+
+
+# --------------------------------------------------------------------------
+# guards: the step's projections and attention skip a finished window
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dt,M,K,Nq,Nkv", [("bf16", 64, 3584, 3584, 512), ("bf16", 256, 3584, 3584, 512),
+                                           ("bf16", 8, 1536, 1536, 256), ("f32", 24, 256, 256, 128)])
+def test_guarded_projections(dt, M, K, Nq, Nkv):
+    """With the guard live (some bits[b] & mask != 0) the guarded calls give
+    exactly the unguarded results; with it dead they leave every output as it
+    was (K split over waves at 64 rows, over work-groups at 256 rows with its
+    reduction, fp32)."""
+    say(f"[guard] projections {dt} M{M} K{K}")
+    o = ops()
+    T = tdt(dt)
+    x = up(bi.normal(11, "h", (M, K), 0.5, dt), T)
+    wq, wk, wv = (up(bi.normal(11, n, (N, K), 0.02, dt), T) for n, N in (("Wq", Nq), ("Wk", Nkv), ("Wv", Nkv)))
+    wo = up(bi.normal(11, "Wo", (K, Nq), 0.02, dt), T)
+    r = up(bi.normal(12, "h", (M, K), 0.5, dt), T)
+    B = 5
+    bits = torch.zeros(B, dtype=torch.int64, device=DEV)
+    bits[3] = 1 << 17
+    dense = o.dense(M)
+    want = [torch.zeros(M, n, dtype=T, device=DEV) for n in (Nq, Nkv, Nkv)]
+    o.bd_qkv_proj(x, dense, wq, want[0], dense, wk, wv, want[1], dense, want[2], dense, M=M)
+    y_want = torch.zeros(M, K, dtype=T, device=DEV)
+    o.bd_linear(want[0], dense, wo, y_want, dense, M=M, res=r, rr=dense)
+    for mask, live in ((1 << 17, True), (0xFF << 16, True), (1 << 16, False), (0, False)):
+        got = [torch.full((M, n), 7.0, dtype=T, device=DEV) for n in (Nq, Nkv, Nkv)]
+        o.bd_qkv_proj(x, dense, wq, got[0], dense, wk, wv, got[1], dense, got[2], dense, M=M, guard=(bits, mask, B))
+        y = torch.full((M, K), 7.0, dtype=T, device=DEV)
+        o.bd_linear(want[0], dense, wo, y, dense, M=M, res=r, rr=dense, guard=(bits, mask, B))
+        torch.cuda.synchronize()
+        for g, w in zip(got + [y], want + [y_want]):
+            assert torch.equal(g, w) if live else bool((g == 7.0).all()), (mask, live)
+
+
+@pytest.mark.parametrize("dt,lens,n_q,q_off", [("bf16", [3000, 1500, 77], 8, 8), ("bf16", [16384] * 4, 32, 0),
+                                              ("f32", [64, 30], 8, 16)])
+def test_guarded_attention(dt, lens, n_q, q_off):
+    """bd_block_attn with a live guard equals the unguarded call bit for bit;
+    with a dead guard o and lse keep their contents (split keys and merge
+    included)."""
+    say(f"[guard] attention {dt} lens {lens[:3]}")
+    o_ = ops()
+    T = tdt(dt)
+    B, Hq, Hkv, d = len(lens), (28 if dt == "bf16" else 4), (4 if dt == "bf16" else 2), (128 if dt == "bf16" else 64)
+    lens = np.array(lens, dtype=np.int32)
+    cap = int(lens.max() + 64)
+    kc = up(bi.normal(3, "cache_k", (B, Hkv, cap, d), 0.02, dt), T)
+    vc = up(bi.normal(3, "cache_v", (B, Hkv, cap, d), 0.02, dt), T)
+    q = up(bi.normal(3, "q", (B, n_q, Hq, d), 0.02, dt), T)
+    kb = up(bi.normal(3, "blk_k", (B, 32, Hkv, d), 0.02, dt), T)
+    vb = up(bi.normal(3, "blk_v", (B, 32, Hkv, d), 0.02, dt), T)
+    L = up(lens)
+    o_want = torch.zeros(B, n_q, Hq, d, dtype=T, device=DEV)
+    l_want = torch.zeros(B, Hq, n_q, dtype=torch.float32, device=DEV)
+    o_.bd_block_attn(q, kc, vc, L, kb, vb, o_want, D=32, q_off=q_off, lse=l_want)
+    bits = torch.zeros(B, dtype=torch.int64, device=DEV)
+    bits[B - 1] = -1                          # every position masked
+    for mask, live in ((1 << 40, True), (0, False)):
+        bits_g = bits if live else torch.zeros_like(bits)
+        o = torch.full_like(o_want, 3.0)
+        lse = torch.full_like(l_want, 3.0)
+        o_.bd_block_attn(q, kc, vc, L, kb, vb, o, D=32, q_off=q_off, lse=lse, guard=(bits_g, mask or 1, B))
+        torch.cuda.synchronize()
+        if live:
+            assert torch.equal(o, o_want) and torch.equal(lse, l_want)
+        else:
+            assert bool((o == 3.0).all()) and bool((lse == 3.0).all())
