@@ -64,6 +64,16 @@ constexpr int kAttnThreads = 64 * kWaves;
 constexpr int kXcd = 8;                         // work-groups are dispatched round-robin over 8 XCDs
 constexpr int kMinChunk = BD_ATTN_MIN_CHUNK;    // keys per work item, lower bound
 constexpr int kTargetWGs = BD_ATTN_TARGET_WGS;  // one work-group per CU: the stage ring fills the LDS
+// Calls whose committed K/V are at most this large (they sit in the
+// last-level cache between steps, so their loads return sooner) run a
+// shorter stage ring, two work-groups per CU and twice the work-groups.
+#ifndef BD_ATTN_LIGHT_MAX_BYTES
+#define BD_ATTN_LIGHT_MAX_BYTES (96ll << 20)
+#endif
+#ifndef BD_ATTN_LIGHT_NS
+#define BD_ATTN_LIGHT_NS 4
+#endif
+constexpr int kLightNS = BD_ATTN_LIGHT_NS;
 constexpr int kQpwMax = BD_ATTN_QPW_MAX;        // query tiles per wave, at most (1, 2 or 4)
 constexpr float kLazyMax = 8.f;                 // running-max slack (log2 units), see the softmax
 
@@ -210,8 +220,11 @@ __device__ __forceinline__ void wait_stages(int later) {
 // global_load_lds_dwordx4: instruction i of a tile writes 64 consecutive
 // 16-byte slots, and each lane's global address is chosen so that its slot
 // receives the right chunk.
+// Waves per SIMD: two work-groups of 8 waves per CU for the short stage ring
+// of one query tile per wave (at most 128 VGPRs), else one work-group.
 template <int DH, int KT, int QPW, int NS, int CAUX>
-__global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : 2)) void attn_bf16_kernel(AttnK a) {
+__global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 ? 4 : 2))) void attn_bf16_kernel(
+    AttnK a) {
   constexpr int KCH = DH / 8;             // 16-byte chunks per key row
   constexpr int TU4 = KT * KCH;           // 16-byte slots per K (or V) tile
   constexpr int NI = TU4 / 64;            // DMA instructions per K (or V) tile
@@ -726,8 +739,12 @@ BdAttnPlan bd_attn_plan(bd_dtype dt, int B, int Hq, int Hkv, int d, int n_q, int
     p.nchunks = 1;
     return p;
   }
+  // one query tile per wave only (the register budget of two work-groups per
+  // CU): exact steps split into two query groups measured slower
+  p.light = (long long)B * Hkv * cap * d * 2 * 2 <= BD_ATTN_LIGHT_MAX_BYTES && p.qpw == 1;
   const long base = (long)B * Hkv * p.nqg;
-  int nch = (int)((kTargetWGs + base - 1) / base);
+  const long target = p.light ? 2 * kTargetWGs : kTargetWGs;
+  int nch = (int)((target + base - 1) / base);
   const int max_ch = (tmax + kMinChunk - 1) / kMinChunk;
   nch = nch < 1 ? 1 : (nch > max_ch ? max_ch : nch);
   int chunk = (tmax + nch - 1) / nch;
@@ -773,12 +790,14 @@ hipError_t bd_attn_launch(bd_dtype dt, const BdAttnPlan& p, const BdAttnArgs& x,
   a.g_mask = x.guard ? x.guard->mask : 0;
   a.g_n = x.guard ? x.guard->n : 0;
   const int n_wg = kXcd * a.nqg * ((a.n_units + kXcd - 1) / kXcd);
-#define BD_ATTN_LAUNCH(DH, QPW)                                                                           \
-  do {                                                                                                    \
-    if (p.stream_nt)                                                                                      \
-      hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS, 2>), dim3(n_wg), dim3(kAttnThreads), 0, s, a); \
-    else                                                                                                  \
-      hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS, 0>), dim3(n_wg), dim3(kAttnThreads), 0, s, a); \
+#define BD_ATTN_LAUNCH(DH, QPW)                                                                               \
+  do {                                                                                                        \
+    if (p.stream_nt)                                                                                          \
+      hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS, 2>), dim3(n_wg), dim3(kAttnThreads), 0, s, a);     \
+    else if (p.light)                                                                                         \
+      hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kLightNS, 0>), dim3(n_wg), dim3(kAttnThreads), 0, s, a); \
+    else                                                                                                      \
+      hipLaunchKernelGGL((attn_bf16_kernel<DH, kKT, QPW, kNS, 0>), dim3(n_wg), dim3(kAttnThreads), 0, s, a);     \
   } while (0)
   if (x.d == 128) {
     if (p.qpw == 1) BD_ATTN_LAUNCH(128, 1);

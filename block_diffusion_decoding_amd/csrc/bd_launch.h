@@ -26,6 +26,7 @@ struct BdAttnPlan {
   int chunk;      // keys per work item
   int nchunks;    // key chunks (max over sequences)
   int stream_nt;  // committed K/V loaded with the non-temporal hint (bf16)
+  int light;      // small call: short stage ring, two work-groups per CU (bf16)
   size_t part_o;  // workspace offsets / sizes in bytes
   size_t part_ml;
   size_t ws_bytes;
