@@ -139,6 +139,8 @@ def test_lmhead_confidence(name):
         rows_close(down(lg), ref, TOL[dt], f"logits {name}")
     ex = lm_stats_close(am.cpu().numpy(), down(conf), down(mx), down(lse), ref, TOL[dt], name)
     say(f"    exempt argmax rows: {ex}")
+    # the measured tie band leaves almost every row compared exactly
+    assert ex <= max(2, M // 20), f"{name}: {ex} of {M} argmax rows exempt"
 
 
 @pytest.mark.parametrize("M", [4, 80, 300])

@@ -257,11 +257,13 @@ def test_small_bf16_model_steps_match_the_oracle(B):
         wl = dec.last
         am, cf = wl["argmax"].cpu().numpy().reshape(-1), wl["conf"].cpu().numpy().reshape(-1)
         cand = before[:, S:2 * S].reshape(-1)
-        lm_stats_close(am[cand], cf[cand], None, None, logits[cand], tol, f"{kind} LM head")
+        mx = wl["maxl"].float().cpu().numpy().reshape(-1)
+        lm_stats_close(am[cand], cf[cand], mx[cand], None, logits[cand], tol, f"{kind} LM head")
         # the window's decisions: exact except near-threshold confidences and
         # fallback ties (where exactly one tied candidate must be picked)
         n_cmp, n_tie = unmask_close(dec.masked_host(), np.stack([q.masked for q in seqs]), before,
-                                    [r.conf for r in res], S, cfg.tau, tol, f"{kind} unmask")
+                                    [r.conf for r in res], S, cfg.tau, tol, f"{kind} unmask",
+                                    got_conf_win=wl["conf"].float().cpu().numpy())
         say(f"    {kind}: {n_cmp} candidate decisions compared, {n_tie} fallback ties")
         dec.set_tokens(np.stack([q.tokens for q in seqs]), np.stack([q.masked for q in seqs]))
 

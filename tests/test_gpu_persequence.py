@@ -66,7 +66,8 @@ def test_per_sequence_progression_teacher_forced(graph):
             what = f"step {n} seq {b} window {s_b} {kind}"
             lm_stats_close(dec.argmax[b].cpu().numpy(), down(dec.conf[b]), down(dec.maxl[b]), down(dec.lse[b]),
                            ref, rtol, what)
-            unmask_close(got[b:b + 1], q.masked[None], before[None], [res.conf], s_b * S, tau, rtol, what)
+            unmask_close(got[b:b + 1], q.masked[None], before[None], [res.conf], s_b * S, tau, rtol, what,
+                         got_conf_win=[down(dec.conf[b])])
         dec.set_tokens(np.stack([q.tokens for q in seqs]), np.stack([q.masked for q in seqs]))
         n += 1
         assert n < 4 * D

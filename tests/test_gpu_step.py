@@ -42,7 +42,7 @@ def compare_step(cfg, dec, m, seqs, results, kind, s, S, before_masked, what, se
     # unmask decisions
     ref_masked = np.stack([q.masked for q in seqs])
     n_cmp, n_tie = unmask_close(dec.masked_host()[ids], ref_masked, before_masked, [r.conf for r in results], s * S,
-                                cfg.tau, rtol, f"{what} unmask")
+                                cfg.tau, rtol, f"{what} unmask", got_conf_win=down(w["conf"])[ids])
     return [len(r.picked) for r in results]
 
 

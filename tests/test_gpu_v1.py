@@ -48,7 +48,7 @@ def test_v1_generation_teacher_forced(case, mode):
                 lm_stats_close(am[b], cf[b], mx[b], lse[b], R.lm_logits(model.Wlm, r.src), rtol, f"{what} seq {b}")
             got = ((dec.mask_bits_host()[:, None] >> np.arange(D, dtype=np.uint64)) & np.uint64(1)).astype(bool)
             ref = np.stack([q.masked[lo:lo + D] for q in seqs])
-            unmask_close(got, ref, before, [r.conf for r in res], 0, tau, rtol, what)
+            unmask_close(got, ref, before, [r.conf for r in res], 0, tau, rtol, what, got_conf_win=cf)
             passes += int((before & ~ref).sum())
             # teacher forcing: the oracle's block state
             dec.tok_blk.copy_(torch.from_numpy(np.stack([q.tokens[lo:lo + D] for q in seqs]).astype(np.int32)))
