@@ -94,6 +94,21 @@ __device__ __forceinline__ int seg_of(const GemmS& a, int gt) {
   return gt >= a.tb[2] ? 2 : (gt >= a.tb[1] ? 1 : 0);
 }
 
+// Rotated segments in the K-split-over-waves kernel: tile tt of a q or k
+// segment is a "pair tile" whose rows 0..7 are the output columns
+// h*d + 8t .. +7 of head h = tt / (d/16), t = tt % (d/16), and whose rows
+// 8..15 are their rotation partners h*d + d/2 + 8t .. +7.  The rotate-half
+// pairs (j, j + d/2) then sit in lanes c and c ^ 8 of the same 16-lane group
+// of an MFMA result, so the rotation needs no other work-group's columns.
+// Needs d % 16 == 0.
+__device__ __forceinline__ int pair_tile_col(int tt, int r, int d) {
+  const int th = d >> 4, h = tt / th, t = tt - h * th;
+  return h * d + (r < 8 ? 8 * t + r : (d >> 1) + 8 * t + r - 8);
+}
+__device__ __forceinline__ bool rotated_seg(const GemmS& a, int sg) {
+  return a.mode == BD_GEMM_ROPE && sg < 2 && (a.d & 15) == 0;
+}
+
 // Work-group (blockIdx.x, row block blockIdx.y, K slice blockIdx.z) owns
 // scheduling units [g0, g0 + ng) of the T/G units (G = 1: a 16-column tile;
 // G = 2 in SwiGLU mode: a gate tile and the matching up tile, adjacent in the
@@ -363,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kwave_kernel(GemmS a, int ny
           row = a.w[0] + (size_t)((gt & 1) ? a.N[0] + c : c) * K + koff;
         } else {
           const int sg = seg_of(a, gt);
-          int c = (gt - a.tb[sg]) * 16 + r;
+          int c = rotated_seg(a, sg) ? pair_tile_col(gt - a.tb[sg], r, a.d) : (gt - a.tb[sg]) * 16 + r;
           c = c < a.N[sg] ? c : a.N[sg] - 1;
           row = a.w[sg] + (size_t)c * K + koff;
         }
@@ -457,6 +472,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kwave_kernel(GemmS a, int ny
     const int i = p / NT, j = p % NT;
     if (j >= n) continue;
     const int gt = t0 + j, sg = seg_of(a, gt);
+    if (rotated_seg(a, sg)) {
+      // pair tile: lane c < 8 holds x1 = column j of the head's first half,
+      // lane c ^ 8 its partner x2 = column j + d/2; angle pos * theta^(-2j/d)
+      // in fp64, the rotation in fp32 (as the K-split reduction does)
+      const bd_f32x4 v = total(p);
+      const int tt = gt - a.tb[sg], th = a.d >> 4, hd = tt / th, jf = 8 * (tt - hd * th) + (l16 & 7);
+      const bool first = l16 < 8;
+      const int col = hd * a.d + (first ? jf : (a.d >> 1) + jf);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float other = __shfl_xor(v[r], 8);
+        const int m = m0 + i * 16 + 4 * g + r;
+        if (m >= a.M) continue;
+        const double pos = (double)(a.pos_base[m / a.n_rows] + a.pos_off + m % a.n_rows);
+        const double ang = pos * exp2(-(2.0 * jf / a.d) * a.log2_theta);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const float c = (float)cs, sv = (float)sn;
+        const float x1 = first ? v[r] : other, x2 = first ? other : v[r];
+        const float y = first ? x1 * c - x2 * sv : x2 * c + x1 * sv;
+        a.y[sg][(size_t)bd_map_row(a.yr[sg], m) * a.N[sg] + col] = (uint16_t)bd_f2bf(y);
+      }
+      continue;
+    }
     const int col = (gt - a.tb[sg]) * 16 + l16;
     if (col >= a.N[sg]) continue;
     const bd_f32x4 v = total(p);
@@ -1182,7 +1221,9 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
   if (post_norm != nullptr && !fused_norm)
     return bd_rmsnorm_launch(dt, M, segs[0].N, segs[0].y, segs[0].yr, post_norm->eps, post_norm->h, post_norm->hr, s);
   // rotary embedding as its own pass where the projection had no reduction
-  if (mode == BD_GEMM_ROPE && (dt == BD_F32 || p.ksplit == 1)) {
+  // (the K-split-over-waves kernel rotates its pair tiles itself)
+  const bool rotated_in_kernel = dt == BD_BF16 && p.kw_nt != 0 && mode == BD_GEMM_ROPE && rope->d % 16 == 0;
+  if (mode == BD_GEMM_ROPE && (dt == BD_F32 || p.ksplit == 1) && !rotated_in_kernel) {
     for (int i = 0; i < 2 && i < nseg; ++i) {
       hipError_t e = bd_rope_launch(dt, M / rope->n_rows, rope->n_rows, segs[i].N / rope->d, rope->d, segs[i].y,
                                     segs[i].yr, rope->pos_base, rope->pos_off, rope->theta, s);

@@ -90,11 +90,13 @@ def test_row_ops_at_widths_off_the_vector_path(dtype, hidden, inter):
 @pytest.mark.parametrize("dtype,B,n,Hq,Hkv,d,K", [("bf16", 16, 8, 12, 2, 128, 1536), ("bf16", 3, 8, 4, 2, 64, 512),
                                                   ("bf16", 2, 4, 4, 2, 64, 256), ("f32", 3, 8, 4, 2, 64, 256),
                                                   ("bf16", 16, 32, 12, 2, 128, 1536),
-                                                  ("bf16", 128, 32, 12, 2, 128, 512)])
+                                                  ("bf16", 128, 32, 12, 2, 128, 512),
+                                                  ("bf16", 8, 8, 28, 4, 128, 3584), ("bf16", 5, 8, 6, 2, 64, 1024)])
 def test_qkv_proj_rope_matches_projection_then_rotation(dtype, B, n, Hq, Hkv, d, K):
     """q and k rotated at their absolute positions, v plain; the K-split path
-    rotates in the reduction, the others (one slice; 256-row tiles at 4096
-    rows) in a rotary pass."""
+    rotates in the reduction, the K split over waves (128 and 64 rows) in its
+    epilogue on pair tiles, the others (256-row tiles at 4096 rows) in a
+    rotary pass."""
     say(f"[model] qkv+rope {dtype} B{B} n{n} Hq{Hq} Hkv{Hkv} d{d} K{K}")
     o = ops()
     T = tdt(dtype)
