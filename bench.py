@@ -39,6 +39,7 @@ for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
     os.environ[_v] = str(_CORES)
 
 import argparse
+import collections
 import hashlib
 import json
 import sys
@@ -290,72 +291,79 @@ class Loop:
             self._next_window()
         return steps
 
-    def queued(self, budget: int) -> int:
-        """At most `budget` refinement steps queued with one wait at the end.
-        At a window start with a window's S slots left in the budget: whole
-        windows back to back (a window's S slots always finish it), with
-        their commits and the next block's set-up, over at most two blocks
-        (the two ring parities); otherwise the slots of the current window
-        from the next one on, at most `budget` of them.  Returns the steps
-        taken (slots past the end of a window are not steps)."""
+    def pipelined(self, n: int, stop_blk=None):
+        """Exactly n refinement steps, queued ahead of the host.  A cursor
+        walks the step slots in order (S per window; a window's S slots
+        always finish it, so the cursor moves on without looking at the
+        bits) and queues as many slots as the worst case allows: slots in
+        flight (each may be a step) never exceed the steps still to take.
+        Whole windows from their first slot go as one graph, other runs as
+        per-slot graphs.  The host waits only for the oldest run in flight
+        when the budget is used up (or the ring parity of the cursor's block
+        is still unread: at most two blocks in flight) and books it; runs
+        that turn out to hold slots past the end of their window free that
+        much budget.  Requires windows_complete(S).  With stop_blk (from a
+        block start): whole blocks until block stop_blk starts, n ignored."""
         cfg, dec = self.cfg, self.dec
         S, nw = cfg.S, cfg.D // cfg.S
-        units = []                       # (block, window, first slot, end slot, bits before the first slot or None)
-        whole = self.slot == 0 and budget >= S
-        if whole:
-            blk0 = self.blk
-            while self.slot == 0 and budget >= S and self.blk < blk0 + 2:
-                before = self.bits if (not units or self.s == 0) else None   # else: the previous window's last bits
-                dec.run_window(self.s, S, cfg.tau, wait=False, parity=self.blk % 2)
-                units.append((self.blk, self.s, 0, S, before))
-                budget -= S
-                self.s += 1
-                if self.s == nw:
-                    dec.commit()
-                    self._new_block()        # queued copies; its bookkeeping follows the wait
-        else:
-            k = min(budget, S - self.slot)
-            dec.run_slots(self.s, S, cfg.tau, self.slot, self.slot + k, parity=self.blk % 2)
-            units.append((self.blk, self.s, self.slot, self.slot + k, self.bits))
-        dec.wait()
-        steps = 0
-        prev_blk, cur = units[0][0], None
-        for blk, s, i0, i1, before in units:
-            if blk != prev_blk:              # the previous block ended with its last window
-                self._book_block()
-                prev_blk = blk
+        if stop_blk is not None:
+            assert self.slot == 0 and self.s == 0
+            n = 1 << 62
+        left = n                          # steps not yet booked
+        worst = 0                         # slots in flight (each may be a step)
+        pend = collections.deque()        # runs in flight: (event, block, window, first slot, end slot)
+        cur = self.bits                   # mask bits after the last booked slot
+        while left > 0:
+            if stop_blk is not None and self.blk >= stop_blk and not pend:
+                break
+            room = left - worst
+            if (room > 0 and (not pend or pend[0][1] >= self.blk - 1)
+                    and (stop_blk is None or self.blk < stop_blk)):
+                k = min(room, S - self.slot)
+                if self.slot == 0 and k == S:
+                    dec.run_window(self.s, S, cfg.tau, wait=False, parity=self.blk % 2)
+                else:
+                    dec.run_slots(self.s, S, cfg.tau, self.slot, self.slot + k, parity=self.blk % 2)
+                pend.append((dec.fence(), self.blk, self.s, self.slot, self.slot + k))
+                worst += k
+                self.slot += k
+                if self.slot == S:
+                    self.s, self.slot = self.s + 1, 0
+                    if self.s == nw:
+                        dec.commit()
+                        self._new_block()  # queued copies; the block is booked when read back
+                continue
+            ev, blk, s, i0, i1 = pend.popleft()
+            ev.synchronize()
             ring = dec.window_bits(s, S, blk % 2)[i0:i1]
-            steps += self._account(ring, s, cur if before is None else before)
+            before = self.full if (s == 0 and i0 == 0) else cur
+            left -= self._account(ring, s, before)
+            worst -= i1 - i0
             cur = ring[-1]
-            if whole and (cur & self.wmask[s]).any():
-                raise RuntimeError(f"window {s} still has masked positions after its {S} slots")
-        if whole:
-            if self.s == 0:                  # the last window ended a block
-                self._book_block()
-            else:
-                self.bits = cur
-                self.first, self.slot = True, 0
-        else:
-            self.bits = cur
-            self.first = False
-            self.slot = units[0][3]
-            if not (cur & self.wmask[self.s]).any():
-                self._next_window()
-        return steps
+            if i1 == S:
+                if (cur & self.wmask[s]).any():
+                    raise RuntimeError(f"window {s} still has masked positions after its {S} slots")
+                if s == nw - 1:
+                    self._book_block()
+            if not pend:
+                self.bits = self.full.copy() if (self.s == 0 and self.slot == 0) else cur
+                if self.slot > 0 and not (cur & self.wmask[self.s]).any():
+                    self._next_window()   # the cursor's window ended early: skip its other slots
+        self.first = self.slot == 0
 
     def run(self, n: int, windows: bool):
-        """Exactly n refinement steps.  With window graphs: queued runs
-        (whole windows back to back, or slots of one window) with one wait
-        each when a window's slots always finish it, else window graphs while
-        at least a graph's slots remain; single steps otherwise."""
+        """Exactly n refinement steps.  With window graphs: whole windows
+        queued ahead of the host (pipelined) when a window's slots always
+        finish it, else window graphs while at least a graph's slots remain;
+        single steps otherwise."""
         left = n
         S = self.cfg.S
         slots = self.dec.slots(S)
-        piped = windows and self.dec.windows_complete(S)
+        if windows and self.dec.windows_complete(S):
+            self.pipelined(n)
+            return
         while left > 0:
-            if piped:
-                left -= self.queued(left)
-            elif windows and self.first and left >= slots:
+            if windows and self.first and left >= slots:
                 left -= self.window()
             else:
                 self.step()
@@ -741,20 +749,19 @@ def extras_persequence(w3, n_blocks=4):
     dec.capture(cfg.S, cfg.tau)
     loop = Loop(dec, cfg, plants)
 
-    def advance():
+    def advance_to(blk):
         if dec.windows_complete(cfg.S):
-            loop.queued(cfg.D)
-        elif loop.first:
-            loop.window()
-        else:
-            loop.step()
-    while loop.blk < 1:                           # warm-up block
-        advance()
+            loop.pipelined(0, stop_blk=blk)
+        while loop.blk < blk:
+            if loop.first:
+                loop.window()
+            else:
+                loop.step()
+    advance_to(1)                                 # warm-up block
     torch.cuda.synchronize()
     s0 = loop.steps
     t0 = time.perf_counter()
-    while loop.blk < 1 + n_blocks:
-        advance()
+    advance_to(1 + n_blocks)
     torch.cuda.synchronize()
     t_ls = time.perf_counter() - t0
     tokens = n_blocks * cfg.B * cfg.D

@@ -491,6 +491,13 @@ class BlockDecoder:
         """Wait for the queued steps (their mask bits are then on the host)."""
         self._bits_ev.synchronize()
 
+    def fence(self) -> torch.cuda.Event:
+        """An event recorded after the work queued so far: once it has
+        completed, the rings written by that work can be read."""
+        ev = torch.cuda.Event()
+        ev.record()
+        return ev
+
     def window_bits(self, s: int, S: int, parity: int = 0) -> np.ndarray:
         """Mask bits after every slot of window s's last run [slots(S), B]
         (uint64); valid once that run has finished (run_window or wait)."""

@@ -1,9 +1,10 @@
 """Host logic of bench.py's decode loop, on the CPU with a stand-in decoder
 whose steps unmask positions deterministically from the mask bits alone:
-queued runs (whole windows back to back over two blocks with two ring
-parities, or slots of one window, one wait each) book exactly the steps,
+pipelined runs (whole windows queued ahead of the host over at most two
+blocks with two ring parities, the oldest read back while later ones run;
+slots of one window with one wait at the ends) book exactly the steps,
 tokens, commits and per-block schedules of the same loop taken one step at
-a time."""
+a time, and book them from rings no later block has overwritten."""
 from types import SimpleNamespace
 
 import numpy as np
@@ -23,6 +24,8 @@ class FakeDecoder:
         self.bits = np.zeros(B, np.uint64)
         self.blk = -1
         self.rings = np.zeros((2, D // S, S, B), np.uint64)
+        self.inflight = []                          # blocks of the runs queued and not yet read back
+        self.max_inflight = 0
         self.commits = 0
         self.log = []
 
@@ -66,18 +69,35 @@ class FakeDecoder:
         for i in range(S):
             self._step(s)
             self.rings[parity, s, i] = self.bits
-        return self.rings[parity, s].copy() if wait else None
+        if wait:
+            return self.rings[parity, s].copy()
+        self._queued()
+        return None
+
+    def fence(self):
+        return SimpleNamespace(synchronize=lambda: None)
 
     def run_slots(self, s, S, tau, i0, i1, parity=0):
         for i in range(i0, i1):
             self._step(s)
             self.rings[parity, s, i] = self.bits
+        self._queued()
 
     def wait(self):
         pass
 
     def window_bits(self, s, S, parity=0):
+        # one read per queued run (the loop books runs in order); a ring row
+        # overwritten by a later block before its run was booked would make
+        # the booking differ from the one-step-at-a-time loop
+        self.inflight.pop(0)
         return self.rings[parity, s].copy()
+
+    def _queued(self):
+        self.inflight.append(self.blk)
+        self.max_inflight = max(self.max_inflight, len(self.inflight))
+        # a block's windows write the ring parity of the block two back
+        assert len(set(self.inflight)) <= 2, "more than two blocks in flight"
 
 
 def _state(loop):
@@ -86,19 +106,22 @@ def _state(loop):
 
 
 @pytest.mark.parametrize("B,S", [(8, 8), (3, 4), (5, 16)])
-def test_queued_runs_book_like_single_steps(B, S):
+def test_pipelined_runs_book_like_single_steps(B, S):
     cfg = SimpleNamespace(B=B, D=32, S=S, tau=0.9)
     a = bench.Loop(FakeDecoder(B, 32, S), cfg, [None])
     b = bench.Loop(FakeDecoder(B, 32, S), cfg, [None])
-    for n in [10, 60, 7, 1, 33, 64, 5, 120, 3]:
-        a.run(n, windows=True)            # queued runs
+    for n in [10, 60, 7, 1, 33, 64, 5, 120, 3, 400]:
+        a.run(n, windows=True)            # pipelined runs
         b.run(n, windows=False)           # one step and one wait at a time
         assert _state(a) == _state(b), n
         assert a.dec.commits == b.dec.commits == a.commits
+        assert a.dec.inflight == []       # every queued window read back before run() returns
         # the same real steps on the device, in order (queued runs add only
         # slots past the end of a window)
         assert b.dec.log == _real_steps(a.dec.log, b.dec.log)
     assert a.commits >= 3
+    # runs really were queued ahead of the read-backs (up to two blocks)
+    assert a.dec.max_inflight > 1
 
 
 def _real_steps(log_a, log_b):
@@ -112,11 +135,26 @@ def _real_steps(log_a, log_b):
     return out
 
 
-def test_queued_runs_stop_at_the_second_block():
-    """One queued run never starts the windows of a block whose ring parity
-    is still unread (at most two blocks per run)."""
+def test_pipelined_runs_keep_at_most_two_blocks_in_flight():
+    """A window is queued only while no window of the block two back is
+    unread (its ring parity): with a large budget the GPU is never more than
+    two blocks ahead of the host's read-backs."""
     cfg = SimpleNamespace(B=2, D=32, S=8, tau=0.9)
     dec = FakeDecoder(2, 32, 8)
     loop = bench.Loop(dec, cfg, [None])
-    loop.queued(10 ** 6)
-    assert loop.commits == 2 and loop.blk == 2 and dec.blk == 2 and loop.s == 0
+    loop.run(200, windows=True)
+    assert loop.steps == 200 and dec.inflight == []
+    assert dec.max_inflight > 4
+
+
+def test_pipelined_whole_blocks_book_like_single_steps():
+    """stop_blk: whole blocks, pipelined, until a given block starts."""
+    cfg = SimpleNamespace(B=3, D=32, S=8, tau=0.9)
+    a = bench.Loop(FakeDecoder(3, 32, 8), cfg, [None])
+    b = bench.Loop(FakeDecoder(3, 32, 8), cfg, [None])
+    for blk in (1, 4, 5):
+        a.pipelined(0, stop_blk=blk)
+        while b.blk < blk:
+            b.step()
+        assert a.blk == blk and a.dec.inflight == []
+        assert _state(a) == _state(b), blk
