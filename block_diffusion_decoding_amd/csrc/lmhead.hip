@@ -15,7 +15,9 @@
 //
 // bf16, up to 64 rows: streaming MFMA GEMM, persistent over the vocabulary
 // (lm_stream_kernel): weights streamed once from HBM through a 3-stage
-// asynchronous global->LDS pipeline, every work-group an equal share.
+// asynchronous global->LDS pipeline, every work-group an equal share; each
+// lane keeps running statistics of its own columns across the passes, and
+// the lanes and waves of a row meet once at the end.
 // bf16, more rows (a whole batch's window or block, where the product is
 // MFMA-bound): 256-row work-group tiles, see lm_big_kernel.
 // fp32: plain VALU kernel.
@@ -41,8 +43,16 @@ constexpr int kThreads = 256;
 #ifndef BD_LM_NS
 #define BD_LM_NS 3
 #endif
+// Work-groups of the streaming kernel.  For rows of 2048 and more columns
+// one per CU: the weight stream runs faster with one stream per CU (a
+// global->LDS read probe of the 7B head's 1.09 GB in this kernel's order:
+// 158 us with 256 work-groups, 173 us with 512); narrower rows (fewer chunks
+// per pass) keep two per CU.
 #ifndef BD_LM_STREAM_WGS
-#define BD_LM_STREAM_WGS 512
+#define BD_LM_STREAM_WGS 256
+#endif
+#ifndef BD_LM_STREAM_WGS_NARROW
+#define BD_LM_STREAM_WGS_NARROW 512
 #endif
 // Cache policy of the streaming kernel's W loads: 2 = non-temporal.  The
 // LM-head weights are read once per step and are far larger than the caches;
@@ -52,11 +62,15 @@ constexpr int kThreads = 256;
 #ifndef BD_LM_AUX
 #define BD_LM_AUX 2
 #endif
+// waves per work-group of the streaming kernel
+#ifndef BD_LM_WAVES
+#define BD_LM_WAVES 4
+#endif
 constexpr int kNTW = BD_LM_NTW;  // 16-column tiles per pass (bf16, up to 64 rows)
 constexpr int kNS = BD_LM_NS;    // pipeline stages (bf16)
-constexpr int kStreamWGs = BD_LM_STREAM_WGS;  // work-groups of the streaming kernel: two per CU
-// s_waitcnt immediate waiting for lgkmcnt(0) only
-constexpr int kLgkm0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
+constexpr int kStreamWGs = BD_LM_STREAM_WGS;         // rows of >= 2048 columns
+constexpr int kStreamWGsNarrow = BD_LM_STREAM_WGS_NARROW;
+constexpr int kLmWaves = BD_LM_WAVES;
 constexpr int kF32Rows = 16;  // rows per work-group (fp32)
 
 struct LmK {
@@ -100,6 +114,63 @@ __device__ __forceinline__ const uint16_t* lm_row_ptr(const LmK& a, int m, int r
   return (m < Meff && r >= 0 && r < a.n_src) ? a.h + (size_t)r * a.hidden : nullptr;
 }
 
+// Running statistics of one lane's logits of one row over the passes: the
+// exponentials use a lazy offset (raised only when a logit exceeds it by more
+// than kLmLazy, so every term stays below 2^(kLmLazy*log2 e) and most passes
+// need no rescale), next to the exact maximum and its lowest column.  The
+// lanes' statistics meet once, at the end of the work-group's range.
+constexpr float kLmLazy = 5.5f;
+struct LmLane {
+  float off;  // offset of the sum (-inf until a finite logit is seen)
+  float s;    // sum of exp(v - off)
+  float bv;   // largest logit
+  int idx;    // its lowest column
+};
+template <int N>
+__device__ __forceinline__ void lm_lane_update(LmLane& st, const float (&v)[N], const int (&col)[N]) {
+  float mt = v[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) mt = fmaxf(mt, v[j]);
+  if (mt > st.off + kLmLazy) {  // -inf + kLmLazy is -inf: the first finite logit sets the offset
+    st.s *= bd_exp2((st.off - mt) * BD_LOG2E);
+    st.off = mt;
+  }
+  const float mu = st.off == BD_NEG_INF ? 0.f : st.off;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    st.s += bd_exp2((v[j] - mu) * BD_LOG2E);
+    if (v[j] > st.bv) {  // columns arrive in increasing order: the first maximum is the lowest
+      st.bv = v[j];
+      st.idx = col[j];
+    }
+  }
+}
+// (max, lowest argmax, sum of exp(v - max)) of a row over the 16 lanes of its group
+__device__ __forceinline__ BdArgStat lm_lane_row(const LmLane& st) {
+  const float m = bd_row16_max(st.bv);
+  const float mu = m == BD_NEG_INF ? 0.f : m;
+  const float sl = st.off == BD_NEG_INF ? 0.f : st.s * bd_exp2((st.off - mu) * BD_LOG2E);
+  const int il = (st.bv == m && m != BD_NEG_INF) ? st.idx : INT_MAX;
+  return BdArgStat{m, bd_row16_min(il), bd_row16_sum(sl)};
+}
+
+template <int MT, int NWV>
+struct LmCfg {  // the stage layout of stream_gemm.h over NWV waves
+  static constexpr int NS = kNS;
+  static constexpr int MTW = MT < 2 ? MT : 2;  // row tiles per wave
+  static constexpr int WM = MT / MTW;          // waves along the rows
+  static constexpr int WN = NWV / WM;          // waves along the columns
+  static constexpr int NTP = kNTW / WN;        // column tiles per wave
+  static constexpr int KSC = 2;                // 32-wide k-steps per chunk
+  static constexpr int KC = 64;                // k per chunk
+  static constexpr int FR = 2 * (kNTW + MT);   // DMA instructions per stage (1 KiB each)
+  static constexpr int LW = (FR + NWV - 1) / NWV, LW_LO = FR / NWV;  // per wave (waves >= FR % NWV: LW_LO)
+  static constexpr int WI = 2 * kNTW / NWV;    // W instructions per wave
+  static constexpr int STAGE_U4 = FR * 64;
+  static_assert(kNTW % WN == 0 && (2 * kNTW) % NWV == 0, "split");
+  static_assert(NS >= 2 && NS <= 5, "stages");
+};
+
 // Streaming LM head for up to 64 rows, persistent over the vocabulary.
 // Work-group w of nwg owns the 16-column tiles [w*T/nwg, (w+1)*T/nwg),
 // T = ceil(V/16), and walks them in P passes of at most kNTW tiles (equal
@@ -107,16 +178,17 @@ __device__ __forceinline__ const uint16_t* lm_row_ptr(const LmK& a, int m, int r
 // all of them finish together.  The 64-wide K chunks of all its passes form
 // one stream of pipeline stages (stage s: pass s / nch, chunk s % nch): the
 // first stages of a pass are in flight while the previous pass finishes its
-// MFMAs and reduces its logits.  A pass's statistics are folded into one
-// running (max, argmax, sum) per row, stored once at the end.
+// MFMAs and folds its logits into each lane's running statistics (LmLane: no
+// cross-lane work and no barrier between passes); the lanes and waves of a
+// row meet once at the end, and one (max, argmax, sum) per row is stored.
 // Stage layout as in stream_gemm.h: kNTW W tiles then MT X tiles, each 16
 // rows x 64 k (2 KiB, two whole-line DMA instructions, XOR-swizzled).  A pass
 // with fewer than kNTW tiles fills its unused W slots from row 0 of h (an L2
 // hit), so every stage issues the same loads per wave and the waits count
 // exactly; the epilogue ignores the logits of those slots.
-template <int MT>
-__global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
-  using C = bd_stream::Cfg<MT, kNTW, kNS>;
+template <int MT, int NWV>
+__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void lm_stream_kernel(LmK a, int P) {
+  using C = LmCfg<MT, NWV>;
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
   __shared__ BdArgStat red[C::WN * MT * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -137,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
   int xm[C::LW], xi[C::LW];
 #pragma unroll
   for (int i = 0; i < C::LW; ++i) {  // row indices first: their loads are in flight together
-    const int f = wave + 4 * i, t = f >> 1;
+    const int f = wave + NWV * i, t = f >> 1;
     xm[i] = m0 + (t - kNTW) * 16 + 8 * (f & 1) + lrow;
     xi[i] = (f < C::FR && t >= kNTW) ? lm_row_index(a, xm[i]) : 0;
   }
@@ -152,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
     const int b = pass_begin(p), n = pass_begin(p + 1) - b;
 #pragma unroll
     for (int i = 0; i < C::LW; ++i) {
-      const int f = wave + 4 * i, t = f >> 1;
+      const int f = wave + NWV * i, t = f >> 1;
       if (f < C::FR && t < kNTW) {
         const int col = (b + t) * 16 + 8 * (f & 1) + lrow;
         src[i] = t >= n ? hdummy : a.w + (size_t)(col < a.V ? col : 0) * K + 8 * lkb;
@@ -163,24 +235,23 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
   set_pass(0);
   auto issue_next = [&]() {
     uint4* st = sbuf + (iss % C::NS) * C::STAGE_U4;
-    // instructions i < kNTW/2 load W tiles (for every wave), the rest X rows
-    static_assert(kNTW % 2 == 0, "W instructions per wave");
+    // instructions i < WI load W tiles (for every wave), the rest X rows
 #pragma unroll
-    for (int i = 0; i < kNTW / 2; ++i)
+    for (int i = 0; i < C::WI; ++i)
       __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ich * C::KC),
-                                       (bd_stream::lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, BD_LM_AUX);
+                                       (bd_stream::lds_void_t*)(st + (wave + NWV * i) * 64), 16, 0, BD_LM_AUX);
 #pragma unroll
-    for (int i = kNTW / 2; i < C::LW; ++i)
-      if (C::FR % 4 == 0 || wave + 4 * i < C::FR)
+    for (int i = C::WI; i < C::LW; ++i)
+      if (C::FR % NWV == 0 || wave + NWV * i < C::FR)
         __builtin_amdgcn_global_load_lds((bd_stream::glb_void_t*)(src[i] + (size_t)ich * C::KC),
-                                         (bd_stream::lds_void_t*)(st + (wave + 4 * i) * 64), 16, 0, 0);
+                                         (bd_stream::lds_void_t*)(st + (wave + NWV * i) * 64), 16, 0, 0);
     ++iss;
     if (++ich == nch) {
       ich = 0;
       if (++ip < P) set_pass(ip);
     }
   };
-  const bool more = wave < C::FR % 4;  // this wave issues LW (else LW_LO) loads per stage
+  const bool more = wave < C::FR % NWV;  // this wave issues LW (else LW_LO) loads per stage
   const int fo0 = bd_stream::frag_offset(lane, 0) / 16, fo1 = bd_stream::frag_offset(lane, 1) / 16;
 
   bd_f32x4 acc[C::MTW][C::NTP];
@@ -188,7 +259,11 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
   for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
     for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
-  BdArgStat run{BD_NEG_INF, INT_MAX, 0.f};  // threads tid < MT*16: row m0 + tid over the passes so far
+  LmLane ls[C::MTW][4];  // this lane's columns of rows m0 + (wm*MTW + i)*16 + 4g + r, over the passes
+#pragma unroll
+  for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls[i][r] = LmLane{BD_NEG_INF, 0.f, BD_NEG_INF, INT_MAX};
 
   // the skip test's bits load with the row indices (at most 64 sequences)
   uint64_t skip_word = 0;
@@ -259,6 +334,8 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
             if (m < Meff && cok[j]) a.logits[(size_t)m * a.V + col[j]] = acc[i][j][r];
         }
     }
+    // no cross-lane work here: each lane folds its logits into its own
+    // running statistics, so the next pass's stages keep streaming
 #pragma unroll
     for (int i = 0; i < C::MTW; ++i) {
 #pragma unroll
@@ -266,25 +343,30 @@ __global__ __launch_bounds__(kThreads, 2) void lm_stream_kernel(LmK a, int P) {
         float v[C::NTP];
 #pragma unroll
         for (int j = 0; j < C::NTP; ++j) v[j] = cok[j] ? acc[i][j][r] : BD_NEG_INF;
-        const BdArgStat rs = bd_row16_stat(v, col);
-        if (l16 == 0) red[wn * (MT * 16) + (wm * C::MTW + i) * 16 + 4 * g + r] = rs;
+        lm_lane_update(ls[i][r], v, col);
       }
     }
 #pragma unroll
     for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
       for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
-    // the stat writes must land before the barrier (it carries no fence, so
-    // the loads in flight are not drained); red is next written a whole pass
-    // later, after further barriers
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
-    bd_stream::pipe_barrier();
-    if (tid < MT * 16) {
-#pragma unroll
-      for (int w = 0; w < C::WN; ++w) run = bd_stat_combine(run, red[w * (MT * 16) + tid]);
-    }
     cch = 0;
     ++cp;
+  }
+  // the rows' statistics: over the 16 lanes of each row group, then over the
+  // WN waves that hold the row's columns (in wave order)
+#pragma unroll
+  for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const BdArgStat rs = lm_lane_row(ls[i][r]);
+      if (l16 == 0) red[wn * (MT * 16) + (wm * C::MTW + i) * 16 + 4 * g + r] = rs;
+    }
+  __syncthreads();
+  BdArgStat run{BD_NEG_INF, INT_MAX, 0.f};
+  if (tid < MT * 16) {
+#pragma unroll
+    for (int w = 0; w < C::WN; ++w) run = bd_stat_combine(run, red[w * (MT * 16) + tid]);
   }
   if (tid < MT * 16 && m0 + tid < Meff) {
     const size_t pi = (size_t)blockIdx.x * a.M + m0 + tid;  // [work-group][row]: whole cache lines
@@ -753,7 +835,8 @@ BdLmPlan bd_lm_plan(bd_dtype dt, int M, int hidden, int V) {
     const int mt = (M + 15) / 16;
     p.rows_per_wg = 16 * (mt <= 1 ? 1 : (mt == 2 ? 2 : 4));
     const int T = (V + 15) / 16;
-    p.nvt = T < kStreamWGs ? T : kStreamWGs;
+    const int wgs = hidden >= 2048 ? kStreamWGs : kStreamWGsNarrow;
+    p.nvt = T < wgs ? T : wgs;
     const int per = (T + p.nvt - 1) / p.nvt;  // tiles of the largest range
     p.passes = (per + kNTW - 1) / kNTW;
     p.cols_per_wg = per * 16;
@@ -790,9 +873,9 @@ hipError_t bd_lm_launch(bd_dtype dt, const BdLmPlan& p, const BdLmArgs& x, hipSt
           hipLaunchKernelGGL(lm_big_kernel<8>, dim3(cb8 * p.nmb), dim3(kBigThreads), 0, s, a, p.nmb, p.nvt);
         break;
       }
-      case 1: hipLaunchKernelGGL(lm_stream_kernel<1>, grid, dim3(kThreads), 0, s, a, p.passes); break;
-      case 2: hipLaunchKernelGGL(lm_stream_kernel<2>, grid, dim3(kThreads), 0, s, a, p.passes); break;
-      default: hipLaunchKernelGGL(lm_stream_kernel<4>, grid, dim3(kThreads), 0, s, a, p.passes); break;
+      case 1: hipLaunchKernelGGL((lm_stream_kernel<1, kLmWaves>), grid, dim3(64 * kLmWaves), 0, s, a, p.passes); break;
+      case 2: hipLaunchKernelGGL((lm_stream_kernel<2, kLmWaves>), grid, dim3(64 * kLmWaves), 0, s, a, p.passes); break;
+      default: hipLaunchKernelGGL((lm_stream_kernel<4, kLmWaves>), grid, dim3(64 * kLmWaves), 0, s, a, p.passes); break;
     }
   }
   hipError_t e = hipGetLastError();

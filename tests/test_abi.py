@@ -90,7 +90,8 @@ def test_lmhead_unmask_append_argument_errors():
     lib = _lib.load()
     E, U, C = _lib.BD_EINVAL, _lib.BD_EUNSUPPORTED, _lib.BD_ECAPACITY
     ws = lib.bd_lmhead_workspace_size(1, 64, 3584, 152064)
-    assert ws >= 64 * 512 * 12          # one (max, argmax, sum) per row and streaming work-group
+    assert ws >= 64 * 256 * 12          # one (max, argmax, sum) per row and streaming work-group (one per CU)
+    assert lib.bd_lmhead_workspace_size(1, 8, 1536, 151936) >= 8 * 512 * 12  # narrower rows: two per CU
     assert lib.bd_lmhead_workspace_size(1, 1024, 3584, 152064) >= 1024 * 594 * 12  # per row and 256-column block
     lm = lambda **k: lib.bd_lmhead_confidence(k.get("dt", 1), k.get("M", 8), k.get("hidden", 1536), 151936,
                                               FAKE, k.get("n_src", 9), k.get("ri", FAKE), FAKE, FAKE, FAKE,
