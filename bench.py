@@ -575,7 +575,10 @@ def extras_proj(reps):
     the LM head's weight stream comes between two uses of a projection's
     weights): the 7B QKV and output projections at the 7B DualCache (64
     rows) and exact (256 rows) steps, and the 1.5B layer's four projections at
-    the 28-layer decode's DualCache step (128 rows)."""
+    the 28-layer decode's DualCache (128 rows) and exact (512 rows) steps.
+    Beside each, the vendor GEMM (torch.matmul, hipBLASLt) of the same
+    product without the epilogue, timed the same way: the reference rate of
+    this part at these shapes."""
     from block_diffusion_decoding_amd import ops
     from block_diffusion_decoding_amd.ops import dense
     T = torch.bfloat16
@@ -591,28 +594,38 @@ def extras_proj(reps):
 
     def rnd(*shape, s=1.0):
         return (torch.randn(*shape, device="cuda") * s).to(T)
+    def vendor(xm, w):  # the same product as a plain vendor GEMM (torch.matmul -> hipBLASLt), no epilogue
+        yv = torch.empty(xm.shape[0], w.shape[0], dtype=T, device="cuda")
+        wt = w.t()
+        return cold(lambda: torch.matmul(xm, wt, out=yv)).record()["us"]
+
     out = {}
     for M, K, Nq, Nkv, inter, tag in ((64, 3584, 3584, 512, None, "7B_M64"), (256, 3584, 3584, 512, None, "7B_M256"),
-                                      (128, 1536, 1536, 256, 8960, "1.5B_M128")):
+                                      (128, 1536, 1536, 256, 8960, "1.5B_M128"), (512, 1536, 1536, 256, 8960,
+                                                                                  "1.5B_M512")):
         x, wq, wk, wv = rnd(M, K), rnd(Nq, K, s=.02), rnd(Nkv, K, s=.02), rnd(Nkv, K, s=.02)
         q, k, v = rnd(M, Nq), rnd(M, Nkv), rnd(M, Nkv)
         t = cold(lambda: ops.bd_qkv_proj(x, dense(M), wq, q, dense(M), wk, wv, k, dense(M), v, dense(M), M=M))
         by = (Nq + 2 * Nkv) * K * 2
-        out[f"qkv_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
+        out[f"qkv_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9,
+                             "vendor_us": vendor(x, torch.cat([wq, wk, wv]))}
         wo, y = rnd(K, Nq, s=.02), rnd(M, K)
         t = cold(lambda: ops.bd_linear(q, dense(M), wo, y, dense(M), M=M, res=x, rr=dense(M)))
         by = K * Nq * 2
-        out[f"o_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
+        out[f"o_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9, "vendor_us": vendor(q, wo)}
         if inter:
             wgu, a = rnd(2 * inter, K, s=.02), rnd(M, inter)
             t = cold(lambda: ops.bd_gate_up_swiglu(x, dense(M), wgu, a, dense(M), M=M))
             by = 2 * inter * K * 2
-            out[f"gate_up_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
+            out[f"gate_up_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9,
+                                     "vendor_us": vendor(x, wgu)}
             wd = rnd(K, inter, s=.02)
             t = cold(lambda: ops.bd_linear(a, dense(M), wd, y, dense(M), M=M, res=y, rr=dense(M)))
             by = K * inter * 2
-            out[f"down_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9}
-    log("[bench] projections (cold caches): " + ", ".join(f"{k} {v['us']:.1f} us" for k, v in out.items()))
+            out[f"down_{tag}"] = {**t.record(), "weight_bytes": by, "GB/s": by / t.mean / 1e9,
+                                  "vendor_us": vendor(a, wd)}
+    log("[bench] projections (cold caches; vendor GEMM of the same product): " +
+        ", ".join(f"{k} {v['us']:.1f} us ({v['vendor_us']:.1f})" for k, v in out.items()))
     del flush_src, flush_dst
     torch.cuda.empty_cache()
     return {"projections": out}

@@ -60,6 +60,10 @@ constexpr int kLdsPerCU = 160 * 1024;
 #ifndef BD_GEMM_KWAVE
 #define BD_GEMM_KWAVE 1
 #endif
+// cost of a 256 x 256 tile of the large-M kernel relative to a 256 x 128 one, x10
+#ifndef BD_GEMM_BIG16_COST
+#define BD_GEMM_BIG16_COST 16
+#endif
 #ifndef BD_GEMM_PART_BPNS
 #define BD_GEMM_PART_BPNS 4000
 #endif
@@ -1091,16 +1095,22 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
       }
     }
   }
-  // large M: 256-row tiles when their blocks alone fill the GPU
+  // large M: 256-row tiles when their blocks fill the GPU; of the two tile
+  // widths the one with the fewer rounds of work-groups (one per CU) weighted
+  // by the cost of its tiles (a 256-column tile costs BD_GEMM_BIG16_COST/10 of
+  // a 128-column one)
   const int rbk = (M + kBigRows - 1) / kBigRows;
-  for (int ct = 16; ct >= 8 && M >= kBigRows; ct /= 2) {
-    const int cbk = (T + ct - 1) / ct;
-    if ((long)rbk * cbk >= kCUs) {
+  if (M >= kBigRows) {
+    const long t16 = (long)rbk * ((T + 15) / 16), t8 = (long)rbk * ((T + 7) / 8);
+    const long r16 = (t16 + kCUs - 1) / kCUs, r8 = (t8 + kCUs - 1) / kCUs;
+    int ct = 0;
+    if (t16 >= kCUs || (t8 >= kCUs && r16 * BD_GEMM_BIG16_COST < r8 * 10)) ct = 16;
+    else if (t8 >= kCUs) ct = 8;
+    if (ct != 0) {
       best.big_ct = ct;
       best.kw_nt = 0;
       best.ksplit = 1;
       best.ws_bytes = 0;
-      break;
     }
   }
   return best;
