@@ -101,6 +101,8 @@ SIGNATURES = {
                                  c_void_p, c_size_t, c_void_p]),
     "bd_gate_up_swiglu": (c_int, [c_int, c_int, c_int, c_void_p, BdRows, c_void_p, c_int, c_void_p, BdRows,
                                   c_void_p]),
+    "bd_gate_up_swiglu_rmsnorm": (c_int, [c_int, c_int, c_int, c_void_p, BdRows, c_float, c_void_p, c_int, c_void_p,
+                                          BdRows, c_void_p]),
     "bd_train_attn_workspace_size": (c_size_t, [c_int] * 7),
     "bd_train_attn": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
                               c_float, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -284,7 +284,8 @@ bd_status bd_embed_rows(bd_dtype dt, int B, int D, int row_off, int n_rows, int 
 
 static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const BdGemmSeg* segs, int nseg,
                              int mode, const BdGemmRope* rope, const BdGemmNorm* post_norm, void* workspace,
-                             size_t ws_bytes, void* stream, const bd_guard* guard = nullptr) {
+                             size_t ws_bytes, void* stream, const bd_guard* guard = nullptr,
+                             float in_norm_eps = -1.f) {
   if (!valid_dtype(dt) || M < 0 || !valid_guard(guard)) return BD_EINVAL;
   if (M == 0) return BD_OK;
   if (K <= 0 || !x || !valid_rows(xr)) return BD_EINVAL;
@@ -305,11 +306,15 @@ static bd_status gemm_common(bd_dtype dt, int M, int K, const void* x, bd_rows x
     for (int i = 0; i < nseg; ++i)
       if (!aligned16(segs[i].w)) return BD_EUNSUPPORTED;
   }
-  const BdGemmPlan p = bd_gemm_plan(dt, M, K, N, nseg, mode);
+  BdGemmPlan p = bd_gemm_plan(dt, M, K, N, nseg, mode);
+  if (in_norm_eps >= 0.f && p.kw_nt != 0) {  // the input norm rides on the streaming kernel instead
+    p.kw_nt = p.kw_mt = 0;
+    p.ny = (M + p.MT * 16 - 1) / (p.MT * 16);
+  }
   if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes || !aligned16(workspace)))
     return BD_EINVAL;
   return hip_status(bd_gemm_launch(dt, p, M, K, x, xr, segs, nseg, mode, rope, post_norm, workspace,
-                                   static_cast<hipStream_t>(stream), guard));
+                                   static_cast<hipStream_t>(stream), guard, in_norm_eps));
 }
 
 size_t bd_linear_workspace_size(bd_dtype dt, int M, int N, int K) {
@@ -385,6 +390,14 @@ bd_status bd_gate_up_swiglu(bd_dtype dt, int M, int K, const void* x, bd_rows xr
   const bd_rows none{1, 1, 0};
   BdGemmSeg seg{w_gu, a, ar, nullptr, none, inter};
   return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_SWIGLU, nullptr, nullptr, nullptr, 0, stream);
+}
+
+bd_status bd_gate_up_swiglu_rmsnorm(bd_dtype dt, int M, int K, const void* x, bd_rows xr, float eps,
+                                    const void* w_gu, int inter, void* a, bd_rows ar, void* stream) {
+  if (!(eps >= 0.f)) return BD_EINVAL;
+  const bd_rows none{1, 1, 0};
+  BdGemmSeg seg{w_gu, a, ar, nullptr, none, inter};
+  return gemm_common(dt, M, K, x, xr, &seg, 1, BD_GEMM_SWIGLU, nullptr, nullptr, nullptr, 0, stream, nullptr, eps);
 }
 
 // ---------------------------------------------------------------------------

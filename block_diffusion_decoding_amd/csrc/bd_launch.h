@@ -155,10 +155,12 @@ struct BdGemmNorm {
 };
 
 // guard: optional (bd_guard), honoured by every kernel of the launch.
+// in_norm_eps >= 0 (SwiGLU mode only): the rows of x are RMS-normalised
+// (unit gains) before the product; not with the K split over waves.
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
                           const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope,
                           const BdGemmNorm* post_norm, void* workspace, hipStream_t s,
-                          const bd_guard* guard = nullptr);
+                          const bd_guard* guard = nullptr, float in_norm_eps = -1.f);
 
 hipError_t bd_embed_launch(bd_dtype dt, int B, int D, int row_off, int n_rows, int hidden, int V,
                            const void* E, const int32_t* tokens, const uint64_t* mask_bits,

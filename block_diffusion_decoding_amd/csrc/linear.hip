@@ -92,7 +92,32 @@ struct GemmS {
   const uint64_t* g_bits;   // guard (bd_guard): the launch does nothing when no
   uint64_t g_mask;          // g_bits[b], b < g_n, has a bit of g_mask set
   int g_n;
+  int norm_x;               // SwiGLU mode: the rows of x are RMS-normalised first
+  float norm_eps;
 };
+
+// Input RMSNorm (unit gains) folded into a SwiGLU projection: the product of
+// a normalised row is the product of the raw row times rsqrt(mean x^2 + eps),
+// so the kernels multiply raw x (bf16 from memory) and scale the gate and up
+// sums of each row.  The sum of squares comes from the A fragments the MFMAs
+// read anyway: lane L holds 8 values of row L % 16 per k-step, and the four
+// lanes L % 16 == c together cover every k once.
+typedef __bf16 bd_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float bf16x8_sumsq(uint4 v, float s) {  // s + sum of the 8 squares (4 dot2 steps)
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const bd_bf16x2 p = __builtin_bit_cast(bd_bf16x2, w[h]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
+  }
+  return s;
+}
+// Row total of a fragment tile's squares: lanes L with L % 16 == c end up
+// with the sum of row c (every lane of the wave calls it).
+__device__ __forceinline__ float frag_row_total(float ss) {
+  const float t = ss + __shfl_xor(ss, 16);
+  return t + __shfl_xor(t, 32);
+}
 
 __device__ __forceinline__ int seg_of(const GemmS& a, int gt) {
   return gt >= a.tb[2] ? 2 : (gt >= a.tb[1] ? 1 : 0);
@@ -199,6 +224,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
   for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
     for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+  // input RMSNorm: the sums of squares of the rows, from the first pass's
+  // fragments; row tile i of a row group is summed by the wave wn == i % WN
+  // of the group, the scales meet in LDS at the end of the first pass
+  __shared__ float nscale[MT * 16];
+  float ss[C::MTW], scl[C::MTW][4];
+#pragma unroll
+  for (int i = 0; i < C::MTW; ++i) {
+    ss[i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) scl[i][r] = 1.f;
+  }
 
 #pragma unroll
   for (int c = 0; c < C::NS - 1; ++c)
@@ -238,6 +274,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
       for (int i = 0; i < C::MTW; ++i)
 #pragma unroll
         for (int j = 0; j < C::NTP; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+      if (a.norm_x && cp == 0)
+#pragma unroll
+        for (int i = 0; i < C::MTW; ++i)
+          if (i % C::WN == wn) ss[i] = bf16x8_sumsq(xa[i], ss[i]);
     }
     if (++cch < nch) continue;
 
@@ -245,6 +285,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
     // wn*NTP + j of the pass, column l16 of each
     const int b = pass_begin(cp), n = pass_begin(cp + 1) - b;
     if (a.mode == BD_GEMM_SWIGLU) {
+      if (a.norm_x && cp == 0) {
+        const uint32_t ns = bd_stream::lds_addr(nscale);
+#pragma unroll
+        for (int i = 0; i < C::MTW; ++i)
+          if (i % C::WN == wn) {
+            const float t = frag_row_total(ss[i]);
+            if (g == 0) bd_stream::lds_write_f32(ns + ((wm * C::MTW + i) * 16 + l16) * 4, rsqrtf(t / (float)K + a.norm_eps));
+          }
+        bd_stream::pipe_barrier();
+#pragma unroll
+        for (int i = 0; i < C::MTW; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) scl[i][r] = bd_stream::lds_read_f32(ns + ((wm * C::MTW + i) * 16 + 4 * g + r) * 4);
+      }
 #pragma unroll
       for (int j = 0; j < C::NTP; j += 2) {
         const int slot = wn * C::NTP + j;
@@ -256,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
             for (int r = 0; r < 4; ++r) {
               const int m = m0 + (wm * C::MTW + i) * 16 + 4 * g + r;
               if (m < a.M) {
-                const float zg = acc[i][j][r], u = acc[i][j + 1][r];
+                const float zg = acc[i][j][r] * scl[i][r], u = acc[i][j + 1][r] * scl[i][r];
                 a.y[0][(size_t)bd_map_row(a.yr[0], m) * a.N[0] + col] =
                     (uint16_t)bd_f2bf(zg / (1.f + __expf(-zg)) * u);
               }
@@ -636,6 +690,13 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
   for (int i = 0; i < P::MW; ++i)
 #pragma unroll
     for (int j = 0; j < P::NWT; ++j) acc[i][j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
+  // input RMSNorm: the waves of a row group (wc = 0 .. WC-1) take turns over
+  // the k-steps, each summing the squares of all its row tiles on its steps;
+  // the partial sums meet in LDS after the loop
+  __shared__ float nsq[P::WC][kBigRows];
+  float ss[P::MW];
+#pragma unroll
+  for (int i = 0; i < P::MW; ++i) ss[i] = 0.f;
   const uint32_t sbase = bd_stream::lds_addr(sbuf);
   const uint32_t fo[2] = {(uint32_t)bd_stream::frag_offset(lane, 0), (uint32_t)bd_stream::frag_offset(lane, 1)};
   // row tile i of this wave is row tile i*WR + wr of the block
@@ -661,6 +722,10 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
         if (i < live)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = bd_mfma16(xa[i], wb[j], acc[i][j]);
+      const bool sq = a.norm_x && (2 * ch + ks) % P::WC == wc;
+      if (sq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss[i] = bf16x8_sumsq(xa[i], ss[i]);
 #pragma unroll
       for (int i0 = 4; i0 < P::MW; i0 += 4) {
         if (i0 >= live) break;
@@ -670,12 +735,32 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
           if (i0 + i < live)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i0 + i][j] = bd_mfma16(xa[i], wb[j], acc[i0 + i][j]);
+        if (sq)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ss[i0 + i] = bf16x8_sumsq(xa[i], ss[i0 + i]);
       }
     }
   }
 
   // acc[i][j][r]: row m0 + (i*WR + wr)*16 + 4g + r, tile cb*CT + wc*NWT + j, column l16
   const int gt0 = cb * CT + wc * P::NWT;
+  // input RMSNorm: nsq[0][row] becomes the scale of the block's row (no DMA in flight any more)
+  if (a.norm_x) {
+#pragma unroll
+    for (int i = 0; i < P::MW; ++i) {
+      const float t = frag_row_total(ss[i]);
+      if (g == 0) nsq[wc][(i * P::WR + wr) * 16 + l16] = t;
+    }
+    __syncthreads();
+    if (tid < kBigRows) {
+      float t = nsq[0][tid];
+#pragma unroll
+      for (int w = 1; w < P::WC; ++w) t += nsq[w][tid];
+      nsq[0][tid] = rsqrtf(t / (float)a.K + a.norm_eps);
+    }
+    __syncthreads();
+  }
+  auto row_scale = [&](int i, int r) { return a.norm_x ? nsq[0][(i * P::WR + wr) * 16 + 4 * g + r] : 1.f; };
   if (a.vec_out) {
     // Stores through LDS: in rounds of 64 rows the fp32 results (after the
     // SwiGLU gate) are staged as rows, then written out as 4-column vectors
@@ -698,7 +783,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
           if (swiglu) {
 #pragma unroll
             for (int j = 0; j < P::NWT; j += 2) {
-              const float zg = acc[i][j][r], u = acc[i][j + 1][r];
+              const float sc = row_scale(i, r);
+              const float zg = acc[i][j][r] * sc, u = acc[i][j + 1][r] * sc;
               lrow[((wc * P::NWT + j) >> 1) * 16 + l16] = zg / (1.f + __expf(-zg)) * u;
             }
           } else {
@@ -750,7 +836,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
         for (int r = 0; r < 4; ++r) {
           const int m = m0 + (i * P::WR + wr) * 16 + 4 * g + r;
           if (m < a.M) {
-            const float zg = acc[i][j][r], u = acc[i][j + 1][r];
+            const float sc = row_scale(i, r);
+            const float zg = acc[i][j][r] * sc, u = acc[i][j + 1][r] * sc;
             a.y[0][(size_t)bd_map_row(a.yr[0], m) * a.N[0] + col] = (uint16_t)bd_f2bf(zg / (1.f + __expf(-zg)) * u);
           }
         }
@@ -943,6 +1030,8 @@ struct GemmF {
   const uint64_t* g_bits;
   uint64_t g_mask;
   int g_n;
+  int norm_x;
+  float norm_eps;
 };
 
 // fp32 projections: one thread per output element (small test shapes); in
@@ -954,12 +1043,20 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmF a, int swiglu)
   if (n >= a.N) return;
   const float* xr = a.x + (size_t)bd_map_row(a.xr, m) * a.K;
   const float* wr = a.w + (size_t)n * a.K;
-  float acc = 0.f;
-  for (int k = 0; k < a.K; ++k) acc += xr[k] * wr[k];
+  float acc = 0.f, ss = 0.f;
+  for (int k = 0; k < a.K; ++k) {
+    acc += xr[k] * wr[k];
+    ss += xr[k] * xr[k];
+  }
   if (swiglu) {
     const float* ur = a.w + (size_t)(a.N + n) * a.K;
     float up = 0.f;
     for (int k = 0; k < a.K; ++k) up += xr[k] * ur[k];
+    if (a.norm_x) {  // input RMSNorm (unit gains): both sums scale with the row
+      const float sc = rsqrtf(ss / (float)a.K + a.norm_eps);
+      acc *= sc;
+      up *= sc;
+    }
     acc = acc / (1.f + __expf(-acc)) * up;
   }
   if (a.res) acc += a.res[(size_t)bd_map_row(a.rr, m) * a.N + n];
@@ -1118,7 +1215,10 @@ BdGemmPlan bd_gemm_plan(bd_dtype dt, int M, int K, const int* N, int nseg, int m
 
 hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const void* x, bd_rows xr,
                           const BdGemmSeg* segs, int nseg, int mode, const BdGemmRope* rope,
-                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s, const bd_guard* guard) {
+                          const BdGemmNorm* post_norm, void* workspace, hipStream_t s, const bd_guard* guard,
+                          float in_norm_eps) {
+  const int norm_x = mode == BD_GEMM_SWIGLU && in_norm_eps >= 0.f ? 1 : 0;
+  if (norm_x && p.kw_nt != 0) return hipErrorInvalidValue;  // the K split over waves has no input norm
   const uint64_t* g_bits = guard ? guard->bits : nullptr;
   const uint64_t g_mask = guard ? guard->mask : 0;
   const int g_n = guard ? guard->n : 0;
@@ -1130,7 +1230,7 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
     for (int i = 0; i < nseg; ++i) {
       GemmF a{static_cast<const float*>(x), xr, M, K, static_cast<const float*>(segs[i].w),
               static_cast<float*>(segs[i].y), static_cast<const float*>(segs[i].res), segs[i].yr, segs[i].rr,
-              segs[i].N, g_bits, g_mask, g_n};
+              segs[i].N, g_bits, g_mask, g_n, norm_x, in_norm_eps};
       hipLaunchKernelGGL(gemm_f32_kernel, dim3((segs[i].N + kThreads - 1) / kThreads, M), dim3(kThreads), 0, s,
                          a, mode == BD_GEMM_SWIGLU ? 1 : 0);
       hipError_t e = hipGetLastError();
@@ -1143,6 +1243,8 @@ hipError_t bd_gemm_launch(bd_dtype dt, const BdGemmPlan& p, int M, int K, const 
     a.g_bits = g_bits;
     a.g_mask = g_mask;
     a.g_n = g_n;
+    a.norm_x = norm_x;
+    a.norm_eps = in_norm_eps;
     a.M = M;
     a.K = K;
     a.nseg = nseg;

@@ -76,6 +76,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
+// One 4-byte LDS write / read as asm that waits inside the block, for use
+// while global->LDS DMA is in flight (plain accesses would get a wait for
+// every outstanding DMA in front of them).
+__device__ __forceinline__ void lds_write_f32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ float lds_read_f32(uint32_t addr) {
+  float v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
 // Fragment reads written as asm with the wait inside the block: the compiler
 // then cannot guard them with a wait for every outstanding global->LDS DMA
 // (it cannot tell which LDS bytes a DMA writes), which would serialise the

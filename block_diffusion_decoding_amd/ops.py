@@ -361,6 +361,15 @@ def bd_gate_up_swiglu(x, xr, w_gu, a, ar, *, M, stream=None):
     _check("bd_gate_up_swiglu", st)
 
 
+def bd_gate_up_swiglu_rmsnorm(x, xr, w_gu, a, ar, *, M, eps, stream=None):
+    """bd_gate_up_swiglu on rmsnorm(x[xr(m)]) (unit gains), the norm folded
+    into the projection's kernels."""
+    inter2, K = w_gu.shape
+    st = _lib.load().bd_gate_up_swiglu_rmsnorm(_dt(w_gu), M, K, _p(x), xr, float(eps), _p(w_gu), inter2 // 2, _p(a),
+                                               ar, _stream(stream))
+    _check("bd_gate_up_swiglu_rmsnorm", st)
+
+
 def bd_rmsnorm(x, xr, y, yr, *, M, eps, stream=None):
     """y[yr(m)] = rmsnorm(x[xr(m)]) (unit gains); rows of x.shape[-1] elements."""
     st = _lib.load().bd_rmsnorm(_dt(x), M, x.shape[-1], _p(x), xr, float(eps), _p(y), yr, _stream(stream))

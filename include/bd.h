@@ -431,6 +431,16 @@ bd_status bd_qkv_proj_rope(bd_dtype dt, int M, int K, const void* x, bd_rows xr,
 bd_status bd_gate_up_swiglu(bd_dtype dt, int M, int K, const void* x, bd_rows xr, const void* w_gu, int inter,
                             void* a, bd_rows ar, void* stream);
 
+/* bd_gate_up_swiglu on RMS-normalised rows (unit gains), the pre-MLP norm of
+ * a pre-norm layer folded into the projection:
+ *   a[ar(m), n] = silu(h_m . w_gu[n]) * (h_m . w_gu[inter + n]),
+ *   h_m = x[xr(m)] / sqrt(mean_k x[xr(m)][k]^2 + eps)
+ * The kernels multiply the raw rows and scale each row's gate and up sums by
+ * 1/sqrt(mean x^2 + eps), its sum of squares taken from the same loads (bf16:
+ * of the bf16 values, in fp32).  eps >= 0.  No workspace. */
+bd_status bd_gate_up_swiglu_rmsnorm(bd_dtype dt, int M, int K, const void* x, bd_rows xr, float eps,
+                                    const void* w_gu, int inter, void* a, bd_rows ar, void* stream);
+
 /* ------------------------------------------------------------------------
  * Layer pieces of the multi-layer decode (support calls).  The pages name the
  * model family ([v2 notes] main results: Qwen2.5-style decoders adapted to

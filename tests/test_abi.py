@@ -30,7 +30,7 @@ def test_header_declares_the_four_calls_and_support():
               "bd_embed_rows", "bd_linear", "bd_qkv_proj", "bd_block_attn_workspace_size",
               "bd_linear_workspace_size", "bd_qkv_proj_workspace_size",
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
-              "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu",
+              "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu", "bd_gate_up_swiglu_rmsnorm",
               "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau",
               "bd_lmhead_unmask", "bd_threshold_unmask_windows", "bd_copy_rows", "bd_block_attn_noalloc"]:
         assert n in names
@@ -254,6 +254,10 @@ def test_fused_layer_call_argument_errors():
     assert lib.bd_gate_up_swiglu(1, 128, 1000, FAKE, d1, FAKE, 8960, FAKE, d1, None) == _lib.BD_EUNSUPPORTED
     assert lib.bd_gate_up_swiglu(1, 128, 1536, FAKE, d1, None, 8960, FAKE, d1, None) == E
     assert lib.bd_gate_up_swiglu(1, 0, 1536, FAKE, d1, FAKE, 8960, FAKE, d1, None) == 0
+    gn = lambda **k: lib.bd_gate_up_swiglu_rmsnorm(1, k.get("M", 128), k.get("K", 1536), FAKE, d1, k.get("eps", 1e-6),
+                                                   k.get("w", FAKE), 8960, FAKE, d1, None)
+    assert gn(eps=-1.0) == E and gn(eps=float("nan")) == E and gn(w=None) == E
+    assert gn(K=1000) == _lib.BD_EUNSUPPORTED and gn(M=0) == 0
 
 
 def test_training_form_argument_errors():

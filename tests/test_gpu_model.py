@@ -145,6 +145,35 @@ def test_gate_up_swiglu_matches_projections_then_gate(dtype, M, K, inter):
     assert not got[:2].any() and not got[2 + M:].any()
 
 
+@pytest.mark.parametrize("dtype,M,K,inter", [("bf16", 128, 1536, 8960), ("bf16", 5, 512, 1000),
+                                             ("bf16", 37, 256, 520), ("bf16", 300, 512, 256),
+                                             ("f32", 9, 256, 100), ("bf16", 512, 1536, 8960),
+                                             ("bf16", 1100, 512, 4096), ("bf16", 64, 3584, 1024),
+                                             ("bf16", 64, 256, 40960)])
+def test_gate_up_swiglu_rmsnorm_matches_norm_then_projections(dtype, M, K, inter):
+    """The pre-MLP RMSNorm folded into the gate/up projection (streaming
+    kernel at 5..300 rows, in two passes at 40960 columns, 256-row tiles at
+    512 and 1100 rows, fp32) against the
+    oracle's rmsnorm followed by the two projections and the gate; rows of
+    different scales, so a missing or misplaced row scale shows."""
+    say(f"[model] gate/up+swiglu with input rmsnorm {dtype} M{M} K{K} inter{inter}")
+    o = ops()
+    T = tdt(dtype)
+    scale = (0.25 + 4.0 * (np.arange(M) % 7) / 7.0)[:, None]
+    x = (bi.normal(15, "x", (M, K), 0.5, "f32") * scale).astype(np.float32)
+    if dtype == "bf16":
+        x = down(up(x, torch.bfloat16))
+    w = bi.normal(15, "mWg", (2 * inter, K), 0.05, dtype)
+    a = torch.zeros(M + 3, inter, dtype=T, device=DEV)
+    o.bd_gate_up_swiglu_rmsnorm(up(x, T), o.dense(M), up(w, T), a, o.rows(M, M + 3, 2), M=M, eps=1e-6)
+    h = OM.rmsnorm(x.astype(np.float64), 1e-6)
+    w64 = w.astype(np.float64)
+    ref = OM.silu(h @ w64[:inter].T) * (h @ w64[inter:].T)
+    got = down(a)
+    rows_close(got[2:2 + M], ref, TOL[dtype], "swiglu projection of normalised rows")
+    assert not got[:2].any() and not got[2 + M:].any()
+
+
 @pytest.mark.parametrize("dtype,M,N,K", [("bf16", 128, 1536, 1536), ("bf16", 128, 1536, 8960),
                                          ("bf16", 512, 1536, 8960), ("bf16", 8, 1536, 1536),
                                          ("bf16", 100, 4608, 512), ("bf16", 256, 8192, 512), ("f32", 9, 256, 512)])
