@@ -26,6 +26,11 @@ class BdGuard(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_void_p), ("mask", ctypes.c_uint64), ("n", ctypes.c_int32)]
 
 
+class BdNextRows(ctypes.Structure):
+    """The next step's input rows written by bd_lmhead_unmask_next."""
+    _fields_ = [("embedding", ctypes.c_void_p), ("plant", ctypes.c_void_p), ("x", ctypes.c_void_p)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "bd_version": (ctypes.c_char_p, []),
@@ -64,6 +69,11 @@ SIGNATURES = {
                                  c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "bd_lmhead_unmask_next": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_void_p, c_int, c_void_p, c_void_p, c_float, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      ctypes.POINTER(BdNextRows), c_void_p, c_size_t, c_void_p]),
     "bd_candidate_rows": (c_int, [c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "bd_threshold_unmask": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_float,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -166,20 +166,43 @@ bd_status bd_lmhead_confidence(bd_dtype dt, int M, int hidden, int V, const void
                    logits, workspace, ws_bytes, stream);
 }
 
-bd_status bd_lmhead_unmask(bd_dtype dt, int B, int D, int win_lo, int win_len, int hidden, int V, const void* h_src,
-                           int n_src, const int32_t* row_idx, const void* w, float threshold,
-                           const float* threshold_dev, int32_t* argmax, float* conf, float* max_logit, float* lse,
-                           int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked, int32_t* unmasked_pos,
-                           uint64_t* mask_bits_host, void* workspace, size_t ws_bytes, void* stream) {
+bd_status bd_lmhead_unmask_next(bd_dtype dt, int B, int D, int win_lo, int win_len, int hidden, int V,
+                                const void* h_src, int n_src, const int32_t* row_idx, const void* w, float threshold,
+                                const float* threshold_dev, int32_t* argmax, float* conf, float* max_logit, float* lse,
+                                int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked, int32_t* unmasked_pos,
+                                uint64_t* mask_bits_host, const bd_next_rows* next, void* workspace,
+                                size_t ws_bytes, void* stream) {
   if (B < 0) return BD_EINVAL;
   if (B == 0) return BD_OK;
   if (D < 1 || D > 64 || win_lo < 0 || win_len < 1 || win_len > 64 || win_lo + win_len > D) return BD_EINVAL;
   if ((long)B * win_len > 64 || !tokens || !mask_bits) return BD_EINVAL;
   if (threshold_dev == nullptr && !(threshold == threshold)) return BD_EINVAL;
   BdLmUnmask um{B, D, win_lo, win_len, threshold, threshold_dev, tokens, mask_bits, n_unmasked, unmasked_pos,
-                mask_bits_host};
+                mask_bits_host, nullptr, nullptr, nullptr, 0, 0, 0};
+  if (next != nullptr) {
+    if (!valid_dtype(dt) || !next->embedding || !next->x) return BD_EINVAL;
+    if (hidden % (dt == BD_BF16 ? 8 : 4) != 0 || !aligned16(next->embedding) || !aligned16(next->x) ||
+        (next->plant && !aligned16(next->plant)))
+      return BD_EUNSUPPORTED;
+    um.emb = next->embedding;
+    um.plant = next->plant;
+    um.x = next->x;
+    um.hidden = hidden;
+    um.V = V;
+    um.f32 = dt == BD_F32 ? 1 : 0;
+  }
   return lm_common(dt, B * win_len, hidden, V, h_src, n_src, row_idx, nullptr, nullptr, 0, w, argmax, conf,
                    max_logit, lse, nullptr, workspace, ws_bytes, stream, &um);
+}
+
+bd_status bd_lmhead_unmask(bd_dtype dt, int B, int D, int win_lo, int win_len, int hidden, int V, const void* h_src,
+                           int n_src, const int32_t* row_idx, const void* w, float threshold,
+                           const float* threshold_dev, int32_t* argmax, float* conf, float* max_logit, float* lse,
+                           int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked, int32_t* unmasked_pos,
+                           uint64_t* mask_bits_host, void* workspace, size_t ws_bytes, void* stream) {
+  return bd_lmhead_unmask_next(dt, B, D, win_lo, win_len, hidden, V, h_src, n_src, row_idx, w, threshold,
+                               threshold_dev, argmax, conf, max_logit, lse, tokens, mask_bits, n_unmasked,
+                               unmasked_pos, mask_bits_host, nullptr, workspace, ws_bytes, stream);
 }
 
 bd_status bd_lmhead_confidence_rows(bd_dtype dt, int M, int hidden, int V, const void* h_src, int n_src,

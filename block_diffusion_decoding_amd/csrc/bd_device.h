@@ -154,7 +154,8 @@ __device__ __forceinline__ BdArgStat bd_row16_stat(const float (&v)[N], const in
 // A NaN confidence never passes and ranks last.  Writes the picked tokens,
 // the new mask bits (also to bits_out when given: a second copy, e.g. in
 // host memory the device can write), the count and the ascending positions.
-__device__ inline void bd_unmask_wave(int r, int b, int D, int win_lo, int win_len, uint64_t bits, float c, int32_t am,
+// Returns the window entries it unmasked (bit r: entry r; the same in every lane).
+__device__ inline uint64_t bd_unmask_wave(int r, int b, int D, int win_lo, int win_len, uint64_t bits, float c, int32_t am,
                                       float thr, int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
                                       int32_t* unmasked_pos, uint64_t* bits_out) {
   const int pos = win_lo + r;
@@ -183,4 +184,5 @@ __device__ inline void bd_unmask_wave(int r, int b, int D, int win_lo, int win_l
     if (bits_out != nullptr) bits_out[b] = left;
     if (n_unmasked != nullptr) n_unmasked[b] = n;
   }
+  return pick;
 }

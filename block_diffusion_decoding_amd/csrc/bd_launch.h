@@ -95,6 +95,12 @@ struct BdLmUnmask {
   int32_t* n_unmasked;
   int32_t* unmasked_pos;
   uint64_t* bits_out;          // second copy of the new mask bits, or NULL
+  // next step's input rows (x != NULL): the row of every position unmasked
+  // here becomes E[token] (+ plant), x / plant [B, D, hidden], E [V+1, hidden]
+  const void* emb;
+  const void* plant;
+  void* x;
+  int hidden, V, f32;
 };
 
 // um != NULL: the merge also applies the threshold rule (a.M = B * win_len,

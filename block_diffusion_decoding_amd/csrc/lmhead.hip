@@ -799,7 +799,9 @@ __global__ __launch_bounds__(kFuseThreads) void lm_merge_unmask_kernel(const int
   for (int off = RP; off < 64; off <<= 1) st = bd_stat_combine(st, bd_stat_shfl_xor(st, off));
   if (q == 0) sh[wave][r] = st;
   __syncthreads();
-  if (wave != 0) return;
+  __shared__ uint64_t sh_pick;  // entries unmasked here, their tokens and their list (next rows)
+  __shared__ int32_t sh_tok[64], sh_pos[64];
+  if (wave == 0) {
   if (q == 0)
     for (int w = 1; w < NW; ++w) st = bd_stat_combine(st, sh[w][r]);
   float c = BD_NEG_INF;
@@ -817,8 +819,53 @@ __global__ __launch_bounds__(kFuseThreads) void lm_merge_unmask_kernel(const int
   }
   // lane r (< RP, so q == 0) holds window entry r
   const float thr = u.threshold_dev != nullptr ? u.threshold_dev[b] : u.threshold;
-  bd_unmask_wave(lane, b, u.D, u.win_lo, u.win_len, bits0, lane < RP ? c : BD_NEG_INF,
-                 lane < RP ? am : -1, thr, u.tokens, u.mask_bits, u.n_unmasked, u.unmasked_pos, u.bits_out);
+  const uint64_t pick = bd_unmask_wave(lane, b, u.D, u.win_lo, u.win_len, bits0, lane < RP ? c : BD_NEG_INF,
+                                       lane < RP ? am : -1, thr, u.tokens, u.mask_bits, u.n_unmasked,
+                                       u.unmasked_pos, u.bits_out);
+  if (u.x != nullptr) {
+    if (lane == 0) sh_pick = pick;
+    if (lane < RP) sh_tok[lane] = am;
+    if ((pick >> lane) & 1ull) sh_pos[__popcll(pick & ((1ull << lane) - 1ull))] = lane;
+  }
+  }
+  if (u.x == nullptr) return;
+  // Next step's input rows: the row of every position decoded here becomes
+  // its token's embedding (+ the plant), as bd_embed_rows would write it; the
+  // rows of positions still masked keep the [MASK] embedding they hold.
+  __syncthreads();
+  const uint64_t pk = sh_pick;
+  const int np = __popcll(pk);
+  const int per = u.f32 ? 4 : 8;  // elements per 16-byte vector
+  const int nv = u.hidden / per;
+  for (int t = tid; t < np * nv; t += kFuseThreads) {
+    const int k = t / nv, e = (t - k * nv) * per;
+    const int ent = sh_pos[k], tok = sh_tok[ent];
+    const bool ok = tok >= 0 && tok < u.V;
+    const size_t row = (size_t)b * u.D + u.win_lo + ent;
+    const size_t eoff = (size_t)(ok ? tok : 0) * u.hidden + e, roff = row * u.hidden + e;
+    if (u.f32) {
+      float4 f = *(reinterpret_cast<const float4*>(static_cast<const float*>(u.emb) + eoff));
+      if (u.plant) {
+        const float4 p = *(reinterpret_cast<const float4*>(static_cast<const float*>(u.plant) + roff));
+        f.x += p.x; f.y += p.y; f.z += p.z; f.w += p.w;
+      }
+      if (!ok) f = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+      *reinterpret_cast<float4*>(static_cast<float*>(u.x) + roff) = f;
+    } else {
+      const uint4 ev = *(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(u.emb) + eoff));
+      const uint4 pv = u.plant ? *(reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(u.plant) + roff))
+                               : make_uint4(0, 0, 0, 0);
+      const uint32_t ew[4] = {ev.x, ev.y, ev.z, ev.w}, pw[4] = {pv.x, pv.y, pv.z, pv.w};
+      uint32_t ow[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        ow[h] = !ok ? 0x7fc07fc0u
+                    : (u.plant ? bd_pack_bf2(bd_bf2f(ew[h] & 0xffffu) + bd_bf2f(pw[h] & 0xffffu),
+                                             bd_bf2f(ew[h] >> 16) + bd_bf2f(pw[h] >> 16))
+                               : ew[h]);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(u.x) + roff) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+  }
 }
 
 }  // namespace

@@ -59,6 +59,9 @@ class BlockDecoder:
     # rest one by one.
     window_graphs = True
     window_slots = 8
+    # X holds the block's input rows between steps (false where X is a
+    # working buffer that every step refills)
+    input_rows_kept = True
 
     def slots(self, S: int) -> int:
         """Step slots of a window graph for windows of S positions."""
@@ -107,6 +110,10 @@ class BlockDecoder:
         self._held_ws = {}      # tag -> workspace the captured graphs point into
         self._guard = None      # (bits, mask, n): the step's projections and attention skip a finished window
         self._rings = {}        # S -> [2, D // S, slots(S), B] pinned: mask bits after each step slot of each window
+        # whether X [B, D, hidden] holds the current input rows of the whole
+        # block (kept so by the fused LM head + unmask, which rewrites the rows
+        # of the positions it decodes: DualCache steps then embed nothing)
+        self._rows_current = False
 
     # ------------------------------------------------------------------ state
     def set_synthetic_prefix(self, kv_len, cache_k, cache_v, carry):
@@ -131,6 +138,7 @@ class BlockDecoder:
         self.tokens.copy_(torch.from_numpy(t).pin_memory(), non_blocking=True)
         self.mask_bits.copy_(torch.from_numpy(bits.view(np.int64)).pin_memory(), non_blocking=True)
         self._bits_fresh = False
+        self._rows_current = False
 
     def set_block(self, tokens, masked, plant=None, carry_offset=None):
         """Current block: tokens [B, D], masked [B, D] bool, optional plant
@@ -149,6 +157,7 @@ class BlockDecoder:
                 self.plant.copy_(src)
         if carry_offset is not None:
             self.H[:, 0] += torch.as_tensor(carry_offset).to(self.device, self.dtype)
+        self._rows_current = False
 
     def has_graphs(self) -> bool:
         """Whether captured graphs hold pointers into this decoder's buffers."""
@@ -197,20 +206,43 @@ class BlockDecoder:
             self._win[key] = w
         return w
 
-    def _forward_rows(self, lo: int, n: int):
-        """Input rows, Q/K/V and attention of block rows [lo, lo + n)."""
+    def _forward_rows(self, lo: int, n: int, kept: bool = False):
+        """Input rows, Q/K/V and attention of block rows [lo, lo + n).
+        Returns (X, its row map, o).  All D rows: X is embedded whole; kept:
+        the rows are read in place from X [B, D, hidden], which holds the
+        block's current input rows; otherwise the window's rows are embedded
+        into a packed [B, n, hidden] view."""
         dm, W = self.dims, self.W
         B, D = dm.B, dm.D
-        X = self.X[:, :n] if n == D else self.X.view(-1)[: B * n * dm.hidden].view(B, n, dm.hidden)
         q = self.q.view(-1)[: B * n * dm.Hq * dm.d].view(B, n, dm.Hq, dm.d)
         o = self.o.view(-1)[: B * n * dm.Hq * dm.d].view(B, n, dm.Hq, dm.d)
-        ops.bd_embed_rows(W["E"], self.tokens, self.mask_bits, X, row_off=lo, n_rows=n, plant=self.plant)
+        if n == D or kept:
+            X, xr = self.X, (dense(B * D) if n == D else rows(n, D, lo))
+            if n == D:
+                ops.bd_embed_rows(W["E"], self.tokens, self.mask_bits, X, row_off=0, n_rows=D, plant=self.plant)
+        else:
+            X, xr = self.X.view(-1)[: B * n * dm.hidden].view(B, n, dm.hidden), dense(B * n)
+            ops.bd_embed_rows(W["E"], self.tokens, self.mask_bits, X, row_off=lo, n_rows=n, plant=self.plant)
         kr = rows(n, D, lo)
-        ops.bd_qkv_proj(X, dense(B * n), W["Wq"], q, dense(B * n), W["Wk"], W["Wv"], self.blk_k, kr,
+        ops.bd_qkv_proj(X, xr, W["Wq"], q, dense(B * n), W["Wk"], W["Wv"], self.blk_k, kr,
                         self.blk_v, kr, M=B * n, guard=self._guard)
         ops.bd_block_attn(q, self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, o,
                           D=D, q_off=lo, guard=self._guard)
-        return X, o
+        return X, xr, o
+
+    def keeps_rows(self, S: int) -> bool:
+        """Whether steps of S-position windows keep X current: the LM head
+        runs fused with the unmask (bd_lmhead_unmask_next), which rewrites the
+        rows of the positions it decodes."""
+        return self.input_rows_kept and not self.uses_compaction(S) and self.dims.B * S <= 64
+
+    def _make_rows_current(self):
+        """Embed the whole block into X (after the token state changed from
+        the host), so that DualCache steps can read their rows in place."""
+        dm = self.dims
+        ops.bd_embed_rows(self.W["E"], self.tokens, self.mask_bits, self.X, row_off=0, n_rows=dm.D,
+                          plant=self.plant)
+        self._rows_current = True
 
     def _lm_and_unmask(self, s: int, S: int, tau: float, bits_out=None):
         """LM head on the window's rows, then the threshold rule; the new mask
@@ -234,7 +266,8 @@ class BlockDecoder:
             ops.bd_lmhead_unmask(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"], w["conf"],
                                  self.tokens, self.mask_bits, win_lo=s * S, threshold=tau, max_logit=w["maxl"],
                                  lse=w["lse"], n_unmasked=self.n_unmasked, unmasked_pos=w["pos"],
-                                 mask_bits_host=bits_out)
+                                 mask_bits_host=bits_out,
+                                 next_rows=(self.W["E"], self.plant, self.X) if self.input_rows_kept else None)
             fused = True
         else:
             ops.bd_lmhead_confidence(self.H.view(-1, dm.hidden), w["row_idx"], self.W["Wlm"], w["argmax"],
@@ -259,29 +292,34 @@ class BlockDecoder:
         if eager or not self._replay("E", s, S, tau):
             dm = self.dims
             B, D = dm.B, dm.D
-            X, o = self._forward_rows(0, D)
+            X, xr, o = self._forward_rows(0, D)
             ops.bd_linear(o, dense(B * D), self.W["Wo"], self.H, rows(D, 1 + D, 1), M=B * D,
-                          res=X, rr=dense(B * D), guard=self._guard)
+                          res=X, rr=xr, guard=self._guard)
             self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
+            self._rows_current = self.keeps_rows(S)
             self._step_done()
 
     def dc_step(self, s: int, S: int, tau: float, eager: bool = False, bits_out=None):
         """DualCache step for window s (snapshot rows outside the window)."""
+        kept = self.keeps_rows(S)
+        if kept and not self._capturing and not self._rows_current:
+            self._make_rows_current()
         if eager or not self._replay("DC", s, S, tau):
             dm = self.dims
             B, D = dm.B, dm.D
-            X, o = self._forward_rows(s * S, S)
+            X, xr, o = self._forward_rows(s * S, S, kept=kept)
             ops.bd_linear(o, dense(B * S), self.W["Wo"], self.H, rows(S, 1 + D, 1 + s * S), M=B * S,
-                          res=X, rr=dense(B * S), guard=self._guard)
+                          res=X, rr=xr, guard=self._guard)
             self._lm_and_unmask(s, S, tau, bits_out)
         if not self._capturing:
+            self._rows_current = kept
             self._step_done()
 
     def _commit_kernels(self):
         dm = self.dims
         B, D = dm.B, dm.D
-        X, o = self._forward_rows(0, D)
+        X, _, o = self._forward_rows(0, D)
         ops.bd_linear(o, rows(1, D, D - 1), self.W["Wo"], self.H, rows(1, 1 + D, 0), M=B,
                       res=X, rr=rows(1, D, D - 1))
         ops.bd_kv_append(self.cache_k, self.cache_v, self.kv_len, self.blk_k, self.blk_v, n_rows=self.dims.D)
@@ -295,6 +333,7 @@ class BlockDecoder:
         if not self._replay("commit", 0, 0, 0.0):
             self._commit_kernels()
         self.kv_len_host = self.kv_len_host + D
+        self._rows_current = False
 
     def prefill(self, prompt):
         """Block-aligned prompt [B, P] under the hybrid mask (multi-block
@@ -453,6 +492,7 @@ class BlockDecoder:
         if g is not None and self._replay_ok(S, tau):
             g.replay()
             self.last = self._window(s, S)
+            self._rows_current = self.keeps_rows(S)
         else:
             self._guard = (self.mask_bits, ((1 << S) - 1) << (s * S), self.dims.B)
             try:
@@ -476,7 +516,10 @@ class BlockDecoder:
         for i in range(i0, i1):
             g = self.graphs.get(("P", s, i, parity))
             if g is not None and ok:
+                if i > 0 and self.keeps_rows(S) and not self._rows_current:
+                    self._make_rows_current()   # a DualCache slot reads its rows in place
                 g.replay()
+                self._rows_current = self.keeps_rows(S)
             else:
                 self._guard = (self.mask_bits, ((1 << S) - 1) << (s * S), self.dims.B)
                 try:

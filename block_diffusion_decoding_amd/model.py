@@ -45,6 +45,8 @@ class ModelDecoder(BlockDecoder):
 
     # a step slot past the end of a window still runs every layer: no window graphs
     window_graphs = False
+    # X is the residual stream of the step's rows, refilled by every step
+    input_rows_kept = False
     # below this many rows the MLP's RMSNorm is folded into the gate/up
     # projection (its streaming kernel takes the sums of squares from the A
     # fragments it loads anyway: 32.9 us against 37.3 for norm + projection at

@@ -172,12 +172,16 @@ def bd_lmhead_confidence_rows(h_src, row_idx, out_pos, m_dev, w, argmax, conf, *
 
 
 def bd_lmhead_unmask(h_src, row_idx, w, argmax, conf, tokens, mask_bits, *, win_lo, threshold, max_logit=None,
-                     lse=None, n_unmasked=None, unmasked_pos=None, mask_bits_host=None, ws=None, stream=None):
+                     lse=None, n_unmasked=None, unmasked_pos=None, mask_bits_host=None, next_rows=None, ws=None,
+                     stream=None):
     """LM head with fused confidence and the threshold unmask in one call:
     argmax/conf [B, win_len] (row b * win_len + r predicts position
     win_lo + r); tokens [B, D] int32, mask_bits [B] (64-bit) in/out;
     threshold a float or a [B] fp32 device tensor; mask_bits_host an
-    optional pinned host tensor [B] (64-bit) that receives the new bits."""
+    optional pinned host tensor [B] (64-bit) that receives the new bits;
+    next_rows = (E [V+1, hidden], plant [B, D, hidden] or None, x [B, D,
+    hidden]): the rows of the positions decoded here are rewritten in x
+    (bd_lmhead_unmask_next)."""
     lib = _lib.load()
     hidden = h_src.shape[-1]
     n_src = h_src.numel() // hidden
@@ -194,11 +198,22 @@ def bd_lmhead_unmask(h_src, row_idx, w, argmax, conf, tokens, mask_bits, *, win_
     need = lib.bd_lmhead_workspace_size(dt, B * win_len, hidden, V)
     if ws is None:
         ws = workspace(need, h_src.device, "lm")
-    st = lib.bd_lmhead_unmask(dt, B, D, win_lo, win_len, hidden, V, _p(h_src), n_src, _p(row_idx), _p(w),
-                              float(threshold), _p(tau_dev), _p(argmax), _p(conf), _p(max_logit), _p(lse),
-                              _p(tokens), _p(mask_bits), _p(n_unmasked), _p(unmasked_pos), _p(mask_bits_host),
-                              _p(ws), ws.numel(), _stream(stream))
-    _check("bd_lmhead_unmask", st)
+    if next_rows is None:
+        st = lib.bd_lmhead_unmask(dt, B, D, win_lo, win_len, hidden, V, _p(h_src), n_src, _p(row_idx), _p(w),
+                                  float(threshold), _p(tau_dev), _p(argmax), _p(conf), _p(max_logit), _p(lse),
+                                  _p(tokens), _p(mask_bits), _p(n_unmasked), _p(unmasked_pos), _p(mask_bits_host),
+                                  _p(ws), ws.numel(), _stream(stream))
+        _check("bd_lmhead_unmask", st)
+        return
+    E, plant, x = next_rows
+    assert E.dtype == x.dtype == w.dtype and E.shape == (V + 1, hidden) and x.shape == (B, D, hidden)
+    assert plant is None or (plant.dtype == x.dtype and plant.shape == x.shape)
+    nr = _lib.BdNextRows(_p(E), _p(plant), _p(x))
+    st = lib.bd_lmhead_unmask_next(dt, B, D, win_lo, win_len, hidden, V, _p(h_src), n_src, _p(row_idx), _p(w),
+                                   float(threshold), _p(tau_dev), _p(argmax), _p(conf), _p(max_logit), _p(lse),
+                                   _p(tokens), _p(mask_bits), _p(n_unmasked), _p(unmasked_pos), _p(mask_bits_host),
+                                   ctypes.byref(nr), _p(ws), ws.numel(), _stream(stream))
+    _check("bd_lmhead_unmask_next", st)
 
 
 def bd_candidate_rows(mask_bits, row_idx, out_pos, count, *, win_lo, win_len, rows_per_seq, stream=None):

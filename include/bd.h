@@ -327,6 +327,34 @@ bd_status bd_lmhead_unmask(bd_dtype dt, int B, int D, int win_lo, int win_len, i
                            int32_t* unmasked_pos, uint64_t* mask_bits_host,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* The next step's input rows, kept current by bd_lmhead_unmask_next: after
+ * the unmask, the row of every position it decoded becomes that token's
+ * embedding plus the position's plant, bit for bit as bd_embed_rows writes
+ * it (an invalid token: a NaN row); positions still masked keep the [MASK]
+ * row they hold.  A DualCache step that follows on the same window then
+ * needs no bd_embed_rows call ([v2 notes] Key design 2: a masked position
+ * is embedded as [MASK], a decoded one as its token).
+ *   embedding [V + 1, hidden] (the call's dtype and V)
+ *   plant     [B, D, hidden] or NULL
+ *   x         [B, D, hidden] the block's input rows (device; written)
+ * 16-byte aligned; hidden % 8 (bf16) or % 4 (fp32) == 0, else
+ * BD_EUNSUPPORTED. */
+typedef struct bd_next_rows {
+  const void* embedding;
+  const void* plant;
+  void* x;
+} bd_next_rows;
+
+/* bd_lmhead_unmask that also writes the next step's input rows (next may be
+ * NULL: then it is bd_lmhead_unmask). */
+bd_status bd_lmhead_unmask_next(bd_dtype dt, int B, int D, int win_lo, int win_len, int hidden, int V,
+                                const void* h_src, int n_src, const int32_t* row_idx, const void* w,
+                                float threshold, const float* threshold_dev,
+                                int32_t* argmax, float* conf, float* max_logit, float* lse,
+                                int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
+                                int32_t* unmasked_pos, uint64_t* mask_bits_host, const bd_next_rows* next,
+                                void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * bd_kv_append -- commit a finished block to the block-level cache ([v2
  * notes] Key design 3: a decoded block's K/V become read-only context; [v2

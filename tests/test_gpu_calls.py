@@ -326,6 +326,46 @@ def test_lmhead_unmask(name):
         assert np.array_equal(f[key][same], u[key][same]), f"{name}: {key} differs from the two-call path"
 
 
+@pytest.mark.parametrize("name", ["f32-tiny", "bf16-B16-S4-dev", "bf16-B5-S6", "bf16-B2-S32"])
+@pytest.mark.parametrize("planted", [False, True])
+def test_lmhead_unmask_next_rows_equal_embedding_of_new_state(name, planted):
+    """bd_lmhead_unmask_next: starting from the block's embedded rows, the
+    rows after the call equal bd_embed_rows of the new tokens and bits, bit
+    for bit (the decoded positions rewritten, every other row untouched),
+    and every other output equals bd_lmhead_unmask's."""
+    dt, B, S, D, win, hidden, V, hs, tau = FUSE_CASES[name]
+    say(f"[lmhead+unmask next rows] {name} plant={planted}")
+    T = tdt(dt)
+    n_src = B * (1 + D)
+    w = bi.normal(6, "Wlm", (V, hidden), 0.02, dt)
+    h = bi.normal(6, "h", (n_src, hidden), 0.02 * hs, dt)
+    E = up(bi.normal(6, "E", (V + 1, hidden), 0.5, dt), T)
+    plant = up(bi.normal(6, "plant", (B, D, hidden), 0.3, dt), T) if planted else None
+    rng = np.random.default_rng(B * S + V)
+    ridx = up(np.array([b * (1 + D) + win * S + r for b in range(B) for r in range(S)], dtype=np.int32))
+    masked = rng.random((B, D)) < 0.6
+    masked[0, win * S:(win + 1) * S] = True
+    tokens = np.where(masked, 0, rng.integers(0, V, size=(B, D))).astype(np.int32)
+    outs = []
+    for nxt in (True, False):
+        am = torch.zeros((B, S), dtype=torch.int32, device=DEV)
+        conf = torch.zeros((B, S), dtype=torch.float32, device=DEV)
+        t_tok, t_bits = up(tokens), up(bi.mask_bits(masked).view(np.int64))
+        x = torch.zeros(B, D, hidden, dtype=T, device=DEV)
+        ops().bd_embed_rows(E, t_tok, t_bits, x, row_off=0, n_rows=D, plant=plant)
+        ops().bd_lmhead_unmask(up(h, T), ridx, up(w, T), am, conf, t_tok, t_bits, win_lo=win * S, threshold=0.9,
+                               next_rows=(E, plant, x) if nxt else None)
+        ref = torch.zeros_like(x)
+        ops().bd_embed_rows(E, t_tok, t_bits, ref, row_off=0, n_rows=D, plant=plant)
+        torch.cuda.synchronize()
+        outs.append((am.cpu().numpy(), conf.cpu().numpy(), t_tok.cpu().numpy(), t_bits.cpu().numpy(), x, ref))
+    (a1, c1, k1, b1, x1, r1), (a0, c0, k0, b0, x0, _) = outs
+    assert np.array_equal(a1, a0) and np.array_equal(c1, c0) and np.array_equal(k1, k0) and np.array_equal(b1, b0)
+    assert int((bi.mask_bits(masked) ^ b1.view(np.uint64)).astype(bool).sum()) > 0  # something was decoded
+    assert torch.equal(x1.view(torch.int16 if dt == "bf16" else torch.int32),
+                       r1.view(torch.int16 if dt == "bf16" else torch.int32)), "next rows differ from the embedding"
+
+
 def test_lmhead_unmask_window_without_candidates():
     """No sequence has a masked position in the window: the call changes no
     token, bit or statistic (the LM head is skipped) and still writes the
