@@ -75,10 +75,10 @@ CALIB_BYTES = 1 << 30  # plain device copy that calibrates the HBM byte counters
 TRAFFIC = {
     "lm": {"file": "lmhead_7B_M64_traffic.json", "section": "lm",
            "sources": ("lmhead.hip", "stream_gemm.h", "bd_device.h", "bd_launch.h"),
-           "main": "lm_stream_kernel<4>", "then": "lm_merge_unmask_kernel",
-           "launch": "bd_lmhead_unmask: lm_stream_kernel<4> (512 work-groups, weight tiles with the "
-                     "non-temporal hint) + lm_merge_unmask_kernel (8 work-groups x 512), 64 rows x 152064 x 3584 "
-                     "(8 sequences x window of 8)"},
+           "main": "lm_stream_kernel<4, 4>", "then": "lm_merge_unmask_kernel",
+           "launch": "bd_lmhead_unmask: lm_stream_kernel<4, 4> (256 work-groups, one per CU, weight tiles with "
+                     "the non-temporal hint) + lm_merge_unmask_kernel (8 work-groups x 512), 64 rows x 152064 x "
+                     "3584 (8 sequences x window of 8)"},
     "attn_dualcache": {"file": "attention_long_context_dualcache_traffic.json", "section": "attn",
                        "sources": ("attn.hip", "bd_device.h", "bd_launch.h"),
                        "main": "attn_bf16_kernel<128, 32, 1,", "then": "attn_merge_kernel",
@@ -1190,7 +1190,7 @@ def main():
                              "included)"}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "bd_lmhead_unmask (lm_stream_kernel<4> + lm_merge_unmask_kernel: the LM head's final reduction "
+                "kernel": "bd_lmhead_unmask (lm_stream_kernel<4, 4> + lm_merge_unmask_kernel: the LM head's final reduction "
                           "with the threshold unmask), 64 rows x 152064 x 3584",
                 "algorithmic_bytes": lm_bytes, "launch_us_mean": round(lm_mean * 1e6, 2),
                 "launch_us_median": round(float(np.median(lm_t)) * 1e6, 2),
