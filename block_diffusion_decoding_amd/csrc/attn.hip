@@ -184,6 +184,14 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((bd_f32x2){lo, hi}, bd_bf16x2));
 }
 
+// max(a, b, c) in one instruction (fmaxf chains add NaN-quieting copies of
+// MFMA results)
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
@@ -274,8 +282,12 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
   bool tact[QPW];
   int qblk[QPW];  // visibility limit (exclusive) per query row
   uint4 qf[QPW][KS];
-  float m_run[QPW], l_run[QPW];
-  bd_f32x4 oacc[QPW][DH / 16];
+  // running max (log2 units) and, for the lazy test, the raw score above which
+  // it moves; running sums per lane (l_run, summed over the lanes at the end)
+  // or from the P.V MFMAs (lsum, below)
+  constexpr bool MS = NS > 4;  // not the 4-stage ring, whose 128 registers are full
+  float m_run[QPW], m_raw[QPW], l_run[QPW];
+  bd_f32x4 oacc[QPW][DH / 16], lsum[QPW];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     const int t = (qg * kWaves + wave) * QPW + j;
@@ -293,10 +305,18 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
     for (int ks = 0; ks < KS; ++ks)
       qf[j][ks] = rok ? *reinterpret_cast<const uint4*>(qp + 8 * g + 32 * ks) : make_uint4(0, 0, 0, 0);
     m_run[j] = BD_NEG_INF;
+    m_raw[j] = BD_NEG_INF;
     l_run[j] = 0.f;
+    lsum[j] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) oacc[j][dt] = bd_f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // Row sums of the probabilities (MS): one more P.V MFMA per query tile against
+  // an all-ones V^T tile, whose 16 output rows all equal sum_k P[q][k] of the
+  // same bf16 probabilities that weight V (no per-score adds in the softmax,
+  // and no cross-lane sum at the end)
+  const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+  const float inv_scale = 1.f / a.scale_log2;
   bool any_active = false;
 #pragma unroll
   for (int j = 0; j < QPW; ++j) any_active |= tact[j];
@@ -431,19 +451,31 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
           // contribution to a row uses it, so m_run only moves when some
           // score exceeds it by more than kLazyMax (probabilities stay below
           // 2^kLazyMax); otherwise no cross-lane reduction and no rescale.
-          float mx = s[j][0][0];
+          // (MS: the test is on raw scores, against m_raw = (m_run + kLazyMax) / scale)
+          float mx;
+          if constexpr (NKT == 2) {
+            mx = vmax3(vmax3(s[j][0][0], s[j][0][1], s[j][0][2]), vmax3(s[j][0][3], s[j][1][0], s[j][1][1]),
+                       vmax3(s[j][1][2], s[j][1][3], s[j][1][3]));
+          } else {
+            mx = s[j][0][0];
 #pragma unroll
-          for (int kt = 0; kt < NKT; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][kt][r]);
-          const float smx = mx * a.scale_log2;
-          if (__ballot(smx > m_run[j] + kLazyMax) != 0) {
+              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][kt][r]);
+          }
+          bool up;
+          if constexpr (MS) up = __ballot(mx > m_raw[j]) != 0;
+          else up = __ballot(mx * a.scale_log2 > m_run[j] + kLazyMax) != 0;
+          if (up) {
+            const float smx = mx * a.scale_log2;
             float mall = fmaxf(smx, __shfl_xor(smx, 16));
             mall = fmaxf(mall, __shfl_xor(mall, 32));
             const float mnew = fmaxf(m_run[j], mall);
             const float alpha = bd_exp2(m_run[j] - mnew);
             m_run[j] = mnew;
-            l_run[j] *= alpha;
+            if constexpr (MS) m_raw[j] = (mnew + kLazyMax) * inv_scale;
+            if constexpr (MS) lsum[j] *= alpha;
+            else l_run[j] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DH / 16; ++dt) oacc[j][dt] *= alpha;
           }
@@ -459,24 +491,24 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
               const float p1 = bd_exp2(__builtin_fmaf(sv[1], a.scale_log2, mneg));
               const float p2 = bd_exp2(__builtin_fmaf(sv[2], a.scale_log2, mneg));
               const float p3 = bd_exp2(__builtin_fmaf(sv[3], a.scale_log2, mneg));
-              ps += (p0 + p1) + (p2 + p3);
+              if constexpr (!MS) ps += (p0 + p1) + (p2 + p3);
               w[2 * h] = cvt_pk_bf16(p0, p1);
               w[2 * h + 1] = cvt_pk_bf16(p2, p3);
             }
             pf[j][u] = make_uint4(w[0], w[1], w[2], w[3]);
           }
-          l_run[j] += ps;
+          if constexpr (!MS) l_run[j] += ps;
           continue;
         }
         float mx = BD_NEG_INF;
         {
-          const int lim = min(kend, qblk[j]);
+          // key kbase + 16kt + 4g + r is visible iff 16kt + r < rel
+          const int rel = min(kend, qblk[j]) - kbase - 4 * g;
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int key = kbase + kt * 16 + 4 * g + r;
-              const float v = key < lim ? s[j][kt][r] * a.scale_log2 : BD_NEG_INF;
+              const float v = kt * 16 + r < rel ? s[j][kt][r] * a.scale_log2 : BD_NEG_INF;
               s[j][kt][r] = v;
               mx = fmaxf(mx, v);
             }
@@ -487,6 +519,7 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
         const float muse = (mnew == BD_NEG_INF) ? 0.f : mnew;
         const float alpha = bd_exp2(m_run[j] - muse);
         m_run[j] = mnew;
+        if constexpr (MS) m_raw[j] = (mnew + kLazyMax) * inv_scale;
         float ps = 0.f;
 #pragma unroll
         for (int u = 0; u < KT / 32; ++u) {
@@ -496,14 +529,15 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
             const bd_f32x4 sv = s[j][2 * u + h];
             const float p0 = bd_exp2(sv[0] - muse), p1 = bd_exp2(sv[1] - muse);
             const float p2 = bd_exp2(sv[2] - muse), p3 = bd_exp2(sv[3] - muse);
-            ps += (p0 + p1) + (p2 + p3);
+            if constexpr (!MS) ps += (p0 + p1) + (p2 + p3);
             w[2 * h] = cvt_pk_bf16(p0, p1);
             w[2 * h + 1] = cvt_pk_bf16(p2, p3);
           }
           pf[j][u] = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        l_run[j] = l_run[j] * alpha + ps;
+        if constexpr (!MS) l_run[j] = l_run[j] * alpha + ps;
         if (__ballot(alpha != 1.f) != 0) {  // the running max moved for some row
+          if constexpr (MS) lsum[j] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DH / 16; ++dt) oacc[j][dt] *= alpha;
         }
@@ -532,6 +566,10 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
           for (int j = 0; j < QPW; ++j)
             oacc[j][dt] = bd_mfma16(vf, pf[j][u], oacc[j][dt]);
         }
+        if constexpr (MS) {
+#pragma unroll
+          for (int j = 0; j < QPW; ++j) lsum[j] = bd_mfma16(ones, pf[j][u], lsum[j]);
+        }
       }
     }
   }
@@ -540,9 +578,14 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     if (!tact[j]) continue;
-    float l = l_run[j];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    float l;
+    if constexpr (MS) {
+      l = lsum[j][0];
+    } else {
+      l = l_run[j];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+    }
     const int r = ((qg * kWaves + wave) * QPW + j) * 16 + l16;
     if (r >= a.R) continue;
     const int i = r / a.G, hg = r % a.G;
