@@ -732,7 +732,9 @@ def oracle_one_thread(n_steps=3):
 def extras_persequence(w3, n_blocks=4):
     """The headline workload (7B shape, planted pass rate 0.5) decoded block by
     block with per-sequence window progression (one captured mixed step per
-    batched step) against the lockstep loop (window graphs), same blocks."""
+    batched step; queued: the schedule on the device and the steps replayed
+    back to back; host: the host schedules every step) against the lockstep
+    loop (window graphs), same blocks."""
     from block_diffusion_decoding_amd.decoder import Dims
     from block_diffusion_decoding_amd.persequence import PerSequenceDecoder
     cfg = bi.C3
@@ -746,16 +748,29 @@ def extras_persequence(w3, n_blocks=4):
     dec.set_synthetic_prefix(pre.kv_len, pre.cache_k, pre.cache_v, pre.carry)
     dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plants[0])
     dec.capture_step(cfg.tau)
-    dec.decode_block(cfg.tau)                     # warm-up block
-    torch.cuda.synchronize()
-    steps = 0
-    t0 = time.perf_counter()
-    for k in range(n_blocks):
-        dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plants[1 + k])
-        steps += dec.decode_block(cfg.tau)
-    torch.cuda.synchronize()
-    t_ps = time.perf_counter() - t0
-    del dec
+    dec.capture_step(cfg.tau, on_device=True)
+    ctx = (dec.kv_len.clone(), dec.cache_k.clone(), dec.cache_v.clone(), dec.H[:, 0].clone())
+
+    def run_ps(queued):
+        dec.kv_len.copy_(ctx[0])
+        dec.kv_len_host = ctx[0].cpu().numpy()
+        dec.cache_k.copy_(ctx[1])
+        dec.cache_v.copy_(ctx[2])
+        dec.H[:, 0].copy_(ctx[3])
+        decode = dec.decode_block_queued if queued else dec.decode_block
+        dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plants[0])
+        decode(cfg.tau)                           # warm-up block
+        torch.cuda.synchronize()
+        n = 0
+        t0 = time.perf_counter()
+        for k in range(n_blocks):
+            dec.set_block(np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool), plants[1 + k])
+            n += decode(cfg.tau)
+        torch.cuda.synchronize()
+        return n, time.perf_counter() - t0
+    steps_h, t_h = run_ps(False)
+    steps, t_ps = run_ps(True)
+    del dec, ctx
     torch.cuda.empty_cache()
     # lockstep (window graphs), the same blocks from the same context
     dec = make_decoder(cfg, w3, pre)
@@ -780,10 +795,14 @@ def extras_persequence(w3, n_blocks=4):
     tokens = n_blocks * cfg.B * cfg.D
     out["per_sequence_7B"] = {"blocks": n_blocks, "tokens": tokens,
                               "per_sequence": {"steps": steps, "ms": t_ps * 1e3, "tokens_per_s": tokens / t_ps,
-                                               "ms_per_step": t_ps / steps * 1e3},
+                                               "ms_per_step": t_ps / steps * 1e3, "schedule": "device, queued"},
+                              "per_sequence_host_schedule": {"steps": steps_h, "ms": t_h * 1e3,
+                                                             "tokens_per_s": tokens / t_h,
+                                                             "ms_per_step": t_h / steps_h * 1e3},
                               "lockstep": {"steps": loop.steps - s0, "ms": t_ls * 1e3, "tokens_per_s": tokens / t_ls,
                                            "ms_per_step": t_ls / (loop.steps - s0) * 1e3}}
-    log(f"[bench] per-sequence progression: {steps} steps, {tokens / t_ps:.0f} tokens/s; lockstep "
+    log(f"[bench] per-sequence progression: {steps} steps, {tokens / t_ps:.0f} tokens/s queued "
+        f"({tokens / t_h:.0f} with the host scheduling every step); lockstep "
         f"{loop.steps - s0} steps, {tokens / t_ls:.0f} tokens/s ({n_blocks} blocks)")
     del dec, loop
     torch.cuda.empty_cache()

@@ -260,6 +260,18 @@ bd_status bd_threshold_unmask_windows(int B, int D, int win_len, const int32_t* 
                                      n_unmasked, unmasked_pos, static_cast<hipStream_t>(stream), win_lo));
 }
 
+bd_status bd_persequence_schedule(int B, int D, int S, const uint64_t* mask_bits, int32_t* win, int32_t* opening,
+                                  int32_t* ran, uint64_t* restore, uint64_t* save, uint64_t* save_h,
+                                  int32_t* row_idx, int32_t* win_lo, int32_t* kinds, int32_t* live, void* stream) {
+  if (B < 0) return BD_EINVAL;
+  if (B == 0) return BD_OK;
+  if (S < 1 || D < S || D > 63 || D % S != 0 || (long)B * (1 + D) * 2 > INT32_MAX) return BD_EINVAL;
+  if (!mask_bits || !win || !opening || !ran || !restore || !save || !save_h || !row_idx || !win_lo)
+    return BD_EINVAL;
+  return hip_status(bd_persequence_schedule_launch(B, D, S, mask_bits, win, opening, ran, restore, save, save_h,
+                                                   row_idx, win_lo, kinds, live, static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------------------
 bd_status bd_copy_rows(int B, int n_rows, int row_bytes, const uint64_t* row_mask, const void* src0, void* dst0,
                        const void* src1, void* dst1, void* stream) {

@@ -177,6 +177,10 @@ hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* 
                             const int32_t* argmax, float threshold, const float* threshold_dev,
                             int32_t* tokens, uint64_t* mask_bits, int32_t* n_unmasked,
                             int32_t* unmasked_pos, hipStream_t s, const int32_t* win_lo_dev = nullptr);
+hipError_t bd_persequence_schedule_launch(int B, int D, int S, const uint64_t* mask_bits, int32_t* win,
+                                         int32_t* opening, int32_t* ran, uint64_t* restore, uint64_t* save,
+                                         uint64_t* save_h, int32_t* row_idx, int32_t* win_lo, int32_t* kinds,
+                                         int32_t* live, hipStream_t s);
 hipError_t bd_copy_rows_launch(int B, int n_rows, int row_bytes, const uint64_t* row_mask, const void* src0,
                                void* dst0, const void* src1, void* dst1, hipStream_t s);
 

@@ -56,6 +56,59 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(int n_rows, int row_byte
   }
 }
 
+// Per-sequence window schedule (one work-group; thread t takes sequences t,
+// t + blockDim.x, ...): the host's bookkeeping of per-sequence window
+// progression done on the device before each batched step, so that steps can
+// be queued without a host round trip.  A sequence that took part in the
+// previous step has opened its window; it then moves past every window with
+// no masked position left (opening the next one), and the step's inputs
+// follow from its window and whether the step opens it.  Rows of the LM
+// head's source buffer [2, B, 1 + D, hidden]: buffer 0 this step's output
+// rows, buffer 1 the snapshot rows (row 0 the carry); window position p reads
+// the output row of position p - 1, i.e. row p.
+__global__ __launch_bounds__(256) void persequence_schedule_kernel(int B, int D, int S, const uint64_t* mask_bits,
+                                                                   int32_t* win, int32_t* opening, int32_t* ran,
+                                                                   uint64_t* restore, uint64_t* save,
+                                                                   uint64_t* save_h, int32_t* row_idx,
+                                                                   int32_t* win_lo, int32_t* kinds, int32_t* live) {
+  __shared__ int any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  const int nw = D / S;
+  const uint64_t full = (1ull << D) - 1ull, wmask = (1ull << S) - 1ull;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const uint64_t bits = mask_bits[b];
+    int w = win[b], op = opening[b];
+    if (ran[b]) op = 0;
+    while (w < nw && ((bits >> (w * S)) & wmask) == 0) {
+      ++w;
+      op = 1;
+    }
+    const bool active = w < nw;
+    win[b] = w;
+    opening[b] = op;
+    ran[b] = active ? 1 : 0;
+    const int w0 = active ? w * S : 0;
+    const uint64_t wb = wmask << w0;
+    restore[b] = active && !op ? (full & ~wb) : 0ull;
+    save[b] = active && op ? full : 0ull;
+    save_h[b] = active && op ? (((full << 1) | 1ull) ^ 1ull) : 0ull;  // output rows 1 .. D
+    win_lo[b] = active ? w0 : D;
+    for (int j = 0; j < S; ++j) {
+      const int q = w0 + j - 1;  // the token shift: position w0 + j reads the output of position q
+      const bool fresh = op || q >= w0;
+      int r;
+      if (q < 0 || !active) r = (B + b) * (1 + D);
+      else r = (fresh ? b : B + b) * (1 + D) + q + 1;
+      row_idx[(size_t)b * S + j] = r;
+    }
+    if (kinds != nullptr) kinds[b] = active ? 2 * w + (op ? 0 : 1) : -1;
+    if (active) any = 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && live != nullptr && any) live[0] += 1;
+}
+
 // One work-group per sequence: copy n_rows in-block rows behind the committed
 // rows of every KV head, then advance the committed length.
 __global__ __launch_bounds__(256) void append_kernel(int Hkv, int row_bytes, int cap, uint8_t* k_cache,
@@ -129,6 +182,15 @@ hipError_t bd_unmask_launch(int B, int D, int win_lo, int win_len, const float* 
                             int32_t* n_unmasked, int32_t* unmasked_pos, hipStream_t s, const int32_t* win_lo_dev) {
   hipLaunchKernelGGL(unmask_kernel, dim3(B), dim3(64), 0, s, D, win_lo, win_len, conf, argmax, threshold,
                      threshold_dev, win_lo_dev, tokens, mask_bits, n_unmasked, unmasked_pos);
+  return hipGetLastError();
+}
+
+hipError_t bd_persequence_schedule_launch(int B, int D, int S, const uint64_t* mask_bits, int32_t* win,
+                                         int32_t* opening, int32_t* ran, uint64_t* restore, uint64_t* save,
+                                         uint64_t* save_h, int32_t* row_idx, int32_t* win_lo, int32_t* kinds,
+                                         int32_t* live, hipStream_t s) {
+  hipLaunchKernelGGL(persequence_schedule_kernel, dim3(1), dim3(256), 0, s, B, D, S, mask_bits, win, opening, ran,
+                     restore, save, save_h, row_idx, win_lo, kinds, live);
   return hipGetLastError();
 }
 

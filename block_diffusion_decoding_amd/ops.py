@@ -266,6 +266,21 @@ def bd_copy_rows(row_mask, src0, dst0, src1=None, dst1=None, *, stream=None):
     _check("bd_copy_rows", st)
 
 
+def bd_persequence_schedule(mask_bits, state, restore, save, save_h, row_idx, win_lo, *, D, S, kinds=None,
+                            live=None, stream=None):
+    """mask_bits [B] (64-bit) device; state [3, B] int32 device (win, opening,
+    ran); restore/save/save_h [B] 64-bit; row_idx [B * S] int32; win_lo [B]
+    int32; kinds [B] int32 or None; live [1] int32 or None."""
+    lib = _lib.load()
+    B = mask_bits.shape[0]
+    assert state.shape == (3, B) and state.dtype == torch.int32 and state.is_contiguous()
+    assert row_idx.numel() == B * S and win_lo.numel() == B
+    st = lib.bd_persequence_schedule(B, D, S, _p(mask_bits), _p(state[0]), _p(state[1]), _p(state[2]),
+                                     _p(restore), _p(save), _p(save_h), _p(row_idx), _p(win_lo), _p(kinds),
+                                     _p(live), _stream(stream))
+    _check("bd_persequence_schedule", st)
+
+
 def bd_kv_append(k_cache, v_cache, kv_len, k_blk, v_blk, *, n_rows, kv_len_host=None, row_off=0, stream=None):
     """k/v_cache [B, Hkv, cap, d]; kv_len [B] int32 (in/out); k/v_blk [B, n_blk, Hkv, d];
     appends rows row_off .. row_off + n_rows - 1 of each sequence's k/v_blk."""

@@ -27,7 +27,12 @@ One step, every arithmetic part a libbd call:
 Row buffers: Hcat [2, B, 1 + D, hidden]: Hcat[0] holds this step's output rows,
 Hcat[1] the snapshot rows (row 0 = carry).  The step is captured as one HIP
 graph; the host writes the per-sequence windows, row lists and row masks
-before each replay.
+before each replay (step, decode_block).  Queued mode (decode_block_queued):
+the same bookkeeping runs on the device (bd_persequence_schedule, first in
+the captured step), so the steps are replayed back to back, one ahead of the
+host, which only reads the mask bits to stop after the block is done; a step
+queued after that finds every sequence finished and changes nothing that the
+commit keeps (the commit recomputes the block's rows from its tokens).
 """
 from __future__ import annotations
 
@@ -67,6 +72,11 @@ class PerSequenceDecoder(BlockDecoder):
         i32 = self._inbuf[3 * B:].view(torch.int32)
         self.row_idx, self.win_lo = i32[:B * S], i32[B * S:B * S + B]
         self._graph = None
+        # device schedule (queued mode): win, opening, ran [3, B]; live-step count; kinds [B]
+        self.ps_state = torch.zeros(3, B, dtype=torch.int32, device=dev)
+        self.ps_live = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ps_kinds = torch.zeros(B, dtype=torch.int32, device=dev)
+        self._qgraph = None
         self.win = np.zeros(B, np.int64)         # current window per sequence (D // S = block done)
         self.opening = np.ones(B, bool)          # next step opens the window (exact step)
         self.own_steps = np.zeros(B, np.int64)
@@ -109,10 +119,13 @@ class PerSequenceDecoder(BlockDecoder):
         self._inbuf.copy_(self._stage, non_blocking=True)
 
     # ---------------------------------------------------------------- step
-    def _kernels(self, tau):
+    def _kernels(self, tau, on_device: bool = False):
         dm, W = self.dims, self.W
         B, D, S, hid = dm.B, dm.D, self.S, dm.hidden
         X = self.X
+        if on_device:   # the windows, row list and masks from the device state
+            ops.bd_persequence_schedule(self.mask_bits, self.ps_state, self.restore, self.save, self.save_h,
+                                        self.row_idx, self.win_lo, D=D, S=S, kinds=self.ps_kinds, live=self.ps_live)
         ops.bd_embed_rows(W["E"], self.tokens, self.mask_bits, X, row_off=0, n_rows=D, plant=self.plant)
         kr = rows(D, D, 0)
         ops.bd_qkv_proj(X, dense(B * D), W["Wq"], self.q, dense(B * D), W["Wk"], W["Wv"], self.blk_k, kr,
@@ -130,8 +143,10 @@ class PerSequenceDecoder(BlockDecoder):
         ops.bd_copy_rows(self.save_h, self.Hcat[0], self.Hcat[1])
         self.bits_host.copy_(self.mask_bits, non_blocking=True)
 
-    def capture_step(self, tau: float):
-        """Capture the step as one HIP graph (every workspace sized first)."""
+    def capture_step(self, tau: float, on_device: bool = False):
+        """Capture the step as one HIP graph (every workspace sized first);
+        on_device: the queued mode's step, which starts with the device
+        schedule."""
         dm = self.dims
         B, D = dm.B, dm.D
         if self.plant is None:
@@ -145,8 +160,11 @@ class PerSequenceDecoder(BlockDecoder):
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self._kernels(tau)
-        self._graph, self._graph_tau_ps = g, tau
+            self._kernels(tau, on_device)
+        if on_device:
+            self._qgraph, self._qgraph_tau = g, tau
+        else:
+            self._graph, self._graph_tau_ps = g, tau
         torch.cuda.synchronize()
 
     def _advance(self, bits):
@@ -191,3 +209,37 @@ class PerSequenceDecoder(BlockDecoder):
             n += 1
         self.commit()
         return n
+
+    def decode_block_queued(self, tau: float) -> int:
+        """decode_block with the schedule on the device (needs
+        capture_step(tau, on_device=True)): the captured step is replayed back
+        to back, one step ahead of the host, which waits for the step before
+        the one just queued and stops once the mask bits of the block are all
+        clear.  Returns the batched steps in which some sequence took part
+        (those of decode_block)."""
+        assert self._qgraph is not None and tau == self._qgraph_tau, "capture_step(tau, on_device=True) first"
+        D = self.dims.D
+        self.begin_block()
+        self.ps_state[0].zero_()
+        self.ps_state[1].fill_(1)
+        self.ps_state[2].zero_()
+        self.ps_live.zero_()
+        full = np.uint64((1 << D) - 1)
+        bits = self.bits_host.numpy().view(np.uint64)
+        prev = None
+        # every step with a sequence in it decodes at least one of its masked
+        # positions, so D steps finish the block; the host sees that one later
+        for _ in range(D + 2):
+            self._qgraph.replay()
+            ev = torch.cuda.Event()
+            ev.record()
+            if prev is not None:
+                prev.synchronize()
+                if not (bits & full).any():   # bits of that step or a later one: the block is done
+                    break
+            prev = ev
+        else:
+            raise RuntimeError("per-sequence block did not finish within D + 2 steps")
+        self._step_done()
+        self.commit()
+        return int(self.ps_live.item())

@@ -14,7 +14,8 @@
  *     (only the masked candidates)      bd_candidate_rows + bd_lmhead_confidence_rows
  *   confidence-threshold unmasking      bd_threshold_unmask
  *     (LM head + unmask, one call)      bd_lmhead_unmask
- *     (per-sequence windows)            bd_threshold_unmask_windows, bd_copy_rows
+ *     (per-sequence windows)            bd_threshold_unmask_windows, bd_copy_rows,
+ *                                       bd_persequence_schedule
  *   (block finished) cache append       bd_kv_append
  *
  * Sources, by page title and section:
@@ -279,6 +280,45 @@ bd_status bd_threshold_unmask_windows(int B, int D, int win_len, const int32_t* 
                                       const float* conf, const int32_t* argmax, float threshold,
                                       int32_t* tokens, uint64_t* mask_bits,
                                       int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
+
+/* Per-sequence window schedule on the device, so that the batched steps of
+ * per-sequence window progression can be queued without a host round trip
+ * ([v2 notes] Key designs 3 and 4: windows of S positions decoded left to
+ * right, each opened by an exact step that refreshes the DualCache snapshot).
+ * Before each step every sequence b updates its state and writes the step's
+ * inputs:
+ *   state, device int32 [B] each, kept between steps (a block starts with
+ *   win = 0, opening = 1, ran = 0):
+ *     win[b]      current window (D / S: the sequence has finished the block)
+ *     opening[b]  1 when this step opens window win[b] (an exact step)
+ *     ran[b]      1 when the sequence took part in the previous step
+ *   update: if ran[b], opening[b] = 0; then while win[b] < D / S and
+ *     positions [S win[b], S win[b] + S) of mask_bits[b] are all clear:
+ *     win[b] += 1, opening[b] = 1; finally ran[b] = (win[b] < D / S).
+ *   outputs, device (written for every b):
+ *     restore[b], save[b], save_h[b] uint64   bd_copy_rows masks: a DualCache
+ *         sequence restores its snapshot K/V rows outside its window
+ *         (restore); an opening sequence saves its K/V rows 0 .. D-1 (save)
+ *         and output rows 1 .. D (save_h) as its new snapshot; 0 otherwise
+ *     row_idx [B * S] int32   LM-head source rows in a row buffer
+ *         [2, B, 1 + D, hidden] (buffer 0: this step's output rows; buffer 1:
+ *         the snapshot rows, row 0 the carry): window position p reads row p
+ *         of its sequence (the output of position p - 1), from buffer 0 when
+ *         the step opens the window or p - 1 lies in it, else from buffer 1;
+ *         a finished sequence and position 0 read the carry
+ *     win_lo [B] int32        S win[b], or D for a finished sequence (for
+ *                             bd_threshold_unmask_windows)
+ *     kinds [B] int32 or NULL 2 win[b] + 1 for a DualCache step, 2 win[b]
+ *                             for an opening step, -1 when finished
+ *     live [1] int32 or NULL  incremented when some sequence takes part
+ * mask_bits [B] (the batch's bits before the step) is read only.  One
+ * work-group; the call is asynchronous on `stream`.  Requires
+ * 1 <= S <= D <= 63 and D % S == 0 (BD_EINVAL otherwise or for a NULL
+ * required pointer). */
+bd_status bd_persequence_schedule(int B, int D, int S, const uint64_t* mask_bits, int32_t* win,
+                                  int32_t* opening, int32_t* ran, uint64_t* restore, uint64_t* save,
+                                  uint64_t* save_h, int32_t* row_idx, int32_t* win_lo, int32_t* kinds,
+                                  int32_t* live, void* stream);
 
 /* Per-sequence masked row copy (support for per-sequence window progression:
  * restoring a sequence's DualCache snapshot rows outside its window, saving

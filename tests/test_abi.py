@@ -32,7 +32,8 @@ def test_header_declares_the_four_calls_and_support():
               "bd_lmhead_workspace_size", "bd_status_string", "bd_last_hip_error", "bd_version",
               "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu", "bd_gate_up_swiglu_rmsnorm",
               "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau",
-              "bd_lmhead_unmask", "bd_threshold_unmask_windows", "bd_copy_rows", "bd_block_attn_noalloc"]:
+              "bd_lmhead_unmask", "bd_threshold_unmask_windows", "bd_copy_rows", "bd_block_attn_noalloc",
+              "bd_persequence_schedule"]:
         assert n in names
 
 
@@ -317,6 +318,12 @@ def test_per_sequence_window_calls_argument_errors():
     assert cp(n=65) == E and cp(rb=3000) == E and cp(mask=None) == E and cp(s1=FAKE) == E
     assert cp(s1=FAKE + 8, d1=FAKE) == E          # misaligned
     assert cp(B=0) == 0 and cp(n=0) == 0
+    sc = lambda **k: lib.bd_persequence_schedule(k.get("B", 4), k.get("D", 32), k.get("S", 8), k.get("bits", FAKE),
+                                                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("rows", FAKE), FAKE,
+                                                 None, None, None)
+    assert sc(B=-1) == E and sc(S=0) == E and sc(D=64, S=8) == E and sc(D=32, S=12) == E and sc(D=4, S=8) == E
+    assert sc(bits=None) == E and sc(rows=None) == E
+    assert sc(B=0) == 0
 
 
 def test_guard_argument_errors():

@@ -210,3 +210,117 @@ def test_graph_keeps_plant_and_workspaces_after_reset_and_growth():
         n += 1
         assert n < 4 * cfg.D
     say(f"    {n} steps replayed, bit-identical to eager")
+
+
+# --------------------------------------------------------------------------
+# queued mode: the schedule on the device
+# --------------------------------------------------------------------------
+def schedule_rule(B, D, S, bits, win, opening, ran):
+    """The per-sequence schedule as bd.h states it, one sequence at a time."""
+    nw = D // S
+    full, wmask = (1 << D) - 1, (1 << S) - 1
+    out = {k: np.zeros(B, np.int64) for k in ("win", "opening", "ran", "win_lo", "kinds")}
+    out.update({k: np.zeros(B, np.uint64) for k in ("restore", "save", "save_h")})
+    row_idx = np.zeros((B, S), np.int64)
+    live = 0
+    for b in range(B):
+        w, op = int(win[b]), int(opening[b])
+        if ran[b]:
+            op = 0
+        while w < nw and (int(bits[b]) >> (w * S)) & wmask == 0:
+            w, op = w + 1, 1
+        active = w < nw
+        live |= active
+        w0 = w * S if active else 0
+        out["win"][b], out["opening"][b], out["ran"][b] = w, op, int(active)
+        out["restore"][b] = (full & ~(wmask << w0)) if active and not op else 0
+        out["save"][b] = full if active and op else 0
+        out["save_h"][b] = (full << 1) if active and op else 0
+        out["win_lo"][b] = w0 if active else D
+        out["kinds"][b] = 2 * w + (0 if op else 1) if active else -1
+        for j in range(S):
+            q = w0 + j - 1
+            if q < 0 or not active:
+                row_idx[b, j] = (B + b) * (1 + D)
+            else:
+                row_idx[b, j] = (b if (op or q >= w0) else B + b) * (1 + D) + q + 1
+    return out, row_idx, live
+
+
+@pytest.mark.parametrize("B,D,S", [(40, 32, 8), (300, 32, 4), (9, 48, 16), (64, 63, 9), (5, 8, 8)])
+def test_persequence_schedule_against_the_rule(B, D, S):
+    """bd_persequence_schedule against the rule of its declaration, over three
+    calls in a row (the state carried between them, bits cleared in between):
+    state, copy masks, LM-head rows, windows, kinds and the live count, bit
+    for bit."""
+    from gpu_util import up
+    from block_diffusion_decoding_amd import ops as o
+    say(f"[per-sequence] schedule B={B} D={D} S={S}")
+    rng = np.random.default_rng(B * 131 + D + S)
+    nw = D // S
+    masked = rng.random((B, D)) < rng.choice([0.0, 0.05, 0.3, 0.9], size=(B, 1))
+    masked[:3] = [np.zeros(D, bool), np.ones(D, bool), np.arange(D) >= D - S]
+    state = np.stack([rng.integers(0, nw + 1, B), rng.integers(0, 2, B), rng.integers(0, 2, B)]).astype(np.int32)
+    t_state = up(state)
+    t_bits = up(bi.mask_bits(masked).view(np.int64))
+    masks = torch.zeros(3, B, dtype=torch.int64, device=DEV)
+    rows_t = torch.full((B * S,), -7, dtype=torch.int32, device=DEV)
+    lo = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    kinds = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    live = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ref_live = 0
+    for call in range(3):
+        bits = bi.mask_bits(masked)
+        ref, ref_rows, any_active = schedule_rule(B, D, S, bits, *state)
+        ref_live += int(any_active)
+        o.bd_persequence_schedule(t_bits, t_state, masks[0], masks[1], masks[2], rows_t, lo, D=D, S=S, kinds=kinds,
+                                  live=live)
+        got_state = t_state.cpu().numpy()
+        got_masks = masks.cpu().numpy().view(np.uint64)
+        what = f"call {call}"
+        assert np.array_equal(got_state[0], ref["win"]) and np.array_equal(got_state[1], ref["opening"]), what
+        assert np.array_equal(got_state[2], ref["ran"]), what
+        for i, k in enumerate(("restore", "save", "save_h")):
+            assert np.array_equal(got_masks[i], ref[k]), (what, k)
+        assert np.array_equal(rows_t.cpu().numpy().reshape(B, S), ref_rows), what
+        assert np.array_equal(lo.cpu().numpy(), ref["win_lo"]) and np.array_equal(kinds.cpu().numpy(), ref["kinds"])
+        assert int(live.item()) == ref_live, what
+        state = got_state
+        # the step decodes something in some of the active windows
+        for b in range(B):
+            if state[2][b]:
+                w0 = int(state[0][b]) * S
+                pos = np.flatnonzero(masked[b, w0:w0 + S])
+                if len(pos) and rng.random() < 0.7:
+                    masked[b, w0 + rng.choice(pos, size=rng.integers(1, len(pos) + 1), replace=False)] = False
+        t_bits.copy_(up(bi.mask_bits(masked).view(np.int64)))
+
+
+def test_per_sequence_queued_equals_host_schedule():
+    """The queued mode (schedule on the device, steps replayed back to back)
+    against the host-scheduled captured steps on the same two blocks: tokens,
+    mask bits, the committed cache and lengths, the carry and the number of
+    batched steps, bit for bit (the host-scheduled path is the one checked
+    against the oracle above)."""
+    cfg = MID
+    say(f"[per-sequence] queued vs host schedule, {cfg.name}")
+    w, pre, st, plant, _ = workload(cfg, 0, all_masked=True, plant_rate=1.0)
+    plant = np.array(plant, copy=True)
+    keep = np.random.default_rng(5).random((cfg.B, cfg.D)) < np.array([0.9, 0.6, 0.3, 0.05])[:, None]
+    plant[~keep] = 0.0
+    plant2 = np.roll(plant, 1, axis=0)
+    host = make_decoder(cfg, w, pre, st, plant)
+    queued = make_decoder(cfg, w, pre, st, plant)
+    host.capture_step(cfg.tau)
+    queued.capture_step(cfg.tau, on_device=True)
+    for blk, pl in enumerate((plant, plant2)):
+        if blk:
+            for dec in (host, queued):
+                dec.set_block(st.tokens, st.masked, pl)
+        n_host = host.decode_block(cfg.tau)
+        n_queued = queued.decode_block_queued(cfg.tau)
+        torch.cuda.synchronize()
+        say(f"    block {blk}: {n_host} steps (host schedule), {n_queued} (device schedule)")
+        assert n_host == n_queued
+        for name in ("tokens", "mask_bits", "kv_len", "cache_k", "cache_v", "H"):
+            assert torch.equal(getattr(host, name), getattr(queued, name)), (blk, name)
