@@ -47,7 +47,7 @@ constexpr int kThreads = 256;  // merge and fp32 kernels
 #define BD_ATTN_TARGET_WGS 256
 #endif
 #ifndef BD_ATTN_MIN_CHUNK
-#define BD_ATTN_MIN_CHUNK 256
+#define BD_ATTN_MIN_CHUNK 128
 #endif
 // committed K/V of a call larger than this stream through with the
 // non-temporal hint (they cannot stay cached until the next step anyway)
