@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kAttnThreads, (QPW == 4 ? 1 : (NS <= 4 && QPW == 1 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar DMA bases
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
