@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_stream_kernel(GemmS a, int P
   using C = bd_stream::Cfg<MT, NTW, kNS>;
   static_assert(C::NTP % 2 == 0, "a wave holds whole gate/up tile pairs");
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int m0 = blockIdx.y * MT * 16;
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(GemmS a, int r
   using P = GBig<CT>;
   __shared__ uint4 sbuf[P::NS * P::STAGE_U4];
   if (bd_guard_dead(a.g_bits, a.g_mask, a.g_n)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int wr = wave % P::WR, wc = wave / P::WR;
   // work-group w runs on XCD w % 8; its (w / 8)-th work-group takes the next

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void lm_stream_kernel(L
   using C = LmCfg<MT, NWV>;
   __shared__ uint4 sbuf[C::NS * C::STAGE_U4];
   __shared__ BdArgStat red[C::WN * MT * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int m0 = blockIdx.y * MT * 16;
@@ -413,7 +413,7 @@ template <int CT>
 __global__ __launch_bounds__(kBigThreads, 1) void lm_big_kernel(LmK a, int rb_count, int cb_count) {
   using P = Big<CT>;
   __shared__ uint4 sbuf[P::NS * P::STAGE_U4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int wr = wave % P::WR, wc = wave / P::WR;
   // XCD-aware order: work-group w runs on XCD w % 8; the (w / 8)-th work-group
