@@ -902,7 +902,11 @@ def stored_traffic(kind: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    return rec.get("bytes_per_launch") if rec.get("kernel_source_hash") == kernel_source_hash(kind) else None
+    if rec.get("kernel_source_hash") != kernel_source_hash(kind):
+        log(f"[bench] traffic record {TRAFFIC[kind]['file']} was measured on other sources of its kernels: "
+            f"traffic reported as null (retake it with --traffic-from)")
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def extras_attn(c4, reps):

@@ -4,7 +4,10 @@ pipelined runs (whole windows queued ahead of the host over at most two
 blocks with two ring parities, the oldest read back while later ones run;
 slots of one window with one wait at the ends) book exactly the steps,
 tokens, commits and per-block schedules of the same loop taken one step at
-a time, and book them from rings no later block has overwritten."""
+a time, and book them from rings no later block has overwritten.  Also: the
+committed traffic records belong to the current kernel sources."""
+import json
+import os
 from types import SimpleNamespace
 
 import numpy as np
@@ -158,3 +161,16 @@ def test_pipelined_whole_blocks_book_like_single_steps():
             b.step()
         assert a.blk == blk and a.dec.inflight == []
         assert _state(a) == _state(b), blk
+
+
+def test_traffic_records_match_the_kernel_sources():
+    """Every committed HBM traffic record under profiles/ was measured on the
+    current sources of its kernels (bench.py reports it only then): a kernel
+    change without a new counter run fails here rather than silently turning
+    the reported traffic into null."""
+    import bench
+    for kind, spec in bench.TRAFFIC.items():
+        rec = json.load(open(os.path.join(bench.ROOT, "profiles", spec["file"])))
+        assert rec["kernel_source_hash"] == bench.kernel_source_hash(kind), \
+            f"{spec['file']}: retake the FETCH_SIZE/WRITE_SIZE passes of bench.py --section {spec['section']}"
+        assert rec["bytes_per_launch"] > 0
