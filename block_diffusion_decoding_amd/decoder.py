@@ -500,11 +500,10 @@ class BlockDecoder:
                     (self.e_step if i == 0 else self.dc_step)(s, S, tau, eager=True, bits_out=ring[parity, s, i])
             finally:
                 self._guard = None
-        self._bits_ev.record()
         self._bits_fresh = False
         if not wait:
             return None
-        self._bits_ev.synchronize()
+        self.wait()
         return self.window_bits(s, S, parity)
 
     def run_slots(self, s: int, S: int, tau, i0: int, i1: int, parity: int = 0):
@@ -527,11 +526,14 @@ class BlockDecoder:
                 finally:
                     self._guard = None
         self.last = self._window(s, S)
-        self._bits_ev.record()
         self._bits_fresh = False
 
     def wait(self):
-        """Wait for the queued steps (their mask bits are then on the host)."""
+        """Wait for the queued steps (their mask bits are then on the host).
+        Queued windows and slots record no event of their own (an event
+        record is a barrier with a cache release between two graphs); the
+        wait records one after them."""
+        self._bits_ev.record()
         self._bits_ev.synchronize()
 
     def fence(self) -> torch.cuda.Event:
