@@ -296,14 +296,15 @@ def test_persequence_schedule_against_the_rule(B, D, S):
         t_bits.copy_(up(bi.mask_bits(masked).view(np.int64)))
 
 
-def test_per_sequence_queued_equals_host_schedule():
+@pytest.mark.parametrize("S", [4, 8, 16])
+def test_per_sequence_queued_equals_host_schedule(S):
     """The queued mode (schedule on the device, steps replayed back to back)
     against the host-scheduled captured steps on the same two blocks: tokens,
     mask bits, the committed cache and lengths, the carry and the number of
     batched steps, bit for bit (the host-scheduled path is the one checked
-    against the oracle above)."""
-    cfg = MID
-    say(f"[per-sequence] queued vs host schedule, {cfg.name}")
+    against the oracle above), for windows of 4, 8 and 16 positions."""
+    cfg = replace(MID, S=S)
+    say(f"[per-sequence] queued vs host schedule, {cfg.name} S={S}")
     w, pre, st, plant, _ = workload(cfg, 0, all_masked=True, plant_rate=1.0)
     plant = np.array(plant, copy=True)
     keep = np.random.default_rng(5).random((cfg.B, cfg.D)) < np.array([0.9, 0.6, 0.3, 0.05])[:, None]
