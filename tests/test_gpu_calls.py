@@ -186,8 +186,10 @@ def test_lmhead_7B_batched_sampled():
 # bd_threshold_unmask (bit-exact)
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("D,S,win", [(32, 8, 0), (32, 8, 3), (32, 32, 0), (64, 8, 7), (64, 64, 0), (8, 4, 1)])
-@pytest.mark.parametrize("tau", [0.9, 1.0, 0.3])
+@pytest.mark.parametrize("tau", [0.9, 1.0, 0.3, 0.0])
 def test_threshold_unmask(D, S, win, tau):
+    """Bit for bit against the oracle's rule; tau = 1.0 passes nothing (one
+    fallback token per step), tau = 0.0 every candidate."""
     say(f"[unmask] D={D} S={S} win={win} tau={tau}")
     B = 37
     rng = np.random.default_rng(D * 100 + S + win)
