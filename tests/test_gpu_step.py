@@ -50,7 +50,11 @@ def force(dec, seqs):
     dec.set_tokens(np.stack([q.tokens for q in seqs]), np.stack([q.masked for q in seqs]))
 
 
-@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96], ids=["tiny-64", "tiny-96"])
+# blocks of 64 positions: the most a sequence's 64-bit mask word holds
+TINY_D64 = replace(bi.C1, name="c1-D64", D=64, S=16)
+
+
+@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96, TINY_D64], ids=["tiny-64", "tiny-96", "tiny-D64"])
 def test_tiny_prefill_and_commit_equal_oracle_cache(cfg):
     say(f"[step] prefill+commit {cfg.name}")
     w, pre, st, _, _ = workload(cfg, 0, all_masked=True)
@@ -66,8 +70,14 @@ def test_tiny_prefill_and_commit_equal_oracle_cache(cfg):
         rows_close(down(dec.H)[b, 0], q.carry, TOL[cfg.dtype], "carry")
 
 
-@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96, replace(bi.C1, S=4), replace(bi.C1_96, S=16)],
-                         ids=["tiny-64", "tiny-96", "tiny-64-S4", "tiny-96-S16"])
+# bf16 at unit LM-head scale, as the bf16 workloads (c1's scale sharpens fp32 logits)
+TINY_D64_BF16 = replace(TINY_D64, name="c1-D64-bf16", dtype="bf16", S=64, lm_scale=1.0)
+
+
+@pytest.mark.parametrize("cfg", [bi.C1, bi.C1_96, replace(bi.C1, S=4), replace(bi.C1_96, S=16), TINY_D64,
+                                 replace(TINY_D64, S=64), TINY_D64_BF16],
+                         ids=["tiny-64", "tiny-96", "tiny-64-S4", "tiny-96-S16", "tiny-D64-S16", "tiny-D64-S64",
+                              "tiny-D64-S64-bf16"])
 @pytest.mark.parametrize("mode", ["exact", "dual"])
 def test_tiny_block_decode_teacher_forced(cfg, mode):
     say(f"[step] tiny block loop {cfg.name} {mode}")
