@@ -1053,6 +1053,20 @@ def extras_lm(w3, reps):
     out["lmhead_unmask_7B_B8_S8"] = {"us_with_bits_reset": mean * 1e6, **t.record(), "GB/s": nbytes / mean / 1e9,
                                      "frac_hbm": nbytes / mean / 1e9 / HBM_PEAK_GBS}
     log(f"[bench] lm head + unmask B=8 S=8: {mean * 1e6:.1f} us with the bits reset, {nbytes / mean / 1e9:.0f} GB/s")
+    # ---- the 64-row LM head's load pattern alone (bd_probe_weight_stream: the
+    # same global->LDS stages over the same weights, no arithmetic), with and
+    # without the 64 rows of h per stage, at the LM head's 256 work-groups and
+    # at 512: the floor of the load design, to set the LM head against
+    h64 = torch.randn(64, 3584, device="cuda", dtype=T) * 0.05
+    probe = {}
+    for wgs in (256, 512):
+        for with_x in (False, True):
+            tp = time_call(lambda: ops.bd_probe_weight_stream(Wlm, h64 if with_x else None, work_groups=wgs), reps)
+            probe[f"{'w_and_x' if with_x else 'w_only'}_{wgs}"] = {**tp.record(), "GB/s": Wlm.numel() * 2 / tp.mean / 1e9}
+    out["lmhead_7B_M64_load_pattern"] = {**probe, "what": "bd_probe_weight_stream over the 7B head (1.09 GB): "
+                                         "the streaming LM head's loads with no arithmetic; w_and_x adds its 64 "
+                                         "rows of h to every stage"}
+    log("[bench] lm head load pattern alone: " + ", ".join(f"{k} {v['us']:.1f} us" for k, v in probe.items()))
     del Wlm
     # ---- LM head alone: batch 1 on the 1.5B head (HBM bound)
     c2 = bi.C2

@@ -266,6 +266,18 @@ def bd_copy_rows(row_mask, src0, dst0, src1=None, dst1=None, *, stream=None):
     _check("bd_copy_rows", st)
 
 
+def bd_probe_weight_stream(w, x=None, *, work_groups, stream=None):
+    """Measurement support: the streaming LM head's load pattern over w
+    [rows, K] (and the 64 rows of x [64, K] when given), no arithmetic."""
+    lib = _lib.load()
+    rows, row_bytes = w.shape[0], w.shape[1] * w.element_size()
+    if x is not None:
+        assert x.shape[0] >= 64 and x.shape[1] * x.element_size() == row_bytes
+    st = lib.bd_probe_weight_stream(_p(w), rows, row_bytes, _p(x), 0 if x is None else 4, int(work_groups),
+                                    _stream(stream))
+    _check("bd_probe_weight_stream", st)
+
+
 def bd_persequence_schedule(mask_bits, state, restore, save, save_h, row_idx, win_lo, *, D, S, kinds=None,
                             live=None, stream=None):
     """mask_bits [B] (64-bit) device; state [3, B] int32 device (win, opening,

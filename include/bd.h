@@ -281,6 +281,21 @@ bd_status bd_threshold_unmask_windows(int B, int D, int win_len, const int32_t* 
                                       int32_t* tokens, uint64_t* mask_bits,
                                       int32_t* n_unmasked, int32_t* unmasked_pos, void* stream);
 
+/* Measurement support, not a step of the method: the streaming LM head's
+ * load pattern with no arithmetic, so that timing it next to the LM head on
+ * the same matrix separates the cost of the loads from the rest of the
+ * kernel.  Work-group w of work_groups takes an equal range of the 16-row
+ * tiles of w [rows, row_bytes] (row-major, device) and reads it into LDS in
+ * passes of 8 tiles, one 128-byte piece of each row of the pass per stage;
+ * with x_tiles = 4 every stage also reads the matching piece of 64 rows of
+ * x [64, row_bytes] (device), as the LM head reads its rows.  Nothing is
+ * written to memory.  Requires rows % 16 == 0, row_bytes % 128 == 0,
+ * x_tiles in {0, 4} (x may be NULL when 0), 16-byte aligned pointers and
+ * 1 <= work_groups <= min(4096, rows / 16); BD_EINVAL otherwise.
+ * Asynchronous on `stream`. */
+bd_status bd_probe_weight_stream(const void* w, int rows, int row_bytes, const void* x, int x_tiles,
+                                 int work_groups, void* stream);
+
 /* Per-sequence window schedule on the device, so that the batched steps of
  * per-sequence window progression can be queued without a host round trip
  * ([v2 notes] Key designs 3 and 4: windows of S positions decoded left to

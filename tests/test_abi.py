@@ -33,7 +33,7 @@ def test_header_declares_the_four_calls_and_support():
               "bd_qkv_proj_rope", "bd_qkv_proj_rope_workspace_size", "bd_gate_up_swiglu", "bd_gate_up_swiglu_rmsnorm",
               "bd_train_attn", "bd_train_attn_workspace_size", "bd_masked_nll", "bd_threshold_unmask_tau",
               "bd_lmhead_unmask", "bd_threshold_unmask_windows", "bd_copy_rows", "bd_block_attn_noalloc",
-              "bd_persequence_schedule"]:
+              "bd_persequence_schedule", "bd_probe_weight_stream"]:
         assert n in names
 
 
@@ -324,6 +324,15 @@ def test_per_sequence_window_calls_argument_errors():
     assert sc(B=-1) == E and sc(S=0) == E and sc(D=64, S=8) == E and sc(D=32, S=12) == E and sc(D=4, S=8) == E
     assert sc(bits=None) == E and sc(rows=None) == E
     assert sc(B=0) == 0
+
+
+def test_probe_argument_errors():
+    lib = _lib.load()
+    E = _lib.BD_EINVAL
+    pr = lambda **k: lib.bd_probe_weight_stream(k.get("w", FAKE), k.get("rows", 1024), k.get("rb", 7168),
+                                                k.get("x", None), k.get("xt", 0), k.get("wg", 64), None)
+    assert pr(w=None) == E and pr(rows=1000) == E and pr(rb=7000) == E and pr(xt=4) == E and pr(xt=2, x=FAKE) == E
+    assert pr(wg=0) == E and pr(wg=65) == E and pr(w=FAKE + 8) == E and pr(xt=4, x=FAKE + 8) == E
 
 
 def test_guard_argument_errors():

@@ -593,3 +593,19 @@ def test_guarded_attention(dt, lens, n_q, q_off):
             assert torch.equal(o, o_want) and torch.equal(lse, l_want)
         else:
             assert bool((o == 3.0).all()) and bool((lse == 3.0).all())
+
+
+def test_probe_weight_stream_runs_and_writes_nothing():
+    """The LM head's load pattern alone (measurement support): runs at one,
+    a ragged number of and many work-groups, with and without the rows of x,
+    and leaves its inputs as they were."""
+    say("[probe] load pattern")
+    T = torch.bfloat16
+    w = torch.randn(4096, 3584, device=DEV, dtype=T)
+    x = torch.randn(64, 3584, device=DEV, dtype=T)
+    wc, xc = w.clone(), x.clone()
+    for wg in (1, 7, 256):
+        for xx in (None, x):
+            ops().bd_probe_weight_stream(w, xx, work_groups=wg)
+    torch.cuda.synchronize()
+    assert torch.equal(w, wc) and torch.equal(x, xc)
