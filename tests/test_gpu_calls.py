@@ -34,6 +34,10 @@ ATTN_CASES = {
     "bf16-sharp": ("bf16", 2, 12, 2, 128, 32, 8, 0, [3000, 1500], 32, 1.0, None),
     "bf16-prefill-4blk": ("bf16", 2, 12, 2, 128, 32, 128, 0, [0, 0], 128, 1.0, None),
     "bf16-d64": ("bf16", 2, 8, 2, 64, 32, 8, 8, [700, 1300], 32, 0.5, None),
+    # blocks of 64 positions (the most a mask word holds): exact step, and a
+    # DualCache step on the third window of 16
+    "bf16-D64-exact": ("bf16", 3, 28, 4, 128, 64, 64, 0, [0, 640, 2049], 64, 0.3, None),
+    "bf16-D64-dc": ("bf16", 3, 28, 4, 128, 64, 16, 32, [0, 640, 2049], 64, 0.3, None),
     "bf16-7B-long-dc": ("bf16", 32, 28, 4, 128, 32, 8, 8, [16384] * 32, 32, 0.02, [0, 13, 31]),
     "bf16-7B-long-exact": ("bf16", 32, 28, 4, 128, 32, 32, 0, [16384] * 32, 32, 0.02, [5, 30]),
     # long key streams of few (sequence, KV head) items: many key chunks per
