@@ -115,6 +115,9 @@ LM_CASES = {
     "bf16-7B-M17-sharp": ("bf16", 17, 20, 3584, 152064, 1.0, 60.0, False),
     "bf16-7B-M100": ("bf16", 100, 128, 3584, 152064, 1.0, 1.0, False),
     "bf16-ragged-vocab": ("bf16", 33, 40, 512, 1000, 1.0, 30.0, True),
+    # the one-work-group-per-CU streaming path (rows of 2048+ columns) with a
+    # ragged last tile and ~2 tiles per work-group
+    "bf16-M64-wide-ragged": ("bf16", 64, 70, 3584, 9001, 1.0, 30.0, True),
     # more than 256 rows: 256 x 256 tiles; two row blocks, the second ragged
     # (by one row in -257), and a ragged last vocabulary block
     "bf16-big-ragged": ("bf16", 300, 310, 512, 5000, 1.0, 30.0, True),
