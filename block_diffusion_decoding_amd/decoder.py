@@ -1,4 +1,4 @@
-"""Block-diffusion refinement driver on one GPU (one attention layer + LM head).
+"""Block-diffusion refinement decoder on one GPU (one attention layer + LM head).
 
 Every arithmetic step runs in libbd's HIP kernels through ``ops``; torch only
 allocates device memory and supplies the stream.  Names follow the method

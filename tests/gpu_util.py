@@ -1,4 +1,4 @@
-"""Helpers of the GPU parity tests: upload seeded inputs, build the driver
+"""Helpers of the GPU parity tests: upload seeded inputs, build the decoder
 and the oracle from the same draws, and the tolerance rules.
 
 Tolerances (per element type): 1e-3 relative for fp32, 2e-2 for bf16.

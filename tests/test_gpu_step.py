@@ -1,4 +1,4 @@
-"""GPU parity of whole refinement steps and block loops (driver + all calls)
+"""GPU parity of whole refinement steps and block loops (decoder + all calls)
 against the fp64 oracle on the same seeded inputs.
 
 Multi-step comparisons use teacher forcing: after every step the GPU state is
