@@ -370,6 +370,55 @@ class Loop:
                 left -= 1
 
 
+def graph_costs(dec, cfg, plant, reps=10) -> dict:
+    """GPU time of the captured graphs the loop replays, each from a fresh
+    block (every position masked, so every slot of window 0 is a refinement
+    step): a whole window (its exact step and DualCache slots as one graph),
+    the exact step alone, a DualCache step alone, and the commit.  HIP events
+    around each replay, medians.  A window against its slots gives a step's
+    cost inside one graph; a graph launched on its own adds its launch."""
+    S = cfg.S
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    zeros, ones = np.zeros((cfg.B, cfg.D), np.int32), np.ones((cfg.B, cfg.D), bool)
+
+    def fresh():
+        dec.set_block(zeros, ones, plant)
+        torch.cuda.synchronize()
+
+    def med(fn, n=reps, prep=fresh):
+        ts = []
+        for i in range(n + 2):
+            prep()
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        return round(float(np.median(ts)), 1)
+
+    def after_exact():  # a DualCache step follows its window's exact step (which leaves the rows current)
+        fresh()
+        dec.e_step(0, S, cfg.tau)
+        torch.cuda.synchronize()
+
+    win = med(lambda: dec.run_window(0, S, cfg.tau, wait=False))
+    fresh()
+    bits = dec.run_window(0, S, cfg.tau, wait=True)
+    before = np.concatenate([np.full((1, cfg.B), (1 << cfg.D) - 1, np.uint64), bits[:-1]])
+    live = int(((before & np.uint64((1 << S) - 1)) != 0).any(axis=1).sum())
+    out = {"window_graph_us": win, "window_slots": int(len(bits)), "window_live_slots": live,
+           "us_per_slot_in_window": round(win / len(bits), 1),
+           "exact_step_graph_us": med(lambda: dec.e_step(0, S, cfg.tau)),
+           "dualcache_step_graph_us": med(lambda: dec.dc_step(0, S, cfg.tau), prep=after_exact)}
+    n_commit = 3
+    if np.all(dec.kv_len_host + cfg.D * (n_commit + 2) <= cfg.cap):
+        out["commit_graph_us"] = med(dec.commit, n_commit, prep=torch.cuda.synchronize)
+    out["what"] = ("medians of HIP-event intervals around replays of the captured graphs, each from a fresh "
+                   "block: window 0 as one graph, its exact step alone, a DualCache step alone, the commit")
+    return out
+
+
 class Timing(NamedTuple):
     median: float
     mean: float
@@ -1225,6 +1274,9 @@ def main():
                      "note": "LM head + QKV/O weights + the batch's K/V at the starting lengths, read once, "
                              "against the whole loop's time per step (exact steps, window ends and host waits "
                              "included)"}
+    if windows:
+        step_roofline["graphs"] = graph_costs(dec, cfg, plants[0])
+        log(f"[bench] graphs: {json.dumps(step_roofline['graphs'])}")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "bd_lmhead_unmask (lm_stream_kernel<4, 4> + lm_merge_unmask_kernel: the LM head's final reduction "
